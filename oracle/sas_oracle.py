@@ -1,0 +1,354 @@
+"""CPU oracle for content-selected block-sparse attention (test infrastructure only).
+
+Only the tests, the package's smoke check and the CPU-baseline leg of the benchmark
+may import this module; the product path (the HIP library and its Python binding)
+never does.  Everything is plain numpy in float64 after an exact upcast of the
+(float32 or bf16-valued) inputs.  The module shares no code, table or helper with
+the GPU path.
+
+Pages cited below (by title; section in brackets):
+  [SAS]  "SAS: 通过端到端优化上下文排序的简单注意力稀疏化"  (ai-feeds.com, paper 2609.13141)
+  [BLOG] "稀疏注意力"  (blog.vegetog.com, ai-infra/sparse-attention)
+  [GSA]  "开源大模型注意力机制演进:从全注意力到门控稀疏注意力的工程实践"  (ruibaoantu.com)
+  [SSA]  "通过Gist Token的简化稀疏注意力"  (ai-feeds.com, paper 2604.20920)
+  [SF]   "稀疏注意力的Trade-offs：Transformer大语言模型实证研究"  (review of The Sparse Frontier)
+
+What is computed (plain definitions, no blocking or fusion beyond them):
+  1. block representative of block j = mean of the present keys of that block
+     ([SF] 2.1, representation heuristics: block-pooled token representations;
+     [GSA] section 4, pseudo-code step 1 aggregates keys per block).
+     Gist mode: the representative is the given gist key ([SSA] method, relevance scoring).
+  2. selection unit = the (query row, query head) pairs that share one block list:
+     decode -> one row; prefill -> the rows of one query block ([SF] 2.1 key constraint:
+     prefill selects block to block).  Per KV group (rows x the group's heads pooled) or
+     per query head ([SSA] method item 2, grouped expansion for GQA).
+  3. score of block j for unit u = mean over (row, head) in u of scale * q . r_j.
+  4. top-k by (score descending, block index ascending) among the blocks before the
+     current one, plus the current block always and block 0 when the sink is on
+     ([SAS] core modules 3 and 4; [BLOG] 4.6; [SF] 2.2.3 Star Attention).
+  5. optional gate: g(j) = s_j - log sum_{j' in Sel} exp(s_j'), added inside the
+     softmax ([SAS] core insight and core modules 2-3: the selector's score enters the
+     logits in log form, normalised by a softmax over the kept set that includes the
+     current block).
+  6. attention = softmax(q K^T * scale + M + g) V with M = 0 for allowed keys and
+     -inf otherwise ([BLOG] sections 1 and 2).  Allowed: keys of selected blocks at
+     positions <= the row's position.  Gist mode adds the gist tokens of the complete,
+     non-selected chunks before the current one ([SSA] method items 2 and 3).
+
+Readings taken where the pages leave a step open are listed in the repository's design
+notes; each is restated at the function that applies it.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+NEG_INF = float("-inf")
+
+
+# ---------------------------------------------------------------------------------------------
+# 1. block representatives
+# ---------------------------------------------------------------------------------------------
+def num_blocks(L: int, blk: int) -> int:
+    return (L + blk - 1) // blk
+
+
+def block_reps(K: np.ndarray, L: int, blk: int) -> np.ndarray:
+    """Mean-pooled key of every block of one (sequence, KV head) slab.
+
+    K: [>= L, d].  Returns [ceil(L/blk), d] float64; block j covers positions
+    [j*blk, min((j+1)*blk, L)) and its representative is the sum of those keys divided
+    by their count (the last block may be partial).  [SF] 2.1; [GSA] section 4 step 1.
+    """
+    K = np.asarray(K, dtype=np.float64)
+    nb = num_blocks(L, blk)
+    out = np.empty((nb, K.shape[1]), dtype=np.float64)
+    for j in range(nb):
+        lo, hi = j * blk, min((j + 1) * blk, L)
+        out[j] = K[lo:hi].sum(axis=0) / float(hi - lo)
+    return out
+
+
+# ---------------------------------------------------------------------------------------------
+# 2. selection units
+# ---------------------------------------------------------------------------------------------
+@dataclass
+class Unit:
+    """One selection unit of one sequence.
+
+    sel_head: KV head g (per-group selection) or query head h (per-head selection).
+    c: block index of the unit's query rows (the current block).
+    t_lo, t_hi: local query-row range [t_lo, t_hi) (positions q_start + t).
+    heads: query heads whose rows belong to the unit.
+    """
+    sel_head: int
+    c: int
+    t_lo: int
+    t_hi: int
+    heads: Tuple[int, ...]
+    scores: Optional[np.ndarray] = None       # [c+1] (index j <= c), float64
+    sel: Optional[List[int]] = None           # ascending block ids (forced ones included)
+    k: int = 0                                # budget actually used for the top-k part
+    gate: Optional[Dict[int, float]] = None   # block id -> log-gate value (None if gate off)
+
+
+def query_blocks(q_start: int, rows: int, blk: int) -> List[Tuple[int, int, int]]:
+    """(c, t_lo, t_hi) for every block c touched by positions q_start .. q_start+rows-1."""
+    out = []
+    t = 0
+    while t < rows:
+        p = q_start + t
+        c = p // blk
+        t_hi = min(rows, (c + 1) * blk - q_start)
+        out.append((c, t, t_hi))
+        t = t_hi
+    return out
+
+
+def make_units(q_start: int, rows: int, blk: int, hq: int, hkv: int, sel_mode: str) -> List[Unit]:
+    """Enumerate units in (selector head, query block) order.  sel_mode: 'group' | 'head'."""
+    G = hq // hkv
+    units = []
+    nsel = hkv if sel_mode == "group" else hq
+    for s in range(nsel):
+        heads = tuple(range(s * G, (s + 1) * G)) if sel_mode == "group" else (s,)
+        for (c, t_lo, t_hi) in query_blocks(q_start, rows, blk):
+            units.append(Unit(sel_head=s, c=c, t_lo=t_lo, t_hi=t_hi, heads=heads))
+    return units
+
+
+def kv_head_of(unit: Unit, G: int, sel_mode: str) -> int:
+    return unit.sel_head if sel_mode == "group" else unit.sel_head // G
+
+
+# ---------------------------------------------------------------------------------------------
+# 3. scores
+# ---------------------------------------------------------------------------------------------
+def unit_query_vectors(Qb: np.ndarray, unit: Unit) -> np.ndarray:
+    """All query vectors of the unit, [rows * heads, d] float64.  Qb: [hq, rows, d]."""
+    q = np.asarray(Qb[list(unit.heads), unit.t_lo:unit.t_hi, :], dtype=np.float64)
+    return q.reshape(-1, q.shape[-1])
+
+
+def unit_scores(qvecs: np.ndarray, reps: np.ndarray, upto: int, scale: float) -> np.ndarray:
+    """s_j for j in [0, upto): the mean over the unit's query vectors of scale * q . r_j.
+
+    Written as the definition (mean of the per-vector dot products), not as a dot with a
+    pooled query; the two agree by linearity.  [GSA] section 4 step 1; [SSA] method item 1
+    (query against every historical gist); reading: a unit's score averages its rows and
+    heads, as for the grouped decode workload whose scores average a group's query heads.
+    """
+    if upto <= 0:
+        return np.zeros(0, dtype=np.float64)
+    dots = qvecs @ np.asarray(reps[:upto], dtype=np.float64).T      # [n, upto]
+    return dots.sum(axis=0) / float(qvecs.shape[0]) * scale
+
+
+# ---------------------------------------------------------------------------------------------
+# 4. budget and top-k
+# ---------------------------------------------------------------------------------------------
+def budget_k(c: int, n_cand: int, k_fixed: int, frac_num: int, frac_den: int, count_current: int) -> int:
+    """Number of blocks the top-k part keeps for a unit whose current block is c.
+
+    Fixed budget: k_fixed.  Fractional budget: ceil(frac_num * (c + count_current) / frac_den)
+    in integers (the pages state budgets as a kept fraction, [GSA] section 4 pseudo-code
+    keep_ratio, [SF] 1.2: 0.95 sparsity keeps 1/20).  Never more than the candidates.
+    """
+    if frac_den == 0:
+        k = k_fixed
+    else:
+        num = frac_num * (c + count_current)
+        k = (num + frac_den - 1) // frac_den
+    return max(0, min(n_cand, k))
+
+
+def topk_blocks(scores: Sequence[float], c: int, k: int, sink: bool) -> List[int]:
+    """Selected block set of a unit, ascending.
+
+    Candidates are the blocks strictly before the current block c, minus the forced ones.
+    The k best by (score descending, index ascending) are kept; the current block is always
+    added ([SAS] core insight: the always-kept current block), and block 0 when the sink is
+    on ([SF] 2.2.3: local block plus the first prefix block).  Ties go to the lower index
+    (the pages are silent; the lower index is the stated rule for this library).
+    """
+    forced = {c}
+    if sink:
+        forced.add(0)
+    cand = [j for j in range(c) if j not in forced]
+    ranked = sorted(cand, key=lambda j: (-float(scores[j]), j))
+    return sorted(set(ranked[:k]) | forced)
+
+
+def gate_values(scores: Sequence[float], sel: Sequence[int]) -> Dict[int, float]:
+    """log of the softmax over the selected set of the selector scores ([SAS] core modules 2-3).
+
+    g(j) = s_j - log(sum_{j' in Sel} exp(s_j')), computed with the maximum subtracted.
+    Temperature 1 (the scores already carry the 1/sqrt(d) scale).
+    """
+    v = np.array([float(scores[j]) for j in sel], dtype=np.float64)
+    m = v.max()
+    lse = m + math.log(float(np.exp(v - m).sum()))
+    return {int(j): float(scores[j]) - lse for j in sel}
+
+
+# ---------------------------------------------------------------------------------------------
+# 5./6. attention
+# ---------------------------------------------------------------------------------------------
+def _softmax_rows(logits: np.ndarray) -> np.ndarray:
+    m = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def attend_unit(qrows: np.ndarray, pos: np.ndarray, K: np.ndarray, V: np.ndarray, L: int, blk: int,
+                sel: Sequence[int], gate: Optional[Dict[int, float]], scale: float,
+                mode: str = "skip", gist_k: Optional[np.ndarray] = None,
+                gist_v: Optional[np.ndarray] = None, gist_ids: Sequence[int] = ()) -> np.ndarray:
+    """softmax(q K^T * scale + M + g) V for the rows of one unit.
+
+    qrows: [n, d]; pos: [n] absolute positions of the rows; K, V: [>= L, d] of the unit's KV
+    head.  Key sigma is allowed iff its block is in ``sel`` and sigma <= the row's position
+    (and sigma < L).  ``g`` is the unit's log-gate per block (0 when None).
+    mode 'literal': every key's logit is formed and the mask M (0 / -inf) is added, as in
+    [BLOG] section 2; mode 'skip': only allowed keys are visited.  The two give identical
+    float64 results because exp(-inf) is exactly 0 and the kept terms are summed in the
+    same key order.
+    Gist mode ([SSA] method items 2-3): ``gist_ids`` lists the chunks whose gist token joins
+    the key set (complete, non-selected chunks before the current one); gist j contributes
+    key gist_k[j] and value gist_v[j], with no gate.  Gist tokens follow the raw keys in
+    the key order.
+    """
+    q = np.asarray(qrows, dtype=np.float64)
+    n = q.shape[0]
+    pos = np.asarray(pos, dtype=np.int64)
+    gate = gate or {}
+    sel_set = set(int(j) for j in sel)
+    if mode == "literal":
+        keys = np.arange(L)
+        Kd = np.asarray(K[:L], dtype=np.float64)
+        Vd = np.asarray(V[:L], dtype=np.float64)
+        logits = (q @ Kd.T) * scale                                     # [n, L]
+        blocks = keys // blk
+        allowed_blk = np.array([int(b) in sel_set for b in blocks], dtype=bool)
+        g = np.array([gate.get(int(b), 0.0) for b in blocks], dtype=np.float64)
+        M = np.where(allowed_blk[None, :] & (keys[None, :] <= pos[:, None]), 0.0, NEG_INF)
+        logits = logits + M + g[None, :]
+        vals = Vd
+    elif mode == "skip":
+        keys = np.concatenate([np.arange(j * blk, min((j + 1) * blk, L)) for j in sorted(sel_set)]) \
+            if sel_set else np.zeros(0, dtype=np.int64)
+        Kd = np.asarray(K[keys], dtype=np.float64)
+        vals = np.asarray(V[keys], dtype=np.float64)
+        g = np.array([gate.get(int(k) // blk, 0.0) for k in keys], dtype=np.float64)
+        logits = (q @ Kd.T) * scale + g[None, :]
+        logits = np.where(keys[None, :] <= pos[:, None], logits, NEG_INF)
+    else:
+        raise ValueError(mode)
+    if len(gist_ids):
+        gk = np.asarray(gist_k[list(gist_ids)], dtype=np.float64)
+        gv = np.asarray(gist_v[list(gist_ids)], dtype=np.float64)
+        logits = np.concatenate([logits, (q @ gk.T) * scale], axis=1)
+        vals = np.concatenate([vals, gv], axis=0)
+    p = _softmax_rows(logits)
+    return p @ vals
+
+
+# ---------------------------------------------------------------------------------------------
+# whole-sequence drivers
+# ---------------------------------------------------------------------------------------------
+@dataclass
+class SeqResult:
+    reps: np.ndarray                   # [hkv, NB, d] (gist mode: the gist keys)
+    units: List[Unit]
+    O: np.ndarray                      # [hq, rows, dv]; NaN where not computed
+    pairs: int = 0                     # visible raw (row, key) pairs over computed rows
+    gist_pairs: int = 0                # visible gist (row, gist) pairs over computed rows
+
+
+def run_sequence(Qb: np.ndarray, Kb: np.ndarray, Vb: np.ndarray, L: int, q_start: int, blk: int,
+                 sel_mode: str, k_fixed: int = 0, frac_num: int = 0, frac_den: int = 0,
+                 count_current: int = 0, sink: bool = False, gate: bool = False,
+                 scale: Optional[float] = None, gist_k: Optional[np.ndarray] = None,
+                 gist_v: Optional[np.ndarray] = None, mode: str = "skip",
+                 unit_filter=None, attend: bool = True, reps: Optional[np.ndarray] = None,
+                 explicit: Optional[Dict[Tuple[int, int], Tuple[List[int], Optional[Dict[int, float]]]]] = None
+                 ) -> SeqResult:
+    """Oracle for one sequence: reps -> scores -> top-k (+forced, +gate) -> attention.
+
+    Qb: [hq, rows, d] rows at positions q_start..q_start+rows-1 (decode: rows == 1 at L-1).
+    Kb, Vb: [hkv, >= L, d].  gist_k/gist_v: [hkv, >= c, d] switch on gist mode (decode).
+    unit_filter(unit) -> bool restricts which units are scored/attended (others are skipped).
+    explicit[(sel_head, c)] = (sel, gate) replaces the unit's own selection (used to check the
+    attention step on a list produced elsewhere when selections differ inside the tie band).
+    """
+    hq, rows, d = Qb.shape
+    hkv = Kb.shape[0]
+    G = hq // hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    gist_mode = gist_k is not None
+    if gist_mode and gate:
+        raise ValueError("the log-gate is not defined for gist tokens")
+    if reps is None:
+        if gist_mode:
+            reps = np.asarray(gist_k, dtype=np.float64)
+        else:
+            reps = np.stack([block_reps(Kb[g], L, blk) for g in range(hkv)])
+    units = make_units(q_start, rows, blk, hq, hkv, sel_mode)
+    O = np.full((hq, rows, Vb.shape[-1]), np.nan)
+    pairs = 0
+    gpairs = 0
+    for u in units:
+        if unit_filter is not None and not unit_filter(u):
+            continue
+        g = kv_head_of(u, G, sel_mode)
+        qv = unit_query_vectors(Qb, u)
+        if gist_mode:
+            # gists exist for the complete chunks before the current one only
+            s = np.full(u.c + 1, NEG_INF)
+            s[:u.c] = unit_scores(qv, reps[g], u.c, scale)
+        else:
+            s = unit_scores(qv, reps[g], u.c + 1, scale)
+        u.scores = s
+        n_cand = u.c - (1 if (sink and u.c > 0) else 0)
+        u.k = budget_k(u.c, n_cand, k_fixed, frac_num, frac_den, count_current)
+        u.sel = topk_blocks(s, u.c, u.k, sink)
+        u.gate = gate_values(s, u.sel) if gate else None
+        sel, gv = u.sel, u.gate
+        if explicit is not None and (u.sel_head, u.c) in explicit:
+            sel, gv = explicit[(u.sel_head, u.c)]
+        if not attend:
+            continue
+        gist_ids = [j for j in range(u.c) if j not in set(sel)] if gist_mode else []
+        for h in u.heads:
+            qrows = Qb[h, u.t_lo:u.t_hi, :]
+            pos = q_start + np.arange(u.t_lo, u.t_hi)
+            O[h, u.t_lo:u.t_hi, :] = attend_unit(qrows, pos, Kb[g], Vb[g], L, blk, sel, gv, scale, mode,
+                                                 gist_k[g] if gist_mode else None,
+                                                 gist_v[g] if gist_mode else None, gist_ids)
+            pairs += visible_raw_pairs(pos, sel, blk, L)
+            gpairs += len(gist_ids) * len(pos)
+    return SeqResult(reps=reps, units=units, O=O, pairs=pairs, gist_pairs=gpairs)
+
+
+def visible_raw_pairs(pos: np.ndarray, sel: Sequence[int], blk: int, L: int) -> int:
+    """Number of (row, raw key) pairs a row set may attend: keys of selected blocks at <= the row."""
+    pos = np.asarray(pos, dtype=np.int64)
+    total = 0
+    for j in sel:
+        hi = np.minimum(np.minimum((j + 1) * blk, L), pos + 1)
+        total += int(np.clip(hi - j * blk, 0, None).sum())
+    return total
+
+
+def dense_causal_pairs(q_start: int, rows: int) -> int:
+    """(row, key) pairs of full causal attention for the rows: sum over rows of (p + 1)."""
+    return sum(q_start + t + 1 for t in range(rows))
+
+
+def sparsity(computed_pairs: int, full_pairs: int) -> float:
+    """1 - computed / full ([SF] 1.2)."""
+    return 1.0 - computed_pairs / float(full_pairs)

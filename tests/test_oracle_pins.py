@@ -1,0 +1,311 @@
+"""Pins of the CPU oracle against facts fixed outside it (CPU only).
+
+Each test checks the oracle against something it does not compute itself: a pattern
+printed on the pages (tests/golden), a hand-worked example, a library routine
+(torch's scaled_dot_product_attention in float64 on the CPU, numpy reductions), a
+brute-force enumeration, or a closed form.  Together they are chosen so that a dropped
+term, a wrong sign or index, or a transposed operand in any oracle step fails one of them.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import sas_oracle as o
+from workloads import Workload, round_bf16
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load_matrix(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append([int(x) for x in line.split()])
+    return np.array(rows)
+
+
+def _sdpa(q, k, v, additive):
+    """torch SDPA in float64 on the CPU with an additive float mask [n, L]."""
+    qt = torch.from_numpy(np.asarray(q, np.float64))[None, None]
+    kt = torch.from_numpy(np.asarray(k, np.float64))[None, None]
+    vt = torch.from_numpy(np.asarray(v, np.float64))[None, None]
+    mt = torch.from_numpy(np.asarray(additive, np.float64))[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mt)[0, 0].numpy()
+
+
+# ------------------------------------------------------------------------------------ P1
+def test_window_pattern_from_topk_recency():
+    """Token-level blocks with recency scores and k = w - 1 = 2 reproduce the printed w=3 window."""
+    L, d = 6, 2
+    q = np.zeros((1, L, d)); q[0, :, 0] = math.sqrt(2.0)          # score of key j == j
+    K = np.zeros((1, L, d)); K[0, :, 0] = np.arange(L)
+    V = np.eye(L)[None]                                            # output row == attention weights
+    r = o.run_sequence(q, K, V, L, 0, 1, "group", k_fixed=2)
+    mask = (r.O[0] > 0).astype(int)
+    np.testing.assert_array_equal(mask, _load_matrix("window_w3_pattern.txt"))
+
+
+# ------------------------------------------------------------------------------------ P2
+def test_block_pattern_from_explicit_lists():
+    """The printed 4x4 block-sparse pattern is what the mask expansion of its block lists gives."""
+    blk, L, d = 3, 12, 4
+    rng = np.random.default_rng(0)
+    q = rng.standard_normal((1, L, d)); K = rng.standard_normal((1, L, d))
+    V = np.eye(L)[None]
+    lists = {0: [0], 1: [0, 1], 2: [1, 2], 3: [0, 2, 3]}           # Q1:{1} Q2:{1,2} Q3:{2,3} Q4:{1,3,4}
+    explicit = {(0, c): (sel, None) for c, sel in lists.items()}
+    r = o.run_sequence(q, K, V, L, 0, blk, "group", k_fixed=0, explicit=explicit)
+    tok = r.O[0] > 0                                                # [query token, key token]
+    blocks = tok.reshape(4, blk, 4, blk).any(axis=(1, 3)).astype(int)
+    np.testing.assert_array_equal(blocks, _load_matrix("block_sparse_4x4_pattern.txt"))
+
+
+# ------------------------------------------------------------------------------------ hand example
+def test_hand_worked_three_keys():
+    g = {}
+    with open(os.path.join(GOLDEN, "hand_three_keys.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                name, a, b = line.split()
+                g[name] = (float(a), float(b))
+    q = np.array([[[math.sqrt(2.0), 0.0]]])
+    K = np.array([[[0.0, 0.0], [math.log(3.0), 0.0], [0.0, 0.0]]])
+    V = np.array([[[1.0, 0.0], [0.0, 1.0], [1.0, 1.0]]])
+    for name, kw in (("dense", dict(k_fixed=5)), ("top1", dict(k_fixed=1)),
+                     ("top1_gate", dict(k_fixed=1, gate=True))):
+        r = o.run_sequence(q, K, V, 3, 2, 1, "group", **kw)
+        np.testing.assert_allclose(r.O[0, 0], g[name], rtol=0, atol=1e-14)
+
+
+# ------------------------------------------------------------------------------------ P3
+@pytest.mark.parametrize("q_start,rows", [(0, 37), (20, 17)])
+@pytest.mark.parametrize("sel_mode", ["group", "head"])
+def test_all_blocks_is_dense_causal_sdpa(q_start, rows, sel_mode):
+    """Budget >= #blocks with the gate off is dense causal attention (torch SDPA, float64)."""
+    rng = np.random.default_rng(1)
+    hq, hkv, d, L, blk = 4, 2, 8, 37, 4
+    Q = rng.standard_normal((hq, rows, d)); K = rng.standard_normal((hkv, L, d)); V = rng.standard_normal((hkv, L, d))
+    r = o.run_sequence(Q, K, V, L, q_start, blk, sel_mode, k_fixed=100)
+    pos = q_start + np.arange(rows)
+    add = np.where(np.arange(L)[None, :] <= pos[:, None], 0.0, -np.inf)
+    for h in range(hq):
+        ref = _sdpa(Q[h], K[h // 2], V[h // 2], add)
+        np.testing.assert_allclose(r.O[h], ref, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------------------------ P4
+@pytest.mark.parametrize("gate", [False, True])
+@pytest.mark.parametrize("sink", [False, True])
+def test_selected_equals_sdpa_with_minus_inf_mask(gate, sink):
+    """Sparse output == dense attention with unselected blocks at -inf (+ the gate), via SDPA."""
+    rng = np.random.default_rng(2)
+    hq, hkv, d, L, blk = 6, 2, 16, 53, 5
+    q_start, rows = 11, 42
+    Q = rng.standard_normal((hq, rows, d)); K = rng.standard_normal((hkv, L, d)); V = rng.standard_normal((hkv, L, d))
+    r = o.run_sequence(Q, K, V, L, q_start, blk, "group", k_fixed=3, sink=sink, gate=gate)
+    lit = o.run_sequence(Q, K, V, L, q_start, blk, "group", k_fixed=3, sink=sink, gate=gate, mode="literal")
+    np.testing.assert_allclose(r.O, lit.O, rtol=0, atol=1e-13)
+    G = hq // hkv
+    for u in r.units:
+        for h in u.heads:
+            pos = q_start + np.arange(u.t_lo, u.t_hi)
+            keys = np.arange(L)
+            ok = np.isin(keys // blk, u.sel)[None, :] & (keys[None, :] <= pos[:, None])
+            add = np.where(ok, 0.0, -np.inf)
+            if gate:
+                add = add + np.array([u.gate.get(int(j), 0.0) for j in keys // blk])[None, :]
+            ref = _sdpa(Q[h, u.t_lo:u.t_hi], K[h // G], V[h // G], add)
+            np.testing.assert_allclose(r.O[h, u.t_lo:u.t_hi], ref, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------------------------ P5
+def _brute_topk(scores, c, k, sink):
+    forced = {c} | ({0} if sink else set())
+    cand = [j for j in range(c) if j not in forced]
+    best = None
+    for sub in itertools.combinations(cand, min(k, len(cand))):
+        key = (sorted((scores[j] for j in sub), reverse=True), [-x for x in sorted(sub)])
+        # best = lexicographically largest sorted score vector; among equal, smallest indices
+        if best is None or key[0] > best[0][0] or (key[0] == best[0][0] and sorted(sub) < best[1]):
+            best = (key, sorted(sub))
+    return sorted(set(best[1]) | forced)
+
+
+def test_topk_brute_force_with_ties():
+    rng = np.random.default_rng(3)
+    for trial in range(300):
+        c = int(rng.integers(0, 11))
+        scores = [float(x) for x in rng.integers(0, 4, size=c + 1)]   # many exact ties
+        sink = bool(rng.integers(0, 2))
+        k = int(rng.integers(0, c + 2))
+        assert o.topk_blocks(scores, c, k, sink) == _brute_topk(scores, c, k, sink), (scores, c, k, sink)
+
+
+def test_topk_prefers_lower_index_on_ties_and_keeps_forced():
+    assert o.topk_blocks([1.0, 5.0, 5.0, 5.0, 0.0], 4, 2, False) == [1, 2, 4]
+    assert o.topk_blocks([9.0, 5.0, 5.0, 7.0, 0.0], 4, 1, True) == [0, 3, 4]
+    assert o.topk_blocks([0.0], 0, 3, True) == [0]
+
+
+# ------------------------------------------------------------------------------------ budgets
+def test_budget_rules():
+    # fixed budget, capped by the candidate count
+    assert o.budget_k(c=511, n_cand=511, k_fixed=16, frac_num=0, frac_den=0, count_current=0) == 16
+    assert o.budget_k(c=3, n_cand=3, k_fixed=16, frac_num=0, frac_den=0, count_current=0) == 3
+    # top 1/8 of the prior blocks: ceil(c/8)
+    assert [o.budget_k(c, c, 0, 1, 8, 0) for c in (0, 1, 8, 9, 255)] == [0, 1, 1, 2, 32]
+    # 5% of the visible blocks (c+1), rounded up
+    assert [o.budget_k(c, c, 0, 1, 20, 1) for c in (0, 19, 20, 2047)] == [0, 1, 2, 103]
+
+
+# ------------------------------------------------------------------------------------ P6
+def test_gate_constant_shift_invariance():
+    rng = np.random.default_rng(4)
+    d, L, blk = 8, 24, 4
+    q = rng.standard_normal((5, d)); K = rng.standard_normal((L, d)); V = rng.standard_normal((L, d))
+    pos = np.arange(19, 24)
+    sel = [0, 2, 5]
+    g = o.gate_values([0.3] * 6, sel)
+    assert all(abs(v + math.log(3.0)) < 1e-15 for v in g.values())
+    a = o.attend_unit(q, pos, K, V, L, blk, sel, g, 0.5)
+    b = o.attend_unit(q, pos, K, V, L, blk, sel, None, 0.5)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-14)
+    assert o.gate_values([2.5], [0]) == {0: 0.0}
+
+
+# ------------------------------------------------------------------------------------ P7
+def test_gate_block_decomposition_closed_form():
+    """With the gate, out = sum_j pi_j Z_j o_j / sum_j pi_j Z_j (pi = softmax over Sel of s)."""
+    rng = np.random.default_rng(5)
+    hq, hkv, d, L, blk = 2, 1, 8, 40, 8
+    Q = rng.standard_normal((hq, 1, d)); K = rng.standard_normal((hkv, L, d)); V = rng.standard_normal((hkv, L, d))
+    r = o.run_sequence(Q, K, V, L, L - 1, blk, "head", k_fixed=2, gate=True)
+    sc = 1.0 / math.sqrt(d)
+    for u in r.units:
+        h = u.sel_head
+        s = u.scores
+        pi = np.exp(np.array([s[j] for j in u.sel]) - max(s[j] for j in u.sel))
+        pi /= pi.sum()
+        num = np.zeros(d); den = 0.0
+        for w, j in zip(pi, u.sel):
+            lo, hi = j * blk, min((j + 1) * blk, L)
+            logit = K[0, lo:hi] @ Q[h, 0] * sc
+            e = np.exp(logit)
+            Z = e.sum()
+            oj = (e[:, None] * V[0, lo:hi]).sum(axis=0) / Z
+            num += w * Z * oj; den += w * Z
+        np.testing.assert_allclose(r.O[h, 0], num / den, rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------------------------------------ P8 / scores
+def test_scores_closed_form():
+    """Constant-key blocks: rep = that key, score = scale * mean(q) . key (hand values)."""
+    d, blk, L = 4, 2, 6
+    K = np.zeros((1, L, d))
+    K[0, 0:2] = [1, 0, 0, 0]; K[0, 2:4] = [0, 2, 0, 0]; K[0, 4:6] = [1, 1, 1, 1]
+    Q = np.zeros((2, 2, d))                                   # 2 heads of one group, rows at 4, 5
+    Q[0, 0] = [2, 0, 0, 0]; Q[0, 1] = [0, 0, 0, 2]; Q[1, 0] = [0, 4, 0, 0]; Q[1, 1] = [2, 2, 2, 2]
+    V = np.zeros((1, L, d))
+    r = o.run_sequence(Q, K, V, L, 4, blk, "group", k_fixed=0, scale=0.5)
+    (u,) = r.units
+    # mean q = (1, 1.5, 0.5, 1); scores = 0.5 * (1, 3, 4)
+    np.testing.assert_allclose(u.scores, [0.5, 1.5, 2.0], rtol=0, atol=1e-15)
+    # per-head selection: head 0 mean q = (1,0,0,1) -> 0.5*(1, 0, 2); head 1 = (1,3,1,1) -> 0.5*(1, 6, 6)
+    r2 = o.run_sequence(Q, K, V, L, 4, blk, "head", k_fixed=0, scale=0.5)
+    np.testing.assert_allclose(r2.units[0].scores, [0.5, 0.0, 1.0], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(r2.units[1].scores, [0.5, 3.0, 3.0], rtol=0, atol=1e-15)
+
+
+def test_score_linearity_pooled_query():
+    rng = np.random.default_rng(6)
+    qv = rng.standard_normal((50, 16)); reps = rng.standard_normal((9, 16))
+    s = o.unit_scores(qv, reps, 9, 0.25)
+    np.testing.assert_allclose(s, 0.25 * (qv.mean(axis=0) @ reps.T), rtol=1e-13, atol=1e-14)
+
+
+# ------------------------------------------------------------------------------------ P9
+def test_decode_equals_last_prefill_row():
+    rng = np.random.default_rng(7)
+    hq, hkv, d, blk = 4, 2, 16, 8
+    L = blk * 9 + 1                                           # last block holds only position L-1
+    Q = rng.standard_normal((hq, L, d)); K = rng.standard_normal((hkv, L, d)); V = rng.standard_normal((hkv, L, d))
+    kw = dict(k_fixed=3, gate=True, sink=True)
+    pre = o.run_sequence(Q, K, V, L, 0, blk, "head", **kw)
+    dec = o.run_sequence(Q[:, L - 1:], K, V, L, L - 1, blk, "head", **kw)
+    np.testing.assert_allclose(dec.O[:, 0], pre.O[:, L - 1], rtol=0, atol=1e-13)
+
+
+# ------------------------------------------------------------------------------------ P11 gist limits
+def test_gist_limits():
+    rng = np.random.default_rng(8)
+    hq, hkv, d, blk = 2, 1, 8, 4
+    L = blk * 7 + 3                                           # 7 complete chunks, query in chunk 7
+    Q = rng.standard_normal((hq, 1, d)); K = rng.standard_normal((hkv, L, d)); V = rng.standard_normal((hkv, L, d))
+    gk = rng.standard_normal((hkv, 7, d)); gv = rng.standard_normal((hkv, 7, d))
+    p = L - 1
+    # every chunk expanded: plain causal attention over the raw tokens
+    r = o.run_sequence(Q, K, V, L, p, blk, "group", k_fixed=100, gist_k=gk, gist_v=gv)
+    add = np.zeros((1, L))
+    for h in range(hq):
+        np.testing.assert_allclose(r.O[h], _sdpa(Q[h], K[0], V[0], add), rtol=0, atol=1e-12)
+    assert r.gist_pairs == 0
+    # nothing expanded: the 7 gists plus the raw tokens of the current chunk
+    r0 = o.run_sequence(Q, K, V, L, p, blk, "group", k_fixed=0, gist_k=gk, gist_v=gv)
+    kk = np.concatenate([gk[0], K[0, 7 * blk:L]]); vv = np.concatenate([gv[0], V[0, 7 * blk:L]])
+    for h in range(hq):
+        np.testing.assert_allclose(r0.O[h], _sdpa(Q[h], kk, vv, np.zeros((1, kk.shape[0]))), rtol=0, atol=1e-12)
+    assert r0.gist_pairs == 7 * hq and r0.pairs == 3 * hq
+
+
+# ------------------------------------------------------------------------------------ P12 reps
+def test_reps_closed_forms_and_library_mean():
+    rng = np.random.default_rng(9)
+    d, blk = 8, 4
+    K = rng.standard_normal((4 * blk + 1, d))
+    K[blk:2 * blk] = K[blk]                                   # constant block
+    reps = o.block_reps(K, 4 * blk + 1, blk)
+    assert reps.shape == (5, d)
+    np.testing.assert_array_equal(reps[1], K[blk])
+    np.testing.assert_array_equal(reps[4], K[4 * blk])        # 1-token partial block
+    np.testing.assert_allclose(reps[:4], K[:4 * blk].reshape(4, blk, d).mean(axis=1), rtol=1e-14, atol=1e-15)
+    reps2 = o.block_reps(K, 4 * blk - 2, blk)                 # partial block of 2 tokens
+    np.testing.assert_allclose(reps2[3], K[3 * blk:4 * blk - 2].mean(axis=0), rtol=1e-14)
+
+
+# ------------------------------------------------------------------------------------ P13 sparsity
+def test_sparsity_accounting_tiny_prefill_closed_form():
+    """Config 1: sum over query blocks of (min(c,4)*64*64 + 64*65/2) = 254,464 visible pairs."""
+    w = Workload(1)
+    Q = w.q(0); K, V = w.kv(0)
+    r = o.run_sequence(Q, K, V, w.seq_lens[0], 0, w.block, "group", k_fixed=4)
+    closed = sum(min(c, 4) * 64 * 64 + 64 * 65 // 2 for c in range(16))
+    assert r.pairs == closed == 254464
+    assert abs(o.sparsity(r.pairs, o.dense_causal_pairs(0, 1024)) - (1 - 254464 / 524800)) < 1e-15
+
+
+def test_sparsity_accounting_block_rules():
+    # decode, 32K context, 64-token blocks, 16 + current: 17 blocks of 64 keys per row
+    assert 1 - 17 * 64 / 32768 == pytest.approx(0.96680, abs=1e-5)
+    # causal prefill, 256 blocks of 128, ceil(c/8) + sink + current
+    per_head = 0
+    for c in range(256):
+        n = len(o.topk_blocks(list(range(c + 1)), c, o.budget_k(c, max(c - 1, 0), 0, 1, 8, 0), True))
+        per_head += (n - 1) * 128 * 128 + 128 * 129 // 2
+    assert per_head == 74956800
+    # gist decode: 104 expanded chunks, 1 raw token of the current chunk, 1944 gists
+    assert 104 * 64 + 1 + (2048 - 104) == 8601
+
+
+def test_workload_inputs_are_bf16_and_seeded():
+    w = Workload(2, mini=True)
+    K, V = w.kv(3)
+    np.testing.assert_array_equal(K, round_bf16(K))
+    K2, _ = Workload(2, mini=True).kv(3)
+    np.testing.assert_array_equal(K, K2)
+    assert K.shape == (8, 4096, 128)
