@@ -1,0 +1,176 @@
+/*
+ * sas.h - C ABI of the MI355X (gfx950) content-selected block-sparse attention library.
+ *
+ * Pages cited (by title; section in brackets):
+ *   [SAS]  "SAS: 通过端到端优化上下文排序的简单注意力稀疏化"
+ *   [BLOG] "稀疏注意力" (blog.vegetog.com)
+ *   [GSA]  "开源大模型注意力机制演进:从全注意力到门控稀疏注意力的工程实践"
+ *   [SSA]  "通过Gist Token的简化稀疏注意力"
+ *   [SF]   "稀疏注意力的Trade-offs：Transformer大语言模型实证研究"
+ *
+ * The path ([GSA] section 4 pseudo-code steps 1-3, [SAS] method, [SSA] method):
+ *   sas_block_reps    one representative key per block (mean of its keys)
+ *   sas_block_scores  score every earlier block against each selection unit's queries
+ *   sas_topk_select   top-k blocks + the current block (+ block 0), optional log-gate
+ *   sas_sparse_prefill / sas_sparse_decode  attention over the selected blocks only
+ *
+ * Conventions shared by every entry point
+ *   - Shapes.  B sequences, Hq query heads, Hkv KV heads (Hq % Hkv == 0, G = Hq/Hkv),
+ *     head dim d in {64, 128}, block size blk in {64, 128}.  Sequence b holds L_b
+ *     tokens; block j covers positions [j*blk, min((j+1)*blk, L_b)); NB_b = ceil(L_b/blk).
+ *   - Element strides are in elements (not bytes); the last dimension (d) is contiguous.
+ *     Q and O are [B, Hq, T, d]; K and V are [B, Hkv, Lmax, d]; gist K/V [B, Hkv, NC, d].
+ *   - seq_lens and q_start are HOST arrays of int32 (read during the call, not kept).
+ *     Every other pointer is DEVICE memory owned by the caller; the library never
+ *     allocates, frees or keeps device memory, and never synchronises the stream.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream).
+ *   - Arguments are validated on the host before anything is launched; validation makes
+ *     no HIP call, so an invalid call returns an error code and touches nothing.
+ *     Launch failures return SAS_ERR_HIP.  sas_last_error() gives a thread-local text.
+ *   - Selection unit ([SF] 2.1: prefill selects block to block; [SSA] method item 2:
+ *     grouped or per-head expansion):
+ *       decode : one unit per (sequence, selector head), the row at position L_b - 1;
+ *       prefill: rows at positions q_start[b] + t, t < tq; the rows that fall in one
+ *                block c form one unit per selector head.
+ *     Selector head: SAS_SEL_GROUP -> KV head g (its G query heads pooled);
+ *                    SAS_SEL_HEAD  -> query head h (uses KV head h / G).
+ *     Unit array index: u = (b * S + s) * QB + i, S = Hkv or Hq, QB = sas_num_qblocks(tq, blk),
+ *     i = c - floor(q_start[b] / blk).  Decode: QB = 1, i = 0.
+ */
+#ifndef SAS_H
+#define SAS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SAS_OK = 0,
+  SAS_ERR_NULL = -1,        /* a required pointer is NULL                                  */
+  SAS_ERR_SHAPE = -2,       /* inconsistent sizes, strides, lengths, budget or kcap        */
+  SAS_ERR_UNSUPPORTED = -3, /* valid but not built: d, blk, dtype or mode combination      */
+  SAS_ERR_WORKSPACE = -4,   /* workspace smaller than the size query returns               */
+  SAS_ERR_HIP = -5          /* a HIP launch failed; see sas_last_error()                   */
+} sas_status;
+
+typedef enum { SAS_F32 = 0, SAS_BF16 = 1 } sas_dtype;
+typedef enum { SAS_SEL_GROUP = 0, SAS_SEL_HEAD = 1 } sas_sel_mode;
+typedef enum { SAS_REPS_POOLED = 0, SAS_REPS_GIST = 1 } sas_reps_kind;
+
+#define SAS_MAX_BATCH 64 /* sequences per call */
+
+typedef struct sas_problem {
+  int32_t batch;            /* B, 1 .. SAS_MAX_BATCH                                       */
+  int32_t hq, hkv;          /* query heads, KV heads                                        */
+  int32_t head_dim;         /* d                                                            */
+  int32_t block;            /* blk: tokens per block (SSA: per chunk)                       */
+  int32_t dtype;            /* sas_dtype of Q, K, V, O and gist K/V                         */
+  int32_t max_len;          /* Lmax: token capacity of K/V (every L_b <= Lmax)              */
+  const int32_t *seq_lens;  /* HOST [B]: L_b >= 1                                           */
+} sas_problem;
+
+/* Budget ([SAS] method: a fixed budget of k context units per query, configurable;
+ * [GSA] section 4 pseudo-code keep_ratio).  For a unit whose current block is c:
+ *   candidates = blocks 0 .. c-1, minus block 0 when force_sink;
+ *   k = k_fixed                                            if frac_den == 0
+ *   k = ceil(frac_num * (c + count_current) / frac_den)    otherwise (integer arithmetic)
+ *   k is capped at the candidate count; the current block c is always added ([SAS] core
+ *   insight), and block 0 when force_sink ([SF] 2.2.3, first prefix block). */
+typedef struct sas_budget {
+  int32_t k_fixed;
+  int32_t frac_num, frac_den, count_current;
+  int32_t force_sink;       /* 1: block 0 is always kept                                    */
+  int32_t gate;             /* 1: write the log-gate over the selected set                  */
+} sas_budget;
+
+/* Number of query blocks tq consecutive positions can touch: ceil((tq-1)/blk) + 1. */
+int32_t sas_num_qblocks(int32_t tq, int32_t block);
+
+/* Smallest kcap that holds every unit's selected list for this call (>= 1), or a negative
+ * sas_status for invalid arguments.  q_start: HOST [B], or NULL for decode. */
+int32_t sas_required_kcap(const sas_problem *p, int32_t tq, const int32_t *q_start,
+                          const sas_budget *budget);
+
+/* A1 - block representatives ([SF] 2.1 representation heuristics: block-pooled token
+ * representations; [GSA] section 4 step 1).
+ *   reps[b, g, j, :] = (1/n_j) * sum of K[b, g, t, :] over the n_j present tokens of block j,
+ *   for j < NB_b, in fp32 (blocks >= NB_b are left untouched).
+ *   K: [B, Hkv, Lmax, d] dtype, k_stride = {batch, head, token}.
+ *   reps: [B, Hkv, >= NB_b, d] fp32, rep_stride = {batch, head, block}. */
+sas_status sas_block_reps(const sas_problem *p, const void *K, const int64_t k_stride[3],
+                          float *reps, const int64_t rep_stride[3], void *stream);
+
+/* A2 - block scores ([GSA] section 4 step 1; [SSA] method item 1, query against every
+ * historical gist).  For unit u with current block c and query vectors q (its rows times
+ * its heads):  scores[u, j] = scale * mean_q (q . r_j)   for every block j <= c that has a
+ * representative, -inf for the other j <= c; entries j > c are not written.
+ *   reps_kind SAS_REPS_POOLED: r = fp32 reps from sas_block_reps (every block has one).
+ *   reps_kind SAS_REPS_GIST  : r = gist keys of dtype p->dtype, one per complete chunk
+ *                              ([SSA] method: a gist token after each chunk); only the
+ *                              chunks j < c are scored (the current chunk is attended raw).
+ *   Q: [B, Hq, T, d] dtype, q_stride = {batch, head, row}; tq rows per sequence.
+ *   q_start: HOST [B] first row position, or NULL for decode (tq == 1, row at L_b - 1).
+ *   scale: > 0, or 0 for 1/sqrt(d).
+ *   scores: [B * S * QB, scores_ld] fp32, scores_ld >= max_b NB_b.
+ *   workspace: device scratch of sas_block_scores_workspace() bytes (0 for decode). */
+size_t sas_block_scores_workspace(const sas_problem *p, int32_t tq, int32_t sel_mode);
+sas_status sas_block_scores(const sas_problem *p, const void *Q, const int64_t q_stride[3],
+                            int32_t tq, const int32_t *q_start, const void *reps, int32_t reps_kind,
+                            const int64_t rep_stride[3], int32_t sel_mode, float scale,
+                            float *scores, int64_t scores_ld, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/* A3 - top-k + forced blocks + log-gate ([SAS] core modules 2-4; [BLOG] 4.6).
+ *   Keeps the k best candidates by (score descending, block index ascending), adds the
+ *   current block and, with force_sink, block 0.
+ *   idx [units, kcap] int32: the selected blocks in ascending order, then -1 padding;
+ *   nsel [units] int32: list length (0 for unit slots no row falls in);
+ *   gate [units, kcap] fp32 (required iff budget->gate, else ignored and may be NULL):
+ *   g = s_j - log(sum over the selected set of exp(s)), 0 in the padding.
+ *   kcap must be >= sas_required_kcap(). */
+sas_status sas_topk_select(const sas_problem *p, const float *scores, int64_t scores_ld,
+                           int32_t tq, const int32_t *q_start, int32_t sel_mode,
+                           const sas_budget *budget, int32_t kcap, int32_t *idx, int32_t *nsel,
+                           float *gate, void *stream);
+
+/* A4 - sparse prefill ([BLOG] sections 2 and 7: masked softmax attention computed block by
+ * block, skipping masked blocks; [SAS] core modules 2-3: log-gate inside the softmax).
+ *   O[b, h, t] = softmax_s(scale * q . k_s + gate_u(block(s))) v_s over keys s of the
+ *   unit's selected blocks with s <= q_start[b] + t.
+ *   Q, O: [B, Hq, T, d] (q_stride, o_stride = {batch, head, row}); K, V: kv_stride.
+ *   gate: [units, kcap] or NULL for no gate.  scale: > 0 or 0 for 1/sqrt(d). */
+sas_status sas_sparse_prefill(const sas_problem *p, const void *Q, const int64_t q_stride[3],
+                              const void *K, const void *V, const int64_t kv_stride[3],
+                              int32_t tq, const int32_t *q_start, int32_t sel_mode,
+                              const int32_t *idx, const int32_t *nsel, const float *gate,
+                              int32_t kcap, float scale, void *O, const int64_t o_stride[3],
+                              void *stream);
+
+/* A5/A6 - sparse decode; one row per (sequence, query head) at position L_b - 1.
+ *   Q, O: [B, Hq, d] (q_stride, o_stride = {batch, head}).
+ *   Gist mode ([SSA] method items 2-3: hybrid attention) when gist_k and gist_v are both
+ *   non-NULL: the key set is the raw tokens of the selected chunks plus the gist token of
+ *   every complete chunk before the current one that is not selected; gist_stride =
+ *   {batch, head, chunk}; the gate must be NULL in gist mode.
+ *   workspace: device scratch of sas_sparse_decode_workspace() bytes for the split-K
+ *   partial results. */
+size_t sas_sparse_decode_workspace(const sas_problem *p, int32_t sel_mode, int32_t kcap,
+                                   int32_t gist);
+sas_status sas_sparse_decode(const sas_problem *p, const void *Q, const int64_t q_stride[2],
+                             const void *K, const void *V, const int64_t kv_stride[3],
+                             const void *gist_k, const void *gist_v, const int64_t gist_stride[3],
+                             int32_t sel_mode, const int32_t *idx, const int32_t *nsel,
+                             const float *gate, int32_t kcap, float scale, void *O,
+                             const int64_t o_stride[2], void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/* Text of the last non-OK status returned on this thread ("" if none). */
+const char *sas_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SAS_H */

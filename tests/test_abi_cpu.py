@@ -1,0 +1,156 @@
+"""The C ABI library loads, exports every declared symbol, and rejects invalid calls on the host.
+
+These tests make no compute call: every call below fails host-side validation, which makes
+no HIP call, so they run on a machine without a GPU.
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from top_block_sparse_gist_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sas.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libsas.so not built")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sas_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = _lib.load()
+    names = _declared()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.EXPORTED)
+
+
+def _problem(batch=2, hq=8, hkv=2, d=128, block=64, dtype=_lib.SAS_BF16, max_len=1000, lens=(1000, 700)):
+    arr = _lib.i32x(lens)
+    p = _lib.Problem(batch, hq, hkv, d, block, dtype, max_len, C.cast(arr, C.POINTER(C.c_int32)))
+    return p, arr
+
+
+FAKE = C.c_void_p(0x10000)   # 16-byte aligned non-NULL; never dereferenced (validation fails first)
+
+
+def _reps(lib, p, **kw):
+    ks = _lib.i64x([8 * 1000 * 128, 1000 * 128, 128])
+    rs = _lib.i64x([2 * 16 * 128, 16 * 128, 128])
+    return lib.sas_block_reps(C.byref(p), kw.get("K", FAKE), ks, kw.get("reps", FAKE), rs, None)
+
+
+def test_reps_validation_codes():
+    lib = _lib.load()
+    p, a = _problem()
+    assert lib.sas_block_reps(None, FAKE, _lib.i64x([1, 1, 1]), FAKE, _lib.i64x([1, 1, 1]), None) == _lib.SAS_ERR_NULL
+    assert _reps(lib, p, K=None) == _lib.SAS_ERR_NULL
+    p2, a2 = _problem(d=96)
+    assert _reps(lib, p2) == _lib.SAS_ERR_UNSUPPORTED
+    p3, a3 = _problem(block=32)
+    assert _reps(lib, p3) == _lib.SAS_ERR_UNSUPPORTED
+    p4, a4 = _problem(hq=6, hkv=4)
+    assert _reps(lib, p4) == _lib.SAS_ERR_SHAPE
+    p5, a5 = _problem(lens=(1001, 5))
+    assert _reps(lib, p5) == _lib.SAS_ERR_SHAPE
+    assert b"seq_lens[0]" in lib.sas_last_error()
+    p6, a6 = _problem(batch=65, lens=[10] * 65)
+    assert _reps(lib, p6) == _lib.SAS_ERR_UNSUPPORTED
+    p7, a7 = _problem(dtype=7)
+    assert _reps(lib, p7) == _lib.SAS_ERR_UNSUPPORTED
+    # misaligned pointer
+    assert _reps(lib, p, K=C.c_void_p(0x10002)) == _lib.SAS_ERR_SHAPE
+
+
+def test_num_qblocks_and_required_kcap():
+    lib = _lib.load()
+    assert lib.sas_num_qblocks(1, 64) == 1
+    assert lib.sas_num_qblocks(64, 64) == 2
+    assert lib.sas_num_qblocks(4096, 64) == 65
+    assert lib.sas_num_qblocks(0, 64) < 0
+    p, a = _problem(lens=(32768, 32768), max_len=32768)
+    b16 = _lib.Budget(16, 0, 0, 0, 0, 0)
+    assert lib.sas_required_kcap(C.byref(p), 1, None, C.byref(b16)) == 17
+    # ceil(c/8) + sink + current over the full prefill of 256 blocks of 128 (c = 255 -> 32 + 2)
+    p1, a1 = _problem(batch=1, hq=28, hkv=4, block=128, lens=(32768,), max_len=32768)
+    b8 = _lib.Budget(0, 1, 8, 0, 1, 1)
+    qs = _lib.i32x([0])
+    assert lib.sas_required_kcap(C.byref(p1), 32768, qs, C.byref(b8)) == 34
+    # 5% of (c+1) + current at c = 2047 -> 103 + 1
+    p2, a2 = _problem(batch=1, lens=(131072,), max_len=131072)
+    b20 = _lib.Budget(0, 1, 20, 1, 0, 1)
+    assert lib.sas_required_kcap(C.byref(p2), 1, None, C.byref(b20)) == 104
+    bad = _lib.Budget(-1, 0, 0, 0, 0, 0)
+    assert lib.sas_required_kcap(C.byref(p2), 1, None, C.byref(bad)) == _lib.SAS_ERR_SHAPE
+
+
+def test_scores_topk_validation_codes():
+    lib = _lib.load()
+    p, a = _problem()
+    qs3 = _lib.i64x([8 * 100 * 128, 100 * 128, 128])
+    rs = _lib.i64x([2 * 16 * 128, 16 * 128, 128])
+    # decode needs tq == 1
+    assert lib.sas_block_scores(C.byref(p), FAKE, qs3, 5, None, FAKE, 0, rs, 0, 0.0, FAKE, 16, None, 0,
+                                None) == _lib.SAS_ERR_SHAPE
+    # rows beyond the sequence
+    qst = _lib.i32x([950, 0])
+    assert lib.sas_block_scores(C.byref(p), FAKE, qs3, 100, qst, FAKE, 0, rs, 0, 0.0, FAKE, 16, FAKE, 1 << 20,
+                                None) == _lib.SAS_ERR_SHAPE
+    # scores_ld too small (needs 16 blocks)
+    assert lib.sas_block_scores(C.byref(p), FAKE, qs3, 1, None, FAKE, 0, rs, 0, 0.0, FAKE, 15, None, 0,
+                                None) == _lib.SAS_ERR_SHAPE
+    # prefill workspace too small
+    qs0 = _lib.i32x([0, 0])
+    assert lib.sas_block_scores(C.byref(p), FAKE, qs3, 100, qs0, FAKE, 0, rs, 0, 0.0, FAKE, 16, FAKE, 16,
+                                None) == _lib.SAS_ERR_WORKSPACE
+    # bad selection mode / negative scale
+    assert lib.sas_block_scores(C.byref(p), FAKE, qs3, 1, None, FAKE, 0, rs, 7, 0.0, FAKE, 16, None, 0,
+                                None) == _lib.SAS_ERR_SHAPE
+    assert lib.sas_block_scores(C.byref(p), FAKE, qs3, 1, None, FAKE, 0, rs, 0, -1.0, FAKE, 16, None, 0,
+                                None) == _lib.SAS_ERR_SHAPE
+    b = _lib.Budget(4, 0, 0, 0, 0, 1)
+    # kcap below the required 5, gate requested without a gate buffer
+    assert lib.sas_topk_select(C.byref(p), FAKE, 16, 1, None, 0, C.byref(b), 4, FAKE, FAKE, FAKE,
+                               None) == _lib.SAS_ERR_SHAPE
+    assert lib.sas_topk_select(C.byref(p), FAKE, 16, 1, None, 0, C.byref(b), 5, FAKE, FAKE, None,
+                               None) == _lib.SAS_ERR_NULL
+    assert lib.sas_topk_select(C.byref(p), FAKE, 16, 1, None, 0, None, 5, FAKE, FAKE, FAKE,
+                               None) == _lib.SAS_ERR_NULL
+
+
+def test_attention_validation_codes():
+    lib = _lib.load()
+    p, a = _problem()
+    qs3 = _lib.i64x([8 * 100 * 128, 100 * 128, 128])
+    kvs = _lib.i64x([2 * 1000 * 128, 1000 * 128, 128])
+    qs2 = _lib.i64x([8 * 128, 128])
+    # prefill without q_start
+    assert lib.sas_sparse_prefill(C.byref(p), FAKE, qs3, FAKE, FAKE, kvs, 100, None, 0, FAKE, FAKE, None, 8, 0.0,
+                                  FAKE, qs3, None) == _lib.SAS_ERR_NULL
+    # odd row stride for bf16 (not a multiple of 8 elements)
+    bad = _lib.i64x([8 * 100 * 128, 100 * 128, 130])
+    qs0 = _lib.i32x([0, 0])
+    assert lib.sas_sparse_prefill(C.byref(p), FAKE, bad, FAKE, FAKE, kvs, 100, qs0, 0, FAKE, FAKE, None, 8, 0.0,
+                                  FAKE, qs3, None) == _lib.SAS_ERR_SHAPE
+    # decode: gist with a gate is not defined; half a gist pair is an error; workspace too small
+    gs = _lib.i64x([2 * 15 * 128, 15 * 128, 128])
+    assert lib.sas_sparse_decode(C.byref(p), FAKE, qs2, FAKE, FAKE, kvs, FAKE, FAKE, gs, 0, FAKE, FAKE, FAKE, 8, 0.0,
+                                 FAKE, qs2, FAKE, 1 << 30, None) == _lib.SAS_ERR_UNSUPPORTED
+    assert lib.sas_sparse_decode(C.byref(p), FAKE, qs2, FAKE, FAKE, kvs, FAKE, None, gs, 0, FAKE, FAKE, None, 8, 0.0,
+                                 FAKE, qs2, FAKE, 1 << 30, None) == _lib.SAS_ERR_NULL
+    need = lib.sas_sparse_decode_workspace(C.byref(p), 0, 8, 0)
+    assert need > 0
+    assert lib.sas_sparse_decode(C.byref(p), FAKE, qs2, FAKE, FAKE, kvs, None, None, None, 0, FAKE, FAKE, None, 8,
+                                 0.0, FAKE, qs2, FAKE, need - 1, None) == _lib.SAS_ERR_WORKSPACE
+    # more than 16 query heads per KV head in per-group decode
+    p9, a9 = _problem(hq=34, hkv=2)
+    need9 = lib.sas_sparse_decode_workspace(C.byref(p9), 0, 8, 0)
+    assert lib.sas_sparse_decode(C.byref(p9), FAKE, qs2, FAKE, FAKE, kvs, None, None, None, 0, FAKE, FAKE, None, 8,
+                                 0.0, FAKE, qs2, FAKE, need9, None) == _lib.SAS_ERR_UNSUPPORTED

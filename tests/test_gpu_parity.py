@@ -1,0 +1,189 @@
+"""GPU parity of the HIP path (through the C ABI binding) against the CPU oracle.
+
+Every case runs reps -> scores -> top-k -> attention on the GPU and compares block
+representatives, scores, block lists (tie rule), gates and outputs with the oracle on
+the same seeded inputs.  Small cases compare every unit; the full-size configurations
+(the shapes the benchmark times) compare a seeded sample of units.
+"""
+import os
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+from workloads import Workload  # noqa: E402
+
+from gpu_harness import run_case, say  # noqa: E402
+import top_block_sparse_gist_amd as sas  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sas.load()
+    yield
+
+
+# ------------------------------------------------------------------------------ the five workloads, small
+def test_c1_tiny_prefill_f32():
+    w = Workload(1)
+    run_case(w, [0])
+
+
+def test_c2_decode_mini():
+    w = Workload(2, mini=True)
+    run_case(w, list(range(w.batch)))
+
+
+def test_c3_prefill_mini():
+    w = Workload(3, mini=True)
+    run_case(w, [0])
+
+
+def test_c4_gist_decode_mini():
+    w = Workload(4, mini=True)
+    run_case(w, list(range(w.batch)))
+
+
+def test_c5_mixed_mini_prefill_half():
+    w = Workload(5, mini=True)
+    run_case(w, w.prefill_seqs())
+
+
+def test_c5_mixed_mini_decode_half():
+    w = Workload(5, mini=True)
+    run_case(w, w.decode_seqs())
+
+
+# ------------------------------------------------------------------------------ edge cases
+def test_decode_ragged_lengths_sink_gate():
+    """L = 1 (only the current block), partial blocks, k larger than the candidates."""
+    w = Workload(2, overrides=dict(tag="ragged", seq_lens=[1, 63, 64, 65, 200, 4097, 777, 3000], k_fixed=3,
+                                   sink=True, gate=True, seq_len=None))
+    run_case(w, list(range(8)))
+
+
+def test_decode_per_head_block128_d64():
+    w = Workload(2, overrides=dict(tag="h128d64", seq_lens=[129, 1000, 4096, 2500], batch=4, block=128, d=64,
+                                   sel="head", k_fixed=2, gate=True, hq=8, hkv=2))
+    run_case(w, list(range(4)))
+
+
+def test_prefill_unaligned_rows_and_partial_blocks():
+    """q_start not on a block boundary, tq not a multiple of the block, per-group G=2."""
+    w = Workload(3, overrides=dict(tag="unaligned", seq_len=1000, tq=300, block=64, hq=4, hkv=2,
+                                   frac_num=1, frac_den=4, sink=True, gate=True))
+    run_case(w, [0])
+
+
+def test_prefill_short_rows_per_head():
+    w = Workload(3, overrides=dict(tag="short", seq_len=520, tq=17, block=64, hq=6, hkv=2, sel="head",
+                                   frac_num=0, frac_den=0, k_fixed=2, sink=False, gate=True))
+    run_case(w, [0])
+
+
+def test_prefill_zero_budget_only_current_and_sink():
+    w = Workload(3, overrides=dict(tag="k0", seq_len=2048, tq=2048, block=128, hq=4, hkv=1,
+                                   frac_num=0, frac_den=0, k_fixed=0, sink=True, gate=True))
+    run_case(w, [0])
+
+
+def test_decode_f32_and_gist_f32():
+    w = Workload(2, overrides=dict(tag="f32", dtype="f32", seq_lens=[100, 1500, 4096, 64], batch=4, k_fixed=3,
+                                   gate=True, hq=8, hkv=2))
+    run_case(w, list(range(4)))
+    wg = Workload(4, overrides=dict(tag="f32", dtype="f32", seq_len=4097, batch=2, k_fixed=5, hq=8, hkv=2))
+    run_case(wg, [0, 1])
+
+
+def test_gist_decode_when_current_chunk_is_complete():
+    """L a multiple of the chunk: the current chunk has a gist, which must not be used."""
+    w = Workload(4, overrides=dict(tag="aligned", seq_len=8192, batch=2, k_fixed=7))
+    run_case(w, [0, 1])
+
+
+def test_decode_equals_last_prefill_row_on_gpu():
+    """Decode at L-1 == the last row of a full prefill when that row is alone in its block."""
+    L = 64 * 9 + 1
+    w = Workload(3, overrides=dict(tag="p9", seq_len=L, tq=L, block=64, hq=4, hkv=2, sel="head", frac_num=0,
+                                   frac_den=0, k_fixed=3, sink=True, gate=True, batch=1))
+    from workloads.device import upload
+    inp = upload(w, [0])
+    dt = sas.SAS_BF16
+    b = sas.Budget(k_fixed=3, sink=True, gate=True)
+    reps = sas.block_reps(inp.K, inp.seq_lens, w.block)
+    # prefill over all rows
+    sc = sas.block_scores(inp.Q, reps, inp.seq_lens, w.block, w.hkv, L, q_start=[0], sel_mode="head")
+    idx, nsel, gate = sas.topk_select(sc, inp.seq_lens, w.block, w.hq, w.hkv, w.d, dt, L, b, tq=L, q_start=[0],
+                                      sel_mode="head")
+    Op = sas.sparse_prefill(inp.Q, inp.K, inp.V, inp.seq_lens, w.block, [0], idx, nsel, gate, sel_mode="head")
+    # decode of the last row
+    Qd = inp.Q[:, :, L - 1, :].contiguous()
+    sd = sas.block_scores(Qd, reps, inp.seq_lens, w.block, w.hkv, L, sel_mode="head")
+    idd, nsd, gd = sas.topk_select(sd, inp.seq_lens, w.block, w.hq, w.hkv, w.d, dt, L, b, sel_mode="head")
+    Od = sas.sparse_decode(Qd, inp.K, inp.V, inp.seq_lens, w.block, idd, nsd, gd, sel_mode="head")
+    torch.cuda.synchronize()
+    a = Op[0, :, L - 1].float().cpu().numpy()
+    d_ = np.abs(a - Od[0].float().cpu().numpy()).max()
+    say(f"[p9] decode vs last prefill row max-abs {d_:.3e}")
+    assert d_ <= 2e-2
+
+
+def test_explicit_block_pattern_prefill_on_gpu():
+    """The printed 4x4 block pattern, given as explicit lists, reaches exactly those key blocks."""
+    B, hq, hkv, d, blk, L = 1, 1, 1, 128, 64, 256
+    g = torch.Generator().manual_seed(0)
+    Q = torch.zeros((B, hq, L, d), dtype=torch.bfloat16)
+    K = torch.zeros((B, hkv, L, d), dtype=torch.bfloat16)
+    # V = one-hot of the key's block in dims 0..3: the output shows the weight on each key block
+    V = torch.zeros((B, hkv, L, d), dtype=torch.bfloat16)
+    for j in range(4):
+        V[0, 0, j * blk:(j + 1) * blk, j] = 1.0
+    lists = {0: [0], 1: [0, 1], 2: [1, 2], 3: [0, 2, 3]}
+    qb = sas.num_qblocks(L, blk)           # unit slots per (sequence, head); the last one is empty
+    idx = torch.full((qb, 4), -1, dtype=torch.int32)
+    nsel = torch.zeros(qb, dtype=torch.int32)
+    for c, sel in lists.items():
+        idx[c, :len(sel)] = torch.tensor(sel, dtype=torch.int32)
+        nsel[c] = len(sel)
+    O = sas.sparse_prefill(Q.cuda(), K.cuda(), V.cuda(), [L], blk, [0], idx.cuda(), nsel.cuda(), None)
+    w = O[0, 0, :, :4].float().cpu().numpy().reshape(4, blk, 4)
+    pattern = (w > 0).any(axis=1).astype(int)
+    golden = np.loadtxt(os.path.join(os.path.dirname(__file__), "golden", "block_sparse_4x4_pattern.txt"),
+                        dtype=int)
+    np.testing.assert_array_equal(pattern, golden)
+
+
+# ------------------------------------------------------------------------------ full sizes, sampled units
+@pytest.mark.timeout(600)
+def test_c2_decode_full_sampled():
+    w = Workload(2)
+    run_case(w, list(range(w.batch)), unit_sample=16, seed=2)
+
+
+@pytest.mark.timeout(600)
+def test_c3_prefill_full_sampled():
+    w = Workload(3)
+    run_case(w, [0], unit_sample=6, seed=3)
+
+
+@pytest.mark.timeout(600)
+def test_c4_gist_decode_full_sampled():
+    w = Workload(4)
+    run_case(w, list(range(w.batch)), unit_sample=8, seed=4)
+
+
+@pytest.mark.timeout(600)
+def test_c5_prefill_half_full_sampled():
+    w = Workload(5)
+    run_case(w, w.prefill_seqs(), unit_sample=24, seed=5)
+
+
+@pytest.mark.timeout(600)
+def test_c5_decode_half_full_sampled():
+    w = Workload(5)
+    run_case(w, w.decode_seqs(), unit_sample=32, seed=6)

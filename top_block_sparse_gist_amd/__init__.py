@@ -1,0 +1,234 @@
+"""Content-selected block-sparse attention on MI355X (gfx950): thin Python binding.
+
+Each function marshals torch tensors (device memory) and the current HIP stream into one
+call of the C ABI in libsas.so (include/sas.h) and returns the outputs.  Every step of
+the computation runs in the library's HIP kernels; when libsas.so is missing the import
+of the first call raises.
+
+Layouts (last dim contiguous):  Q, O [B, Hq, T, d] (decode: [B, Hq, d]);
+K, V [B, Hkv, Lmax, d];  reps [B, Hkv, NBmax, d] fp32;  gist K/V [B, Hkv, NC, d];
+scores [B*S*QB, NBmax] fp32;  idx / gate [B*S*QB, kcap];  nsel [B*S*QB].
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+from typing import Optional, Sequence, Tuple
+
+from . import _lib
+from ._lib import (SAS_BF16, SAS_F32, SAS_REPS_GIST, SAS_REPS_POOLED, SAS_SEL_GROUP, SAS_SEL_HEAD,
+                   SasError, check, i32x, i64x, load)
+
+__all__ = ["Budget", "block_reps", "block_scores", "topk_select", "sparse_prefill", "sparse_decode",
+           "num_qblocks", "required_kcap", "SasError", "load", "sel_code"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+@dataclass
+class Budget:
+    """k = k_fixed, or ceil(frac_num * (c + count_current) / frac_den) when frac_den > 0."""
+    k_fixed: int = 0
+    frac_num: int = 0
+    frac_den: int = 0
+    count_current: int = 0
+    sink: bool = False
+    gate: bool = False
+
+    def c_struct(self) -> _lib.Budget:
+        return _lib.Budget(self.k_fixed, self.frac_num, self.frac_den, self.count_current,
+                           int(bool(self.sink)), int(bool(self.gate)))
+
+
+def sel_code(sel_mode) -> int:
+    if sel_mode in (SAS_SEL_GROUP, "group"):
+        return SAS_SEL_GROUP
+    if sel_mode in (SAS_SEL_HEAD, "head"):
+        return SAS_SEL_HEAD
+    raise ValueError(f"sel_mode {sel_mode!r}")
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return SAS_BF16
+    if t.dtype == torch.float32:
+        return SAS_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+class _Prob:
+    """sas_problem plus the host arrays it points to (kept alive for the call)."""
+
+    def __init__(self, batch, hq, hkv, d, block, dtype, max_len, seq_lens):
+        self.lens = i32x(seq_lens)
+        self.s = _lib.Problem(batch, hq, hkv, d, block, dtype, max_len,
+                              C.cast(self.lens, C.POINTER(C.c_int32)))
+
+    @property
+    def ref(self):
+        return C.byref(self.s)
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return C.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _strides(t, n):
+    return i64x(t.stride()[:n])
+
+
+def _qstart(q_start):
+    if q_start is None:
+        return None
+    return i32x(q_start)
+
+
+def num_qblocks(tq: int, block: int) -> int:
+    return int(load().sas_num_qblocks(tq, block))
+
+
+def required_kcap(batch, hq, hkv, d, block, dtype, max_len, seq_lens, tq, q_start, budget: Budget) -> int:
+    p = _Prob(batch, hq, hkv, d, block, dtype, max_len, seq_lens)
+    qs = _qstart(q_start)
+    bs = budget.c_struct()
+    r = load().sas_required_kcap(p.ref, tq, qs, C.byref(bs))
+    if r < 0:
+        check(r, "sas_required_kcap")
+    return int(r)
+
+
+def block_reps(K, seq_lens: Sequence[int], block: int, hq: Optional[int] = None, reps=None, stream=None):
+    """A1: fp32 mean of every block's keys; K [B, Hkv, Lmax, d] -> reps [B, Hkv, NBmax, d]."""
+    torch = _torch()
+    B, hkv, lmax, d = K.shape
+    nb = max(-(-int(L) // block) for L in seq_lens)
+    if reps is None:
+        reps = torch.empty((B, hkv, nb, d), dtype=torch.float32, device=K.device)
+    p = _Prob(B, hq or hkv, hkv, d, block, _dtype_code(K), lmax, seq_lens)
+    check(load().sas_block_reps(p.ref, _ptr(K), _strides(K, 3), _ptr(reps), _strides(reps, 3), _stream(stream)),
+          "sas_block_reps")
+    return reps
+
+
+def block_scores(Q, reps, seq_lens, block, hkv, max_len, q_start=None, sel_mode="group", gist=False,
+                 scale=0.0, scores=None, workspace=None, stream=None):
+    """A2: scores [B*S*QB, NBmax] fp32 (entries j <= c of each unit row are written).
+
+    Q: [B, Hq, T, d] (prefill, q_start given) or [B, Hq, d] (decode).
+    reps: fp32 pooled reps, or gist keys (gist=True) of Q's dtype.
+    """
+    torch = _torch()
+    decode = q_start is None
+    if decode:
+        B, hq, d = Q.shape
+        tq = 1
+        qs = i64x([Q.stride(0), Q.stride(1), 0])
+    else:
+        B, hq, tq, d = Q.shape
+        qs = _strides(Q, 3)
+    sm = sel_code(sel_mode)
+    S = hq if sm == SAS_SEL_HEAD else hkv
+    nb = max(-(-int(L) // block) for L in seq_lens)
+    QB = 1 if decode else num_qblocks(tq, block)
+    if scores is None:
+        scores = torch.full((B * S * QB, nb), float("-inf"), dtype=torch.float32, device=Q.device)
+    p = _Prob(B, hq, hkv, d, block, _dtype_code(Q), max_len, seq_lens)
+    lib = load()
+    need = lib.sas_block_scores_workspace(p.ref, tq, sm) if not decode else 0
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    check(lib.sas_block_scores(p.ref, _ptr(Q), qs, tq, _qstart(q_start), _ptr(reps),
+                               SAS_REPS_GIST if gist else SAS_REPS_POOLED, _strides(reps, 3), sm, float(scale),
+                               _ptr(scores), scores.stride(0), _ptr(workspace),
+                               workspace.numel() if workspace is not None else 0, _stream(stream)),
+          "sas_block_scores")
+    return scores
+
+
+def topk_select(scores, seq_lens, block, hq, hkv, d, dtype, max_len, budget: Budget, tq=1, q_start=None,
+                sel_mode="group", kcap=None, idx=None, nsel=None, gate=None, stream=None):
+    """A3: (idx [U, kcap] int32 ascending, -1 padded; nsel [U] int32; gate [U, kcap] fp32 or None)."""
+    torch = _torch()
+    sm = sel_code(sel_mode)
+    B = len(seq_lens)
+    p = _Prob(B, hq, hkv, d, block, dtype, max_len, seq_lens)
+    bs = budget.c_struct()
+    lib = load()
+    if kcap is None:
+        kcap = lib.sas_required_kcap(p.ref, tq, _qstart(q_start), C.byref(bs))
+        if kcap < 0:
+            check(kcap, "sas_required_kcap")
+    U = scores.shape[0]
+    if idx is None:
+        idx = torch.empty((U, kcap), dtype=torch.int32, device=scores.device)
+    if nsel is None:
+        nsel = torch.empty((U,), dtype=torch.int32, device=scores.device)
+    if budget.gate and gate is None:
+        gate = torch.empty((U, kcap), dtype=torch.float32, device=scores.device)
+    check(lib.sas_topk_select(p.ref, _ptr(scores), scores.stride(0), tq, _qstart(q_start), sm, C.byref(bs),
+                              kcap, _ptr(idx), _ptr(nsel), _ptr(gate) if budget.gate else None, _stream(stream)),
+          "sas_topk_select")
+    return idx, nsel, (gate if budget.gate else None)
+
+
+def sparse_prefill(Q, K, V, seq_lens, block, q_start, idx, nsel, gate=None, sel_mode="group", scale=0.0,
+                   O=None, stream=None):
+    """A4: O [B, Hq, T, d] = attention of each row over its unit's selected blocks (causal)."""
+    torch = _torch()
+    B, hq, tq, d = Q.shape
+    _, hkv, lmax, _ = K.shape
+    if K.stride() != V.stride():
+        raise ValueError("K and V must share strides")
+    if O is None:
+        O = torch.empty_like(Q)
+    p = _Prob(B, hq, hkv, d, block, _dtype_code(Q), lmax, seq_lens)
+    check(load().sas_sparse_prefill(p.ref, _ptr(Q), _strides(Q, 3), _ptr(K), _ptr(V), _strides(K, 3), tq,
+                                    _qstart(q_start), sel_code(sel_mode), _ptr(idx), _ptr(nsel), _ptr(gate),
+                                    idx.shape[1], float(scale), _ptr(O), _strides(O, 3), _stream(stream)),
+          "sas_sparse_prefill")
+    return O
+
+
+def decode_workspace_bytes(B, hq, hkv, d, block, dtype, max_len, seq_lens, sel_mode, kcap, gist) -> int:
+    p = _Prob(B, hq, hkv, d, block, dtype, max_len, seq_lens)
+    return int(load().sas_sparse_decode_workspace(p.ref, sel_code(sel_mode), kcap, int(bool(gist))))
+
+
+def sparse_decode(Q, K, V, seq_lens, block, idx, nsel, gate=None, sel_mode="group", scale=0.0, gist_k=None,
+                  gist_v=None, O=None, workspace=None, stream=None):
+    """A5/A6: O [B, Hq, d] for the row at position L_b - 1 (gist mode when gist_k/gist_v are given)."""
+    torch = _torch()
+    B, hq, d = Q.shape
+    _, hkv, lmax, _ = K.shape
+    if K.stride() != V.stride():
+        raise ValueError("K and V must share strides")
+    gist = gist_k is not None
+    if gist and gist_k.stride() != gist_v.stride():
+        raise ValueError("gist K and V must share strides")
+    if O is None:
+        O = torch.empty_like(Q)
+    kcap = idx.shape[1]
+    dt = _dtype_code(Q)
+    p = _Prob(B, hq, hkv, d, block, dt, lmax, seq_lens)
+    lib = load()
+    need = lib.sas_sparse_decode_workspace(p.ref, sel_code(sel_mode), kcap, int(gist))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    check(lib.sas_sparse_decode(p.ref, _ptr(Q), _strides(Q, 2), _ptr(K), _ptr(V), _strides(K, 3),
+                                _ptr(gist_k) if gist else None, _ptr(gist_v) if gist else None,
+                                _strides(gist_k, 3) if gist else None, sel_code(sel_mode), _ptr(idx), _ptr(nsel),
+                                _ptr(gate), kcap, float(scale), _ptr(O), _strides(O, 2), _ptr(workspace),
+                                workspace.numel() if workspace is not None else 0, _stream(stream)),
+          "sas_sparse_decode")
+    return O

@@ -1,0 +1,293 @@
+// Host layer of libsas: argument validation (no HIP call), launch configuration, error text.
+// The exported entry points and their contracts are declared and documented in sas.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "common.h"
+
+using namespace sas;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+sas_status fail(sas_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+sas_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return SAS_OK;
+  return fail(SAS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+int elem_bytes(int32_t dtype) { return dtype == SAS_BF16 ? 2 : 4; }
+
+// 16-byte vector loads need every row start 16-byte aligned.
+bool strides_ok(const int64_t *st, int n, int esize) {
+  const int64_t v = 16 / esize;
+  for (int x = 0; x < n; ++x)
+    if (st[x] < 0 || st[x] % v != 0) return false;
+  return true;
+}
+
+sas_status check_problem(const sas_problem *p, SeqTable *tab) {
+  if (!p) return fail(SAS_ERR_NULL, "problem is NULL");
+  if (!p->seq_lens) return fail(SAS_ERR_NULL, "seq_lens is NULL");
+  if (p->batch < 1) return fail(SAS_ERR_SHAPE, "batch must be >= 1 (got %d)", p->batch);
+  if (p->batch > SAS_MAX_BATCH)
+    return fail(SAS_ERR_UNSUPPORTED, "batch %d exceeds SAS_MAX_BATCH (%d) per call", p->batch, SAS_MAX_BATCH);
+  if (p->hq < 1 || p->hkv < 1 || p->hq % p->hkv != 0)
+    return fail(SAS_ERR_SHAPE, "hq (%d) must be a positive multiple of hkv (%d)", p->hq, p->hkv);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(SAS_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128)", p->head_dim);
+  if (p->block != 64 && p->block != 128)
+    return fail(SAS_ERR_UNSUPPORTED, "block %d not supported (64, 128)", p->block);
+  if (p->dtype != SAS_F32 && p->dtype != SAS_BF16) return fail(SAS_ERR_UNSUPPORTED, "dtype %d", p->dtype);
+  if (p->max_len < 1) return fail(SAS_ERR_SHAPE, "max_len must be >= 1");
+  for (int b = 0; b < p->batch; ++b) {
+    const int L = p->seq_lens[b];
+    if (L < 1 || L > p->max_len)
+      return fail(SAS_ERR_SHAPE, "seq_lens[%d] = %d outside [1, max_len = %d]", b, L, p->max_len);
+    if (tab) {
+      tab->len[b] = L;
+      tab->q0[b] = L - 1;
+    }
+  }
+  return SAS_OK;
+}
+
+// Prefill rows: q_start (host) gives the first row position, rows [q0, q0 + tq) within [0, L).
+sas_status check_rows(const sas_problem *p, int32_t tq, const int32_t *q_start, SeqTable *tab) {
+  if (tq < 1) return fail(SAS_ERR_SHAPE, "tq must be >= 1 (got %d)", tq);
+  if (!q_start) {
+    if (tq != 1) return fail(SAS_ERR_SHAPE, "decode (q_start == NULL) needs tq == 1 (got %d)", tq);
+    return SAS_OK;
+  }
+  for (int b = 0; b < p->batch; ++b) {
+    const int q0 = q_start[b];
+    if (q0 < 0 || (int64_t)q0 + tq > p->seq_lens[b])
+      return fail(SAS_ERR_SHAPE, "rows [%d, %d) of sequence %d exceed its length %d", q0, q0 + tq, b,
+                  p->seq_lens[b]);
+    if (tab) tab->q0[b] = q0;
+  }
+  return SAS_OK;
+}
+
+sas_status check_sel(int32_t sel_mode) {
+  if (sel_mode != SAS_SEL_GROUP && sel_mode != SAS_SEL_HEAD)
+    return fail(SAS_ERR_SHAPE, "sel_mode %d is neither SAS_SEL_GROUP nor SAS_SEL_HEAD", sel_mode);
+  return SAS_OK;
+}
+
+sas_status check_budget(const sas_budget *bg) {
+  if (!bg) return fail(SAS_ERR_NULL, "budget is NULL");
+  if (bg->k_fixed < 0 || bg->frac_num < 0 || bg->frac_den < 0)
+    return fail(SAS_ERR_SHAPE, "budget fields must be >= 0");
+  if (bg->count_current != 0 && bg->count_current != 1)
+    return fail(SAS_ERR_SHAPE, "count_current must be 0 or 1");
+  return SAS_OK;
+}
+
+float resolve_scale(float scale, int d) { return scale == 0.f ? 1.f / sqrtf((float)d) : scale; }
+
+int32_t required_kcap(const sas_problem *p, int32_t tq, const int32_t *q_start, const sas_budget *bg) {
+  Budget b{bg->k_fixed, bg->frac_num, bg->frac_den, bg->count_current, bg->force_sink ? 1 : 0, bg->gate};
+  int32_t need = 1;
+  for (int s = 0; s < p->batch; ++s) {
+    const int L = p->seq_lens[s];
+    const int lo_pos = q_start ? q_start[s] : L - 1;
+    const int hi_pos = q_start ? q_start[s] + tq - 1 : L - 1;
+    for (int c = lo_pos / p->block; c <= hi_pos / p->block; ++c) {
+      const bool sink = b.sink && c > 0;
+      const int ncand = c - (sink ? 1 : 0);
+      const int n = budget_k(b, c, ncand) + 1 + (sink ? 1 : 0);
+      need = std::max(need, n);
+    }
+  }
+  return need;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *sas_last_error(void) { return g_err; }
+
+int32_t sas_num_qblocks(int32_t tq, int32_t block) {
+  if (tq < 1 || block < 1) return (int32_t)fail(SAS_ERR_SHAPE, "tq and block must be >= 1");
+  return num_qblocks(tq, block);
+}
+
+int32_t sas_required_kcap(const sas_problem *p, int32_t tq, const int32_t *q_start, const sas_budget *budget) {
+  sas_status st;
+  if ((st = check_problem(p, nullptr)) != SAS_OK) return st;
+  if ((st = check_rows(p, tq, q_start, nullptr)) != SAS_OK) return st;
+  if ((st = check_budget(budget)) != SAS_OK) return st;
+  return required_kcap(p, tq, q_start, budget);
+}
+
+sas_status sas_block_reps(const sas_problem *p, const void *K, const int64_t k_stride[3], float *reps,
+                          const int64_t rep_stride[3], void *stream) {
+  SeqTable tab{};
+  sas_status st;
+  if ((st = check_problem(p, &tab)) != SAS_OK) return st;
+  if (!K || !reps || !k_stride || !rep_stride) return fail(SAS_ERR_NULL, "K, reps or a stride array is NULL");
+  if (!aligned16(K) || !aligned16(reps) || !strides_ok(k_stride, 3, elem_bytes(p->dtype)) ||
+      !strides_ok(rep_stride, 3, 4))
+    return fail(SAS_ERR_SHAPE, "K / reps must be 16-byte aligned with 16-byte-multiple row strides");
+  return hip_status(launch_reps(*p, tab, K, k_stride, reps, rep_stride, (hipStream_t)stream), "sas_block_reps");
+}
+
+size_t sas_block_scores_workspace(const sas_problem *p, int32_t tq, int32_t sel_mode) {
+  if (!p || tq <= 1) return 0;
+  const int S = sel_mode == SAS_SEL_HEAD ? p->hq : p->hkv;
+  return (size_t)p->batch * S * num_qblocks(tq, p->block) * p->head_dim * sizeof(float);
+}
+
+sas_status sas_block_scores(const sas_problem *p, const void *Q, const int64_t q_stride[3], int32_t tq,
+                            const int32_t *q_start, const void *reps, int32_t reps_kind,
+                            const int64_t rep_stride[3], int32_t sel_mode, float scale, float *scores,
+                            int64_t scores_ld, void *workspace, size_t workspace_bytes, void *stream) {
+  SeqTable tab{};
+  sas_status st;
+  if ((st = check_problem(p, &tab)) != SAS_OK) return st;
+  if ((st = check_rows(p, tq, q_start, &tab)) != SAS_OK) return st;
+  if ((st = check_sel(sel_mode)) != SAS_OK) return st;
+  if (!Q || !q_stride || !reps || !rep_stride || !scores) return fail(SAS_ERR_NULL, "a required pointer is NULL");
+  if (reps_kind != SAS_REPS_POOLED && reps_kind != SAS_REPS_GIST)
+    return fail(SAS_ERR_SHAPE, "reps_kind %d", reps_kind);
+  if (scale < 0.f || !isfinite(scale)) return fail(SAS_ERR_SHAPE, "scale must be finite and >= 0");
+  const int rep_bytes = reps_kind == SAS_REPS_GIST ? elem_bytes(p->dtype) : 4;
+  if (!aligned16(Q) || !aligned16(reps) || !strides_ok(q_stride, 3, elem_bytes(p->dtype)) ||
+      !strides_ok(rep_stride, 3, rep_bytes))
+    return fail(SAS_ERR_SHAPE, "Q / reps must be 16-byte aligned with 16-byte-multiple row strides");
+  int nbmax = 0;
+  for (int b = 0; b < p->batch; ++b) nbmax = std::max(nbmax, cdiv(p->seq_lens[b], p->block));
+  if (scores_ld < nbmax) return fail(SAS_ERR_SHAPE, "scores_ld %lld < %d blocks", (long long)scores_ld, nbmax);
+  const float sc = resolve_scale(scale, p->head_dim);
+  const hipStream_t s = (hipStream_t)stream;
+  if (!q_start)
+    return hip_status(launch_scores_decode(*p, tab, Q, q_stride, reps, reps_kind, rep_stride, sel_mode, sc, scores,
+                                           scores_ld, s),
+                      "sas_block_scores");
+  const size_t need = sas_block_scores_workspace(p, tq, sel_mode);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(SAS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  if (need > 0 && !aligned16(workspace)) return fail(SAS_ERR_SHAPE, "workspace must be 16-byte aligned");
+  float *qbar = (float *)workspace;
+  hipError_t e = launch_pool_queries(*p, tab, Q, q_stride, tq, sel_mode, qbar, s);
+  if (e != hipSuccess) return hip_status(e, "sas_block_scores (pool)");
+  return hip_status(launch_scores_prefill(*p, tab, qbar, tq, reps, reps_kind, rep_stride, sel_mode, sc, scores,
+                                          scores_ld, s),
+                    "sas_block_scores");
+}
+
+sas_status sas_topk_select(const sas_problem *p, const float *scores, int64_t scores_ld, int32_t tq,
+                           const int32_t *q_start, int32_t sel_mode, const sas_budget *budget, int32_t kcap,
+                           int32_t *idx, int32_t *nsel, float *gate, void *stream) {
+  SeqTable tab{};
+  sas_status st;
+  if ((st = check_problem(p, &tab)) != SAS_OK) return st;
+  if ((st = check_rows(p, tq, q_start, &tab)) != SAS_OK) return st;
+  if ((st = check_sel(sel_mode)) != SAS_OK) return st;
+  if ((st = check_budget(budget)) != SAS_OK) return st;
+  if (!scores || !idx || !nsel) return fail(SAS_ERR_NULL, "scores, idx or nsel is NULL");
+  if (budget->gate && !gate) return fail(SAS_ERR_NULL, "budget->gate is set but gate is NULL");
+  int nbmax = 0;
+  for (int b = 0; b < p->batch; ++b) nbmax = std::max(nbmax, cdiv(p->seq_lens[b], p->block));
+  if (scores_ld < nbmax) return fail(SAS_ERR_SHAPE, "scores_ld %lld < %d blocks", (long long)scores_ld, nbmax);
+  const int32_t need = required_kcap(p, tq, q_start, budget);
+  if (kcap < need) return fail(SAS_ERR_SHAPE, "kcap %d < %d selected blocks", kcap, need);
+  Budget bg{budget->k_fixed, budget->frac_num, budget->frac_den, budget->count_current,
+            budget->force_sink ? 1 : 0, budget->gate ? 1 : 0};
+  return hip_status(launch_topk(*p, tab, scores, scores_ld, tq, sel_mode, bg, kcap, idx, nsel,
+                                budget->gate ? gate : nullptr, (hipStream_t)stream),
+                    "sas_topk_select");
+}
+
+sas_status sas_sparse_prefill(const sas_problem *p, const void *Q, const int64_t q_stride[3], const void *K,
+                              const void *V, const int64_t kv_stride[3], int32_t tq, const int32_t *q_start,
+                              int32_t sel_mode, const int32_t *idx, const int32_t *nsel, const float *gate,
+                              int32_t kcap, float scale, void *O, const int64_t o_stride[3], void *stream) {
+  SeqTable tab{};
+  sas_status st;
+  if ((st = check_problem(p, &tab)) != SAS_OK) return st;
+  if (!q_start) return fail(SAS_ERR_NULL, "q_start is NULL (prefill needs the first row position)");
+  if ((st = check_rows(p, tq, q_start, &tab)) != SAS_OK) return st;
+  if ((st = check_sel(sel_mode)) != SAS_OK) return st;
+  if (!Q || !q_stride || !K || !V || !kv_stride || !idx || !nsel || !O || !o_stride)
+    return fail(SAS_ERR_NULL, "a required pointer is NULL");
+  if (kcap < 1) return fail(SAS_ERR_SHAPE, "kcap must be >= 1");
+  if (scale < 0.f || !isfinite(scale)) return fail(SAS_ERR_SHAPE, "scale must be finite and >= 0");
+  const int eb = elem_bytes(p->dtype);
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !strides_ok(q_stride, 3, eb) ||
+      !strides_ok(kv_stride, 3, eb) || !strides_ok(o_stride, 3, eb))
+    return fail(SAS_ERR_SHAPE, "Q/K/V/O must be 16-byte aligned with 16-byte-multiple row strides");
+  const float sc = resolve_scale(scale, p->head_dim);
+  const hipStream_t s = (hipStream_t)stream;
+  if (p->dtype == SAS_BF16)
+    return hip_status(launch_prefill_bf16(*p, tab, Q, q_stride, K, V, kv_stride, tq, sel_mode, idx, nsel, gate, kcap,
+                                          sc, O, o_stride, s),
+                      "sas_sparse_prefill");
+  return hip_status(launch_attend_f32(*p, tab, Q, q_stride, K, V, kv_stride, nullptr, nullptr, nullptr, tq, sel_mode,
+                                      idx, nsel, gate, kcap, sc, O, o_stride, s),
+                    "sas_sparse_prefill");
+}
+
+size_t sas_sparse_decode_workspace(const sas_problem *p, int32_t sel_mode, int32_t kcap, int32_t gist) {
+  if (!p || kcap < 1 || p->dtype != SAS_BF16 || p->block < 64 || p->max_len < 1) return 0;
+  return decode_workspace_bytes(*p, sel_mode, kcap, gist);
+}
+
+sas_status sas_sparse_decode(const sas_problem *p, const void *Q, const int64_t q_stride[2], const void *K,
+                             const void *V, const int64_t kv_stride[3], const void *gist_k, const void *gist_v,
+                             const int64_t gist_stride[3], int32_t sel_mode, const int32_t *idx,
+                             const int32_t *nsel, const float *gate, int32_t kcap, float scale, void *O,
+                             const int64_t o_stride[2], void *workspace, size_t workspace_bytes, void *stream) {
+  SeqTable tab{};
+  sas_status st;
+  if ((st = check_problem(p, &tab)) != SAS_OK) return st;
+  if ((st = check_sel(sel_mode)) != SAS_OK) return st;
+  if (!Q || !q_stride || !K || !V || !kv_stride || !idx || !nsel || !O || !o_stride)
+    return fail(SAS_ERR_NULL, "a required pointer is NULL");
+  const bool gist = gist_k != nullptr || gist_v != nullptr;
+  if (gist && (!gist_k || !gist_v || !gist_stride)) return fail(SAS_ERR_NULL, "gist mode needs gist_k, gist_v and gist_stride");
+  if (gist && gate) return fail(SAS_ERR_UNSUPPORTED, "the log-gate is not defined for gist tokens");
+  if (kcap < 1) return fail(SAS_ERR_SHAPE, "kcap must be >= 1");
+  if (scale < 0.f || !isfinite(scale)) return fail(SAS_ERR_SHAPE, "scale must be finite and >= 0");
+  const int eb = elem_bytes(p->dtype);
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !strides_ok(q_stride, 2, eb) ||
+      !strides_ok(kv_stride, 3, eb) || !strides_ok(o_stride, 2, eb) ||
+      (gist && (!aligned16(gist_k) || !aligned16(gist_v) || !strides_ok(gist_stride, 3, eb))))
+    return fail(SAS_ERR_SHAPE, "Q/K/V/O/gist must be 16-byte aligned with 16-byte-multiple row strides");
+  const float sc = resolve_scale(scale, p->head_dim);
+  const hipStream_t s = (hipStream_t)stream;
+  if (p->dtype == SAS_F32) {
+    const int64_t qs3[3] = {q_stride[0], q_stride[1], 0};
+    const int64_t os3[3] = {o_stride[0], o_stride[1], 0};
+    return hip_status(launch_attend_f32(*p, tab, Q, qs3, K, V, kv_stride, gist_k, gist_v, gist_stride, 1, sel_mode,
+                                        idx, nsel, gate, kcap, sc, O, os3, s),
+                      "sas_sparse_decode");
+  }
+  if (sel_mode == SAS_SEL_GROUP && p->hq / p->hkv > 16)
+    return fail(SAS_ERR_UNSUPPORTED, "per-group decode supports at most 16 query heads per KV head");
+  const size_t need = decode_workspace_bytes(*p, sel_mode, kcap, gist ? 1 : 0);
+  if (!workspace || workspace_bytes < need)
+    return fail(SAS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  if (!aligned16(workspace)) return fail(SAS_ERR_SHAPE, "workspace must be 16-byte aligned");
+  return hip_status(launch_decode_bf16(*p, tab, Q, q_stride, K, V, kv_stride, gist_k, gist_v, gist_stride, sel_mode,
+                                       idx, nsel, gate, kcap, sc, O, o_stride, (float *)workspace, s),
+                    "sas_sparse_decode");
+}
+
+}  // extern "C"

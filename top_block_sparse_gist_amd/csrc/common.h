@@ -1,0 +1,137 @@
+// Internal definitions shared by the HIP kernels and the host layer of libsas.
+// gfx950 (CDNA4) only: wave64, MFMA bf16 16x16x32 / 32x32x16, 160 KiB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/sas.h"
+
+namespace sas {
+
+// Per-call sequence table, passed by value as a kernel argument (no device upload).
+struct SeqTable {
+  int32_t len[SAS_MAX_BATCH];  // L_b
+  int32_t q0[SAS_MAX_BATCH];   // position of the first query row (decode: L_b - 1)
+};
+
+struct Budget {
+  int32_t k_fixed, frac_num, frac_den, count_current, sink, gate;
+};
+
+// ---------------------------------------------------------------------------------------
+// host + device helpers
+// ---------------------------------------------------------------------------------------
+__host__ __device__ inline int32_t cdiv(int32_t a, int32_t b) { return (a + b - 1) / b; }
+
+// ceil((tq-1)/blk) + 1: blocks that tq consecutive positions can touch.
+__host__ __device__ inline int32_t num_qblocks(int32_t tq, int32_t blk) {
+  return tq <= 1 ? 1 : cdiv(tq - 1, blk) + 1;
+}
+
+// Number of top-k blocks for a unit with current block c and n_cand candidates.
+__host__ __device__ inline int32_t budget_k(const Budget &bg, int32_t c, int32_t n_cand) {
+  int32_t k;
+  if (bg.frac_den == 0) {
+    k = bg.k_fixed;
+  } else {
+    int64_t num = (int64_t)bg.frac_num * (int64_t)(c + bg.count_current);
+    k = (int32_t)((num + bg.frac_den - 1) / bg.frac_den);
+  }
+  if (k > n_cand) k = n_cand;
+  if (k < 0) k = 0;
+  return k;
+}
+
+// ---------------------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// fp32 -> bf16 round-to-nearest-even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Order-preserving map of fp32 to uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t float_order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace sas
+
+// ---------------------------------------------------------------------------------------
+// launchers (defined in the kernel files, called by the host layer)
+// ---------------------------------------------------------------------------------------
+namespace sas {
+
+hipError_t launch_reps(const sas_problem &p, const SeqTable &st, const void *K, const int64_t *ks,
+                       float *reps, const int64_t *rs, hipStream_t s);
+
+hipError_t launch_pool_queries(const sas_problem &p, const SeqTable &st, const void *Q,
+                               const int64_t *qs, int32_t tq, int32_t sel_mode, float *qbar,
+                               hipStream_t s);
+
+hipError_t launch_scores_prefill(const sas_problem &p, const SeqTable &st, const float *qbar,
+                                 int32_t tq, const void *reps, int32_t reps_kind, const int64_t *rs,
+                                 int32_t sel_mode, float scale, float *scores, int64_t ld,
+                                 hipStream_t s);
+
+hipError_t launch_scores_decode(const sas_problem &p, const SeqTable &st, const void *Q,
+                                const int64_t *qs, const void *reps, int32_t reps_kind,
+                                const int64_t *rs, int32_t sel_mode, float scale, float *scores,
+                                int64_t ld, hipStream_t s);
+
+hipError_t launch_topk(const sas_problem &p, const SeqTable &st, const float *scores, int64_t ld,
+                       int32_t tq, int32_t sel_mode, const Budget &bg, int32_t kcap, int32_t *idx,
+                       int32_t *nsel, float *gate, hipStream_t s);
+
+hipError_t launch_prefill_bf16(const sas_problem &p, const SeqTable &st, const void *Q, const int64_t *qs,
+                               const void *K, const void *V, const int64_t *kvs, int32_t tq,
+                               int32_t sel_mode, const int32_t *idx, const int32_t *nsel,
+                               const float *gate, int32_t kcap, float scale, void *O, const int64_t *os,
+                               hipStream_t s);
+
+hipError_t launch_decode_bf16(const sas_problem &p, const SeqTable &st, const void *Q, const int64_t *qs,
+                              const void *K, const void *V, const int64_t *kvs, const void *gk,
+                              const void *gv, const int64_t *gs, int32_t sel_mode, const int32_t *idx,
+                              const int32_t *nsel, const float *gate, int32_t kcap, float scale, void *O,
+                              const int64_t *os, float *work, hipStream_t s);
+
+hipError_t launch_attend_f32(const sas_problem &p, const SeqTable &st, const void *Q, const int64_t *qs,
+                             const void *K, const void *V, const int64_t *kvs, const void *gk, const void *gv,
+                             const int64_t *gs, int32_t tq, int32_t sel_mode, const int32_t *idx,
+                             const int32_t *nsel, const float *gate, int32_t kcap, float scale, void *O,
+                             const int64_t *os, hipStream_t s);
+
+// Bytes of split-K partials the decode path needs (host formula shared with the size query).
+size_t decode_workspace_bytes(const sas_problem &p, int32_t sel_mode, int32_t kcap, int32_t gist);
+
+}  // namespace sas

@@ -1,0 +1,287 @@
+// A4: sparse causal prefill over the gathered block list (bf16 inputs, fp32 accumulation).
+// Page "稀疏注意力" sections 2, 4.5 and 7 (masked softmax attention; block-sparse so that
+// matrix units see dense tiles; block-sparse FlashAttention: exact tiled attention that
+// never stores the n x n matrix); page "SAS: 通过端到端优化上下文排序的简单注意力稀疏化",
+// method (the selector score enters the logits in log form).
+//
+// A workgroup owns NW*32 query rows of one selection unit (rows x heads of the unit,
+// flattened) and walks the unit's selected blocks in 64-key tiles:
+//   K and V tiles go HBM -> registers -> LDS; the next tile's loads are issued before the
+//   current tile is computed (register double buffering), so HBM latency overlaps MFMA work.
+//   S^T = K Q^T : v_mfma_f32_32x32x16_bf16, M = 32 keys, N = 32 query rows of the wave,
+//                 K = 16 dims; Q^T stays in registers for the whole walk.
+//   online softmax per query column (exp2 domain): the column's 64 logits sit in 32 VGPRs of
+//                 the lane and 32 of the lane 32 apart, so the row max is one cross-half swap.
+//   O^T += V^T P^T : same MFMA, M = 32 dims, K = 16 keys; P^T is taken straight from the
+//                 S^T accumulator (keys in accumulator order), V^T is gathered from the LDS
+//                 tile in that same key order.
+// Only the current block needs the causal mask.  Workgroups are numbered heavy-first (later
+// query blocks select more blocks) and packed per XCD so that the workgroups of one unit,
+// which share its K/V tiles, land on the same XCD's L2.
+#include "common.h"
+
+namespace sas {
+
+static constexpr int KPAD = 8;  // LDS row padding (bf16 elements)
+
+__device__ __forceinline__ bf16x8 as_bf16x8p(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(
+    SeqTable st, const uint16_t *__restrict__ Q, int64_t qb, int64_t qh, int64_t qt,
+    const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, int64_t kb, int64_t kh, int64_t kt,
+    int tq, int blk, int S, int QB, int G, int per_head, int batch, int rtiles,
+    const int32_t *__restrict__ idx, const int32_t *__restrict__ nsel, const float *__restrict__ gate,
+    int kcap, float scale_log2, uint16_t *__restrict__ O, int64_t ob, int64_t oh, int64_t ot) {
+  constexpr int NT = NW * 64;
+  constexpr int ROW = D + KPAD;
+  constexpr int NKK = D / 16;        // k-steps of S^T over the head dim
+  constexpr int NDT = D / 32;        // 32-dim output tiles
+  constexpr int CH = D / 8;          // 16-byte chunks per K/V row
+  constexpr int LOADS = 64 * CH / NT;  // per lane, for each of K and V
+  static_assert((64 * CH) % NT == 0, "tile loads must divide evenly");
+  __shared__ __attribute__((aligned(16))) uint16_t klds[64 * ROW];
+  __shared__ __attribute__((aligned(16))) uint16_t vlds[64 * ROW];
+
+  // ---- workgroup -> (query block i (heavy first), sequence, selector head, row tile)
+  const int nwg = gridDim.x;
+  int logical;
+  {
+    const int k = blockIdx.x, x = k & 7, q = k >> 3;
+    int r = nwg & 7, per = nwg >> 3;
+    if (r == 0) { r = 8; per -= 1; }
+    // XCD x holds per + (x < r) consecutive logical workgroups
+    logical = x * per + min(x, r) + q;
+  }
+  const int rt = logical % rtiles;
+  int rest = logical / rtiles;
+  const int s = rest % S;
+  rest /= S;
+  const int b = rest % batch;
+  const int i = QB - 1 - rest / batch;
+
+  const int L = st.len[b];
+  const int q0 = st.q0[b];
+  const int c0 = q0 / blk;
+  const int c = c0 + i;
+  const int t_lo = max(0, c * blk - q0);
+  const int t_hi = min(tq, (c + 1) * blk - q0);
+  if (t_lo >= t_hi) return;
+  const int rows = t_hi - t_lo;
+  const int nh = per_head ? 1 : G;
+  const int h0 = per_head ? s : s * G;
+  const int g = per_head ? s / G : s;
+  const int R = rows * nh;
+  const int r0 = rt * NW * 32;
+  if (r0 >= R) return;
+  const int64_t u = ((int64_t)b * S + s) * QB + i;
+  const int ns = nsel[u];
+  const int tpb = blk / 64;
+  const int ntiles = ns * tpb;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 31, half = lane >> 5;
+
+  // ---- this lane's query row (column of S^T)
+  const int rq = r0 + wave * 32 + col;
+  const bool qvalid = rq < R;
+  const int qh_idx = h0 + (qvalid ? rq / rows : 0);
+  const int qt_idx = t_lo + (qvalid ? rq % rows : 0);
+  const int qpos = q0 + qt_idx;
+  bf16x8 qreg[NKK];
+  {
+    const uint16_t *qp = Q + b * qb + (int64_t)qh_idx * qh + (int64_t)qt_idx * qt + 8 * half;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (qvalid) v = *reinterpret_cast<const u32x4 *>(qp + 16 * kk);
+      qreg[kk] = as_bf16x8p(v);
+    }
+  }
+
+  const uint16_t *kbase = K + b * kb + g * kh;
+  const uint16_t *vbase = V + b * kb + g * kh;
+  const int32_t *ulist = idx + u * kcap;
+  const float *glist = gate ? gate + u * kcap : nullptr;
+
+  u32x4 kst[LOADS], vst[LOADS];
+  auto load_tile = [&](int t) {
+    const int j = ulist[t / tpb];
+    const int key0 = j * blk + (t % tpb) * 64;
+#pragma unroll
+    for (int x = 0; x < LOADS; ++x) {
+      const int e = x * NT + tid;
+      const int key = e / CH, ch = e % CH;
+      const int pos = key0 + key;
+      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      if (pos < L) {
+        kv = *reinterpret_cast<const u32x4 *>(kbase + (int64_t)pos * kt + ch * 8);
+        vv = *reinterpret_cast<const u32x4 *>(vbase + (int64_t)pos * kt + ch * 8);
+      }
+      kst[x] = kv;
+      vst[x] = vv;
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int x = 0; x < LOADS; ++x) {
+      const int e = x * NT + tid;
+      const int key = e / CH, ch = e % CH;
+      *reinterpret_cast<u32x4 *>(klds + key * ROW + ch * 8) = kst[x];
+      *reinterpret_cast<u32x4 *>(vlds + key * ROW + ch * 8) = vst[x];
+    }
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 acc_o[NDT];
+#pragma unroll
+  for (int x = 0; x < NDT; ++x)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc_o[x][r] = 0.f;
+
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile();
+  }
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles) load_tile(t + 1);
+    const int j = ulist[t / tpb];
+    const int key0 = j * blk + (t % tpb) * 64;
+    const float gl2 = glist ? glist[t / tpb] * 1.4426950408889634f : 0.f;
+    // ---- S^T = K Q^T (two 32-key halves)
+    f32x16 sacc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      f32x16 a;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) a[r] = 0.f;
+      const uint16_t *kr = klds + (mt * 32 + col) * ROW + 8 * half;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        u32x4 kv = *reinterpret_cast<const u32x4 *>(kr + 16 * kk);
+        a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8p(kv), qreg[kk], a, 0, 0, 0);
+      }
+      sacc[mt] = a;
+    }
+    // ---- scale, gate, causal mask (current block only), online softmax
+    const bool diag = (j == c);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        float v = sacc[mt][r] * scale_log2 + gl2;
+        if (diag && key0 + key > qpos) v = -INFINITY;
+        sacc[mt][r] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float mref = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - mref);
+    m_run = m_new;
+    float ls = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = __builtin_amdgcn_exp2f(sacc[mt][r] - mref);
+        sacc[mt][r] = p;
+        ls += p;
+      }
+    l_run = l_run * alpha + ls;
+#pragma unroll
+    for (int x = 0; x < NDT; ++x)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc_o[x][r] *= alpha;
+    // ---- P^T operands: 16-key step ks uses accumulator registers 8*(ks&1) .. +7 of half ks>>1
+    bf16x8 preg[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int mt = ks >> 1, r0p = 8 * (ks & 1);
+      u32x4 w;
+      w[0] = pack_bf16x2(sacc[mt][r0p + 0], sacc[mt][r0p + 1]);
+      w[1] = pack_bf16x2(sacc[mt][r0p + 2], sacc[mt][r0p + 3]);
+      w[2] = pack_bf16x2(sacc[mt][r0p + 4], sacc[mt][r0p + 5]);
+      w[3] = pack_bf16x2(sacc[mt][r0p + 6], sacc[mt][r0p + 7]);
+      preg[ks] = as_bf16x8p(w);
+    }
+    // ---- O^T += V^T P^T; step ks holds keys 16ks + 4half + {0..3} and 16ks + 8 + 4half + {0..3}
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int dim = dt * 32 + col;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int k0 = 16 * ks + 4 * half;
+        const uint16_t *vp = vlds + k0 * ROW + dim;
+        u32x4 w;
+        w[0] = (uint32_t)vp[0 * ROW] | ((uint32_t)vp[1 * ROW] << 16);
+        w[1] = (uint32_t)vp[2 * ROW] | ((uint32_t)vp[3 * ROW] << 16);
+        w[2] = (uint32_t)vp[8 * ROW] | ((uint32_t)vp[9 * ROW] << 16);
+        w[3] = (uint32_t)vp[10 * ROW] | ((uint32_t)vp[11 * ROW] << 16);
+        acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8p(w), preg[ks], acc_o[dt], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+    if (t + 1 < ntiles) {
+      store_tile();
+      __syncthreads();
+    }
+  }
+  // ---- normalise and write O (lane holds dims 32dt + 8(r/4) + 4half + r%4 of its query)
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (!qvalid) return;
+  const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
+  uint16_t *op = O + b * ob + (int64_t)qh_idx * oh + (int64_t)qt_idx * ot;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int dim = dt * 32 + 8 * rb + 4 * half;
+      u32x2 w;
+      w[0] = pack_bf16x2(acc_o[dt][4 * rb + 0] * inv, acc_o[dt][4 * rb + 1] * inv);
+      w[1] = pack_bf16x2(acc_o[dt][4 * rb + 2] * inv, acc_o[dt][4 * rb + 3] * inv);
+      *reinterpret_cast<u32x2 *>(op + dim) = w;
+    }
+}
+
+template <int D, int NW>
+static hipError_t prefill_dispatch(const sas_problem &p, const SeqTable &st, const void *Q, const int64_t *qs,
+                                   const void *K, const void *V, const int64_t *kvs, int32_t tq,
+                                   int32_t sel_mode, const int32_t *idx, const int32_t *nsel,
+                                   const float *gate, int32_t kcap, float scale, void *O, const int64_t *os,
+                                   hipStream_t s) {
+  const int per_head = sel_mode == SAS_SEL_HEAD;
+  const int S = per_head ? p.hq : p.hkv;
+  const int G = p.hq / p.hkv;
+  const int QB = num_qblocks(tq, p.block);
+  const int nh = per_head ? 1 : G;
+  const int rows_max = min(tq, p.block);
+  const int rtiles = cdiv(rows_max * nh, NW * 32);
+  const int64_t nwg = (int64_t)QB * p.batch * S * rtiles;
+  const float scale_log2 = scale * 1.4426950408889634f;
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, NW>), dim3((unsigned)nwg), dim3(NW * 64), 0, s, st,
+                     (const uint16_t *)Q, qs[0], qs[1], qs[2], (const uint16_t *)K, (const uint16_t *)V, kvs[0],
+                     kvs[1], kvs[2], tq, p.block, S, QB, G, per_head, p.batch, rtiles, idx, nsel, gate, kcap,
+                     scale_log2, (uint16_t *)O, os[0], os[1], os[2]);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_bf16(const sas_problem &p, const SeqTable &st, const void *Q, const int64_t *qs,
+                               const void *K, const void *V, const int64_t *kvs, int32_t tq,
+                               int32_t sel_mode, const int32_t *idx, const int32_t *nsel,
+                               const float *gate, int32_t kcap, float scale, void *O, const int64_t *os,
+                               hipStream_t s) {
+  // rows per unit: blk (x G when the group shares one list); 2 waves cover a 64-row unit
+  const int nh = sel_mode == SAS_SEL_HEAD ? 1 : p.hq / p.hkv;
+  const bool small = std::min(tq, p.block) * nh <= 64;
+  if (p.head_dim == 128)
+    return small ? prefill_dispatch<128, 2>(p, st, Q, qs, K, V, kvs, tq, sel_mode, idx, nsel, gate, kcap, scale, O, os, s)
+                 : prefill_dispatch<128, 4>(p, st, Q, qs, K, V, kvs, tq, sel_mode, idx, nsel, gate, kcap, scale, O, os, s);
+  return small ? prefill_dispatch<64, 2>(p, st, Q, qs, K, V, kvs, tq, sel_mode, idx, nsel, gate, kcap, scale, O, os, s)
+               : prefill_dispatch<64, 4>(p, st, Q, qs, K, V, kvs, tq, sel_mode, idx, nsel, gate, kcap, scale, O, os, s);
+}
+
+}  // namespace sas

@@ -1,0 +1,191 @@
+// A3: per-unit exact top-k + forced blocks + log-gate.
+// Page "SAS: 通过端到端优化上下文排序的简单注意力稀疏化", method (core modules 2-4: hard
+// top-k at inference over the selector's scores, the current block always kept, the
+// selector score entering the softmax in log form, normalised over the kept set); page
+// "稀疏注意力" section 4.6 (dynamic top-k over a cheap candidate score).
+//
+// One 256-lane workgroup per unit.  Scores map to order-preserving 32-bit keys; an MSB-first
+// radix select (four 8-bit passes, LDS histogram, one-wave suffix scan) finds the k-th
+// largest key T and how many keys equal to T are taken.  Keys equal to T are taken in
+// ascending block order (ties go to the lower block index).  Selected candidates are
+// compacted in ascending order with ballot/popcount block scans, so the list comes out
+// sorted without a sort.  The gate is s_j - logsumexp over the selected set (fp32).
+#include "common.h"
+
+namespace sas {
+
+// Exclusive prefix count of `f` over the workgroup in lane order; `total` gets the sum.
+__device__ __forceinline__ uint32_t block_scan_flag(bool f, uint32_t *sh, uint32_t &total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint64_t bal = __ballot(f);
+  const uint32_t wpre = (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+  if (lane == 0) sh[w] = (uint32_t)__popcll(bal);
+  __syncthreads();
+  uint32_t pre = 0, tot = 0;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    uint32_t v = sh[x];
+    pre += (x < w) ? v : 0u;
+    tot += v;
+  }
+  total = tot;
+  __syncthreads();
+  return pre + wpre;
+}
+
+__device__ __forceinline__ float block_reduce_max(float v, float *sh) {
+  v = wave_max(v);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) sh[w] = v;
+  __syncthreads();
+  float r = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ float block_reduce_sum(float v, float *sh) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) sh[w] = v;
+  __syncthreads();
+  float r = (sh[0] + sh[1]) + (sh[2] + sh[3]);
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(256) void topk_kernel(SeqTable st, const float *__restrict__ scores,
+                                                   int64_t ld, int tq, int blk, int S, int QB,
+                                                   Budget bg, int kcap, int32_t *__restrict__ idx,
+                                                   int32_t *__restrict__ nsel,
+                                                   float *__restrict__ gate) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sh_digit, sh_above;
+  __shared__ uint32_t scan_sh[4];
+  __shared__ float red_sh[4];
+
+  const int64_t u = blockIdx.x;
+  const int i = (int)(u % QB);
+  const int b = (int)(u / QB) / S;
+  const int tid = threadIdx.x;
+  const int q0 = st.q0[b];
+  const int c0 = q0 / blk;
+  const int nqb = (q0 + tq - 1) / blk - c0 + 1;
+  int32_t *out = idx + u * kcap;
+  float *gout = bg.gate ? gate + u * kcap : nullptr;
+  if (i >= nqb) {
+    for (int p = tid; p < kcap; p += 256) {
+      out[p] = -1;
+      if (gout) gout[p] = 0.f;
+    }
+    if (tid == 0) nsel[u] = 0;
+    return;
+  }
+  const int c = c0 + i;
+  const float *row = scores + u * ld;
+  const bool sink = bg.sink && c > 0;
+  const int lo = sink ? 1 : 0;
+  const int ncand = c - lo;
+  const int k = budget_k(bg, c, ncand);
+  const int base = sink ? 1 : 0;
+
+  if (k >= ncand) {
+    for (int j = lo + tid; j < c; j += 256) out[base + (j - lo)] = j;
+  } else if (k > 0) {
+    // ---- radix select of the k-th largest key among the candidates
+    uint32_t prefix = 0u, pmask = 0u;
+    uint32_t want = (uint32_t)k;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      hist[tid] = 0u;
+      __syncthreads();
+      for (int j = lo + tid; j < c; j += 256) {
+        uint32_t key = float_order_key(row[j]);
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid < 64) {
+        uint32_t cnt[4], tot = 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          cnt[t] = hist[255 - 4 * tid - t];
+          tot += cnt[t];
+        }
+        uint32_t incl = tot;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          uint32_t v = __shfl_up(incl, o, 64);
+          if (tid >= o) incl += v;
+        }
+        const uint32_t excl = incl - tot;
+        if (excl < want && want <= incl) {
+          uint32_t run = excl;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            if (run + cnt[t] >= want) {
+              sh_digit = (uint32_t)(255 - 4 * tid - t);
+              sh_above = run;
+              break;
+            }
+            run += cnt[t];
+          }
+        }
+      }
+      __syncthreads();
+      want -= sh_above;
+      prefix |= sh_digit << shift;
+      pmask |= 255u << shift;
+      __syncthreads();
+    }
+    const uint32_t T = prefix;
+    // ---- compaction in ascending block order
+    uint32_t eq_seen = 0, pos_run = 0;
+    for (int j0 = lo; j0 < c; j0 += 256) {
+      const int j = j0 + tid;
+      const bool valid = j < c;
+      const uint32_t key = valid ? float_order_key(row[j]) : 0u;
+      const bool gt = valid && key > T;
+      const bool eq = valid && key == T;
+      uint32_t eq_tot, sel_tot;
+      const uint32_t eq_rank = block_scan_flag(eq, scan_sh, eq_tot) + eq_seen;
+      const bool sel = gt || (eq && eq_rank < want);
+      const uint32_t pos = block_scan_flag(sel, scan_sh, sel_tot) + pos_run;
+      if (sel) out[base + pos] = j;
+      eq_seen += eq_tot;
+      pos_run += sel_tot;
+    }
+  }
+  const int n = base + k + 1;
+  if (tid == 0) {
+    if (sink) out[0] = 0;
+    out[base + k] = c;
+    nsel[u] = n;
+  }
+  for (int p = n + tid; p < kcap; p += 256) {
+    out[p] = -1;
+    if (gout) gout[p] = 0.f;
+  }
+  if (gout) {
+    __syncthreads();  // the list written above is read back below by other lanes
+    float mx = -INFINITY;
+    for (int p = tid; p < n; p += 256) mx = fmaxf(mx, row[out[p]]);
+    mx = block_reduce_max(mx, red_sh);
+    float sm = 0.f;
+    for (int p = tid; p < n; p += 256) sm += expf(row[out[p]] - mx);
+    sm = block_reduce_sum(sm, red_sh);
+    const float lse = mx + logf(sm);
+    for (int p = tid; p < n; p += 256) gout[p] = row[out[p]] - lse;
+  }
+}
+
+hipError_t launch_topk(const sas_problem &p, const SeqTable &st, const float *scores, int64_t ld,
+                       int32_t tq, int32_t sel_mode, const Budget &bg, int32_t kcap, int32_t *idx,
+                       int32_t *nsel, float *gate, hipStream_t s) {
+  const int QB = num_qblocks(tq, p.block);
+  const int S = sel_mode == SAS_SEL_HEAD ? p.hq : p.hkv;
+  const int64_t units = (int64_t)p.batch * S * QB;
+  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)units), dim3(256), 0, s, st, scores, ld, tq, p.block, S,
+                     QB, bg, kcap, idx, nsel, gate);
+  return hipGetLastError();
+}
+
+}  // namespace sas

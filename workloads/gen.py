@@ -103,6 +103,7 @@ _MINI = {
 class Workload:
     cfg_id: int
     mini: bool = False
+    overrides: Optional[dict] = None
     spec: dict = field(init=False)
     seed: int = field(init=False)
 
@@ -111,8 +112,11 @@ class Workload:
         if self.mini:
             spec.update(_MINI[self.cfg_id])
             spec["name"] = spec["name"] + "_mini"
+        if self.overrides:
+            spec.update(self.overrides)
+            spec["name"] = spec["name"] + "_" + str(self.overrides.get("tag", "custom"))
         self.spec = spec
-        self.seed = 1000 + self.cfg_id
+        self.seed = 1000 + self.cfg_id + int(spec.get("seed_offset", 0))
         s = spec
         self.name: str = s["name"]
         self.kind: str = s["kind"]
@@ -137,7 +141,7 @@ class Workload:
             self.seq_kind = ["prefill"] * npf + ["decode"] * (self.batch - npf)
             self.tq = s["tq"]
         else:
-            self.seq_lens = [s["seq_len"]] * self.batch
+            self.seq_lens = list(s["seq_lens"]) if "seq_lens" in s else [s["seq_len"]] * self.batch
             self.seq_kind = ["prefill" if self.kind == "prefill" else "decode"] * self.batch
             self.tq = s.get("tq", 1)
         # first query row position per sequence
