@@ -1,0 +1,415 @@
+#!/usr/bin/env python3
+"""Benchmark of content-selected block-sparse attention on one MI355X.
+
+Headline (`value`): decode GB/s on the 32K decode workload (batch 8, 32 query / 8 KV heads,
+d 128, 64-token blocks, top-16 + current block).  One step = block scores + top-k + sparse
+decode for the whole batch; the block representatives are resident (computed once per
+context, like the KV cache itself) and are timed separately under extra.reps.
+Throughput = algorithmic bytes of the step / step time; the L2s and the 256 MB MALL are
+flushed (1 GiB written) before every timed step, outside the timed interval, so bytes come
+from HBM.  extra.* holds the other workloads: causal prefill (TFLOP/s), the SSA-style gist
+decode, and the mixed variable-length batch at sparsity 0.95 (prefill TFLOP/s, decode GB/s).
+
+Usage: python bench.py [--steps K] [--warmup W] [--only NAME,...] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+FLUSH_BYTES = 1 << 30
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------------------------------------
+# timing helpers
+# ------------------------------------------------------------------------------------------------
+class Timer:
+    """HIP event timing on the stream the library launches on.
+
+    Each timed call is preceded by a 1 GiB write (outside the timed interval) that evicts
+    the L2s and the MALL.  Launch-bound sequences are captured once in a HIP graph and
+    replayed, so host-side launch cost is not part of the device time.
+    """
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+
+    def flush(self):
+        self.flush_buf.fill_(1)
+
+    def graph(self, fn):
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    def time(self, fn, steps, warmup, use_graph=True):
+        """Mean device ms of fn over `steps` calls (graph replay when use_graph), and the wall
+        seconds of the whole timed loop (flushes included)."""
+        torch = self.torch
+        run = fn
+        if use_graph:
+            g = self.graph(fn)
+            run = g.replay
+        for _ in range(warmup):
+            self.flush()
+            run()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        evs = []
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.flush()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            run()
+            b.record(stream)
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return sum(a.elapsed_time(b) for a, b in evs) / len(evs), wall
+
+
+# ------------------------------------------------------------------------------------------------
+# workloads
+# ------------------------------------------------------------------------------------------------
+def decode_step_setup(sas, w, inp, gist=False):
+    """Preallocated buffers + a step closure for scores -> top-k -> decode (reps resident)."""
+    import torch
+    lens = inp.seq_lens
+    Lmax = inp.K.shape[2]
+    dt = sas.SAS_BF16
+    budget = sas.Budget(k_fixed=w.k_fixed, frac_num=w.frac_num, frac_den=w.frac_den,
+                        count_current=w.count_current, sink=w.sink, gate=w.gate)
+    reps = inp.gist_k if gist else sas.block_reps(inp.K, lens, w.block)
+    scores = sas.block_scores(inp.Q, reps, lens, w.block, w.hkv, Lmax, sel_mode=w.sel, gist=gist)
+    idx, nsel, gate = sas.topk_select(scores, lens, w.block, w.hq, w.hkv, w.d, dt, Lmax, budget,
+                                      sel_mode=w.sel)
+    O = torch.empty_like(inp.Q)
+    ws = torch.empty(sas.decode_workspace_bytes(len(lens), w.hq, w.hkv, w.d, w.block, dt, Lmax, lens, w.sel,
+                                                idx.shape[1], gist), dtype=torch.uint8, device="cuda")
+    gk = inp.gist_k if gist else None
+    gv = inp.gist_v if gist else None
+
+    def attend():
+        sas.sparse_decode(inp.Q, inp.K, inp.V, lens, w.block, idx, nsel, gate, sel_mode=w.sel, gist_k=gk,
+                          gist_v=gv, O=O, workspace=ws)
+
+    def step():
+        sas.block_scores(inp.Q, reps, lens, w.block, w.hkv, Lmax, sel_mode=w.sel, gist=gist, scores=scores)
+        sas.topk_select(scores, lens, w.block, w.hq, w.hkv, w.d, dt, Lmax, budget, sel_mode=w.sel, idx=idx,
+                        nsel=nsel, gate=gate)
+        attend()
+
+    return dict(step=step, attend=attend), dict(reps=reps, scores=scores, idx=idx, nsel=nsel, gate=gate, O=O)
+
+
+def prefill_step_setup(sas, w, inp):
+    import torch
+    lens = inp.seq_lens
+    Lmax = inp.K.shape[2]
+    dt = sas.SAS_BF16
+    budget = sas.Budget(k_fixed=w.k_fixed, frac_num=w.frac_num, frac_den=w.frac_den,
+                        count_current=w.count_current, sink=w.sink, gate=w.gate)
+    reps = sas.block_reps(inp.K, lens, w.block)
+    scores = sas.block_scores(inp.Q, reps, lens, w.block, w.hkv, Lmax, q_start=inp.q_start, sel_mode=w.sel)
+    ws = torch.empty(max(1, len(lens) * (w.hq if w.sel == "head" else w.hkv) * sas.num_qblocks(w.tq, w.block)
+                         * w.d * 4), dtype=torch.uint8, device="cuda")
+    idx, nsel, gate = sas.topk_select(scores, lens, w.block, w.hq, w.hkv, w.d, dt, Lmax, budget, tq=w.tq,
+                                      q_start=inp.q_start, sel_mode=w.sel)
+    O = torch.empty_like(inp.Q)
+
+    def make_reps():
+        sas.block_reps(inp.K, lens, w.block, reps=reps)
+
+    def attend():
+        sas.sparse_prefill(inp.Q, inp.K, inp.V, lens, w.block, inp.q_start, idx, nsel, gate, sel_mode=w.sel, O=O)
+
+    def step():
+        make_reps()
+        sas.block_scores(inp.Q, reps, lens, w.block, w.hkv, Lmax, q_start=inp.q_start, sel_mode=w.sel,
+                         scores=scores, workspace=ws)
+        sas.topk_select(scores, lens, w.block, w.hq, w.hkv, w.d, dt, Lmax, budget, tq=w.tq, q_start=inp.q_start,
+                        sel_mode=w.sel, idx=idx, nsel=nsel, gate=gate)
+        attend()
+
+    return dict(step=step, attend=attend, reps=make_reps), dict(reps=reps, idx=idx, nsel=nsel, O=O)
+
+
+# ------------------------------------------------------------------------------------------------
+# algorithmic work (from the selected lists, copied to the host once)
+# ------------------------------------------------------------------------------------------------
+def decode_bytes(w, inp, bufs, gist=False):
+    """Bytes the decode step must move: representatives of the candidate blocks (once per KV
+    head), the union over a KV group's query heads of the selected K/V rows, Q and O."""
+    import numpy as np
+    idx = bufs["idx"].cpu().numpy()
+    nsel = bufs["nsel"].cpu().numpy()
+    B = len(inp.seq_lens)
+    S = w.hq if w.sel == "head" else w.hkv
+    G = w.hq // w.hkv
+    e = 2
+    total = 0
+    kv_bytes = 0
+    rep_bytes = 0
+    for bi, L in enumerate(inp.seq_lens):
+        c = (L - 1) // w.block
+        for g in range(w.hkv):
+            heads = range(g * G, (g + 1) * G) if w.sel == "head" else [g]
+            union = set()
+            for s in heads:
+                u = bi * S + s
+                union |= set(int(x) for x in idx[u, : nsel[u]])
+            rows = sum(min((j + 1) * w.block, L) - j * w.block for j in union)
+            kv_bytes += rows * w.d * e * 2
+            if gist:
+                ncand = c
+                rep_bytes += ncand * w.d * e                               # gist K, scored once
+                kv_bytes += (c - len([j for j in union if j < c])) * w.d * e  # gist V of the others
+            else:
+                rep_bytes += c * w.d * 4                                   # fp32 reps j < c
+    qo = 2 * B * w.hq * w.d * e
+    total = kv_bytes + rep_bytes + qo
+    return dict(total=total, kv=kv_bytes, reps=rep_bytes, qo=qo)
+
+
+def prefill_flops(w, inp, bufs):
+    """4*d per visible (row, head, key) pair of the selected blocks (QK^T and PV)."""
+    import numpy as np
+    idx = bufs["idx"].cpu().numpy()
+    nsel = bufs["nsel"].cpu().numpy()
+    S = w.hq if w.sel == "head" else w.hkv
+    nh = 1 if w.sel == "head" else w.hq // w.hkv
+    QB = (w.tq - 1 + w.block - 1) // w.block + 1 if w.tq > 1 else 1
+    pairs = 0
+    for bi, L in enumerate(inp.seq_lens):
+        q0 = inp.q_start[bi]
+        c0 = q0 // w.block
+        for s in range(S):
+            for i in range(QB):
+                u = (bi * S + s) * QB + i
+                n = int(nsel[u])
+                if n == 0:
+                    continue
+                c = c0 + i
+                p_lo = max(q0, c * w.block)
+                p_hi = min(q0 + w.tq, (c + 1) * w.block) - 1
+                pos = np.arange(p_lo, p_hi + 1)
+                for j in idx[u, :n]:
+                    j = int(j)
+                    hi = np.minimum(min((j + 1) * w.block, L), pos + 1)
+                    pairs += int(np.clip(hi - j * w.block, 0, None).sum()) * nh
+    full = sum(sum(q0 + t + 1 for t in range(w.tq)) for q0 in inp.q_start) * w.hq
+    return dict(flops=4.0 * w.d * pairs, pairs=pairs, sparsity=1.0 - pairs / full)
+
+
+# ------------------------------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on a bounded sample of the decode workload
+# ------------------------------------------------------------------------------------------------
+def cpu_baseline_decode(w, host, bytes_per_step, seconds):
+    import numpy as np
+    from oracle import sas_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    seqs = sorted(host)
+    reps = {b: np.stack([orc.block_reps(host[b]["k"][g], w.seq_lens[b], w.block) for g in range(w.hkv)])
+            for b in seqs}
+    units = 0
+    t0 = time.perf_counter()
+    while True:
+        for b in seqs:
+            h = host[b]
+            orc.run_sequence(h["q"], h["k"], h["v"], w.seq_lens[b], w.q_start[b], w.block, w.sel,
+                             k_fixed=w.k_fixed, reps=reps[b])
+            units += w.hkv
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    units_per_step = w.batch * w.hkv
+    step_s = dt / units * units_per_step
+    return {"value": round(bytes_per_step / step_s / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{units} (sequence, KV group) decode units of the 32K decode workload "
+                      f"({len(seqs)} sequences repeated for {dt:.1f} s; reps precomputed), scaled to the "
+                      f"{units_per_step}-unit step: {step_s * 1e3:.1f} ms/step"}
+
+
+# ------------------------------------------------------------------------------------------------
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default="decode,reps,prefill,gist,mixed",
+                    help="comma list of measurements: decode,reps,prefill,gist,mixed,copy")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path (each GPU would run the same "
+              "kernels on its own share of sequences / KV heads); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    only = set(x for x in args.only.split(",") if x)
+
+    import torch
+    import top_block_sparse_gist_amd as sas
+    from workloads import Workload
+    from workloads.device import upload
+
+    sas.load()
+    torch.cuda.init()
+    timer = Timer(torch)
+    extra = {}
+    result = None
+    K_, W_ = args.steps, args.warmup
+    k_small = max(3, args.steps // 10)
+
+    # ---------------------------------------------------------------- headline: 32K decode
+    w2 = Workload(2)
+    log("[bench] generating the 32K decode workload")
+    keep = {0, 1} if not args.no_cpu_baseline else set()
+    inp2 = upload(w2, list(range(w2.batch)), keep_host=keep)
+    fns, bufs = decode_step_setup(sas, w2, inp2)
+    torch.cuda.synchronize()
+    by = decode_bytes(w2, inp2, bufs)
+    if "decode" in only:
+        log("[bench] timing decode")
+        ms, wall = timer.time(fns["step"], K_, W_)
+        ms_eager, _ = timer.time(fns["step"], K_, W_, use_graph=False)
+        ms_att, _ = timer.time(fns["attend"], K_, W_)
+        value = by["total"] / (ms * 1e-3) / 1e9
+        dec_bytes = by["kv"] + by["qo"]
+        ach = dec_bytes / (ms_att * 1e-3) / 1e9
+        result = {
+            "metric": "decode GB/s (%HBM peak) + prefill TFLOP/s (%MFMA peak) at sparsity 0.95",
+            "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K_, "warmup": W_,
+            "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16", "data": "synthetic (seeded; needle blocks planted)",
+            "config": {"workload": "decode_b8_h32x8_d128_ctx32768_blk64_top16+current",
+                       "batch": w2.batch, "hq": w2.hq, "hkv": w2.hkv, "d": w2.d, "context": w2.seq_lens[0],
+                       "block": w2.block, "k": w2.k_fixed, "selection": "per KV group",
+                       "step": "block scores + top-k + sparse decode (HIP graph replay); block reps resident",
+                       "bytes_per_step": by["total"], "sparsity": round(1 - 17 / 512, 4),
+                       "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+                       "eager_ms_per_step": round(ms_eager, 5),
+                       "wall_ms_per_step_incl_cache_flush": round(wall / K_ * 1e3, 4)},
+            "roofline": {"bound": "hbm", "kernel": "sas_sparse_decode (split-K attention + combine)",
+                         "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                         "bytes_per_launch": dec_bytes, "avg_launch_ms": round(ms_att, 5)},
+        }
+        log(f"[bench] decode step {ms * 1e3:.1f} us (eager {ms_eager * 1e3:.1f}) -> {value:.0f} GB/s; "
+            f"attention {ms_att * 1e3:.1f} us -> {ach:.0f} GB/s")
+    if "reps" in only:
+        K = inp2.K
+        reps = bufs["reps"]
+        t, _ = timer.time(lambda: sas.block_reps(K, inp2.seq_lens, w2.block, reps=reps), k_small, 2)
+        rb = K.numel() * 2 + reps.numel() * 4
+        extra["reps_32k"] = {"us": round(t * 1e3, 2), "GB/s": round(rb / (t * 1e-3) / 1e9, 1), "bytes": rb}
+        log(f"[bench] reps 32K: {t * 1e3:.1f} us -> {rb / (t * 1e-3) / 1e9:.0f} GB/s")
+    if not args.no_cpu_baseline and result is not None:
+        log("[bench] cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline_decode(w2, inp2.host, by["total"], args.cpu_seconds)
+    del inp2, bufs, fns
+    torch.cuda.empty_cache()
+
+    def prefill_measure(name, w, inp, desc):
+        fns, bufs = prefill_step_setup(sas, w, inp)
+        torch.cuda.synchronize()
+        fl = prefill_flops(w, inp, bufs)
+        t_step, _ = timer.time(fns["step"], k_small, 2)
+        t_att, _ = timer.time(fns["attend"], k_small, 2)
+        t_rep, _ = timer.time(fns["reps"], k_small, 2)
+        tf = fl["flops"] / (t_att * 1e-3) / 1e12
+        extra[name] = {"workload": desc, "step_ms": round(t_step, 4), "prefill_ms": round(t_att, 4),
+                       "reps_ms": round(t_rep, 4), "TFLOP/s": round(tf, 1),
+                       "pct_mfma_peak": round(100 * tf / BF16_PEAK_TFLOPS, 2),
+                       "step_TFLOP/s": round(fl["flops"] / (t_step * 1e-3) / 1e12, 1),
+                       "flops": fl["flops"], "sparsity": round(fl["sparsity"], 4)}
+        log(f"[bench] {name}: prefill {t_att:.3f} ms -> {tf:.0f} TFLOP/s; step {t_step:.3f} ms; "
+            f"sparsity {fl['sparsity']:.3f}")
+
+    def decode_measure(name, w, inp, desc, gist=False):
+        fns, bufs = decode_step_setup(sas, w, inp, gist=gist)
+        torch.cuda.synchronize()
+        byw = decode_bytes(w, inp, bufs, gist=gist)
+        t_step, _ = timer.time(fns["step"], K_, W_)
+        t_att, _ = timer.time(fns["attend"], K_, W_)
+        gbs = byw["total"] / (t_step * 1e-3) / 1e9
+        extra[name] = {"workload": desc, "step_us": round(t_step * 1e3, 2), "attend_us": round(t_att * 1e3, 2),
+                       "GB/s": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                       "attend_GB/s": round((byw["kv"] + byw["qo"]) / (t_att * 1e-3) / 1e9, 1),
+                       "bytes_per_step": byw["total"]}
+        log(f"[bench] {name}: step {t_step * 1e3:.1f} us -> {gbs:.0f} GB/s; attend {t_att * 1e3:.1f} us")
+
+    if "prefill" in only:
+        w3 = Workload(3)
+        log("[bench] generating the 32K prefill workload")
+        inp3 = upload(w3, [0])
+        prefill_measure("prefill_32k", w3, inp3, "prefill_b1_h28x4_d128_32768_blk128_top1/8+sink+current_gate")
+        del inp3
+        torch.cuda.empty_cache()
+    if "gist" in only:
+        w4 = Workload(4)
+        log("[bench] generating the 128K gist decode workload")
+        inp4 = upload(w4, list(range(w4.batch)), gist=True)
+        decode_measure("gist_decode_128k", w4, inp4, "gist_decode_b4_h64x8_d128_ctx131073_chunk64_top104",
+                       gist=True)
+        del inp4
+        torch.cuda.empty_cache()
+    if "mixed" in only:
+        w5 = Workload(5)
+        log("[bench] generating the mixed variable-length workload")
+        inp5p = upload(w5, w5.prefill_seqs())
+        prefill_measure("mixed_prefill_half", w5, inp5p,
+                        f"8 seqs, last 4096 rows, lens {inp5p.seq_lens}, 32/8 heads, per-head, 5% + current, gate")
+        del inp5p
+        torch.cuda.empty_cache()
+        inp5d = upload(w5, w5.decode_seqs())
+        decode_measure("mixed_decode_half", w5, inp5d,
+                       f"8 seqs decode, lens {inp5d.seq_lens}, 32/8 heads, per-head, 5% + current, gate")
+        del inp5d
+        torch.cuda.empty_cache()
+    if "copy" in only:
+        # plain copy of known size: calibrates the profiler's HBM byte counters
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        b_ = torch.empty_like(a)
+        for _ in range(3):
+            b_.copy_(a)
+        torch.cuda.synchronize()
+        extra["copy_calibration_bytes"] = {"read": a.numel(), "write": a.numel()}
+
+    if result is None:
+        result = {"metric": "decode GB/s (%HBM peak) + prefill TFLOP/s (%MFMA peak) at sparsity 0.95",
+                  "value": None, "unit": "GB/s", "n_gpus": 1, "steps": K_, "warmup": W_}
+    result["extra"] = extra
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
