@@ -46,10 +46,13 @@ class Timer:
 
     def __init__(self, torch):
         self.torch = torch
-        self.flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        self.flush_f32 = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        self.sink = None
 
     def flush(self):
-        self.flush_buf.fill_(1)
+        # read 1 GiB: evicts the L2s and the MALL with clean lines (a write-based flush would leave
+        # dirty lines whose write-back would be charged to the timed kernels)
+        self.sink = self.flush_f32.sum()
 
     def graph(self, fn):
         torch = self.torch
@@ -104,11 +107,12 @@ def decode_step_setup(sas, w, inp, gist=False):
     budget = sas.Budget(k_fixed=w.k_fixed, frac_num=w.frac_num, frac_den=w.frac_den,
                         count_current=w.count_current, sink=w.sink, gate=w.gate)
     reps = inp.gist_k if gist else sas.block_reps(inp.K, lens, w.block)
-    scores = sas.block_scores(inp.Q, reps, lens, w.block, w.hkv, Lmax, sel_mode=w.sel, gist=gist)
-    idx, nsel, gate = sas.topk_select(scores, lens, w.block, w.hq, w.hkv, w.d, dt, Lmax, budget,
-                                      sel_mode=w.sel)
+    sel_ws = torch.zeros(sas.select_decode_workspace_bytes(len(lens), w.hq, w.hkv, w.d, w.block, dt, Lmax, lens),
+                         dtype=torch.uint8, device="cuda")
+    scores, idx, nsel, gate = sas.select_decode(inp.Q, reps, lens, w.block, w.hkv, Lmax, budget, sel_mode=w.sel,
+                                                gist=gist, workspace=sel_ws)
     O = torch.empty_like(inp.Q)
-    ws = torch.empty(sas.decode_workspace_bytes(len(lens), w.hq, w.hkv, w.d, w.block, dt, Lmax, lens, w.sel,
+    ws = torch.zeros(sas.decode_workspace_bytes(len(lens), w.hq, w.hkv, w.d, w.block, dt, Lmax, lens, w.sel,
                                                 idx.shape[1], gist), dtype=torch.uint8, device="cuda")
     gk = inp.gist_k if gist else None
     gv = inp.gist_v if gist else None
@@ -118,9 +122,8 @@ def decode_step_setup(sas, w, inp, gist=False):
                           gist_v=gv, O=O, workspace=ws)
 
     def step():
-        sas.block_scores(inp.Q, reps, lens, w.block, w.hkv, Lmax, sel_mode=w.sel, gist=gist, scores=scores)
-        sas.topk_select(scores, lens, w.block, w.hq, w.hkv, w.d, dt, Lmax, budget, sel_mode=w.sel, idx=idx,
-                        nsel=nsel, gate=gate)
+        sas.select_decode(inp.Q, reps, lens, w.block, w.hkv, Lmax, budget, sel_mode=w.sel, gist=gist,
+                          kcap=idx.shape[1], scores=scores, idx=idx, nsel=nsel, gate=gate, workspace=sel_ws)
         attend()
 
     return dict(step=step, attend=attend), dict(reps=reps, scores=scores, idx=idx, nsel=nsel, gate=gate, O=O)
@@ -313,12 +316,12 @@ def main():
             "config": {"workload": "decode_b8_h32x8_d128_ctx32768_blk64_top16+current",
                        "batch": w2.batch, "hq": w2.hq, "hkv": w2.hkv, "d": w2.d, "context": w2.seq_lens[0],
                        "block": w2.block, "k": w2.k_fixed, "selection": "per KV group",
-                       "step": "block scores + top-k + sparse decode (HIP graph replay); block reps resident",
+                       "step": "fused block scores + top-k, then sparse decode (2 launches, HIP graph replay); block reps resident",
                        "bytes_per_step": by["total"], "sparsity": round(1 - 17 / 512, 4),
                        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
                        "eager_ms_per_step": round(ms_eager, 5),
                        "wall_ms_per_step_incl_cache_flush": round(wall / K_ * 1e3, 4)},
-            "roofline": {"bound": "hbm", "kernel": "sas_sparse_decode (split-K attention + combine)",
+            "roofline": {"bound": "hbm", "kernel": "sas_sparse_decode (decode_bf16_kernel, split-K with in-kernel merge)",
                          "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
                          "bytes_per_launch": dec_bytes, "avg_launch_ms": round(ms_att, 5)},

@@ -149,14 +149,31 @@ sas_status sas_sparse_prefill(const sas_problem *p, const void *Q, const int64_t
                               int32_t kcap, float scale, void *O, const int64_t o_stride[3],
                               void *stream);
 
+/* A2 + A3 fused for decode: the scores and the selection of sas_block_scores (q_start = NULL)
+ * followed by sas_topk_select, in one launch ([GSA] section 4 pseudo-code steps 1-2).  Same
+ * outputs (scores rows j <= c, idx, nsel, gate).  Needs every current block c <= 2048 (e.g.
+ * 131,136 tokens at blk 64; longer contexts: use the two calls) and at most 16 query heads
+ * per KV head.
+ *   workspace: sas_select_decode_workspace() bytes of arrival counters.  It must be zero
+ *   before its first use; every call leaves it zero again.  Calls that share one workspace
+ *   must not overlap in time (two streams running at once would race on the counters). */
+size_t sas_select_decode_workspace(const sas_problem *p);
+sas_status sas_select_decode(const sas_problem *p, const void *Q, const int64_t q_stride[2],
+                             const void *reps, int32_t reps_kind, const int64_t rep_stride[3],
+                             int32_t sel_mode, float scale, const sas_budget *budget, int32_t kcap,
+                             float *scores, int64_t scores_ld, int32_t *idx, int32_t *nsel,
+                             float *gate, void *workspace, size_t workspace_bytes, void *stream);
+
 /* A5/A6 - sparse decode; one row per (sequence, query head) at position L_b - 1.
  *   Q, O: [B, Hq, d] (q_stride, o_stride = {batch, head}).
  *   Gist mode ([SSA] method items 2-3: hybrid attention) when gist_k and gist_v are both
  *   non-NULL: the key set is the raw tokens of the selected chunks plus the gist token of
  *   every complete chunk before the current one that is not selected; gist_stride =
  *   {batch, head, chunk}; the gate must be NULL in gist mode.
- *   workspace: device scratch of sas_sparse_decode_workspace() bytes for the split-K
- *   partial results. */
+ *   workspace: sas_sparse_decode_workspace() bytes: per-unit arrival counters followed by
+ *   the split-K partial records (bf16 path; 0 bytes for fp32).  The counters must be zero
+ *   before the workspace's first use; every call leaves them zero again.  Calls that share
+ *   one workspace must not overlap in time. */
 size_t sas_sparse_decode_workspace(const sas_problem *p, int32_t sel_mode, int32_t kcap,
                                    int32_t gist);
 sas_status sas_sparse_decode(const sas_problem *p, const void *Q, const int64_t q_stride[2],

@@ -125,6 +125,17 @@ def run_case(w: Workload, seqs: List[int], unit_sample: Optional[int] = None, se
                               gist=gist)
     idx, nsel, gate = sas.topk_select(scores, lens, w.block, w.hq, w.hkv, w.d, dtype_code, Lmax, budget, tq=tq,
                                       q_start=inp.q_start, sel_mode=w.sel)
+    if decode and max((L - 1) // w.block for L in lens) <= 2048:
+        # the fused decode selection must give the same scores, lists and gates as the two calls
+        s2, i2, n2, g2 = sas.select_decode(inp.Q, reps, lens, w.block, w.hkv, Lmax, budget, sel_mode=w.sel,
+                                           gist=gist, kcap=idx.shape[1])
+        torch.cuda.synchronize()
+        assert torch.equal(n2, nsel), "fused selection: nsel differs from the two-call path"
+        assert torch.equal(i2, idx), "fused selection: lists differ from the two-call path"
+        if g2 is not None:
+            assert torch.allclose(g2, gate, rtol=0, atol=1e-6), "fused selection: gates differ"
+        scores, idx, nsel, gate = s2, i2, n2, g2
+        say("[case] fused decode selection == two-call selection")
     if decode:
         O = sas.sparse_decode(inp.Q, inp.K, inp.V, lens, w.block, idx, nsel, gate, sel_mode=w.sel,
                               gist_k=inp.gist_k if gist else None, gist_v=inp.gist_v if gist else None)

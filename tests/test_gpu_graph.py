@@ -46,13 +46,16 @@ def test_decode_step_graph_replays_match_eager(cfg):
     idx, nsel, gate = sas.topk_select(scores, lens, w.block, w.hq, w.hkv, w.d, sas.SAS_BF16, Lmax, bud,
                                       sel_mode=w.sel)
     O = torch.empty_like(inp.Q)
-    ws = torch.empty(sas.decode_workspace_bytes(len(lens), w.hq, w.hkv, w.d, w.block, sas.SAS_BF16, Lmax, lens,
+    ws = torch.zeros(sas.decode_workspace_bytes(len(lens), w.hq, w.hkv, w.d, w.block, sas.SAS_BF16, Lmax, lens,
                                                 w.sel, idx.shape[1], False), dtype=torch.uint8, device="cuda")
 
+    sel_ws = torch.zeros(sas.select_decode_workspace_bytes(len(lens), w.hq, w.hkv, w.d, w.block, sas.SAS_BF16,
+                                                           Lmax, lens), dtype=torch.uint8, device="cuda")
+
     def step():
-        sas.block_scores(inp.Q, reps, lens, w.block, w.hkv, Lmax, sel_mode=w.sel, scores=scores)
-        sas.topk_select(scores, lens, w.block, w.hq, w.hkv, w.d, sas.SAS_BF16, Lmax, bud, sel_mode=w.sel, idx=idx,
-                        nsel=nsel, gate=gate)
+        # the two-launch step the benchmark replays: fused selection, then attention
+        sas.select_decode(inp.Q, reps, lens, w.block, w.hkv, Lmax, bud, sel_mode=w.sel, kcap=idx.shape[1],
+                          scores=scores, idx=idx, nsel=nsel, gate=gate, workspace=sel_ws)
         sas.sparse_decode(inp.Q, inp.K, inp.V, lens, w.block, idx, nsel, gate, sel_mode=w.sel, O=O, workspace=ws)
 
     step()

@@ -19,8 +19,8 @@ from . import _lib
 from ._lib import (SAS_BF16, SAS_F32, SAS_REPS_GIST, SAS_REPS_POOLED, SAS_SEL_GROUP, SAS_SEL_HEAD,
                    SasError, check, i32x, i64x, load)
 
-__all__ = ["Budget", "block_reps", "block_scores", "topk_select", "sparse_prefill", "sparse_decode",
-           "num_qblocks", "required_kcap", "SasError", "load", "sel_code"]
+__all__ = ["Budget", "block_reps", "block_scores", "topk_select", "select_decode", "sparse_prefill",
+           "sparse_decode", "num_qblocks", "required_kcap", "SasError", "load", "sel_code"]
 
 
 def _torch():
@@ -182,6 +182,50 @@ def topk_select(scores, seq_lens, block, hq, hkv, d, dtype, max_len, budget: Bud
     return idx, nsel, (gate if budget.gate else None)
 
 
+def select_decode(Q, reps, seq_lens, block, hkv, max_len, budget: Budget, sel_mode="group", gist=False,
+                  scale=0.0, kcap=None, scores=None, idx=None, nsel=None, gate=None, workspace=None,
+                  stream=None):
+    """A2 + A3 fused for decode (one launch): (scores, idx, nsel, gate) as block_scores + topk_select.
+
+    workspace: arrival counters, zero before first use (allocated zeroed when not given) and left
+    zero by every call.
+    """
+    torch = _torch()
+    B, hq, d = Q.shape
+    sm = sel_code(sel_mode)
+    S = hq if sm == SAS_SEL_HEAD else hkv
+    nb = max(-(-int(L) // block) for L in seq_lens)
+    p = _Prob(B, hq, hkv, d, block, _dtype_code(Q), max_len, seq_lens)
+    bs = budget.c_struct()
+    lib = load()
+    if kcap is None:
+        kcap = lib.sas_required_kcap(p.ref, 1, None, C.byref(bs))
+        if kcap < 0:
+            check(kcap, "sas_required_kcap")
+    if scores is None:
+        scores = torch.full((B * S, nb), float("-inf"), dtype=torch.float32, device=Q.device)
+    if idx is None:
+        idx = torch.empty((B * S, kcap), dtype=torch.int32, device=Q.device)
+    if nsel is None:
+        nsel = torch.empty((B * S,), dtype=torch.int32, device=Q.device)
+    if budget.gate and gate is None:
+        gate = torch.empty((B * S, kcap), dtype=torch.float32, device=Q.device)
+    if workspace is None:
+        workspace = torch.zeros(lib.sas_select_decode_workspace(p.ref), dtype=torch.uint8, device=Q.device)
+    check(lib.sas_select_decode(p.ref, _ptr(Q), _strides(Q, 2), _ptr(reps),
+                                SAS_REPS_GIST if gist else SAS_REPS_POOLED, _strides(reps, 3), sm, float(scale),
+                                C.byref(bs), kcap, _ptr(scores), scores.stride(0), _ptr(idx), _ptr(nsel),
+                                _ptr(gate) if budget.gate else None, _ptr(workspace), workspace.numel(),
+                                _stream(stream)),
+          "sas_select_decode")
+    return scores, idx, nsel, (gate if budget.gate else None)
+
+
+def select_decode_workspace_bytes(B, hq, hkv, d, block, dtype, max_len, seq_lens) -> int:
+    p = _Prob(B, hq, hkv, d, block, dtype, max_len, seq_lens)
+    return int(load().sas_select_decode_workspace(p.ref))
+
+
 def sparse_prefill(Q, K, V, seq_lens, block, q_start, idx, nsel, gate=None, sel_mode="group", scale=0.0,
                    O=None, stream=None):
     """A4: O [B, Hq, T, d] = attention of each row over its unit's selected blocks (causal)."""
@@ -224,7 +268,8 @@ def sparse_decode(Q, K, V, seq_lens, block, idx, nsel, gate=None, sel_mode="grou
     lib = load()
     need = lib.sas_sparse_decode_workspace(p.ref, sel_code(sel_mode), kcap, int(gist))
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+        # arrival counters must start at zero (the library leaves them zero after each call)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=Q.device)
     check(lib.sas_sparse_decode(p.ref, _ptr(Q), _strides(Q, 2), _ptr(K), _ptr(V), _strides(K, 3),
                                 _ptr(gist_k) if gist else None, _ptr(gist_v) if gist else None,
                                 _strides(gist_k, 3) if gist else None, sel_code(sel_mode), _ptr(idx), _ptr(nsel),

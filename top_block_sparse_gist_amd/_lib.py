@@ -21,8 +21,8 @@ STATUS_NAMES = {0: "SAS_OK", -1: "SAS_ERR_NULL", -2: "SAS_ERR_SHAPE", -3: "SAS_E
                 -4: "SAS_ERR_WORKSPACE", -5: "SAS_ERR_HIP"}
 
 EXPORTED = ("sas_num_qblocks", "sas_required_kcap", "sas_block_reps", "sas_block_scores_workspace",
-            "sas_block_scores", "sas_topk_select", "sas_sparse_prefill", "sas_sparse_decode_workspace",
-            "sas_sparse_decode", "sas_last_error")
+            "sas_block_scores", "sas_topk_select", "sas_select_decode_workspace", "sas_select_decode",
+            "sas_sparse_prefill", "sas_sparse_decode_workspace", "sas_sparse_decode", "sas_last_error")
 
 
 class Problem(C.Structure):
@@ -51,6 +51,9 @@ _SIGS = {
                                    C.c_int32, C.c_float, _VP, C.c_int64, _VP, C.c_size_t, _VP]),
     "sas_topk_select": (C.c_int, [_P, _VP, C.c_int64, C.c_int32, C.POINTER(C.c_int32), C.c_int32, _B, C.c_int32,
                                   _VP, _VP, _VP, _VP]),
+    "sas_select_decode_workspace": (C.c_size_t, [_P]),
+    "sas_select_decode": (C.c_int, [_P, _VP, _I64_3, _VP, C.c_int32, _I64_3, C.c_int32, C.c_float, _B, C.c_int32,
+                                    _VP, C.c_int64, _VP, _VP, _VP, _VP, C.c_size_t, _VP]),
     "sas_sparse_prefill": (C.c_int, [_P, _VP, _I64_3, _VP, _VP, _I64_3, C.c_int32, C.POINTER(C.c_int32), C.c_int32,
                                      _VP, _VP, _VP, C.c_int32, C.c_float, _VP, _I64_3, _VP]),
     "sas_sparse_decode_workspace": (C.c_size_t, [_P, C.c_int32, C.c_int32, C.c_int32]),

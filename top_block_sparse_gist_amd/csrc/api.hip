@@ -176,6 +176,8 @@ sas_status sas_block_scores(const sas_problem *p, const void *Q, const int64_t q
   if (scores_ld < nbmax) return fail(SAS_ERR_SHAPE, "scores_ld %lld < %d blocks", (long long)scores_ld, nbmax);
   const float sc = resolve_scale(scale, p->head_dim);
   const hipStream_t s = (hipStream_t)stream;
+  if (!q_start && sel_mode == SAS_SEL_HEAD && p->hq / p->hkv > 16)
+    return fail(SAS_ERR_UNSUPPORTED, "per-head decode scoring supports at most 16 query heads per KV head");
   if (!q_start)
     return hip_status(launch_scores_decode(*p, tab, Q, q_stride, reps, reps_kind, rep_stride, sel_mode, sc, scores,
                                            scores_ld, s),
@@ -242,6 +244,56 @@ sas_status sas_sparse_prefill(const sas_problem *p, const void *Q, const int64_t
   return hip_status(launch_attend_f32(*p, tab, Q, q_stride, K, V, kv_stride, nullptr, nullptr, nullptr, tq, sel_mode,
                                       idx, nsel, gate, kcap, sc, O, o_stride, s),
                     "sas_sparse_prefill");
+}
+
+size_t sas_select_decode_workspace(const sas_problem *p) {
+  if (!p || p->batch < 1 || p->hkv < 1) return 0;
+  return ((size_t)p->batch * p->hkv * 4 + 255) / 256 * 256;
+}
+
+sas_status sas_select_decode(const sas_problem *p, const void *Q, const int64_t q_stride[2], const void *reps,
+                             int32_t reps_kind, const int64_t rep_stride[3], int32_t sel_mode, float scale,
+                             const sas_budget *budget, int32_t kcap, float *scores, int64_t scores_ld, int32_t *idx,
+                             int32_t *nsel, float *gate, void *workspace, size_t workspace_bytes, void *stream) {
+  SeqTable tab{};
+  sas_status st;
+  if ((st = check_problem(p, &tab)) != SAS_OK) return st;
+  if ((st = check_sel(sel_mode)) != SAS_OK) return st;
+  if ((st = check_budget(budget)) != SAS_OK) return st;
+  if (!Q || !q_stride || !reps || !rep_stride || !scores || !idx || !nsel)
+    return fail(SAS_ERR_NULL, "a required pointer is NULL");
+  if (budget->gate && !gate) return fail(SAS_ERR_NULL, "budget->gate is set but gate is NULL");
+  if (reps_kind != SAS_REPS_POOLED && reps_kind != SAS_REPS_GIST)
+    return fail(SAS_ERR_SHAPE, "reps_kind %d", reps_kind);
+  if (scale < 0.f || !isfinite(scale)) return fail(SAS_ERR_SHAPE, "scale must be finite and >= 0");
+  if (p->hq / p->hkv > 16)
+    return fail(SAS_ERR_UNSUPPORTED, "the fused decode selection supports at most 16 query heads per KV head");
+  const int rep_bytes = reps_kind == SAS_REPS_GIST ? elem_bytes(p->dtype) : 4;
+  if (!aligned16(Q) || !aligned16(reps) || !strides_ok(q_stride, 2, elem_bytes(p->dtype)) ||
+      !strides_ok(rep_stride, 3, rep_bytes))
+    return fail(SAS_ERR_SHAPE, "Q / reps must be 16-byte aligned with 16-byte-multiple row strides");
+  int nbmax = 0, maxc = 0;
+  for (int b = 0; b < p->batch; ++b) {
+    nbmax = std::max(nbmax, cdiv(p->seq_lens[b], p->block));
+    maxc = std::max(maxc, (p->seq_lens[b] - 1) / p->block);
+  }
+  if (maxc > SELECT_DECODE_MAX_C)
+    return fail(SAS_ERR_UNSUPPORTED, "current block %d > %d: use sas_block_scores + sas_topk_select", maxc,
+                SELECT_DECODE_MAX_C);
+  if (scores_ld < nbmax) return fail(SAS_ERR_SHAPE, "scores_ld %lld < %d blocks", (long long)scores_ld, nbmax);
+  const int32_t need = required_kcap(p, 1, nullptr, budget);
+  if (kcap < need) return fail(SAS_ERR_SHAPE, "kcap %d < %d selected blocks", kcap, need);
+  const size_t wneed = sas_select_decode_workspace(p);
+  if (!workspace || workspace_bytes < wneed)
+    return fail(SAS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", wneed, workspace_bytes);
+  if (!aligned16(workspace)) return fail(SAS_ERR_SHAPE, "workspace must be 16-byte aligned");
+  Budget bg{budget->k_fixed, budget->frac_num, budget->frac_den, budget->count_current,
+            budget->force_sink ? 1 : 0, budget->gate ? 1 : 0};
+  const int64_t qs3[3] = {q_stride[0], q_stride[1], 0};
+  return hip_status(launch_select_decode(*p, tab, Q, qs3, reps, reps_kind, rep_stride, sel_mode,
+                                         resolve_scale(scale, p->head_dim), scores, scores_ld, bg, kcap, idx, nsel,
+                                         budget->gate ? gate : nullptr, (uint32_t *)workspace, (hipStream_t)stream),
+                    "sas_select_decode");
 }
 
 size_t sas_sparse_decode_workspace(const sas_problem *p, int32_t sel_mode, int32_t kcap, int32_t gist) {

@@ -79,6 +79,50 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Cross-workgroup hand-off without whole-L2 maintenance.  The 8 XCDs have separate L2s, and a
+// device-scope release/acquire fence writes back and invalidates the whole L2 of the XCD.
+// Data handed to another workgroup is instead written with device-coherent stores (sc1) and
+// read with device-coherent loads (sc1); the writer waits for its stores to be acknowledged
+// (vmcnt 0) before it bumps the arrival counter with a device-scope atomic, and the reader
+// issues its loads only after its own atomic has returned.
+__device__ __forceinline__ void store_dev(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
+
+// 16-byte device-coherent accesses through a raw buffer resource (aux 16 = sc1).  Accesses
+// past `bytes` read 0 / are dropped by the hardware range check.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store16_dev(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)off, 0, 16);
+}
+__device__ __forceinline__ f32x4 load16_dev(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 16));
+}
+__device__ __forceinline__ void store4_dev(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v), r, (int)off, 0, 16);
+}
+__device__ __forceinline__ float load4_dev(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 16));
+}
+
+// gfx950 LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane i of
+// the group receives element (i % 4) of the 64-bit words addressed by lanes (i / 4) + 4e of the
+// group, for e = 0..3.  So when lane s of a group addresses 4 consecutive bf16 of a row-major
+// tile at row R(s / 4), columns c0 + 4 (s % 4), lane i receives column c0 + i of rows
+// R(0..3): the MFMA operand layout of the transposed tile, with no scalar LDS reads.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t *p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
 // Order-preserving map of fp32 to uint32 (larger float -> larger key).
 __device__ __forceinline__ uint32_t float_order_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -130,6 +174,14 @@ hipError_t launch_attend_f32(const sas_problem &p, const SeqTable &st, const voi
                              const int64_t *gs, int32_t tq, int32_t sel_mode, const int32_t *idx,
                              const int32_t *nsel, const float *gate, int32_t kcap, float scale, void *O,
                              const int64_t *os, hipStream_t s);
+
+hipError_t launch_select_decode(const sas_problem &p, const SeqTable &st, const void *Q, const int64_t *qs,
+                                const void *reps, int32_t reps_kind, const int64_t *rs, int32_t sel_mode,
+                                float scale, float *scores, int64_t ld, const Budget &bg, int32_t kcap,
+                                int32_t *idx, int32_t *nsel, float *gate, uint32_t *counters, hipStream_t s);
+
+// Largest current-block index the fused decode selection handles (its scores stay in registers).
+constexpr int32_t SELECT_DECODE_MAX_C = 2048;
 
 // Bytes of split-K partials the decode path needs (host formula shared with the size query).
 size_t decode_workspace_bytes(const sas_problem &p, int32_t sel_mode, int32_t kcap, int32_t gist);

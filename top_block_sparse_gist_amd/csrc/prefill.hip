@@ -22,7 +22,7 @@
 
 namespace sas {
 
-static constexpr int KPAD = 8;  // LDS row padding (bf16 elements)
+static constexpr int KPAD = 16;  // LDS row padding (bf16 elements): rows start 8 banks apart
 
 __device__ __forceinline__ bf16x8 as_bf16x8p(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -208,19 +208,17 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(
       w[3] = pack_bf16x2(sacc[mt][r0p + 6], sacc[mt][r0p + 7]);
       preg[ks] = as_bf16x8p(w);
     }
-    // ---- O^T += V^T P^T; step ks holds keys 16ks + 4half + {0..3} and 16ks + 8 + 4half + {0..3}
+    // ---- O^T += V^T P^T; step ks holds keys 16ks + 4half + {0..3} and 16ks + 8 + 4half + {0..3};
+    //      the V^T operand (dim 32dt + col) comes from two transpose reads of the row-major tile
+    const int c16 = col & 15, chi = col >> 4;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const int dim = dt * 32 + col;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const int k0 = 16 * ks + 4 * half;
-        const uint16_t *vp = vlds + k0 * ROW + dim;
-        u32x4 w;
-        w[0] = (uint32_t)vp[0 * ROW] | ((uint32_t)vp[1 * ROW] << 16);
-        w[1] = (uint32_t)vp[2 * ROW] | ((uint32_t)vp[3 * ROW] << 16);
-        w[2] = (uint32_t)vp[8 * ROW] | ((uint32_t)vp[9 * ROW] << 16);
-        w[3] = (uint32_t)vp[10 * ROW] | ((uint32_t)vp[11 * ROW] << 16);
+        const uint16_t *src = vlds + (16 * ks + 4 * half + (c16 >> 2)) * ROW + dt * 32 + 16 * chi + 4 * (c16 & 3);
+        const u32x2 lo = lds_read_tr16(src);
+        const u32x2 hi = lds_read_tr16(src + 8 * ROW);
+        const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
         acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8p(w), preg[ks], acc_o[dt], 0, 0, 0);
       }
     }
