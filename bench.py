@@ -294,12 +294,15 @@ def main():
 
     # ---------------------------------------------------------------- headline: 32K decode
     w2 = Workload(2)
-    log("[bench] generating the 32K decode workload")
+    need_decode = bool(only & {"decode", "reps"}) or not args.no_cpu_baseline
+    if not need_decode:
+        log("[bench] skipping the 32K decode workload")
+    log("[bench] generating the 32K decode workload") if need_decode else None
     keep = {0, 1} if not args.no_cpu_baseline else set()
-    inp2 = upload(w2, list(range(w2.batch)), keep_host=keep)
-    fns, bufs = decode_step_setup(sas, w2, inp2)
+    inp2 = upload(w2, list(range(w2.batch)), keep_host=keep) if need_decode else None
+    fns, bufs = decode_step_setup(sas, w2, inp2) if need_decode else (None, None)
     torch.cuda.synchronize()
-    by = decode_bytes(w2, inp2, bufs)
+    by = decode_bytes(w2, inp2, bufs) if need_decode else None
     if "decode" in only:
         log("[bench] timing decode")
         ms, wall = timer.time(fns["step"], K_, W_)

@@ -61,6 +61,11 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
+    # a kernel whose host stub failed to emit leaves an undefined __device_stub__ symbol
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in nm.stdout.splitlines() if "__device_stub__" in l]
+    if missing:
+        raise RuntimeError("kernel host stubs missing from the link: " + ", ".join(missing))
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -56,17 +56,14 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
-// fp32 -> bf16 round-to-nearest-even (finite inputs; NaN stays NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
+// fp32 -> bf16 round-to-nearest-even: gfx950's v_cvt_pk_bf16_f32 (two values per instruction).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)(pack_bf16x2(f, 0.f) & 0xffffu); }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -121,6 +118,35 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t *p) {
   const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)p);
   return __builtin_bit_cast(u32x2, v);
+}
+
+// 16 bytes per lane straight from global memory into LDS (global_load_lds_dwordx4): the wave
+// writes 64 x 16 B contiguously at `lds`, lane l at lds + 16 l.  Completion is tracked by vmcnt.
+__device__ __forceinline__ void load_lds16(const void *g, void *lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
+// BYTES (1, 2, 4, 12 or 16) per lane from global memory into LDS (global_load_lds): the wave
+// writes 64 x BYTES contiguously at `lds`, lane l at lds + l * BYTES.  Tracked by vmcnt.
+template <int BYTES>
+__device__ __forceinline__ void load_lds(const void *g, void *lds) {
+  // the size operand must be a literal
+  auto *l = (__attribute__((address_space(3))) void *)lds;
+  if constexpr (BYTES == 2) __builtin_amdgcn_global_load_lds(g, l, 2, 0, 0);
+  else if constexpr (BYTES == 4) __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
+  else __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+}
+
+// BYTES per lane through a buffer resource into LDS (buffer_load ... lds): the wave writes
+// 64 x BYTES contiguously at `lds`; the lane reads rsrc + soff + voff.  Reads past the
+// resource's byte range return 0.  Row offsets stay scalar (soff), so the address needs no
+// per-lane arithmetic.  Tracked by vmcnt.
+template <int BYTES>
+__device__ __forceinline__ void buf_load_lds(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voff, uint32_t soff) {
+  auto *l = (__attribute__((address_space(3))) void *)lds;
+  if constexpr (BYTES == 2) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 2, voff, soff, 0, 0);
+  else if constexpr (BYTES == 4) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 4, voff, soff, 0, 0);
+  else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, voff, soff, 0, 0);
 }
 
 // Order-preserving map of fp32 to uint32 (larger float -> larger key).

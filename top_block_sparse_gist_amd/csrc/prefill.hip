@@ -18,30 +18,29 @@
 // Only the current block needs the causal mask.  Workgroups are numbered heavy-first (later
 // query blocks select more blocks) and packed per XCD so that the workgroups of one unit,
 // which share its K/V tiles, land on the same XCD's L2.
+#include <type_traits>
+
 #include "common.h"
 
 namespace sas {
 
-static constexpr int KPAD = 16;  // LDS row padding (bf16 elements): rows start 8 banks apart
-
 __device__ __forceinline__ bf16x8 as_bf16x8p(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(
+template <int D, int NW, int BLK>
+__global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
     SeqTable st, const uint16_t *__restrict__ Q, int64_t qb, int64_t qh, int64_t qt,
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, int64_t kb, int64_t kh, int64_t kt,
     int tq, int blk, int S, int QB, int G, int per_head, int batch, int rtiles,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ nsel, const float *__restrict__ gate,
     int kcap, float scale_log2, uint16_t *__restrict__ O, int64_t ob, int64_t oh, int64_t ot) {
-  constexpr int NT = NW * 64;
-  constexpr int ROW = D + KPAD;
   constexpr int NKK = D / 16;        // k-steps of S^T over the head dim
   constexpr int NDT = D / 32;        // 32-dim output tiles
-  constexpr int CH = D / 8;          // 16-byte chunks per K/V row
-  constexpr int LOADS = 64 * CH / NT;  // per lane, for each of K and V
-  static_assert((64 * CH) % NT == 0, "tile loads must divide evenly");
-  __shared__ __attribute__((aligned(16))) uint16_t klds[64 * ROW];
-  __shared__ __attribute__((aligned(16))) uint16_t vlds[64 * ROW];
+  // padded rows: K rows 4 banks apart (16-byte operand reads conflict-free), V rows 8 banks apart
+  // (8-byte transpose reads conflict-free)
+  constexpr int ROWK = D + 8, ROWV = D + 16;
+  constexpr int DMA = D * 2 / 64;    // bytes per lane of one row copy (a row = 64 lanes)
+  __shared__ __attribute__((aligned(16))) uint16_t klds2[2][64 * ROWK];
+  __shared__ __attribute__((aligned(16))) uint16_t vlds2[2][64 * ROWV];
 
   // ---- workgroup -> (query block i (heavy first), sequence, selector head, row tile)
   const int nwg = gridDim.x;
@@ -76,10 +75,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(
   if (r0 >= R) return;
   const int64_t u = ((int64_t)b * S + s) * QB + i;
   const int ns = nsel[u];
-  const int tpb = blk / 64;
+  constexpr int tpb = BLK / 64;
   const int ntiles = ns * tpb;
+  // the current block c is the last list entry: its tiles are the only ones needing the mask
+  const int nplain = ntiles - tpb;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps row offsets scalar
   const int col = lane & 31, half = lane >> 5;
 
   // ---- this lane's query row (column of S^T)
@@ -104,34 +106,28 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(
   const int32_t *ulist = idx + u * kcap;
   const float *glist = gate ? gate + u * kcap : nullptr;
 
-  u32x4 kst[LOADS], vst[LOADS];
-  auto load_tile = [&](int t) {
-    const int j = ulist[t / tpb];
-    const int key0 = j * blk + (t % tpb) * 64;
+  // Tile loads: one key row per instruction, HBM -> LDS directly (buffer_load ... lds, DMA
+  // bytes per lane).  The row offset and the LDS row address are wave-uniform (SGPR soffset
+  // and M0), so no per-lane address arithmetic is spent.  One buffer resource covers the K
+  // (V) slab of this (sequence, KV head); rows at or past L fall outside it and read as zero
+  // (those keys are masked anyway).
+  constexpr int RPW = 64 / NW;  // rows of a tile each wave copies
+  const uint32_t slab = (uint32_t)min((int64_t)L * kt * 2, (int64_t)0x7fffffff);
+  const __amdgpu_buffer_rsrc_t krs = dev_rsrc(kbase, slab), vrs = dev_rsrc(vbase, slab);
+  const uint32_t row_bytes = (uint32_t)(kt * 2);
+  auto load_tile = [&](int t, int buf) {
+    const int key0 = ulist[t / tpb] * BLK + (t % tpb) * 64;
+    uint32_t soff = (uint32_t)(key0 + wave) * row_bytes;
 #pragma unroll
-    for (int x = 0; x < LOADS; ++x) {
-      const int e = x * NT + tid;
-      const int key = e / CH, ch = e % CH;
-      const int pos = key0 + key;
-      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (pos < L) {
-        kv = *reinterpret_cast<const u32x4 *>(kbase + (int64_t)pos * kt + ch * 8);
-        vv = *reinterpret_cast<const u32x4 *>(vbase + (int64_t)pos * kt + ch * 8);
-      }
-      kst[x] = kv;
-      vst[x] = vv;
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int x = 0; x < LOADS; ++x) {
-      const int e = x * NT + tid;
-      const int key = e / CH, ch = e % CH;
-      *reinterpret_cast<u32x4 *>(klds + key * ROW + ch * 8) = kst[x];
-      *reinterpret_cast<u32x4 *>(vlds + key * ROW + ch * 8) = vst[x];
+    for (int x = 0; x < RPW; ++x) {
+      const int row = wave + x * NW;
+      buf_load_lds<DMA>(krs, &klds2[buf][row * ROWK], lane * DMA, soff);
+      buf_load_lds<DMA>(vrs, &vlds2[buf][row * ROWV], lane * DMA, soff);
+      soff += NW * row_bytes;
     }
   };
 
+  // running max (log2 units), running sum (this lane's half of the keys), O^T accumulators
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 acc_o[NDT];
 #pragma unroll
@@ -139,15 +135,12 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc_o[x][r] = 0.f;
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile();
-  }
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) load_tile(t + 1);
-    const int j = ulist[t / tpb];
-    const int key0 = j * blk + (t % tpb) * 64;
+  // one 64-key tile; DIAG: the current block (keys beyond the row's position masked)
+  auto tile = [&](int t, auto diag_tag) {
+    constexpr bool DIAG = decltype(diag_tag)::value;
+    const uint16_t *klds = klds2[t & 1];
+    const uint16_t *vlds = vlds2[t & 1];
+    const int key0 = ulist[t / tpb] * BLK + (t % tpb) * 64;
     const float gl2 = glist ? glist[t / tpb] * 1.4426950408889634f : 0.f;
     // ---- S^T = K Q^T (two 32-key halves)
     f32x16 sacc[2];
@@ -156,46 +149,52 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(
       f32x16 a;
 #pragma unroll
       for (int r = 0; r < 16; ++r) a[r] = 0.f;
-      const uint16_t *kr = klds + (mt * 32 + col) * ROW + 8 * half;
+      const uint16_t *kr = klds + (mt * 32 + col) * ROWK + 8 * half;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        u32x4 kv = *reinterpret_cast<const u32x4 *>(kr + 16 * kk);
+        const u32x4 kv = *reinterpret_cast<const u32x4 *>(kr + 16 * kk);
         a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8p(kv), qreg[kk], a, 0, 0, 0);
       }
       sacc[mt] = a;
     }
-    // ---- scale, gate, causal mask (current block only), online softmax
-    const bool diag = (j == c);
+    // ---- max over the raw scores (scale > 0 keeps the order), causal mask on the current block
     float mx = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        float v = sacc[mt][r] * scale_log2 + gl2;
-        if (diag && key0 + key > qpos) v = -INFINITY;
-        sacc[mt][r] = v;
-        mx = fmaxf(mx, v);
+        if constexpr (DIAG) {
+          const int key = mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (key0 + key > qpos) sacc[mt][r] = -INFINITY;
+        }
+        mx = fmaxf(mx, sacc[mt][r]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float mref = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - mref);
-    m_run = m_new;
+    const float m_tile = (mx == -INFINITY) ? -INFINITY : mx * scale_log2 + gl2;
+    // lazy rescale: keep the stale running max unless some column's max grows by more than 2^8,
+    // so that p = exp2(logit - m_run) stays <= 256 (exact in fp32, representable in bf16)
+    if (__ballot(m_tile > m_run + 8.f)) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int x = 0; x < NDT; ++x)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_o[x][r] *= alpha;
+    }
+    // p = exp2(scale_log2 * s + gate - m_run): one FMA and one exp2 per score
+    const float bias = gl2 - ((m_run == -INFINITY) ? 0.f : m_run);
     float ls = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = __builtin_amdgcn_exp2f(sacc[mt][r] - mref);
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[mt][r], scale_log2, bias));
         sacc[mt][r] = p;
         ls += p;
       }
-    l_run = l_run * alpha + ls;
-#pragma unroll
-    for (int x = 0; x < NDT; ++x)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc_o[x][r] *= alpha;
+    l_run += ls;
     // ---- P^T operands: 16-key step ks uses accumulator registers 8*(ks&1) .. +7 of half ks>>1
     bf16x8 preg[4];
 #pragma unroll
@@ -209,24 +208,38 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(
       preg[ks] = as_bf16x8p(w);
     }
     // ---- O^T += V^T P^T; step ks holds keys 16ks + 4half + {0..3} and 16ks + 8 + 4half + {0..3};
-    //      the V^T operand (dim 32dt + col) comes from two transpose reads of the row-major tile
+    //      the V^T operand (dim 32dt + col) comes from two transpose reads of the tile
     const int c16 = col & 15, chi = col >> 4;
+    const uint16_t *vb = vlds + (4 * half + (c16 >> 2)) * ROWV + 16 * chi + 4 * (c16 & 3);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const uint16_t *src = vlds + (16 * ks + 4 * half + (c16 >> 2)) * ROW + dt * 32 + 16 * chi + 4 * (c16 & 3);
+        const uint16_t *src = vb + 16 * ks * ROWV + dt * 32;
         const u32x2 lo = lds_read_tr16(src);
-        const u32x2 hi = lds_read_tr16(src + 8 * ROW);
+        const u32x2 hi = lds_read_tr16(src + 8 * ROWV);
         const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
         acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8p(w), preg[ks], acc_o[dt], 0, 0, 0);
       }
     }
+  };
+
+  if (ntiles > 0) load_tile(0, 0);
+  wait_stores();  // vmcnt(0): this wave's loads (Q, tile 0) have landed
+  __syncthreads();
+  // tile t+1 streams into the other buffer while tile t is computed; that buffer was last read
+  // in iteration t-1, which every wave finished before the barrier that closed it
+  for (int t = 0; t < nplain; ++t) {
+    load_tile(t + 1, (t + 1) & 1);
+    tile(t, std::integral_constant<bool, false>{});
+    wait_stores();
     __syncthreads();
-    if (t + 1 < ntiles) {
-      store_tile();
-      __syncthreads();
-    }
+  }
+  for (int t = max(nplain, 0); t < ntiles; ++t) {
+    if (t + 1 < ntiles) load_tile(t + 1, (t + 1) & 1);
+    tile(t, std::integral_constant<bool, true>{});
+    wait_stores();
+    __syncthreads();
   }
   // ---- normalise and write O (lane holds dims 32dt + 8(r/4) + 4half + r%4 of its query)
   l_run += __shfl_xor(l_run, 32, 64);
@@ -245,7 +258,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(
     }
 }
 
-template <int D, int NW>
+template <int D, int NW, int BLK>
 static hipError_t prefill_dispatch(const sas_problem &p, const SeqTable &st, const void *Q, const int64_t *qs,
                                    const void *K, const void *V, const int64_t *kvs, int32_t tq,
                                    int32_t sel_mode, const int32_t *idx, const int32_t *nsel,
@@ -260,7 +273,7 @@ static hipError_t prefill_dispatch(const sas_problem &p, const SeqTable &st, con
   const int rtiles = cdiv(rows_max * nh, NW * 32);
   const int64_t nwg = (int64_t)QB * p.batch * S * rtiles;
   const float scale_log2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, NW>), dim3((unsigned)nwg), dim3(NW * 64), 0, s, st,
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, BLK>), dim3((unsigned)nwg), dim3(NW * 64), 0, s, st,
                      (const uint16_t *)Q, qs[0], qs[1], qs[2], (const uint16_t *)K, (const uint16_t *)V, kvs[0],
                      kvs[1], kvs[2], tq, p.block, S, QB, G, per_head, p.batch, rtiles, idx, nsel, gate, kcap,
                      scale_log2, (uint16_t *)O, os[0], os[1], os[2]);
@@ -275,11 +288,19 @@ hipError_t launch_prefill_bf16(const sas_problem &p, const SeqTable &st, const v
   // rows per unit: blk (x G when the group shares one list); 2 waves cover a 64-row unit
   const int nh = sel_mode == SAS_SEL_HEAD ? 1 : p.hq / p.hkv;
   const bool small = std::min(tq, p.block) * nh <= 64;
-  if (p.head_dim == 128)
-    return small ? prefill_dispatch<128, 2>(p, st, Q, qs, K, V, kvs, tq, sel_mode, idx, nsel, gate, kcap, scale, O, os, s)
-                 : prefill_dispatch<128, 4>(p, st, Q, qs, K, V, kvs, tq, sel_mode, idx, nsel, gate, kcap, scale, O, os, s);
-  return small ? prefill_dispatch<64, 2>(p, st, Q, qs, K, V, kvs, tq, sel_mode, idx, nsel, gate, kcap, scale, O, os, s)
-               : prefill_dispatch<64, 4>(p, st, Q, qs, K, V, kvs, tq, sel_mode, idx, nsel, gate, kcap, scale, O, os, s);
+#define SAS_PF(D_, NW_, B_) \
+  return prefill_dispatch<D_, NW_, B_>(p, st, Q, qs, K, V, kvs, tq, sel_mode, idx, nsel, gate, kcap, scale, O, os, s)
+#define SAS_PF_NW(D_, B_) \
+  if (small) SAS_PF(D_, 2, B_);  \
+  SAS_PF(D_, 4, B_)
+  if (p.head_dim == 128) {
+    if (p.block == 64) { SAS_PF_NW(128, 64); }
+    SAS_PF_NW(128, 128);
+  }
+  if (p.block == 64) { SAS_PF_NW(64, 64); }
+  SAS_PF_NW(64, 128);
+#undef SAS_PF_NW
+#undef SAS_PF
 }
 
 }  // namespace sas
