@@ -141,7 +141,9 @@ sas_status sas_topk_select(const sas_problem *p, const float *scores, int64_t sc
  *   O[b, h, t] = softmax_s(scale * q . k_s + gate_u(block(s))) v_s over keys s of the
  *   unit's selected blocks with s <= q_start[b] + t.
  *   Q, O: [B, Hq, T, d] (q_stride, o_stride = {batch, head, row}); K, V: kv_stride.
- *   gate: [units, kcap] or NULL for no gate.  scale: > 0 or 0 for 1/sqrt(d). */
+ *   gate: [units, kcap] or NULL for no gate.  scale: > 0 or 0 for 1/sqrt(d).
+ *   bf16: the K/V rows of one (sequence, KV head) must span less than 4 GiB
+ *   ((max_len - 1) * row stride + d elements), else SAS_ERR_UNSUPPORTED. */
 sas_status sas_sparse_prefill(const sas_problem *p, const void *Q, const int64_t q_stride[3],
                               const void *K, const void *V, const int64_t kv_stride[3],
                               int32_t tq, const int32_t *q_start, int32_t sel_mode,

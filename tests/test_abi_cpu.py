@@ -139,6 +139,10 @@ def test_attention_validation_codes():
     qs0 = _lib.i32x([0, 0])
     assert lib.sas_sparse_prefill(C.byref(p), FAKE, bad, FAKE, FAKE, kvs, 100, qs0, 0, FAKE, FAKE, None, 8, 0.0,
                                   FAKE, qs3, None) == _lib.SAS_ERR_SHAPE
+    # bf16 K/V slab of one (sequence, KV head) beyond 32-bit byte offsets: 1000 rows at a 2^22-element stride
+    huge = _lib.i64x([1 << 40, 1 << 32, 1 << 22])
+    assert lib.sas_sparse_prefill(C.byref(p), FAKE, qs3, FAKE, FAKE, huge, 100, qs0, 0, FAKE, FAKE, None, 8, 0.0,
+                                  FAKE, qs3, None) == _lib.SAS_ERR_UNSUPPORTED
     # decode: gist with a gate is not defined; half a gist pair is an error; workspace too small
     gs = _lib.i64x([2 * 15 * 128, 15 * 128, 128])
     assert lib.sas_sparse_decode(C.byref(p), FAKE, qs2, FAKE, FAKE, kvs, FAKE, FAKE, gs, 0, FAKE, FAKE, FAKE, 8, 0.0,

@@ -235,6 +235,9 @@ sas_status sas_sparse_prefill(const sas_problem *p, const void *Q, const int64_t
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !strides_ok(q_stride, 3, eb) ||
       !strides_ok(kv_stride, 3, eb) || !strides_ok(o_stride, 3, eb))
     return fail(SAS_ERR_SHAPE, "Q/K/V/O must be 16-byte aligned with 16-byte-multiple row strides");
+  // the bf16 kernel addresses one (sequence, KV head) K/V slab with 32-bit byte offsets
+  if (p->dtype == SAS_BF16 && (int64_t)(p->max_len - 1) * kv_stride[2] * eb + (int64_t)p->head_dim * eb > 0xFFFFFFFFll)
+    return fail(SAS_ERR_UNSUPPORTED, "one (sequence, KV head) K/V slab must span less than 4 GiB");
   const float sc = resolve_scale(scale, p->head_dim);
   const hipStream_t s = (hipStream_t)stream;
   if (p->dtype == SAS_BF16)

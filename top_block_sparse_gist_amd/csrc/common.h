@@ -23,6 +23,7 @@ struct Budget {
 // host + device helpers
 // ---------------------------------------------------------------------------------------
 __host__ __device__ inline int32_t cdiv(int32_t a, int32_t b) { return (a + b - 1) / b; }
+__host__ __device__ inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // ceil((tq-1)/blk) + 1: blocks that tq consecutive positions can touch.
 __host__ __device__ inline int32_t num_qblocks(int32_t tq, int32_t blk) {

@@ -6,18 +6,22 @@
 //
 // A workgroup owns NW*32 query rows of one selection unit (rows x heads of the unit,
 // flattened) and walks the unit's selected blocks in 64-key tiles:
-//   K and V tiles go HBM -> registers -> LDS; the next tile's loads are issued before the
-//   current tile is computed (register double buffering), so HBM latency overlaps MFMA work.
+//   K and V tiles are copied HBM -> LDS by the buffer unit (buffer_load ... lds, one key row
+//   per instruction, into padded rows) into a double buffer: tile t+1 is in flight while
+//   tile t is computed, and one barrier per tile hands the buffers over.
 //   S^T = K Q^T : v_mfma_f32_32x32x16_bf16, M = 32 keys, N = 32 query rows of the wave,
 //                 K = 16 dims; Q^T stays in registers for the whole walk.
 //   online softmax per query column (exp2 domain): the column's 64 logits sit in 32 VGPRs of
-//                 the lane and 32 of the lane 32 apart, so the row max is one cross-half swap.
+//                 the lane and 32 of the lane 32 apart, so the row max is one cross-half swap;
+//                 max on the raw scores, then one FMA (scale, gate, running max) and one exp2
+//                 per score; the accumulator is rescaled only when a column's max grows by
+//                 more than 2^8.
 //   O^T += V^T P^T : same MFMA, M = 32 dims, K = 16 keys; P^T is taken straight from the
-//                 S^T accumulator (keys in accumulator order), V^T is gathered from the LDS
-//                 tile in that same key order.
-// Only the current block needs the causal mask.  Workgroups are numbered heavy-first (later
-// query blocks select more blocks) and packed per XCD so that the workgroups of one unit,
-// which share its K/V tiles, land on the same XCD's L2.
+//                 S^T accumulator (keys in accumulator order), V^T is read from the LDS tile
+//                 in that same key order with transposing reads (ds_read_b64_tr_b16).
+// Only the current block needs the causal mask.  Units are taken heavy-first (later query
+// blocks select more blocks) and dealt round-robin to the XCDs; the row tiles of one unit,
+// which share its K/V tiles, run on the same XCD (one L2).
 #include <type_traits>
 
 #include "common.h"
@@ -35,25 +39,24 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
     int kcap, float scale_log2, uint16_t *__restrict__ O, int64_t ob, int64_t oh, int64_t ot) {
   constexpr int NKK = D / 16;        // k-steps of S^T over the head dim
   constexpr int NDT = D / 32;        // 32-dim output tiles
-  // padded rows: K rows 4 banks apart (16-byte operand reads conflict-free), V rows 8 banks apart
-  // (8-byte transpose reads conflict-free)
-  constexpr int ROWK = D + 8, ROWV = D + 16;
+  // padded rows (64 LDS banks of 4 bytes): K rows 4 banks apart mod 64, so the 16 lanes of a
+  // 16-byte operand read cover all banks; V rows 16 (D 128) or 48 (D 64) banks apart mod 64, so
+  // the 32 lanes of an 8-byte transposing read (4 rows x 2 column halves x 4 columns) do too
+  constexpr int ROWK = D + 8, ROWV = D + 32;
   constexpr int DMA = D * 2 / 64;    // bytes per lane of one row copy (a row = 64 lanes)
   __shared__ __attribute__((aligned(16))) uint16_t klds2[2][64 * ROWK];
   __shared__ __attribute__((aligned(16))) uint16_t vlds2[2][64 * ROWV];
 
   // ---- workgroup -> (query block i (heavy first), sequence, selector head, row tile)
-  const int nwg = gridDim.x;
-  int logical;
-  {
-    const int k = blockIdx.x, x = k & 7, q = k >> 3;
-    int r = nwg & 7, per = nwg >> 3;
-    if (r == 0) { r = 8; per -= 1; }
-    // XCD x holds per + (x < r) consecutive logical workgroups
-    logical = x * per + min(x, r) + q;
-  }
-  const int rt = logical % rtiles;
-  int rest = logical / rtiles;
+  // Workgroup k runs on XCD k % 8.  Units (in heavy-first order) are dealt round-robin to the
+  // XCDs, and all row tiles of a unit go to the same XCD, one after another, so they share the
+  // unit's K/V tiles in that XCD's L2 and every XCD gets an even share of heavy and light units.
+  // The grid holds 8 * ceil(units / 8) * rtiles workgroups; slots past the last unit exit.
+  const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+  const int slot = (q / rtiles) * 8 + xcd;
+  const int rt = q % rtiles;
+  if (slot >= QB * batch * S) return;
+  int rest = slot;
   const int s = rest % S;
   rest /= S;
   const int b = rest % batch;
@@ -108,22 +111,22 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
 
   // Tile loads: one key row per instruction, HBM -> LDS directly (buffer_load ... lds, DMA
   // bytes per lane).  The row offset and the LDS row address are wave-uniform (SGPR soffset
-  // and M0), so no per-lane address arithmetic is spent.  One buffer resource covers the K
-  // (V) slab of this (sequence, KV head); rows at or past L fall outside it and read as zero
-  // (those keys are masked anyway).
+  // and M0), so no per-lane address arithmetic is spent.  One buffer resource spans the K (V)
+  // slab of this (sequence, KV head) (the host checks that it fits 32-bit offsets).  Rows at
+  // or past L (the tail of a partial last block) re-read row L-1: in bounds and finite, and
+  // those keys are masked, so their p is exactly 0.
   constexpr int RPW = 64 / NW;  // rows of a tile each wave copies
-  const uint32_t slab = (uint32_t)min((int64_t)L * kt * 2, (int64_t)0x7fffffff);
-  const __amdgpu_buffer_rsrc_t krs = dev_rsrc(kbase, slab), vrs = dev_rsrc(vbase, slab);
   const uint32_t row_bytes = (uint32_t)(kt * 2);
+  const uint32_t slab = (uint32_t)(L - 1) * row_bytes + D * 2;
+  const __amdgpu_buffer_rsrc_t krs = dev_rsrc(kbase, slab), vrs = dev_rsrc(vbase, slab);
   auto load_tile = [&](int t, int buf) {
     const int key0 = ulist[t / tpb] * BLK + (t % tpb) * 64;
-    uint32_t soff = (uint32_t)(key0 + wave) * row_bytes;
 #pragma unroll
     for (int x = 0; x < RPW; ++x) {
       const int row = wave + x * NW;
+      const uint32_t soff = (uint32_t)min(key0 + row, L - 1) * row_bytes;
       buf_load_lds<DMA>(krs, &klds2[buf][row * ROWK], lane * DMA, soff);
       buf_load_lds<DMA>(vrs, &vlds2[buf][row * ROWV], lane * DMA, soff);
-      soff += NW * row_bytes;
     }
   };
 
@@ -271,7 +274,8 @@ static hipError_t prefill_dispatch(const sas_problem &p, const SeqTable &st, con
   const int nh = per_head ? 1 : G;
   const int rows_max = min(tq, p.block);
   const int rtiles = cdiv(rows_max * nh, NW * 32);
-  const int64_t nwg = (int64_t)QB * p.batch * S * rtiles;
+  const int64_t units = (int64_t)QB * p.batch * S;
+  const int64_t nwg = 8 * cdiv64(units, 8) * rtiles;
   const float scale_log2 = scale * 1.4426950408889634f;
   hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, BLK>), dim3((unsigned)nwg), dim3(NW * 64), 0, s, st,
                      (const uint16_t *)Q, qs[0], qs[1], qs[2], (const uint16_t *)K, (const uint16_t *)V, kvs[0],
