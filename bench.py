@@ -68,8 +68,9 @@ class Timer:
         return g
 
     def time(self, fn, steps, warmup, use_graph=False):
-        """Mean device ms of fn over `steps` calls, and the wall seconds of the whole timed loop
-        (flushes included).
+        """Median device ms of fn over `steps` calls, and the wall seconds of the whole timed loop
+        (flushes included).  The median keeps a rare host-side stall (which lets the GPU run
+        dry inside one interval) out of the figure.
 
         Each call is bracketed by two events on the current stream (the stream the library
         launches on).  The call is queued behind the ~270 us flush, so host launch latency is
@@ -98,7 +99,10 @@ class Timer:
             evs.append((a, b))
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        return sum(a.elapsed_time(b) for a, b in evs) / len(evs), wall
+        ts = sorted(a.elapsed_time(b) for a, b in evs)
+        n = len(ts)
+        med = ts[n // 2] if n % 2 else 0.5 * (ts[n // 2 - 1] + ts[n // 2])
+        return med, wall
 
 
 # ------------------------------------------------------------------------------------------------

@@ -90,6 +90,12 @@ __device__ __forceinline__ float load_dev(const float *p) {
   return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
+// s_waitcnt vmcnt(N) (N < 64; the count is split over bits 3:0 and 15:14), other counters free
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 // 16-byte device-coherent accesses through a raw buffer resource (aux 16 = sc1).  Accesses
 // past `bytes` read 0 / are dropped by the hardware range check.
