@@ -7,8 +7,10 @@
 // A workgroup owns NW*32 query rows of one selection unit (rows x heads of the unit,
 // flattened) and walks the unit's selected blocks in 64-key tiles:
 //   K and V tiles are copied HBM -> LDS by the buffer unit (buffer_load ... lds, one key row
-//   per instruction, into padded rows) into a double buffer: tile t+1 is in flight while
-//   tile t is computed, and one barrier per tile hands the buffers over.
+//   per instruction, into padded rows).  128-row workgroups double-buffer: tile t+1 is in
+//   flight while tile t is computed, and one barrier per tile hands the buffers over.  64-row
+//   workgroups keep one K and one V buffer, so that twice as many fit per CU; their copies
+//   overlap the phases of a tile that do not read that buffer.
 //   S^T = K Q^T : v_mfma_f32_32x32x16_bf16, M = 32 keys, N = 32 query rows of the wave,
 //                 K = 16 dims; Q^T stays in registers for the whole walk.
 //   online softmax per query column (exp2 domain): the column's 64 logits sit in 32 VGPRs of
@@ -33,7 +35,7 @@ __device__ __forceinline__ bf16x8 as_bf16x8p(u32x4 v) { return __builtin_bit_cas
 // NW = 4: 128 rows per workgroup, K/V double buffered (2 workgroups per CU).
 // NW = 2: 64 rows per workgroup (one 64-row unit), single K and V buffers (4 workgroups per CU,
 //         so 2 waves per SIMD as well): K of tile t+1 is copied during the softmax and PV of tile
-//         t, V of tile t+1 during the S and softmax of tile t+1.
+//         t, V of tile t+1 during the S phase and softmax of tile t+1.
 template <int D, int NW, int BLK>
 __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
     SeqTable st, const uint16_t *__restrict__ Q, int64_t qb, int64_t qh, int64_t qt,
@@ -49,13 +51,9 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
   constexpr int ROWK = D + 8, ROWV = D + 32;
   constexpr int DMA = D * 2 / 64;    // bytes per lane of one row copy (a row = 64 lanes)
   constexpr bool SINGLE = NW == 2;   // single-buffered K and V
-  // The buffers are distinct arrays and every use names its array statically: the compiler can
-  // then tell that the tile being read and the tile in flight are different memory, and does not
-  // wait for the copies in flight before reading.
-  __shared__ __attribute__((aligned(16))) uint16_t kA[64 * ROWK];
-  __shared__ __attribute__((aligned(16))) uint16_t kB[SINGLE ? 8 : 64 * ROWK];
-  __shared__ __attribute__((aligned(16))) uint16_t vA[64 * ROWV];
-  __shared__ __attribute__((aligned(16))) uint16_t vB[SINGLE ? 8 : 64 * ROWV];
+  constexpr int NBUF = SINGLE ? 1 : 2;
+  __shared__ __attribute__((aligned(16))) uint16_t klds2[NBUF][64 * ROWK];
+  __shared__ __attribute__((aligned(16))) uint16_t vlds2[NBUF][64 * ROWV];
 
   // ---- workgroup -> (query block i (heavy first), sequence, selector head, row tile)
   // Workgroup k runs on XCD k % 8.  Units (in heavy-first order) are dealt round-robin to the
@@ -129,15 +127,15 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
   const uint32_t row_bytes = (uint32_t)(kt * 2);
   const uint32_t slab = (uint32_t)(L - 1) * row_bytes + D * 2;
   const __amdgpu_buffer_rsrc_t krs = dev_rsrc(kbase, slab), vrs = dev_rsrc(vbase, slab);
-  // copy tile t's rows of K (if kdst) and V (if vdst)
-  auto load_tile = [&](int t, uint16_t *kdst, uint16_t *vdst) __attribute__((always_inline)) {
+  // copy tile t's rows of K and / or V into buffer buf
+  auto load_tile = [&](int t, int buf, bool k, bool v) {
     const int key0 = ulist[t / tpb] * BLK + (t % tpb) * 64;
 #pragma unroll
     for (int x = 0; x < RPW; ++x) {
       const int row = wave + x * NW;
       const uint32_t soff = (uint32_t)min(key0 + row, L - 1) * row_bytes;
-      if (kdst) buf_load_lds<DMA>(krs, kdst + row * ROWK, lane * DMA, soff);
-      if (vdst) buf_load_lds<DMA>(vrs, vdst + row * ROWV, lane * DMA, soff);
+      if (k) buf_load_lds<DMA>(krs, &klds2[buf][row * ROWK], lane * DMA, soff);
+      if (v) buf_load_lds<DMA>(vrs, &vlds2[buf][row * ROWV], lane * DMA, soff);
     }
   };
 
@@ -149,53 +147,33 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc_o[x][r] = 0.f;
 
-  // One 64-key tile t, read from klds / vlds; with `pre`, the copies of tile t+1 into kdst / vdst
-  // are issued first.  DIAG: the current block (keys beyond the row's position masked).
-  auto tile = [&](int t, auto diag_tag, bool pre, const uint16_t *klds, const uint16_t *vlds, uint16_t *kdst,
-                  uint16_t *vdst) __attribute__((always_inline)) {
+  // one 64-key tile; DIAG: the current block (keys beyond the row's position masked)
+  auto tile = [&](int t, auto diag_tag) {
     constexpr bool DIAG = decltype(diag_tag)::value;
-    if constexpr (!SINGLE) {
-      if (pre) load_tile(t + 1, kdst, vdst);
-    }
+    const uint16_t *klds = klds2[SINGLE ? 0 : (t & 1)];
+    const uint16_t *vlds = vlds2[SINGLE ? 0 : (t & 1)];
     const int key0 = ulist[t / tpb] * BLK + (t % tpb) * 64;
     const float gl2 = glist ? glist[t / tpb] * 1.4426950408889634f : 0.f;
-    // ---- S^T = K Q^T (two 32-key halves, alternating so that consecutive MFMAs are independent);
-    //      the operands of step kk+1 are read while the MFMAs of step kk run
+    // ---- S^T = K Q^T (two 32-key halves)
     f32x16 sacc[2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 2; ++mt) {
+      f32x16 a;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.f;
-    {
-      const uint16_t *kr = klds + col * ROWK + 8 * half;
-      u32x4 kf[2][2];  // [step parity][half]: fully unrolled, so the parity index is static
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) kf[0][mt] = *reinterpret_cast<const u32x4 *>(kr + mt * 32 * ROWK);
+      for (int r = 0; r < 16; ++r) a[r] = 0.f;
+      const uint16_t *kr = klds + (mt * 32 + col) * ROWK + 8 * half;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        if (kk + 1 < NKK) {
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-            kf[(kk + 1) & 1][mt] = *reinterpret_cast<const u32x4 *>(kr + mt * 32 * ROWK + 16 * (kk + 1));
-        }
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-          sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8p(kf[kk & 1][mt]), qreg[kk], sacc[mt], 0, 0, 0);
+        const u32x4 kv = *reinterpret_cast<const u32x4 *>(kr + 16 * kk);
+        a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8p(kv), qreg[kk], a, 0, 0, 0);
       }
-      // issue order: 2 reads, then (2 reads, 2 MFMAs) per step, then the last 2 MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-      for (int kk = 0; kk + 1 < NKK; ++kk) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      sacc[mt] = a;
     }
     if constexpr (SINGLE) {
       // every wave has read K of tile t: its buffer takes tile t+1 (on the last tile, tile t
       // again: unconditional copies keep the wait counts static; nobody reads that copy)
       __syncthreads();
-      load_tile(min(t + 1, ntiles - 1), kA, nullptr);
+      load_tile(min(t + 1, ntiles - 1), 0, true, false);
     }
     // ---- max over the raw scores (scale > 0 keeps the order), causal mask on the current block
     float mx = -INFINITY;
@@ -254,79 +232,49 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
     }
     // ---- O^T += V^T P^T; step ks holds keys 16ks + 4half + {0..3} and 16ks + 8 + 4half + {0..3};
     //      the V^T operand (dim 32dt + col) comes from two transpose reads of the tile
-    //      key-step-major, so consecutive MFMAs go to different output tiles; the V^T operands of
-    //      step ks+1 are read while the MFMAs of step ks run
     const int c16 = col & 15, chi = col >> 4;
     const uint16_t *vb = vlds + (4 * half + (c16 >> 2)) * ROWV + 16 * chi + 4 * (c16 & 3);
-    auto read_v = [&](int ks, u32x4 *w) __attribute__((always_inline)) {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
+    for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
         const uint16_t *src = vb + 16 * ks * ROWV + dt * 32;
         const u32x2 lo = lds_read_tr16(src);
         const u32x2 hi = lds_read_tr16(src + 8 * ROWV);
-        w[dt] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+        acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8p(w), preg[ks], acc_o[dt], 0, 0, 0);
       }
-    };
-    {
-      u32x4 vf[2][NDT];  // [step parity][output tile]
-      read_v(0, vf[0]);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        if (ks + 1 < 4) read_v(ks + 1, vf[(ks + 1) & 1]);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-          acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8p(vf[ks & 1][dt]), preg[ks], acc_o[dt], 0, 0, 0);
-      }
-      // issue order: the reads of step 0, then (reads of ks+1, MFMAs of ks), then the last MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * NDT, 0);
-#pragma unroll
-      for (int ks = 0; ks < 3; ++ks) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * NDT, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, NDT, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, NDT, 0);
     }
   };
 
-  if (ntiles > 0) load_tile(0, kA, vA);
+  if (ntiles > 0) load_tile(0, 0, true, true);
   wait_stores();  // vmcnt(0): this wave's loads (Q, tile 0) have landed
   __syncthreads();
-  // Tile t+1 streams into the other buffer while tile t is computed; that buffer was last read in
-  // iteration t-1, which every wave finished before the barrier that closed it.  The walk is
-  // unrolled by two (one tile from each buffer per iteration) so that both buffers are named
-  // statically and the accumulators stay in the same registers on every path.
-  auto walk = [&](int t0, int t1, auto diag_tag, auto start_b) __attribute__((always_inline)) {
-    constexpr bool SB = decltype(start_b)::value;
-    uint16_t *k0 = SB ? kB : kA, *v0 = SB ? vB : vA, *k1 = SB ? kA : kB, *v1 = SB ? vA : vB;
-    for (int t = t0; t < t1; t += 2) {
-      tile(t, diag_tag, t + 1 < ntiles, k0, v0, k1, v1);
+  if constexpr (SINGLE) {
+    // one buffer each: after tile t, K of tile t+1 has landed and V of tile t is no longer read
+    for (int t = 0; t < ntiles; ++t) {
+      if (t < nplain) tile(t, std::integral_constant<bool, false>{});
+      else tile(t, std::integral_constant<bool, true>{});
       wait_stores();
       __syncthreads();
-      if (t + 1 >= t1) break;
-      tile(t + 1, diag_tag, t + 2 < ntiles, k1, v1, k0, v0);
+      load_tile(min(t + 1, ntiles - 1), 0, false, true);
+    }
+    wait_stores();  // no copy into LDS may outlive the workgroup
+  } else {
+    // tile t+1 streams into the other buffer while tile t is computed; that buffer was last read
+    // in iteration t-1, which every wave finished before the barrier that closed it
+    for (int t = 0; t < nplain; ++t) {
+      load_tile(t + 1, (t + 1) & 1, true, true);
+      tile(t, std::integral_constant<bool, false>{});
       wait_stores();
       __syncthreads();
     }
-  };
-  const std::integral_constant<bool, false> plain, in_a;
-  const std::integral_constant<bool, true> diag, in_b;
-  if constexpr (SINGLE) {
-    // one buffer each: after tile t, K of tile t+1 has landed and V of tile t is no longer read
-    auto walk1 = [&](int t0, int t1, auto diag_tag) __attribute__((always_inline)) {
-      for (int t = t0; t < t1; ++t) {
-        tile(t, diag_tag, true, kA, vA, kA, vA);
-        wait_stores();
-        __syncthreads();
-        load_tile(min(t + 1, ntiles - 1), nullptr, vA);
-      }
-    };
-    walk1(0, nplain, plain);
-    walk1(max(nplain, 0), ntiles, diag);
-    wait_stores();  // no copy into LDS may outlive the workgroup
-  } else {
-    walk(0, nplain, plain, in_a);  // tile 0 is in A
-    if (max(nplain, 0) & 1) walk(max(nplain, 0), ntiles, diag, in_b);
-    else walk(max(nplain, 0), ntiles, diag, in_a);
+    for (int t = max(nplain, 0); t < ntiles; ++t) {
+      if (t + 1 < ntiles) load_tile(t + 1, (t + 1) & 1, true, true);
+      tile(t, std::integral_constant<bool, true>{});
+      wait_stores();
+      __syncthreads();
+    }
   }
   // ---- normalise and write O (lane holds dims 32dt + 8(r/4) + 4half + r%4 of its query)
   l_run += __shfl_xor(l_run, 32, 64);
