@@ -187,3 +187,44 @@ def test_c5_prefill_half_full_sampled():
 def test_c5_decode_half_full_sampled():
     w = Workload(5)
     run_case(w, w.decode_seqs(), unit_sample=32, seed=6)
+
+
+# ------------------------------------------------------------------------------ exact ties
+@pytest.mark.parametrize("lens", [[64 * 40 + 5, 64 * 34], [64 * 700 + 9, 64 * 40 + 1]], ids=["c_le_512", "c_gt_512"])
+def test_exact_ties_go_to_the_lower_block(lens):
+    """Blocks repeat with period 4, so their representatives, and hence their scores, are equal
+    bit for bit: the lists (both selection paths) must be the oracle's, lowest indices first."""
+    from oracle import sas_oracle as orc
+    from workloads.gen import round_bf16
+    B, hq, hkv, d, blk, k = len(lens), 8, 2, 128, 64, 6
+    rng = np.random.default_rng(11)
+    Lmax = max(lens)
+    base = round_bf16(rng.standard_normal((hkv, 4, blk, d), dtype=np.float32))
+    K = np.zeros((B, hkv, Lmax, d), dtype=np.float32)
+    for b, L in enumerate(lens):
+        for j in range(-(-L // blk)):
+            n = min(blk, L - j * blk)
+            K[b, :, j * blk:j * blk + n] = base[:, j % 4, :n]
+    V = round_bf16(rng.standard_normal((B, hkv, Lmax, d), dtype=np.float32))
+    Q = round_bf16(rng.standard_normal((B, hq, d), dtype=np.float32))
+    Kd = torch.from_numpy(K).to(torch.bfloat16).cuda()
+    Qd = torch.from_numpy(Q).to(torch.bfloat16).cuda()
+    bud = sas.Budget(k_fixed=k)
+    reps = sas.block_reps(Kd, lens, blk)
+    sc = sas.block_scores(Qd, reps, lens, blk, hkv, Lmax)
+    idx, nsel, _ = sas.topk_select(sc, lens, blk, hq, hkv, d, sas.SAS_BF16, Lmax, bud)
+    _, idx2, nsel2, _ = sas.select_decode(Qd, reps, lens, blk, hkv, Lmax, bud, kcap=idx.shape[1])
+    torch.cuda.synchronize()
+    idx_h, nsel_h = idx.cpu().numpy(), nsel.cpu().numpy()
+    assert torch.equal(idx, idx2) and torch.equal(nsel, nsel2), "fused selection differs from the two-call path"
+    ties = 0
+    for b, L in enumerate(lens):
+        r = orc.run_sequence(Q[b][:, None, :], K[b], V[b], L, L - 1, blk, "group", k_fixed=k, attend=False)
+        for un in r.units:
+            u = b * hkv + un.sel_head
+            got = [int(x) for x in idx_h[u, :nsel_h[u]]]
+            assert got == list(un.sel), f"sequence {b}, KV head {un.sel_head}: {got} != {list(un.sel)}"
+            s = np.sort(un.scores[:un.c])[::-1]
+            ties += int(s[k - 1] == s[k])
+    say(f"[ties] {ties} of {B * hkv} units have the k-th and (k+1)-th scores exactly equal")
+    assert ties == B * hkv

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 #include "../../include/sas.h"
 
@@ -154,6 +155,24 @@ __device__ __forceinline__ void buf_load_lds(__amdgpu_buffer_rsrc_t r, void *lds
   if constexpr (BYTES == 2) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 2, voff, soff, 0, 0);
   else if constexpr (BYTES == 4) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 4, voff, soff, 0, 0);
   else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, voff, soff, 0, 0);
+}
+
+// Sum over aligned groups of W lanes (W = 8, 16 or 32), valid in the group's first lane (lane %
+// W == 0).  Within a 16-lane row the adds use DPP (quad xor 1, quad xor 2, row rotate 4, row
+// rotate 8: no LDS round trip); W = 32 adds the other row with one cross-lane read.  The order of
+// the adds is fixed, so every kernel that uses it gets the same bits for the same inputs.
+template <int W>
+__device__ __forceinline__ float group_sum(float s) {
+  static_assert(W == 8 || W == 16 || W == 32, "group of 8, 16 or 32 lanes");
+  auto dpp = [](float v, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value, 0xF, 0xF, false));
+  };
+  s += dpp(s, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]: lane ^ 1
+  s += dpp(s, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]: lane ^ 2
+  s += dpp(s, std::integral_constant<int, 0x124>{});  // row_ror:4: quads q and q+1
+  if constexpr (W >= 16) s += dpp(s, std::integral_constant<int, 0x128>{});  // row_ror:8: whole row
+  if constexpr (W == 32) s += __shfl_xor(s, 16, 64);
+  return s;
 }
 
 // Order-preserving map of fp32 to uint32 (larger float -> larger key).

@@ -261,8 +261,7 @@ __global__ __launch_bounds__(256) void score_decode_kernel(SeqTable st, const T 
       float part = 0.f;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) part = fmaf(qs[u][cc * VEC + e], rv[e], part);
-#pragma unroll
-      for (int o = TPR / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
+      part = group_sum<TPR>(part);
       if (cc == 0 && j <= c) {
         int s = per_head ? g * G + u : g;
         scores[((int64_t)b * S + s) * ld + j] = (j < nrep) ? part * scale : -INFINITY;

@@ -40,58 +40,79 @@ __device__ void wave_topk(const float *__restrict__ row, int c, bool sinkf, cons
   uint32_t T = 0u, want = 0u;
   bool all = k >= ncand;
   if (!all && k > 0) {
-    uint32_t prefix = 0u, pmask = 0u;
     want = (uint32_t)k;
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
+    if constexpr (NPL <= 8) {
+      // MSB-first, one bit per step, counted with ballots (no LDS): among the keys that match the
+      // prefix, count those with the next bit set; if they hold the wanted rank the bit is set,
+      // else they are all taken and the rank moves past them.  Stops once the keys at or above
+      // the prefix are exactly the ones still wanted.
+      uint32_t prefix = 0u;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t m = ~0u << bit, target = prefix | (1u << bit);
+        uint32_t cnt = 0;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) hist[lane * 16 + q] = 0u;
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-      uint32_t *hc = hist + 256 * (lane >> 4);  // this 16-lane group's copy
-#pragma unroll
-      for (int r = 0; r < NPL; ++r) {
-        const int j = lane + 64 * r;
-        if (j >= lo && j < c && (key[r] & pmask) == prefix) atomicAdd(&hc[(key[r] >> shift) & 255u], 1u);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-      uint32_t cnt[4], tot = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int bin = 255 - 4 * lane - q;
-        cnt[q] = hist[bin] + hist[256 + bin] + hist[512 + bin] + hist[768 + bin];
-        tot += cnt[q];
-      }
-      uint32_t incl = tot;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        uint32_t v = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += v;
-      }
-      const uint32_t excl = incl - tot;
-      int dsel = -1;
-      uint32_t above = 0;
-      if (excl < want && want <= incl) {
-        uint32_t run = excl;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (dsel < 0 && run + cnt[q] >= want) {
-            dsel = 255 - 4 * lane - q;
-            above = run;
-          }
-          run += cnt[q];
+        for (int r = 0; r < NPL; ++r) cnt += (uint32_t)__popcll(__ballot((key[r] & m) == target));
+        if (cnt >= want) {
+          prefix = target;
+          if (cnt == want) break;
+        } else {
+          want -= cnt;
         }
       }
-      // broadcast from the lane that found the digit
-      const uint64_t bal = __ballot(dsel >= 0);
-      const int src = __ffsll((unsigned long long)bal) - 1;
-      dsel = __shfl(dsel, src, 64);
-      above = __shfl(above, src, 64);
-      want -= above;
-      prefix |= ((uint32_t)dsel) << shift;
-      pmask |= 255u << shift;
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+      T = prefix;
+    } else {
+      uint32_t prefix = 0u, pmask = 0u;
+      for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) hist[lane * 16 + q] = 0u;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        uint32_t *hc = hist + 256 * (lane >> 4);  // this 16-lane group's copy
+#pragma unroll
+        for (int r = 0; r < NPL; ++r) {
+          const int j = lane + 64 * r;
+          if (j >= lo && j < c && (key[r] & pmask) == prefix) atomicAdd(&hc[(key[r] >> shift) & 255u], 1u);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        uint32_t cnt[4], tot = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int bin = 255 - 4 * lane - q;
+          cnt[q] = hist[bin] + hist[256 + bin] + hist[512 + bin] + hist[768 + bin];
+          tot += cnt[q];
+        }
+        uint32_t incl = tot;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          uint32_t v = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += v;
+        }
+        const uint32_t excl = incl - tot;
+        int dsel = -1;
+        uint32_t above = 0;
+        if (excl < want && want <= incl) {
+          uint32_t run = excl;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (dsel < 0 && run + cnt[q] >= want) {
+              dsel = 255 - 4 * lane - q;
+              above = run;
+            }
+            run += cnt[q];
+          }
+        }
+        // broadcast from the lane that found the digit
+        const uint64_t bal = __ballot(dsel >= 0);
+        const int src = __ffsll((unsigned long long)bal) - 1;
+        dsel = __shfl(dsel, src, 64);
+        above = __shfl(above, src, 64);
+        want -= above;
+        prefix |= ((uint32_t)dsel) << shift;
+        pmask |= 255u << shift;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+      }
+      T = prefix;
     }
-    T = prefix;
   }
   // which candidates are kept (bit r of `selbits`: block lane + 64r)
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -246,8 +267,7 @@ __global__ __launch_bounds__(256) void select_decode_kernel(
       float part = 0.f;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) part = fmaf(qs[u][cc * VEC + e], rv[e], part);
-#pragma unroll
-      for (int o = TPR / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
+      part = group_sum<TPR>(part);
       if (cc == 0) scs[u][r + ps * RPP] = (j < nrep) ? part * scale : -INFINITY;
     }
   }
