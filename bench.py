@@ -136,7 +136,8 @@ def decode_step_setup(sas, w, inp, gist=False):
                           kcap=idx.shape[1], scores=scores, idx=idx, nsel=nsel, gate=gate, workspace=sel_ws)
         attend()
 
-    return dict(step=step, attend=attend), dict(reps=reps, scores=scores, idx=idx, nsel=nsel, gate=gate, O=O)
+    fns = dict(step=step, attend=attend)
+    return fns, dict(reps=reps, scores=scores, idx=idx, nsel=nsel, gate=gate, O=O)
 
 
 def prefill_step_setup(sas, w, inp):

@@ -1,0 +1,686 @@
+// Device bodies of the decode kernels: the selection of one 64-block tile of representatives (with
+// the top-k of a (sequence, KV head) by its last tile) and the attention of one workgroup's tiles
+// (with the split-K merge by a unit's last workgroup).  The kernels (select_decode_kernel,
+// decode_bf16_kernel) call them with their indices and LDS.
+#pragma once
+
+#include "common.h"
+
+namespace sas {
+
+template <int NPL>
+__device__ void wave_topk(const float *__restrict__ row, int c, bool sinkf, const Budget &bg, int kcap,
+                          int32_t *__restrict__ out, int32_t *__restrict__ nsel_out, float *__restrict__ gout,
+                          uint32_t *hist) {
+  const int lane = threadIdx.x & 63;
+  const bool sink = sinkf && c > 0;
+  const int lo = sink ? 1 : 0;
+  const int ncand = c - lo;
+  const int k = budget_k(bg, c, ncand);
+  const int base = sink ? 1 : 0;
+  uint32_t key[NPL];
+  float sv[NPL];
+#pragma unroll
+  for (int r = 0; r < NPL; ++r) {
+    const int j = lane + 64 * r;
+    sv[r] = (j < c) ? load_dev(row + j) : -INFINITY;
+    key[r] = (j >= lo && j < c) ? float_order_key(sv[r]) : 0u;
+  }
+  const float s_c = load_dev(row + c);
+  const float s_0 = load_dev(row);
+  uint32_t T = 0u, want = 0u;
+  bool all = k >= ncand;
+  if (!all && k > 0) {
+    want = (uint32_t)k;
+    if constexpr (NPL <= 8) {
+      // MSB-first, one bit per step, counted with ballots (no LDS): among the keys that match the
+      // prefix, count those with the next bit set; if they hold the wanted rank the bit is set,
+      // else they are all taken and the rank moves past them.  Stops once the keys at or above
+      // the prefix are exactly the ones still wanted.
+      uint32_t prefix = 0u;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t m = ~0u << bit, target = prefix | (1u << bit);
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int r = 0; r < NPL; ++r) cnt += (uint32_t)__popcll(__ballot((key[r] & m) == target));
+        if (cnt >= want) {
+          prefix = target;
+          if (cnt == want) break;
+        } else {
+          want -= cnt;
+        }
+      }
+      T = prefix;
+    } else {
+      uint32_t prefix = 0u, pmask = 0u;
+      for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) hist[lane * 16 + q] = 0u;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        uint32_t *hc = hist + 256 * (lane >> 4);  // this 16-lane group's copy
+#pragma unroll
+        for (int r = 0; r < NPL; ++r) {
+          const int j = lane + 64 * r;
+          if (j >= lo && j < c && (key[r] & pmask) == prefix) atomicAdd(&hc[(key[r] >> shift) & 255u], 1u);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        uint32_t cnt[4], tot = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int bin = 255 - 4 * lane - q;
+          cnt[q] = hist[bin] + hist[256 + bin] + hist[512 + bin] + hist[768 + bin];
+          tot += cnt[q];
+        }
+        uint32_t incl = tot;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          uint32_t v = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += v;
+        }
+        const uint32_t excl = incl - tot;
+        int dsel = -1;
+        uint32_t above = 0;
+        if (excl < want && want <= incl) {
+          uint32_t run = excl;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (dsel < 0 && run + cnt[q] >= want) {
+              dsel = 255 - 4 * lane - q;
+              above = run;
+            }
+            run += cnt[q];
+          }
+        }
+        // broadcast from the lane that found the digit
+        const uint64_t bal = __ballot(dsel >= 0);
+        const int src = __ffsll((unsigned long long)bal) - 1;
+        dsel = __shfl(dsel, src, 64);
+        above = __shfl(above, src, 64);
+        want -= above;
+        prefix |= ((uint32_t)dsel) << shift;
+        pmask |= 255u << shift;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+      }
+      T = prefix;
+    }
+  }
+  // which candidates are kept (bit r of `selbits`: block lane + 64r)
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint64_t selbits = 0ull;
+  uint32_t eq_seen = 0;
+#pragma unroll
+  for (int r = 0; r < NPL; ++r) {
+    const int j = lane + 64 * r;
+    const bool cand = j >= lo && j < c;
+    bool sel;
+    if (all) {
+      sel = cand;
+    } else if (k == 0) {
+      sel = false;
+    } else {
+      const bool gt = cand && key[r] > T;
+      const bool eq = cand && key[r] == T;
+      const uint64_t eb = __ballot(eq);
+      const uint32_t eq_rank = eq_seen + (uint32_t)__popcll(eb & below);
+      eq_seen += (uint32_t)__popcll(eb);
+      sel = gt || (eq && eq_rank < want);
+    }
+    selbits |= (uint64_t)sel << r;
+  }
+  // log-gate: g_j = s_j - logsumexp over the selected set (forced blocks included)
+  float lse = 0.f;
+  if (gout) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < NPL; ++r)
+      if ((selbits >> r) & 1ull) mx = fmaxf(mx, sv[r]);
+    mx = fmaxf(mx, s_c);
+    if (sink) mx = fmaxf(mx, s_0);
+    mx = wave_max(mx);
+    float sm = 0.f;
+#pragma unroll
+    for (int r = 0; r < NPL; ++r)
+      if ((selbits >> r) & 1ull) sm += expf(sv[r] - mx);
+    sm = wave_sum(sm);
+    sm += expf(s_c - mx);
+    if (sink) sm += expf(s_0 - mx);
+    lse = mx + logf(sm);
+  }
+  // compaction in ascending block order
+  uint32_t pos_run = 0;
+#pragma unroll
+  for (int r = 0; r < NPL; ++r) {
+    const bool sel = (selbits >> r) & 1ull;
+    const uint64_t sb = __ballot(sel);
+    const uint32_t pos = pos_run + (uint32_t)__popcll(sb & below);
+    pos_run += (uint32_t)__popcll(sb);
+    if (sel) {
+      out[base + pos] = lane + 64 * r;
+      if (gout) gout[base + pos] = sv[r] - lse;
+    }
+  }
+  const int n = base + k + 1;
+  if (lane == 0) {
+    if (sink) {
+      out[0] = 0;
+      if (gout) gout[0] = s_0 - lse;
+    }
+    out[base + k] = c;
+    if (gout) gout[base + k] = s_c - lse;
+    *nsel_out = n;
+  }
+  for (int p = n + lane; p < kcap; p += 64) {
+    out[p] = -1;
+    if (gout) gout[p] = 0.f;
+  }
+}
+
+// LDS of one selection workgroup.
+template <int D>
+struct SelectLds {
+  static constexpr int QS = 0;                              // float [16][D]  unit queries
+  static constexpr int QSUM = QS + 16 * D * 4;              // float [D]      group mean
+  static constexpr int SCS = QSUM + D * 4;                  // float [16][64] staged scores
+  static constexpr int HIST = SCS + 16 * 64 * 4;            // uint [4][1024] top-k histograms
+  static constexpr int LAST = HIST + 4 * 1024 * 4;          // int            last-arrival flag
+  static constexpr int BYTES = LAST + 16;
+};
+
+// One selection workgroup: the 64-block tile bx of (sequence b, KV head g), hkv KV heads.  The last
+// tile of (b, g) to arrive runs the top-k of its units.
+template <typename T, typename R, int D, int NPL>
+__device__ __forceinline__ void select_tile_body(
+    int bx, int g, int b, int hkv, unsigned char *lds, SeqTable st, const T *__restrict__ Q, int64_t qb, int64_t qh,
+    const R *__restrict__ reps, int64_t rb, int64_t rh, int64_t rj, int gist, int blk, int S, int G, int per_head,
+    float scale, float *__restrict__ scores, int64_t ld, Budget bg, int kcap, int32_t *__restrict__ idx,
+    int32_t *__restrict__ nsel, float *__restrict__ gate, uint32_t *__restrict__ counters) {
+  constexpr int VEC = 16 / sizeof(R);
+  constexpr int TPR = D / VEC;
+  constexpr int RPP = 256 / TPR;
+  constexpr int PASSES = 64 / RPP;
+  using Lds = SelectLds<D>;
+  auto qs = reinterpret_cast<float(*)[D]>(lds + Lds::QS);
+  float *qsum = reinterpret_cast<float *>(lds + Lds::QSUM);
+  auto scs = reinterpret_cast<float(*)[64]>(lds + Lds::SCS);
+  auto hist = reinterpret_cast<uint32_t(*)[1024]>(lds + Lds::HIST);
+  int &last_sh = *reinterpret_cast<int *>(lds + Lds::LAST);
+  const int j0 = bx * 64;
+  const int L = st.len[b];
+  const int c = (L - 1) / blk;
+  if (j0 > c) return;
+  const int ntile = c / 64 + 1;  // tiles covering blocks 0..c
+  const int nrep = gist ? min(L / blk, c) : cdiv(L, blk);
+  const int nU = per_head ? G : 1;
+  const int tid = threadIdx.x;
+  const int cc = tid % TPR, r = tid / TPR;
+  // representative loads first: they depend on nothing else
+  const R *rbase = reps + b * rb + g * rh + cc * VEC;
+  u32x4 raw[PASSES];
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) {
+    const int j = j0 + r + ps * RPP;
+    if (j <= c && j < nrep) raw[ps] = *reinterpret_cast<const u32x4 *>(rbase + (int64_t)j * rj);
+    else raw[ps] = u32x4{0u, 0u, 0u, 0u};
+  }
+  // the group's query rows (G x D <= 16 x 128 values): one element per lane per round, loaded
+  // alongside the representative loads; pooled per unit through LDS
+  constexpr int QR = 16 * D / 256;
+  float qv[QR];
+#pragma unroll
+  for (int x = 0; x < QR; ++x) {
+    const int e = tid + 256 * x;
+    const int h = e / D, kd = e % D;
+    qv[x] = 0.f;
+    if (h < G) {
+      const T *q = Q + b * qb + (int64_t)(g * G + h) * qh + kd;
+      qv[x] = sizeof(T) == 2 ? bf16_to_f32(*(const uint16_t *)q) : *(const float *)q;
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < QR; ++x) {
+    const int e = tid + 256 * x;
+    if (e / D < G) qs[e / D][e % D] = qv[x];
+  }
+  __syncthreads();
+  if (!per_head) {
+    // unit 0 = mean over the group's heads (sequential sum: the same order as the two-call path)
+    for (int kd = tid; kd < D; kd += 256) {
+      float sum = 0.f;
+      for (int h = 0; h < G; ++h) sum += qs[h][kd];
+      qsum[kd] = sum / (float)G;
+    }
+    __syncthreads();
+    for (int kd = tid; kd < D; kd += 256) qs[0][kd] = qsum[kd];
+    __syncthreads();
+  }
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) {
+    const int j = j0 + r + ps * RPP;
+    float rv[VEC];
+    if constexpr (sizeof(R) == 2) {
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        rv[2 * x] = bf16_lo(raw[ps][x]);
+        rv[2 * x + 1] = bf16_hi(raw[ps][x]);
+      }
+    } else {
+#pragma unroll
+      for (int x = 0; x < 4; ++x) rv[x] = __uint_as_float(raw[ps][x]);
+    }
+    for (int u = 0; u < nU; ++u) {
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) part = fmaf(qs[u][cc * VEC + e], rv[e], part);
+      part = group_sum<TPR>(part);
+      if (cc == 0) scs[u][r + ps * RPP] = (j < nrep) ? part * scale : -INFINITY;
+    }
+  }
+  __syncthreads();
+  // device-coherent 16-byte stores of the tile's scores (entries j <= c only)
+  for (int e = tid; e < nU * 16; e += 256) {
+    const int u = e / 16, q = e % 16;
+    const int s = per_head ? g * G + u : g;
+    const __amdgpu_buffer_rsrc_t rrow = dev_rsrc(scores + ((int64_t)b * S + s) * ld, (uint32_t)ld * 4u);
+    const int j = j0 + 4 * q;
+    if (j + 3 <= c) {
+      store16_dev(rrow, (uint32_t)j * 4u, *reinterpret_cast<const f32x4 *>(&scs[u][4 * q]));
+    } else {
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        if (j + x <= c) store4_dev(rrow, (uint32_t)(j + x) * 4u, scs[u][4 * q + x]);
+    }
+  }
+  // ---- arrival: the last tile of this (sequence, KV head) selects for its units
+  wait_stores();
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t old =
+        __hip_atomic_fetch_add(&counters[b * hkv + g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_sh = (old == (uint32_t)(ntile - 1));
+  }
+  __syncthreads();
+  if (!last_sh) return;
+  const int wave = tid >> 6;
+  for (int u = wave; u < nU; u += 4) {
+    const int s = per_head ? g * G + u : g;
+    const int64_t urow = (int64_t)b * S + s;
+    wave_topk<NPL>(scores + urow * ld, c, bg.sink != 0, bg, kcap, idx + urow * kcap, nsel + urow,
+                   bg.gate ? gate + urow * kcap : nullptr, hist[wave]);
+  }
+  if (tid == 0) __hip_atomic_store(&counters[b * hkv + g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+static constexpr int VPAD = 16;  // LDS row padding (bf16 elements) of the V tile: rows start 8 banks apart
+
+// Split record: acc [nh][D] fp32, then m [nh] (log2 units) and l [nh], padded to 16 bytes.
+__host__ __device__ inline int64_t record_floats(int nh, int D) { return (int64_t)nh * D + ((2 * nh + 3) / 4) * 4; }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// LDS of one attention workgroup: the V tiles (reused for the merges), then small arrays.
+template <int D, int WPW>
+struct DecodeLds {
+  static constexpr int VROW = D + VPAD;
+  static constexpr int TILE_BYTES = WPW * 64 * VROW * 2;
+  static constexpr int SMALL_FLOATS = 2 * WPW * 16 + 4 + 32;  // m, l per wave; flag; M, L per head
+  static constexpr int BYTES = TILE_BYTES + SMALL_FLOATS * 4;
+};
+
+// One attention workgroup: tiles bx*WPW .. bx*WPW+WPW-1 of unit u (one wave each), merged into the
+// unit's record bx; the last of the unit's nwg workgroups to arrive merges the records and writes
+// O.
+template <int D, int WPW, typename OT>
+__device__ __forceinline__ void decode_tile_body(
+    int bx, int64_t u, int nwg, unsigned char *lds, SeqTable st, const uint16_t *__restrict__ Q, int64_t qb,
+    int64_t qh, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, int64_t kb, int64_t kh, int64_t kt,
+    const uint16_t *__restrict__ GK, const uint16_t *__restrict__ GV, int64_t gb, int64_t gh, int64_t gt, int gist,
+    int blk, int S, int G, int per_head, const int32_t *__restrict__ idx, const float *__restrict__ gate, int kcap,
+    float scale_log2, float *__restrict__ work, uint32_t *__restrict__ counters, OT *__restrict__ O, int64_t ob,
+    int64_t oh) {
+  constexpr int NKK = D / 32;   // MFMA k-steps over the head dim
+  constexpr int NDT = D / 16;   // 16-dim output tiles
+  constexpr int VROW = D + VPAD;
+  constexpr int NT = WPW * 64;
+  using Lds = DecodeLds<D, WPW>;
+  auto vlds = reinterpret_cast<uint16_t(*)[64 * VROW]>(lds);
+  float *small = reinterpret_cast<float *>(lds + Lds::TILE_BYTES);
+  auto m_sh = reinterpret_cast<float(*)[16]>(small);
+  auto l_sh = reinterpret_cast<float(*)[16]>(small + WPW * 16);
+  int &last_sh = *reinterpret_cast<int *>(small + 2 * WPW * 16);
+  float *Mh = small + 2 * WPW * 16 + 4, *Lh = Mh + 16;
+
+  const int b = (int)(u / S), s = (int)(u % S);
+  const int g = per_head ? s / G : s;
+  const int nh = per_head ? 1 : G;
+  const int h0 = per_head ? s : s * G;
+  const int L = st.len[b];
+  const int c = (L - 1) / blk;
+  const int tpb = blk / 64;
+  const int nraw = kcap * tpb;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = bx * WPW + wave;
+  const int col = lane & 15, grp = lane >> 4;
+  const int64_t rec_sz = record_floats(nh, D);
+
+  // ---- which keys this wave's tile holds (one dependent load: the block index)
+  const uint16_t *kbase = nullptr, *vbase = nullptr;
+  int64_t rstride = 0;
+  int key0 = 0, nvalid = 0;
+  float gl2 = 0.f;
+  uint64_t excl = 0;
+  if (t < nraw) {
+    const int e = t / tpb, sub = t % tpb;
+    const int j = idx[u * kcap + e];
+    if (j >= 0) {
+      key0 = j * blk + sub * 64;
+      nvalid = min(64, L - key0);
+      kbase = K + b * kb + g * kh;
+      vbase = V + b * kb + g * kh;
+      rstride = kt;
+      if (gate) gl2 = gate[u * kcap + e] * 1.4426950408889634f;
+    }
+  } else if (gist) {
+    key0 = (t - nraw) * 64;
+    nvalid = min(64, c - key0);
+    kbase = GK + b * gb + g * gh;
+    vbase = GV + b * gb + g * gh;
+    rstride = gt;
+    if (nvalid > 0) {
+      // gists of selected chunks are replaced by their raw tokens: exclude them
+      for (int e0 = 0; e0 < kcap; e0 += 64) {
+        uint64_t bit = 0;
+        if (e0 + lane < kcap) {
+          const int j = idx[u * kcap + e0 + lane];
+          if (j >= key0 && j < key0 + 64) bit = 1ull << (j - key0);
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+          const uint32_t lo = __shfl_xor((uint32_t)bit, o, 64);
+          const uint32_t hi = __shfl_xor((uint32_t)(bit >> 32), o, 64);
+          bit |= ((uint64_t)hi << 32) | lo;
+        }
+        excl |= bit;
+      }
+    }
+  }
+  nvalid = max(nvalid, 0);
+
+  // ---- Q^T as the B operand: lane -> head `col`, dims 32*kk + 8*grp .. +8
+  bf16x8 qreg[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (col < nh && nvalid > 0)
+      v = *reinterpret_cast<const u32x4 *>(Q + b * qb + (int64_t)(h0 + col) * qh + 32 * kk + 8 * grp);
+    qreg[kk] = as_bf16x8(v);
+  }
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 acc_o[NDT];
+#pragma unroll
+  for (int x = 0; x < NDT; ++x) acc_o[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (nvalid > 0) {
+    // ---- K straight to A-operand registers, V rows to registers (then LDS)
+    u32x4 kreg[4][NKK];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int key = mt * 16 + col;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (key < nvalid)
+          v = *reinterpret_cast<const u32x4 *>(kbase + (int64_t)(key0 + key) * rstride + 32 * kk + 8 * grp);
+        kreg[mt][kk] = v;
+      }
+    }
+    constexpr int VCH = D / 8;  // 16-byte chunks per V row; VCH loads per lane
+    u32x4 vreg[VCH];
+#pragma unroll
+    for (int x = 0; x < VCH; ++x) {
+      const int e = x * 64 + lane;
+      const int key = e / VCH, ch = e % VCH;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (key < nvalid) v = *reinterpret_cast<const u32x4 *>(vbase + (int64_t)(key0 + key) * rstride + ch * 8);
+      vreg[x] = v;
+    }
+    // ---- S^T = K Q^T
+    f32x4 sacc[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kreg[mt][kk]), qreg[kk], a, 0, 0, 0);
+      sacc[mt] = a;
+    }
+    uint16_t *vl = vlds[wave];
+#pragma unroll
+    for (int x = 0; x < VCH; ++x) {
+      const int e = x * 64 + lane;
+      const int key = e / VCH, ch = e % VCH;
+      *reinterpret_cast<u32x4 *>(vl + key * VROW + ch * 8) = vreg[x];
+    }
+    // ---- softmax over the tile's keys, per head column
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = mt * 16 + 4 * grp + r;
+        const bool ok = key < nvalid && !((excl >> key) & 1ull);
+        const float v = ok ? sacc[mt][r] * scale_log2 + gl2 : -INFINITY;
+        sacc[mt][r] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    m_run = mx;
+    const float mref = (mx == -INFINITY) ? 0.f : mx;
+    float ls = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = __builtin_amdgcn_exp2f(sacc[mt][r] - mref);
+        sacc[mt][r] = p;
+        ls += p;
+      }
+    l_run = ls;
+    // P^T as the B operand of each 32-key step (keys 32ks + 4grp + {0..3} and +16)
+    bf16x8 preg[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4 w;
+      w[0] = pack_bf16x2(sacc[2 * ks][0], sacc[2 * ks][1]);
+      w[1] = pack_bf16x2(sacc[2 * ks][2], sacc[2 * ks][3]);
+      w[2] = pack_bf16x2(sacc[2 * ks + 1][0], sacc[2 * ks + 1][1]);
+      w[3] = pack_bf16x2(sacc[2 * ks + 1][2], sacc[2 * ks + 1][3]);
+      preg[ks] = as_bf16x8(w);
+    }
+    // the V tile is written and read by this wave only: wait for its LDS writes
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    // ---- O^T = V^T P^T; the V^T operand (dim 16dt + col, keys 32ks + 4grp + {0..3} then
+    //      32ks + 16 + 4grp + {0..3}) comes from two transpose reads of the row-major tile
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint16_t *src = vl + (ks * 32 + 4 * grp + (col >> 2)) * VROW + dt * 16 + 4 * (col & 3);
+        const u32x2 lo = lds_read_tr16(src);
+        const u32x2 hi = lds_read_tr16(src + 16 * VROW);
+        const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+        acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w), preg[ks], acc_o[dt], 0, 0, 0);
+      }
+    }
+  }
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+
+  // ---- this workgroup's record: [nh][D] acc, then m[nh], l[nh] (m in log2 units), written with
+  //      device-coherent 16-byte stores so that the merging workgroup (any XCD) reads them
+  const uint32_t rec_bytes = (uint32_t)rec_sz * 4u;
+  const __amdgpu_buffer_rsrc_t rr = dev_rsrc(work + u * nwg * rec_sz, nwg * rec_bytes);
+  const uint32_t my = bx * rec_bytes;
+  if constexpr (WPW == 1) {
+    if (col < nh) {
+      if (grp == 0) {
+        store4_dev(rr, my + (uint32_t)(nh * D + col) * 4u, m_run);
+        store4_dev(rr, my + (uint32_t)(nh * D + nh + col) * 4u, l_run);
+      }
+      if (m_run != -INFINITY) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) store16_dev(rr, my + (uint32_t)(col * D + dt * 16 + 4 * grp) * 4u, acc_o[dt]);
+      }
+    }
+  } else {
+    __syncthreads();
+    float *osh = reinterpret_cast<float *>(&vlds[0][0]);  // [WPW][16][D] fp32 over the V tiles
+    if (grp == 0) {
+      m_sh[wave][col] = m_run;
+      l_sh[wave][col] = l_run;
+    }
+    if (col < nh) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        *reinterpret_cast<f32x4 *>(osh + (wave * 16 + col) * D + dt * 16 + 4 * grp) = acc_o[dt];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < nh * (D / 4); e += NT) {
+      const int n = e / (D / 4), q = e % (D / 4);
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < WPW; ++w) M = fmaxf(M, m_sh[w][n]);
+      const float Mr = (M == -INFINITY) ? 0.f : M;
+      f32x4 o = {0.f, 0.f, 0.f, 0.f};
+      float l = 0.f;
+#pragma unroll
+      for (int w = 0; w < WPW; ++w) {
+        const float f = (m_sh[w][n] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_sh[w][n] - Mr);
+        o += f * *reinterpret_cast<const f32x4 *>(osh + (w * 16 + n) * D + 4 * q);
+        l += f * l_sh[w][n];
+      }
+      store16_dev(rr, my + (uint32_t)(n * D + 4 * q) * 4u, o);
+      if (q == 0) {
+        store4_dev(rr, my + (uint32_t)(nh * D + n) * 4u, M);
+        store4_dev(rr, my + (uint32_t)(nh * D + nh + n) * 4u, l);
+      }
+    }
+  }
+
+  // ---- arrival; the last workgroup of the unit merges every record and writes O
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(&counters[u], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_sh = (old == (uint32_t)nwg - 1);
+  }
+  __syncthreads();
+  if (!last_sh) return;
+  const int nrec = nwg;
+  const int tid = threadIdx.x;
+  float *msh = reinterpret_cast<float *>(&vlds[0][0]);  // [nrec][nh] m, then l, then weights
+  float *lsh = msh + nrec * nh;
+  float *fsh = lsh + nrec * nh;
+  f32x4 *red = reinterpret_cast<f32x4 *>(msh + ((3 * nrec * nh + 3) / 4) * 4);
+  // (1) every record's m and l in one round of loads
+  for (int e = tid; e < nrec * nh; e += NT) {
+    const int x = e / nh, n = e % nh;
+    msh[e] = load4_dev(rr, x * rec_bytes + (uint32_t)(nh * D + n) * 4u);
+    lsh[e] = load4_dev(rr, x * rec_bytes + (uint32_t)(nh * D + nh + n) * 4u);
+  }
+  __syncthreads();
+  if (tid < nh) {
+    float M = -INFINITY;
+    for (int x = 0; x < nrec; ++x) M = fmaxf(M, msh[x * nh + tid]);
+    Mh[tid] = (M == -INFINITY) ? 0.f : M;
+  }
+  __syncthreads();
+  for (int e = tid; e < nrec * nh; e += NT) {
+    const float m = msh[e];
+    fsh[e] = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - Mh[e % nh]);
+  }
+  __syncthreads();
+  if (tid < nh) {
+    float l = 0.f;
+    for (int x = 0; x < nrec; ++x) l += fsh[x * nh + tid] * lsh[x * nh + tid];
+    Lh[tid] = l;
+  }
+  // (2) weighted sum of the acc quads; lanes split the records into RG groups
+  const int Q4 = nh * (D / 4);
+  const int RG = Q4 >= NT ? 1 : NT / Q4;
+  const int rg = tid / Q4 < RG ? tid / Q4 : RG;  // RG marks an idle lane
+  for (int q0 = 0; q0 < Q4; q0 += NT) {
+    const int qq = q0 + tid % Q4 + (Q4 >= NT ? tid - tid % Q4 : 0);
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    const bool act = rg < RG && qq < Q4;
+    const int n = act ? qq / (D / 4) : 0;
+    if (act) {
+      for (int x0 = rg; x0 < nrec; x0 += RG * 8) {
+        f32x4 v[8];
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int x = x0 + i * RG;
+          const bool ok = x < nrec;
+          f[i] = ok ? fsh[x * nh + n] : 0.f;
+          v[i] = (ok && f[i] != 0.f) ? load16_dev(rr, x * rec_bytes + (uint32_t)(4 * qq) * 4u)
+                                     : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a += f[i] * v[i];
+      }
+    }
+    if (RG > 1) {
+      __syncthreads();
+      if (act) red[rg * Q4 + qq] = a;
+      __syncthreads();
+      if (act && rg == 0)
+        for (int g2 = 1; g2 < RG; ++g2) a += red[g2 * Q4 + qq];
+    } else {
+      __syncthreads();
+    }
+    if (act && rg == 0) {
+      const float inv = 1.f / Lh[n];
+      const int dim = 4 * (qq % (D / 4));
+      OT *dst = O + b * ob + (int64_t)(h0 + n) * oh + dim;
+      if constexpr (sizeof(OT) == 2) {
+        u32x2 w;
+        w[0] = pack_bf16x2(a[0] * inv, a[1] * inv);
+        w[1] = pack_bf16x2(a[2] * inv, a[3] * inv);
+        *reinterpret_cast<u32x2 *>(dst) = w;
+      } else {
+        *reinterpret_cast<f32x4 *>(dst) = a * inv;
+      }
+    }
+  }
+  if (tid == 0) __hip_atomic_store(&counters[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct DecodeShape {
+  int S, nh, tiles_cap, wpw, nwg_cap;
+  int64_t units;
+};
+
+static inline DecodeShape decode_shape(const sas_problem &p, int32_t sel_mode, int32_t kcap, int gist, int maxc) {
+  DecodeShape d;
+  const int per_head = sel_mode == SAS_SEL_HEAD;
+  d.S = per_head ? p.hq : p.hkv;
+  d.nh = per_head ? 1 : p.hq / p.hkv;
+  d.units = (int64_t)p.batch * d.S;
+  d.tiles_cap = kcap * (p.block / 64) + (gist ? (maxc + 63) / 64 : 0);
+  // one wave per workgroup keeps every CU busy; wide units (many heads x many tiles) merge
+  // 4 waves per workgroup first so that the final merge reads fewer records
+  d.wpw = 4;
+  auto fits = [&](int wpw) {
+    const int nwg = (d.tiles_cap + wpw - 1) / wpw;
+    const int lds = wpw * 64 * (p.head_dim + VPAD) * 2;
+    return 12 * nwg * d.nh + 16 + 16 * 64 * wpw <= lds;
+  };
+  if (!fits(d.wpw)) d.wpw = 4;
+  d.nwg_cap = (d.tiles_cap + d.wpw - 1) / d.wpw;
+  return d;
+}
+
+}  // namespace sas
