@@ -22,8 +22,10 @@
 //                 S^T accumulator (keys in accumulator order), V^T is read from the LDS tile
 //                 in that same key order with transposing reads (ds_read_b64_tr_b16).
 // Only the current block needs the causal mask.  Units are taken heavy-first (later query
-// blocks select more blocks) and dealt round-robin to the XCDs; the row tiles of one unit,
-// which share its K/V tiles, run on the same XCD (one L2).
+// blocks select more blocks; per-head units grouped by (sequence, KV head) for MALL reuse) and
+// dealt round-robin to the XCDs; the row tiles of one unit, which share its K/V tiles, run on
+// the same XCD (one L2).
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -36,9 +38,14 @@ __device__ __forceinline__ bf16x8 as_bf16x8p(u32x4 v) { return __builtin_bit_cas
 // NW = 2: 64 rows per workgroup (one 64-row unit), single K and V buffers (4 workgroups per CU,
 //         so 2 waves per SIMD as well): K of tile t+1 is copied during the softmax and PV of tile
 //         t, V of tile t+1 during the S phase and softmax of tile t+1.
+// Sequences in descending length (the order per-head units are walked in).
+struct SeqOrder {
+  int32_t b[SAS_MAX_BATCH];
+};
+
 template <int D, int NW, int BLK>
 __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
-    SeqTable st, const uint16_t *__restrict__ Q, int64_t qb, int64_t qh, int64_t qt,
+    SeqTable st, SeqOrder ord, const uint16_t *__restrict__ Q, int64_t qb, int64_t qh, int64_t qt,
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, int64_t kb, int64_t kh, int64_t kt,
     int tq, int blk, int S, int QB, int G, int per_head, int batch, int rtiles,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ nsel, const float *__restrict__ gate,
@@ -64,11 +71,28 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
   const int slot = (q / rtiles) * 8 + xcd;
   const int rt = q % rtiles;
   if (slot >= QB * batch * S) return;
-  int rest = slot;
-  const int s = rest % S;
-  rest /= S;
-  const int b = rest % batch;
-  const int i = QB - 1 - rest / batch;
+  int s, b, i;
+  if (per_head) {
+    // Per-head lists share few tiles across the batch but many within one (sequence, KV head)
+    // (its heads and query blocks pick from the same key blocks): walk the units (sequence, KV
+    // head)-major, longest sequences first, heavy-first within, the group's heads adjacent, so
+    // that the K/V slabs in use at any time fit the MALL and each tile comes from HBM about once.
+    int rest = slot;
+    const int hh = rest % G;
+    rest /= G;
+    i = QB - 1 - rest % QB;
+    rest /= QB;
+    const int hkv = S / G;
+    s = (rest % hkv) * G + hh;
+    b = ord.b[rest / hkv];
+  } else {
+    // per-group units: heavy-first over the whole batch
+    int rest = slot;
+    s = rest % S;
+    rest /= S;
+    b = rest % batch;
+    i = QB - 1 - rest / batch;
+  }
 
   const int L = st.len[b];
   const int q0 = st.q0[b];
@@ -309,7 +333,10 @@ static hipError_t prefill_dispatch(const sas_problem &p, const SeqTable &st, con
   const int64_t units = (int64_t)QB * p.batch * S;
   const int64_t nwg = 8 * cdiv64(units, 8) * rtiles;
   const float scale_log2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, BLK>), dim3((unsigned)nwg), dim3(NW * 64), 0, s, st,
+  SeqOrder ord{};
+  for (int b = 0; b < p.batch; ++b) ord.b[b] = b;
+  std::stable_sort(ord.b, ord.b + p.batch, [&](int x, int y) { return st.len[x] > st.len[y]; });
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, BLK>), dim3((unsigned)nwg), dim3(NW * 64), 0, s, st, ord,
                      (const uint16_t *)Q, qs[0], qs[1], qs[2], (const uint16_t *)K, (const uint16_t *)V, kvs[0],
                      kvs[1], kvs[2], tq, p.block, S, QB, G, per_head, p.batch, rtiles, idx, nsel, gate, kcap,
                      scale_log2, (uint16_t *)O, os[0], os[1], os[2]);
