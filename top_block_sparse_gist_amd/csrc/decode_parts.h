@@ -8,156 +8,177 @@
 
 namespace sas {
 
+// Inverse of float_order_key.
+__device__ __forceinline__ float order_key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Wave-wide reduction of a u32 to a uniform value: DPP within each 16-lane row, then the four
+// row results through scalar registers.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
+  auto dpp = [](uint32_t x, auto ctrl) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, decltype(ctrl)::value, 0xF, 0xF, false);
+  };
+  v = op(v, dpp(v, std::integral_constant<int, 0xB1>{}));   // lane ^ 1
+  v = op(v, dpp(v, std::integral_constant<int, 0x4E>{}));   // lane ^ 2
+  v = op(v, dpp(v, std::integral_constant<int, 0x124>{}));  // row_ror:4
+  v = op(v, dpp(v, std::integral_constant<int, 0x128>{}));  // row_ror:8
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return op(op(r0, r1), op(r2, r3));
+}
+
+// Number of keys >= t over the wave: per-lane counts in four independent chains, one reduction.
+template <int NPL>
+__device__ __forceinline__ uint32_t count_ge(const uint32_t (&key)[NPL], uint32_t t) {
+  uint32_t a[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int r = 0; r < NPL; ++r) a[r & 3] += key[r] >= t ? 1u : 0u;
+  return wave_reduce_u32((a[0] + a[1]) + (a[2] + a[3]), [](uint32_t x, uint32_t y) { return x + y; });
+}
+
+// Top-k of one unit's scores row[0..c] by one wave (block lane + 64r in register r; the scores
+// are read back from memory, where the unit's tiles left them).  Ties go to the lower block.
 template <int NPL>
 __device__ void wave_topk(const float *__restrict__ row, int c, bool sinkf, const Budget &bg, int kcap,
-                          int32_t *__restrict__ out, int32_t *__restrict__ nsel_out, float *__restrict__ gout,
-                          uint32_t *hist) {
-  const int lane = threadIdx.x & 63;
+                          int32_t *__restrict__ out, int32_t *__restrict__ nsel_out, float *__restrict__ gout) {
+  static_assert(NPL <= 32, "one selection bit per register in a 32-bit mask");
+  // opaque per call: keeps the compiler from hoisting the per-register block numbers and masks out
+  // of a caller's loop over units, where they would hold ~100 registers across the whole kernel
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
   const bool sink = sinkf && c > 0;
   const int lo = sink ? 1 : 0;
   const int ncand = c - lo;
   const int k = budget_k(bg, c, ncand);
   const int base = sink ? 1 : 0;
+  // order-preserving keys of the candidates, 0 elsewhere: a candidate's key is never 0 (that is
+  // the key of one NaN pattern only, and NaN scores are not ranked)
   uint32_t key[NPL];
-  float sv[NPL];
 #pragma unroll
   for (int r = 0; r < NPL; ++r) {
+    // every lane loads (entries up to c exist), so the loads issue back to back
     const int j = lane + 64 * r;
-    sv[r] = (j < c) ? load_dev(row + j) : -INFINITY;
-    key[r] = (j >= lo && j < c) ? float_order_key(sv[r]) : 0u;
+    const float s = load_dev(row + min(j, c));
+    key[r] = (j >= lo && j < c) ? max(float_order_key(s), 1u) : 0u;
   }
   const float s_c = load_dev(row + c);
   const float s_0 = load_dev(row);
+  // The kept candidates: all keys > T, then the `want` lowest blocks with key == T (ties: only
+  // when T is the exact k-th largest key and more keys share it).
   uint32_t T = 0u, want = 0u;
-  bool all = k >= ncand;
+  bool ties = false;
+  const bool all = k >= ncand;
   if (!all && k > 0) {
-    want = (uint32_t)k;
-    if constexpr (NPL <= 8) {
-      // MSB-first, one bit per step, counted with ballots (no LDS): among the keys that match the
-      // prefix, count those with the next bit set; if they hold the wanted rank the bit is set,
-      // else they are all taken and the rank moves past them.  Stops once the keys at or above
-      // the prefix are exactly the ones still wanted.
-      uint32_t prefix = 0u;
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t m = ~0u << bit, target = prefix | (1u << bit);
-        uint32_t cnt = 0;
+    // the candidates' key range
+    uint32_t kmin = ~0u, kmax = 0u;  // kmin over key - 1: a non-candidate's 0 wraps to the top
 #pragma unroll
-        for (int r = 0; r < NPL; ++r) cnt += (uint32_t)__popcll(__ballot((key[r] & m) == target));
-        if (cnt >= want) {
-          prefix = target;
-          if (cnt == want) break;
-        } else {
-          want -= cnt;
-        }
-      }
-      T = prefix;
+    for (int r = 0; r < NPL; ++r) {
+      kmin = min(kmin, key[r] - 1u);
+      kmax = max(kmax, key[r]);
+    }
+    kmin = wave_reduce_u32(kmin, [](uint32_t x, uint32_t y) { return min(x, y); }) + 1u;
+    kmax = wave_reduce_u32(kmax, [](uint32_t x, uint32_t y) { return max(x, y); });
+    const uint32_t c_hi = count_ge(key, kmax);
+    if (c_hi >= (uint32_t)k) {
+      T = kmax;  // the largest key alone fills the budget: its first k holders in block order
+      want = (uint32_t)k;
+      ties = c_hi > (uint32_t)k;
     } else {
-      uint32_t prefix = 0u, pmask = 0u;
-      for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 24 - 8 * pass;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) hist[lane * 16 + q] = 0u;
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-        uint32_t *hc = hist + 256 * (lane >> 4);  // this 16-lane group's copy
-#pragma unroll
-        for (int r = 0; r < NPL; ++r) {
-          const int j = lane + 64 * r;
-          if (j >= lo && j < c && (key[r] & pmask) == prefix) atomicAdd(&hc[(key[r] >> shift) & 255u], 1u);
+      // Safeguarded interpolation search for the largest key value T with at least k keys at or
+      // above it.  Invariant: count_ge(lo) = cl >= k > ch = count_ge(hi).  Each probe goes where
+      // a straight line between (lo, cl) and (hi, ch) reaches k -- or to the midpoint after a
+      // probe that did not halve the range -- and replaces lo or hi.  A probe with exactly k keys
+      // at or above it ends the search: those keys are the selection.  Otherwise the range
+      // closes to hi = lo + 1 and lo is the k-th largest key, with k - ch of its holders taken.
+      uint32_t lo = kmin, hi = kmax, cl = (uint32_t)ncand, ch = c_hi;
+      bool exact = false, bisect = false;
+      while (hi - lo > 1u) {
+        const uint32_t span = hi - lo;
+        uint32_t step;
+        if (bisect) {
+          step = span >> 1;
+        } else {
+          // f in [0, 1); the float product is clamped below 2^32 before the conversion
+          const float f = __fdividef((float)(cl - (uint32_t)k), (float)(cl - ch));
+          step = (uint32_t)fminf((float)span * f, 4294967040.f);
+          step = max(min(step, span - 1u), 1u);
         }
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-        uint32_t cnt[4], tot = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int bin = 255 - 4 * lane - q;
-          cnt[q] = hist[bin] + hist[256 + bin] + hist[512 + bin] + hist[768 + bin];
-          tot += cnt[q];
-        }
-        uint32_t incl = tot;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          uint32_t v = __shfl_up(incl, o, 64);
-          if (lane >= o) incl += v;
-        }
-        const uint32_t excl = incl - tot;
-        int dsel = -1;
-        uint32_t above = 0;
-        if (excl < want && want <= incl) {
-          uint32_t run = excl;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (dsel < 0 && run + cnt[q] >= want) {
-              dsel = 255 - 4 * lane - q;
-              above = run;
-            }
-            run += cnt[q];
+        const uint32_t t = lo + step;
+        const uint32_t c_t = count_ge(key, t);
+        if (c_t >= (uint32_t)k) {
+          lo = t;
+          cl = c_t;
+          if (c_t == (uint32_t)k) {
+            exact = true;
+            break;
           }
+        } else {
+          hi = t;
+          ch = c_t;
         }
-        // broadcast from the lane that found the digit
-        const uint64_t bal = __ballot(dsel >= 0);
-        const int src = __ffsll((unsigned long long)bal) - 1;
-        dsel = __shfl(dsel, src, 64);
-        above = __shfl(above, src, 64);
-        want -= above;
-        prefix |= ((uint32_t)dsel) << shift;
-        pmask |= 255u << shift;
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        bisect = (hi - lo) > (span >> 1);
       }
-      T = prefix;
+      T = lo;
+      want = exact ? (uint32_t)k : (uint32_t)k - ch;
+      ties = !exact;
     }
   }
   // which candidates are kept (bit r of `selbits`: block lane + 64r)
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  uint64_t selbits = 0ull;
-  uint32_t eq_seen = 0;
+  uint32_t selbits = 0u;
+  if (all) {
 #pragma unroll
-  for (int r = 0; r < NPL; ++r) {
-    const int j = lane + 64 * r;
-    const bool cand = j >= lo && j < c;
-    bool sel;
-    if (all) {
-      sel = cand;
-    } else if (k == 0) {
-      sel = false;
-    } else {
-      const bool gt = cand && key[r] > T;
-      const bool eq = cand && key[r] == T;
+    for (int r = 0; r < NPL; ++r) selbits |= (key[r] != 0u ? 1u : 0u) << r;
+  } else if (k > 0 && !ties) {
+#pragma unroll
+    for (int r = 0; r < NPL; ++r) selbits |= (key[r] >= T ? 1u : 0u) << r;  // T >= 1: candidates only
+  } else if (k > 0) {
+    uint32_t eq_seen = 0;
+#pragma unroll
+    for (int r = 0; r < NPL; ++r) {
+      const bool eq = key[r] == T;  // T >= 1 here, so both tests pass over the non-candidates
       const uint64_t eb = __ballot(eq);
       const uint32_t eq_rank = eq_seen + (uint32_t)__popcll(eb & below);
       eq_seen += (uint32_t)__popcll(eb);
-      sel = gt || (eq && eq_rank < want);
+      selbits |= ((key[r] > T) || (eq && eq_rank < want) ? 1u : 0u) << r;
     }
-    selbits |= (uint64_t)sel << r;
   }
   // log-gate: g_j = s_j - logsumexp over the selected set (forced blocks included)
   float lse = 0.f;
   if (gout) {
     float mx = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < NPL; ++r)
-      if ((selbits >> r) & 1ull) mx = fmaxf(mx, sv[r]);
+    for (int r = 0; r < NPL; ++r) mx = fmaxf(mx, ((selbits >> r) & 1u) ? order_key_float(key[r]) : -INFINITY);
     mx = fmaxf(mx, s_c);
     if (sink) mx = fmaxf(mx, s_0);
     mx = wave_max(mx);
+    // exp(x - mx) as 2^((x - mx) log2 e): one v_exp_f32 each; terms that flush to 0 are below the
+    // largest (1) by more than the float's precision
+    constexpr float L2E = 1.4426950408889634f;
     float sm = 0.f;
 #pragma unroll
-    for (int r = 0; r < NPL; ++r)
-      if ((selbits >> r) & 1ull) sm += expf(sv[r] - mx);
+    for (int r = 0; r < NPL; ++r) {
+      const float e = __builtin_amdgcn_exp2f((order_key_float(key[r]) - mx) * L2E);
+      sm += ((selbits >> r) & 1u) ? e : 0.f;
+    }
     sm = wave_sum(sm);
-    sm += expf(s_c - mx);
-    if (sink) sm += expf(s_0 - mx);
+    sm += __builtin_amdgcn_exp2f((s_c - mx) * L2E);
+    if (sink) sm += __builtin_amdgcn_exp2f((s_0 - mx) * L2E);
     lse = mx + logf(sm);
   }
   // compaction in ascending block order
   uint32_t pos_run = 0;
 #pragma unroll
   for (int r = 0; r < NPL; ++r) {
-    const bool sel = (selbits >> r) & 1ull;
+    const bool sel = (selbits >> r) & 1u;
     const uint64_t sb = __ballot(sel);
     const uint32_t pos = pos_run + (uint32_t)__popcll(sb & below);
     pos_run += (uint32_t)__popcll(sb);
     if (sel) {
       out[base + pos] = lane + 64 * r;
-      if (gout) gout[base + pos] = sv[r] - lse;
+      if (gout) gout[base + pos] = order_key_float(key[r]) - lse;
     }
   }
   const int n = base + k + 1;
@@ -182,8 +203,7 @@ struct SelectLds {
   static constexpr int QS = 0;                              // float [16][D]  unit queries
   static constexpr int QSUM = QS + 16 * D * 4;              // float [D]      group mean
   static constexpr int SCS = QSUM + D * 4;                  // float [16][64] staged scores
-  static constexpr int HIST = SCS + 16 * 64 * 4;            // uint [4][1024] top-k histograms
-  static constexpr int LAST = HIST + 4 * 1024 * 4;          // int            last-arrival flag
+  static constexpr int LAST = SCS + 16 * 64 * 4;            // int            last-arrival flag
   static constexpr int BYTES = LAST + 16;
 };
 
@@ -203,7 +223,6 @@ __device__ __forceinline__ void select_tile_body(
   auto qs = reinterpret_cast<float(*)[D]>(lds + Lds::QS);
   float *qsum = reinterpret_cast<float *>(lds + Lds::QSUM);
   auto scs = reinterpret_cast<float(*)[64]>(lds + Lds::SCS);
-  auto hist = reinterpret_cast<uint32_t(*)[1024]>(lds + Lds::HIST);
   int &last_sh = *reinterpret_cast<int *>(lds + Lds::LAST);
   const int j0 = bx * 64;
   const int L = st.len[b];
@@ -301,12 +320,12 @@ __device__ __forceinline__ void select_tile_body(
   }
   __syncthreads();
   if (!last_sh) return;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   for (int u = wave; u < nU; u += 4) {
     const int s = per_head ? g * G + u : g;
     const int64_t urow = (int64_t)b * S + s;
     wave_topk<NPL>(scores + urow * ld, c, bg.sink != 0, bg, kcap, idx + urow * kcap, nsel + urow,
-                   bg.gate ? gate + urow * kcap : nullptr, hist[wave]);
+                   bg.gate ? gate + urow * kcap : nullptr);
   }
   if (tid == 0) __hip_atomic_store(&counters[b * hkv + g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -13,21 +13,41 @@
 // scores are loaded once into registers, an MSB-first radix select (4 passes of 8 bits,
 // per-wave LDS histogram, shuffle scan) finds the k-th largest key, and a ballot/popcount
 // compaction writes the selected blocks in ascending order (ties go to the lower block).
+#include <algorithm>
+
 #include "common.h"
 #include "decode_parts.h"
 
 namespace sas {
 
+// The grid lists only live tiles: sequences in descending length (their top-k tails are the
+// longest, so they start first), each as ntile x hkv workgroups, tile-major.
+struct SelGrid {
+  int32_t b[SAS_MAX_BATCH];          // sequence of the i-th entry
+  int32_t first[SAS_MAX_BATCH + 1];  // first workgroup of the i-th entry; first[nseq] = grid size
+  int32_t nseq;
+};
+
+// At most 128 VGPRs (4 workgroups per CU): the top-k's 32 registers per lane of keys would
+// otherwise set the register count, and the occupancy, of every tile workgroup.
 template <typename T, typename R, int D, int NPL>
-__global__ __launch_bounds__(256) void select_decode_kernel(
-    SeqTable st, const T *__restrict__ Q, int64_t qb, int64_t qh, const R *__restrict__ reps, int64_t rb,
-    int64_t rh, int64_t rj, int gist, int blk, int S, int G, int per_head, float scale, float *__restrict__ scores,
-    int64_t ld, Budget bg, int kcap, int32_t *__restrict__ idx, int32_t *__restrict__ nsel, float *__restrict__ gate,
-    uint32_t *__restrict__ counters) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void select_decode_kernel(
+    SeqTable st, SelGrid sg, const T *__restrict__ Q, int64_t qb, int64_t qh, const R *__restrict__ reps,
+    int64_t rb, int64_t rh, int64_t rj, int gist, int blk, int hkv, int S, int G, int per_head, float scale,
+    float *__restrict__ scores, int64_t ld, Budget bg, int kcap, int32_t *__restrict__ idx,
+    int32_t *__restrict__ nsel, float *__restrict__ gate, uint32_t *__restrict__ counters) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[SelectLds<D>::BYTES];
-  select_tile_body<T, R, D, NPL>(blockIdx.x, blockIdx.y, blockIdx.z, gridDim.y, lds, st, Q, qb, qh, reps,
-                                        rb, rh, rj, gist, blk, S, G, per_head, scale, scores, ld, bg, kcap, idx,
-                                        nsel, gate, counters);
+  const int id = blockIdx.x;
+  int lo = 0, hi = sg.nseq - 1;  // last entry with first <= id
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (sg.first[mid] <= id) lo = mid;
+    else hi = mid - 1;
+  }
+  const int rem = id - sg.first[lo];
+  select_tile_body<T, R, D, NPL>(rem / hkv, rem % hkv, sg.b[lo], hkv, lds, st, Q, qb, qh, reps, rb, rh, rj,
+                                 gist, blk, S, G, per_head, scale, scores, ld, bg, kcap, idx, nsel, gate,
+                                 counters);
 }
 
 template <typename T, typename R, int D>
@@ -39,11 +59,20 @@ static hipError_t sel_dispatch(const sas_problem &p, const SeqTable &st, const v
   const int S = per_head ? p.hq : p.hkv;
   int maxc = 0;
   for (int b = 0; b < p.batch; ++b) maxc = max(maxc, (st.len[b] - 1) / p.block);
-  dim3 grid(maxc / 64 + 1, p.hkv, p.batch);
+  SelGrid sg{};
+  for (int b = 0; b < p.batch; ++b) sg.b[b] = b;
+  std::stable_sort(sg.b, sg.b + p.batch, [&](int x, int y) { return st.len[x] > st.len[y]; });
+  sg.nseq = p.batch;
+  sg.first[0] = 0;
+  for (int i = 0; i < p.batch; ++i) {
+    const int ntile = (st.len[sg.b[i]] - 1) / p.block / 64 + 1;
+    sg.first[i + 1] = sg.first[i] + ntile * p.hkv;
+  }
+  const dim3 grid((unsigned)sg.first[p.batch]);
 #define SAS_SEL_LAUNCH(NPL_)                                                                                   \
-  hipLaunchKernelGGL((select_decode_kernel<T, R, D, NPL_>), grid, dim3(256), 0, s, st, (const T *)Q, qs[0],     \
-                     qs[1], (const R *)reps, rs[0], rs[1], rs[2], gist, p.block, S, p.hq / p.hkv, per_head,     \
-                     scale, scores, ld, bg, kcap, idx, nsel, gate, counters)
+  hipLaunchKernelGGL((select_decode_kernel<T, R, D, NPL_>), grid, dim3(256), 0, s, st, sg, (const T *)Q, qs[0], \
+                     qs[1], (const R *)reps, rs[0], rs[1], rs[2], gist, p.block, p.hkv, S, p.hq / p.hkv,        \
+                     per_head, scale, scores, ld, bg, kcap, idx, nsel, gate, counters)
   if (maxc <= 512) SAS_SEL_LAUNCH(8);
   else SAS_SEL_LAUNCH(32);
 #undef SAS_SEL_LAUNCH
