@@ -10,9 +10,10 @@
 // are formed with a shuffle reduction and written.  The last workgroup to finish a
 // (sequence, KV head) -- found with one device-scope atomic on an arrival counter, which it
 // resets to zero -- runs the top-k of that KV head's units, one wave per unit: the unit's
-// scores are loaded once into registers, an MSB-first radix select (4 passes of 8 bits,
-// per-wave LDS histogram, shuffle scan) finds the k-th largest key, and a ballot/popcount
-// compaction writes the selected blocks in ascending order (ties go to the lower block).
+// scores are loaded once into registers as order-preserving integer keys, an interpolation
+// search over the key range (counts of keys at or above a probe, VALU counts + one DPP
+// reduction per probe) finds the k-th largest key, and a ballot/popcount compaction writes the
+// selected blocks in ascending order (ties go to the lower block).
 #include <algorithm>
 
 #include "common.h"
