@@ -30,11 +30,12 @@ __global__ __launch_bounds__(WPW * 64) void decode_bf16_kernel(
     SeqTable st, const uint16_t *__restrict__ Q, int64_t qb, int64_t qh, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, int64_t kb, int64_t kh, int64_t kt, const uint16_t *__restrict__ GK,
     const uint16_t *__restrict__ GV, int64_t gb, int64_t gh, int64_t gt, int gist, int blk, int S, int G,
-    int per_head, const int32_t *__restrict__ idx, const float *__restrict__ gate, int kcap, float scale_log2,
-    float *__restrict__ work, uint32_t *__restrict__ counters, OT *__restrict__ O, int64_t ob, int64_t oh) {
+    int per_head, const int32_t *__restrict__ idx, const int32_t *__restrict__ nsel, const float *__restrict__ gate,
+    int kcap, float scale_log2, float *__restrict__ work, uint32_t *__restrict__ counters, OT *__restrict__ O,
+    int64_t ob, int64_t oh) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[DecodeLds<D, WPW>::BYTES];
   decode_tile_body<D, WPW, OT>(blockIdx.x, blockIdx.y, gridDim.x, lds, st, Q, qb, qh, K, V, kb, kh, kt, GK,
-                                      GV, gb, gh, gt, gist, blk, S, G, per_head, idx, gate, kcap, scale_log2, work,
+                                      GV, gb, gh, gt, gist, blk, S, G, per_head, idx, nsel, gate, kcap, scale_log2, work,
                                       counters, O, ob, oh);
 }
 
@@ -51,12 +52,13 @@ template <int D, int WPW>
 static hipError_t decode_launch(const sas_problem &p, const SeqTable &st, const DecodeShape &d, int nwg,
                                 const void *Q, const int64_t *qs, const void *K, const void *V, const int64_t *kvs,
                                 const void *gk, const void *gv, int64_t gb, int64_t gh, int64_t gt, int gist,
-                                int per_head, const int32_t *idx, const float *gate, int32_t kcap, float scale_log2,
+                                int per_head, const int32_t *idx, const int32_t *nsel, const float *gate, int32_t kcap,
+                                float scale_log2,
                                 float *work, uint32_t *counters, void *O, const int64_t *os, hipStream_t s) {
   hipLaunchKernelGGL((decode_bf16_kernel<D, WPW, uint16_t>), dim3(nwg, (unsigned)d.units), dim3(WPW * 64), 0, s,
                      st, (const uint16_t *)Q, qs[0], qs[1], (const uint16_t *)K, (const uint16_t *)V, kvs[0], kvs[1],
                      kvs[2], (const uint16_t *)gk, (const uint16_t *)gv, gb, gh, gt, gist, p.block, d.S,
-                     p.hq / p.hkv, per_head, idx, gate, kcap, scale_log2, work, counters, (uint16_t *)O, os[0],
+                     p.hq / p.hkv, per_head, idx, nsel, gate, kcap, scale_log2, work, counters, (uint16_t *)O, os[0],
                      os[1]);
   return hipGetLastError();
 }
@@ -66,7 +68,6 @@ hipError_t launch_decode_bf16(const sas_problem &p, const SeqTable &st, const vo
                               const void *gv, const int64_t *gs, int32_t sel_mode, const int32_t *idx,
                               const int32_t *nsel, const float *gate, int32_t kcap, float scale, void *O,
                               const int64_t *os, float *workspace, hipStream_t s) {
-  (void)nsel;
   const int gist = gk != nullptr;
   const int per_head = sel_mode == SAS_SEL_HEAD;
   int maxc = 0;
@@ -83,8 +84,8 @@ hipError_t launch_decode_bf16(const sas_problem &p, const SeqTable &st, const vo
   if (gist) { gb = gs[0]; gh = gs[1]; gt = gs[2]; }
   const float sl2 = scale * 1.4426950408889634f;
 #define SAS_DEC(D_, W_)                                                                                          \
-  return decode_launch<D_, W_>(p, st, d, nwg, Q, qs, K, V, kvs, gk, gv, gb, gh, gt, gist, per_head, idx, gate,   \
-                               kcap, sl2, work, counters, O, os, s)
+  return decode_launch<D_, W_>(p, st, d, nwg, Q, qs, K, V, kvs, gk, gv, gb, gh, gt, gist, per_head, idx, nsel,   \
+                               gate, kcap, sl2, work, counters, O, os, s)
   if (p.head_dim == 128) {
     if (d.wpw == 1) SAS_DEC(128, 1);
     SAS_DEC(128, 4);

@@ -347,14 +347,17 @@ struct DecodeLds {
 };
 
 // One attention workgroup: tiles bx*WPW .. bx*WPW+WPW-1 of unit u (one wave each), merged into the
-// unit's record bx; the last of the unit's nwg workgroups to arrive merges the records and writes
-// O.
+// unit's record bx (records nwg apart per unit).  A unit has nsel[u] list entries (the padding
+// past them is -1), so it needs only the first nwg_u of the nwg workgroups: the others exit
+// before touching the records, and the last of the nwg_u to arrive merges their records and
+// writes O.
 template <int D, int WPW, typename OT>
 __device__ __forceinline__ void decode_tile_body(
     int bx, int64_t u, int nwg, unsigned char *lds, SeqTable st, const uint16_t *__restrict__ Q, int64_t qb,
     int64_t qh, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, int64_t kb, int64_t kh, int64_t kt,
     const uint16_t *__restrict__ GK, const uint16_t *__restrict__ GV, int64_t gb, int64_t gh, int64_t gt, int gist,
-    int blk, int S, int G, int per_head, const int32_t *__restrict__ idx, const float *__restrict__ gate, int kcap,
+    int blk, int S, int G, int per_head, const int32_t *__restrict__ idx, const int32_t *__restrict__ nsel,
+    const float *__restrict__ gate, int kcap,
     float scale_log2, float *__restrict__ work, uint32_t *__restrict__ counters, OT *__restrict__ O, int64_t ob,
     int64_t oh) {
   constexpr int NKK = D / 32;   // MFMA k-steps over the head dim
@@ -376,7 +379,11 @@ __device__ __forceinline__ void decode_tile_body(
   const int L = st.len[b];
   const int c = (L - 1) / blk;
   const int tpb = blk / 64;
-  const int nraw = kcap * tpb;
+  // this unit's tiles: the raw tiles of its list entries, then (gist mode) one tile per 64 gists
+  const int nent = min(max(nsel[u], 0), kcap);
+  const int nraw = nent * tpb;
+  const int nwg_u = max(1, (nraw + (gist ? (c + 63) / 64 : 0) + WPW - 1) / WPW);
+  if (bx >= nwg_u) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = bx * WPW + wave;
   const int col = lane & 15, grp = lane >> 4;
@@ -540,7 +547,7 @@ __device__ __forceinline__ void decode_tile_body(
   // ---- this workgroup's record: [nh][D] acc, then m[nh], l[nh] (m in log2 units), written with
   //      device-coherent 16-byte stores so that the merging workgroup (any XCD) reads them
   const uint32_t rec_bytes = (uint32_t)rec_sz * 4u;
-  const __amdgpu_buffer_rsrc_t rr = dev_rsrc(work + u * nwg * rec_sz, nwg * rec_bytes);
+  const __amdgpu_buffer_rsrc_t rr = dev_rsrc(work + u * nwg * rec_sz, nwg_u * rec_bytes);
   const uint32_t my = bx * rec_bytes;
   if constexpr (WPW == 1) {
     if (col < nh) {
@@ -593,11 +600,11 @@ __device__ __forceinline__ void decode_tile_body(
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t old = __hip_atomic_fetch_add(&counters[u], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last_sh = (old == (uint32_t)nwg - 1);
+    last_sh = (old == (uint32_t)nwg_u - 1);
   }
   __syncthreads();
   if (!last_sh) return;
-  const int nrec = nwg;
+  const int nrec = nwg_u;
   const int tid = threadIdx.x;
   float *msh = reinterpret_cast<float *>(&vlds[0][0]);  // [nrec][nh] m, then l, then weights
   float *lsh = msh + nrec * nh;
