@@ -85,9 +85,30 @@ __device__ void wave_topk(const float *__restrict__ row, int c, bool sinkf, cons
       T = kmax;  // the largest key alone fills the budget: its first k holders in block order
       want = (uint32_t)k;
       ties = c_hi > (uint32_t)k;
+    } else if constexpr (NPL <= 8) {
+      // Few registers per lane: MSB-first bit steps below the keys' common prefix (the bits
+      // above the highest bit in which the smallest and largest key differ), each one count;
+      // an exact count of k ends the search.  (kmin != kmax here: equal keys would all count.)
+      const int top = 31 - __builtin_clz(kmin ^ kmax);
+      uint32_t prefix = top >= 31 ? 0u : (kmax & ~((2u << top) - 1u));
+      bool exact = false;
+      for (int bit = top; bit >= 0; --bit) {
+        const uint32_t cand_t = prefix | (1u << bit);
+        const uint32_t ge = count_ge(key, cand_t);
+        if (ge >= (uint32_t)k) {
+          prefix = cand_t;
+          if (ge == (uint32_t)k) {
+            exact = true;
+            break;
+          }
+        }
+      }
+      T = prefix;
+      want = exact ? (uint32_t)k : (uint32_t)k - count_ge(key, T + 1u);
+      ties = !exact;
     } else {
       // Safeguarded interpolation search for the largest key value T with at least k keys at or
-      // above it.  Invariant: count_ge(lo) = cl >= k > ch = count_ge(hi).  Each probe goes where
+      // above it (fewer probes than bit steps on 32 registers per lane).  Invariant: count_ge(lo) = cl >= k > ch = count_ge(hi).  Each probe goes where
       // a straight line between (lo, cl) and (hi, ch) reaches k -- or to the midpoint after a
       // probe that did not halve the range -- and replaces lo or hi.  A probe with exactly k keys
       // at or above it ends the search: those keys are the selection.  Otherwise the range
@@ -379,32 +400,36 @@ __device__ __forceinline__ void decode_tile_body(
   const int L = st.len[b];
   const int c = (L - 1) / blk;
   const int tpb = blk / 64;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int t = bx * WPW + wave;
+  const int col = lane & 15, grp = lane >> 4;
+  // the list entry of this wave's tile (if it is a raw tile) and its gate, loaded beside nsel so
+  // that the K/V loads wait for one load only
+  const int e = t / tpb, sub = t % tpb;
+  const int jraw = e < kcap ? idx[u * kcap + e] : -1;
+  const float graw = (gate && e < kcap) ? gate[u * kcap + e] : 0.f;
   // this unit's tiles: the raw tiles of its list entries, then (gist mode) one tile per 64 gists
   const int nent = min(max(nsel[u], 0), kcap);
   const int nraw = nent * tpb;
   const int nwg_u = max(1, (nraw + (gist ? (c + 63) / 64 : 0) + WPW - 1) / WPW);
   if (bx >= nwg_u) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = bx * WPW + wave;
-  const int col = lane & 15, grp = lane >> 4;
   const int64_t rec_sz = record_floats(nh, D);
 
-  // ---- which keys this wave's tile holds (one dependent load: the block index)
+  // ---- which keys this wave's tile holds
   const uint16_t *kbase = nullptr, *vbase = nullptr;
   int64_t rstride = 0;
   int key0 = 0, nvalid = 0;
   float gl2 = 0.f;
   uint64_t excl = 0;
   if (t < nraw) {
-    const int e = t / tpb, sub = t % tpb;
-    const int j = idx[u * kcap + e];
+    const int j = jraw;
     if (j >= 0) {
       key0 = j * blk + sub * 64;
       nvalid = min(64, L - key0);
       kbase = K + b * kb + g * kh;
       vbase = V + b * kb + g * kh;
       rstride = kt;
-      if (gate) gl2 = gate[u * kcap + e] * 1.4426950408889634f;
+      gl2 = graw * 1.4426950408889634f;
     }
   } else if (gist) {
     key0 = (t - nraw) * 64;
