@@ -86,6 +86,15 @@ def test_prefill_short_rows_per_head():
     run_case(w, [0])
 
 
+@pytest.mark.parametrize("sel", ["group", "head"])
+def test_prefill_head_dim_64(sel):
+    """d = 64: per-group units (4 heads x 128-block rows: 128-row workgroups, swizzled 16-byte copies,
+    a partial last block) and per-head units (64-row workgroups, padded one-row copies)."""
+    w = Workload(3, overrides=dict(tag="d64" + sel, seq_len=1500, tq=600, block=128 if sel == "group" else 64,
+                                   d=64, hq=8, hkv=2, sel=sel, frac_num=1, frac_den=4, sink=True, gate=True))
+    run_case(w, [0])
+
+
 def test_prefill_zero_budget_only_current_and_sink():
     w = Workload(3, overrides=dict(tag="k0", seq_len=2048, tq=2048, block=128, hq=4, hkv=1,
                                    frac_num=0, frac_den=0, k_fixed=0, sink=True, gate=True))

@@ -145,15 +145,15 @@ __device__ __forceinline__ void load_lds(const void *g, void *lds) {
   else __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
 }
 
-// BYTES per lane through a buffer resource into LDS (buffer_load ... lds): the wave writes
-// 64 x BYTES contiguously at `lds`; the lane reads rsrc + soff + voff.  Reads past the
-// resource's byte range return 0.  Row offsets stay scalar (soff), so the address needs no
-// per-lane arithmetic.  Tracked by vmcnt.
+// BYTES (4 or 16) per lane through a buffer resource into LDS (buffer_load ... lds): the wave
+// writes 64 x BYTES contiguously at `lds`, lane i at lds + BYTES * i; the lane reads
+// rsrc + soff + voff.  Row offsets can stay scalar (soff).  Tracked by vmcnt.  (2-byte copies
+// are not offered: a head-dim-64 prefill that used them read wrong values.)
 template <int BYTES>
 __device__ __forceinline__ void buf_load_lds(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voff, uint32_t soff) {
+  static_assert(BYTES == 4 || BYTES == 16, "4- or 16-byte copies");
   auto *l = (__attribute__((address_space(3))) void *)lds;
-  if constexpr (BYTES == 2) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 2, voff, soff, 0, 0);
-  else if constexpr (BYTES == 4) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 4, voff, soff, 0, 0);
+  if constexpr (BYTES == 4) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 4, voff, soff, 0, 0);
   else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, voff, soff, 0, 0);
 }
 

@@ -7,8 +7,9 @@
 // A workgroup owns NW*32 query rows of one selection unit (rows x heads of the unit,
 // flattened) and walks the unit's selected blocks in 64-key tiles:
 //   K and V tiles are copied HBM -> LDS by the buffer unit (buffer_load ... lds): 128-row
-//   workgroups copy 16 bytes per lane, whole rows per instruction, into XOR-swizzled unpadded
-//   rows; 64-row workgroups copy one row per instruction into padded rows.  128-row workgroups double-buffer: tile t+1 is in
+//   workgroups (and all head-dim-64 ones) copy 16 bytes per lane, whole rows per instruction, into
+//   XOR-swizzled unpadded rows; 64-row workgroups at head dim 128 copy one row per instruction
+//   into padded rows.  128-row workgroups double-buffer: tile t+1 is in
 //   flight while tile t is computed, and one barrier per tile hands the buffers over.  64-row
 //   workgroups keep one K and one V buffer, so that twice as many fit per CU; their copies
 //   overlap the phases of a tile that do not read that buffer.
@@ -59,17 +60,18 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
   // LDS tiles, two layouts (64 banks of 4 bytes; both keep the reads below conflict-free: a
   // 16-byte K operand read covers 16 consecutive rows at one chunk, an 8-byte transposing V read
   // 4 rows x 4 chunks x 2 halves):
-  //  SWZ (128-row workgroups): unpadded rows of D bf16, the 16-byte chunk c of row r stored at
-  //    chunk position c ^ fK(r) (K) or c ^ fV(r) (V); a 16-byte-per-lane copy writes 64 / (D / 8)
-  //    whole rows per instruction.
-  //  padded (64-row workgroups): K rows D + 8 and V rows D + 32 bf16 apart, one row per copy
-  //    instruction (D * 2 / 64 bytes per lane).  On the per-head batches these run on, which are
-  //    bound by L2 misses, it measured ~5 % faster than the swizzled copy.
-  constexpr bool SWZ = !SINGLE;
+  //  SWZ (128-row workgroups, and every D = 64 workgroup): unpadded rows of D bf16, the 16-byte
+  //    chunk c of row r stored at chunk position c ^ fK(r) (K) or c ^ fV(r) (V); a 16-byte-per-lane
+  //    copy writes 64 / (D / 8) whole rows per instruction.
+  //  padded (64-row workgroups, D = 128): K rows D + 8 and V rows D + 32 bf16 apart, one row per
+  //    copy instruction (4 bytes per lane).  On the per-head batches these run on, which are bound
+  //    by L2 misses, it measured ~5 % faster than the swizzled copy.  (A D = 64 row would take
+  //    2 bytes per lane, a copy width that does not land packed in LDS.)
+  constexpr bool SWZ = !SINGLE || D == 64;
   constexpr int ROWK = SWZ ? D : D + 8, ROWV = SWZ ? D : D + 32;
   constexpr int CPR = D / 8;         // 16-byte chunks per row
   constexpr int RPI = SWZ ? 64 / CPR : 1;  // rows per copy instruction
-  constexpr int DMA = SWZ ? 16 : D * 2 / 64;  // bytes per lane of one copy instruction
+  constexpr int DMA = SWZ ? 16 : 4;  // bytes per lane of one copy instruction
   __shared__ __attribute__((aligned(16))) uint16_t klds2[NBUF][64 * ROWK];
   __shared__ __attribute__((aligned(16))) uint16_t vlds2[NBUF][64 * ROWV];
   auto fK = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
