@@ -101,6 +101,23 @@ def test_prefill_zero_budget_only_current_and_sink():
     run_case(w, [0])
 
 
+def test_decode_group_and_gist_d64():
+    """d = 64 on the bf16 decode path: per-group lists with sink and gate, and gist mode."""
+    w = Workload(2, overrides=dict(tag="g64", seq_lens=[300, 2000, 4096, 1000], batch=4, d=64, k_fixed=4,
+                                   sink=True, gate=True, hq=8, hkv=2, seq_len=None))
+    run_case(w, list(range(4)))
+    wg = Workload(4, overrides=dict(tag="gist64", d=64, seq_len=5000, batch=2, k_fixed=6, hq=8, hkv=2))
+    run_case(wg, [0, 1])
+
+
+def test_decode_per_head_sixteen_heads_per_kv_head():
+    """Per-head selection with G = 16: each wave of the fused selection's last workgroup takes
+    four units in turn; 5 % budget over ~80-700 candidates."""
+    w = Workload(2, overrides=dict(tag="h16", seq_lens=[45000, 5000], batch=2, sel="head", hq=32, hkv=2,
+                                   k_fixed=0, frac_num=1, frac_den=20, gate=True, seq_len=None))
+    run_case(w, [0, 1])
+
+
 def test_decode_f32_and_gist_f32():
     w = Workload(2, overrides=dict(tag="f32", dtype="f32", seq_lens=[100, 1500, 4096, 64], batch=4, k_fixed=3,
                                    gate=True, hq=8, hkv=2))

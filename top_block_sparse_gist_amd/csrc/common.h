@@ -158,9 +158,11 @@ __device__ __forceinline__ void buf_load_lds(__amdgpu_buffer_rsrc_t r, void *lds
 }
 
 // Sum over aligned groups of W lanes (W = 8, 16 or 32), valid in the group's first lane (lane %
-// W == 0).  Within a 16-lane row the adds use DPP (quad xor 1, quad xor 2, row rotate 4, row
-// rotate 8: no LDS round trip); W = 32 adds the other row with one cross-lane read.  The order of
-// the adds is fixed, so every kernel that uses it gets the same bits for the same inputs.
+// W == 0).  Within a 16-lane row the adds use DPP (quad xor 1, quad xor 2, then row rotates: a
+// rotate right by N hands lane i the value of lane i - N mod 16, so rotating by 12 adds the next
+// quad, lanes i + 4, and rotating by 8 the other half row; no LDS round trip); W = 32 adds the
+// other row with one cross-lane read.  The order of the adds is fixed, so every kernel that uses
+// it gets the same bits for the same inputs.
 template <int W>
 __device__ __forceinline__ float group_sum(float s) {
   static_assert(W == 8 || W == 16 || W == 32, "group of 8, 16 or 32 lanes");
@@ -169,7 +171,7 @@ __device__ __forceinline__ float group_sum(float s) {
   };
   s += dpp(s, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]: lane ^ 1
   s += dpp(s, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]: lane ^ 2
-  s += dpp(s, std::integral_constant<int, 0x124>{});  // row_ror:4: quads q and q+1
+  s += dpp(s, std::integral_constant<int, 0x12C>{});  // row_ror:12: quads q and q+1
   if constexpr (W >= 16) s += dpp(s, std::integral_constant<int, 0x128>{});  // row_ror:8: whole row
   if constexpr (W == 32) s += __shfl_xor(s, 16, 64);
   return s;
