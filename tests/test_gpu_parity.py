@@ -118,6 +118,26 @@ def test_decode_per_head_sixteen_heads_per_kv_head():
     run_case(w, [0, 1])
 
 
+def test_decode_group_block128_sink_gate():
+    w = Workload(2, overrides=dict(tag="g128", seq_lens=[5000, 300, 129, 8000], batch=4, block=128, k_fixed=3,
+                                   sink=True, gate=True, hq=8, hkv=2, seq_len=None))
+    run_case(w, list(range(4)))
+
+
+def test_decode_beyond_fused_selection_limit():
+    """Current block 2187 > 2048: selection by the two calls, then a 10-entry list in decode."""
+    w = Workload(2, overrides=dict(tag="long", seq_lens=[140000], batch=1, hq=8, hkv=2, k_fixed=8, sink=True,
+                                   gate=True, seq_len=None))
+    run_case(w, [0])
+
+
+def test_prefill_group_few_rows():
+    """20 query rows x 2 heads per unit: 64-row workgroups on per-group lists."""
+    w = Workload(3, overrides=dict(tag="few", seq_len=700, tq=20, block=64, hq=4, hkv=2, frac_num=1, frac_den=4,
+                                   sink=True, gate=True))
+    run_case(w, [0])
+
+
 def test_decode_f32_and_gist_f32():
     w = Workload(2, overrides=dict(tag="f32", dtype="f32", seq_lens=[100, 1500, 4096, 64], batch=4, k_fixed=3,
                                    gate=True, hq=8, hkv=2))
