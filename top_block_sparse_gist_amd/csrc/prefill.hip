@@ -28,6 +28,7 @@
 // dealt round-robin to the XCDs; the row tiles of one unit, which share its K/V tiles, run on
 // the same XCD (one L2).
 #include <algorithm>
+#include <numeric>
 #include <type_traits>
 
 #include "common.h"
@@ -49,7 +50,7 @@ template <int D, int NW, int BLK>
 __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
     SeqTable st, SeqOrder ord, const uint16_t *__restrict__ Q, int64_t qb, int64_t qh, int64_t qt,
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, int64_t kb, int64_t kh, int64_t kt,
-    int tq, int blk, int S, int QB, int G, int per_head, int batch, int rtiles,
+    int tq, int blk, int S, int QB, int G, int per_head, int batch, int rtiles, int pchunks,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ nsel, const float *__restrict__ gate,
     int kcap, float scale_log2, uint16_t *__restrict__ O, int64_t ob, int64_t oh, int64_t ot) {
   constexpr int NKK = D / 16;        // k-steps of S^T over the head dim
@@ -78,31 +79,37 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
   auto fV = [](int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); };
 
   // ---- workgroup -> (query block i (heavy first), sequence, selector head, row tile)
-  // Workgroup k runs on XCD k % 8.  Units (in heavy-first order) are dealt round-robin to the
-  // XCDs, and all row tiles of a unit go to the same XCD, one after another, so they share the
-  // unit's K/V tiles in that XCD's L2 and every XCD gets an even share of heavy and light units.
-  // The grid holds 8 * ceil(units / 8) * rtiles workgroups; slots past the last unit exit.
+  // Workgroup k runs on XCD k % 8 (and the k-th workgroups of the XCDs start at about the same
+  // time); all row tiles of a unit go to the same XCD, one after another, so they share the unit's
+  // K/V tiles in that XCD's L2.
   const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
-  const int slot = (q / rtiles) * 8 + xcd;
   const int rt = q % rtiles;
-  if (slot >= QB * batch * S) return;
   int s, b, i;
   if (per_head) {
-    // Per-head lists share few tiles across the batch but many within one (sequence, KV head)
-    // (its heads and query blocks pick from the same key blocks): walk the units (sequence, KV
-    // head)-major, longest sequences first, heavy-first within, the group's heads adjacent, so
-    // that the K/V slabs in use at any time fit the MALL and each tile comes from HBM about once.
-    int rest = slot;
-    const int hh = rest % G;
-    rest /= G;
-    i = QB - 1 - rest % QB;
-    rest /= QB;
+    // Per-head lists share few tiles across the batch but many within one (sequence, KV head):
+    // each key block is picked by several of the pair's QB x G units, whose ascending lists of
+    // about the same length move through the key range at about the same pace.  So each pair runs
+    // on one XCD with its units dispatched together (query blocks heavy-first, the group's heads
+    // adjacent), and the units that pick a block read it while it is in that XCD's L2.  Pairs go
+    // longest sequence first, pair p to XCD p % 8; with fewer pairs than XCDs, or a count that
+    // does not split evenly, each pair is cut into pchunks interleaved query-block chunks
+    // (pairs * pchunks is a multiple of 8), chunk cid on XCD cid % 8.
     const int hkv = S / G;
-    s = (rest % hkv) * G + hh;
-    b = ord.b[rest / hkv];
+    const int upc = ((QB + pchunks - 1) / pchunks) * G;  // units per chunk
+    const int qq = q / rtiles;
+    const int cid = (qq / upc) * 8 + xcd;
+    if (cid >= batch * hkv * pchunks) return;
+    const int r = qq % upc;
+    const int pair = cid / pchunks, ch = cid % pchunks;
+    i = QB - 1 - (ch + pchunks * (r / G));
+    if (i < 0) return;
+    s = (pair % hkv) * G + r % G;
+    b = ord.b[pair / hkv];
   } else {
-    // per-group units: heavy-first over the whole batch
-    int rest = slot;
+    // per-group units, heavy-first over the whole batch, dealt round-robin to the XCDs so that
+    // every XCD gets an even share of heavy and light units; slots past the last unit exit
+    int rest = (q / rtiles) * 8 + xcd;
+    if (rest >= QB * batch * S) return;
     s = rest % S;
     rest /= S;
     b = rest % batch;
@@ -379,14 +386,19 @@ static hipError_t prefill_dispatch(const sas_problem &p, const SeqTable &st, con
   const int rows_max = min(tq, p.block);
   const int rtiles = cdiv(rows_max * nh, NW * 32);
   const int64_t units = (int64_t)QB * p.batch * S;
-  const int64_t nwg = 8 * cdiv64(units, 8) * rtiles;
+  // per-head: (sequence, KV head) pairs, each cut into pchunks query-block chunks so that the
+  // chunk count is a multiple of the 8 XCDs
+  const int pairs = p.batch * p.hkv;
+  const int pchunks = per_head ? 8 / std::gcd(pairs, 8) : 1;
+  const int64_t nwg = per_head ? 8 * cdiv64((int64_t)pairs * pchunks, 8) * (cdiv(QB, pchunks) * G) * rtiles
+                               : 8 * cdiv64(units, 8) * rtiles;
   const float scale_log2 = scale * 1.4426950408889634f;
   SeqOrder ord{};
   for (int b = 0; b < p.batch; ++b) ord.b[b] = b;
   std::stable_sort(ord.b, ord.b + p.batch, [&](int x, int y) { return st.len[x] > st.len[y]; });
   hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, BLK>), dim3((unsigned)nwg), dim3(NW * 64), 0, s, st, ord,
                      (const uint16_t *)Q, qs[0], qs[1], qs[2], (const uint16_t *)K, (const uint16_t *)V, kvs[0],
-                     kvs[1], kvs[2], tq, p.block, S, QB, G, per_head, p.batch, rtiles, idx, nsel, gate, kcap,
+                     kvs[1], kvs[2], tq, p.block, S, QB, G, per_head, p.batch, rtiles, pchunks, idx, nsel, gate, kcap,
                      scale_log2, (uint16_t *)O, os[0], os[1], os[2]);
   return hipGetLastError();
 }
