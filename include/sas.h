@@ -175,7 +175,10 @@ sas_status sas_select_decode(const sas_problem *p, const void *Q, const int64_t 
  *   workspace: sas_sparse_decode_workspace() bytes: per-unit arrival counters followed by
  *   the split-K partial records (bf16 path; 0 bytes for fp32).  The counters must be zero
  *   before the workspace's first use; every call leaves them zero again.  Calls that share
- *   one workspace must not overlap in time. */
+ *   one workspace must not overlap in time.
+ *   bf16: SAS_ERR_UNSUPPORTED when kcap (plus the gist tiles) needs more split-K records per
+ *   unit than the in-kernel merge can stage (with 16 heads per KV head at d 128: about 3000
+ *   list entries of 64 keys; far more with fewer heads). */
 size_t sas_sparse_decode_workspace(const sas_problem *p, int32_t sel_mode, int32_t kcap,
                                    int32_t gist);
 sas_status sas_sparse_decode(const sas_problem *p, const void *Q, const int64_t q_stride[2],

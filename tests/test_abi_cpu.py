@@ -153,6 +153,15 @@ def test_attention_validation_codes():
     assert need > 0
     assert lib.sas_sparse_decode(C.byref(p), FAKE, qs2, FAKE, FAKE, kvs, None, None, None, 0, FAKE, FAKE, None, 8,
                                  0.0, FAKE, qs2, FAKE, need - 1, None) == _lib.SAS_ERR_WORKSPACE
+    # a list capacity whose split-K records per unit exceed what the merge can stage in LDS:
+    # 16 heads per KV head at d 128 hold 383 records; kcap 4000 at two tiles per wave needs 500
+    p16, a16 = _problem(hq=32, hkv=2)
+    need16 = lib.sas_sparse_decode_workspace(C.byref(p16), 0, 4000, 0)
+    assert lib.sas_sparse_decode(C.byref(p16), FAKE, qs2, FAKE, FAKE, kvs, None, None, None, 0, FAKE, FAKE, None,
+                                 4000, 0.0, FAKE, qs2, FAKE, need16, None) == _lib.SAS_ERR_UNSUPPORTED
+    assert b"merge holds 383" in lib.sas_last_error()
+    need_ok = lib.sas_sparse_decode_workspace(C.byref(p16), 0, 3000, 0)
+    assert need_ok > 0  # 3000 entries: 375 records, within the merge
     # more than 16 query heads per KV head in per-group decode
     p9, a9 = _problem(hq=34, hkv=2)
     need9 = lib.sas_sparse_decode_workspace(C.byref(p9), 0, 8, 0)

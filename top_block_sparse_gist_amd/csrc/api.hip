@@ -336,6 +336,10 @@ sas_status sas_sparse_decode(const sas_problem *p, const void *Q, const int64_t 
   }
   if (sel_mode == SAS_SEL_GROUP && p->hq / p->hkv > 16)
     return fail(SAS_ERR_UNSUPPORTED, "per-group decode supports at most 16 query heads per KV head");
+  int nwg = 0, cap = 0;
+  if (!decode_merge_fits(*p, tab, sel_mode, kcap, gist ? 1 : 0, &nwg, &cap))
+    return fail(SAS_ERR_UNSUPPORTED, "kcap %d needs %d split-K records per unit; the merge holds %d", kcap, nwg,
+                cap);
   const size_t need = decode_workspace_bytes(*p, sel_mode, kcap, gist ? 1 : 0);
   if (!workspace || workspace_bytes < need)
     return fail(SAS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);

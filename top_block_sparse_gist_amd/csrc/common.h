@@ -239,5 +239,9 @@ constexpr int32_t SELECT_DECODE_MAX_C = 2048;
 
 // Bytes of split-K partials the decode path needs (host formula shared with the size query).
 size_t decode_workspace_bytes(const sas_problem &p, int32_t sel_mode, int32_t kcap, int32_t gist);
+// whether the split-K merge of the bf16 decode fits its LDS for this list capacity (nwg records
+// per unit against cap)
+bool decode_merge_fits(const sas_problem &p, const SeqTable &st, int32_t sel_mode, int32_t kcap, int32_t gist,
+                       int *nwg, int *cap);
 
 }  // namespace sas

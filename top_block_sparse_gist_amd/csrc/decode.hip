@@ -25,8 +25,8 @@
 
 namespace sas {
 
-template <int D, int WPW, typename OT>
-__global__ __launch_bounds__(WPW * 64) void decode_bf16_kernel(
+template <int D, int WPW, int TPW, typename OT>
+__global__ __launch_bounds__(WPW * 64) __attribute__((amdgpu_waves_per_eu(2))) void decode_bf16_kernel(
     SeqTable st, const uint16_t *__restrict__ Q, int64_t qb, int64_t qh, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, int64_t kb, int64_t kh, int64_t kt, const uint16_t *__restrict__ GK,
     const uint16_t *__restrict__ GV, int64_t gb, int64_t gh, int64_t gt, int gist, int blk, int S, int G,
@@ -34,12 +34,23 @@ __global__ __launch_bounds__(WPW * 64) void decode_bf16_kernel(
     int kcap, float scale_log2, float *__restrict__ work, uint32_t *__restrict__ counters, OT *__restrict__ O,
     int64_t ob, int64_t oh) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[DecodeLds<D, WPW>::BYTES];
-  decode_tile_body<D, WPW, OT>(blockIdx.x, blockIdx.y, gridDim.x, lds, st, Q, qb, qh, K, V, kb, kh, kt, GK,
+  decode_tile_body<D, WPW, TPW, OT>(blockIdx.x, blockIdx.y, gridDim.x, lds, st, Q, qb, qh, K, V, kb, kh, kt, GK,
                                       GV, gb, gh, gt, gist, blk, S, G, per_head, idx, nsel, gate, kcap, scale_log2, work,
                                       counters, O, ob, oh);
 }
 
 // ---- host side -------------------------------------------------------------------------------
+bool decode_merge_fits(const sas_problem &p, const SeqTable &st, int32_t sel_mode, int32_t kcap, int32_t gist,
+                       int *nwg_out, int *cap_out) {
+  int maxc = 0;
+  for (int b = 0; b < p.batch; ++b) maxc = max(maxc, (st.len[b] - 1) / p.block);
+  const DecodeShape d = decode_shape(p, sel_mode, kcap, gist, maxc);
+  const int tpw = decode_tiles_per_wave(d);
+  *nwg_out = (d.tiles_cap + d.wpw * tpw - 1) / (d.wpw * tpw);
+  *cap_out = decode_merge_capacity(d.nh, p.head_dim, d.wpw);
+  return *nwg_out <= *cap_out;
+}
+
 size_t decode_workspace_bytes(const sas_problem &p, int32_t sel_mode, int32_t kcap, int32_t gist) {
   const int maxc = (p.max_len - 1) / p.block;
   DecodeShape d = decode_shape(p, sel_mode, kcap, gist, maxc);
@@ -48,14 +59,14 @@ size_t decode_workspace_bytes(const sas_problem &p, int32_t sel_mode, int32_t kc
   return counters + (size_t)d.units * d.nwg_cap * record_floats(d.nh, p.head_dim) * sizeof(float);
 }
 
-template <int D, int WPW>
+template <int D, int WPW, int TPW>
 static hipError_t decode_launch(const sas_problem &p, const SeqTable &st, const DecodeShape &d, int nwg,
                                 const void *Q, const int64_t *qs, const void *K, const void *V, const int64_t *kvs,
                                 const void *gk, const void *gv, int64_t gb, int64_t gh, int64_t gt, int gist,
                                 int per_head, const int32_t *idx, const int32_t *nsel, const float *gate, int32_t kcap,
                                 float scale_log2,
                                 float *work, uint32_t *counters, void *O, const int64_t *os, hipStream_t s) {
-  hipLaunchKernelGGL((decode_bf16_kernel<D, WPW, uint16_t>), dim3(nwg, (unsigned)d.units), dim3(WPW * 64), 0, s,
+  hipLaunchKernelGGL((decode_bf16_kernel<D, WPW, TPW, uint16_t>), dim3(nwg, (unsigned)d.units), dim3(WPW * 64), 0, s,
                      st, (const uint16_t *)Q, qs[0], qs[1], (const uint16_t *)K, (const uint16_t *)V, kvs[0], kvs[1],
                      kvs[2], (const uint16_t *)gk, (const uint16_t *)gv, gb, gh, gt, gist, p.block, d.S,
                      p.hq / p.hkv, per_head, idx, nsel, gate, kcap, scale_log2, work, counters, (uint16_t *)O, os[0],
@@ -76,22 +87,23 @@ hipError_t launch_decode_bf16(const sas_problem &p, const SeqTable &st, const vo
   const DecodeShape cap = decode_shape(p, sel_mode, kcap, gist, (p.max_len - 1) / p.block);
   DecodeShape d = decode_shape(p, sel_mode, kcap, gist, maxc);
   d.wpw = cap.wpw;
-  const int nwg = (d.tiles_cap + d.wpw - 1) / d.wpw;
+  const int tpw = decode_tiles_per_wave(d);
+  const int nwg = (d.tiles_cap + d.wpw * tpw - 1) / (d.wpw * tpw);
   uint32_t *counters = reinterpret_cast<uint32_t *>(workspace);
   const size_t cbytes = ((size_t)d.units * 4 + 255) / 256 * 256;
   float *work = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + cbytes);
   int64_t gb = 0, gh = 0, gt = 0;
   if (gist) { gb = gs[0]; gh = gs[1]; gt = gs[2]; }
   const float sl2 = scale * 1.4426950408889634f;
-#define SAS_DEC(D_, W_)                                                                                          \
-  return decode_launch<D_, W_>(p, st, d, nwg, Q, qs, K, V, kvs, gk, gv, gb, gh, gt, gist, per_head, idx, nsel,   \
-                               gate, kcap, sl2, work, counters, O, os, s)
+#define SAS_DEC(D_, T_)                                                                                          \
+  return decode_launch<D_, 4, T_>(p, st, d, nwg, Q, qs, K, V, kvs, gk, gv, gb, gh, gt, gist, per_head, idx, nsel, \
+                                  gate, kcap, sl2, work, counters, O, os, s)
   if (p.head_dim == 128) {
-    if (d.wpw == 1) SAS_DEC(128, 1);
-    SAS_DEC(128, 4);
+    if (tpw == 2) SAS_DEC(128, 2);
+    SAS_DEC(128, 1);
   }
-  if (d.wpw == 1) SAS_DEC(64, 1);
-  SAS_DEC(64, 4);
+  if (tpw == 2) SAS_DEC(64, 2);
+  SAS_DEC(64, 1);
 #undef SAS_DEC
 }
 

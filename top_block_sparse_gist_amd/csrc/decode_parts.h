@@ -367,12 +367,14 @@ struct DecodeLds {
   static constexpr int BYTES = TILE_BYTES + SMALL_FLOATS * 4;
 };
 
-// One attention workgroup: tiles bx*WPW .. bx*WPW+WPW-1 of unit u (one wave each), merged into the
+// One attention workgroup: tiles bx*WPW*TPW .. +WPW*TPW-1 of unit u (TPW = 1 or 2 per wave: wave w
+// takes tiles w and w + WPW of the workgroup's range, the second one's K/V loads issued as soon as
+// the first one's registers are consumed, so they overlap its softmax and PV), merged into the
 // unit's record bx (records nwg apart per unit).  A unit has nsel[u] list entries (the padding
 // past them is -1), so it needs only the first nwg_u of the nwg workgroups: the others exit
 // before touching the records, and the last of the nwg_u to arrive merges their records and
 // writes O.
-template <int D, int WPW, typename OT>
+template <int D, int WPW, int TPW, typename OT>
 __device__ __forceinline__ void decode_tile_body(
     int bx, int64_t u, int nwg, unsigned char *lds, SeqTable st, const uint16_t *__restrict__ Q, int64_t qb,
     int64_t qh, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, int64_t kb, int64_t kh, int64_t kt,
@@ -401,68 +403,86 @@ __device__ __forceinline__ void decode_tile_body(
   const int c = (L - 1) / blk;
   const int tpb = blk / 64;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int t = bx * WPW + wave;
   const int col = lane & 15, grp = lane >> 4;
-  // the list entry of this wave's tile (if it is a raw tile) and its gate, loaded beside nsel so
-  // that the K/V loads wait for one load only
-  const int e = t / tpb, sub = t % tpb;
-  const int jraw = e < kcap ? idx[u * kcap + e] : -1;
-  const float graw = (gate && e < kcap) ? gate[u * kcap + e] : 0.f;
+  // this wave's tiles, and their list entries and gates, loaded beside nsel so that the K/V loads
+  // wait for one load only
+  int tt[TPW], jraw[TPW];
+  float graw[TPW];
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) {
+    tt[k] = bx * WPW * TPW + k * WPW + wave;
+    const int e = tt[k] / tpb;
+    jraw[k] = e < kcap ? idx[u * kcap + e] : -1;
+    graw[k] = (gate && e < kcap) ? gate[u * kcap + e] : 0.f;
+  }
   // this unit's tiles: the raw tiles of its list entries, then (gist mode) one tile per 64 gists
   const int nent = min(max(nsel[u], 0), kcap);
   const int nraw = nent * tpb;
-  const int nwg_u = max(1, (nraw + (gist ? (c + 63) / 64 : 0) + WPW - 1) / WPW);
+  const int nwg_u = max(1, (nraw + (gist ? (c + 63) / 64 : 0) + WPW * TPW - 1) / (WPW * TPW));
   if (bx >= nwg_u) return;
   const int64_t rec_sz = record_floats(nh, D);
 
-  // ---- which keys this wave's tile holds
-  const uint16_t *kbase = nullptr, *vbase = nullptr;
-  int64_t rstride = 0;
-  int key0 = 0, nvalid = 0;
-  float gl2 = 0.f;
-  uint64_t excl = 0;
-  if (t < nraw) {
-    const int j = jraw;
-    if (j >= 0) {
-      key0 = j * blk + sub * 64;
-      nvalid = min(64, L - key0);
-      kbase = K + b * kb + g * kh;
-      vbase = V + b * kb + g * kh;
-      rstride = kt;
-      gl2 = graw * 1.4426950408889634f;
-    }
-  } else if (gist) {
-    key0 = (t - nraw) * 64;
-    nvalid = min(64, c - key0);
-    kbase = GK + b * gb + g * gh;
-    vbase = GV + b * gb + g * gh;
-    rstride = gt;
-    if (nvalid > 0) {
-      // gists of selected chunks are replaced by their raw tokens: exclude them
-      for (int e0 = 0; e0 < kcap; e0 += 64) {
-        uint64_t bit = 0;
-        if (e0 + lane < kcap) {
-          const int j = idx[u * kcap + e0 + lane];
-          if (j >= key0 && j < key0 + 64) bit = 1ull << (j - key0);
-        }
+  // ---- which keys tile k of this wave holds
+  struct Tile {
+    const uint16_t *kbase, *vbase;
+    int64_t rstride;
+    int key0, nvalid;
+    float gl2;
+    uint64_t excl;
+  };
+  auto describe = [&](int k) {
+    Tile d{nullptr, nullptr, 0, 0, 0, 0.f, 0ull};
+    const int tk = tt[k];
+    if (tk < nraw) {
+      const int j = jraw[k];
+      if (j >= 0) {
+        d.key0 = j * blk + (tk % tpb) * 64;
+        d.nvalid = min(64, L - d.key0);
+        d.kbase = K + b * kb + g * kh;
+        d.vbase = V + b * kb + g * kh;
+        d.rstride = kt;
+        d.gl2 = graw[k] * 1.4426950408889634f;
+      }
+    } else if (gist) {
+      d.key0 = (tk - nraw) * 64;
+      d.nvalid = min(64, c - d.key0);
+      d.kbase = GK + b * gb + g * gh;
+      d.vbase = GV + b * gb + g * gh;
+      d.rstride = gt;
+      if (d.nvalid > 0) {
+        // gists of selected chunks are replaced by their raw tokens: exclude them
+        for (int e0 = 0; e0 < kcap; e0 += 64) {
+          uint64_t bit = 0;
+          if (e0 + lane < kcap) {
+            const int j = idx[u * kcap + e0 + lane];
+            if (j >= d.key0 && j < d.key0 + 64) bit = 1ull << (j - d.key0);
+          }
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-          const uint32_t lo = __shfl_xor((uint32_t)bit, o, 64);
-          const uint32_t hi = __shfl_xor((uint32_t)(bit >> 32), o, 64);
-          bit |= ((uint64_t)hi << 32) | lo;
+          for (int o = 32; o >= 1; o >>= 1) {
+            const uint32_t lo = __shfl_xor((uint32_t)bit, o, 64);
+            const uint32_t hi = __shfl_xor((uint32_t)(bit >> 32), o, 64);
+            bit |= ((uint64_t)hi << 32) | lo;
+          }
+          d.excl |= bit;
         }
-        excl |= bit;
       }
     }
-  }
-  nvalid = max(nvalid, 0);
+    d.nvalid = max(d.nvalid, 0);
+    return d;
+  };
+  Tile tl[TPW];
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) tl[k] = describe(k);
+  bool any = false;
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) any = any || tl[k].nvalid > 0;
 
   // ---- Q^T as the B operand: lane -> head `col`, dims 32*kk + 8*grp .. +8
   bf16x8 qreg[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (col < nh && nvalid > 0)
+    if (col < nh && any)
       v = *reinterpret_cast<const u32x4 *>(Q + b * qb + (int64_t)(h0 + col) * qh + 32 * kk + 8 * grp);
     qreg[kk] = as_bf16x8(v);
   }
@@ -472,97 +492,118 @@ __device__ __forceinline__ void decode_tile_body(
 #pragma unroll
   for (int x = 0; x < NDT; ++x) acc_o[x] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (nvalid > 0) {
-    // ---- K straight to A-operand registers, V rows to registers (then LDS)
-    u32x4 kreg[4][NKK];
+  // ---- K straight to A-operand registers, V rows to registers (then LDS)
+  constexpr int VCH = D / 8;  // 16-byte chunks per V row; VCH loads per lane
+  u32x4 kreg[4][NKK];
+  u32x4 vreg[VCH];
+  auto issue = [&](const Tile &d) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const int key = mt * 16 + col;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         u32x4 v = {0u, 0u, 0u, 0u};
-        if (key < nvalid)
-          v = *reinterpret_cast<const u32x4 *>(kbase + (int64_t)(key0 + key) * rstride + 32 * kk + 8 * grp);
+        if (key < d.nvalid)
+          v = *reinterpret_cast<const u32x4 *>(d.kbase + (int64_t)(d.key0 + key) * d.rstride + 32 * kk + 8 * grp);
         kreg[mt][kk] = v;
       }
     }
-    constexpr int VCH = D / 8;  // 16-byte chunks per V row; VCH loads per lane
-    u32x4 vreg[VCH];
 #pragma unroll
     for (int x = 0; x < VCH; ++x) {
       const int e = x * 64 + lane;
       const int key = e / VCH, ch = e % VCH;
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (key < nvalid) v = *reinterpret_cast<const u32x4 *>(vbase + (int64_t)(key0 + key) * rstride + ch * 8);
+      if (key < d.nvalid) v = *reinterpret_cast<const u32x4 *>(d.vbase + (int64_t)(d.key0 + key) * d.rstride + ch * 8);
       vreg[x] = v;
     }
-    // ---- S^T = K Q^T
+  };
+  uint16_t *vl = vlds[wave];
+  issue(tl[0]);
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) {
+    const Tile &d = tl[k];
     f32x4 sacc[4];
+    if (d.nvalid > 0) {
+      // ---- S^T = K Q^T
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kreg[mt][kk]), qreg[kk], a, 0, 0, 0);
-      sacc[mt] = a;
-    }
-    uint16_t *vl = vlds[wave];
-#pragma unroll
-    for (int x = 0; x < VCH; ++x) {
-      const int e = x * 64 + lane;
-      const int key = e / VCH, ch = e % VCH;
-      *reinterpret_cast<u32x4 *>(vl + key * VROW + ch * 8) = vreg[x];
-    }
-    // ---- softmax over the tile's keys, per head column
-    float mx = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = mt * 16 + 4 * grp + r;
-        const bool ok = key < nvalid && !((excl >> key) & 1ull);
-        const float v = ok ? sacc[mt][r] * scale_log2 + gl2 : -INFINITY;
-        sacc[mt][r] = v;
-        mx = fmaxf(mx, v);
+        for (int kk = 0; kk < NKK; ++kk)
+          a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kreg[mt][kk]), qreg[kk], a, 0, 0, 0);
+        sacc[mt] = a;
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    m_run = mx;
-    const float mref = (mx == -INFINITY) ? 0.f : mx;
-    float ls = 0.f;
+      // the V tile region is this wave's own: the reads of the previous tile's PV precede these
+      // writes in the wave's LDS queue
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = __builtin_amdgcn_exp2f(sacc[mt][r] - mref);
-        sacc[mt][r] = p;
-        ls += p;
+      for (int x = 0; x < VCH; ++x) {
+        const int e = x * 64 + lane;
+        const int key = e / VCH, ch = e % VCH;
+        *reinterpret_cast<u32x4 *>(vl + key * VROW + ch * 8) = vreg[x];
       }
-    l_run = ls;
-    // P^T as the B operand of each 32-key step (keys 32ks + 4grp + {0..3} and +16)
-    bf16x8 preg[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      u32x4 w;
-      w[0] = pack_bf16x2(sacc[2 * ks][0], sacc[2 * ks][1]);
-      w[1] = pack_bf16x2(sacc[2 * ks][2], sacc[2 * ks][3]);
-      w[2] = pack_bf16x2(sacc[2 * ks + 1][0], sacc[2 * ks + 1][1]);
-      w[3] = pack_bf16x2(sacc[2 * ks + 1][2], sacc[2 * ks + 1][3]);
-      preg[ks] = as_bf16x8(w);
     }
-    // the V tile is written and read by this wave only: wait for its LDS writes
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    // ---- O^T = V^T P^T; the V^T operand (dim 16dt + col, keys 32ks + 4grp + {0..3} then
-    //      32ks + 16 + 4grp + {0..3}) comes from two transpose reads of the row-major tile
+    // the registers are free: the next tile's loads fly during this tile's softmax and PV
+    if (k + 1 < TPW) issue(tl[k + 1]);
+    if (d.nvalid > 0) {
+      // ---- online softmax over the tile's keys, per head column
+      float mx = -INFINITY;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = mt * 16 + 4 * grp + r;
+          const bool ok = key < d.nvalid && !((d.excl >> key) & 1ull);
+          const float v = ok ? sacc[mt][r] * scale_log2 + d.gl2 : -INFINITY;
+          sacc[mt][r] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      if (k > 0) {
+        // rescale what the earlier tiles left (alpha 0 while m_run is still -inf)
+        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int x = 0; x < NDT; ++x) acc_o[x] *= alpha;
+      }
+      m_run = m_new;
+      const float mref = (m_new == -INFINITY) ? 0.f : m_new;
+      float ls = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(sacc[mt][r] - mref);
+          sacc[mt][r] = p;
+          ls += p;
+        }
+      l_run += ls;
+      // P^T as the B operand of each 32-key step (keys 32ks + 4grp + {0..3} and +16)
+      bf16x8 preg[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const uint16_t *src = vl + (ks * 32 + 4 * grp + (col >> 2)) * VROW + dt * 16 + 4 * (col & 3);
-        const u32x2 lo = lds_read_tr16(src);
-        const u32x2 hi = lds_read_tr16(src + 16 * VROW);
-        const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-        acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w), preg[ks], acc_o[dt], 0, 0, 0);
+        u32x4 w;
+        w[0] = pack_bf16x2(sacc[2 * ks][0], sacc[2 * ks][1]);
+        w[1] = pack_bf16x2(sacc[2 * ks][2], sacc[2 * ks][3]);
+        w[2] = pack_bf16x2(sacc[2 * ks + 1][0], sacc[2 * ks + 1][1]);
+        w[3] = pack_bf16x2(sacc[2 * ks + 1][2], sacc[2 * ks + 1][3]);
+        preg[ks] = as_bf16x8(w);
+      }
+      // the V tile is written and read by this wave only: wait for its LDS writes
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+      // ---- O^T += V^T P^T; the V^T operand (dim 16dt + col, keys 32ks + 4grp + {0..3} then
+      //      32ks + 16 + 4grp + {0..3}) comes from two transpose reads of the row-major tile
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const uint16_t *src = vl + (ks * 32 + 4 * grp + (col >> 2)) * VROW + dt * 16 + 4 * (col & 3);
+          const u32x2 lo = lds_read_tr16(src);
+          const u32x2 hi = lds_read_tr16(src + 16 * VROW);
+          const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+          acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w), preg[ks], acc_o[dt], 0, 0, 0);
+        }
       }
     }
   }
@@ -721,17 +762,24 @@ static inline DecodeShape decode_shape(const sas_problem &p, int32_t sel_mode, i
   d.nh = per_head ? 1 : p.hq / p.hkv;
   d.units = (int64_t)p.batch * d.S;
   d.tiles_cap = kcap * (p.block / 64) + (gist ? (maxc + 63) / 64 : 0);
-  // one wave per workgroup keeps every CU busy; wide units (many heads x many tiles) merge
-  // 4 waves per workgroup first so that the final merge reads fewer records
-  d.wpw = 4;
-  auto fits = [&](int wpw) {
-    const int nwg = (d.tiles_cap + wpw - 1) / wpw;
-    const int lds = wpw * 64 * (p.head_dim + VPAD) * 2;
-    return 12 * nwg * d.nh + 16 + 16 * 64 * wpw <= lds;
-  };
-  if (!fits(d.wpw)) d.wpw = 4;
-  d.nwg_cap = (d.tiles_cap + d.wpw - 1) / d.wpw;
+  d.wpw = 4;  // 4 waves per workgroup merge in LDS first, so the final merge reads fewer records
+  d.nwg_cap = (d.tiles_cap + d.wpw - 1) / d.wpw;  // at one tile per wave: the most workgroups
   return d;
+}
+
+// Tiles per wave for a launch: two on long lists (the second tile's loads overlap the first one's
+// compute, and the merge reads half the records), one on short lists, where more workgroups in
+// flight matter more.
+static inline int decode_tiles_per_wave(const DecodeShape &d) { return d.tiles_cap >= 32 ? 2 : 1; }
+
+// Records the split-K merge can stage in its workgroup's V-tile region: m, l and a weight per
+// (record, head), rounded up to 16 bytes, then (narrow units) RG groups of partial f32x4 sums.
+static inline int decode_merge_capacity(int nh, int D, int wpw) {
+  const int nt = wpw * 64, q4 = nh * (D / 4);
+  const int rg = q4 >= nt ? 1 : nt / q4;
+  const int tile_bytes = wpw * 64 * (D + VPAD) * 2;
+  const int red_bytes = rg > 1 ? rg * q4 * 16 : 0;
+  return (tile_bytes - red_bytes - 16) / (12 * nh);
 }
 
 }  // namespace sas
