@@ -131,6 +131,15 @@ def test_decode_beyond_fused_selection_limit():
     run_case(w, [0])
 
 
+def test_decode_three_tiles_per_wave():
+    """74-entry lists over 64 units: at two tiles per wave the grid would need two rounds of
+    resident workgroups on a 256-CU device, so each wave takes three tiles; ragged lengths leave
+    some units short of the capacity (workgroups past their list exit), with sink and gate."""
+    w = Workload(2, overrides=dict(tag="tpw3", seq_lens=[16000, 9000, 12000, 16384, 4000, 15000, 7000, 16300],
+                                   batch=8, k_fixed=72, sink=True, gate=True, seq_len=None))
+    run_case(w, list(range(8)))
+
+
 def test_prefill_group_few_rows():
     """20 query rows x 2 heads per unit: 64-row workgroups on per-group lists."""
     w = Workload(3, overrides=dict(tag="few", seq_len=700, tq=20, block=64, hq=4, hkv=2, frac_num=1, frac_den=4,

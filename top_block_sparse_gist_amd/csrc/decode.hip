@@ -20,6 +20,9 @@
 // workgroup of a unit to arrive (one device-scope atomic on an arrival counter, which it
 // resets) merges all records of the unit and writes O.  All G heads of a KV group share
 // each K/V load (per-group selection).
+#include <atomic>
+#include <cstdint>
+
 #include "common.h"
 #include "decode_parts.h"
 
@@ -45,7 +48,9 @@ bool decode_merge_fits(const sas_problem &p, const SeqTable &st, int32_t sel_mod
   int maxc = 0;
   for (int b = 0; b < p.batch; ++b) maxc = max(maxc, (st.len[b] - 1) / p.block);
   const DecodeShape d = decode_shape(p, sel_mode, kcap, gist, maxc);
-  const int tpw = decode_tiles_per_wave(d);
+  // validation makes no HIP call: the count is taken without the device's resident capacity, the
+  // largest record count any launch of this shape uses
+  const int tpw = decode_tiles_per_wave(d, INT64_MAX);
   *nwg_out = (d.tiles_cap + d.wpw * tpw - 1) / (d.wpw * tpw);
   *cap_out = decode_merge_capacity(d.nh, p.head_dim, d.wpw);
   return *nwg_out <= *cap_out;
@@ -57,6 +62,23 @@ size_t decode_workspace_bytes(const sas_problem &p, int32_t sel_mode, int32_t kc
   // arrival counters (one per unit, 256-byte aligned region) + one record per workgroup
   const size_t counters = ((size_t)d.units * 4 + 255) / 256 * 256;
   return counters + (size_t)d.units * d.nwg_cap * record_floats(d.nh, p.head_dim) * sizeof(float);
+}
+
+// Attention workgroups resident at once on the current device: as many per CU as the 160 KB LDS
+// holds (the 4 V tiles of a workgroup: two at head dim 128, three at 64).
+static int64_t decode_resident_workgroups(int head_dim) {
+  static std::atomic<int> cus[64];
+  const int per_cu = 160 * 1024 / (head_dim == 128 ? DecodeLds<128, 4>::BYTES : DecodeLds<64, 4>::BYTES);
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+    n = cus[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+      if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+      if (n > 0) cus[dev].store(n, std::memory_order_relaxed);
+    }
+  }
+  if (n <= 0) n = 256;
+  return (int64_t)per_cu * n;
 }
 
 template <int D, int WPW, int TPW>
@@ -87,7 +109,7 @@ hipError_t launch_decode_bf16(const sas_problem &p, const SeqTable &st, const vo
   const DecodeShape cap = decode_shape(p, sel_mode, kcap, gist, (p.max_len - 1) / p.block);
   DecodeShape d = decode_shape(p, sel_mode, kcap, gist, maxc);
   d.wpw = cap.wpw;
-  const int tpw = decode_tiles_per_wave(d);
+  const int tpw = decode_tiles_per_wave(d, decode_resident_workgroups(p.head_dim));
   const int nwg = (d.tiles_cap + d.wpw * tpw - 1) / (d.wpw * tpw);
   uint32_t *counters = reinterpret_cast<uint32_t *>(workspace);
   const size_t cbytes = ((size_t)d.units * 4 + 255) / 256 * 256;
@@ -99,9 +121,11 @@ hipError_t launch_decode_bf16(const sas_problem &p, const SeqTable &st, const vo
   return decode_launch<D_, 4, T_>(p, st, d, nwg, Q, qs, K, V, kvs, gk, gv, gb, gh, gt, gist, per_head, idx, nsel, \
                                   gate, kcap, sl2, work, counters, O, os, s)
   if (p.head_dim == 128) {
+    if (tpw == 3) SAS_DEC(128, 3);
     if (tpw == 2) SAS_DEC(128, 2);
     SAS_DEC(128, 1);
   }
+  if (tpw == 3) SAS_DEC(64, 3);
   if (tpw == 2) SAS_DEC(64, 2);
   SAS_DEC(64, 1);
 #undef SAS_DEC

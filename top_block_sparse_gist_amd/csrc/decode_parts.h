@@ -228,6 +228,11 @@ struct SelectLds {
   static constexpr int BYTES = LAST + 16;
 };
 
+// Selection tiles of one (sequence, KV head): 64-block tiles covering blocks 0..c (the current
+// block's score feeds the gate), or in gist mode the gists 0..c-1 only (at least one tile, which
+// runs the top-k).
+__host__ __device__ inline int select_tiles(int c, int gist) { return gist ? max(1, (c + 63) / 64) : c / 64 + 1; }
+
 // One selection workgroup: the 64-block tile bx of (sequence b, KV head g), hkv KV heads.  The last
 // tile of (b, g) to arrive runs the top-k of its units.
 template <typename T, typename R, int D, int NPL>
@@ -248,8 +253,8 @@ __device__ __forceinline__ void select_tile_body(
   const int j0 = bx * 64;
   const int L = st.len[b];
   const int c = (L - 1) / blk;
-  if (j0 > c) return;
-  const int ntile = c / 64 + 1;  // tiles covering blocks 0..c
+  const int ntile = select_tiles(c, gist);
+  if (bx >= ntile) return;
   const int nrep = gist ? min(L / blk, c) : cdiv(L, blk);
   const int nU = per_head ? G : 1;
   const int tid = threadIdx.x;
@@ -331,6 +336,11 @@ __device__ __forceinline__ void select_tile_body(
         if (j + x <= c) store4_dev(rrow, (uint32_t)(j + x) * 4u, scs[u][4 * q + x]);
     }
   }
+  if (gist && j0 + 64 == c && tid < nU) {
+    // gist mode: no tile starts at the current chunk, which has no gist; the last tile writes its -inf
+    const int s = per_head ? g * G + tid : g;
+    store4_dev(dev_rsrc(scores + ((int64_t)b * S + s) * ld, (uint32_t)ld * 4u), (uint32_t)c * 4u, -INFINITY);
+  }
   // ---- arrival: the last tile of this (sequence, KV head) selects for its units
   wait_stores();
   __syncthreads();
@@ -367,9 +377,9 @@ struct DecodeLds {
   static constexpr int BYTES = TILE_BYTES + SMALL_FLOATS * 4;
 };
 
-// One attention workgroup: tiles bx*WPW*TPW .. +WPW*TPW-1 of unit u (TPW = 1 or 2 per wave: wave w
-// takes tiles w and w + WPW of the workgroup's range, the second one's K/V loads issued as soon as
-// the first one's registers are consumed, so they overlap its softmax and PV), merged into the
+// One attention workgroup: tiles bx*WPW*TPW .. +WPW*TPW-1 of unit u (TPW = 1 to 3 per wave: wave w
+// takes tiles w, w + WPW, ... of the workgroup's range, each next tile's K/V loads issued as soon
+// as the previous one's registers are consumed, so they overlap its softmax and PV), merged into the
 // unit's record bx (records nwg apart per unit).  A unit has nsel[u] list entries (the padding
 // past them is -1), so it needs only the first nwg_u of the nwg workgroups: the others exit
 // before touching the records, and the last of the nwg_u to arrive merges their records and
@@ -769,8 +779,14 @@ static inline DecodeShape decode_shape(const sas_problem &p, int32_t sel_mode, i
 
 // Tiles per wave for a launch: two on long lists (the second tile's loads overlap the first one's
 // compute, and the merge reads half the records), one on short lists, where more workgroups in
-// flight matter more.
-static inline int decode_tiles_per_wave(const DecodeShape &d) { return d.tiles_cap >= 32 ? 2 : 1; }
+// flight matter more; three when that brings a grid that would need two rounds of `slots`
+// resident workgroups down to one.
+static inline int decode_tiles_per_wave(const DecodeShape &d, int64_t slots) {
+  if (d.tiles_cap < 32) return 1;
+  const int64_t wg2 = d.units * ((d.tiles_cap + 2 * d.wpw - 1) / (2 * d.wpw));
+  const int64_t wg3 = d.units * ((d.tiles_cap + 3 * d.wpw - 1) / (3 * d.wpw));
+  return (wg2 > slots && wg3 <= slots) ? 3 : 2;
+}
 
 // Records the split-K merge can stage in its workgroup's V-tile region: m, l and a weight per
 // (record, head), rounded up to 16 bytes, then (narrow units) RG groups of partial f32x4 sums.

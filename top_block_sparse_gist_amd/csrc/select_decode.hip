@@ -66,7 +66,7 @@ static hipError_t sel_dispatch(const sas_problem &p, const SeqTable &st, const v
   sg.nseq = p.batch;
   sg.first[0] = 0;
   for (int i = 0; i < p.batch; ++i) {
-    const int ntile = (st.len[sg.b[i]] - 1) / p.block / 64 + 1;
+    const int ntile = select_tiles((st.len[sg.b[i]] - 1) / p.block, gist);
     sg.first[i + 1] = sg.first[i] + ntile * p.hkv;
   }
   const dim3 grid((unsigned)sg.first[p.batch]);
