@@ -131,6 +131,15 @@ def test_decode_beyond_fused_selection_limit():
     run_case(w, [0])
 
 
+def test_decode_group_long_lists_sink_gate():
+    """Per-group selection over 468-1562 candidates: the last selection workgroup's 4 waves share
+    each unit's candidates (counts, tie ranks, gate sums and output offsets combined across
+    waves), with sink and gate."""
+    w = Workload(2, overrides=dict(tag="glong", seq_lens=[30000, 45000, 70000, 100000], batch=4, k_fixed=40,
+                                   sink=True, gate=True, hq=8, hkv=2, seq_len=None))
+    run_case(w, list(range(4)))
+
+
 def test_decode_three_tiles_per_wave():
     """74-entry lists over 64 units: at two tiles per wave the grid would need two rounds of
     resident workgroups on a 256-CU device, so each wave takes three tiles; ragged lengths leave

@@ -38,16 +38,70 @@ __device__ __forceinline__ uint32_t count_ge(const uint32_t (&key)[NPL], uint32_
   return wave_reduce_u32((a[0] + a[1]) + (a[2] + a[3]), [](uint32_t x, uint32_t y) { return x + y; });
 }
 
-// Top-k of one unit's scores row[0..c] by one wave (block lane + 64r in register r; the scores
-// are read back from memory, where the unit's tiles left them).  Ties go to the lower block.
-template <int NPL>
-__device__ void wave_topk(const float *__restrict__ row, int c, bool sinkf, const Budget &bg, int kcap,
-                          int32_t *__restrict__ out, int32_t *__restrict__ nsel_out, float *__restrict__ gout) {
+// A team of waves that selects for one unit; each wave holds its own contiguous share of the
+// candidates, and the team's values are the combination of wave-uniform partials.
+// SoloTeam: one wave holds all of them.
+struct SoloTeam {
+  static constexpr int SIZE = 1;
+  __device__ int rank() const { return 0; }
+  __device__ uint32_t sum(uint32_t v) const { return v; }
+  __device__ uint32_t min(uint32_t v) const { return v; }
+  __device__ uint32_t max(uint32_t v) const { return v; }
+  __device__ float fmax(float v) const { return v; }
+  __device__ float fsum(float v) const { return v; }
+  __device__ uint32_t before(uint32_t) const { return 0u; }  // sum over the earlier waves
+};
+// GroupTeam: the 4 waves of a workgroup; each combination passes the 4 partials through LDS
+// (lane 0 of each wave writes one slot, one barrier, every wave reads all four).  The slot sets
+// alternate, so a wave that is a combination ahead never overwrites slots a slower wave has yet
+// to read.  Every wave of the workgroup must make the same sequence of combinations.
+struct GroupTeam {
+  static constexpr int SIZE = 4;
+  uint32_t *slots;       // LDS [2][4]
+  int w;                 // wave-uniform rank
+  mutable int phase;     // slot set of the next combination
+  __device__ int rank() const { return w; }
+  template <typename F>
+  __device__ uint32_t combine(uint32_t v, F f, bool prefix = false) const {
+    uint32_t *sl = slots + 4 * phase;
+    phase ^= 1;
+    if ((threadIdx.x & 63) == 0) sl[w] = v;
+    __syncthreads();
+    const uint32_t a = sl[0], b = sl[1], c = sl[2], d = sl[3];
+    if (prefix) return (w > 0 ? a : 0u) + (w > 1 ? b : 0u) + (w > 2 ? c : 0u);
+    return f(f(a, b), f(c, d));
+  }
+  __device__ uint32_t sum(uint32_t v) const { return combine(v, [](uint32_t x, uint32_t y) { return x + y; }); }
+  __device__ uint32_t min(uint32_t v) const {
+    return combine(v, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
+  }
+  __device__ uint32_t max(uint32_t v) const {
+    return combine(v, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
+  }
+  __device__ float fmax(float v) const {
+    return __uint_as_float(
+        combine(__float_as_uint(v), [](uint32_t x, uint32_t y) { return __float_as_uint(fmaxf(__uint_as_float(x), __uint_as_float(y))); }));
+  }
+  __device__ float fsum(float v) const {
+    return __uint_as_float(
+        combine(__float_as_uint(v), [](uint32_t x, uint32_t y) { return __float_as_uint(__uint_as_float(x) + __uint_as_float(y)); }));
+  }
+  __device__ uint32_t before(uint32_t v) const { return combine(v, [](uint32_t x, uint32_t) { return x; }, true); }
+};
+
+// Top-k of one unit's scores row[0..c] by a team of waves: wave w of the team holds blocks
+// 64 * NPL * w + lane + 64r in its register r (the scores are read back from memory, where the
+// unit's tiles left them).  Ties go to the lower block.
+template <int NPL, typename Team>
+__device__ void team_topk(const float *__restrict__ row, int c, bool sinkf, const Budget &bg, int kcap,
+                          int32_t *__restrict__ out, int32_t *__restrict__ nsel_out, float *__restrict__ gout,
+                          const Team &team) {
   static_assert(NPL <= 32, "one selection bit per register in a 32-bit mask");
   // opaque per call: keeps the compiler from hoisting the per-register block numbers and masks out
   // of a caller's loop over units, where they would hold ~100 registers across the whole kernel
   int lane = threadIdx.x & 63;
   asm volatile("" : "+v"(lane));
+  const int jw = 64 * NPL * team.rank();  // this wave's first block
   const bool sink = sinkf && c > 0;
   const int lo = sink ? 1 : 0;
   const int ncand = c - lo;
@@ -59,12 +113,13 @@ __device__ void wave_topk(const float *__restrict__ row, int c, bool sinkf, cons
 #pragma unroll
   for (int r = 0; r < NPL; ++r) {
     // every lane loads (entries up to c exist), so the loads issue back to back
-    const int j = lane + 64 * r;
+    const int j = jw + lane + 64 * r;
     const float s = load_dev(row + min(j, c));
     key[r] = (j >= lo && j < c) ? max(float_order_key(s), 1u) : 0u;
   }
   const float s_c = load_dev(row + c);
   const float s_0 = load_dev(row);
+  auto count = [&](uint32_t t) { return team.sum(count_ge(key, t)); };
   // The kept candidates: all keys > T, then the `want` lowest blocks with key == T (ties: only
   // when T is the exact k-th largest key and more keys share it).
   uint32_t T = 0u, want = 0u;
@@ -78,15 +133,15 @@ __device__ void wave_topk(const float *__restrict__ row, int c, bool sinkf, cons
       kmin = min(kmin, key[r] - 1u);
       kmax = max(kmax, key[r]);
     }
-    kmin = wave_reduce_u32(kmin, [](uint32_t x, uint32_t y) { return min(x, y); }) + 1u;
-    kmax = wave_reduce_u32(kmax, [](uint32_t x, uint32_t y) { return max(x, y); });
-    const uint32_t c_hi = count_ge(key, kmax);
+    kmin = team.min(wave_reduce_u32(kmin, [](uint32_t x, uint32_t y) { return min(x, y); })) + 1u;
+    kmax = team.max(wave_reduce_u32(kmax, [](uint32_t x, uint32_t y) { return max(x, y); }));
+    const uint32_t c_hi = count(kmax);
     if (c_hi >= (uint32_t)k) {
       T = kmax;  // the largest key alone fills the budget: its first k holders in block order
       want = (uint32_t)k;
       ties = c_hi > (uint32_t)k;
-    } else if constexpr (NPL <= 8) {
-      // Few registers per lane: MSB-first bit steps below the keys' common prefix (the bits
+    } else if constexpr (NPL * Team::SIZE <= 8) {
+      // Few candidates per lane: MSB-first bit steps below the keys' common prefix (the bits
       // above the highest bit in which the smallest and largest key differ), each one count;
       // an exact count of k ends the search.  (kmin != kmax here: equal keys would all count.)
       const int top = 31 - __builtin_clz(kmin ^ kmax);
@@ -94,7 +149,7 @@ __device__ void wave_topk(const float *__restrict__ row, int c, bool sinkf, cons
       bool exact = false;
       for (int bit = top; bit >= 0; --bit) {
         const uint32_t cand_t = prefix | (1u << bit);
-        const uint32_t ge = count_ge(key, cand_t);
+        const uint32_t ge = count(cand_t);
         if (ge >= (uint32_t)k) {
           prefix = cand_t;
           if (ge == (uint32_t)k) {
@@ -104,15 +159,16 @@ __device__ void wave_topk(const float *__restrict__ row, int c, bool sinkf, cons
         }
       }
       T = prefix;
-      want = exact ? (uint32_t)k : (uint32_t)k - count_ge(key, T + 1u);
+      want = exact ? (uint32_t)k : (uint32_t)k - count(T + 1u);
       ties = !exact;
     } else {
       // Safeguarded interpolation search for the largest key value T with at least k keys at or
-      // above it (fewer probes than bit steps on 32 registers per lane).  Invariant: count_ge(lo) = cl >= k > ch = count_ge(hi).  Each probe goes where
-      // a straight line between (lo, cl) and (hi, ch) reaches k -- or to the midpoint after a
-      // probe that did not halve the range -- and replaces lo or hi.  A probe with exactly k keys
-      // at or above it ends the search: those keys are the selection.  Otherwise the range
-      // closes to hi = lo + 1 and lo is the k-th largest key, with k - ch of its holders taken.
+      // above it (fewer probes than bit steps on many candidates per lane).  Invariant:
+      // count(lo) = cl >= k > ch = count(hi).  Each probe goes where a straight line between
+      // (lo, cl) and (hi, ch) reaches k -- or to the midpoint after a probe that did not halve
+      // the range -- and replaces lo or hi.  A probe with exactly k keys at or above it ends the
+      // search: those keys are the selection.  Otherwise the range closes to hi = lo + 1 and lo
+      // is the k-th largest key, with k - ch of its holders taken.
       uint32_t lo = kmin, hi = kmax, cl = (uint32_t)ncand, ch = c_hi;
       bool exact = false, bisect = false;
       while (hi - lo > 1u) {
@@ -127,7 +183,7 @@ __device__ void wave_topk(const float *__restrict__ row, int c, bool sinkf, cons
           step = max(min(step, span - 1u), 1u);
         }
         const uint32_t t = lo + step;
-        const uint32_t c_t = count_ge(key, t);
+        const uint32_t c_t = count(t);
         if (c_t >= (uint32_t)k) {
           lo = t;
           cl = c_t;
@@ -146,7 +202,7 @@ __device__ void wave_topk(const float *__restrict__ row, int c, bool sinkf, cons
       ties = !exact;
     }
   }
-  // which candidates are kept (bit r of `selbits`: block lane + 64r)
+  // which candidates are kept (bit r of `selbits`: block jw + lane + 64r)
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   uint32_t selbits = 0u;
   if (all) {
@@ -156,7 +212,11 @@ __device__ void wave_topk(const float *__restrict__ row, int c, bool sinkf, cons
 #pragma unroll
     for (int r = 0; r < NPL; ++r) selbits |= (key[r] >= T ? 1u : 0u) << r;  // T >= 1: candidates only
   } else if (k > 0) {
-    uint32_t eq_seen = 0;
+    // holders of T rank in block order, after those of the team's earlier waves
+    uint32_t eq_w = 0;
+#pragma unroll
+    for (int r = 0; r < NPL; ++r) eq_w += (uint32_t)__popcll(__ballot(key[r] == T));
+    uint32_t eq_seen = team.before(eq_w);
 #pragma unroll
     for (int r = 0; r < NPL; ++r) {
       const bool eq = key[r] == T;  // T >= 1 here, so both tests pass over the non-candidates
@@ -174,7 +234,7 @@ __device__ void wave_topk(const float *__restrict__ row, int c, bool sinkf, cons
     for (int r = 0; r < NPL; ++r) mx = fmaxf(mx, ((selbits >> r) & 1u) ? order_key_float(key[r]) : -INFINITY);
     mx = fmaxf(mx, s_c);
     if (sink) mx = fmaxf(mx, s_0);
-    mx = wave_max(mx);
+    mx = team.fmax(wave_max(mx));
     // exp(x - mx) as 2^((x - mx) log2 e): one v_exp_f32 each; terms that flush to 0 are below the
     // largest (1) by more than the float's precision
     constexpr float L2E = 1.4426950408889634f;
@@ -184,13 +244,16 @@ __device__ void wave_topk(const float *__restrict__ row, int c, bool sinkf, cons
       const float e = __builtin_amdgcn_exp2f((order_key_float(key[r]) - mx) * L2E);
       sm += ((selbits >> r) & 1u) ? e : 0.f;
     }
-    sm = wave_sum(sm);
+    sm = team.fsum(wave_sum(sm));
     sm += __builtin_amdgcn_exp2f((s_c - mx) * L2E);
     if (sink) sm += __builtin_amdgcn_exp2f((s_0 - mx) * L2E);
     lse = mx + logf(sm);
   }
-  // compaction in ascending block order
-  uint32_t pos_run = 0;
+  // compaction in ascending block order, after the team's earlier waves' selections
+  uint32_t sel_w = 0;
+#pragma unroll
+  for (int r = 0; r < NPL; ++r) sel_w += (uint32_t)__popcll(__ballot((selbits >> r) & 1u));
+  uint32_t pos_run = team.before(sel_w);
 #pragma unroll
   for (int r = 0; r < NPL; ++r) {
     const bool sel = (selbits >> r) & 1u;
@@ -198,12 +261,12 @@ __device__ void wave_topk(const float *__restrict__ row, int c, bool sinkf, cons
     const uint32_t pos = pos_run + (uint32_t)__popcll(sb & below);
     pos_run += (uint32_t)__popcll(sb);
     if (sel) {
-      out[base + pos] = lane + 64 * r;
+      out[base + pos] = jw + lane + 64 * r;
       if (gout) gout[base + pos] = order_key_float(key[r]) - lse;
     }
   }
   const int n = base + k + 1;
-  if (lane == 0) {
+  if (team.rank() == 0 && lane == 0) {
     if (sink) {
       out[0] = 0;
       if (gout) gout[0] = s_0 - lse;
@@ -212,7 +275,7 @@ __device__ void wave_topk(const float *__restrict__ row, int c, bool sinkf, cons
     if (gout) gout[base + k] = s_c - lse;
     *nsel_out = n;
   }
-  for (int p = n + lane; p < kcap; p += 64) {
+  for (int p = n + 64 * team.rank() + lane; p < kcap; p += 64 * Team::SIZE) {
     out[p] = -1;
     if (gout) gout[p] = 0.f;
   }
@@ -352,11 +415,20 @@ __device__ __forceinline__ void select_tile_body(
   __syncthreads();
   if (!last_sh) return;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  for (int u = wave; u < nU; u += 4) {
-    const int s = per_head ? g * G + u : g;
-    const int64_t urow = (int64_t)b * S + s;
-    wave_topk<NPL>(scores + urow * ld, c, bg.sink != 0, bg, kcap, idx + urow * kcap, nsel + urow,
-                   bg.gate ? gate + urow * kcap : nullptr);
+  if (NPL == 32 && nU == 1) {
+    // one unit with up to 2048 candidates: the 4 waves share them (8 registers per lane each),
+    // combining their counts through LDS (the pooled queries' region, no longer read)
+    const int64_t urow = (int64_t)b * S + (per_head ? g * G : g);
+    const GroupTeam team{reinterpret_cast<uint32_t *>(lds + Lds::QS), wave, 0};
+    team_topk<NPL / 4>(scores + urow * ld, c, bg.sink != 0, bg, kcap, idx + urow * kcap, nsel + urow,
+                       bg.gate ? gate + urow * kcap : nullptr, team);
+  } else {
+    for (int u = wave; u < nU; u += 4) {
+      const int s = per_head ? g * G + u : g;
+      const int64_t urow = (int64_t)b * S + s;
+      team_topk<NPL>(scores + urow * ld, c, bg.sink != 0, bg, kcap, idx + urow * kcap, nsel + urow,
+                     bg.gate ? gate + urow * kcap : nullptr, SoloTeam{});
+    }
   }
   if (tid == 0) __hip_atomic_store(&counters[b * hkv + g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
