@@ -384,6 +384,12 @@ def main():
         rb = K.numel() * 2 + reps.numel() * 4
         extra["reps_32k"] = {"us": round(t * 1e3, 2), "GB/s": round(rb / (t * 1e-3) / 1e9, 1), "bytes": rb}
         log(f"[bench] reps 32K: {t * 1e3:.1f} us -> {rb / (t * 1e-3) / 1e9:.0f} GB/s")
+        # a decode loop pools again only the block its new token lands in (one per sequence and KV head)
+        first = [(L - 1) // w2.block for L in inp2.seq_lens]
+        tu, _ = timer.time(lambda: sas.block_reps(K, inp2.seq_lens, w2.block, reps=reps, first_block=first), K_, W_)
+        extra["reps_update_32k"] = {"us": round(tu * 1e3, 2), "blocks": len(inp2.seq_lens) * w2.hkv,
+                                    "what": "the current block of every (sequence, KV head) pooled again"}
+        log(f"[bench] reps update (current block only): {tu * 1e3:.1f} us")
     if not args.no_cpu_baseline and result is not None:
         log("[bench] cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline_decode(w2, inp2.host, by["total"], args.cpu_seconds)

@@ -10,6 +10,7 @@
  *
  * The path ([GSA] section 4 pseudo-code steps 1-3, [SAS] method, [SSA] method):
  *   sas_block_reps    one representative key per block (mean of its keys)
+ *   sas_block_reps_update  the same for the blocks from a given one on (a decode loop)
  *   sas_block_scores  score every earlier block against each selection unit's queries
  *   sas_topk_select   top-k blocks + the current block (+ block 0), optional log-gate
  *   sas_sparse_prefill / sas_sparse_decode  attention over the selected blocks only
@@ -102,6 +103,18 @@ int32_t sas_required_kcap(const sas_problem *p, int32_t tq, const int32_t *q_sta
  *   reps: [B, Hkv, >= NB_b, d] fp32, rep_stride = {batch, head, block}. */
 sas_status sas_block_reps(const sas_problem *p, const void *K, const int64_t k_stride[3],
                           float *reps, const int64_t rep_stride[3], void *stream);
+
+/* A1, incremental (a decode loop that appends tokens: only the blocks that changed are pooled
+ * again).  Same arguments and layout as sas_block_reps, plus
+ *   first_block: HOST [B]; blocks first_block[b] .. NB_b - 1 of sequence b are recomputed
+ *                (0 <= first_block[b] <= NB_b; NB_b means none).  After appending tokens to a
+ *                sequence whose length was L_old, first_block[b] = floor(L_old / blk) makes reps
+ *                equal, bit for bit, to a full sas_block_reps at the new length (each block is
+ *                pooled by the same code in the same order).
+ *   Errors: first_block NULL -> SAS_ERR_NULL; an entry outside [0, NB_b] -> SAS_ERR_SHAPE. */
+sas_status sas_block_reps_update(const sas_problem *p, const void *K, const int64_t k_stride[3],
+                                 float *reps, const int64_t rep_stride[3], const int32_t *first_block,
+                                 void *stream);
 
 /* A2 - block scores ([GSA] section 4 step 1; [SSA] method item 1, query against every
  * historical gist).  For unit u with current block c and query vectors q (its rows times

@@ -69,6 +69,28 @@ def test_reps_validation_codes():
     assert _reps(lib, p, K=C.c_void_p(0x10002)) == _lib.SAS_ERR_SHAPE
 
 
+def test_reps_update_validation_codes():
+    """The incremental form validates like the full one, plus its per-sequence first block."""
+    lib = _lib.load()
+    p, a = _problem()  # lengths 1000 and 700: 16 and 11 blocks
+    ks = _lib.i64x([8 * 1000 * 128, 1000 * 128, 128])
+    rs = _lib.i64x([2 * 16 * 128, 16 * 128, 128])
+
+    def upd(first, K=FAKE):
+        fb = None if first is None else _lib.i32x(first)
+        return lib.sas_block_reps_update(C.byref(p), K, ks, FAKE, rs, fb, None)
+
+    assert upd(None) == _lib.SAS_ERR_NULL
+    assert upd([15, 10], K=None) == _lib.SAS_ERR_NULL
+    assert upd([-1, 0]) == _lib.SAS_ERR_SHAPE
+    assert upd([16, 12]) == _lib.SAS_ERR_SHAPE
+    assert b"first_block[1] = 12" in lib.sas_last_error()
+    assert upd([15, 10], K=C.c_void_p(0x10002)) == _lib.SAS_ERR_SHAPE
+    p2, a2 = _problem(d=96)
+    assert lib.sas_block_reps_update(C.byref(p2), FAKE, ks, FAKE, rs, _lib.i32x([0, 0]), None) == \
+        _lib.SAS_ERR_UNSUPPORTED
+
+
 def test_num_qblocks_and_required_kcap():
     lib = _lib.load()
     assert lib.sas_num_qblocks(1, 64) == 1

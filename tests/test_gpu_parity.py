@@ -292,3 +292,60 @@ def test_exact_ties_go_to_the_lower_block(lens):
             ties += int(s[k - 1] == s[k])
     say(f"[ties] {ties} of {B * hkv} units have the k-th and (k+1)-th scores exactly equal")
     assert ties == B * hkv
+
+
+# ------------------------------------------------------------------------------ decode loop
+def test_decode_loop_incremental_reps():
+    """A decode loop that appends one token per sequence per step: sas_block_reps_update pools
+    only the block the token lands in, and the reps then equal a full sas_block_reps bit for bit;
+    each step's selection and output match the oracle at the new length (lengths cross block
+    boundaries: a block fills up, a new one opens with a single token)."""
+    from oracle import sas_oracle as orc
+    from workloads.gen import round_bf16
+    from gpu_harness import list_matches, BF16_MAX_ABS, BF16_MEAN_ABS
+    lens = [1000, 2047, 4096, 63]
+    steps, B, hq, hkv, d, blk, k = 3, 4, 8, 2, 128, 64, 4
+    Lmax = max(lens) + steps
+    rng = np.random.default_rng(29)
+    K = round_bf16(rng.standard_normal((B, hkv, Lmax, d), dtype=np.float32))
+    V = round_bf16(rng.standard_normal((B, hkv, Lmax, d), dtype=np.float32))
+    Q = round_bf16(rng.standard_normal((B, hq, d), dtype=np.float32))
+    Kd = torch.from_numpy(K).to(torch.bfloat16).cuda()
+    Vd = torch.from_numpy(V).to(torch.bfloat16).cuda()
+    Qd = torch.from_numpy(Q).to(torch.bfloat16).cuda()
+    bud = sas.Budget(k_fixed=k, sink=True, gate=True)
+    nbmax = -(-Lmax // blk)
+    reps = torch.zeros((B, hkv, nbmax, d), dtype=torch.float32, device="cuda")
+    sas.block_reps(Kd, lens, blk, reps=reps)
+    for step in range(steps):
+        old, lens = lens, [L + 1 for L in lens]
+        sas.block_reps(Kd, lens, blk, reps=reps, first_block=[L // blk for L in old])
+        full = sas.block_reps(Kd, lens, blk, reps=torch.full_like(reps, float("nan")))
+        scores, idx, nsel, gate = sas.select_decode(Qd, reps, lens, blk, hkv, Lmax, bud)
+        O = sas.sparse_decode(Qd, Kd, Vd, lens, blk, idx, nsel, gate)
+        torch.cuda.synchronize()
+        for b, L in enumerate(lens):
+            nb = -(-L // blk)
+            assert torch.equal(reps[b, :, :nb], full[b, :, :nb]), f"step {step}: reps of sequence {b} differ"
+        idx_h, nsel_h, O_h = idx.cpu().numpy(), nsel.cpu().numpy(), O.float().cpu().numpy()
+        err_sum, err_n = 0.0, 0
+        for b, L in enumerate(lens):
+            r = orc.run_sequence(Q[b][:, None, :], K[b], V[b], L, L - 1, blk, "group", k_fixed=k, sink=True,
+                                 gate=True)
+            explicit = {}
+            for un in r.units:
+                u = b * hkv + un.sel_head
+                got = [int(x) for x in idx_h[u, :nsel_h[u]]]
+                ok, band, why = list_matches(un.sel, got, un.scores, un.c, un.k, True)
+                assert ok, f"step {step}, sequence {b}, KV head {un.sel_head}: {why}"
+                if band:
+                    explicit[(un.sel_head, un.c)] = (got, orc.gate_values(un.scores, got))
+            if explicit:
+                r = orc.run_sequence(Q[b][:, None, :], K[b], V[b], L, L - 1, blk, "group", k_fixed=k, sink=True,
+                                     gate=True, explicit=explicit)
+            diff = np.abs(O_h[b] - r.O[:, 0, :])
+            assert diff.max() <= BF16_MAX_ABS, f"step {step}, sequence {b}: max-abs {diff.max():.3e}"
+            err_sum += float(diff.sum())
+            err_n += diff.size
+        assert err_sum / err_n <= BF16_MEAN_ABS
+        say(f"[loop] step {step}: lengths {lens}, reps equal a full pass, lists and outputs match")

@@ -108,16 +108,29 @@ def required_kcap(batch, hq, hkv, d, block, dtype, max_len, seq_lens, tq, q_star
     return int(r)
 
 
-def block_reps(K, seq_lens: Sequence[int], block: int, hq: Optional[int] = None, reps=None, stream=None):
-    """A1: fp32 mean of every block's keys; K [B, Hkv, Lmax, d] -> reps [B, Hkv, NBmax, d]."""
+def block_reps(K, seq_lens: Sequence[int], block: int, hq: Optional[int] = None, reps=None, stream=None,
+               first_block: Optional[Sequence[int]] = None):
+    """A1: fp32 mean of every block's keys; K [B, Hkv, Lmax, d] -> reps [B, Hkv, NBmax, d].
+
+    first_block (one int per sequence): recompute only blocks first_block[b] .. NB_b - 1 of an
+    existing ``reps`` (sas_block_reps_update), e.g. floor(L_old / block) after appending tokens.
+    """
     torch = _torch()
     B, hkv, lmax, d = K.shape
     nb = max(-(-int(L) // block) for L in seq_lens)
     if reps is None:
+        if first_block is not None:
+            raise ValueError("an incremental update needs the existing reps")
         reps = torch.empty((B, hkv, nb, d), dtype=torch.float32, device=K.device)
     p = _Prob(B, hq or hkv, hkv, d, block, _dtype_code(K), lmax, seq_lens)
-    check(load().sas_block_reps(p.ref, _ptr(K), _strides(K, 3), _ptr(reps), _strides(reps, 3), _stream(stream)),
-          "sas_block_reps")
+    lib = load()
+    if first_block is None:
+        check(lib.sas_block_reps(p.ref, _ptr(K), _strides(K, 3), _ptr(reps), _strides(reps, 3), _stream(stream)),
+              "sas_block_reps")
+    else:
+        fb = i32x(first_block)
+        check(lib.sas_block_reps_update(p.ref, _ptr(K), _strides(K, 3), _ptr(reps), _strides(reps, 3), fb,
+                                        _stream(stream)), "sas_block_reps_update")
     return reps
 
 

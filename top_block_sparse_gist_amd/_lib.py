@@ -20,7 +20,8 @@ SAS_MAX_BATCH = 64
 STATUS_NAMES = {0: "SAS_OK", -1: "SAS_ERR_NULL", -2: "SAS_ERR_SHAPE", -3: "SAS_ERR_UNSUPPORTED",
                 -4: "SAS_ERR_WORKSPACE", -5: "SAS_ERR_HIP"}
 
-EXPORTED = ("sas_num_qblocks", "sas_required_kcap", "sas_block_reps", "sas_block_scores_workspace",
+EXPORTED = ("sas_num_qblocks", "sas_required_kcap", "sas_block_reps", "sas_block_reps_update",
+            "sas_block_scores_workspace",
             "sas_block_scores", "sas_topk_select", "sas_select_decode_workspace", "sas_select_decode",
             "sas_sparse_prefill", "sas_sparse_decode_workspace", "sas_sparse_decode", "sas_last_error")
 
@@ -46,6 +47,7 @@ _SIGS = {
     "sas_num_qblocks": (C.c_int32, [C.c_int32, C.c_int32]),
     "sas_required_kcap": (C.c_int32, [_P, C.c_int32, C.POINTER(C.c_int32), _B]),
     "sas_block_reps": (C.c_int, [_P, _VP, _I64_3, _VP, _I64_3, _VP]),
+    "sas_block_reps_update": (C.c_int, [_P, _VP, _I64_3, _VP, _I64_3, C.POINTER(C.c_int32), _VP]),
     "sas_block_scores_workspace": (C.c_size_t, [_P, C.c_int32, C.c_int32]),
     "sas_block_scores": (C.c_int, [_P, _VP, _I64_3, C.c_int32, C.POINTER(C.c_int32), _VP, C.c_int32, _I64_3,
                                    C.c_int32, C.c_float, _VP, C.c_int64, _VP, C.c_size_t, _VP]),

@@ -145,7 +145,27 @@ sas_status sas_block_reps(const sas_problem *p, const void *K, const int64_t k_s
   if (!aligned16(K) || !aligned16(reps) || !strides_ok(k_stride, 3, elem_bytes(p->dtype)) ||
       !strides_ok(rep_stride, 3, 4))
     return fail(SAS_ERR_SHAPE, "K / reps must be 16-byte aligned with 16-byte-multiple row strides");
-  return hip_status(launch_reps(*p, tab, K, k_stride, reps, rep_stride, (hipStream_t)stream), "sas_block_reps");
+  return hip_status(launch_reps(*p, tab, K, k_stride, reps, rep_stride, nullptr, (hipStream_t)stream),
+                    "sas_block_reps");
+}
+
+sas_status sas_block_reps_update(const sas_problem *p, const void *K, const int64_t k_stride[3], float *reps,
+                                 const int64_t rep_stride[3], const int32_t *first_block, void *stream) {
+  SeqTable tab{};
+  sas_status st;
+  if ((st = check_problem(p, &tab)) != SAS_OK) return st;
+  if (!K || !reps || !k_stride || !rep_stride || !first_block)
+    return fail(SAS_ERR_NULL, "K, reps, a stride array or first_block is NULL");
+  if (!aligned16(K) || !aligned16(reps) || !strides_ok(k_stride, 3, elem_bytes(p->dtype)) ||
+      !strides_ok(rep_stride, 3, 4))
+    return fail(SAS_ERR_SHAPE, "K / reps must be 16-byte aligned with 16-byte-multiple row strides");
+  for (int b = 0; b < p->batch; ++b) {
+    const int nb = cdiv(tab.len[b], p->block);
+    if (first_block[b] < 0 || first_block[b] > nb)
+      return fail(SAS_ERR_SHAPE, "first_block[%d] = %d is outside [0, %d]", b, first_block[b], nb);
+  }
+  return hip_status(launch_reps(*p, tab, K, k_stride, reps, rep_stride, first_block, (hipStream_t)stream),
+                    "sas_block_reps_update");
 }
 
 size_t sas_block_scores_workspace(const sas_problem *p, int32_t tq, int32_t sel_mode) {

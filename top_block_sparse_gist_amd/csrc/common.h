@@ -190,8 +190,9 @@ __device__ __forceinline__ uint32_t float_order_key(float f) {
 // ---------------------------------------------------------------------------------------
 namespace sas {
 
+// first: host [batch] first block to compute per sequence, or NULL for every block
 hipError_t launch_reps(const sas_problem &p, const SeqTable &st, const void *K, const int64_t *ks,
-                       float *reps, const int64_t *rs, hipStream_t s);
+                       float *reps, const int64_t *rs, const int32_t *first, hipStream_t s);
 
 hipError_t launch_pool_queries(const sas_problem &p, const SeqTable &st, const void *Q,
                                const int64_t *qs, int32_t tq, int32_t sel_mode, float *qbar,

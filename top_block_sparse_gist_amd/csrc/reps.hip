@@ -2,7 +2,9 @@
 // Page "稀疏注意力的Trade-offs" section 2.1 (block-pooled token representations) and page
 // "开源大模型注意力机制演进" section 4, pseudo-code step 1 (keys aggregated per block).
 //
-// HBM-streaming reduction: one workgroup per (block, KV head, sequence).  The workgroup's
+// HBM-streaming reduction: one workgroup per (block, KV head, sequence).  The incremental form
+// (decode: only the blocks from a given one on, normally the block the new tokens landed in)
+// runs the same workgroups on fewer blocks, so its results equal a full pass bit for bit.  The workgroup's
 // 256 lanes read the block's blk x d slab with 16-byte loads (a key row is covered by
 // d/VEC consecutive lanes, so every load instruction reads whole rows), all loads of the
 // block are issued before the first add, partial row sums are folded through LDS, and the
@@ -11,8 +13,13 @@
 
 namespace sas {
 
+// First block computed per sequence (grid x counts blocks from it).
+struct BlockStart {
+  int32_t j[SAS_MAX_BATCH];
+};
+
 template <typename T, int D, int BLK>
-__global__ __launch_bounds__(256) void reps_kernel(SeqTable st, const T *__restrict__ K, int64_t kb,
+__global__ __launch_bounds__(256) void reps_kernel(SeqTable st, BlockStart start, const T *__restrict__ K, int64_t kb,
                                                    int64_t kh, int64_t kt, float *__restrict__ reps,
                                                    int64_t rb, int64_t rh, int64_t rj) {
   constexpr int VEC = 16 / sizeof(T);      // elements per 16-byte load
@@ -22,7 +29,8 @@ __global__ __launch_bounds__(256) void reps_kernel(SeqTable st, const T *__restr
   static_assert(BLK % RPP == 0, "block must be a multiple of rows per pass");
   __shared__ float part[RPP][D + 1];
 
-  const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int j = start.j[b] + (int)blockIdx.x;
   const int L = st.len[b];
   const int t0 = j * BLK;
   if (t0 >= L) return;
@@ -67,27 +75,33 @@ __global__ __launch_bounds__(256) void reps_kernel(SeqTable st, const T *__restr
 
 template <typename T, int D>
 static hipError_t reps_dispatch_blk(const sas_problem &p, const SeqTable &st, const void *K,
-                                    const int64_t *ks, float *reps, const int64_t *rs, hipStream_t s) {
+                                    const int64_t *ks, float *reps, const int64_t *rs, const int32_t *first,
+                                    hipStream_t s) {
+  BlockStart start{};
   int nbmax = 0;
-  for (int b = 0; b < p.batch; ++b) nbmax = max(nbmax, cdiv(st.len[b], p.block));
+  for (int b = 0; b < p.batch; ++b) {
+    start.j[b] = first ? first[b] : 0;
+    nbmax = max(nbmax, cdiv(st.len[b], p.block) - start.j[b]);
+  }
+  if (nbmax <= 0) return hipSuccess;  // nothing to compute
   dim3 grid(nbmax, p.hkv, p.batch);
   if (p.block == 64)
-    hipLaunchKernelGGL((reps_kernel<T, D, 64>), grid, dim3(256), 0, s, st, (const T *)K, ks[0], ks[1],
+    hipLaunchKernelGGL((reps_kernel<T, D, 64>), grid, dim3(256), 0, s, st, start, (const T *)K, ks[0], ks[1],
                        ks[2], reps, rs[0], rs[1], rs[2]);
   else
-    hipLaunchKernelGGL((reps_kernel<T, D, 128>), grid, dim3(256), 0, s, st, (const T *)K, ks[0], ks[1],
+    hipLaunchKernelGGL((reps_kernel<T, D, 128>), grid, dim3(256), 0, s, st, start, (const T *)K, ks[0], ks[1],
                        ks[2], reps, rs[0], rs[1], rs[2]);
   return hipGetLastError();
 }
 
 hipError_t launch_reps(const sas_problem &p, const SeqTable &st, const void *K, const int64_t *ks,
-                       float *reps, const int64_t *rs, hipStream_t s) {
+                       float *reps, const int64_t *rs, const int32_t *first, hipStream_t s) {
   if (p.dtype == SAS_BF16) {
-    if (p.head_dim == 128) return reps_dispatch_blk<uint16_t, 128>(p, st, K, ks, reps, rs, s);
-    return reps_dispatch_blk<uint16_t, 64>(p, st, K, ks, reps, rs, s);
+    if (p.head_dim == 128) return reps_dispatch_blk<uint16_t, 128>(p, st, K, ks, reps, rs, first, s);
+    return reps_dispatch_blk<uint16_t, 64>(p, st, K, ks, reps, rs, first, s);
   }
-  if (p.head_dim == 128) return reps_dispatch_blk<float, 128>(p, st, K, ks, reps, rs, s);
-  return reps_dispatch_blk<float, 64>(p, st, K, ks, reps, rs, s);
+  if (p.head_dim == 128) return reps_dispatch_blk<float, 128>(p, st, K, ks, reps, rs, first, s);
+  return reps_dispatch_blk<float, 64>(p, st, K, ks, reps, rs, first, s);
 }
 
 }  // namespace sas
