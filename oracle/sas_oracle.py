@@ -352,3 +352,108 @@ def dense_causal_pairs(q_start: int, rows: int) -> int:
 def sparsity(computed_pairs: int, full_pairs: int) -> float:
     """1 - computed / full ([SF] 1.2)."""
     return 1.0 - computed_pairs / float(full_pairs)
+
+
+# ---------------------------------------------------------------------------------------------
+# 7. two-level gist selection (H-SSA), decode
+# ---------------------------------------------------------------------------------------------
+# [SSA] method, hierarchical extension: meta-gist tokens ("gists of gists") make a second level;
+# a coarse choice among them comes first, then the ordinary gists of the chosen part are scored
+# and the best chunks expanded.  The pages give no more detail; the readings taken here:
+#   H1  a group is M consecutive chunks; group i (chunks iM .. iM+M-1) has a meta-gist only when
+#       it is complete and lies wholly before the current chunk c: i < floor(c / M);
+#   H2  level 1 keeps the top-k1 complete groups by meta-gist score (ties to the lower index);
+#       the trailing group (chunks floor(c/M)*M .. c-1, no meta-gist yet) is always open, as the
+#       current block always is;
+#   H3  level 2 keeps the top-k2 chunks of the open groups by gist score (ties to the lower
+#       index); the current chunk is always attended raw;
+#   H4  the key set is the raw tokens of the expanded chunks and of the current chunk (up to the
+#       row), the gists of the open groups' chunks that were not expanded, and the meta-gists of
+#       the complete groups that were not opened; no gate (as in gist mode);
+#   H5  scores are those of step 3 (mean over the unit's heads of scale * q . x).
+
+@dataclass
+class HssaUnit:
+    sel_head: int
+    c: int
+    heads: Tuple[int, ...]
+    meta_scores: np.ndarray            # [floor(c/M)]
+    groups: List[int]                  # opened groups, ascending; the last is the trailing group
+    cand: List[int]                    # chunks of the opened groups (< c), ascending
+    gist_scores: np.ndarray            # [c]: -inf outside cand
+    sel: List[int]                     # expanded chunks + the current chunk, ascending
+    k1: int = 0
+    k2: int = 0
+
+
+def topk_among(scores: Sequence[float], cand: Sequence[int], k: int) -> List[int]:
+    """The k best of ``cand`` by (score descending, index ascending), ascending."""
+    ranked = sorted(cand, key=lambda j: (-float(scores[j]), j))
+    return sorted(ranked[:k])
+
+
+def hssa_select(qv: np.ndarray, gist_k: np.ndarray, meta_k: np.ndarray, c: int, M: int, k1: int, k2: int,
+                scale: float) -> Tuple[np.ndarray, List[int], List[int], np.ndarray, List[int], int, int]:
+    """Readings H1-H3 for one unit with query vectors ``qv``: (meta scores, opened groups,
+    candidate chunks, gist scores, expanded chunks + c, k1 used, k2 used)."""
+    nm = c // M
+    s1 = unit_scores(qv, meta_k, nm, scale)
+    k1u = max(0, min(k1, nm))
+    groups = topk_among(s1, range(nm), k1u) + [nm]
+    cand = [j for j in range(c) if j // M in set(groups)]
+    s2 = np.full(c, NEG_INF)
+    if cand:
+        full = unit_scores(qv, gist_k, c, scale)
+        s2[cand] = full[cand]
+    k2u = max(0, min(k2, len(cand)))
+    sel = topk_among(s2, cand, k2u) + [c]
+    return s1, groups, cand, s2, sel, k1u, k2u
+
+
+def hssa_decode_sequence(Qb: np.ndarray, Kb: np.ndarray, Vb: np.ndarray, L: int, blk: int, sel_mode: str,
+                         M: int, k1: int, k2: int, gist_k: np.ndarray, gist_v: np.ndarray,
+                         meta_k: np.ndarray, meta_v: np.ndarray, scale: Optional[float] = None,
+                         attend: bool = True, mode: str = "skip",
+                         explicit: Optional[Dict[int, Tuple[List[int], List[int]]]] = None
+                         ) -> Tuple[List[HssaUnit], np.ndarray]:
+    """H-SSA decode of one sequence at position L - 1 (readings H1-H5).
+
+    Qb: [hq, 1, d]; Kb, Vb: [hkv, >= L, d]; gist_k/gist_v: [hkv, >= c, d]; meta_k/meta_v:
+    [hkv, >= floor(c/M), d].  explicit[sel_head] = (groups, sel) replaces a unit's own choice
+    (attention checked on lists produced elsewhere when they differ inside the tie band).
+    Returns the units and O [hq, 1, d].
+    """
+    hq, rows, d = Qb.shape
+    assert rows == 1
+    hkv = Kb.shape[0]
+    G = hq // hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    c = (L - 1) // blk
+    nm = c // M
+    units = make_units(L - 1, 1, blk, hq, hkv, sel_mode)
+    out_units: List[HssaUnit] = []
+    O = np.full((hq, 1, Vb.shape[-1]), np.nan)
+    for u in units:
+        g = kv_head_of(u, G, sel_mode)
+        qv = unit_query_vectors(Qb, u)
+        s1, groups, cand, s2, sel, k1u, k2u = hssa_select(qv, gist_k[g], meta_k[g], c, M, k1, k2, scale)
+        out_units.append(HssaUnit(u.sel_head, c, u.heads, s1, groups, cand, s2, sel, k1u, k2u))
+        if not attend:
+            continue
+        if explicit is not None and u.sel_head in explicit:
+            groups, sel = explicit[u.sel_head]
+            cand = [j for j in range(c) if j // M in set(groups)]
+        sel_set = set(sel)
+        gist_ids = [j for j in cand if j not in sel_set]
+        meta_ids = [i for i in range(nm) if i not in set(groups)]
+        # gists, then meta-gists, follow the raw keys (both enter without a gate)
+        extra_k = np.concatenate([np.asarray(gist_k[g][gist_ids], dtype=np.float64).reshape(-1, d),
+                                  np.asarray(meta_k[g][meta_ids], dtype=np.float64).reshape(-1, d)])
+        extra_v = np.concatenate([np.asarray(gist_v[g][gist_ids], dtype=np.float64).reshape(-1, Vb.shape[-1]),
+                                  np.asarray(meta_v[g][meta_ids], dtype=np.float64).reshape(-1, Vb.shape[-1])])
+        ids = list(range(len(gist_ids) + len(meta_ids)))
+        for h in u.heads:
+            O[h, 0, :] = attend_unit(Qb[h, 0:1, :], np.array([L - 1]), Kb[g], Vb[g], L, blk, sel, None, scale,
+                                     mode, extra_k, extra_v, ids)[0]
+    return out_units, O

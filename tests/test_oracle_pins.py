@@ -309,3 +309,92 @@ def test_workload_inputs_are_bf16_and_seeded():
     K2, _ = Workload(2, mini=True).kv(3)
     np.testing.assert_array_equal(K, K2)
     assert K.shape == (8, 4096, 128)
+
+
+# ------------------------------------------------------------------------------------ H-SSA
+def _hssa_data(seed, hq, hkv, d, blk, L):
+    rng = np.random.default_rng(seed)
+    c = (L - 1) // blk
+    Q = rng.standard_normal((hq, 1, d)); K = rng.standard_normal((hkv, L, d)); V = rng.standard_normal((hkv, L, d))
+    gk = rng.standard_normal((hkv, c, d)); gv = rng.standard_normal((hkv, c, d))
+    mk = rng.standard_normal((hkv, c, d)); mv = rng.standard_normal((hkv, c, d))
+    return Q, K, V, gk, gv, mk, mv
+
+
+@pytest.mark.parametrize("sel_mode", ["group", "head"])
+def test_hssa_with_every_group_open_is_gist_selection(sel_mode):
+    """k1 >= the complete groups: every chunk is a candidate and no meta-gist is visible, so the
+    two-level choice is the one-level gist selection with k = k2, bit for bit."""
+    hq, hkv, d, blk, M = 4, 2, 8, 4, 3
+    L = blk * 17 + 2                                               # c = 17: 5 complete groups + 2 trailing chunks
+    Q, K, V, gk, gv, mk, mv = _hssa_data(31, hq, hkv, d, blk, L)
+    units, O = o.hssa_decode_sequence(Q, K, V, L, blk, sel_mode, M, 5, 6, gk, gv, mk, mv)
+    r = o.run_sequence(Q, K, V, L, L - 1, blk, sel_mode, k_fixed=6, gist_k=gk, gist_v=gv)
+    for hu, su in zip(units, r.units):
+        assert hu.groups == [0, 1, 2, 3, 4, 5] and hu.cand == list(range(17))
+        assert hu.sel == list(su.sel)
+    assert np.array_equal(O, r.O)
+
+
+def test_hssa_with_every_chunk_expanded_is_dense_causal():
+    hq, hkv, d, blk, M = 2, 1, 8, 4, 2
+    L = blk * 9 + 1
+    Q, K, V, gk, gv, mk, mv = _hssa_data(32, hq, hkv, d, blk, L)
+    _, O = o.hssa_decode_sequence(Q, K, V, L, blk, "group", M, 100, 100, gk, gv, mk, mv)
+    for h in range(hq):
+        np.testing.assert_allclose(O[h], _sdpa(Q[h], K[0], V[0], np.zeros((1, L))), rtol=0, atol=1e-12)
+
+
+def test_hssa_nothing_opened_attends_meta_gists_and_the_current_chunk():
+    """k1 = k2 = 0 with c a multiple of M (no trailing chunk): the key set is every meta-gist
+    plus the raw tokens of the current chunk, checked with the library routine over that set."""
+    hq, hkv, d, blk, M = 2, 1, 8, 4, 4
+    L = blk * 12 + 3                                               # c = 12 = 3 complete groups of 4
+    Q, K, V, gk, gv, mk, mv = _hssa_data(33, hq, hkv, d, blk, L)
+    units, O = o.hssa_decode_sequence(Q, K, V, L, blk, "group", M, 0, 0, gk, gv, mk, mv)
+    assert units[0].groups == [3] and units[0].cand == [] and units[0].sel == [12]
+    kk = np.concatenate([K[0, 12 * blk:L], mk[0, :3]]); vv = np.concatenate([V[0, 12 * blk:L], mv[0, :3]])
+    for h in range(hq):
+        np.testing.assert_allclose(O[h], _sdpa(Q[h], kk, vv, np.zeros((1, kk.shape[0]))), rtol=0, atol=1e-12)
+
+
+def test_hssa_selection_invariants_and_key_set():
+    """Level 1 and level 2 each keep a top set (no kept score below a dropped one, ties to the
+    lower index), the trailing group is always open, and the attended key set follows the
+    visibility rules: checked against the library routine with a mask built key by key."""
+    hq, hkv, d, blk, M = 2, 1, 8, 2, 3
+    for seed, L, k1, k2 in [(34, 2 * 23 + 1, 2, 3), (35, 2 * 24 + 2, 1, 5), (36, 2 * 7 + 1, 5, 2)]:
+        Q, K, V, gk, gv, mk, mv = _hssa_data(seed, hq, hkv, d, blk, L)
+        # plant exact ties: repeat some meta-gists and gists
+        mk[0, 1] = mk[0, 0]; gk[0, 4] = gk[0, 3]
+        units, O = o.hssa_decode_sequence(Q, K, V, L, blk, "group", M, k1, k2, gk, gv, mk, mv)
+        u = units[0]
+        c, nm = u.c, u.c // M
+        qbar = Q[:, 0, :].mean(axis=0)
+        s1 = np.array([qbar @ mk[0, i] for i in range(nm)]) / math.sqrt(d)
+        s2 = np.array([qbar @ gk[0, j] for j in range(c)]) / math.sqrt(d)
+        opened = [i for i in u.groups if i < nm]
+        assert u.groups[-1] == nm and len(opened) == min(k1, nm)
+        closed = [i for i in range(nm) if i not in opened]
+        for a in opened:
+            for b in closed:
+                assert s1[a] > s1[b] + 1e-12 or (abs(s1[a] - s1[b]) <= 1e-12 and a < b)
+        cand = [j for j in range(c) if j // M in set(u.groups)]
+        assert u.cand == cand and len(cand) <= (min(k1, nm) + 1) * M
+        exp = [j for j in u.sel if j != c]
+        assert u.sel[-1] == c and len(exp) == min(k2, len(cand))
+        for a in exp:
+            for b in set(cand) - set(exp):
+                assert s2[a] > s2[b] + 1e-12 or (abs(s2[a] - s2[b]) <= 1e-12 and a < b)
+        # the key set, key by key: raw tokens, gists, meta-gists
+        keys, vals, add = [], [], []
+        for t in range(L):
+            keys.append(K[0, t]); vals.append(V[0, t]); add.append(0.0 if t // blk in u.sel else -np.inf)
+        for j in range(c):
+            keys.append(gk[0, j]); vals.append(gv[0, j])
+            add.append(0.0 if (j // M in set(u.groups) and j not in u.sel) else -np.inf)
+        for i in range(nm):
+            keys.append(mk[0, i]); vals.append(mv[0, i]); add.append(0.0 if i not in u.groups else -np.inf)
+        kk, vv, mask = np.array(keys), np.array(vals), np.array(add)[None, :]
+        for h in range(hq):
+            np.testing.assert_allclose(O[h], _sdpa(Q[h], kk, vv, mask), rtol=0, atol=1e-12)

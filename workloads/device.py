@@ -1,7 +1,7 @@
 """Upload a workload's inputs into padded device tensors (torch), one sequence at a time.
 
 Layouts: Q prefill [B, Hq, tq, d], Q decode [B, Hq, d], K/V [B, Hkv, Lmax, d],
-gist K/V [B, Hkv, NCmax, d]; rows past a sequence's length are zero.  Values are the
+gist K/V [B, Hkv, NCmax, d], meta-gist K/V [B, Hkv, NMmax, d]; rows past a sequence's length are zero.  Values are the
 generator's (bf16-representable) numbers, converted exactly to the workload dtype.
 """
 from __future__ import annotations
@@ -25,10 +25,12 @@ class DeviceInputs:
     gist_k: "object" = None
     gist_v: "object" = None
     host: Dict[int, dict] = field(default_factory=dict)   # kept numpy inputs of some sequences
+    meta_k: "object" = None                                # [B, Hkv, NMmax, d] (two-level gist mode)
+    meta_v: "object" = None
 
 
 def upload(w: Workload, seqs: List[int], device="cuda", keep_host=(), lmax: Optional[int] = None,
-           gist: bool = False) -> DeviceInputs:
+           gist: bool = False, meta: bool = False) -> DeviceInputs:
     import torch
     dt = torch.bfloat16 if w.is_bf16() else torch.float32
     lens = [w.seq_lens[b] for b in seqs]
@@ -48,6 +50,11 @@ def upload(w: Workload, seqs: List[int], device="cuda", keep_host=(), lmax: Opti
         nc = max(L // w.block for L in lens)
         gk = torch.zeros((B, w.hkv, max(nc, 1), w.d), dtype=dt, device=device)
         gv = torch.zeros((B, w.hkv, max(nc, 1), w.d), dtype=dt, device=device)
+    mk = mv = None
+    if meta:
+        nm = max(L // w.block for L in lens) // w.spec["group_chunks"]
+        mk = torch.zeros((B, w.hkv, max(nm, 1), w.d), dtype=dt, device=device)
+        mv = torch.zeros((B, w.hkv, max(nm, 1), w.d), dtype=dt, device=device)
     host = {}
     for i, b in enumerate(seqs):
         q = w.q(b)
@@ -67,10 +74,16 @@ def upload(w: Workload, seqs: List[int], device="cuda", keep_host=(), lmax: Opti
                 gk[i, :, :nc].copy_(torch.from_numpy(g_k).to(dt))
                 gv[i, :, :nc].copy_(torch.from_numpy(g_v).to(dt))
             entry.update(gist_k=g_k, gist_v=g_v)
+        if meta:
+            m_k, m_v = w.meta(b)
+            if m_k.shape[1]:
+                mk[i, :, :m_k.shape[1]].copy_(torch.from_numpy(m_k).to(dt))
+                mv[i, :, :m_v.shape[1]].copy_(torch.from_numpy(m_v).to(dt))
+            entry.update(meta_k=m_k, meta_v=m_v)
         if b in keep_host:
             entry.update(q=q, k=Kb, v=Vb)
             host[b] = entry
     torch.cuda.synchronize()
     q_start = None if decode else [w.q_start[b] for b in seqs]
     return DeviceInputs(seqs=list(seqs), seq_lens=lens, q_start=q_start, Q=Q, K=K, V=V, gist_k=gk, gist_v=gv,
-                        host=host)
+                        host=host, meta_k=mk, meta_v=mv)

@@ -34,7 +34,7 @@ from typing import Dict, List, Optional, Tuple
 import numpy as np
 
 # stream ids (second component of the seed sequence's spawn key)
-_S_LENS, _S_Q, _S_K, _S_V, _S_NEEDLE, _S_OFFSET, _S_GK, _S_GV = range(8)
+_S_LENS, _S_Q, _S_K, _S_V, _S_NEEDLE, _S_OFFSET, _S_GK, _S_GV, _S_MK, _S_MV = range(10)
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
@@ -86,6 +86,13 @@ CONFIGS: Dict[int, dict] = {
             n_prefill=8, tq=4096,
             sel="head", k_fixed=0, frac_num=1, frac_den=20, count_current=1,
             sink=False, gate=True, needles_frac=0.01, offset_sigma=0.0),
+    # The two-level (meta-gist) variant of configuration 4's shape: groups of 32 chunks, the 8
+    # best of the 64 groups opened, then 104 of their chunks expanded as in configuration 4.
+    6: dict(name="hssa_decode_b4_h64x8_128k_m32", kind="gist_decode", dtype="bf16",
+            batch=4, hq=64, hkv=8, d=128, block=64, seq_len=131073,
+            sel="group", k_fixed=104, frac_num=0, frac_den=0, count_current=0,
+            sink=False, gate=False, needles=0, offset_sigma=0.0, gist_sigma=0.1,
+            group_chunks=32, k_groups=8, meta_sigma=0.1),
 }
 
 # "mini" variants: same structure, lengths divided by 8 (budgets that are fixed counts are
@@ -96,6 +103,7 @@ _MINI = {
     3: dict(seq_len=4096, tq=4096),
     4: dict(seq_len=16385, k_fixed=13),
     5: dict(len_lo=512, len_hi=16384, tq=512),
+    6: dict(seq_len=16385, k_fixed=13, group_chunks=8, k_groups=4),
 }
 
 
@@ -236,6 +244,21 @@ class Workload:
             cm = X[:, : nc * self.block, :].astype(np.float64).reshape(self.hkv, nc, self.block, self.d).mean(axis=2)
             noise = _rng(self.seed, stream, b).standard_normal((self.hkv, nc, self.d), dtype=np.float32)
             out.append(self._finish((cm + sig * noise.astype(np.float64)).astype(np.float32)))
+        return out[0], out[1]
+
+    def meta(self, b: int) -> Tuple[np.ndarray, np.ndarray]:
+        """(meta_k, meta_v) of sequence b: each [hkv, NM, d] for the NM complete groups of
+        group_chunks consecutive chunks: the mean of the group's gists plus N(0, meta_sigma^2)
+        noise, as the gists are the chunk means plus noise."""
+        M = self.spec["group_chunks"]
+        gk, gv = self.gist(b)
+        nm = gk.shape[1] // M
+        sig = self.spec.get("meta_sigma", 0.1)
+        out = []
+        for X, stream in ((gk, _S_MK), (gv, _S_MV)):
+            gm = X[:, : nm * M, :].astype(np.float64).reshape(self.hkv, nm, M, self.d).mean(axis=2)
+            noise = _rng(self.seed, stream, b).standard_normal((self.hkv, nm, self.d), dtype=np.float32)
+            out.append(self._finish((gm + sig * noise.astype(np.float64)).astype(np.float32)))
         return out[0], out[1]
 
     # ------------------------------------------------------------------ budget description
