@@ -140,6 +140,65 @@ def decode_step_setup(sas, w, inp, gist=False):
     return fns, dict(reps=reps, scores=scores, idx=idx, nsel=nsel, gate=gate, O=O)
 
 
+def hssa_step_setup(sas, w, inp):
+    """Two-level gist selection + its attention (gist and meta-gist keys resident)."""
+    import torch
+    lens = inp.seq_lens
+    Lmax = inp.K.shape[2]
+    M, k1, k2 = w.spec["group_chunks"], w.spec["k_groups"], w.k_fixed
+    idx, nsel, gidx, gsel = sas.hssa_select_decode(inp.Q, inp.gist_k, inp.meta_k, lens, w.block, w.hkv, Lmax, M,
+                                                   k1, k2, sel_mode=w.sel)
+    O = torch.empty_like(inp.Q)
+    B = len(lens)
+    dec_ws = torch.zeros(sas.hssa_decode_workspace_bytes(B, w.hq, w.hkv, w.d, w.block, Lmax, lens, w.sel,
+                                                         idx.shape[1], gidx.shape[1], M),
+                         dtype=torch.uint8, device="cuda")
+    sel_ws = torch.empty(max(16, sas.hssa_select_workspace_bytes(B, w.hq, w.hkv, w.d, w.block, Lmax, lens, w.sel, M,
+                                                                 k1)), dtype=torch.uint8, device="cuda")
+
+    def attend():
+        sas.hssa_decode(inp.Q, inp.K, inp.V, lens, w.block, inp.gist_k, inp.gist_v, inp.meta_k, inp.meta_v, M,
+                        idx, nsel, gidx, sel_mode=w.sel, O=O, workspace=dec_ws)
+
+    def step():
+        sas.hssa_select_decode(inp.Q, inp.gist_k, inp.meta_k, lens, w.block, w.hkv, Lmax, M, k1, k2,
+                               sel_mode=w.sel, kcap=idx.shape[1], gcap=gidx.shape[1], idx=idx, nsel=nsel, gidx=gidx,
+                               gsel=gsel, workspace=sel_ws)
+        attend()
+
+    return dict(step=step, attend=attend), dict(idx=idx, nsel=nsel, gidx=gidx, gsel=gsel, O=O)
+
+
+def hssa_bytes(w, inp, bufs):
+    """Bytes the two-level step must move, per (sequence, KV group): the meta-gist keys of the
+    complete groups and the gist keys of the open groups' chunks (read once for scoring), the K/V
+    rows of the expanded chunks and of the current chunk, the gist values of the open groups'
+    unexpanded chunks, the meta-gist values of the closed groups, Q and O."""
+    idx = bufs["idx"].cpu().numpy()
+    nsel = bufs["nsel"].cpu().numpy()
+    gidx = bufs["gidx"].cpu().numpy()
+    gsel = bufs["gsel"].cpu().numpy()
+    M = w.spec["group_chunks"]
+    e, d = 2, w.d
+    assert w.sel == "group"
+    total = 0
+    for bi, L in enumerate(inp.seq_lens):
+        c = (L - 1) // w.block
+        nm = c // M
+        for g in range(w.hkv):
+            u = bi * w.hkv + g
+            groups = [int(x) for x in gidx[u, :gsel[u]]]
+            cand = [j for j in range(c) if j // M in set(groups)]
+            sel = [int(x) for x in idx[u, :nsel[u]]]
+            rows = sum(min((j + 1) * w.block, L) - j * w.block for j in sel)
+            total += nm * d * e + len(cand) * d * e                     # scoring reads
+            total += rows * d * e * 2                                   # raw K and V
+            total += (len(cand) - (len(sel) - 1)) * d * e               # gist V of open, unexpanded chunks
+            total += (nm - (len(groups) - 1)) * d * e                   # meta-gist V of closed groups
+            total += w.group * d * e * 2                                # Q and O
+    return total
+
+
 def prefill_step_setup(sas, w, inp):
     import torch
     lens = inp.seq_lens
@@ -311,7 +370,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="decode,reps,prefill,gist,mixed",
+    ap.add_argument("--only", default="decode,reps,prefill,gist,hssa,mixed",
                     help="comma list of measurements: decode,reps,prefill,gist,mixed,copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -439,6 +498,23 @@ def main():
         decode_measure("gist_decode_128k", w4, inp4, "gist_decode_b4_h64x8_d128_ctx131073_chunk64_top104",
                        gist=True)
         del inp4
+        torch.cuda.empty_cache()
+    if "hssa" in only:
+        w6 = Workload(6)
+        log("[bench] generating the 128K two-level gist decode workload")
+        inp6 = upload(w6, list(range(w6.batch)), gist=True, meta=True)
+        fns, bufs = hssa_step_setup(sas, w6, inp6)
+        torch.cuda.synchronize()
+        hb = hssa_bytes(w6, inp6, bufs)
+        t_step, _ = timer.time(fns["step"], K_, W_)
+        t_att, _ = timer.time(fns["attend"], K_, W_)
+        gbs = hb / (t_step * 1e-3) / 1e9
+        extra["hssa_decode_128k"] = {
+            "workload": "hssa_decode_b4_h64x8_d128_ctx131073_chunk64_groups32_open8_top104",
+            "step_us": round(t_step * 1e3, 2), "attend_us": round(t_att * 1e3, 2), "GB/s": round(gbs, 1),
+            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "bytes_per_step": hb}
+        log(f"[bench] hssa_decode_128k: step {t_step * 1e3:.1f} us -> {gbs:.0f} GB/s; attend {t_att * 1e3:.1f} us")
+        del inp6, fns, bufs
         torch.cuda.empty_cache()
     if "mixed" in only:
         w5 = Workload(5)

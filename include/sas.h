@@ -14,6 +14,8 @@
  *   sas_block_scores  score every earlier block against each selection unit's queries
  *   sas_topk_select   top-k blocks + the current block (+ block 0), optional log-gate
  *   sas_sparse_prefill / sas_sparse_decode  attention over the selected blocks only
+ *   sas_hssa_select_decode / sas_hssa_decode  two-level gist selection (meta-gists) and its
+ *                     attention, for decode
  *
  * Conventions shared by every entry point
  *   - Shapes.  B sequences, Hq query heads, Hkv KV heads (Hq % Hkv == 0, G = Hq/Hkv),
@@ -201,6 +203,55 @@ sas_status sas_sparse_decode(const sas_problem *p, const void *Q, const int64_t 
                              const float *gate, int32_t kcap, float scale, void *O,
                              const int64_t o_stride[2], void *workspace, size_t workspace_bytes,
                              void *stream);
+
+/* Two-level gist selection for decode ([SSA] hierarchical extension: meta-gist tokens, gists
+ * of gists, make a coarse level; the ordinary gists of the chosen part are then scored and the
+ * best chunks expanded).  Readings, as the page gives no more: a group is group_chunks (M)
+ * consecutive chunks of blk tokens and has a meta-gist when it is complete and lies before the
+ * current chunk c = floor((L_b - 1) / blk), i.e. groups i < c / M.
+ *   Level 1 opens the top-k1 of those groups by meta-gist score, plus the trailing group
+ *     (chunks floor(c/M) M .. c - 1), which is always open.
+ *   Level 2 expands the top-k2 chunks of the open groups by gist score; the current chunk is
+ *     always attended raw.  Ties go to the lower index at both levels; scores are
+ *     scale * mean over the unit's heads of q . x, as in sas_block_scores.
+ *   Attention (sas_hssa_decode) sees the raw tokens of the expanded chunks and of the current
+ *     chunk, the gists of the open groups' chunks that were not expanded, and the meta-gists of
+ *     the groups that were not opened; no gate.
+ * bf16 only; 4 <= M <= 64; c <= 2048, at most 511 groups, and (k1 + 1) * M <= 2048.
+ *   Q: [B, Hq, d]; gist_k: [B, Hkv, NC, d] (one per complete chunk); meta_k: [B, Hkv, NM, d].
+ *   Outputs per unit u (units as in sas_select_decode):
+ *     idx [units, kcap]: the expanded chunks ascending, then c; -1 padded; nsel[u] = its length
+ *                        (min(k2, candidates) + 1), kcap >= that for every unit.
+ *     gidx [units, gcap]: the opened groups ascending, then the trailing group floor(c/M) (which
+ *                        may hold no complete chunk); -1 padded; gsel[u] = its length
+ *                        (min(k1, floor(c/M)) + 1), gcap >= that.
+ *   workspace: sas_hssa_select_workspace(p, sel_mode, M, k1) bytes (score rows; no state kept
+ *     between calls). */
+size_t sas_hssa_select_workspace(const sas_problem *p, int32_t sel_mode, int32_t group_chunks,
+                                 int32_t k1);
+sas_status sas_hssa_select_decode(const sas_problem *p, const void *Q, const int64_t q_stride[2],
+                                  const void *gist_k, const int64_t gist_stride[3],
+                                  const void *meta_k, const int64_t meta_stride[3],
+                                  int32_t group_chunks, int32_t sel_mode, int32_t k1, int32_t k2,
+                                  float scale, int32_t kcap, int32_t gcap, int32_t *idx,
+                                  int32_t *nsel, int32_t *gidx, int32_t *gsel, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/* Attention of the two-level gist selection (key set above), split-K over 64-key tiles like
+ * sas_sparse_decode: per unit, one tile per gidx entry (that group's gists), 64 meta-gists per
+ * tile, then the raw tiles of idx.  meta_v: [B, Hkv, NM, d] like meta_k.  workspace:
+ * sas_hssa_decode_workspace() bytes; its arrival counters must be zero before the first call,
+ * and every call leaves them zero.  Errors as sas_sparse_decode; bf16 only. */
+size_t sas_hssa_decode_workspace(const sas_problem *p, int32_t sel_mode, int32_t kcap, int32_t gcap,
+                                 int32_t group_chunks);
+sas_status sas_hssa_decode(const sas_problem *p, const void *Q, const int64_t q_stride[2],
+                           const void *K, const void *V, const int64_t kv_stride[3],
+                           const void *gist_k, const void *gist_v, const int64_t gist_stride[3],
+                           const void *meta_k, const void *meta_v, const int64_t meta_stride[3],
+                           int32_t group_chunks, int32_t sel_mode, const int32_t *idx,
+                           const int32_t *nsel, int32_t kcap, const int32_t *gidx, int32_t gcap,
+                           float scale, void *O, const int64_t o_stride[2], void *workspace,
+                           size_t workspace_bytes, void *stream);
 
 /* Text of the last non-OK status returned on this thread ("" if none). */
 const char *sas_last_error(void);

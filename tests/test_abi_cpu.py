@@ -189,3 +189,43 @@ def test_attention_validation_codes():
     need9 = lib.sas_sparse_decode_workspace(C.byref(p9), 0, 8, 0)
     assert lib.sas_sparse_decode(C.byref(p9), FAKE, qs2, FAKE, FAKE, kvs, None, None, None, 0, FAKE, FAKE, None, 8,
                                  0.0, FAKE, qs2, FAKE, need9, None) == _lib.SAS_ERR_UNSUPPORTED
+
+
+def test_hssa_validation_codes():
+    """Two-level gist selection and attention: host validation (no HIP call)."""
+    lib = _lib.load()
+    p, a = _problem(lens=(1000, 700))
+    q2 = _lib.i64x([8 * 128, 128])
+    s3 = _lib.i64x([2 * 16 * 128, 16 * 128, 128])
+    ws = C.c_size_t(1 << 20)
+
+    # max_len 1000, blk 64: current chunk <= 15, so 3 complete groups of 4 chunks
+    def sel(M=4, k1=2, k2=3, kcap=8, gcap=4, ptr=FAKE, prob=p, sm=_lib.SAS_SEL_GROUP):
+        return lib.sas_hssa_select_decode(C.byref(prob), ptr, q2, FAKE, s3, FAKE, s3, M, sm, k1, k2, 0.0, kcap, gcap,
+                                          FAKE, FAKE, FAKE, FAKE, FAKE, ws, None)
+
+    assert sel(ptr=None) == _lib.SAS_ERR_NULL
+    assert sel(M=3) == _lib.SAS_ERR_UNSUPPORTED
+    assert sel(M=65) == _lib.SAS_ERR_UNSUPPORTED
+    assert sel(k1=-1) == _lib.SAS_ERR_SHAPE
+    assert sel(gcap=2) == _lib.SAS_ERR_SHAPE          # 2 opened + the trailing group
+    assert b"gcap 2 < 3" in lib.sas_last_error()
+    assert sel(k1=9, gcap=3) == _lib.SAS_ERR_SHAPE    # k1 capped at the 3 groups: 4 entries
+    assert sel(kcap=3) == _lib.SAS_ERR_SHAPE          # 3 expanded + the current chunk
+    assert sel(sm=7) == _lib.SAS_ERR_SHAPE
+    pf, af = _problem(dtype=_lib.SAS_F32)
+    assert sel(prob=pf) == _lib.SAS_ERR_UNSUPPORTED
+    assert lib.sas_hssa_select_workspace(C.byref(p), _lib.SAS_SEL_GROUP, 8, 2) > 0
+    assert lib.sas_hssa_select_workspace(C.byref(p), _lib.SAS_SEL_GROUP, 2, 2) == 0
+
+    def dec(M=8, kcap=8, gcap=4, ptr=FAKE, wbytes=1 << 30):
+        return lib.sas_hssa_decode(C.byref(p), FAKE, q2, FAKE, FAKE, s3, FAKE, FAKE, s3, ptr, FAKE, s3, M,
+                                   _lib.SAS_SEL_GROUP, FAKE, FAKE, kcap, FAKE, gcap, 0.0, FAKE, q2, FAKE,
+                                   C.c_size_t(wbytes), None)
+
+    assert dec(ptr=None) == _lib.SAS_ERR_NULL
+    assert dec(M=2) == _lib.SAS_ERR_UNSUPPORTED
+    assert dec(gcap=0) == _lib.SAS_ERR_SHAPE
+    assert dec(wbytes=16) == _lib.SAS_ERR_WORKSPACE
+    need = lib.sas_hssa_decode_workspace(C.byref(p), _lib.SAS_SEL_GROUP, 8, 4, 8)
+    assert need > 0 and dec(wbytes=need - 1) == _lib.SAS_ERR_WORKSPACE

@@ -290,3 +290,76 @@ def sparse_decode(Q, K, V, seq_lens, block, idx, nsel, gate=None, sel_mode="grou
                                 workspace.numel() if workspace is not None else 0, _stream(stream)),
           "sas_sparse_decode")
     return O
+
+
+def hssa_select_decode(Q, gist_k, meta_k, seq_lens, block, hkv, max_len, group_chunks, k1, k2, sel_mode="group",
+                       scale=0.0, kcap=None, gcap=None, idx=None, nsel=None, gidx=None, gsel=None, workspace=None,
+                       stream=None):
+    """Two-level gist selection for decode: (idx, nsel, gidx, gsel).
+
+    idx [U, kcap]: expanded chunks ascending, then the current chunk; gidx [U, gcap]: opened groups
+    ascending, then the trailing group (group_chunks chunks per group).
+    """
+    torch = _torch()
+    B, hq, d = Q.shape
+    sm = sel_code(sel_mode)
+    S = hq if sm == SAS_SEL_HEAD else hkv
+    nm_cap = ((int(max_len) - 1) // block) // group_chunks
+    k1u = max(0, min(int(k1), nm_cap))
+    if gcap is None:
+        gcap = k1u + 1
+    if kcap is None:
+        kcap = min(int(k2), (k1u + 1) * group_chunks) + 1
+    p = _Prob(B, hq, hkv, d, block, _dtype_code(Q), max_len, seq_lens)
+    lib = load()
+    dev = Q.device
+    idx = idx if idx is not None else torch.empty((B * S, kcap), dtype=torch.int32, device=dev)
+    nsel = nsel if nsel is not None else torch.empty((B * S,), dtype=torch.int32, device=dev)
+    gidx = gidx if gidx is not None else torch.empty((B * S, gcap), dtype=torch.int32, device=dev)
+    gsel = gsel if gsel is not None else torch.empty((B * S,), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(lib.sas_hssa_select_workspace(p.ref, sm, group_chunks, int(k1)), dtype=torch.uint8,
+                                device=dev)
+    check(lib.sas_hssa_select_decode(p.ref, _ptr(Q), _strides(Q, 2), _ptr(gist_k), _strides(gist_k, 3), _ptr(meta_k),
+                                     _strides(meta_k, 3), group_chunks, sm, int(k1), int(k2), float(scale), kcap, gcap,
+                                     _ptr(idx), _ptr(nsel), _ptr(gidx), _ptr(gsel), _ptr(workspace),
+                                     workspace.numel(), _stream(stream)),
+          "sas_hssa_select_decode")
+    return idx, nsel, gidx, gsel
+
+
+def hssa_decode(Q, K, V, seq_lens, block, gist_k, gist_v, meta_k, meta_v, group_chunks, idx, nsel, gidx,
+                sel_mode="group", scale=0.0, O=None, workspace=None, stream=None):
+    """Attention of the two-level gist selection: O [B, Hq, d] for the row at position L_b - 1."""
+    torch = _torch()
+    B, hq, d = Q.shape
+    _, hkv, lmax, _ = K.shape
+    for a, b_, what in ((K, V, "K and V"), (gist_k, gist_v, "gist K and V"), (meta_k, meta_v, "meta-gist K and V")):
+        if a.stride() != b_.stride():
+            raise ValueError(what + " must share strides")
+    if O is None:
+        O = torch.empty_like(Q)
+    kcap, gcap = idx.shape[1], gidx.shape[1]
+    p = _Prob(B, hq, hkv, d, block, _dtype_code(Q), lmax, seq_lens)
+    lib = load()
+    sm = sel_code(sel_mode)
+    if workspace is None:
+        # arrival counters must start at zero (the library leaves them zero after each call)
+        workspace = torch.zeros(lib.sas_hssa_decode_workspace(p.ref, sm, kcap, gcap, group_chunks), dtype=torch.uint8,
+                                device=Q.device)
+    check(lib.sas_hssa_decode(p.ref, _ptr(Q), _strides(Q, 2), _ptr(K), _ptr(V), _strides(K, 3), _ptr(gist_k),
+                              _ptr(gist_v), _strides(gist_k, 3), _ptr(meta_k), _ptr(meta_v), _strides(meta_k, 3),
+                              group_chunks, sm, _ptr(idx), _ptr(nsel), kcap, _ptr(gidx), gcap, float(scale), _ptr(O),
+                              _strides(O, 2), _ptr(workspace), workspace.numel(), _stream(stream)),
+          "sas_hssa_decode")
+    return O
+
+
+def hssa_select_workspace_bytes(B, hq, hkv, d, block, max_len, seq_lens, sel_mode, group_chunks, k1) -> int:
+    p = _Prob(B, hq, hkv, d, block, SAS_BF16, max_len, seq_lens)
+    return int(load().sas_hssa_select_workspace(p.ref, sel_code(sel_mode), group_chunks, int(k1)))
+
+
+def hssa_decode_workspace_bytes(B, hq, hkv, d, block, max_len, seq_lens, sel_mode, kcap, gcap, group_chunks) -> int:
+    p = _Prob(B, hq, hkv, d, block, SAS_BF16, max_len, seq_lens)
+    return int(load().sas_hssa_decode_workspace(p.ref, sel_code(sel_mode), kcap, gcap, group_chunks))

@@ -23,7 +23,8 @@ STATUS_NAMES = {0: "SAS_OK", -1: "SAS_ERR_NULL", -2: "SAS_ERR_SHAPE", -3: "SAS_E
 EXPORTED = ("sas_num_qblocks", "sas_required_kcap", "sas_block_reps", "sas_block_reps_update",
             "sas_block_scores_workspace",
             "sas_block_scores", "sas_topk_select", "sas_select_decode_workspace", "sas_select_decode",
-            "sas_sparse_prefill", "sas_sparse_decode_workspace", "sas_sparse_decode", "sas_last_error")
+            "sas_sparse_prefill", "sas_sparse_decode_workspace", "sas_sparse_decode", "sas_hssa_select_workspace",
+            "sas_hssa_select_decode", "sas_hssa_decode_workspace", "sas_hssa_decode", "sas_last_error")
 
 
 class Problem(C.Structure):
@@ -61,6 +62,14 @@ _SIGS = {
     "sas_sparse_decode_workspace": (C.c_size_t, [_P, C.c_int32, C.c_int32, C.c_int32]),
     "sas_sparse_decode": (C.c_int, [_P, _VP, _I64_3, _VP, _VP, _I64_3, _VP, _VP, _I64_3, C.c_int32, _VP, _VP, _VP,
                                     C.c_int32, C.c_float, _VP, _I64_3, _VP, C.c_size_t, _VP]),
+    "sas_hssa_select_workspace": (C.c_size_t, [_P, C.c_int32, C.c_int32, C.c_int32]),
+    "sas_hssa_select_decode": (C.c_int, [_P, _VP, _I64_3, _VP, _I64_3, _VP, _I64_3, C.c_int32, C.c_int32, C.c_int32,
+                                         C.c_int32, C.c_float, C.c_int32, C.c_int32, _VP, _VP, _VP, _VP, _VP,
+                                         C.c_size_t, _VP]),
+    "sas_hssa_decode_workspace": (C.c_size_t, [_P, C.c_int32, C.c_int32, C.c_int32, C.c_int32]),
+    "sas_hssa_decode": (C.c_int, [_P, _VP, _I64_3, _VP, _VP, _I64_3, _VP, _VP, _I64_3, _VP, _VP, _I64_3, C.c_int32,
+                                  C.c_int32, _VP, _VP, C.c_int32, _VP, C.c_int32, C.c_float, _VP, _I64_3, _VP,
+                                  C.c_size_t, _VP]),
     "sas_last_error": (C.c_char_p, []),
 }
 

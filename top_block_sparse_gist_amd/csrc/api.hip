@@ -369,4 +369,108 @@ sas_status sas_sparse_decode(const sas_problem *p, const void *Q, const int64_t 
                     "sas_sparse_decode");
 }
 
+// ---- two-level gist selection (H-SSA) -------------------------------------------------------
+// checks shared by the two entry points: bf16, group size, the opened-group list capacity
+static sas_status check_hssa(const sas_problem *p, const SeqTable &tab, int32_t sel_mode, int32_t M, int32_t gcap,
+                             int *maxc_out) {
+  sas_status st;
+  if ((st = check_sel(sel_mode)) != SAS_OK) return st;
+  if (p->dtype != SAS_BF16) return fail(SAS_ERR_UNSUPPORTED, "two-level gist selection needs bf16 inputs");
+  if (M < 4 || M > 64) return fail(SAS_ERR_UNSUPPORTED, "group_chunks %d outside [4, 64]", M);
+  if (gcap < 1) return fail(SAS_ERR_SHAPE, "gcap must be >= 1");
+  int maxc = 0;
+  for (int b = 0; b < p->batch; ++b) maxc = std::max(maxc, (tab.len[b] - 1) / p->block);
+  *maxc_out = maxc;
+  return SAS_OK;
+}
+
+size_t sas_hssa_select_workspace(const sas_problem *p, int32_t sel_mode, int32_t group_chunks, int32_t k1) {
+  if (!p || p->block < 64 || p->max_len < 1 || group_chunks < 4 || group_chunks > 64 || k1 < 0) return 0;
+  return hssa_select_workspace_bytes(*p, sel_mode, group_chunks, k1);
+}
+
+sas_status sas_hssa_select_decode(const sas_problem *p, const void *Q, const int64_t q_stride[2],
+                                  const void *gist_k, const int64_t gist_stride[3], const void *meta_k,
+                                  const int64_t meta_stride[3], int32_t group_chunks, int32_t sel_mode, int32_t k1,
+                                  int32_t k2, float scale, int32_t kcap, int32_t gcap, int32_t *idx, int32_t *nsel,
+                                  int32_t *gidx, int32_t *gsel, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
+  SeqTable tab{};
+  sas_status st;
+  if ((st = check_problem(p, &tab)) != SAS_OK) return st;
+  if (!Q || !q_stride || !gist_k || !gist_stride || !meta_k || !meta_stride || !idx || !nsel || !gidx || !gsel)
+    return fail(SAS_ERR_NULL, "a required pointer is NULL");
+  int maxc = 0;
+  if ((st = check_hssa(p, tab, sel_mode, group_chunks, gcap, &maxc)) != SAS_OK) return st;
+  if (k1 < 0 || k2 < 0) return fail(SAS_ERR_SHAPE, "k1 and k2 must be >= 0");
+  if (scale < 0.f || !isfinite(scale)) return fail(SAS_ERR_SHAPE, "scale must be finite and >= 0");
+  if (p->hq / p->hkv > 16) return fail(SAS_ERR_UNSUPPORTED, "at most 16 query heads per KV head");
+  if (maxc > SELECT_DECODE_MAX_C) return fail(SAS_ERR_UNSUPPORTED, "current chunk %d > %d", maxc, SELECT_DECODE_MAX_C);
+  const int nm_cap = ((p->max_len - 1) / p->block) / group_chunks;
+  if (nm_cap + 1 > 512) return fail(SAS_ERR_UNSUPPORTED, "%d groups of %d chunks: at most 511", nm_cap, group_chunks);
+  const int ncand = hssa_candidates_max(*p, group_chunks, k1);
+  if (ncand > 2048)
+    return fail(SAS_ERR_UNSUPPORTED, "(k1 + 1) * group_chunks = %d candidate chunks: at most 2048", ncand);
+  const int k1u = std::min(k1, nm_cap), k2u = std::min(k2, ncand);
+  if (gcap < k1u + 1) return fail(SAS_ERR_SHAPE, "gcap %d < %d opened groups", gcap, k1u + 1);
+  if (kcap < k2u + 1) return fail(SAS_ERR_SHAPE, "kcap %d < %d selected chunks", kcap, k2u + 1);
+  if (!aligned16(Q) || !aligned16(gist_k) || !aligned16(meta_k) || !strides_ok(q_stride, 2, 2) ||
+      !strides_ok(gist_stride, 3, 2) || !strides_ok(meta_stride, 3, 2))
+    return fail(SAS_ERR_SHAPE, "Q / gist / meta-gist keys must be 16-byte aligned with 16-byte-multiple row strides");
+  const size_t wneed = hssa_select_workspace_bytes(*p, sel_mode, group_chunks, k1);
+  if (!workspace || workspace_bytes < wneed)
+    return fail(SAS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", wneed, workspace_bytes);
+  if (!aligned16(workspace)) return fail(SAS_ERR_SHAPE, "workspace must be 16-byte aligned");
+  return hip_status(launch_hssa_select(*p, tab, Q, q_stride, gist_k, gist_stride, meta_k, meta_stride, group_chunks,
+                                       sel_mode, k1, k2, resolve_scale(scale, p->head_dim), kcap, gcap, idx, nsel,
+                                       gidx, gsel, (float *)workspace, (hipStream_t)stream),
+                    "sas_hssa_select_decode");
+}
+
+size_t sas_hssa_decode_workspace(const sas_problem *p, int32_t sel_mode, int32_t kcap, int32_t gcap,
+                                 int32_t group_chunks) {
+  if (!p || kcap < 1 || gcap < 1 || p->dtype != SAS_BF16 || p->block < 64 || p->max_len < 1 || group_chunks < 4 ||
+      group_chunks > 64)
+    return 0;
+  return hssa_decode_workspace_bytes(*p, sel_mode, kcap, gcap, group_chunks);
+}
+
+sas_status sas_hssa_decode(const sas_problem *p, const void *Q, const int64_t q_stride[2], const void *K,
+                           const void *V, const int64_t kv_stride[3], const void *gist_k, const void *gist_v,
+                           const int64_t gist_stride[3], const void *meta_k, const void *meta_v,
+                           const int64_t meta_stride[3], int32_t group_chunks, int32_t sel_mode, const int32_t *idx,
+                           const int32_t *nsel, int32_t kcap, const int32_t *gidx, int32_t gcap, float scale,
+                           void *O, const int64_t o_stride[2], void *workspace, size_t workspace_bytes,
+                           void *stream) {
+  SeqTable tab{};
+  sas_status st;
+  if ((st = check_problem(p, &tab)) != SAS_OK) return st;
+  if (!Q || !q_stride || !K || !V || !kv_stride || !gist_k || !gist_v || !gist_stride || !meta_k || !meta_v ||
+      !meta_stride || !idx || !nsel || !gidx || !O || !o_stride)
+    return fail(SAS_ERR_NULL, "a required pointer is NULL");
+  int maxc = 0;
+  if ((st = check_hssa(p, tab, sel_mode, group_chunks, gcap, &maxc)) != SAS_OK) return st;
+  if (kcap < 1) return fail(SAS_ERR_SHAPE, "kcap must be >= 1");
+  if (scale < 0.f || !isfinite(scale)) return fail(SAS_ERR_SHAPE, "scale must be finite and >= 0");
+  if (sel_mode == SAS_SEL_GROUP && p->hq / p->hkv > 16)
+    return fail(SAS_ERR_UNSUPPORTED, "per-group decode supports at most 16 query heads per KV head");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(gist_k) || !aligned16(gist_v) ||
+      !aligned16(meta_k) || !aligned16(meta_v) || !strides_ok(q_stride, 2, 2) || !strides_ok(kv_stride, 3, 2) ||
+      !strides_ok(o_stride, 2, 2) || !strides_ok(gist_stride, 3, 2) || !strides_ok(meta_stride, 3, 2))
+    return fail(SAS_ERR_SHAPE, "Q/K/V/O/gist/meta-gist must be 16-byte aligned with 16-byte-multiple row strides");
+  int nwg = 0, cap = 0;
+  if (!hssa_merge_fits(*p, tab, sel_mode, kcap, gcap, group_chunks, &nwg, &cap))
+    return fail(SAS_ERR_UNSUPPORTED, "kcap %d + gcap %d need %d split-K records per unit; the merge holds %d", kcap,
+                gcap, nwg, cap);
+  const size_t need = hssa_decode_workspace_bytes(*p, sel_mode, kcap, gcap, group_chunks);
+  if (!workspace || workspace_bytes < need)
+    return fail(SAS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  if (!aligned16(workspace)) return fail(SAS_ERR_SHAPE, "workspace must be 16-byte aligned");
+  return hip_status(launch_hssa_decode(*p, tab, Q, q_stride, K, V, kv_stride, gist_k, gist_v, gist_stride, meta_k,
+                                       meta_v, meta_stride, group_chunks, sel_mode, idx, nsel, kcap, gidx, gcap,
+                                       resolve_scale(scale, p->head_dim), O, o_stride, (float *)workspace,
+                                       (hipStream_t)stream),
+                    "sas_hssa_decode");
+}
+
 }  // extern "C"

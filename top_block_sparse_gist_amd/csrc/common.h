@@ -244,5 +244,21 @@ size_t decode_workspace_bytes(const sas_problem &p, int32_t sel_mode, int32_t kc
 // per unit against cap)
 bool decode_merge_fits(const sas_problem &p, const SeqTable &st, int32_t sel_mode, int32_t kcap, int32_t gist,
                        int *nwg, int *cap);
+// two-level gist mode (meta-gists): selection and attention
+size_t hssa_select_workspace_bytes(const sas_problem &p, int32_t sel_mode, int32_t M, int32_t k1);
+int hssa_candidates_max(const sas_problem &p, int32_t M, int32_t k1);
+hipError_t launch_hssa_select(const sas_problem &p, const SeqTable &st, const void *Q, const int64_t *qs,
+                              const void *gk, const int64_t *gs, const void *mk, const int64_t *ms, int32_t M,
+                              int32_t sel_mode, int32_t k1, int32_t k2, float scale, int32_t kcap, int32_t gcap,
+                              int32_t *idx, int32_t *nsel, int32_t *gidx, int32_t *gsel, float *work, hipStream_t s);
+bool hssa_merge_fits(const sas_problem &p, const SeqTable &st, int32_t sel_mode, int32_t kcap, int32_t gcap,
+                     int32_t M, int *nwg_out, int *cap_out);
+size_t hssa_decode_workspace_bytes(const sas_problem &p, int32_t sel_mode, int32_t kcap, int32_t gcap, int32_t M);
+hipError_t launch_hssa_decode(const sas_problem &p, const SeqTable &st, const void *Q, const int64_t *qs,
+                              const void *K, const void *V, const int64_t *kvs, const void *gk, const void *gv,
+                              const int64_t *gs, const void *mk, const void *mv, const int64_t *ms, int32_t M,
+                              int32_t sel_mode, const int32_t *idx, const int32_t *nsel, int32_t kcap,
+                              const int32_t *gidx, int32_t gcap, float scale, void *O, const int64_t *os,
+                              float *workspace, hipStream_t s);
 
 }  // namespace sas

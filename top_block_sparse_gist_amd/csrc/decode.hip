@@ -28,18 +28,18 @@
 
 namespace sas {
 
-template <int D, int WPW, int TPW, typename OT>
+template <int D, int WPW, int TPW, typename OT, bool HS>
 __global__ __launch_bounds__(WPW * 64) __attribute__((amdgpu_waves_per_eu(2))) void decode_bf16_kernel(
     SeqTable st, const uint16_t *__restrict__ Q, int64_t qb, int64_t qh, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, int64_t kb, int64_t kh, int64_t kt, const uint16_t *__restrict__ GK,
     const uint16_t *__restrict__ GV, int64_t gb, int64_t gh, int64_t gt, int gist, int blk, int S, int G,
     int per_head, const int32_t *__restrict__ idx, const int32_t *__restrict__ nsel, const float *__restrict__ gate,
     int kcap, float scale_log2, float *__restrict__ work, uint32_t *__restrict__ counters, OT *__restrict__ O,
-    int64_t ob, int64_t oh) {
+    int64_t ob, int64_t oh, MetaArgs ma) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[DecodeLds<D, WPW>::BYTES];
-  decode_tile_body<D, WPW, TPW, OT>(blockIdx.x, blockIdx.y, gridDim.x, lds, st, Q, qb, qh, K, V, kb, kh, kt, GK,
-                                      GV, gb, gh, gt, gist, blk, S, G, per_head, idx, nsel, gate, kcap, scale_log2, work,
-                                      counters, O, ob, oh);
+  decode_tile_body<D, WPW, TPW, OT, HS>(blockIdx.x, blockIdx.y, gridDim.x, lds, st, Q, qb, qh, K, V, kb, kh, kt,
+                                          GK, GV, gb, gh, gt, gist, blk, S, G, per_head, idx, nsel, gate, kcap,
+                                          scale_log2, work, counters, O, ob, oh, ma);
 }
 
 // ---- host side -------------------------------------------------------------------------------
@@ -81,18 +81,18 @@ static int64_t decode_resident_workgroups(int head_dim) {
   return (int64_t)per_cu * n;
 }
 
-template <int D, int WPW, int TPW>
+template <int D, int WPW, int TPW, bool HS>
 static hipError_t decode_launch(const sas_problem &p, const SeqTable &st, const DecodeShape &d, int nwg,
                                 const void *Q, const int64_t *qs, const void *K, const void *V, const int64_t *kvs,
                                 const void *gk, const void *gv, int64_t gb, int64_t gh, int64_t gt, int gist,
                                 int per_head, const int32_t *idx, const int32_t *nsel, const float *gate, int32_t kcap,
-                                float scale_log2,
-                                float *work, uint32_t *counters, void *O, const int64_t *os, hipStream_t s) {
-  hipLaunchKernelGGL((decode_bf16_kernel<D, WPW, TPW, uint16_t>), dim3(nwg, (unsigned)d.units), dim3(WPW * 64), 0, s,
-                     st, (const uint16_t *)Q, qs[0], qs[1], (const uint16_t *)K, (const uint16_t *)V, kvs[0], kvs[1],
-                     kvs[2], (const uint16_t *)gk, (const uint16_t *)gv, gb, gh, gt, gist, p.block, d.S,
+                                float scale_log2, float *work, uint32_t *counters, void *O, const int64_t *os,
+                                const MetaArgs &ma, hipStream_t s) {
+  hipLaunchKernelGGL((decode_bf16_kernel<D, WPW, TPW, uint16_t, HS>), dim3(nwg, (unsigned)d.units), dim3(WPW * 64), 0,
+                     s, st, (const uint16_t *)Q, qs[0], qs[1], (const uint16_t *)K, (const uint16_t *)V, kvs[0],
+                     kvs[1], kvs[2], (const uint16_t *)gk, (const uint16_t *)gv, gb, gh, gt, gist, p.block, d.S,
                      p.hq / p.hkv, per_head, idx, nsel, gate, kcap, scale_log2, work, counters, (uint16_t *)O, os[0],
-                     os[1]);
+                     os[1], ma);
   return hipGetLastError();
 }
 
@@ -118,8 +118,8 @@ hipError_t launch_decode_bf16(const sas_problem &p, const SeqTable &st, const vo
   if (gist) { gb = gs[0]; gh = gs[1]; gt = gs[2]; }
   const float sl2 = scale * 1.4426950408889634f;
 #define SAS_DEC(D_, T_)                                                                                          \
-  return decode_launch<D_, 4, T_>(p, st, d, nwg, Q, qs, K, V, kvs, gk, gv, gb, gh, gt, gist, per_head, idx, nsel, \
-                                  gate, kcap, sl2, work, counters, O, os, s)
+  return decode_launch<D_, 4, T_, false>(p, st, d, nwg, Q, qs, K, V, kvs, gk, gv, gb, gh, gt, gist, per_head, idx, \
+                                         nsel, gate, kcap, sl2, work, counters, O, os, MetaArgs{}, s)
   if (p.head_dim == 128) {
     if (tpw == 3) SAS_DEC(128, 3);
     if (tpw == 2) SAS_DEC(128, 2);
@@ -129,6 +129,66 @@ hipError_t launch_decode_bf16(const sas_problem &p, const SeqTable &st, const vo
   if (tpw == 2) SAS_DEC(64, 2);
   SAS_DEC(64, 1);
 #undef SAS_DEC
+}
+
+// ---- two-level gist mode (meta-gists) ------------------------------------------------------
+// Tiles per unit: gcap opened-group tiles, nmt meta-gist tiles, then kcap raw tiles.
+static DecodeShape hssa_shape(const sas_problem &p, int32_t sel_mode, int32_t kcap, int32_t gcap, int nmt) {
+  DecodeShape d = decode_shape(p, sel_mode, kcap, 0, 0);
+  d.tiles_cap += gcap + nmt;
+  d.nwg_cap = (d.tiles_cap + d.wpw - 1) / d.wpw;
+  return d;
+}
+
+static int hssa_meta_tiles(int maxc, int M) { return (maxc / M + 63) / 64; }
+
+bool hssa_merge_fits(const sas_problem &p, const SeqTable &st, int32_t sel_mode, int32_t kcap, int32_t gcap,
+                     int32_t M, int *nwg_out, int *cap_out) {
+  int maxc = 0;
+  for (int b = 0; b < p.batch; ++b) maxc = max(maxc, (st.len[b] - 1) / p.block);
+  const DecodeShape d = hssa_shape(p, sel_mode, kcap, gcap, hssa_meta_tiles(maxc, M));
+  const int tpw = decode_tiles_per_wave(d, INT64_MAX);
+  *nwg_out = (d.tiles_cap + d.wpw * tpw - 1) / (d.wpw * tpw);
+  *cap_out = decode_merge_capacity(d.nh, p.head_dim, d.wpw);
+  return *nwg_out <= *cap_out;
+}
+
+size_t hssa_decode_workspace_bytes(const sas_problem &p, int32_t sel_mode, int32_t kcap, int32_t gcap, int32_t M) {
+  const DecodeShape d = hssa_shape(p, sel_mode, kcap, gcap, hssa_meta_tiles((p.max_len - 1) / p.block, M));
+  const size_t counters = ((size_t)d.units * 4 + 255) / 256 * 256;
+  return counters + (size_t)d.units * d.nwg_cap * record_floats(d.nh, p.head_dim) * sizeof(float);
+}
+
+hipError_t launch_hssa_decode(const sas_problem &p, const SeqTable &st, const void *Q, const int64_t *qs,
+                              const void *K, const void *V, const int64_t *kvs, const void *gk, const void *gv,
+                              const int64_t *gs, const void *mk, const void *mv, const int64_t *ms, int32_t M,
+                              int32_t sel_mode, const int32_t *idx, const int32_t *nsel, int32_t kcap,
+                              const int32_t *gidx, int32_t gcap, float scale, void *O, const int64_t *os,
+                              float *workspace, hipStream_t s) {
+  const int per_head = sel_mode == SAS_SEL_HEAD;
+  int maxc = 0;
+  for (int b = 0; b < p.batch; ++b) maxc = max(maxc, (st.len[b] - 1) / p.block);
+  const int nmt = hssa_meta_tiles(maxc, M);
+  const DecodeShape d = hssa_shape(p, sel_mode, kcap, gcap, nmt);
+  const int tpw = decode_tiles_per_wave(d, decode_resident_workgroups(p.head_dim));
+  const int nwg = (d.tiles_cap + d.wpw * tpw - 1) / (d.wpw * tpw);
+  uint32_t *counters = reinterpret_cast<uint32_t *>(workspace);
+  const size_t cbytes = ((size_t)d.units * 4 + 255) / 256 * 256;
+  float *work = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + cbytes);
+  const MetaArgs ma{(const uint16_t *)mk, (const uint16_t *)mv, ms[0], ms[1], ms[2], gidx, M, gcap, nmt};
+  const float sl2 = scale * 1.4426950408889634f;
+#define SAS_HDEC(D_, T_)                                                                                           \
+  return decode_launch<D_, 4, T_, true>(p, st, d, nwg, Q, qs, K, V, kvs, gk, gv, gs[0], gs[1], gs[2], 0, per_head, \
+                                        idx, nsel, nullptr, kcap, sl2, work, counters, O, os, ma, s)
+  if (p.head_dim == 128) {
+    if (tpw == 3) SAS_HDEC(128, 3);
+    if (tpw == 2) SAS_HDEC(128, 2);
+    SAS_HDEC(128, 1);
+  }
+  if (tpw == 3) SAS_HDEC(64, 3);
+  if (tpw == 2) SAS_HDEC(64, 2);
+  SAS_HDEC(64, 1);
+#undef SAS_HDEC
 }
 
 }  // namespace sas

@@ -449,6 +449,17 @@ struct DecodeLds {
   static constexpr int BYTES = TILE_BYTES + SMALL_FLOATS * 4;
 };
 
+// Two-level gist mode (meta-gists): the extra inputs of the attention.  Tiles of a unit: one per
+// opened-group entry (that group's gists, the expanded chunks masked), then nmt tiles of 64
+// meta-gists (the opened groups masked), then the raw tiles of the expanded chunks and the current
+// chunk.  All ranges are known before nsel, so every list entry loads beside it.
+struct MetaArgs {
+  const uint16_t *MK, *MV;
+  int64_t mb, mh, mt;   // strides of the meta-gist K/V [B, Hkv, NM, d]
+  const int32_t *gidx;  // [units, gcap] opened groups, ascending, the trailing group last, -1 padded
+  int M, gcap, nmt;     // chunks per group; list capacity; meta tiles per unit (grid-wide)
+};
+
 // One attention workgroup: tiles bx*WPW*TPW .. +WPW*TPW-1 of unit u (TPW = 1 to 3 per wave: wave w
 // takes tiles w, w + WPW, ... of the workgroup's range, each next tile's K/V loads issued as soon
 // as the previous one's registers are consumed, so they overlap its softmax and PV), merged into the
@@ -456,7 +467,7 @@ struct DecodeLds {
 // past them is -1), so it needs only the first nwg_u of the nwg workgroups: the others exit
 // before touching the records, and the last of the nwg_u to arrive merges their records and
 // writes O.
-template <int D, int WPW, int TPW, typename OT>
+template <int D, int WPW, int TPW, typename OT, bool HS = false>
 __device__ __forceinline__ void decode_tile_body(
     int bx, int64_t u, int nwg, unsigned char *lds, SeqTable st, const uint16_t *__restrict__ Q, int64_t qb,
     int64_t qh, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, int64_t kb, int64_t kh, int64_t kt,
@@ -464,7 +475,7 @@ __device__ __forceinline__ void decode_tile_body(
     int blk, int S, int G, int per_head, const int32_t *__restrict__ idx, const int32_t *__restrict__ nsel,
     const float *__restrict__ gate, int kcap,
     float scale_log2, float *__restrict__ work, uint32_t *__restrict__ counters, OT *__restrict__ O, int64_t ob,
-    int64_t oh) {
+    int64_t oh, MetaArgs ma = MetaArgs{}) {
   constexpr int NKK = D / 32;   // MFMA k-steps over the head dim
   constexpr int NDT = D / 16;   // 16-dim output tiles
   constexpr int VROW = D + VPAD;
@@ -490,17 +501,23 @@ __device__ __forceinline__ void decode_tile_body(
   // wait for one load only
   int tt[TPW], jraw[TPW];
   float graw[TPW];
+  const int r0 = HS ? ma.gcap + ma.nmt : 0;  // first raw tile
 #pragma unroll
   for (int k = 0; k < TPW; ++k) {
     tt[k] = bx * WPW * TPW + k * WPW + wave;
-    const int e = tt[k] / tpb;
+    if (HS && tt[k] < ma.gcap) {
+      jraw[k] = ma.gidx[u * ma.gcap + tt[k]];  // an opened group
+      graw[k] = 0.f;
+      continue;
+    }
+    const int e = tt[k] >= r0 ? (tt[k] - r0) / tpb : kcap;  // meta tiles have no entry
     jraw[k] = e < kcap ? idx[u * kcap + e] : -1;
     graw[k] = (gate && e < kcap) ? gate[u * kcap + e] : 0.f;
   }
   // this unit's tiles: the raw tiles of its list entries, then (gist mode) one tile per 64 gists
   const int nent = min(max(nsel[u], 0), kcap);
   const int nraw = nent * tpb;
-  const int nwg_u = max(1, (nraw + (gist ? (c + 63) / 64 : 0) + WPW * TPW - 1) / (WPW * TPW));
+  const int nwg_u = max(1, (r0 + nraw + (gist ? (c + 63) / 64 : 0) + WPW * TPW - 1) / (WPW * TPW));
   if (bx >= nwg_u) return;
   const int64_t rec_sz = record_floats(nh, D);
 
@@ -512,10 +529,50 @@ __device__ __forceinline__ void decode_tile_body(
     float gl2;
     uint64_t excl;
   };
+  // bits of the 64 keys from key0 on that a list names (an entry j sets bit j - key0)
+  auto list_bits = [&](const int32_t *list, int n, int key0) {
+    uint64_t bits = 0;
+    for (int e0 = 0; e0 < n; e0 += 64) {
+      uint64_t bit = 0;
+      if (e0 + lane < n) {
+        const int j = list[e0 + lane];
+        if (j >= key0 && j < key0 + 64) bit = 1ull << (j - key0);
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)bit, o, 64);
+        const uint32_t hi = __shfl_xor((uint32_t)(bit >> 32), o, 64);
+        bit |= ((uint64_t)hi << 32) | lo;
+      }
+      bits |= bit;
+    }
+    return bits;
+  };
   auto describe = [&](int k) {
     Tile d{nullptr, nullptr, 0, 0, 0, 0.f, 0ull};
-    const int tk = tt[k];
-    if (tk < nraw) {
+    const int tk = tt[k] - r0;  // raw tiles count from r0
+    if (HS && tk < 0) {
+      if (tt[k] < ma.gcap) {
+        // gists of an opened group (the trailing group may hold none); expanded chunks masked
+        const int gi = jraw[k];
+        if (gi >= 0) {
+          d.key0 = gi * ma.M;
+          d.nvalid = min(ma.M, c - d.key0);
+          d.kbase = GK + b * gb + g * gh;
+          d.vbase = GV + b * gb + g * gh;
+          d.rstride = gt;
+          if (d.nvalid > 0) d.excl = list_bits(idx + u * kcap, kcap, d.key0);
+        }
+      } else {
+        // 64 meta-gists of the complete groups; the opened ones masked
+        d.key0 = (tt[k] - ma.gcap) * 64;
+        d.nvalid = min(64, c / ma.M - d.key0);
+        d.kbase = ma.MK + b * ma.mb + g * ma.mh;
+        d.vbase = ma.MV + b * ma.mb + g * ma.mh;
+        d.rstride = ma.mt;
+        if (d.nvalid > 0) d.excl = list_bits(ma.gidx + u * ma.gcap, ma.gcap, d.key0);
+      }
+    } else if (tk < nraw) {
       const int j = jraw[k];
       if (j >= 0) {
         d.key0 = j * blk + (tk % tpb) * 64;
@@ -531,23 +588,8 @@ __device__ __forceinline__ void decode_tile_body(
       d.kbase = GK + b * gb + g * gh;
       d.vbase = GV + b * gb + g * gh;
       d.rstride = gt;
-      if (d.nvalid > 0) {
-        // gists of selected chunks are replaced by their raw tokens: exclude them
-        for (int e0 = 0; e0 < kcap; e0 += 64) {
-          uint64_t bit = 0;
-          if (e0 + lane < kcap) {
-            const int j = idx[u * kcap + e0 + lane];
-            if (j >= d.key0 && j < d.key0 + 64) bit = 1ull << (j - d.key0);
-          }
-#pragma unroll
-          for (int o = 32; o >= 1; o >>= 1) {
-            const uint32_t lo = __shfl_xor((uint32_t)bit, o, 64);
-            const uint32_t hi = __shfl_xor((uint32_t)(bit >> 32), o, 64);
-            bit |= ((uint64_t)hi << 32) | lo;
-          }
-          d.excl |= bit;
-        }
-      }
+      // gists of selected chunks are replaced by their raw tokens: exclude them
+      if (d.nvalid > 0) d.excl = list_bits(idx + u * kcap, kcap, d.key0);
     }
     d.nvalid = max(d.nvalid, 0);
     return d;
