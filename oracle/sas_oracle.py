@@ -165,6 +165,26 @@ def budget_k(c: int, n_cand: int, k_fixed: int, frac_num: int, frac_den: int, co
     return max(0, min(n_cand, k))
 
 
+def coverage_k(scores: Sequence[float], c: int, sink: bool, tau: float) -> int:
+    """Coverage budget ([SF] 2.3, threshold-based allocation: keep units until a share of the
+    attention mass is covered).  Reading: the candidates' mass is the softmax of their selector
+    scores; the budget is the smallest k such that the first k candidates in (score descending,
+    index ascending) order hold a share >= tau of it (forced blocks are not candidates and do not
+    count).  0 when there is no candidate.
+    """
+    forced = {c}
+    if sink:
+        forced.add(0)
+    cand = [j for j in range(c) if j not in forced]
+    if not cand:
+        return 0
+    ranked = sorted(cand, key=lambda j: (-float(scores[j]), j))
+    s = np.array([float(scores[j]) for j in ranked], dtype=np.float64)
+    e = np.exp(s - s.max())
+    cum = np.cumsum(e)
+    return int(np.searchsorted(cum, tau * cum[-1], side="left")) + 1
+
+
 def topk_blocks(scores: Sequence[float], c: int, k: int, sink: bool) -> List[int]:
     """Selected block set of a unit, ascending.
 
@@ -272,6 +292,7 @@ def run_sequence(Qb: np.ndarray, Kb: np.ndarray, Vb: np.ndarray, L: int, q_start
                  sel_mode: str, k_fixed: int = 0, frac_num: int = 0, frac_den: int = 0,
                  count_current: int = 0, sink: bool = False, gate: bool = False,
                  scale: Optional[float] = None, gist_k: Optional[np.ndarray] = None,
+                 coverage: float = 0.0,
                  gist_v: Optional[np.ndarray] = None, mode: str = "skip",
                  unit_filter=None, attend: bool = True, reps: Optional[np.ndarray] = None,
                  explicit: Optional[Dict[Tuple[int, int], Tuple[List[int], Optional[Dict[int, float]]]]] = None
@@ -314,7 +335,13 @@ def run_sequence(Qb: np.ndarray, Kb: np.ndarray, Vb: np.ndarray, L: int, q_start
             s = unit_scores(qv, reps[g], u.c + 1, scale)
         u.scores = s
         n_cand = u.c - (1 if (sink and u.c > 0) else 0)
-        u.k = budget_k(u.c, n_cand, k_fixed, frac_num, frac_den, count_current)
+        if coverage > 0.0:
+            # coverage budget, capped by the fixed or fractional rule when one is given
+            kc = coverage_k(s, u.c, sink and u.c > 0, coverage)
+            capped = k_fixed > 0 or frac_den > 0
+            u.k = min(kc, budget_k(u.c, n_cand, k_fixed, frac_num, frac_den, count_current)) if capped else kc
+        else:
+            u.k = budget_k(u.c, n_cand, k_fixed, frac_num, frac_den, count_current)
         u.sel = topk_blocks(s, u.c, u.k, sink)
         u.gate = gate_values(s, u.sel) if gate else None
         sel, gv = u.sel, u.gate

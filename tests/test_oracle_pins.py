@@ -398,3 +398,47 @@ def test_hssa_selection_invariants_and_key_set():
         kk, vv, mask = np.array(keys), np.array(vals), np.array(add)[None, :]
         for h in range(hq):
             np.testing.assert_allclose(O[h], _sdpa(Q[h], kk, vv, mask), rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------------------------ coverage budget
+def test_coverage_budget_closed_form():
+    """Scores log p with p = (1/2, 1/4, 1/8, 1/16, 1/16): the top-k shares are 1/2, 3/4, 7/8, 15/16, 1."""
+    p = np.array([0.0625, 0.5, 0.125, 0.25, 0.0625])           # blocks 0..4, current block 5
+    s = list(np.log(p)) + [0.0]
+    for tau, k in [(0.3, 1), (0.5 - 1e-9, 1), (0.74, 2), (0.76, 3), (0.9, 4), (0.95, 5), (1.0 - 1e-12, 5)]:
+        assert o.coverage_k(s, 5, False, tau) == k, tau
+    # with the sink, block 0 is forced and leaves the candidates: shares over blocks 1..4
+    assert o.coverage_k(s, 5, True, 0.5) == 1          # 0.5 / 0.9375 = 0.53
+    assert o.coverage_k(s, 5, True, 0.93) == 3         # (0.5 + 0.25 + 0.125) / 0.9375 = 0.933
+    assert o.coverage_k(s, 0, False, 0.5) == 0          # no candidate
+
+
+def test_coverage_budget_brute_force_with_ties():
+    """The coverage budget is the smallest size of any candidate subset holding a share >= tau
+    (enumerated), and the list is the top set of that size under the lower-index tie rule."""
+    rng = np.random.default_rng(41)
+    for trial in range(60):
+        c = int(rng.integers(1, 9))
+        s = list(rng.integers(-3, 3, size=c).astype(float) * 0.5) + [0.0]
+        tau = float(rng.uniform(0.05, 1.0))
+        e = np.exp(np.array(s[:c]) - max(s[:c]))
+        best = min(len(sub) for r in range(1, c + 1) for sub in itertools.combinations(range(c), r)
+                   if e[list(sub)].sum() >= tau * e.sum() * (1 - 1e-12))
+        k = o.coverage_k(s, c, False, tau)
+        assert k == best, (s, tau, k, best)
+        assert o.topk_blocks(s, c, k, False)[:-1] == sorted(sorted(range(c), key=lambda j: (-s[j], j))[:k])
+
+
+def test_coverage_budget_in_a_sequence():
+    """run_sequence with a coverage budget: each unit keeps the covering top set, capped by the
+    fixed budget when one is given; tau -> 1 keeps every candidate."""
+    rng = np.random.default_rng(42)
+    hq, hkv, d, blk, L = 4, 2, 8, 4, 4 * 13 + 1
+    Q = rng.standard_normal((hq, 1, d)); K = rng.standard_normal((hkv, L, d)); V = rng.standard_normal((hkv, L, d))
+    r = o.run_sequence(Q, K, V, L, L - 1, blk, "group", coverage=0.6, sink=True, attend=False)
+    for un in r.units:
+        assert un.k == o.coverage_k(un.scores, un.c, True, 0.6) and len(un.sel) == un.k + 2
+    r = o.run_sequence(Q, K, V, L, L - 1, blk, "group", coverage=0.6, k_fixed=2, sink=True, attend=False)
+    assert all(un.k == min(2, o.coverage_k(un.scores, un.c, True, 0.6)) for un in r.units)
+    r = o.run_sequence(Q, K, V, L, L - 1, blk, "group", coverage=1.0, attend=False)
+    assert all(un.k == un.c for un in r.units)
