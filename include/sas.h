@@ -81,12 +81,19 @@ typedef struct sas_problem {
  *   k = k_fixed                                            if frac_den == 0
  *   k = ceil(frac_num * (c + count_current) / frac_den)    otherwise (integer arithmetic)
  *   k is capped at the candidate count; the current block c is always added ([SAS] core
- *   insight), and block 0 when force_sink ([SF] 2.2.3, first prefix block). */
+ *   insight), and block 0 when force_sink ([SF] 2.2.3, first prefix block).
+ * Coverage budget ([SF] 2.3, threshold-based allocation), when coverage > 0: k is the
+ *   smallest number of candidates, in (score descending, index ascending) order, whose share of
+ *   the candidates' softmax mass (softmax of their scores) is >= coverage (<= 1), capped by the
+ *   rule above only when k_fixed > 0 or frac_den > 0.  The shares are summed in fp32: where the
+ *   exact share of the k-th candidate lies within ~1e-5 of coverage, k may differ by one from
+ *   an exact evaluation. */
 typedef struct sas_budget {
   int32_t k_fixed;
   int32_t frac_num, frac_den, count_current;
   int32_t force_sink;       /* 1: block 0 is always kept                                    */
   int32_t gate;             /* 1: write the log-gate over the selected set                  */
+  float coverage;           /* 0: off; else in (0, 1]                                        */
 } sas_budget;
 
 /* Number of query blocks tq consecutive positions can touch: ceil((tq-1)/blk) + 1. */

@@ -72,6 +72,45 @@ def list_matches(oracle_sel: List[int], gpu_sel: List[int], scores: np.ndarray, 
     return True, True, ""
 
 
+COVERAGE_REL = 1e-5
+
+
+def coverage_length_ok(scores: np.ndarray, c: int, sink: bool, tau: float, k: int) -> bool:
+    """A coverage budget summed in fp32 may stop one candidate early or late where the exact share
+    of that candidate lies within COVERAGE_REL of tau: k is accepted when the exact share of the
+    top k reaches tau (within the band) and that of the top k - 1 does not (within the band)."""
+    forced = {c} | ({0} if (sink and c > 0) else set())
+    cand = [j for j in range(c) if j not in forced]
+    ranked = sorted(cand, key=lambda j: (-float(scores[j]), j))
+    sv = np.array([float(scores[j]) for j in ranked])
+    e = np.exp(sv - sv.max())
+    cum = np.cumsum(e) / e.sum()
+    if k < 1 or k > len(cum):
+        return False
+    reach = cum[k - 1] >= tau * (1 - COVERAGE_REL)
+    short = k == 1 or cum[k - 2] < tau * (1 + COVERAGE_REL)
+    return bool(reach and short)
+
+
+def selection_matches(un, gsel: List[int], scores: np.ndarray, budget) -> Tuple[bool, bool, str]:
+    """list_matches, plus (coverage budgets) a list one entry longer or shorter than the oracle's
+    when the coverage band allows that length; such a list counts as inside the tie band."""
+    if budget.coverage <= 0:
+        return list_matches(un.sel, gsel, scores, un.c, un.k, budget.sink)
+    nforced = 1 + (1 if (budget.sink and un.c > 0) else 0)
+    k_gpu = len(gsel) - nforced
+    if k_gpu == un.k:
+        return list_matches(un.sel, gsel, scores, un.c, un.k, budget.sink)
+    capped = budget.k_fixed > 0 or budget.frac_den > 0
+    if capped and k_gpu > un.k:
+        return False, False, f"{k_gpu} kept above the cap's {un.k}"
+    if not coverage_length_ok(scores, un.c, budget.sink, budget.coverage, k_gpu):
+        return False, False, f"coverage keeps {k_gpu} blocks, the oracle {un.k}, outside the band"
+    exp = orc.topk_blocks(scores, un.c, k_gpu, budget.sink)
+    ok, _, why = list_matches(exp, gsel, scores, un.c, k_gpu, budget.sink)
+    return ok, True, why
+
+
 def out_check(rep: Report, gpu: np.ndarray, ref: np.ndarray, bf16: bool) -> None:
     d = np.abs(gpu.astype(np.float64) - ref)
     assert np.isfinite(gpu).all(), "non-finite GPU output"
@@ -94,7 +133,8 @@ def sel_count(w: Workload) -> int:
 
 def budget_of(w: Workload) -> sas.Budget:
     return sas.Budget(k_fixed=w.k_fixed, frac_num=w.frac_num, frac_den=w.frac_den,
-                      count_current=w.count_current, sink=w.sink, gate=w.gate)
+                      count_current=w.count_current, sink=w.sink, gate=w.gate,
+                      coverage=float(w.spec.get("coverage", 0.0)))
 
 
 def run_case(w: Workload, seqs: List[int], unit_sample: Optional[int] = None, seed: int = 0,
@@ -125,7 +165,15 @@ def run_case(w: Workload, seqs: List[int], unit_sample: Optional[int] = None, se
                               gist=gist)
     idx, nsel, gate = sas.topk_select(scores, lens, w.block, w.hq, w.hkv, w.d, dtype_code, Lmax, budget, tq=tq,
                                       q_start=inp.q_start, sel_mode=w.sel)
-    if decode and max((L - 1) // w.block for L in lens) <= 2048:
+    fused = None
+    if decode and max((L - 1) // w.block for L in lens) <= 2048 and budget.coverage > 0:
+        # coverage budgets sum fp32 shares in each path's own order: both lists are checked against
+        # the oracle below (a length may differ by one inside the coverage band)
+        _, i2, n2, _ = sas.select_decode(inp.Q, reps, lens, w.block, w.hkv, Lmax, budget, sel_mode=w.sel,
+                                         gist=gist, kcap=idx.shape[1])
+        torch.cuda.synchronize()
+        fused = (i2.cpu().numpy(), n2.cpu().numpy())
+    elif decode and max((L - 1) // w.block for L in lens) <= 2048:
         # the fused decode selection must give the same scores, lists and gates as the two calls
         s2, i2, n2, g2 = sas.select_decode(inp.Q, reps, lens, w.block, w.hkv, Lmax, budget, sel_mode=w.sel,
                                            gist=gist, kcap=idx.shape[1])
@@ -170,7 +218,7 @@ def run_case(w: Workload, seqs: List[int], unit_sample: Optional[int] = None, se
         r = orc.run_sequence(Qb, hst["k"], hst["v"], L, q0, w.block, w.sel, k_fixed=budget.k_fixed,
                              frac_num=budget.frac_num, frac_den=budget.frac_den,
                              count_current=budget.count_current, sink=budget.sink, gate=budget.gate,
-                             gist_k=gk, gist_v=gv, unit_filter=filt, attend=False)
+                             gist_k=gk, gist_v=gv, unit_filter=filt, attend=False, coverage=budget.coverage)
         if not gist:
             nb = orc.num_blocks(L, w.block)
             dr = np.abs(reps_h[bi, :, :nb] - r.reps)
@@ -194,8 +242,12 @@ def run_case(w: Workload, seqs: List[int], unit_sample: Optional[int] = None, se
             n = int(nsel_h[u])
             gsel = [int(x) for x in idx_h[u, :n]]
             assert all(int(x) == -1 for x in idx_h[u, n:]), f"unit {u}: padding is not -1"
-            ok, tie, why = list_matches(un.sel, gsel, s_or, un.c, un.k, budget.sink)
+            ok, tie, why = selection_matches(un, gsel, s_or, budget)
             assert ok, f"unit {u} (head {un.sel_head}, block {un.c}): {why}"
+            if fused is not None:
+                fs = [int(x) for x in fused[0][u, :fused[1][u]]]
+                ok2, _, why2 = selection_matches(un, fs, s_or, budget)
+                assert ok2, f"unit {u} (head {un.sel_head}, block {un.c}), fused selection: {why2}"
             rep.units += 1
             if tie:
                 rep.tie_band_units += 1
@@ -210,7 +262,8 @@ def run_case(w: Workload, seqs: List[int], unit_sample: Optional[int] = None, se
         r2 = orc.run_sequence(Qb, hst["k"], hst["v"], L, q0, w.block, w.sel, k_fixed=budget.k_fixed,
                               frac_num=budget.frac_num, frac_den=budget.frac_den,
                               count_current=budget.count_current, sink=budget.sink, gate=budget.gate,
-                              gist_k=gk, gist_v=gv, unit_filter=filt, reps=r.reps, explicit=explicit)
+                              gist_k=gk, gist_v=gv, unit_filter=filt, reps=r.reps, explicit=explicit,
+                              coverage=budget.coverage)
         mask = ~np.isnan(r2.O[:, :, 0])
         gpu_rows = O_h[bi] if not decode else O_h[bi][:, None, :]
         out_check(rep, gpu_rows[mask], r2.O[mask], bf16)

@@ -349,3 +349,33 @@ def test_decode_loop_incremental_reps():
             err_n += diff.size
         assert err_sum / err_n <= BF16_MEAN_ABS
         say(f"[loop] step {step}: lengths {lens}, reps equal a full pass, lists and outputs match")
+
+
+# ------------------------------------------------------------------------------ coverage budgets
+def test_coverage_budget_decode_group():
+    """Uncapped coverage on per-group decode units (fused and two-call selection, one wave and the
+    four-wave top-k), then capped with sink and gate."""
+    w = Workload(2, overrides=dict(tag="cov", seq_lens=[3000, 5000, 8000, 1500, 40000, 33000], batch=6, hq=8,
+                                   hkv=2, k_fixed=0, coverage=0.5, seq_len=None))
+    run_case(w, list(range(6)))
+    w2 = Workload(2, overrides=dict(tag="covcap", seq_lens=[3000, 9000, 700], batch=3, hq=8, hkv=2, k_fixed=6,
+                                    coverage=0.3, sink=True, gate=True, seq_len=None))
+    run_case(w2, list(range(3)))
+
+
+def test_coverage_budget_decode_per_head_and_gist():
+    w = Workload(2, overrides=dict(tag="covh", seq_lens=[20000, 6000], batch=2, sel="head", hq=8, hkv=2,
+                                   k_fixed=0, coverage=0.25, gate=True, seq_len=None))
+    run_case(w, [0, 1])
+    wg = Workload(4, overrides=dict(tag="covg", seq_len=9000, batch=2, hq=8, hkv=2, k_fixed=0, coverage=0.4))
+    run_case(wg, [0, 1])
+
+
+def test_coverage_budget_prefill():
+    """Per-group and per-head prefill units through the two-call top-k."""
+    w = Workload(3, overrides=dict(tag="cov", seq_len=3000, tq=1000, hq=8, hkv=2, frac_num=0, frac_den=0,
+                                   k_fixed=0, coverage=0.35, sink=True, gate=True))
+    run_case(w, [0])
+    wh = Workload(3, overrides=dict(tag="covh", seq_len=2500, tq=600, hq=4, hkv=2, block=64, sel="head",
+                                    frac_num=0, frac_den=0, k_fixed=5, coverage=0.6, gate=True))
+    run_case(wh, [0])

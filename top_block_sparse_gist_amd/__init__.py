@@ -30,17 +30,20 @@ def _torch():
 
 @dataclass
 class Budget:
-    """k = k_fixed, or ceil(frac_num * (c + count_current) / frac_den) when frac_den > 0."""
+    """k = k_fixed, or ceil(frac_num * (c + count_current) / frac_den) when frac_den > 0; with
+    coverage > 0, the smallest k whose top candidates hold that share of the softmax mass (capped
+    by the rule when k_fixed or frac_den is set)."""
     k_fixed: int = 0
     frac_num: int = 0
     frac_den: int = 0
     count_current: int = 0
     sink: bool = False
     gate: bool = False
+    coverage: float = 0.0
 
     def c_struct(self) -> _lib.Budget:
         return _lib.Budget(self.k_fixed, self.frac_num, self.frac_den, self.count_current,
-                           int(bool(self.sink)), int(bool(self.gate)))
+                           int(bool(self.sink)), int(bool(self.gate)), float(self.coverage))
 
 
 def sel_code(sel_mode) -> int:

@@ -95,13 +95,15 @@ sas_status check_budget(const sas_budget *bg) {
     return fail(SAS_ERR_SHAPE, "budget fields must be >= 0");
   if (bg->count_current != 0 && bg->count_current != 1)
     return fail(SAS_ERR_SHAPE, "count_current must be 0 or 1");
+  if (!(bg->coverage >= 0.f && bg->coverage <= 1.f)) return fail(SAS_ERR_SHAPE, "coverage must be in [0, 1]");
   return SAS_OK;
 }
 
 float resolve_scale(float scale, int d) { return scale == 0.f ? 1.f / sqrtf((float)d) : scale; }
 
 int32_t required_kcap(const sas_problem *p, int32_t tq, const int32_t *q_start, const sas_budget *bg) {
-  Budget b{bg->k_fixed, bg->frac_num, bg->frac_den, bg->count_current, bg->force_sink ? 1 : 0, bg->gate};
+  Budget b{bg->k_fixed, bg->frac_num, bg->frac_den, bg->count_current, bg->force_sink ? 1 : 0, bg->gate,
+           bg->coverage};
   int32_t need = 1;
   for (int s = 0; s < p->batch; ++s) {
     const int L = p->seq_lens[s];
@@ -231,7 +233,7 @@ sas_status sas_topk_select(const sas_problem *p, const float *scores, int64_t sc
   const int32_t need = required_kcap(p, tq, q_start, budget);
   if (kcap < need) return fail(SAS_ERR_SHAPE, "kcap %d < %d selected blocks", kcap, need);
   Budget bg{budget->k_fixed, budget->frac_num, budget->frac_den, budget->count_current,
-            budget->force_sink ? 1 : 0, budget->gate ? 1 : 0};
+            budget->force_sink ? 1 : 0, budget->gate ? 1 : 0, budget->coverage};
   return hip_status(launch_topk(*p, tab, scores, scores_ld, tq, sel_mode, bg, kcap, idx, nsel,
                                 budget->gate ? gate : nullptr, (hipStream_t)stream),
                     "sas_topk_select");
@@ -311,7 +313,7 @@ sas_status sas_select_decode(const sas_problem *p, const void *Q, const int64_t 
     return fail(SAS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", wneed, workspace_bytes);
   if (!aligned16(workspace)) return fail(SAS_ERR_SHAPE, "workspace must be 16-byte aligned");
   Budget bg{budget->k_fixed, budget->frac_num, budget->frac_den, budget->count_current,
-            budget->force_sink ? 1 : 0, budget->gate ? 1 : 0};
+            budget->force_sink ? 1 : 0, budget->gate ? 1 : 0, budget->coverage};
   const int64_t qs3[3] = {q_stride[0], q_stride[1], 0};
   return hip_status(launch_select_decode(*p, tab, Q, qs3, reps, reps_kind, rep_stride, sel_mode,
                                          resolve_scale(scale, p->head_dim), scores, scores_ld, bg, kcap, idx, nsel,

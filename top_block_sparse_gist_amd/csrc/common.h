@@ -18,6 +18,7 @@ struct SeqTable {
 
 struct Budget {
   int32_t k_fixed, frac_num, frac_den, count_current, sink, gate;
+  float coverage;  // 0: off (see coverage_k in the top-k bodies)
 };
 
 // ---------------------------------------------------------------------------------------
@@ -34,7 +35,9 @@ __host__ __device__ inline int32_t num_qblocks(int32_t tq, int32_t blk) {
 // Number of top-k blocks for a unit with current block c and n_cand candidates.
 __host__ __device__ inline int32_t budget_k(const Budget &bg, int32_t c, int32_t n_cand) {
   int32_t k;
-  if (bg.frac_den == 0) {
+  if (bg.coverage > 0.f && bg.k_fixed <= 0 && bg.frac_den == 0) {
+    k = n_cand;  // an uncapped coverage budget may keep every candidate
+  } else if (bg.frac_den == 0) {
     k = bg.k_fixed;
   } else {
     int64_t num = (int64_t)bg.frac_num * (int64_t)(c + bg.count_current);

@@ -89,10 +89,60 @@ struct GroupTeam {
   __device__ uint32_t before(uint32_t v) const { return combine(v, [](uint32_t x, uint32_t) { return x; }, true); }
 };
 
+// Coverage budget: the smallest number of candidates, in (key descending, block ascending) order,
+// whose share of the candidates' softmax mass is >= cov.  The largest key T with mass(>= T) >= cov
+// times the total is found by bisection over the key range (mass at the smallest key is the total,
+// summed in the same order); the holders of keys above T are all taken, then holders of T, one
+// share each, until the share is reached -- as an exact ranking takes tied candidates in block
+// order.  Shares are fp32 (2^x by v_exp_f32).
+template <int NPL, typename Team>
+__device__ uint32_t coverage_count(const uint32_t (&key)[NPL], float cov, const Team &team) {
+  constexpr float L2E = 1.4426950408889634f;
+  float smax = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < NPL; ++r)
+    if (key[r]) smax = fmaxf(smax, order_key_float(key[r]));
+  smax = team.fmax(wave_max(smax));
+  // a candidate's share is recomputed at each use rather than held: the keys already take NPL
+  // registers per lane
+  auto mass = [&](uint32_t t) {
+    float m = 0.f;
+#pragma unroll
+    for (int r = 0; r < NPL; ++r)
+      m += (key[r] && key[r] >= t) ? __builtin_amdgcn_exp2f((order_key_float(key[r]) - smax) * L2E) : 0.f;
+    return team.fsum(wave_sum(m));
+  };
+  auto count = [&](uint32_t t) { return team.sum(count_ge(key, t)); };
+  uint32_t kmin = ~0u, kmax = 0u;  // over key - 1: a non-candidate's 0 wraps to the top
+#pragma unroll
+  for (int r = 0; r < NPL; ++r) {
+    kmin = min(kmin, key[r] - 1u);
+    kmax = max(kmax, key[r]);
+  }
+  kmin = team.min(wave_reduce_u32(kmin, [](uint32_t x, uint32_t y) { return min(x, y); })) + 1u;
+  kmax = team.max(wave_reduce_u32(kmax, [](uint32_t x, uint32_t y) { return max(x, y); }));
+  const float target = cov * mass(kmin);  // the total: every candidate's key is >= kmin
+  uint64_t lo = kmin, hi = (uint64_t)kmax + 1u;  // mass(lo) >= target > 0 = mass(hi)
+  while (hi - lo > 1u) {
+    const uint64_t mid = lo + (hi - lo) / 2u;
+    if (mass((uint32_t)mid) >= target) lo = mid;
+    else hi = mid;
+  }
+  const uint32_t T = (uint32_t)lo;
+  const bool top = T == 0xFFFFFFFFu;
+  const float m_gt = top ? 0.f : mass(T + 1u);
+  const uint32_t n_gt = top ? 0u : count(T + 1u);
+  const uint32_t n_eq = count(T) - n_gt;
+  const float e_t = __builtin_amdgcn_exp2f((order_key_float(T) - smax) * L2E);
+  uint32_t take = 1u;
+  while (take < n_eq && m_gt + (float)take * e_t < target) ++take;
+  return n_gt + take;
+}
+
 // Top-k of one unit's scores row[0..c] by a team of waves: wave w of the team holds blocks
 // 64 * NPL * w + lane + 64r in its register r (the scores are read back from memory, where the
 // unit's tiles left them).  Ties go to the lower block.
-template <int NPL, typename Team>
+template <int NPL, typename Team, bool COV = false>
 __device__ void team_topk(const float *__restrict__ row, int c, bool sinkf, const Budget &bg, int kcap,
                           int32_t *__restrict__ out, int32_t *__restrict__ nsel_out, float *__restrict__ gout,
                           const Team &team) {
@@ -105,7 +155,7 @@ __device__ void team_topk(const float *__restrict__ row, int c, bool sinkf, cons
   const bool sink = sinkf && c > 0;
   const int lo = sink ? 1 : 0;
   const int ncand = c - lo;
-  const int k = budget_k(bg, c, ncand);
+  int k = budget_k(bg, c, ncand);
   const int base = sink ? 1 : 0;
   // order-preserving keys of the candidates, 0 elsewhere: a candidate's key is never 0 (that is
   // the key of one NaN pattern only, and NaN scores are not ranked)
@@ -120,6 +170,9 @@ __device__ void team_topk(const float *__restrict__ row, int c, bool sinkf, cons
   const float s_c = load_dev(row + c);
   const float s_0 = load_dev(row);
   auto count = [&](uint32_t t) { return team.sum(count_ge(key, t)); };
+  if constexpr (COV) {  // compiled only into the launches that carry a coverage budget
+    if (bg.coverage > 0.f && k > 0) k = min(k, (int)coverage_count(key, bg.coverage, team));
+  }
   // The kept candidates: all keys > T, then the `want` lowest blocks with key == T (ties: only
   // when T is the exact k-th largest key and more keys share it).
   uint32_t T = 0u, want = 0u;
@@ -298,7 +351,7 @@ __host__ __device__ inline int select_tiles(int c, int gist) { return gist ? max
 
 // One selection workgroup: the 64-block tile bx of (sequence b, KV head g), hkv KV heads.  The last
 // tile of (b, g) to arrive runs the top-k of its units.
-template <typename T, typename R, int D, int NPL>
+template <typename T, typename R, int D, int NPL, bool COV>
 __device__ __forceinline__ void select_tile_body(
     int bx, int g, int b, int hkv, unsigned char *lds, SeqTable st, const T *__restrict__ Q, int64_t qb, int64_t qh,
     const R *__restrict__ reps, int64_t rb, int64_t rh, int64_t rj, int gist, int blk, int S, int G, int per_head,
@@ -420,13 +473,13 @@ __device__ __forceinline__ void select_tile_body(
     // combining their counts through LDS (the pooled queries' region, no longer read)
     const int64_t urow = (int64_t)b * S + (per_head ? g * G : g);
     const GroupTeam team{reinterpret_cast<uint32_t *>(lds + Lds::QS), wave, 0};
-    team_topk<NPL / 4>(scores + urow * ld, c, bg.sink != 0, bg, kcap, idx + urow * kcap, nsel + urow,
+    team_topk<NPL / 4, GroupTeam, COV>(scores + urow * ld, c, bg.sink != 0, bg, kcap, idx + urow * kcap, nsel + urow,
                        bg.gate ? gate + urow * kcap : nullptr, team);
   } else {
     for (int u = wave; u < nU; u += 4) {
       const int s = per_head ? g * G + u : g;
       const int64_t urow = (int64_t)b * S + s;
-      team_topk<NPL>(scores + urow * ld, c, bg.sink != 0, bg, kcap, idx + urow * kcap, nsel + urow,
+      team_topk<NPL, SoloTeam, COV>(scores + urow * ld, c, bg.sink != 0, bg, kcap, idx + urow * kcap, nsel + urow,
                      bg.gate ? gate + urow * kcap : nullptr, SoloTeam{});
     }
   }

@@ -31,7 +31,7 @@ struct SelGrid {
 
 // At most 128 VGPRs (4 workgroups per CU): the top-k's 32 registers per lane of keys would
 // otherwise set the register count, and the occupancy, of every tile workgroup.
-template <typename T, typename R, int D, int NPL>
+template <typename T, typename R, int D, int NPL, bool COV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void select_decode_kernel(
     SeqTable st, SelGrid sg, const T *__restrict__ Q, int64_t qb, int64_t qh, const R *__restrict__ reps,
     int64_t rb, int64_t rh, int64_t rj, int gist, int blk, int hkv, int S, int G, int per_head, float scale,
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     else hi = mid - 1;
   }
   const int rem = id - sg.first[lo];
-  select_tile_body<T, R, D, NPL>(rem / hkv, rem % hkv, sg.b[lo], hkv, lds, st, Q, qb, qh, reps, rb, rh, rj,
+  select_tile_body<T, R, D, NPL, COV>(rem / hkv, rem % hkv, sg.b[lo], hkv, lds, st, Q, qb, qh, reps, rb, rh, rj,
                                  gist, blk, S, G, per_head, scale, scores, ld, bg, kcap, idx, nsel, gate,
                                  counters);
 }
@@ -70,12 +70,19 @@ static hipError_t sel_dispatch(const sas_problem &p, const SeqTable &st, const v
     sg.first[i + 1] = sg.first[i] + ntile * p.hkv;
   }
   const dim3 grid((unsigned)sg.first[p.batch]);
-#define SAS_SEL_LAUNCH(NPL_)                                                                                   \
-  hipLaunchKernelGGL((select_decode_kernel<T, R, D, NPL_>), grid, dim3(256), 0, s, st, sg, (const T *)Q, qs[0], \
-                     qs[1], (const R *)reps, rs[0], rs[1], rs[2], gist, p.block, p.hkv, S, p.hq / p.hkv,        \
+#define SAS_SEL_LAUNCH(NPL_, COV_)                                                                          \
+  hipLaunchKernelGGL((select_decode_kernel<T, R, D, NPL_, COV_>), grid, dim3(256), 0, s, st, sg, (const T *)Q, \
+                     qs[0], qs[1], (const R *)reps, rs[0], rs[1], rs[2], gist, p.block, p.hkv, S, p.hq / p.hkv, \
                      per_head, scale, scores, ld, bg, kcap, idx, nsel, gate, counters)
-  if (maxc <= 512) SAS_SEL_LAUNCH(8);
-  else SAS_SEL_LAUNCH(32);
+  // coverage budgets get their own kernels, so that the others carry none of that code
+  const bool cov = bg.coverage > 0.f;
+  if (maxc <= 512) {
+    if (cov) SAS_SEL_LAUNCH(8, true);
+    else SAS_SEL_LAUNCH(8, false);
+  } else {
+    if (cov) SAS_SEL_LAUNCH(32, true);
+    else SAS_SEL_LAUNCH(32, false);
+  }
 #undef SAS_SEL_LAUNCH
   return hipGetLastError();
 }

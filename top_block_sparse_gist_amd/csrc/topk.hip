@@ -14,6 +14,11 @@
 
 namespace sas {
 
+// Inverse of float_order_key.
+__device__ __forceinline__ float order_key_float_tk(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 // Exclusive prefix count of `f` over the workgroup in lane order; `total` gets the sum.
 __device__ __forceinline__ uint32_t block_scan_flag(bool f, uint32_t *sh, uint32_t &total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -85,8 +90,51 @@ __global__ __launch_bounds__(256) void topk_kernel(SeqTable st, const float *__r
   const bool sink = bg.sink && c > 0;
   const int lo = sink ? 1 : 0;
   const int ncand = c - lo;
-  const int k = budget_k(bg, c, ncand);
+  int k = budget_k(bg, c, ncand);
   const int base = sink ? 1 : 0;
+  if (bg.coverage > 0.f && k > 0) {
+    // coverage budget ([SF] 2.3, threshold-based): the smallest number of candidates, in (score
+    // descending, block ascending) order, whose share of the candidates' softmax mass reaches
+    // bg.coverage.  Bisection over the key range for the largest key T with mass(>= T) >= the
+    // target (mass at the smallest key is the total, summed in the same order), then holders of T
+    // one share each, as an exact ranking takes tied candidates in block order.
+    constexpr float L2E = 1.4426950408889634f;
+    float smax = -INFINITY, smin = INFINITY;
+    for (int j = lo + tid; j < c; j += 256) {
+      smax = fmaxf(smax, row[j]);
+      smin = fminf(smin, row[j]);
+    }
+    smax = block_reduce_max(smax, red_sh);
+    smin = -block_reduce_max(-smin, red_sh);
+    auto mass = [&](uint32_t t) {
+      float m = 0.f;
+      for (int j = lo + tid; j < c; j += 256)
+        m += float_order_key(row[j]) >= t ? __builtin_amdgcn_exp2f((row[j] - smax) * L2E) : 0.f;
+      return block_reduce_sum(m, red_sh);
+    };
+    auto count = [&](uint32_t t) {
+      float n = 0.f;  // exact: at most 2^24 candidates
+      for (int j = lo + tid; j < c; j += 256) n += float_order_key(row[j]) >= t ? 1.f : 0.f;
+      return (uint32_t)block_reduce_sum(n, red_sh);
+    };
+    const uint32_t kmin = float_order_key(smin), kmax = float_order_key(smax);
+    const float target = bg.coverage * mass(kmin);
+    uint64_t lo_t = kmin, hi_t = (uint64_t)kmax + 1u;
+    while (hi_t - lo_t > 1u) {
+      const uint64_t mid = lo_t + (hi_t - lo_t) / 2u;
+      if (mass((uint32_t)mid) >= target) lo_t = mid;
+      else hi_t = mid;
+    }
+    const uint32_t T = (uint32_t)lo_t;
+    const bool top = T == 0xFFFFFFFFu;
+    const float m_gt = top ? 0.f : mass(T + 1u);
+    const uint32_t n_gt = top ? 0u : count(T + 1u);
+    const uint32_t n_eq = count(T) - n_gt;
+    const float e_t = __builtin_amdgcn_exp2f((order_key_float_tk(T) - smax) * L2E);
+    uint32_t take = 1u;
+    while (take < n_eq && m_gt + (float)take * e_t < target) ++take;
+    k = min(k, (int)(n_gt + take));
+  }
 
   if (k >= ncand) {
     for (int j = lo + tid; j < c; j += 256) out[base + (j - lo)] = j;
