@@ -370,7 +370,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="decode,reps,prefill,gist,hssa,mixed",
+    ap.add_argument("--only", default="decode,paged,reps,prefill,gist,hssa,mixed",
                     help="comma list of measurements: decode,reps,prefill,gist,mixed,copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -381,6 +381,7 @@ def main():
         sys.exit(2)
     only = set(x for x in args.only.split(",") if x)
 
+    import numpy as np
     import torch
     import top_block_sparse_gist_amd as sas
     from workloads import Workload
@@ -396,7 +397,7 @@ def main():
 
     # ---------------------------------------------------------------- headline: 32K decode
     w2 = Workload(2)
-    need_decode = bool(only & {"decode", "reps"}) or not args.no_cpu_baseline
+    need_decode = bool(only & {"decode", "reps", "paged"}) or not args.no_cpu_baseline
     if not need_decode:
         log("[bench] skipping the 32K decode workload")
     log("[bench] generating the 32K decode workload") if need_decode else None
@@ -436,6 +437,38 @@ def main():
         }
         log(f"[bench] decode step {ms * 1e3:.1f} us (graph replay {ms_graph * 1e3:.1f}) -> {value:.0f} GB/s; "
             f"attention {ms_att * 1e3:.1f} us -> {ach:.0f} GB/s")
+    if "paged" in only and inp2 is not None:
+        # the same 32K decode over a paged cache: the K/V blocks scattered into shuffled pages of one
+        # block each, read through a block table
+        blk, lens2 = w2.block, inp2.seq_lens
+        nbs = [-(-L // blk) for L in lens2]
+        perm = np.random.default_rng(5).permutation(sum(nbs))
+        Kp = torch.zeros((sum(nbs), w2.hkv, blk, w2.d), dtype=inp2.K.dtype, device="cuda")
+        Vp = torch.zeros_like(Kp)
+        table = torch.empty((len(lens2), max(nbs)), dtype=torch.int32)
+        n = 0
+        for b, L in enumerate(lens2):
+            pages = torch.from_numpy(perm[n:n + nbs[b]]).cuda()
+            Kp[pages] = inp2.K[b, :, :nbs[b] * blk].reshape(w2.hkv, nbs[b], blk, w2.d).transpose(0, 1)
+            Vp[pages] = inp2.V[b, :, :nbs[b] * blk].reshape(w2.hkv, nbs[b], blk, w2.d).transpose(0, 1)
+            table[b, :nbs[b]] = torch.from_numpy(perm[n:n + nbs[b]].astype(np.int32))
+            n += nbs[b]
+        table = table.cuda()
+        Op = torch.empty_like(inp2.Q)
+        ws_p = torch.zeros(sas.decode_workspace_bytes(len(lens2), w2.hq, w2.hkv, w2.d, blk, sas.SAS_BF16,
+                                                      inp2.K.shape[2], lens2, w2.sel, bufs["idx"].shape[1], False),
+                           dtype=torch.uint8, device="cuda")
+        Lm = inp2.K.shape[2]
+
+        def attend_paged():
+            sas.sparse_decode_paged(inp2.Q, Kp, Vp, table, lens2, blk, Lm, bufs["idx"], bufs["nsel"], bufs["gate"],
+                                    sel_mode=w2.sel, O=Op, workspace=ws_p)
+        tp, _ = timer.time(attend_paged, K_, W_)
+        extra["decode_paged_32k"] = {"attend_us": round(tp * 1e3, 2),
+                                     "what": "sas_sparse_decode_paged on the 32K decode batch, shuffled pages"}
+        log(f"[bench] paged decode attention: {tp * 1e3:.1f} us")
+        del Kp, Vp, table, Op, ws_p
+        torch.cuda.empty_cache()
     if "reps" in only:
         K = inp2.K
         reps = bufs["reps"]

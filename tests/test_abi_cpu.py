@@ -229,3 +229,29 @@ def test_hssa_validation_codes():
     assert dec(wbytes=16) == _lib.SAS_ERR_WORKSPACE
     need = lib.sas_hssa_decode_workspace(C.byref(p), _lib.SAS_SEL_GROUP, 8, 4, 8)
     assert need > 0 and dec(wbytes=need - 1) == _lib.SAS_ERR_WORKSPACE
+
+
+def test_paged_validation_codes():
+    lib = _lib.load()
+    p, a = _problem(lens=(1000, 700))           # 16 and 11 blocks of 64
+    ps = _lib.i64x([2 * 64 * 128, 64 * 128, 128])
+    rs = _lib.i64x([2 * 16 * 128, 16 * 128, 128])
+
+    def reps(table=FAKE, ld=16, pstride=ps):
+        return lib.sas_block_reps_paged(C.byref(p), FAKE, pstride, table, ld, FAKE, rs, None, None)
+
+    assert reps(table=None) == _lib.SAS_ERR_NULL
+    assert reps(ld=15) == _lib.SAS_ERR_SHAPE
+    assert b"table_ld 15 < 16" in lib.sas_last_error()
+    assert reps(pstride=_lib.i64x([64 * 128, 64 * 128, 128])) == _lib.SAS_ERR_SHAPE   # two heads cannot fit
+    q2 = _lib.i64x([8 * 128, 128])
+
+    def dec(table=FAKE, ld=16, wbytes=1 << 30, prob=p):
+        return lib.sas_sparse_decode_paged(C.byref(prob), FAKE, q2, FAKE, FAKE, ps, table, ld, _lib.SAS_SEL_GROUP,
+                                           FAKE, FAKE, None, 8, 0.0, FAKE, q2, FAKE, C.c_size_t(wbytes), None)
+
+    assert dec(table=None) == _lib.SAS_ERR_NULL
+    assert dec(ld=3) == _lib.SAS_ERR_SHAPE
+    assert dec(wbytes=8) == _lib.SAS_ERR_WORKSPACE
+    pf, af = _problem(dtype=_lib.SAS_F32, lens=(1000, 700))
+    assert dec(prob=pf) == _lib.SAS_ERR_UNSUPPORTED

@@ -366,3 +366,41 @@ def hssa_select_workspace_bytes(B, hq, hkv, d, block, max_len, seq_lens, sel_mod
 def hssa_decode_workspace_bytes(B, hq, hkv, d, block, max_len, seq_lens, sel_mode, kcap, gcap, group_chunks) -> int:
     p = _Prob(B, hq, hkv, d, block, SAS_BF16, max_len, seq_lens)
     return int(load().sas_hssa_decode_workspace(p.ref, sel_code(sel_mode), kcap, gcap, group_chunks))
+
+
+def block_reps_paged(K_pages, block_table, seq_lens, block: int, hkv: int, max_len: int, reps,
+                     first_block: Optional[Sequence[int]] = None, hq: Optional[int] = None, stream=None):
+    """A1 over a paged K: K_pages [num_pages, Hkv, block, d], block_table [B, ld] int32 (page of each
+    block); reps [B, Hkv, NB, d] fp32 by logical block (first_block: only blocks from it on)."""
+    B = block_table.shape[0]
+    d = K_pages.shape[-1]
+    p = _Prob(B, hq or hkv, hkv, d, block, _dtype_code(K_pages), max_len, seq_lens)
+    fb = i32x(first_block) if first_block is not None else None
+    check(load().sas_block_reps_paged(p.ref, _ptr(K_pages), _strides(K_pages, 3), _ptr(block_table),
+                                      block_table.stride(0), _ptr(reps), _strides(reps, 3), fb, _stream(stream)),
+          "sas_block_reps_paged")
+    return reps
+
+
+def sparse_decode_paged(Q, K_pages, V_pages, block_table, seq_lens, block, max_len, idx, nsel, gate=None,
+                        sel_mode="group", scale=0.0, O=None, workspace=None, stream=None):
+    """A5 over paged K/V (see block_reps_paged): O [B, Hq, d] for the row at position L_b - 1."""
+    torch = _torch()
+    B, hq, d = Q.shape
+    hkv = K_pages.shape[1]
+    if K_pages.stride() != V_pages.stride():
+        raise ValueError("K and V pages must share strides")
+    if O is None:
+        O = torch.empty_like(Q)
+    kcap = idx.shape[1]
+    p = _Prob(B, hq, hkv, d, block, _dtype_code(Q), max_len, seq_lens)
+    lib = load()
+    if workspace is None:
+        need = lib.sas_sparse_decode_workspace(p.ref, sel_code(sel_mode), kcap, 0)
+        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=Q.device)
+    check(lib.sas_sparse_decode_paged(p.ref, _ptr(Q), _strides(Q, 2), _ptr(K_pages), _ptr(V_pages),
+                                      _strides(K_pages, 3), _ptr(block_table), block_table.stride(0),
+                                      sel_code(sel_mode), _ptr(idx), _ptr(nsel), _ptr(gate), kcap, float(scale),
+                                      _ptr(O), _strides(O, 2), _ptr(workspace), workspace.numel(), _stream(stream)),
+          "sas_sparse_decode_paged")
+    return O

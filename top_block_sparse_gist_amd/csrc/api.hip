@@ -371,6 +371,79 @@ sas_status sas_sparse_decode(const sas_problem *p, const void *Q, const int64_t 
                     "sas_sparse_decode");
 }
 
+// ---- paged K/V (one block per page, a block table per sequence) ------------------------------
+static sas_status check_table(const sas_problem *p, const SeqTable &tab, const int32_t *table, int64_t table_ld,
+                              const int64_t *page_stride) {
+  if (!table) return fail(SAS_ERR_NULL, "block_table is NULL");
+  // one page holds blk tokens of every KV head, and pages do not overlap
+  if ((int64_t)(p->hkv - 1) * page_stride[1] + (int64_t)(p->block - 1) * page_stride[2] + p->head_dim >
+      page_stride[0])
+    return fail(SAS_ERR_SHAPE, "page stride %lld cannot hold %d tokens of %d KV heads", (long long)page_stride[0],
+                p->block, p->hkv);
+  int nbmax = 0;
+  for (int b = 0; b < p->batch; ++b) nbmax = std::max(nbmax, cdiv(tab.len[b], p->block));
+  if (table_ld < nbmax) return fail(SAS_ERR_SHAPE, "table_ld %lld < %d blocks", (long long)table_ld, nbmax);
+  return SAS_OK;
+}
+
+sas_status sas_block_reps_paged(const sas_problem *p, const void *K_pages, const int64_t page_stride[3],
+                                const int32_t *block_table, int64_t table_ld, float *reps,
+                                const int64_t rep_stride[3], const int32_t *first_block, void *stream) {
+  SeqTable tab{};
+  sas_status st;
+  if ((st = check_problem(p, &tab)) != SAS_OK) return st;
+  if (!K_pages || !reps || !page_stride || !rep_stride) return fail(SAS_ERR_NULL, "K, reps or a stride array is NULL");
+  if ((st = check_table(p, tab, block_table, table_ld, page_stride)) != SAS_OK) return st;
+  if (!aligned16(K_pages) || !aligned16(reps) || !strides_ok(page_stride, 3, elem_bytes(p->dtype)) ||
+      !strides_ok(rep_stride, 3, 4))
+    return fail(SAS_ERR_SHAPE, "K / reps must be 16-byte aligned with 16-byte-multiple row strides");
+  if (first_block) {
+    for (int b = 0; b < p->batch; ++b) {
+      const int nb = cdiv(tab.len[b], p->block);
+      if (first_block[b] < 0 || first_block[b] > nb)
+        return fail(SAS_ERR_SHAPE, "first_block[%d] = %d is outside [0, %d]", b, first_block[b], nb);
+    }
+  }
+  return hip_status(launch_reps(*p, tab, K_pages, page_stride, reps, rep_stride, first_block, (hipStream_t)stream,
+                                block_table, table_ld),
+                    "sas_block_reps_paged");
+}
+
+sas_status sas_sparse_decode_paged(const sas_problem *p, const void *Q, const int64_t q_stride[2],
+                                   const void *K_pages, const void *V_pages, const int64_t page_stride[3],
+                                   const int32_t *block_table, int64_t table_ld, int32_t sel_mode,
+                                   const int32_t *idx, const int32_t *nsel, const float *gate, int32_t kcap,
+                                   float scale, void *O, const int64_t o_stride[2], void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+  SeqTable tab{};
+  sas_status st;
+  if ((st = check_problem(p, &tab)) != SAS_OK) return st;
+  if ((st = check_sel(sel_mode)) != SAS_OK) return st;
+  if (!Q || !q_stride || !K_pages || !V_pages || !page_stride || !idx || !nsel || !O || !o_stride)
+    return fail(SAS_ERR_NULL, "a required pointer is NULL");
+  if ((st = check_table(p, tab, block_table, table_ld, page_stride)) != SAS_OK) return st;
+  if (p->dtype != SAS_BF16) return fail(SAS_ERR_UNSUPPORTED, "paged decode needs bf16 inputs");
+  if (kcap < 1) return fail(SAS_ERR_SHAPE, "kcap must be >= 1");
+  if (scale < 0.f || !isfinite(scale)) return fail(SAS_ERR_SHAPE, "scale must be finite and >= 0");
+  if (!aligned16(Q) || !aligned16(K_pages) || !aligned16(V_pages) || !aligned16(O) || !strides_ok(q_stride, 2, 2) ||
+      !strides_ok(page_stride, 3, 2) || !strides_ok(o_stride, 2, 2))
+    return fail(SAS_ERR_SHAPE, "Q/K/V/O must be 16-byte aligned with 16-byte-multiple row strides");
+  if (sel_mode == SAS_SEL_GROUP && p->hq / p->hkv > 16)
+    return fail(SAS_ERR_UNSUPPORTED, "per-group decode supports at most 16 query heads per KV head");
+  int nwg = 0, cap = 0;
+  if (!decode_merge_fits(*p, tab, sel_mode, kcap, 0, &nwg, &cap))
+    return fail(SAS_ERR_UNSUPPORTED, "kcap %d needs %d split-K records per unit; the merge holds %d", kcap, nwg,
+                cap);
+  const size_t need = decode_workspace_bytes(*p, sel_mode, kcap, 0);
+  if (!workspace || workspace_bytes < need)
+    return fail(SAS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  if (!aligned16(workspace)) return fail(SAS_ERR_SHAPE, "workspace must be 16-byte aligned");
+  return hip_status(launch_decode_bf16(*p, tab, Q, q_stride, K_pages, V_pages, page_stride, nullptr, nullptr,
+                                       nullptr, sel_mode, idx, nsel, gate, kcap, resolve_scale(scale, p->head_dim),
+                                       O, o_stride, (float *)workspace, (hipStream_t)stream, block_table, table_ld),
+                    "sas_sparse_decode_paged");
+}
+
 // ---- two-level gist selection (H-SSA) -------------------------------------------------------
 // checks shared by the two entry points: bf16, group size, the opened-group list capacity
 static sas_status check_hssa(const sas_problem *p, const SeqTable &tab, int32_t sel_mode, int32_t M, int32_t gcap,

@@ -195,7 +195,8 @@ namespace sas {
 
 // first: host [batch] first block to compute per sequence, or NULL for every block
 hipError_t launch_reps(const sas_problem &p, const SeqTable &st, const void *K, const int64_t *ks,
-                       float *reps, const int64_t *rs, const int32_t *first, hipStream_t s);
+                       float *reps, const int64_t *rs, const int32_t *first, hipStream_t s,
+                       const int32_t *table = nullptr, int64_t tld = 0);
 
 hipError_t launch_pool_queries(const sas_problem &p, const SeqTable &st, const void *Q,
                                const int64_t *qs, int32_t tq, int32_t sel_mode, float *qbar,
@@ -221,11 +222,13 @@ hipError_t launch_prefill_bf16(const sas_problem &p, const SeqTable &st, const v
                                const float *gate, int32_t kcap, float scale, void *O, const int64_t *os,
                                hipStream_t s);
 
+// table: DEVICE [B, tld] page of each block (paged K/V; kv strides are then {page, head, token}), or nullptr
 hipError_t launch_decode_bf16(const sas_problem &p, const SeqTable &st, const void *Q, const int64_t *qs,
                               const void *K, const void *V, const int64_t *kvs, const void *gk,
                               const void *gv, const int64_t *gs, int32_t sel_mode, const int32_t *idx,
                               const int32_t *nsel, const float *gate, int32_t kcap, float scale, void *O,
-                              const int64_t *os, float *work, hipStream_t s);
+                              const int64_t *os, float *work, hipStream_t s,
+                              const int32_t *table = nullptr, int64_t tld = 0);
 
 hipError_t launch_attend_f32(const sas_problem &p, const SeqTable &st, const void *Q, const int64_t *qs,
                              const void *K, const void *V, const int64_t *kvs, const void *gk, const void *gv,

@@ -35,11 +35,11 @@ __global__ __launch_bounds__(WPW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     const uint16_t *__restrict__ GV, int64_t gb, int64_t gh, int64_t gt, int gist, int blk, int S, int G,
     int per_head, const int32_t *__restrict__ idx, const int32_t *__restrict__ nsel, const float *__restrict__ gate,
     int kcap, float scale_log2, float *__restrict__ work, uint32_t *__restrict__ counters, OT *__restrict__ O,
-    int64_t ob, int64_t oh, MetaArgs ma) {
+    int64_t ob, int64_t oh, MetaArgs ma, PageArgs pg) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[DecodeLds<D, WPW>::BYTES];
   decode_tile_body<D, WPW, TPW, OT, HS>(blockIdx.x, blockIdx.y, gridDim.x, lds, st, Q, qb, qh, K, V, kb, kh, kt,
                                           GK, GV, gb, gh, gt, gist, blk, S, G, per_head, idx, nsel, gate, kcap,
-                                          scale_log2, work, counters, O, ob, oh, ma);
+                                          scale_log2, work, counters, O, ob, oh, ma, pg);
 }
 
 // ---- host side -------------------------------------------------------------------------------
@@ -87,12 +87,12 @@ static hipError_t decode_launch(const sas_problem &p, const SeqTable &st, const 
                                 const void *gk, const void *gv, int64_t gb, int64_t gh, int64_t gt, int gist,
                                 int per_head, const int32_t *idx, const int32_t *nsel, const float *gate, int32_t kcap,
                                 float scale_log2, float *work, uint32_t *counters, void *O, const int64_t *os,
-                                const MetaArgs &ma, hipStream_t s) {
+                                const MetaArgs &ma, const PageArgs &pg, hipStream_t s) {
   hipLaunchKernelGGL((decode_bf16_kernel<D, WPW, TPW, uint16_t, HS>), dim3(nwg, (unsigned)d.units), dim3(WPW * 64), 0,
                      s, st, (const uint16_t *)Q, qs[0], qs[1], (const uint16_t *)K, (const uint16_t *)V, kvs[0],
                      kvs[1], kvs[2], (const uint16_t *)gk, (const uint16_t *)gv, gb, gh, gt, gist, p.block, d.S,
                      p.hq / p.hkv, per_head, idx, nsel, gate, kcap, scale_log2, work, counters, (uint16_t *)O, os[0],
-                     os[1], ma);
+                     os[1], ma, pg);
   return hipGetLastError();
 }
 
@@ -100,7 +100,9 @@ hipError_t launch_decode_bf16(const sas_problem &p, const SeqTable &st, const vo
                               const void *K, const void *V, const int64_t *kvs, const void *gk,
                               const void *gv, const int64_t *gs, int32_t sel_mode, const int32_t *idx,
                               const int32_t *nsel, const float *gate, int32_t kcap, float scale, void *O,
-                              const int64_t *os, float *workspace, hipStream_t s) {
+                              const int64_t *os, float *workspace, hipStream_t s, const int32_t *table,
+                              int64_t tld) {
+  const PageArgs pg{table, tld};
   const int gist = gk != nullptr;
   const int per_head = sel_mode == SAS_SEL_HEAD;
   int maxc = 0;
@@ -119,7 +121,7 @@ hipError_t launch_decode_bf16(const sas_problem &p, const SeqTable &st, const vo
   const float sl2 = scale * 1.4426950408889634f;
 #define SAS_DEC(D_, T_)                                                                                          \
   return decode_launch<D_, 4, T_, false>(p, st, d, nwg, Q, qs, K, V, kvs, gk, gv, gb, gh, gt, gist, per_head, idx, \
-                                         nsel, gate, kcap, sl2, work, counters, O, os, MetaArgs{}, s)
+                                         nsel, gate, kcap, sl2, work, counters, O, os, MetaArgs{}, pg, s)
   if (p.head_dim == 128) {
     if (tpw == 3) SAS_DEC(128, 3);
     if (tpw == 2) SAS_DEC(128, 2);
@@ -179,7 +181,7 @@ hipError_t launch_hssa_decode(const sas_problem &p, const SeqTable &st, const vo
   const float sl2 = scale * 1.4426950408889634f;
 #define SAS_HDEC(D_, T_)                                                                                           \
   return decode_launch<D_, 4, T_, true>(p, st, d, nwg, Q, qs, K, V, kvs, gk, gv, gs[0], gs[1], gs[2], 0, per_head, \
-                                        idx, nsel, nullptr, kcap, sl2, work, counters, O, os, ma, s)
+                                        idx, nsel, nullptr, kcap, sl2, work, counters, O, os, ma, PageArgs{}, s)
   if (p.head_dim == 128) {
     if (tpw == 3) SAS_HDEC(128, 3);
     if (tpw == 2) SAS_HDEC(128, 2);

@@ -513,6 +513,13 @@ struct MetaArgs {
   int M, gcap, nmt;     // chunks per group; list capacity; meta tiles per unit (grid-wide)
 };
 
+// Paged K/V: block j of sequence b lives in page table[b * tld + j] of the cache (pages of one
+// block; kb is then the page stride).  table == nullptr: K/V are [B, Hkv, Lmax, d].
+struct PageArgs {
+  const int32_t *table;
+  int64_t tld;
+};
+
 // One attention workgroup: tiles bx*WPW*TPW .. +WPW*TPW-1 of unit u (TPW = 1 to 3 per wave: wave w
 // takes tiles w, w + WPW, ... of the workgroup's range, each next tile's K/V loads issued as soon
 // as the previous one's registers are consumed, so they overlap its softmax and PV), merged into the
@@ -528,7 +535,7 @@ __device__ __forceinline__ void decode_tile_body(
     int blk, int S, int G, int per_head, const int32_t *__restrict__ idx, const int32_t *__restrict__ nsel,
     const float *__restrict__ gate, int kcap,
     float scale_log2, float *__restrict__ work, uint32_t *__restrict__ counters, OT *__restrict__ O, int64_t ob,
-    int64_t oh, MetaArgs ma = MetaArgs{}) {
+    int64_t oh, MetaArgs ma = MetaArgs{}, PageArgs pg = PageArgs{}) {
   constexpr int NKK = D / 32;   // MFMA k-steps over the head dim
   constexpr int NDT = D / 16;   // 16-dim output tiles
   constexpr int VROW = D + VPAD;
@@ -578,7 +585,8 @@ __device__ __forceinline__ void decode_tile_body(
   struct Tile {
     const uint16_t *kbase, *vbase;
     int64_t rstride;
-    int key0, nvalid;
+    int key0, nvalid;  // position of the tile's first key; keys present
+    int roff;          // row of that key from kbase (key0, or its row inside a page)
     float gl2;
     uint64_t excl;
   };
@@ -602,7 +610,7 @@ __device__ __forceinline__ void decode_tile_body(
     return bits;
   };
   auto describe = [&](int k) {
-    Tile d{nullptr, nullptr, 0, 0, 0, 0.f, 0ull};
+    Tile d{nullptr, nullptr, 0, 0, 0, 0, 0.f, 0ull};
     const int tk = tt[k] - r0;  // raw tiles count from r0
     if (HS && tk < 0) {
       if (tt[k] < ma.gcap) {
@@ -614,6 +622,7 @@ __device__ __forceinline__ void decode_tile_body(
           d.kbase = GK + b * gb + g * gh;
           d.vbase = GV + b * gb + g * gh;
           d.rstride = gt;
+          d.roff = d.key0;
           if (d.nvalid > 0) d.excl = list_bits(idx + u * kcap, kcap, d.key0);
         }
       } else {
@@ -623,6 +632,7 @@ __device__ __forceinline__ void decode_tile_body(
         d.kbase = ma.MK + b * ma.mb + g * ma.mh;
         d.vbase = ma.MV + b * ma.mb + g * ma.mh;
         d.rstride = ma.mt;
+        d.roff = d.key0;
         if (d.nvalid > 0) d.excl = list_bits(ma.gidx + u * ma.gcap, ma.gcap, d.key0);
       }
     } else if (tk < nraw) {
@@ -630,8 +640,16 @@ __device__ __forceinline__ void decode_tile_body(
       if (j >= 0) {
         d.key0 = j * blk + (tk % tpb) * 64;
         d.nvalid = min(64, L - d.key0);
-        d.kbase = K + b * kb + g * kh;
-        d.vbase = V + b * kb + g * kh;
+        if (pg.table) {
+          const int64_t page = pg.table[b * pg.tld + j];
+          d.kbase = K + page * kb + g * kh;
+          d.vbase = V + page * kb + g * kh;
+          d.roff = (tk % tpb) * 64;
+        } else {
+          d.kbase = K + b * kb + g * kh;
+          d.vbase = V + b * kb + g * kh;
+          d.roff = d.key0;
+        }
         d.rstride = kt;
         d.gl2 = graw[k] * 1.4426950408889634f;
       }
@@ -641,6 +659,7 @@ __device__ __forceinline__ void decode_tile_body(
       d.kbase = GK + b * gb + g * gh;
       d.vbase = GV + b * gb + g * gh;
       d.rstride = gt;
+      d.roff = d.key0;
       // gists of selected chunks are replaced by their raw tokens: exclude them
       if (d.nvalid > 0) d.excl = list_bits(idx + u * kcap, kcap, d.key0);
     }
@@ -681,7 +700,7 @@ __device__ __forceinline__ void decode_tile_body(
       for (int kk = 0; kk < NKK; ++kk) {
         u32x4 v = {0u, 0u, 0u, 0u};
         if (key < d.nvalid)
-          v = *reinterpret_cast<const u32x4 *>(d.kbase + (int64_t)(d.key0 + key) * d.rstride + 32 * kk + 8 * grp);
+          v = *reinterpret_cast<const u32x4 *>(d.kbase + (int64_t)(d.roff + key) * d.rstride + 32 * kk + 8 * grp);
         kreg[mt][kk] = v;
       }
     }
@@ -690,7 +709,7 @@ __device__ __forceinline__ void decode_tile_body(
       const int e = x * 64 + lane;
       const int key = e / VCH, ch = e % VCH;
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (key < d.nvalid) v = *reinterpret_cast<const u32x4 *>(d.vbase + (int64_t)(d.key0 + key) * d.rstride + ch * 8);
+      if (key < d.nvalid) v = *reinterpret_cast<const u32x4 *>(d.vbase + (int64_t)(d.roff + key) * d.rstride + ch * 8);
       vreg[x] = v;
     }
   };

@@ -21,7 +21,8 @@ struct BlockStart {
 template <typename T, int D, int BLK>
 __global__ __launch_bounds__(256) void reps_kernel(SeqTable st, BlockStart start, const T *__restrict__ K, int64_t kb,
                                                    int64_t kh, int64_t kt, float *__restrict__ reps,
-                                                   int64_t rb, int64_t rh, int64_t rj) {
+                                                   int64_t rb, int64_t rh, int64_t rj,
+                                                   const int32_t *__restrict__ table, int64_t tld) {
   constexpr int VEC = 16 / sizeof(T);      // elements per 16-byte load
   constexpr int TPR = D / VEC;             // lanes per key row
   constexpr int RPP = 256 / TPR;           // rows per pass
@@ -37,7 +38,9 @@ __global__ __launch_bounds__(256) void reps_kernel(SeqTable st, BlockStart start
   const int n = min(BLK, L - t0);
   const int tid = threadIdx.x;
   const int c = tid % TPR, r = tid / TPR;
-  const T *base = K + b * kb + g * kh + (int64_t)t0 * kt + c * VEC;
+  // paged K (table != nullptr): block j is page table[b * tld + j], kb its stride
+  const T *base = table ? K + (int64_t)table[b * tld + j] * kb + g * kh + c * VEC
+                        : K + b * kb + g * kh + (int64_t)t0 * kt + c * VEC;
 
   u32x4 raw[PASSES];
 #pragma unroll
@@ -76,7 +79,7 @@ __global__ __launch_bounds__(256) void reps_kernel(SeqTable st, BlockStart start
 template <typename T, int D>
 static hipError_t reps_dispatch_blk(const sas_problem &p, const SeqTable &st, const void *K,
                                     const int64_t *ks, float *reps, const int64_t *rs, const int32_t *first,
-                                    hipStream_t s) {
+                                    hipStream_t s, const int32_t *table, int64_t tld) {
   BlockStart start{};
   int nbmax = 0;
   for (int b = 0; b < p.batch; ++b) {
@@ -87,21 +90,22 @@ static hipError_t reps_dispatch_blk(const sas_problem &p, const SeqTable &st, co
   dim3 grid(nbmax, p.hkv, p.batch);
   if (p.block == 64)
     hipLaunchKernelGGL((reps_kernel<T, D, 64>), grid, dim3(256), 0, s, st, start, (const T *)K, ks[0], ks[1],
-                       ks[2], reps, rs[0], rs[1], rs[2]);
+                       ks[2], reps, rs[0], rs[1], rs[2], table, tld);
   else
     hipLaunchKernelGGL((reps_kernel<T, D, 128>), grid, dim3(256), 0, s, st, start, (const T *)K, ks[0], ks[1],
-                       ks[2], reps, rs[0], rs[1], rs[2]);
+                       ks[2], reps, rs[0], rs[1], rs[2], table, tld);
   return hipGetLastError();
 }
 
 hipError_t launch_reps(const sas_problem &p, const SeqTable &st, const void *K, const int64_t *ks,
-                       float *reps, const int64_t *rs, const int32_t *first, hipStream_t s) {
+                       float *reps, const int64_t *rs, const int32_t *first, hipStream_t s, const int32_t *table,
+                       int64_t tld) {
   if (p.dtype == SAS_BF16) {
-    if (p.head_dim == 128) return reps_dispatch_blk<uint16_t, 128>(p, st, K, ks, reps, rs, first, s);
-    return reps_dispatch_blk<uint16_t, 64>(p, st, K, ks, reps, rs, first, s);
+    if (p.head_dim == 128) return reps_dispatch_blk<uint16_t, 128>(p, st, K, ks, reps, rs, first, s, table, tld);
+    return reps_dispatch_blk<uint16_t, 64>(p, st, K, ks, reps, rs, first, s, table, tld);
   }
-  if (p.head_dim == 128) return reps_dispatch_blk<float, 128>(p, st, K, ks, reps, rs, first, s);
-  return reps_dispatch_blk<float, 64>(p, st, K, ks, reps, rs, first, s);
+  if (p.head_dim == 128) return reps_dispatch_blk<float, 128>(p, st, K, ks, reps, rs, first, s, table, tld);
+  return reps_dispatch_blk<float, 64>(p, st, K, ks, reps, rs, first, s, table, tld);
 }
 
 }  // namespace sas
