@@ -414,7 +414,7 @@ def main():
         value = by["total"] / (ms * 1e-3) / 1e9
         dec_bytes = by["kv"] + by["qo"]
         ach = dec_bytes / (ms_att * 1e-3) / 1e9
-        tr = measured_traffic("decode_bf16_kernel<128, 4, 1, unsigned short>")
+        tr = measured_traffic("decode_bf16_kernel<128, 4, 1, unsigned short, false>")
         result = {
             "metric": "decode GB/s (%HBM peak) + prefill TFLOP/s (%MFMA peak) at sparsity 0.95",
             "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K_, "warmup": W_,
