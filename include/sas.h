@@ -11,7 +11,8 @@
  * The path ([GSA] section 4 pseudo-code steps 1-3, [SAS] method, [SSA] method):
  *   sas_block_reps    one representative key per block (mean of its keys)
  *   sas_block_reps_update  the same for the blocks from a given one on (a decode loop)
- *   sas_block_reps_paged / sas_sparse_decode_paged  the same over a paged KV cache
+ *   sas_block_reps_paged / sas_sparse_prefill_paged / sas_sparse_decode_paged  the same over a
+ *                     paged KV cache
  *   sas_block_scores  score every earlier block against each selection unit's queries
  *   sas_topk_select   top-k blocks + the current block (+ block 0), optional log-gate
  *   sas_sparse_prefill / sas_sparse_decode  attention over the selected blocks only
@@ -221,8 +222,10 @@ sas_status sas_sparse_decode(const sas_problem *p, const void *Q, const int64_t 
  * sas_block_reps_paged: sas_block_reps / sas_block_reps_update over a paged K (first_block: HOST
  *   [B] or NULL for every block); the reps stay [B, Hkv, NB, d] by logical block.
  * sas_sparse_decode_paged: sas_sparse_decode over paged K/V (bf16; no gist mode); same lists,
- *   workspace and errors.  Paged and contiguous caches with equal contents give equal results
- *   bit for bit (the same kernels; only the row addresses differ). */
+ *   workspace and errors.
+ * sas_sparse_prefill_paged: sas_sparse_prefill over paged K/V (bf16); same lists and errors.
+ * Paged and contiguous caches with equal contents give equal results bit for bit (the same
+ * kernels; only the row addresses differ). */
 sas_status sas_block_reps_paged(const sas_problem *p, const void *K_pages, const int64_t page_stride[3],
                                 const int32_t *block_table, int64_t table_ld, float *reps,
                                 const int64_t rep_stride[3], const int32_t *first_block,
@@ -234,6 +237,13 @@ sas_status sas_sparse_decode_paged(const sas_problem *p, const void *Q, const in
                                    const int32_t *nsel, const float *gate, int32_t kcap,
                                    float scale, void *O, const int64_t o_stride[2],
                                    void *workspace, size_t workspace_bytes, void *stream);
+sas_status sas_sparse_prefill_paged(const sas_problem *p, const void *Q, const int64_t q_stride[3],
+                                    const void *K_pages, const void *V_pages,
+                                    const int64_t page_stride[3], const int32_t *block_table,
+                                    int64_t table_ld, int32_t tq, const int32_t *q_start,
+                                    int32_t sel_mode, const int32_t *idx, const int32_t *nsel,
+                                    const float *gate, int32_t kcap, float scale, void *O,
+                                    const int64_t o_stride[3], void *stream);
 
 /* Two-level gist selection for decode ([SSA] hierarchical extension: meta-gist tokens, gists
  * of gists, make a coarse level; the ordinary gists of the chosen part are then scored and the

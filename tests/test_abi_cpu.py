@@ -255,3 +255,20 @@ def test_paged_validation_codes():
     assert dec(wbytes=8) == _lib.SAS_ERR_WORKSPACE
     pf, af = _problem(dtype=_lib.SAS_F32, lens=(1000, 700))
     assert dec(prob=pf) == _lib.SAS_ERR_UNSUPPORTED
+
+
+def test_paged_prefill_validation_codes():
+    lib = _lib.load()
+    p, a = _problem(lens=(1000, 700))
+    ps = _lib.i64x([2 * 64 * 128, 64 * 128, 128])
+    q3 = _lib.i64x([8 * 1000 * 128, 1000 * 128, 128])
+    qs = _lib.i32x([900, 600])
+
+    def pf(table=FAKE, ld=16, tq=100, q_start=qs):
+        return lib.sas_sparse_prefill_paged(C.byref(p), FAKE, q3, FAKE, FAKE, ps, table, ld, tq, q_start,
+                                            _lib.SAS_SEL_GROUP, FAKE, FAKE, None, 8, 0.0, FAKE, q3, None)
+
+    assert pf(table=None) == _lib.SAS_ERR_NULL
+    assert pf(q_start=None) == _lib.SAS_ERR_NULL
+    assert pf(ld=10) == _lib.SAS_ERR_SHAPE
+    assert pf(tq=200) == _lib.SAS_ERR_SHAPE            # q_start + tq > L for the second sequence

@@ -431,3 +431,28 @@ def test_paged_decode_equals_contiguous(sel, blk):
         assert torch.equal(reps[b, :, :nb], reps_p[b, :, :nb]), f"sequence {b}: paged reps differ"
     assert torch.equal(O, Op), "paged decode differs from the contiguous decode"
     say(f"[paged] blk {blk} {sel}: reps and outputs equal the contiguous path bit for bit")
+
+
+@pytest.mark.parametrize("sel,blk,d", [("group", 128, 128), ("head", 64, 128), ("head", 64, 64)])
+def test_paged_prefill_equals_contiguous(sel, blk, d):
+    """Prefill over a paged cache (shuffled one-block pages) equals the contiguous prefill bit for
+    bit: 128-row workgroups with swizzled copies, 64-row ones with padded rows (d 128) and with
+    swizzled rows (d 64), partial last blocks included; the contiguous path is checked against the
+    oracle on the same workload first."""
+    from workloads.device import upload
+    w = Workload(3, overrides=dict(tag=f"paged{sel}{blk}{d}", seq_lens=[3000, 1777], seq_len=None, batch=2, tq=900,
+                                   hq=8, hkv=2, d=d, block=blk, sel=sel, frac_num=1, frac_den=4, sink=True, gate=True))
+    run_case(w, [0, 1])
+    inp = upload(w, [0, 1])
+    lens, Lmax = inp.seq_lens, inp.K.shape[2]
+    budget = sas.Budget(frac_num=1, frac_den=4, sink=True, gate=True)
+    reps = sas.block_reps(inp.K, lens, blk, hq=w.hq)
+    scores = sas.block_scores(inp.Q, reps, lens, blk, w.hkv, Lmax, q_start=inp.q_start, sel_mode=sel)
+    idx, nsel, gate = sas.topk_select(scores, lens, blk, w.hq, w.hkv, d, sas.SAS_BF16, Lmax, budget, tq=w.tq,
+                                      q_start=inp.q_start, sel_mode=sel)
+    O = sas.sparse_prefill(inp.Q, inp.K, inp.V, lens, blk, inp.q_start, idx, nsel, gate, sel_mode=sel)
+    Kp, Vp, table = _paged_copy(inp.K, inp.V, lens, blk, seed=9)
+    Op = sas.sparse_prefill_paged(inp.Q, Kp, Vp, table, lens, blk, Lmax, inp.q_start, idx, nsel, gate, sel_mode=sel)
+    torch.cuda.synchronize()
+    assert torch.equal(O, Op), "paged prefill differs from the contiguous prefill"
+    say(f"[paged] prefill {sel} blk {blk} d {d}: equal to the contiguous path bit for bit")

@@ -404,3 +404,22 @@ def sparse_decode_paged(Q, K_pages, V_pages, block_table, seq_lens, block, max_l
                                       _ptr(O), _strides(O, 2), _ptr(workspace), workspace.numel(), _stream(stream)),
           "sas_sparse_decode_paged")
     return O
+
+
+def sparse_prefill_paged(Q, K_pages, V_pages, block_table, seq_lens, block, max_len, q_start, idx, nsel, gate=None,
+                         sel_mode="group", scale=0.0, O=None, stream=None):
+    """A4 over paged K/V (see block_reps_paged): O like Q [B, Hq, tq, d]."""
+    torch = _torch()
+    B, hq, tq, d = Q.shape
+    hkv = K_pages.shape[1]
+    if K_pages.stride() != V_pages.stride():
+        raise ValueError("K and V pages must share strides")
+    if O is None:
+        O = torch.empty_like(Q)
+    p = _Prob(B, hq, hkv, d, block, _dtype_code(Q), max_len, seq_lens)
+    check(load().sas_sparse_prefill_paged(p.ref, _ptr(Q), _strides(Q, 3), _ptr(K_pages), _ptr(V_pages),
+                                          _strides(K_pages, 3), _ptr(block_table), block_table.stride(0), tq,
+                                          _qstart(q_start), sel_code(sel_mode), _ptr(idx), _ptr(nsel), _ptr(gate),
+                                          idx.shape[1], float(scale), _ptr(O), _strides(O, 3), _stream(stream)),
+          "sas_sparse_prefill_paged")
+    return O

@@ -444,6 +444,33 @@ sas_status sas_sparse_decode_paged(const sas_problem *p, const void *Q, const in
                     "sas_sparse_decode_paged");
 }
 
+sas_status sas_sparse_prefill_paged(const sas_problem *p, const void *Q, const int64_t q_stride[3],
+                                    const void *K_pages, const void *V_pages, const int64_t page_stride[3],
+                                    const int32_t *block_table, int64_t table_ld, int32_t tq,
+                                    const int32_t *q_start, int32_t sel_mode, const int32_t *idx,
+                                    const int32_t *nsel, const float *gate, int32_t kcap, float scale, void *O,
+                                    const int64_t o_stride[3], void *stream) {
+  SeqTable tab{};
+  sas_status st;
+  if ((st = check_problem(p, &tab)) != SAS_OK) return st;
+  if (!q_start) return fail(SAS_ERR_NULL, "q_start is NULL (prefill needs the first row position)");
+  if ((st = check_rows(p, tq, q_start, &tab)) != SAS_OK) return st;
+  if ((st = check_sel(sel_mode)) != SAS_OK) return st;
+  if (!Q || !q_stride || !K_pages || !V_pages || !page_stride || !idx || !nsel || !O || !o_stride)
+    return fail(SAS_ERR_NULL, "a required pointer is NULL");
+  if ((st = check_table(p, tab, block_table, table_ld, page_stride)) != SAS_OK) return st;
+  if (p->dtype != SAS_BF16) return fail(SAS_ERR_UNSUPPORTED, "paged prefill needs bf16 inputs");
+  if (kcap < 1) return fail(SAS_ERR_SHAPE, "kcap must be >= 1");
+  if (scale < 0.f || !isfinite(scale)) return fail(SAS_ERR_SHAPE, "scale must be finite and >= 0");
+  if (!aligned16(Q) || !aligned16(K_pages) || !aligned16(V_pages) || !aligned16(O) || !strides_ok(q_stride, 3, 2) ||
+      !strides_ok(page_stride, 3, 2) || !strides_ok(o_stride, 3, 2))
+    return fail(SAS_ERR_SHAPE, "Q/K/V/O must be 16-byte aligned with 16-byte-multiple row strides");
+  return hip_status(launch_prefill_bf16(*p, tab, Q, q_stride, K_pages, V_pages, page_stride, tq, sel_mode, idx, nsel,
+                                        gate, kcap, resolve_scale(scale, p->head_dim), O, o_stride,
+                                        (hipStream_t)stream, block_table, table_ld),
+                    "sas_sparse_prefill_paged");
+}
+
 // ---- two-level gist selection (H-SSA) -------------------------------------------------------
 // checks shared by the two entry points: bf16, group size, the opened-group list capacity
 static sas_status check_hssa(const sas_problem *p, const SeqTable &tab, int32_t sel_mode, int32_t M, int32_t gcap,

@@ -220,7 +220,8 @@ hipError_t launch_prefill_bf16(const sas_problem &p, const SeqTable &st, const v
                                const void *K, const void *V, const int64_t *kvs, int32_t tq,
                                int32_t sel_mode, const int32_t *idx, const int32_t *nsel,
                                const float *gate, int32_t kcap, float scale, void *O, const int64_t *os,
-                               hipStream_t s);
+                               hipStream_t s,
+                               const int32_t *table = nullptr, int64_t tld = 0);
 
 // table: DEVICE [B, tld] page of each block (paged K/V; kv strides are then {page, head, token}), or nullptr
 hipError_t launch_decode_bf16(const sas_problem &p, const SeqTable &st, const void *Q, const int64_t *qs,

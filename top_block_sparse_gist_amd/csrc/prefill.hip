@@ -52,7 +52,8 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, int64_t kb, int64_t kh, int64_t kt,
     int tq, int blk, int S, int QB, int G, int per_head, int batch, int rtiles, int pchunks,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ nsel, const float *__restrict__ gate,
-    int kcap, float scale_log2, uint16_t *__restrict__ O, int64_t ob, int64_t oh, int64_t ot) {
+    int kcap, float scale_log2, uint16_t *__restrict__ O, int64_t ob, int64_t oh, int64_t ot,
+    const int32_t *__restrict__ table, int64_t tld) {
   constexpr int NKK = D / 16;        // k-steps of S^T over the head dim
   constexpr int NDT = D / 32;        // 32-dim output tiles
   static_assert(D == 64 || D == 128, "head dim 64 or 128");
@@ -177,39 +178,56 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
   const uint32_t row_bytes = (uint32_t)(kt * 2);
   const uint32_t slab = (uint32_t)(L - 1) * row_bytes + D * 2;
   const __amdgpu_buffer_rsrc_t krs = dev_rsrc(kbase, slab), vrs = dev_rsrc(vbase, slab);
+  // Paged K/V (table != nullptr): block j lives in page table[b * tld + j] (kb is the page stride);
+  // a tile's copies then take a resource over its page and rows counted inside the page.
+  struct Src {
+    __amdgpu_buffer_rsrc_t k, v;
+    int r0, rlast;  // the tile's first row and the last present row, from the resource's base
+  };
+  auto tile_src = [&](int t) {
+    const int j = ulist[t / tpb];
+    if (table) {
+      const int64_t page = table[b * tld + j];
+      const uint32_t pbytes = (uint32_t)(BLK - 1) * row_bytes + D * 2;
+      return Src{dev_rsrc(K + page * kb + g * kh, pbytes), dev_rsrc(V + page * kb + g * kh, pbytes),
+                 (t % tpb) * 64, min(BLK, L - j * BLK) - 1};
+    }
+    return Src{krs, vrs, j * BLK + (t % tpb) * 64, L - 1};
+  };
   const int rin = lane / CPR, cslot = lane % CPR;
   const uint32_t lrow = (uint32_t)rin * row_bytes;
   const int kx = cslot ^ fK(rin);
   const uint32_t voff_v = lrow + (uint32_t)(cslot ^ fV(rin)) * 16u;
   // copy tile t's rows of K and / or V into buffer buf
   auto load_tile = [&](int t, int buf, bool k, bool v) {
-    const int key0 = ulist[t / tpb] * BLK + (t % tpb) * 64;
+    const Src sr = tile_src(t);
+    const int key0 = sr.r0;
     if constexpr (SWZ) {
-      if (key0 + 64 <= L) {
+      if (key0 + 63 <= sr.rlast) {
 #pragma unroll
         for (int x = 0; x < NDMA; ++x) {
           const int row0 = wave * RPW + x * RPI;  // wave-uniform
           const uint32_t soff = (uint32_t)(key0 + row0) * row_bytes;
-          if (k) buf_load_lds<16>(krs, &klds2[buf][row0 * D], lrow + (uint32_t)(kx ^ fK(row0)) * 16u, soff);
-          if (v) buf_load_lds<16>(vrs, &vlds2[buf][row0 * D], voff_v, soff);
+          if (k) buf_load_lds<16>(sr.k, &klds2[buf][row0 * D], lrow + (uint32_t)(kx ^ fK(row0)) * 16u, soff);
+          if (v) buf_load_lds<16>(sr.v, &vlds2[buf][row0 * D], voff_v, soff);
         }
       } else {
 #pragma unroll
         for (int x = 0; x < NDMA; ++x) {
           const int row0 = wave * RPW + x * RPI;
           const int row = row0 + rin;
-          const uint32_t roff = (uint32_t)min(key0 + row, L - 1) * row_bytes;
-          if (k) buf_load_lds<16>(krs, &klds2[buf][row0 * D], roff + (uint32_t)(cslot ^ fK(row)) * 16u, 0u);
-          if (v) buf_load_lds<16>(vrs, &vlds2[buf][row0 * D], roff + (uint32_t)(cslot ^ fV(row)) * 16u, 0u);
+          const uint32_t roff = (uint32_t)min(key0 + row, sr.rlast) * row_bytes;
+          if (k) buf_load_lds<16>(sr.k, &klds2[buf][row0 * D], roff + (uint32_t)(cslot ^ fK(row)) * 16u, 0u);
+          if (v) buf_load_lds<16>(sr.v, &vlds2[buf][row0 * D], roff + (uint32_t)(cslot ^ fV(row)) * 16u, 0u);
         }
       }
     } else {
 #pragma unroll
       for (int x = 0; x < RPW; ++x) {
         const int row = wave + x * NW;
-        const uint32_t soff = (uint32_t)min(key0 + row, L - 1) * row_bytes;
-        if (k) buf_load_lds<DMA>(krs, &klds2[buf][row * ROWK], lane * DMA, soff);
-        if (v) buf_load_lds<DMA>(vrs, &vlds2[buf][row * ROWV], lane * DMA, soff);
+        const uint32_t soff = (uint32_t)min(key0 + row, sr.rlast) * row_bytes;
+        if (k) buf_load_lds<DMA>(sr.k, &klds2[buf][row * ROWK], lane * DMA, soff);
+        if (v) buf_load_lds<DMA>(sr.v, &vlds2[buf][row * ROWV], lane * DMA, soff);
       }
     }
   };
@@ -377,7 +395,7 @@ static hipError_t prefill_dispatch(const sas_problem &p, const SeqTable &st, con
                                    const void *K, const void *V, const int64_t *kvs, int32_t tq,
                                    int32_t sel_mode, const int32_t *idx, const int32_t *nsel,
                                    const float *gate, int32_t kcap, float scale, void *O, const int64_t *os,
-                                   hipStream_t s) {
+                                   hipStream_t s, const int32_t *table, int64_t tld) {
   const int per_head = sel_mode == SAS_SEL_HEAD;
   const int S = per_head ? p.hq : p.hkv;
   const int G = p.hq / p.hkv;
@@ -399,7 +417,7 @@ static hipError_t prefill_dispatch(const sas_problem &p, const SeqTable &st, con
   hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, BLK>), dim3((unsigned)nwg), dim3(NW * 64), 0, s, st, ord,
                      (const uint16_t *)Q, qs[0], qs[1], qs[2], (const uint16_t *)K, (const uint16_t *)V, kvs[0],
                      kvs[1], kvs[2], tq, p.block, S, QB, G, per_head, p.batch, rtiles, pchunks, idx, nsel, gate, kcap,
-                     scale_log2, (uint16_t *)O, os[0], os[1], os[2]);
+                     scale_log2, (uint16_t *)O, os[0], os[1], os[2], table, tld);
   return hipGetLastError();
 }
 
@@ -407,12 +425,13 @@ hipError_t launch_prefill_bf16(const sas_problem &p, const SeqTable &st, const v
                                const void *K, const void *V, const int64_t *kvs, int32_t tq,
                                int32_t sel_mode, const int32_t *idx, const int32_t *nsel,
                                const float *gate, int32_t kcap, float scale, void *O, const int64_t *os,
-                               hipStream_t s) {
+                               hipStream_t s, const int32_t *table, int64_t tld) {
   // rows per unit: blk (x G when the group shares one list); 2 waves cover a 64-row unit
   const int nh = sel_mode == SAS_SEL_HEAD ? 1 : p.hq / p.hkv;
   const bool small = std::min(tq, p.block) * nh <= 64;
 #define SAS_PF(D_, NW_, B_) \
-  return prefill_dispatch<D_, NW_, B_>(p, st, Q, qs, K, V, kvs, tq, sel_mode, idx, nsel, gate, kcap, scale, O, os, s)
+  return prefill_dispatch<D_, NW_, B_>(p, st, Q, qs, K, V, kvs, tq, sel_mode, idx, nsel, gate, kcap, scale, O, os, s, \
+                                       table, tld)
 #define SAS_PF_NW(D_, B_) \
   if (small) SAS_PF(D_, 2, B_);  \
   SAS_PF(D_, 4, B_)
