@@ -288,11 +288,24 @@ class SeqResult:
     gist_pairs: int = 0                # visible gist (row, gist) pairs over computed rows
 
 
+def joint_topk(rows: Dict[int, np.ndarray], c: int, k_total: int, sink: bool) -> Dict[int, List[int]]:
+    """Budget shared by the heads of a group ([SF] 2.3, Ada-KV: the top k x h entries over all h
+    heads, so that heads with sharper scores keep more).  Reading: the candidates of every head
+    (blocks before c, minus the forced ones) compete as (head, block) pairs ranked by (score
+    descending, head ascending, block ascending); the first k_total pairs are kept and each head's
+    list is its kept blocks plus its forced blocks, ascending."""
+    forced = {c} | ({0} if (sink and c > 0) else set())
+    pairs = [(h, j) for h in sorted(rows) for j in range(c) if j not in forced]
+    ranked = sorted(pairs, key=lambda hj: (-float(rows[hj[0]][hj[1]]), hj[0], hj[1]))
+    kept = ranked[:max(0, min(k_total, len(ranked)))]
+    return {h: sorted({j for (hh, j) in kept if hh == h} | forced) for h in rows}
+
+
 def run_sequence(Qb: np.ndarray, Kb: np.ndarray, Vb: np.ndarray, L: int, q_start: int, blk: int,
                  sel_mode: str, k_fixed: int = 0, frac_num: int = 0, frac_den: int = 0,
                  count_current: int = 0, sink: bool = False, gate: bool = False,
                  scale: Optional[float] = None, gist_k: Optional[np.ndarray] = None,
-                 coverage: float = 0.0,
+                 coverage: float = 0.0, shared: bool = False,
                  gist_v: Optional[np.ndarray] = None, mode: str = "skip",
                  unit_filter=None, attend: bool = True, reps: Optional[np.ndarray] = None,
                  explicit: Optional[Dict[Tuple[int, int], Tuple[List[int], Optional[Dict[int, float]]]]] = None
@@ -301,7 +314,10 @@ def run_sequence(Qb: np.ndarray, Kb: np.ndarray, Vb: np.ndarray, L: int, q_start
 
     Qb: [hq, rows, d] rows at positions q_start..q_start+rows-1 (decode: rows == 1 at L-1).
     Kb, Vb: [hkv, >= L, d].  gist_k/gist_v: [hkv, >= c, d] switch on gist mode (decode).
-    unit_filter(unit) -> bool restricts which units are scored/attended (others are skipped).
+    shared (per-head selection only): the G heads of a KV group at one query block share a budget
+    of G times the per-head k (joint_topk).
+    unit_filter(unit) -> bool restricts which units are attended (and, unless the budget is
+    shared, scored; a shared budget scores every head of a filtered unit's group).
     explicit[(sel_head, c)] = (sel, gate) replaces the unit's own selection (used to check the
     attention step on a list produced elsewhere when selections differ inside the tie band).
     """
@@ -313,6 +329,8 @@ def run_sequence(Qb: np.ndarray, Kb: np.ndarray, Vb: np.ndarray, L: int, q_start
     gist_mode = gist_k is not None
     if gist_mode and gate:
         raise ValueError("the log-gate is not defined for gist tokens")
+    if shared and sel_mode != "head":
+        raise ValueError("a shared budget needs per-head selection")
     if reps is None:
         if gist_mode:
             reps = np.asarray(gist_k, dtype=np.float64)
@@ -322,9 +340,14 @@ def run_sequence(Qb: np.ndarray, Kb: np.ndarray, Vb: np.ndarray, L: int, q_start
     O = np.full((hq, rows, Vb.shape[-1]), np.nan)
     pairs = 0
     gpairs = 0
-    for u in units:
-        if unit_filter is not None and not unit_filter(u):
-            continue
+    chosen = [u for u in units if unit_filter is None or unit_filter(u)]
+    if shared:
+        groups = {(kv_head_of(u, G, sel_mode), u.c) for u in chosen}
+        scored = [u for u in units if (kv_head_of(u, G, sel_mode), u.c) in groups]
+    else:
+        scored = chosen
+    # ---- scores and budgets
+    for u in scored:
         g = kv_head_of(u, G, sel_mode)
         qv = unit_query_vectors(Qb, u)
         if gist_mode:
@@ -342,8 +365,23 @@ def run_sequence(Qb: np.ndarray, Kb: np.ndarray, Vb: np.ndarray, L: int, q_start
             u.k = min(kc, budget_k(u.c, n_cand, k_fixed, frac_num, frac_den, count_current)) if capped else kc
         else:
             u.k = budget_k(u.c, n_cand, k_fixed, frac_num, frac_den, count_current)
-        u.sel = topk_blocks(s, u.c, u.k, sink)
-        u.gate = gate_values(s, u.sel) if gate else None
+    # ---- selection
+    if shared:
+        by_group: Dict[Tuple[int, int], List[Unit]] = {}
+        for u in scored:
+            by_group.setdefault((kv_head_of(u, G, sel_mode), u.c), []).append(u)
+        for (g, c), us in by_group.items():
+            lists = joint_topk({u.sel_head: u.scores for u in us}, c, sum(u.k for u in us), sink)
+            for u in us:
+                u.sel = lists[u.sel_head]
+                u.gate = gate_values(u.scores, u.sel) if gate else None
+    else:
+        for u in scored:
+            u.sel = topk_blocks(u.scores, u.c, u.k, sink)
+            u.gate = gate_values(u.scores, u.sel) if gate else None
+    # ---- attention
+    for u in chosen:
+        g = kv_head_of(u, G, sel_mode)
         sel, gv = u.sel, u.gate
         if explicit is not None and (u.sel_head, u.c) in explicit:
             sel, gv = explicit[(u.sel_head, u.c)]

@@ -456,3 +456,20 @@ def test_paged_prefill_equals_contiguous(sel, blk, d):
     torch.cuda.synchronize()
     assert torch.equal(O, Op), "paged prefill differs from the contiguous prefill"
     say(f"[paged] prefill {sel} blk {blk} d {d}: equal to the contiguous path bit for bit")
+
+
+def test_decode_and_prefill_at_the_batch_limit():
+    """64 sequences (the largest batch a call takes), ragged lengths from 1 token up, per-group and
+    per-head decode with sink and gate; then a 64-sequence prefill."""
+    rng = np.random.default_rng(77)
+    lens = [int(x) for x in rng.integers(1, 3000, size=64)]
+    w = Workload(2, overrides=dict(tag="b64", seq_lens=lens, batch=64, hq=4, hkv=2, k_fixed=3, sink=True, gate=True,
+                                   seq_len=None))
+    run_case(w, list(range(64)), unit_sample=24)
+    wh = Workload(2, overrides=dict(tag="b64h", seq_lens=lens, batch=64, hq=4, hkv=2, sel="head", k_fixed=2,
+                                    gate=True, seq_len=None))
+    run_case(wh, list(range(64)), unit_sample=24)
+    lp = [int(x) for x in rng.integers(200, 1500, size=64)]
+    wp = Workload(3, overrides=dict(tag="b64", seq_lens=lp, seq_len=None, batch=64, tq=150, hq=4, hkv=2, block=64,
+                                    frac_num=1, frac_den=4, sink=True, gate=True))
+    run_case(wp, list(range(64)), unit_sample=40)

@@ -442,3 +442,70 @@ def test_coverage_budget_in_a_sequence():
     assert all(un.k == min(2, o.coverage_k(un.scores, un.c, True, 0.6)) for un in r.units)
     r = o.run_sequence(Q, K, V, L, L - 1, blk, "group", coverage=1.0, attend=False)
     assert all(un.k == un.c for un in r.units)
+
+
+# ------------------------------------------------------------------------------------ shared budget
+def test_joint_topk_closed_forms():
+    rng = np.random.default_rng(51)
+    c = 12
+    row = rng.standard_normal(c + 1)
+    # identical rows: every head keeps the per-head top-k
+    lists = o.joint_topk({0: row, 1: row, 2: row}, c, 3 * 4, False)
+    assert all(lists[h] == o.topk_blocks(row, c, 4, False) for h in range(3))
+    # one head, or a budget of one head's k: the per-head selection
+    assert o.joint_topk({5: row}, c, 4, True)[5] == o.topk_blocks(row, c, 4, True)
+    # a head whose scores all exceed the other's takes the budget first
+    hi = row + 100.0
+    lists = o.joint_topk({0: row, 1: hi}, c, 2 * 7, False)
+    assert lists[1] == list(range(c + 1)) and lists[0] == o.topk_blocks(row, c, 2 * 7 - c, False)
+    # the budget caps at the candidate count
+    lists = o.joint_topk({0: row, 1: row}, 3, 50, True)
+    assert lists[0] == lists[1] == [0, 1, 2, 3]
+
+
+def test_joint_topk_is_a_top_set_with_planted_ties():
+    """Every kept (head, block) pair ranks above every dropped one: higher score, or an equal score
+    and a lower (head, block); forced blocks are in every list."""
+    rng = np.random.default_rng(52)
+    for trial in range(40):
+        G, c = int(rng.integers(1, 5)), int(rng.integers(1, 15))
+        rows = {h: rng.integers(-2, 3, size=c + 1).astype(float) for h in range(G)}
+        sink = bool(rng.integers(0, 2))
+        K = int(rng.integers(0, G * c + 2))
+        lists = o.joint_topk(rows, c, K, sink)
+        forced = {c} | ({0} if (sink and c > 0) else set())
+        kept = {(h, j) for h in range(G) for j in lists[h] if j not in forced}
+        cand = {(h, j) for h in range(G) for j in range(c) if j not in forced}
+        assert len(kept) == min(K, len(cand)) and all(forced <= set(lists[h]) for h in range(G))
+        for (h, j) in kept:
+            for (h2, j2) in cand - kept:
+                assert rows[h][j] > rows[h2][j2] or (rows[h][j] == rows[h2][j2] and (h, j) < (h2, j2))
+
+
+def test_shared_budget_in_a_sequence():
+    """Per-head prefill units of one query block share G * k; the lists do not depend on which
+    units are attended, and the attended output is the masked softmax of each head's list."""
+    rng = np.random.default_rng(53)
+    hq, hkv, d, blk, L, tq = 4, 2, 8, 4, 4 * 11 + 2, 9
+    Q = rng.standard_normal((hq, tq, d)); K = rng.standard_normal((hkv, L, d)); V = rng.standard_normal((hkv, L, d))
+    r = o.run_sequence(Q, K, V, L, L - tq, blk, "head", k_fixed=2, sink=True, gate=True, shared=True)
+    byg = {}
+    for u in r.units:
+        byg.setdefault((u.sel_head // 2, u.c), []).append(u)
+    for (g, c), us in byg.items():
+        lists = o.joint_topk({u.sel_head: u.scores for u in us}, c, 2 * len(us), True)
+        assert all(u.sel == lists[u.sel_head] for u in us)
+        assert sum(len(u.sel) - len({c} | ({0} if c > 0 else set())) for u in us) == min(4, 2 * max(c - 1, 0))
+    keep = {(r.units[0].sel_head, r.units[0].c)}
+    r2 = o.run_sequence(Q, K, V, L, L - tq, blk, "head", k_fixed=2, sink=True, gate=True, shared=True,
+                        unit_filter=lambda u: (u.sel_head, u.c) in keep)
+    assert r2.units[0].sel == r.units[0].sel
+    u = r.units[0]
+    h = u.heads[0]
+    pos = (L - tq) + np.arange(u.t_lo, u.t_hi)
+    keys = np.arange(L)
+    g = np.array([u.gate.get(int(k) // blk, 0.0) for k in keys])
+    allow = np.isin(keys // blk, u.sel)[None, :] & (keys[None, :] <= pos[:, None])
+    add = np.where(allow, 0.0, -np.inf) + g[None, :]
+    ref = _sdpa(Q[h, u.t_lo:u.t_hi], K[h // 2], V[h // 2], add)
+    np.testing.assert_allclose(r.O[h, u.t_lo:u.t_hi], ref, rtol=0, atol=1e-12)
