@@ -89,13 +89,20 @@ typedef struct sas_problem {
  *   the candidates' softmax mass (softmax of their scores) is >= coverage (<= 1), capped by the
  *   rule above only when k_fixed > 0 or frac_den > 0.  The shares are summed in fp32: where the
  *   exact share of the k-th candidate lies within ~1e-5 of coverage, k may differ by one from
- *   an exact evaluation. */
+ *   an exact evaluation.
+ * Shared budget ([SF] 2.3, Ada-KV: top k x h over h heads), when shared_heads = 1 (per-head
+ *   selection only, no coverage): the G query heads of a KV group at one query block share a
+ *   budget of G times the k above.  Their candidates compete as (head, block) pairs ranked by
+ *   (score descending, head ascending, block ascending); each head keeps its blocks among the
+ *   first G * k pairs, plus its forced blocks, so list lengths vary between heads (kcap from
+ *   sas_required_kcap covers min(G * k, candidates)). */
 typedef struct sas_budget {
   int32_t k_fixed;
   int32_t frac_num, frac_den, count_current;
   int32_t force_sink;       /* 1: block 0 is always kept                                    */
   int32_t gate;             /* 1: write the log-gate over the selected set                  */
   float coverage;           /* 0: off; else in (0, 1]                                        */
+  int32_t shared_heads;     /* 1: the heads of a KV group share G * k (per-head selection)     */
 } sas_budget;
 
 /* Number of query blocks tq consecutive positions can touch: ceil((tq-1)/blk) + 1. */

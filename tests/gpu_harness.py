@@ -111,6 +111,38 @@ def selection_matches(un, gsel: List[int], scores: np.ndarray, budget) -> Tuple[
     return ok, True, why
 
 
+def joint_matches(units, gpu_lists: Dict[int, List[int]], sink: bool) -> Tuple[bool, bool, str]:
+    """Shared budget: the GPU's kept (head, block) pairs over the group's heads must be the
+    oracle's, or differ only by pairs whose scores lie within TIE_REL of the K-th kept score
+    (then the lists count as inside the tie band)."""
+    c = units[0].c
+    forced = {c} | ({0} if (sink and c > 0) else set())
+    rows = {un.sel_head: un.scores for un in units}
+    ora = {(un.sel_head, j) for un in units for j in un.sel if j not in forced}
+    gpu = set()
+    for h, lst in gpu_lists.items():
+        if not forced <= set(lst) or sorted(set(lst)) != lst:
+            return False, False, f"head {h}: malformed list {lst}"
+        gpu |= {(h, j) for j in lst if j not in forced}
+    if gpu == ora:
+        return True, False, ""
+    if len(gpu) != len(ora):
+        return False, False, f"{len(gpu)} pairs kept, the oracle keeps {len(ora)}"
+    cand = [(h, j) for h in rows for j in range(c) if j not in forced]
+    ranked = sorted(cand, key=lambda hj: (-float(rows[hj[0]][hj[1]]), hj[0], hj[1]))
+    K = len(ora)
+    if K == 0 or K >= len(ranked):
+        return False, False, "pairs differ with no choice to make"
+    sk, sk1 = float(rows[ranked[K - 1][0]][ranked[K - 1][1]]), float(rows[ranked[K][0]][ranked[K][1]])
+    band = TIE_REL * max(abs(sk), abs(sk1))
+    if abs(sk - sk1) >= band:
+        return False, False, f"K-th/K+1-th gap {abs(sk - sk1):.3e} >= band {band:.3e}"
+    allowed = {hj for hj in cand if abs(float(rows[hj[0]][hj[1]]) - sk) <= band}
+    if not (gpu ^ ora) <= allowed:
+        return False, True, "pairs differ outside the tie band"
+    return True, True, ""
+
+
 def out_check(rep: Report, gpu: np.ndarray, ref: np.ndarray, bf16: bool) -> None:
     d = np.abs(gpu.astype(np.float64) - ref)
     assert np.isfinite(gpu).all(), "non-finite GPU output"
@@ -134,7 +166,7 @@ def sel_count(w: Workload) -> int:
 def budget_of(w: Workload) -> sas.Budget:
     return sas.Budget(k_fixed=w.k_fixed, frac_num=w.frac_num, frac_den=w.frac_den,
                       count_current=w.count_current, sink=w.sink, gate=w.gate,
-                      coverage=float(w.spec.get("coverage", 0.0)))
+                      coverage=float(w.spec.get("coverage", 0.0)), shared=bool(w.spec.get("shared", False)))
 
 
 def run_case(w: Workload, seqs: List[int], unit_sample: Optional[int] = None, seed: int = 0,
@@ -173,7 +205,7 @@ def run_case(w: Workload, seqs: List[int], unit_sample: Optional[int] = None, se
                                          gist=gist, kcap=idx.shape[1])
         torch.cuda.synchronize()
         fused = (i2.cpu().numpy(), n2.cpu().numpy())
-    elif decode and max((L - 1) // w.block for L in lens) <= 2048:
+    elif decode and max((L - 1) // w.block for L in lens) <= 2048 and not (budget.shared and w.group > 4):
         # the fused decode selection must give the same scores, lists and gates as the two calls
         s2, i2, n2, g2 = sas.select_decode(inp.Q, reps, lens, w.block, w.hkv, Lmax, budget, sel_mode=w.sel,
                                            gist=gist, kcap=idx.shape[1])
@@ -218,13 +250,30 @@ def run_case(w: Workload, seqs: List[int], unit_sample: Optional[int] = None, se
         r = orc.run_sequence(Qb, hst["k"], hst["v"], L, q0, w.block, w.sel, k_fixed=budget.k_fixed,
                              frac_num=budget.frac_num, frac_den=budget.frac_den,
                              count_current=budget.count_current, sink=budget.sink, gate=budget.gate,
-                             gist_k=gk, gist_v=gv, unit_filter=filt, attend=False, coverage=budget.coverage)
+                             gist_k=gk, gist_v=gv, unit_filter=filt, attend=False, coverage=budget.coverage,
+                             shared=budget.shared)
         if not gist:
             nb = orc.num_blocks(L, w.block)
             dr = np.abs(reps_h[bi, :, :nb] - r.reps)
             rep.reps_max_abs = max(rep.reps_max_abs, float(dr.max()))
             assert dr.max() <= 1e-5 * (1.0 + np.abs(r.reps).max()), f"reps differ by {dr.max():.3e}"
         explicit = {}
+        band_units = set()
+        if budget.shared:
+            # a shared budget is checked per group: the kept (head, block) pairs of the G heads
+            groups = {}
+            for un in r.units:
+                if un.scores is not None:
+                    groups.setdefault((un.sel_head // w.group, un.c), []).append(un)
+            for (g, c), us in groups.items():
+                gl = {}
+                for un in us:
+                    u = (bi * S + un.sel_head) * QB + (un.c - q0 // w.block)
+                    gl[un.sel_head] = [int(x) for x in idx_h[u, :int(nsel_h[u])]]
+                ok, band, why = joint_matches(us, gl, budget.sink)
+                assert ok, f"sequence {b}, KV head {g}, block {c}: {why}"
+                if band:
+                    band_units |= {(un.sel_head, un.c) for un in us}
         for un in r.units:
             if un.scores is None:
                 continue
@@ -242,7 +291,12 @@ def run_case(w: Workload, seqs: List[int], unit_sample: Optional[int] = None, se
             n = int(nsel_h[u])
             gsel = [int(x) for x in idx_h[u, :n]]
             assert all(int(x) == -1 for x in idx_h[u, n:]), f"unit {u}: padding is not -1"
-            ok, tie, why = selection_matches(un, gsel, s_or, budget)
+            if budget.shared:
+                ok, tie, why = True, (un.sel_head, un.c) in band_units, ""
+                if not tie:
+                    assert gsel == list(un.sel), f"unit {u}: {gsel} != {un.sel}"
+            else:
+                ok, tie, why = selection_matches(un, gsel, s_or, budget)
             assert ok, f"unit {u} (head {un.sel_head}, block {un.c}): {why}"
             if fused is not None:
                 fs = [int(x) for x in fused[0][u, :fused[1][u]]]
@@ -263,7 +317,7 @@ def run_case(w: Workload, seqs: List[int], unit_sample: Optional[int] = None, se
                               frac_num=budget.frac_num, frac_den=budget.frac_den,
                               count_current=budget.count_current, sink=budget.sink, gate=budget.gate,
                               gist_k=gk, gist_v=gv, unit_filter=filt, reps=r.reps, explicit=explicit,
-                              coverage=budget.coverage)
+                              coverage=budget.coverage, shared=budget.shared)
         mask = ~np.isnan(r2.O[:, :, 0])
         gpu_rows = O_h[bi] if not decode else O_h[bi][:, None, :]
         out_check(rep, gpu_rows[mask], r2.O[mask], bf16)

@@ -272,3 +272,27 @@ def test_paged_prefill_validation_codes():
     assert pf(q_start=None) == _lib.SAS_ERR_NULL
     assert pf(ld=10) == _lib.SAS_ERR_SHAPE
     assert pf(tq=200) == _lib.SAS_ERR_SHAPE            # q_start + tq > L for the second sequence
+
+
+def test_shared_budget_validation():
+    lib = _lib.load()
+    p, a = _problem(hq=16, hkv=2, lens=(5000, 700), max_len=5000)
+    bad = _lib.Budget(4, 0, 0, 0, 0, 0, 0.0, 2)
+    assert lib.sas_required_kcap(C.byref(p), 1, None, C.byref(bad)) == _lib.SAS_ERR_SHAPE
+    both = _lib.Budget(4, 0, 0, 0, 0, 0, 0.5, 1)
+    assert lib.sas_required_kcap(C.byref(p), 1, None, C.byref(both)) == _lib.SAS_ERR_UNSUPPORTED
+    sh = _lib.Budget(4, 0, 0, 0, 1, 0, 0.0, 1)
+    # 8 heads per KV head share 8 x 4: a list may hold min(32, candidates) + current + sink
+    assert lib.sas_required_kcap(C.byref(p), 1, None, C.byref(sh)) == 32 + 2
+    p2, a2 = _problem(hq=16, hkv=2, lens=(1000, 700))
+    assert lib.sas_required_kcap(C.byref(p2), 1, None, C.byref(sh)) == 14 + 2   # capped: 14 candidates
+    q2 = _lib.i64x([16 * 128, 128])
+    r3 = _lib.i64x([2 * 16 * 128, 16 * 128, 128])
+    ws = C.c_size_t(1 << 20)
+    # the fused selection takes at most 4 heads per KV head when they share a budget
+    assert lib.sas_select_decode(C.byref(p), FAKE, q2, FAKE, _lib.SAS_REPS_POOLED, r3, _lib.SAS_SEL_HEAD, 0.0,
+                                 C.byref(sh), 40, FAKE, 16, FAKE, FAKE, None, FAKE, ws, None) == \
+        _lib.SAS_ERR_UNSUPPORTED
+    # per-group selection cannot share a budget
+    assert lib.sas_select_decode(C.byref(p), FAKE, q2, FAKE, _lib.SAS_REPS_POOLED, r3, _lib.SAS_SEL_GROUP, 0.0,
+                                 C.byref(sh), 40, FAKE, 16, FAKE, FAKE, None, FAKE, ws, None) == _lib.SAS_ERR_SHAPE

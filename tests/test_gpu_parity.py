@@ -473,3 +473,22 @@ def test_decode_and_prefill_at_the_batch_limit():
     wp = Workload(3, overrides=dict(tag="b64", seq_lens=lp, seq_len=None, batch=64, tq=150, hq=4, hkv=2, block=64,
                                     frac_num=1, frac_den=4, sink=True, gate=True))
     run_case(wp, list(range(64)), unit_sample=40)
+
+
+# ------------------------------------------------------------------------------ shared budgets
+def test_shared_budget_decode():
+    """Per-head decode units whose 4 heads share 4 k: fused selection (one head per wave, one and
+    four registers of candidates) and the two-call selection must agree with the oracle; then 8
+    heads per KV head through the two-call path only."""
+    w = Workload(2, overrides=dict(tag="sh4", seq_lens=[5000, 300, 40000, 12000], batch=4, sel="head", hq=8, hkv=2,
+                                   k_fixed=6, sink=True, gate=True, shared=True, seq_len=None))
+    run_case(w, list(range(4)))
+    w8 = Workload(2, overrides=dict(tag="sh8", seq_lens=[7000, 2000], batch=2, sel="head", hq=16, hkv=2, k_fixed=3,
+                                    gate=True, shared=True, seq_len=None))
+    run_case(w8, [0, 1])
+
+
+def test_shared_budget_prefill():
+    w = Workload(3, overrides=dict(tag="sh", seq_len=3000, tq=800, hq=8, hkv=2, block=64, sel="head", frac_num=1,
+                                   frac_den=8, sink=True, gate=True, shared=True))
+    run_case(w, [0])

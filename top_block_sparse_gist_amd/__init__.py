@@ -40,10 +40,11 @@ class Budget:
     sink: bool = False
     gate: bool = False
     coverage: float = 0.0
+    shared: bool = False
 
     def c_struct(self) -> _lib.Budget:
         return _lib.Budget(self.k_fixed, self.frac_num, self.frac_den, self.count_current,
-                           int(bool(self.sink)), int(bool(self.gate)), float(self.coverage))
+                           int(bool(self.sink)), int(bool(self.gate)), float(self.coverage), int(bool(self.shared)))
 
 
 def sel_code(sel_mode) -> int:

@@ -96,6 +96,9 @@ sas_status check_budget(const sas_budget *bg) {
   if (bg->count_current != 0 && bg->count_current != 1)
     return fail(SAS_ERR_SHAPE, "count_current must be 0 or 1");
   if (!(bg->coverage >= 0.f && bg->coverage <= 1.f)) return fail(SAS_ERR_SHAPE, "coverage must be in [0, 1]");
+  if (bg->shared_heads != 0 && bg->shared_heads != 1) return fail(SAS_ERR_SHAPE, "shared_heads must be 0 or 1");
+  if (bg->shared_heads && bg->coverage > 0.f)
+    return fail(SAS_ERR_UNSUPPORTED, "a shared budget with a coverage budget is not defined here");
   return SAS_OK;
 }
 
@@ -103,7 +106,8 @@ float resolve_scale(float scale, int d) { return scale == 0.f ? 1.f / sqrtf((flo
 
 int32_t required_kcap(const sas_problem *p, int32_t tq, const int32_t *q_start, const sas_budget *bg) {
   Budget b{bg->k_fixed, bg->frac_num, bg->frac_den, bg->count_current, bg->force_sink ? 1 : 0, bg->gate,
-           bg->coverage};
+           bg->coverage, bg->shared_heads};
+  const int G = p->hq / p->hkv;
   int32_t need = 1;
   for (int s = 0; s < p->batch; ++s) {
     const int L = p->seq_lens[s];
@@ -112,7 +116,9 @@ int32_t required_kcap(const sas_problem *p, int32_t tq, const int32_t *q_start, 
     for (int c = lo_pos / p->block; c <= hi_pos / p->block; ++c) {
       const bool sink = b.sink && c > 0;
       const int ncand = c - (sink ? 1 : 0);
-      const int n = budget_k(b, c, ncand) + 1 + (sink ? 1 : 0);
+      // a shared budget may give one head up to G times its own k
+      const int k = b.shared ? std::min(G * budget_k(b, c, ncand), ncand) : budget_k(b, c, ncand);
+      const int n = k + 1 + (sink ? 1 : 0);
       need = std::max(need, n);
     }
   }
@@ -225,6 +231,8 @@ sas_status sas_topk_select(const sas_problem *p, const float *scores, int64_t sc
   if ((st = check_rows(p, tq, q_start, &tab)) != SAS_OK) return st;
   if ((st = check_sel(sel_mode)) != SAS_OK) return st;
   if ((st = check_budget(budget)) != SAS_OK) return st;
+  if (budget->shared_heads && sel_mode != SAS_SEL_HEAD)
+    return fail(SAS_ERR_SHAPE, "a shared budget needs per-head selection");
   if (!scores || !idx || !nsel) return fail(SAS_ERR_NULL, "scores, idx or nsel is NULL");
   if (budget->gate && !gate) return fail(SAS_ERR_NULL, "budget->gate is set but gate is NULL");
   int nbmax = 0;
@@ -233,7 +241,7 @@ sas_status sas_topk_select(const sas_problem *p, const float *scores, int64_t sc
   const int32_t need = required_kcap(p, tq, q_start, budget);
   if (kcap < need) return fail(SAS_ERR_SHAPE, "kcap %d < %d selected blocks", kcap, need);
   Budget bg{budget->k_fixed, budget->frac_num, budget->frac_den, budget->count_current,
-            budget->force_sink ? 1 : 0, budget->gate ? 1 : 0, budget->coverage};
+            budget->force_sink ? 1 : 0, budget->gate ? 1 : 0, budget->coverage, budget->shared_heads ? 1 : 0};
   return hip_status(launch_topk(*p, tab, scores, scores_ld, tq, sel_mode, bg, kcap, idx, nsel,
                                 budget->gate ? gate : nullptr, (hipStream_t)stream),
                     "sas_topk_select");
@@ -285,6 +293,11 @@ sas_status sas_select_decode(const sas_problem *p, const void *Q, const int64_t 
   if ((st = check_problem(p, &tab)) != SAS_OK) return st;
   if ((st = check_sel(sel_mode)) != SAS_OK) return st;
   if ((st = check_budget(budget)) != SAS_OK) return st;
+  if (budget->shared_heads && sel_mode != SAS_SEL_HEAD)
+    return fail(SAS_ERR_SHAPE, "a shared budget needs per-head selection");
+  if (budget->shared_heads && p->hq / p->hkv > 4)
+    return fail(SAS_ERR_UNSUPPORTED, "the fused selection shares a budget over at most 4 heads per KV head; "
+                "use sas_block_scores + sas_topk_select");
   if (!Q || !q_stride || !reps || !rep_stride || !scores || !idx || !nsel)
     return fail(SAS_ERR_NULL, "a required pointer is NULL");
   if (budget->gate && !gate) return fail(SAS_ERR_NULL, "budget->gate is set but gate is NULL");
@@ -313,7 +326,7 @@ sas_status sas_select_decode(const sas_problem *p, const void *Q, const int64_t 
     return fail(SAS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", wneed, workspace_bytes);
   if (!aligned16(workspace)) return fail(SAS_ERR_SHAPE, "workspace must be 16-byte aligned");
   Budget bg{budget->k_fixed, budget->frac_num, budget->frac_den, budget->count_current,
-            budget->force_sink ? 1 : 0, budget->gate ? 1 : 0, budget->coverage};
+            budget->force_sink ? 1 : 0, budget->gate ? 1 : 0, budget->coverage, budget->shared_heads ? 1 : 0};
   const int64_t qs3[3] = {q_stride[0], q_stride[1], 0};
   return hip_status(launch_select_decode(*p, tab, Q, qs3, reps, reps_kind, rep_stride, sel_mode,
                                          resolve_scale(scale, p->head_dim), scores, scores_ld, bg, kcap, idx, nsel,

@@ -18,7 +18,8 @@ struct SeqTable {
 
 struct Budget {
   int32_t k_fixed, frac_num, frac_den, count_current, sink, gate;
-  float coverage;  // 0: off (see coverage_k in the top-k bodies)
+  float coverage;  // 0: off (see coverage_count in the top-k bodies)
+  int32_t shared;  // 1: the G heads of a KV group share G * k (per-head selection)
 };
 
 // ---------------------------------------------------------------------------------------

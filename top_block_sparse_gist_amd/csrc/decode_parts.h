@@ -139,23 +139,31 @@ __device__ uint32_t coverage_count(const uint32_t (&key)[NPL], float cov, const 
   return n_gt + take;
 }
 
+// Top-k modes: plain, coverage budget, shared budget (the heads of a KV group, one per wave).
+enum { TK_PLAIN = 0, TK_COVERAGE = 1, TK_SHARED = 2 };
+
 // Top-k of one unit's scores row[0..c] by a team of waves: wave w of the team holds blocks
 // 64 * NPL * w + lane + 64r in its register r (the scores are read back from memory, where the
 // unit's tiles left them).  Ties go to the lower block.
-template <int NPL, typename Team, bool COV = false>
+// TK_SHARED: wave w < nact holds all of head w's row (its own unit: row, out, nsel_out, gout) and
+// the nact heads select together, G * k (head, block) pairs ranked by (key, head, block); each
+// wave then writes its head's list, forced blocks and gate (the other waves hold no candidate).
+template <int NPL, typename Team, int TK = TK_PLAIN>
 __device__ void team_topk(const float *__restrict__ row, int c, bool sinkf, const Budget &bg, int kcap,
                           int32_t *__restrict__ out, int32_t *__restrict__ nsel_out, float *__restrict__ gout,
-                          const Team &team) {
+                          const Team &team, int nact = 1) {
   static_assert(NPL <= 32, "one selection bit per register in a 32-bit mask");
+  constexpr bool COV = TK == TK_COVERAGE, JOINT = TK == TK_SHARED;
   // opaque per call: keeps the compiler from hoisting the per-register block numbers and masks out
   // of a caller's loop over units, where they would hold ~100 registers across the whole kernel
   int lane = threadIdx.x & 63;
   asm volatile("" : "+v"(lane));
-  const int jw = 64 * NPL * team.rank();  // this wave's first block
+  const int jw = JOINT ? 0 : 64 * NPL * team.rank();  // this wave's first block
+  const bool act = !JOINT || team.rank() < nact;     // the wave holds candidates
   const bool sink = sinkf && c > 0;
   const int lo = sink ? 1 : 0;
-  const int ncand = c - lo;
-  int k = budget_k(bg, c, ncand);
+  const int ncand = JOINT ? nact * (c - lo) : c - lo;  // over the whole team
+  int k = JOINT ? min(nact * budget_k(bg, c, c - lo), ncand) : budget_k(bg, c, ncand);
   const int base = sink ? 1 : 0;
   // order-preserving keys of the candidates, 0 elsewhere: a candidate's key is never 0 (that is
   // the key of one NaN pattern only, and NaN scores are not ranked)
@@ -164,11 +172,11 @@ __device__ void team_topk(const float *__restrict__ row, int c, bool sinkf, cons
   for (int r = 0; r < NPL; ++r) {
     // every lane loads (entries up to c exist), so the loads issue back to back
     const int j = jw + lane + 64 * r;
-    const float s = load_dev(row + min(j, c));
-    key[r] = (j >= lo && j < c) ? max(float_order_key(s), 1u) : 0u;
+    const float s = act ? load_dev(row + min(j, c)) : 0.f;
+    key[r] = (act && j >= lo && j < c) ? max(float_order_key(s), 1u) : 0u;
   }
-  const float s_c = load_dev(row + c);
-  const float s_0 = load_dev(row);
+  const float s_c = act ? load_dev(row + c) : 0.f;
+  const float s_0 = act ? load_dev(row) : 0.f;
   auto count = [&](uint32_t t) { return team.sum(count_ge(key, t)); };
   if constexpr (COV) {  // compiled only into the launches that carry a coverage budget
     if (bg.coverage > 0.f && k > 0) k = min(k, (int)coverage_count(key, bg.coverage, team));
@@ -287,7 +295,7 @@ __device__ void team_topk(const float *__restrict__ row, int c, bool sinkf, cons
     for (int r = 0; r < NPL; ++r) mx = fmaxf(mx, ((selbits >> r) & 1u) ? order_key_float(key[r]) : -INFINITY);
     mx = fmaxf(mx, s_c);
     if (sink) mx = fmaxf(mx, s_0);
-    mx = team.fmax(wave_max(mx));
+    mx = JOINT ? wave_max(mx) : team.fmax(wave_max(mx));  // shared: each head's own set
     // exp(x - mx) as 2^((x - mx) log2 e): one v_exp_f32 each; terms that flush to 0 are below the
     // largest (1) by more than the float's precision
     constexpr float L2E = 1.4426950408889634f;
@@ -297,7 +305,7 @@ __device__ void team_topk(const float *__restrict__ row, int c, bool sinkf, cons
       const float e = __builtin_amdgcn_exp2f((order_key_float(key[r]) - mx) * L2E);
       sm += ((selbits >> r) & 1u) ? e : 0.f;
     }
-    sm = team.fsum(wave_sum(sm));
+    sm = JOINT ? wave_sum(sm) : team.fsum(wave_sum(sm));
     sm += __builtin_amdgcn_exp2f((s_c - mx) * L2E);
     if (sink) sm += __builtin_amdgcn_exp2f((s_0 - mx) * L2E);
     lse = mx + logf(sm);
@@ -306,7 +314,7 @@ __device__ void team_topk(const float *__restrict__ row, int c, bool sinkf, cons
   uint32_t sel_w = 0;
 #pragma unroll
   for (int r = 0; r < NPL; ++r) sel_w += (uint32_t)__popcll(__ballot((selbits >> r) & 1u));
-  uint32_t pos_run = team.before(sel_w);
+  uint32_t pos_run = JOINT ? 0u : team.before(sel_w);  // shared: each head its own list
 #pragma unroll
   for (int r = 0; r < NPL; ++r) {
     const bool sel = (selbits >> r) & 1u;
@@ -318,19 +326,28 @@ __device__ void team_topk(const float *__restrict__ row, int c, bool sinkf, cons
       if (gout) gout[base + pos] = order_key_float(key[r]) - lse;
     }
   }
-  const int n = base + k + 1;
-  if (team.rank() == 0 && lane == 0) {
+  const int kw = JOINT ? (int)sel_w : k;  // blocks this list keeps besides the forced ones
+  const int n = base + kw + 1;
+  if ((JOINT ? act : team.rank() == 0) && lane == 0) {
     if (sink) {
       out[0] = 0;
       if (gout) gout[0] = s_0 - lse;
     }
-    out[base + k] = c;
-    if (gout) gout[base + k] = s_c - lse;
+    out[base + kw] = c;
+    if (gout) gout[base + kw] = s_c - lse;
     *nsel_out = n;
   }
-  for (int p = n + 64 * team.rank() + lane; p < kcap; p += 64 * Team::SIZE) {
-    out[p] = -1;
-    if (gout) gout[p] = 0.f;
+  if (JOINT) {
+    if (act)
+      for (int p = n + lane; p < kcap; p += 64) {
+        out[p] = -1;
+        if (gout) gout[p] = 0.f;
+      }
+  } else {
+    for (int p = n + 64 * team.rank() + lane; p < kcap; p += 64 * Team::SIZE) {
+      out[p] = -1;
+      if (gout) gout[p] = 0.f;
+    }
   }
 }
 
@@ -351,7 +368,7 @@ __host__ __device__ inline int select_tiles(int c, int gist) { return gist ? max
 
 // One selection workgroup: the 64-block tile bx of (sequence b, KV head g), hkv KV heads.  The last
 // tile of (b, g) to arrive runs the top-k of its units.
-template <typename T, typename R, int D, int NPL, bool COV>
+template <typename T, typename R, int D, int NPL, int TK>
 __device__ __forceinline__ void select_tile_body(
     int bx, int g, int b, int hkv, unsigned char *lds, SeqTable st, const T *__restrict__ Q, int64_t qb, int64_t qh,
     const R *__restrict__ reps, int64_t rb, int64_t rh, int64_t rj, int gist, int blk, int S, int G, int per_head,
@@ -468,18 +485,24 @@ __device__ __forceinline__ void select_tile_body(
   __syncthreads();
   if (!last_sh) return;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (NPL == 32 && nU == 1) {
+  if (TK == TK_SHARED) {
+    // per-head units sharing G * k: wave w holds head w's row (G <= 4, checked on the host)
+    const GroupTeam team{reinterpret_cast<uint32_t *>(lds + Lds::QS), wave, 0};
+    const int64_t urow = (int64_t)b * S + g * G + min(wave, G - 1);
+    team_topk<NPL, GroupTeam, TK_SHARED>(scores + urow * ld, c, bg.sink != 0, bg, kcap, idx + urow * kcap,
+                                         nsel + urow, bg.gate ? gate + urow * kcap : nullptr, team, G);
+  } else if (NPL == 32 && nU == 1) {
     // one unit with up to 2048 candidates: the 4 waves share them (8 registers per lane each),
     // combining their counts through LDS (the pooled queries' region, no longer read)
     const int64_t urow = (int64_t)b * S + (per_head ? g * G : g);
     const GroupTeam team{reinterpret_cast<uint32_t *>(lds + Lds::QS), wave, 0};
-    team_topk<NPL / 4, GroupTeam, COV>(scores + urow * ld, c, bg.sink != 0, bg, kcap, idx + urow * kcap, nsel + urow,
+    team_topk<NPL / 4, GroupTeam, TK>(scores + urow * ld, c, bg.sink != 0, bg, kcap, idx + urow * kcap, nsel + urow,
                        bg.gate ? gate + urow * kcap : nullptr, team);
   } else {
     for (int u = wave; u < nU; u += 4) {
       const int s = per_head ? g * G + u : g;
       const int64_t urow = (int64_t)b * S + s;
-      team_topk<NPL, SoloTeam, COV>(scores + urow * ld, c, bg.sink != 0, bg, kcap, idx + urow * kcap, nsel + urow,
+      team_topk<NPL, SoloTeam, TK>(scores + urow * ld, c, bg.sink != 0, bg, kcap, idx + urow * kcap, nsel + urow,
                      bg.gate ? gate + urow * kcap : nullptr, SoloTeam{});
     }
   }

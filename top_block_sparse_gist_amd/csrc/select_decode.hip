@@ -31,7 +31,7 @@ struct SelGrid {
 
 // At most 128 VGPRs (4 workgroups per CU): the top-k's 32 registers per lane of keys would
 // otherwise set the register count, and the occupancy, of every tile workgroup.
-template <typename T, typename R, int D, int NPL, bool COV>
+template <typename T, typename R, int D, int NPL, int TK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void select_decode_kernel(
     SeqTable st, SelGrid sg, const T *__restrict__ Q, int64_t qb, int64_t qh, const R *__restrict__ reps,
     int64_t rb, int64_t rh, int64_t rj, int gist, int blk, int hkv, int S, int G, int per_head, float scale,
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     else hi = mid - 1;
   }
   const int rem = id - sg.first[lo];
-  select_tile_body<T, R, D, NPL, COV>(rem / hkv, rem % hkv, sg.b[lo], hkv, lds, st, Q, qb, qh, reps, rb, rh, rj,
+  select_tile_body<T, R, D, NPL, TK>(rem / hkv, rem % hkv, sg.b[lo], hkv, lds, st, Q, qb, qh, reps, rb, rh, rj,
                                  gist, blk, S, G, per_head, scale, scores, ld, bg, kcap, idx, nsel, gate,
                                  counters);
 }
@@ -70,18 +70,20 @@ static hipError_t sel_dispatch(const sas_problem &p, const SeqTable &st, const v
     sg.first[i + 1] = sg.first[i] + ntile * p.hkv;
   }
   const dim3 grid((unsigned)sg.first[p.batch]);
-#define SAS_SEL_LAUNCH(NPL_, COV_)                                                                          \
-  hipLaunchKernelGGL((select_decode_kernel<T, R, D, NPL_, COV_>), grid, dim3(256), 0, s, st, sg, (const T *)Q, \
+#define SAS_SEL_LAUNCH(NPL_, TK_)                                                                          \
+  hipLaunchKernelGGL((select_decode_kernel<T, R, D, NPL_, TK_>), grid, dim3(256), 0, s, st, sg, (const T *)Q, \
                      qs[0], qs[1], (const R *)reps, rs[0], rs[1], rs[2], gist, p.block, p.hkv, S, p.hq / p.hkv, \
                      per_head, scale, scores, ld, bg, kcap, idx, nsel, gate, counters)
-  // coverage budgets get their own kernels, so that the others carry none of that code
-  const bool cov = bg.coverage > 0.f;
+  // coverage and shared budgets get kernels of their own, so that the others carry none of that code
+  const int tk = bg.shared ? TK_SHARED : bg.coverage > 0.f ? TK_COVERAGE : TK_PLAIN;
   if (maxc <= 512) {
-    if (cov) SAS_SEL_LAUNCH(8, true);
-    else SAS_SEL_LAUNCH(8, false);
+    if (tk == TK_SHARED) SAS_SEL_LAUNCH(8, TK_SHARED);
+    else if (tk == TK_COVERAGE) SAS_SEL_LAUNCH(8, TK_COVERAGE);
+    else SAS_SEL_LAUNCH(8, TK_PLAIN);
   } else {
-    if (cov) SAS_SEL_LAUNCH(32, true);
-    else SAS_SEL_LAUNCH(32, false);
+    if (tk == TK_SHARED) SAS_SEL_LAUNCH(32, TK_SHARED);
+    else if (tk == TK_COVERAGE) SAS_SEL_LAUNCH(32, TK_COVERAGE);
+    else SAS_SEL_LAUNCH(32, TK_PLAIN);
   }
 #undef SAS_SEL_LAUNCH
   return hipGetLastError();

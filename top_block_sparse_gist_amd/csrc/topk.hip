@@ -225,10 +225,158 @@ __global__ __launch_bounds__(256) void topk_kernel(SeqTable st, const float *__r
   }
 }
 
+// Shared budget (per-head units): one workgroup per (sequence, KV head, query block) selects for
+// the G heads of the group together.  Their candidates compete as (head, block) pairs, candidate
+// e = h * ncand + (j - lo); the radix select finds the K-th largest key over all of them (K = G
+// times the per-head k); then each head's list is compacted in block order, the ranks of keys
+// equal to T carried from head to head, which takes tied pairs in (head, block) order.
+__global__ __launch_bounds__(256) void topk_joint_kernel(SeqTable st, const float *__restrict__ scores,
+                                                         int64_t ld, int tq, int blk, int G, int hkv, int QB,
+                                                         Budget bg, int kcap, int32_t *__restrict__ idx,
+                                                         int32_t *__restrict__ nsel, float *__restrict__ gate) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sh_digit, sh_above;
+  __shared__ uint32_t scan_sh[4];
+  __shared__ float red_sh[4];
+
+  const int64_t wgi = blockIdx.x;
+  const int i = (int)(wgi % QB);
+  const int g = (int)(wgi / QB) % hkv;
+  const int b = (int)(wgi / QB) / hkv;
+  const int S = hkv * G;
+  const int tid = threadIdx.x;
+  auto unit = [&](int h) { return ((int64_t)b * S + g * G + h) * QB + i; };
+  const int q0 = st.q0[b];
+  const int c0 = q0 / blk;
+  const int nqb = (q0 + tq - 1) / blk - c0 + 1;
+  if (i >= nqb) {
+    for (int h = 0; h < G; ++h) {
+      for (int p = tid; p < kcap; p += 256) {
+        idx[unit(h) * kcap + p] = -1;
+        if (bg.gate) gate[unit(h) * kcap + p] = 0.f;
+      }
+      if (tid == 0) nsel[unit(h)] = 0;
+    }
+    return;
+  }
+  const int c = c0 + i;
+  const bool sink = bg.sink && c > 0;
+  const int lo = sink ? 1 : 0;
+  const int ncand = c - lo;
+  const int base = sink ? 1 : 0;
+  const int n_all = G * ncand;
+  const int K = min(G * budget_k(bg, c, ncand), n_all);
+  auto key_of = [&](int e) {
+    const int h = e / ncand;
+    return float_order_key(scores[unit(h) * ld + lo + (e - h * ncand)]);
+  };
+  uint32_t T = 0u, want = 0u;
+  const bool all = K >= n_all;
+  if (!all && K > 0) {
+    uint32_t prefix = 0u, pmask = 0u;
+    want = (uint32_t)K;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      hist[tid] = 0u;
+      __syncthreads();
+      for (int e = tid; e < n_all; e += 256) {
+        const uint32_t key = key_of(e);
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid < 64) {
+        uint32_t cnt[4], tot = 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          cnt[t] = hist[255 - 4 * tid - t];
+          tot += cnt[t];
+        }
+        uint32_t incl = tot;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          uint32_t v = __shfl_up(incl, o, 64);
+          if (tid >= o) incl += v;
+        }
+        const uint32_t excl = incl - tot;
+        if (excl < want && want <= incl) {
+          uint32_t run = excl;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            if (run + cnt[t] >= want) {
+              sh_digit = (uint32_t)(255 - 4 * tid - t);
+              sh_above = run;
+              break;
+            }
+            run += cnt[t];
+          }
+        }
+      }
+      __syncthreads();
+      want -= sh_above;
+      prefix |= sh_digit << shift;
+      pmask |= 255u << shift;
+      __syncthreads();
+    }
+    T = prefix;
+  }
+  // ---- per head: compaction in block order (ranks of T carried across heads), forced blocks, gate
+  uint32_t eq_seen = 0;
+  for (int h = 0; h < G; ++h) {
+    const float *row = scores + unit(h) * ld;
+    int32_t *out = idx + unit(h) * kcap;
+    float *gout = bg.gate ? gate + unit(h) * kcap : nullptr;
+    uint32_t pos_run = 0;
+    if (K > 0) {
+      for (int j0 = lo; j0 < c; j0 += 256) {
+        const int j = j0 + tid;
+        const bool valid = j < c;
+        const uint32_t key = valid ? float_order_key(row[j]) : 0u;
+        const bool gt = valid && (all || key > T);
+        const bool eq = valid && !all && key == T;
+        uint32_t eq_tot, sel_tot;
+        const uint32_t eq_rank = block_scan_flag(eq, scan_sh, eq_tot) + eq_seen;
+        const bool sel = gt || (eq && eq_rank < want);
+        const uint32_t pos = block_scan_flag(sel, scan_sh, sel_tot) + pos_run;
+        if (sel) out[base + pos] = j;
+        eq_seen += eq_tot;
+        pos_run += sel_tot;
+      }
+    }
+    const int n = base + (int)pos_run + 1;
+    if (tid == 0) {
+      if (sink) out[0] = 0;
+      out[base + pos_run] = c;
+      nsel[unit(h)] = n;
+    }
+    for (int p = n + tid; p < kcap; p += 256) {
+      out[p] = -1;
+      if (gout) gout[p] = 0.f;
+    }
+    if (gout) {
+      __syncthreads();  // the list written above is read back below by other lanes
+      float mx = -INFINITY;
+      for (int p = tid; p < n; p += 256) mx = fmaxf(mx, row[out[p]]);
+      mx = block_reduce_max(mx, red_sh);
+      float sm = 0.f;
+      for (int p = tid; p < n; p += 256) sm += expf(row[out[p]] - mx);
+      sm = block_reduce_sum(sm, red_sh);
+      const float lse = mx + logf(sm);
+      for (int p = tid; p < n; p += 256) gout[p] = row[out[p]] - lse;
+    }
+    __syncthreads();  // scan_sh and red_sh are reused by the next head
+  }
+}
+
 hipError_t launch_topk(const sas_problem &p, const SeqTable &st, const float *scores, int64_t ld,
                        int32_t tq, int32_t sel_mode, const Budget &bg, int32_t kcap, int32_t *idx,
                        int32_t *nsel, float *gate, hipStream_t s) {
   const int QB = num_qblocks(tq, p.block);
+  if (bg.shared) {
+    const int64_t groups = (int64_t)p.batch * p.hkv * QB;
+    hipLaunchKernelGGL(topk_joint_kernel, dim3((unsigned)groups), dim3(256), 0, s, st, scores, ld, tq, p.block,
+                       p.hq / p.hkv, p.hkv, QB, bg, kcap, idx, nsel, gate);
+    return hipGetLastError();
+  }
   const int S = sel_mode == SAS_SEL_HEAD ? p.hq : p.hkv;
   const int64_t units = (int64_t)p.batch * S * QB;
   hipLaunchKernelGGL(topk_kernel, dim3((unsigned)units), dim3(256), 0, s, st, scores, ld, tq, p.block, S,
