@@ -509,3 +509,83 @@ def test_shared_budget_in_a_sequence():
     add = np.where(allow, 0.0, -np.inf) + g[None, :]
     ref = _sdpa(Q[h, u.t_lo:u.t_hi], K[h // 2], V[h // 2], add)
     np.testing.assert_allclose(r.O[h, u.t_lo:u.t_hi], ref, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------------------------ backward
+def _loss_numpy(Q, K, V, dO, L, q0, blk, sel_mode, explicit, gate):
+    r = o.run_sequence(Q, K, V, L, q0, blk, sel_mode, k_fixed=2, sink=True, gate=gate, explicit=explicit)
+    return float((r.O * dO).sum())
+
+
+@pytest.mark.parametrize("sel_mode", ["group", "head"])
+def test_backward_matches_finite_differences_of_the_forward_oracle(sel_mode):
+    """The autograd backward against central differences of the numpy forward oracle, with each
+    unit's list held fixed: entries of Q, K, V, one gate value, and one selector score (through
+    the gate's log-softmax)."""
+    from oracle import sas_backward as ob
+    rng = np.random.default_rng(61)
+    hq, hkv, d, blk, L, tq = 4, 2, 8, 4, 4 * 9 + 3, 10
+    q0 = L - tq
+    Q = rng.standard_normal((hq, tq, d)); K = rng.standard_normal((hkv, L, d)); V = rng.standard_normal((hkv, L, d))
+    dO = rng.standard_normal((hq, tq, d))
+    r = o.run_sequence(Q, K, V, L, q0, blk, sel_mode, k_fixed=2, sink=True, gate=True, attend=False)
+    fixed = {(u.sel_head, u.c): (list(u.sel), dict(u.gate)) for u in r.units}
+    grads = ob.backward_sequence(Q, K, V, dO, L, q0, blk, r.units, gate=True)
+    eps = 1e-6
+
+    def fd(mutate):
+        plus, minus = mutate(+eps), mutate(-eps)
+        return (_loss_numpy(*plus) - _loss_numpy(*minus)) / (2 * eps)
+
+    def with_arr(arr_name, index):
+        def mutate(e):
+            arrs = {"Q": Q.copy(), "K": K.copy(), "V": V.copy()}
+            arrs[arr_name][index] += e
+            return (arrs["Q"], arrs["K"], arrs["V"], dO, L, q0, blk, sel_mode, fixed, True)
+        return mutate
+    for name, index in [("Q", (1, 3, 2)), ("Q", (3, 9, 7)), ("K", (0, 30, 1)), ("K", (1, 5, 4)),
+                        ("V", (1, 33, 0)), ("V", (0, 2, 6))]:
+        got = grads["d" + name][index]
+        assert abs(got - fd(with_arr(name, index))) <= 1e-6 * (1 + abs(got)), (name, index)
+    u = r.units[-1]
+    key_u = (u.sel_head, u.c)
+    j0 = u.sel[0]
+
+    def with_gate(e):
+        sel, g = fixed[key_u]
+        g2 = dict(g); g2[j0] += e
+        ex = dict(fixed); ex[key_u] = (sel, g2)
+        return (Q, K, V, dO, L, q0, blk, sel_mode, ex, True)
+
+    assert abs(grads["dgate"][key_u][0] - fd(with_gate)) <= 1e-6
+
+    def with_score(e):
+        s2 = np.array(u.scores, dtype=np.float64); s2[j0] += e
+        ex = dict(fixed); ex[key_u] = (fixed[key_u][0], o.gate_values(s2, fixed[key_u][0]))
+        return (Q, K, V, dO, L, q0, blk, sel_mode, ex, True)
+
+    assert abs(grads["dscore"][key_u][0] - fd(with_score)) <= 1e-6
+    # the log-softmax Jacobian: dscore = dgate - exp(g) * sum(dgate)
+    g = np.array([u.gate[j] for j in u.sel])
+    dg = grads["dgate"][key_u]
+    np.testing.assert_allclose(grads["dscore"][key_u], dg - np.exp(g) * dg.sum(), rtol=0, atol=1e-12)
+
+
+def test_backward_all_blocks_gate_off_is_sdpa_backward():
+    """Every block selected and no gate: the gradients of dense causal attention, from torch's
+    scaled_dot_product_attention in float64."""
+    from oracle import sas_backward as ob
+    rng = np.random.default_rng(62)
+    hq, hkv, d, blk, L = 2, 1, 8, 4, 4 * 6 + 1
+    Q = rng.standard_normal((hq, L, d)); K = rng.standard_normal((hkv, L, d)); V = rng.standard_normal((hkv, L, d))
+    dO = rng.standard_normal((hq, L, d))
+    r = o.run_sequence(Q, K, V, L, 0, blk, "group", k_fixed=100, attend=False)
+    grads = ob.backward_sequence(Q, K, V, dO, L, 0, blk, r.units, gate=False)
+    qt = torch.tensor(Q, dtype=torch.float64, requires_grad=True)
+    kt = torch.tensor(np.repeat(K, hq, axis=0), dtype=torch.float64, requires_grad=True)
+    vt = torch.tensor(np.repeat(V, hq, axis=0), dtype=torch.float64, requires_grad=True)
+    out = torch.nn.functional.scaled_dot_product_attention(qt[None], kt[None], vt[None], is_causal=True)[0]
+    (out * torch.tensor(dO)).sum().backward()
+    np.testing.assert_allclose(grads["dQ"], qt.grad.numpy(), rtol=0, atol=1e-10)
+    np.testing.assert_allclose(grads["dK"], kt.grad.numpy().sum(axis=0, keepdims=True), rtol=0, atol=1e-10)
+    np.testing.assert_allclose(grads["dV"], vt.grad.numpy().sum(axis=0, keepdims=True), rtol=0, atol=1e-10)
