@@ -18,6 +18,7 @@
  *   sas_sparse_prefill / sas_sparse_decode  attention over the selected blocks only
  *   sas_hssa_select_decode / sas_hssa_decode  two-level gist selection (meta-gists) and its
  *                     attention, for decode
+ *   sas_sparse_prefill_backward  gradients of the sparse prefill (Q, K, V, gates, scores)
  *
  * Conventions shared by every entry point
  *   - Shapes.  B sequences, Hq query heads, Hkv KV heads (Hq % Hkv == 0, G = Hq/Hkv),
@@ -303,6 +304,38 @@ sas_status sas_hssa_decode(const sas_problem *p, const void *Q, const int64_t q_
 
 /* Text of the last non-OK status returned on this thread ("" if none). */
 const char *sas_last_error(void);
+
+/* Backward of A4 ([SAS] method, core modules 2-3: the selector score enters the logits through a
+ * log-softmax over the kept set, so training reaches the scores through the gate; [BLOG] sections 2
+ * and 7: the masked softmax attention that sas_sparse_prefill computes).  For the loss
+ * sum(O * dO) of one sas_sparse_prefill call with the same lists, gate and scale:
+ *   dQ [B, Hq, T, d] fp32 (dq_stride), dK / dV [B, Hkv, Lmax, d] fp32 (dkv_stride): every row
+ *   t < tq and every key row < L_b is written (zero where no unit attends it); other rows untouched.
+ *   dgate [units, kcap] fp32: gradient of each list entry's gate value (sum of dS over the
+ *   block's keys over the unit's rows and heads); dscore [units, kcap] fp32: gradient of the
+ *   entry's selector score through g = s - logsumexp(list scores):
+ *   dscore_j = dgate_j - exp(g_j) * sum_j' dgate_j'.  Padding entries get 0.  Both are required
+ *   iff gate != NULL (without a gate they are not written and may be NULL).
+ *   O: the forward output (bf16, o_stride); dO: its gradient (bf16, same strides).
+ *   Q, K, V, idx, nsel, gate, kcap, scale: as given to sas_sparse_prefill (bf16 only).
+ *   kcap <= 32767.  workspace: sas_sparse_prefill_backward_workspace(p, tq, sel_mode, kcap, gate
+ *   != NULL) bytes of device scratch (no initial contents needed; it grows with the batch, the rows,
+ *   the block count and, with a gate, the block count times the units per KV head).
+ *   Arithmetic: P and dS are rounded to bf16 as matrix operands, with fp32 accumulation; dQ, dgate
+ *   and dscore are deterministic; dK and dV are too, except in key tiles that more than 64 units
+ *   (per head) or more than 2048 / (rows x heads) units select, whose partial sums meet in fp32
+ *   atomic adds.
+ *   Errors: as sas_sparse_prefill; SAS_ERR_UNSUPPORTED for fp32; SAS_ERR_WORKSPACE when too small. */
+size_t sas_sparse_prefill_backward_workspace(const sas_problem *p, int32_t tq, int32_t sel_mode, int32_t kcap,
+                                             int32_t gate);
+sas_status sas_sparse_prefill_backward(const sas_problem *p, const void *Q, const int64_t q_stride[3],
+                                       const void *K, const void *V, const int64_t kv_stride[3], int32_t tq,
+                                       const int32_t *q_start, int32_t sel_mode, const int32_t *idx,
+                                       const int32_t *nsel, const float *gate, int32_t kcap, float scale,
+                                       const void *O, const void *dO, const int64_t o_stride[3], float *dQ,
+                                       const int64_t dq_stride[3], float *dK, float *dV,
+                                       const int64_t dkv_stride[3], float *dgate, float *dscore,
+                                       void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

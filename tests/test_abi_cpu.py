@@ -296,3 +296,32 @@ def test_shared_budget_validation():
     # per-group selection cannot share a budget
     assert lib.sas_select_decode(C.byref(p), FAKE, q2, FAKE, _lib.SAS_REPS_POOLED, r3, _lib.SAS_SEL_GROUP, 0.0,
                                  C.byref(sh), 40, FAKE, 16, FAKE, FAKE, None, FAKE, ws, None) == _lib.SAS_ERR_SHAPE
+
+
+def test_prefill_backward_validation_codes():
+    lib = _lib.load()
+    p, a = _problem(lens=(1000, 700))
+    kv = _lib.i64x([2 * 1000 * 128, 1000 * 128, 128])
+    q3 = _lib.i64x([8 * 128 * 128, 128 * 128, 128])
+    qs = _lib.i32x([872, 572])
+    need = lib.sas_sparse_prefill_backward_workspace(C.byref(p), 128, _lib.SAS_SEL_GROUP, 8, 1)
+    assert need > 0
+    assert lib.sas_sparse_prefill_backward_workspace(C.byref(p), 128, _lib.SAS_SEL_GROUP, 40000, 1) == 0
+    # the gate adds the partial sums and the entry positions
+    assert lib.sas_sparse_prefill_backward_workspace(C.byref(p), 128, _lib.SAS_SEL_GROUP, 8, 0) < need
+
+    def bw(gate=None, dgate=FAKE, ws=FAKE, wsb=None, q_start=qs, kcap=8, dQ=FAKE, prob=p):
+        return lib.sas_sparse_prefill_backward(C.byref(prob), FAKE, q3, FAKE, FAKE, kv, 128, q_start,
+                                               _lib.SAS_SEL_GROUP, FAKE, FAKE, gate, kcap, 0.0, FAKE, FAKE, q3, dQ,
+                                               q3, FAKE, FAKE, kv, dgate, FAKE, ws,
+                                               need if wsb is None else wsb, None)
+
+    assert bw(q_start=None) == _lib.SAS_ERR_NULL
+    assert bw(dQ=None) == _lib.SAS_ERR_NULL
+    assert bw(ws=None) == _lib.SAS_ERR_NULL
+    assert bw(gate=FAKE, dgate=None) == _lib.SAS_ERR_NULL          # a gate needs dgate and dscore
+    assert bw(kcap=0) == _lib.SAS_ERR_SHAPE
+    assert bw(kcap=40000) == _lib.SAS_ERR_SHAPE
+    assert bw(gate=FAKE, wsb=need - 1) == _lib.SAS_ERR_WORKSPACE
+    pf, af = _problem(lens=(1000, 700), dtype=_lib.SAS_F32)
+    assert bw(prob=pf) == _lib.SAS_ERR_UNSUPPORTED                  # bf16 only

@@ -1,0 +1,157 @@
+"""GPU parity of the sparse-prefill backward against the float64 autograd oracle.
+
+Both sides take the same inputs: the seeded Q/K/V/dO, the oracle's own block lists and gate values
+(uploaded to the GPU as int32 / fp32) and the oracle's forward output O rounded to bf16.
+
+Bar, per gradient tensor X (dQ, dK, dV, dgate, dscore):
+  max |X_gpu - X_ref| <= 2e-2 * max |X_ref|   and   mean |X_gpu - X_ref| <= 2e-3 * max |X_ref|.
+The GPU rounds P and dS to bf16 as matrix operands (relative error <= 2^-9 each, random in sign)
+and D_row uses O in bf16; all sums are fp32.  A sum of n such terms is off by about 2^-9 times
+the root-sum-square of its terms, a small fraction of max |X| for these inputs.
+"""
+import math
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+from workloads import Workload  # noqa: E402
+from workloads.device import upload  # noqa: E402
+
+from gpu_harness import say  # noqa: E402
+import top_block_sparse_gist_amd as sas  # noqa: E402
+from oracle import sas_oracle as orc  # noqa: E402
+from oracle import sas_backward as orcb  # noqa: E402
+
+MAX_REL = 2e-2
+MEAN_REL = 2e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sas.load()
+    yield
+
+
+def _bf16(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+
+
+def _check(name, got, ref, stats):
+    err = np.abs(got - ref)
+    top = float(np.abs(ref).max()) if ref.size else 0.0
+    mx, mean = float(err.max()) if err.size else 0.0, float(err.mean()) if err.size else 0.0
+    stats[name] = (mx / max(top, 1e-30), mean / max(top, 1e-30), top)
+    assert np.isfinite(got).all(), f"{name}: non-finite values"
+    assert mx <= MAX_REL * top + 1e-6, f"{name}: max-abs {mx:.3e} vs max|ref| {top:.3e}"
+    assert mean <= MEAN_REL * top + 1e-7, f"{name}: mean-abs {mean:.3e} vs max|ref| {top:.3e}"
+
+
+def run_backward_case(w: Workload, seqs=(0,)):
+    seqs = list(seqs)
+    say(f"[bwd] {w.name} seqs={seqs} sel={w.sel} d={w.d} blk={w.block} gate={w.gate}")
+    inp = upload(w, seqs, keep_host=set(seqs))
+    lens = inp.seq_lens
+    B, blk, tq = len(seqs), w.block, w.tq
+    S = w.hkv if w.sel == "group" else w.hq
+    QB = sas.num_qblocks(tq, blk)
+    scale = 1.0 / math.sqrt(w.d)
+    # oracle forward: lists, gate values, O
+    res = {}
+    for b in seqs:
+        h = inp.host[b]
+        res[b] = orc.run_sequence(h["q"], h["k"], h["v"], w.seq_lens[b], w.q_start[b], blk, w.sel,
+                                  k_fixed=w.k_fixed, frac_num=w.frac_num, frac_den=w.frac_den,
+                                  count_current=w.count_current, sink=w.sink, gate=w.gate, scale=scale)
+    kcap = max(len(u.sel) for r in res.values() for u in r.units if u.sel is not None)
+    units = B * S * QB
+    idx = np.full((units, kcap), -1, np.int32)
+    nsel = np.zeros(units, np.int32)
+    gate = np.zeros((units, kcap), np.float32)
+    O = torch.zeros_like(inp.Q)
+    dO = torch.zeros_like(inp.Q)
+    for bi, b in enumerate(seqs):
+        r = res[b]
+        q0 = w.q_start[b]
+        for u in r.units:
+            x = (bi * S + u.sel_head) * QB + (u.c - q0 // blk)
+            nsel[x] = len(u.sel)
+            idx[x, :len(u.sel)] = u.sel
+            if w.gate:
+                gate[x, :len(u.sel)] = [u.gate[j] for j in u.sel]
+        O[bi, :, :w.rows[b]] = _bf16(r.O).to(O.device)
+        dO[bi, :, :w.rows[b]] = _bf16(w.grad_out(b)).to(O.device)
+    dev = inp.Q.device
+    t_idx = torch.from_numpy(idx).to(dev)
+    t_nsel = torch.from_numpy(nsel).to(dev)
+    t_gate = torch.from_numpy(gate).to(dev) if w.gate else None
+    dQ, dK, dV, dgate, dscore = sas.sparse_prefill_backward(inp.Q, inp.K, inp.V, O, dO, lens, blk, inp.q_start,
+                                                            t_idx, t_nsel, t_gate, sel_mode=w.sel)
+    torch.cuda.synchronize()
+    say("[bwd] gpu done")
+    dQ, dK, dV = dQ.cpu().numpy(), dK.cpu().numpy(), dV.cpu().numpy()
+    if w.gate:
+        dgate, dscore = dgate.cpu().numpy(), dscore.cpu().numpy()
+    stats = {}
+    for bi, b in enumerate(seqs):
+        h = inp.host[b]
+        L, q0, rows = w.seq_lens[b], w.q_start[b], w.rows[b]
+        ref = orcb.backward_sequence(h["q"], h["k"], h["v"], w.grad_out(b), L, q0, blk, res[b].units, w.gate,
+                                     scale)
+        _check(f"dQ[{b}]", dQ[bi, :, :rows], ref["dQ"], stats)
+        _check(f"dK[{b}]", dK[bi, :, :L], ref["dK"], stats)
+        _check(f"dV[{b}]", dV[bi, :, :L], ref["dV"], stats)
+        if w.gate:
+            g_got, g_ref, s_got, s_ref = [], [], [], []
+            for u in res[b].units:
+                x = (bi * S + u.sel_head) * QB + (u.c - q0 // blk)
+                n = len(u.sel)
+                g_got.append(dgate[x, :n]); g_ref.append(ref["dgate"][(u.sel_head, u.c)])
+                s_got.append(dscore[x, :n]); s_ref.append(ref["dscore"][(u.sel_head, u.c)])
+                assert not dgate[x, n:].any() and not dscore[x, n:].any(), "padding entries must be 0"
+            _check(f"dgate[{b}]", np.concatenate(g_got), np.concatenate(g_ref), stats)
+            _check(f"dscore[{b}]", np.concatenate(s_got), np.concatenate(s_ref), stats)
+    for k, (a, m, top) in stats.items():
+        say(f"[bwd] {k}: max-abs/max|ref| {a:.2e}  mean-abs/max|ref| {m:.2e}  (max|ref| {top:.3g})")
+    return stats
+
+
+def test_backward_group_unaligned_sink_gate():
+    """Per-group units (G = 2), q_start off a block boundary, a partial last block, d = 128."""
+    w = Workload(3, overrides=dict(tag="bwd_unaligned", seq_len=1000, tq=300, block=64, hq=4, hkv=2,
+                                   frac_num=1, frac_den=4, sink=True, gate=True))
+    run_backward_case(w)
+
+
+def test_backward_per_head_d64_block128():
+    """Per-head units (64-row and partial), d = 64, 128-key blocks (two tiles per block)."""
+    w = Workload(3, overrides=dict(tag="bwd_head64", seq_len=1500, tq=600, block=128, d=64, hq=8, hkv=2,
+                                   sel="head", frac_num=1, frac_den=4, sink=True, gate=True))
+    run_backward_case(w)
+
+
+def test_backward_per_head_sink_tile_split_into_segments():
+    """Block 0 is kept by every unit (64 per-head units per KV head): its key tile's unit list is
+    cut into several segments whose dK/dV partial sums meet in atomic adds."""
+    w = Workload(3, overrides=dict(tag="bwd_split", seq_len=1024, tq=1024, block=64, hq=4, hkv=1, sel="head",
+                                   frac_num=0, frac_den=0, k_fixed=2, sink=True, gate=True))
+    run_backward_case(w)
+
+
+def test_backward_group_no_gate_block128_seven_heads():
+    """No gate (dgate/dscore not written), G = 7 (896 rows per unit: 7 row tiles), 128-key blocks."""
+    w = Workload(3, overrides=dict(tag="bwd_nogate", seq_len=1536, tq=1536, block=128, hq=14, hkv=2,
+                                   frac_num=1, frac_den=8, sink=True, gate=False))
+    run_backward_case(w)
+
+
+def test_backward_two_sequences_ragged():
+    """Two sequences of different lengths in one call (the shorter one's rows past its length unused)."""
+    w = Workload(3, overrides=dict(tag="bwd_two", seq_lens=[1300, 700], batch=2, tq=256, block=64, hq=4, hkv=2,
+                                   frac_num=1, frac_den=4, sink=False, gate=True))
+    run_backward_case(w, seqs=[0, 1])

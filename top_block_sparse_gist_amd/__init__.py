@@ -20,7 +20,7 @@ from ._lib import (SAS_BF16, SAS_F32, SAS_REPS_GIST, SAS_REPS_POOLED, SAS_SEL_GR
                    SasError, check, i32x, i64x, load)
 
 __all__ = ["Budget", "block_reps", "block_scores", "topk_select", "select_decode", "sparse_prefill",
-           "sparse_decode", "num_qblocks", "required_kcap", "SasError", "load", "sel_code"]
+           "sparse_prefill_backward", "sparse_decode", "num_qblocks", "required_kcap", "SasError", "load", "sel_code"]
 
 
 def _torch():
@@ -259,6 +259,47 @@ def sparse_prefill(Q, K, V, seq_lens, block, q_start, idx, nsel, gate=None, sel_
                                     idx.shape[1], float(scale), _ptr(O), _strides(O, 3), _stream(stream)),
           "sas_sparse_prefill")
     return O
+
+
+def prefill_backward_workspace_bytes(B, hq, hkv, d, block, max_len, seq_lens, tq, sel_mode, kcap, gate) -> int:
+    p = _Prob(B, hq, hkv, d, block, SAS_BF16, max_len, seq_lens)
+    return int(load().sas_sparse_prefill_backward_workspace(p.ref, tq, sel_code(sel_mode), kcap, int(bool(gate))))
+
+
+def sparse_prefill_backward(Q, K, V, O, dO, seq_lens, block, q_start, idx, nsel, gate=None, sel_mode="group",
+                            scale=0.0, workspace=None, grads=None, stream=None):
+    """Gradients of sparse_prefill for the loss sum(O * dO): (dQ, dK, dV, dgate, dscore), fp32
+    (dgate and dscore are None without a gate).  grads: optional preallocated (dQ, dK, dV, dgate,
+    dscore); dK/dV rows past a sequence's length are left as given (zeros when allocated here)."""
+    torch = _torch()
+    B, hq, tq, d = Q.shape
+    _, hkv, lmax, _ = K.shape
+    if K.stride() != V.stride() or O.stride() != dO.stride():
+        raise ValueError("K and V (O and dO) must share strides")
+    kcap = idx.shape[1]
+    p = _Prob(B, hq, hkv, d, block, _dtype_code(Q), lmax, seq_lens)
+    lib = load()
+    if grads is None:
+        f32 = dict(dtype=torch.float32, device=Q.device)
+        dQ = torch.empty(B, hq, tq, d, **f32)
+        dK = torch.zeros(B, hkv, lmax, d, **f32)
+        dV = torch.zeros(B, hkv, lmax, d, **f32)
+        dgate = torch.empty(idx.shape, **f32) if gate is not None else None
+        dscore = torch.empty(idx.shape, **f32) if gate is not None else None
+    else:
+        dQ, dK, dV, dgate, dscore = grads
+    if dK.stride() != dV.stride():
+        raise ValueError("dK and dV must share strides")
+    need = lib.sas_sparse_prefill_backward_workspace(p.ref, tq, sel_code(sel_mode), kcap, int(gate is not None))
+    if workspace is None:
+        workspace = torch.empty(max(1, need), dtype=torch.uint8, device=Q.device)
+    check(lib.sas_sparse_prefill_backward(p.ref, _ptr(Q), _strides(Q, 3), _ptr(K), _ptr(V), _strides(K, 3), tq,
+                                          _qstart(q_start), sel_code(sel_mode), _ptr(idx), _ptr(nsel), _ptr(gate),
+                                          kcap, float(scale), _ptr(O), _ptr(dO), _strides(O, 3), _ptr(dQ),
+                                          _strides(dQ, 3), _ptr(dK), _ptr(dV), _strides(dK, 3), _ptr(dgate),
+                                          _ptr(dscore), _ptr(workspace), workspace.numel(), _stream(stream)),
+          "sas_sparse_prefill_backward")
+    return dQ, dK, dV, dgate, dscore
 
 
 def decode_workspace_bytes(B, hq, hkv, d, block, dtype, max_len, seq_lens, sel_mode, kcap, gist) -> int:

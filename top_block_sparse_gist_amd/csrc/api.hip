@@ -588,4 +588,49 @@ sas_status sas_hssa_decode(const sas_problem *p, const void *Q, const int64_t q_
                     "sas_hssa_decode");
 }
 
+size_t sas_sparse_prefill_backward_workspace(const sas_problem *p, int32_t tq, int32_t sel_mode, int32_t kcap,
+                                             int32_t gate) {
+  if (!p || tq < 1 || kcap < 1 || kcap > 32767 || p->batch < 1 || p->hq < 1 || p->hkv < 1 || p->hq % p->hkv ||
+      p->block < 64 || p->max_len < 1 || (sel_mode != SAS_SEL_GROUP && sel_mode != SAS_SEL_HEAD))
+    return 0;
+  return bwd_plan(*p, tq, sel_mode, kcap, gate != 0).bytes;
+}
+
+sas_status sas_sparse_prefill_backward(const sas_problem *p, const void *Q, const int64_t q_stride[3], const void *K,
+                                       const void *V, const int64_t kv_stride[3], int32_t tq, const int32_t *q_start,
+                                       int32_t sel_mode, const int32_t *idx, const int32_t *nsel, const float *gate,
+                                       int32_t kcap, float scale, const void *O, const void *dO,
+                                       const int64_t o_stride[3], float *dQ, const int64_t dq_stride[3], float *dK,
+                                       float *dV, const int64_t dkv_stride[3], float *dgate, float *dscore,
+                                       void *workspace, size_t workspace_bytes, void *stream) {
+  SeqTable tab{};
+  sas_status st;
+  if ((st = check_problem(p, &tab)) != SAS_OK) return st;
+  if (!q_start) return fail(SAS_ERR_NULL, "q_start is NULL (prefill needs the first row position)");
+  if ((st = check_rows(p, tq, q_start, &tab)) != SAS_OK) return st;
+  if ((st = check_sel(sel_mode)) != SAS_OK) return st;
+  if (!Q || !q_stride || !K || !V || !kv_stride || !idx || !nsel || !O || !dO || !o_stride || !dQ || !dq_stride ||
+      !dK || !dV || !dkv_stride || !workspace)
+    return fail(SAS_ERR_NULL, "a required pointer is NULL");
+  if (gate && (!dgate || !dscore)) return fail(SAS_ERR_NULL, "dgate and dscore are required with a gate");
+  if (p->dtype != SAS_BF16) return fail(SAS_ERR_UNSUPPORTED, "the backward takes bf16 Q/K/V/O/dO");
+  if (kcap < 1 || kcap > 32767) return fail(SAS_ERR_SHAPE, "kcap must be in [1, 32767]");
+  if (scale < 0.f || !isfinite(scale)) return fail(SAS_ERR_SHAPE, "scale must be finite and >= 0");
+  const int eb = elem_bytes(p->dtype);
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) || !aligned16(dQ) ||
+      !aligned16(dK) || !aligned16(dV) || !strides_ok(q_stride, 3, eb) || !strides_ok(kv_stride, 3, eb) ||
+      !strides_ok(o_stride, 3, eb) || !strides_ok(dq_stride, 3, 4) || !strides_ok(dkv_stride, 3, 4))
+    return fail(SAS_ERR_SHAPE, "inputs and gradients must be 16-byte aligned with 16-byte-multiple row strides");
+  if ((int64_t)(p->max_len - 1) * kv_stride[2] * eb + (int64_t)p->head_dim * eb > 0xFFFFFFFFll)
+    return fail(SAS_ERR_UNSUPPORTED, "one (sequence, KV head) K/V slab must span less than 4 GiB");
+  const BwdPlan pl = bwd_plan(*p, tq, sel_mode, kcap, gate != nullptr);
+  if (workspace_bytes < pl.bytes)
+    return fail(SAS_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, pl.bytes);
+  const float sc = resolve_scale(scale, p->head_dim);
+  return hip_status(launch_prefill_backward(*p, tab, Q, q_stride, K, V, kv_stride, O, dO, o_stride, tq, sel_mode, idx,
+                                            nsel, gate, kcap, sc, dQ, dq_stride, dK, dV, dkv_stride, dgate, dscore,
+                                            workspace, (hipStream_t)stream),
+                    "sas_sparse_prefill_backward");
+}
+
 }  // extern "C"

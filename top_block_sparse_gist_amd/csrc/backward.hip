@@ -1,0 +1,798 @@
+// Backward of A4: gradients of the gated sparse causal prefill (bf16 inputs, fp32 gradients).
+// Page "稀疏注意力" sections 2 and 7 (the masked softmax attention the forward computes, block by
+// block); page "SAS: 通过端到端优化上下文排序的简单注意力稀疏化", method, core modules 2-3 (the
+// selector score enters the logits through a log-softmax over the kept set, so the loss reaches the
+// scores through it).
+//
+// For each selection unit and each (row, head) of it, the forward takes logits
+// l = scale q.k + g(block of k) over the unit's visible keys, P = softmax(l) and O = P V.  Given dO:
+//   D_row = dO . O,  dP = dO V^T,  dS = P (dP - D_row)
+//   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO,  dgate(j) = sum of dS over the keys of block j
+//   dscore(j) = dgate(j) - exp(g(j)) sum_j' dgate(j')      (g = s - logsumexp of the list's scores)
+// Kernels, in stream order:
+//   bwd_clear  zero the selection bitmap and per-block counts (a fill kernel)
+//   bwd_mark   one lane per list entry: set the unit's bit in its block's row, count it, note the
+//              entry's list position
+//   bwd_plan   one workgroup per (sequence, KV head): cut each key tile's unit list into segments of
+//              bounded work; zero the dK/dV rows of tiles cut into more than one segment
+//   bwd_dq     a unit's row tile, as in the forward (S^T = K Q^T with Q^T in registers): pass 1 walks
+//              the list for each row's log-sum-exp, pass 2 recomputes P, dP^T = V dO^T and dS, and
+//              accumulates dQ^T += K^T dS^T (transposing LDS reads of the K tile); writes LSE, D_row
+//              and per-32-row partial sums of dgate
+//   bwd_dkv    a (64-key tile, segment): the K and V tile stays in LDS while the units that selected
+//              the tile's block stream their rows through LDS 32 at a time (one wave per 32 keys);
+//              S = Q K^T, dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS (transposing LDS reads)
+//   bwd_gate   per unit: dgate (partials summed in a fixed order) and dscore
+// dQ, dgate and dscore are deterministic; dK and dV too, except in tiles whose unit list was cut
+// into several segments (their partial sums meet in fp32 atomic adds).
+#include <algorithm>
+#include <numeric>
+
+#include "common.h"
+
+namespace sas {
+
+namespace {
+
+constexpr float LOG2E = 1.4426950408889634f;
+
+__device__ __forceinline__ bf16x8 as_bf8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// XOR swizzle of the 16-byte chunks of an LDS row (rows of D bf16, unpadded): row-operand reads
+// (16 rows at one chunk) and transposing reads (4 rows x 2 chunks) stay spread over the banks.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+
+// Geometry of selection unit u = (b * S + s) * QB + i.
+struct UnitGeo {
+  int b, s, i, c, t_lo, rows, h0, nh, g;
+};
+__device__ __forceinline__ UnitGeo unit_geo(const SeqTable &st, int64_t u, int S, int QB, int G, int per_head,
+                                            int tq, int blk) {
+  UnitGeo x;
+  x.i = (int)(u % QB);
+  x.s = (int)((u / QB) % S);
+  x.b = (int)(u / ((int64_t)QB * S));
+  const int q0 = st.q0[x.b];
+  x.c = q0 / blk + x.i;
+  x.t_lo = max(0, x.c * blk - q0);
+  const int t_hi = min(tq, (x.c + 1) * blk - q0);
+  x.rows = max(0, t_hi - x.t_lo);
+  x.nh = per_head ? 1 : G;
+  x.h0 = per_head ? x.s : x.s * G;
+  x.g = per_head ? x.s / G : x.s;
+  return x;
+}
+
+// 64 rows of a K or V slab into a swizzled LDS tile: NW waves, 16 bytes per lane, rows past rlast
+// re-read row rlast (in bounds; their keys are masked).
+template <int D, int NW>
+__device__ __forceinline__ void copy_tile(__amdgpu_buffer_rsrc_t rs, uint16_t *lds, int key0, int rlast,
+                                          uint32_t row_bytes, int wave, int lane) {
+  constexpr int CPR = D / 8, RPI = 64 / CPR, RPW = 64 / NW, NDMA = RPW / RPI;
+  static_assert(NDMA >= 1, "rows per wave");
+  const int rin = lane / CPR, cslot = lane % CPR;
+#pragma unroll
+  for (int x = 0; x < NDMA; ++x) {
+    const int row0 = wave * RPW + x * RPI;
+    const int row = row0 + rin;
+    const uint32_t roff = (uint32_t)min(key0 + row, rlast) * row_bytes;
+    buf_load_lds<16>(rs, lds + row0 * D, roff + (uint32_t)(cslot ^ swz<D>(row)) * 16u, 0u);
+  }
+}
+
+// C = A B^T over the head dim for 32 LDS rows (A: rows row0 .. row0+31 of a swizzled tile, one
+// row per lane column) and a register operand (8 bf16 of the head dim per k-step).
+template <int D>
+__device__ __forceinline__ f32x16 rows_dot(const uint16_t *lds, int row0, const bf16x8 *breg, int col, int half) {
+  constexpr int NKK = D / 16;
+  f32x16 a;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) a[r] = 0.f;
+  const int row = row0 + col;
+  const uint16_t *p = lds + row * D;
+  const int f = swz<D>(row);
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(p + 8 * ((2 * kk + half) ^ f));
+    a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(v), breg[kk], a, 0, 0, 0);
+  }
+  return a;
+}
+
+// The same with the B operand read from LDS too (rows b0 .. b0+31 of a swizzled tile).
+template <int D>
+__device__ __forceinline__ f32x16 rows_dot_lds(const uint16_t *la, const uint16_t *lb, int b0, int col, int half) {
+  constexpr int NKK = D / 16;
+  f32x16 a;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) a[r] = 0.f;
+  const uint16_t *pa = la + col * D, *pb = lb + (b0 + col) * D;
+  const int fa = swz<D>(col), fb = swz<D>(b0 + col);
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    const u32x4 va = *reinterpret_cast<const u32x4 *>(pa + 8 * ((2 * kk + half) ^ fa));
+    const u32x4 vb = *reinterpret_cast<const u32x4 *>(pb + 8 * ((2 * kk + half) ^ fb));
+    a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(va), as_bf8(vb), a, 0, 0, 0);
+  }
+  return a;
+}
+
+// Transposed operand of a swizzled LDS tile for k-step ks: lane (col, half) gets column 32 dt + col
+// of rows 16 ks + 4 half + {0..3} and 16 ks + 8 + 4 half + {0..3}, the row order in which an
+// accumulator's registers 8 (ks & 1) .. + 7 hold their rows (keys).
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t *lds, int ks, int dt, int col, int half) {
+  const int c16 = col & 15, chi = col >> 4;
+  const int rlo = 16 * ks + 4 * half + (c16 >> 2), rhi = rlo + 8;
+  const int chunk = 4 * dt + 2 * chi + ((c16 & 3) >> 1);
+  const int sub = 4 * (c16 & 1);
+  const u32x2 lo = lds_read_tr16(lds + rlo * D + 8 * (chunk ^ swz<D>(rlo)) + sub);
+  const u32x2 hi = lds_read_tr16(lds + rhi * D + 8 * (chunk ^ swz<D>(rhi)) + sub);
+  const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+  return as_bf8(w);
+}
+
+// registers 8 (ks & 1) .. + 7 of accumulator a as a bf16 B operand
+__device__ __forceinline__ bf16x8 pack_operand(const f32x16 &a, int r0) {
+  u32x4 w;
+  w[0] = pack_bf16x2(a[r0 + 0], a[r0 + 1]);
+  w[1] = pack_bf16x2(a[r0 + 2], a[r0 + 3]);
+  w[2] = pack_bf16x2(a[r0 + 4], a[r0 + 5]);
+  w[3] = pack_bf16x2(a[r0 + 6], a[r0 + 7]);
+  return as_bf8(w);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------------
+// selection bitmap
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_clear_kernel(uint32_t *p, int64_t n) {
+  for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < n; x += (int64_t)gridDim.x * 256) p[x] = 0u;
+}
+
+__global__ __launch_bounds__(256) void bwd_mark_kernel(const int32_t *__restrict__ idx, const int32_t *__restrict__ nsel,
+                                                      int64_t units, int kcap, int S, int QB, int G, int per_head,
+                                                      int hkv, int NBm, int W, int UG, uint32_t *bits,
+                                                      int32_t *counts, int16_t *epos) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t u = gid / kcap;
+  const int e = (int)(gid % kcap);
+  if (u >= units || e >= nsel[u]) return;
+  const int j = idx[u * kcap + e];
+  if (j < 0 || j >= NBm) return;
+  const int i = (int)(u % QB), s = (int)((u / QB) % S);
+  const int b = (int)(u / ((int64_t)QB * S));
+  const int g = per_head ? s / G : s;
+  const int ug = per_head ? i * G + s % G : i;
+  const int64_t row = (int64_t)(b * hkv + g) * NBm + j;
+  atomicOr(&bits[row * W + (ug >> 5)], 1u << (ug & 31));
+  atomicAdd(&counts[row], 1);
+  if (epos) epos[row * UG + ug] = (int16_t)e;
+}
+
+// Work items of the dK/dV kernel: key tile kt, matches first .. first+count-1 of its block's unit
+// list (in unit order), multi = the tile has several items.
+struct BwdItem {
+  int32_t kt, first, count, multi;
+};
+
+// Workgroup-wide exclusive prefix sum over 256 threads (4 waves); total in *tot.
+__device__ __forceinline__ int block_scan256(int v, int *lds4, int *tot) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) lds4[wave] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int t = lds4[w];
+    before += w < wave ? t : 0;
+    all += t;
+  }
+  __syncthreads();
+  *tot = all;
+  return before + x - v;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_plan_kernel(SeqTable st, int hkv, int NBm, int tpb, int segm, int cap,
+                                                      const int32_t *__restrict__ counts, BwdItem *items,
+                                                      int32_t *icount, float *dK, float *dV, int64_t kb, int64_t kh,
+                                                      int64_t kt_) {
+  __shared__ int scan4[4];
+  __shared__ int multi[256];
+  __shared__ int nmulti;
+  const int pair = blockIdx.x, tid = threadIdx.x;
+  const int b = pair / hkv, g = pair % hkv;
+  const int L = st.len[b];
+  const int T = cdiv(L, 64);
+  int off = 0;
+  for (int k0 = 0; k0 < T; k0 += 256) {
+    if (tid == 0) nmulti = 0;
+    const int kt = k0 + tid;
+    const bool valid = kt < T;
+    const int cnt = valid ? counts[(int64_t)pair * NBm + kt / tpb] : 0;
+    const int nseg = valid ? max(1, cdiv(cnt, segm)) : 0;
+    int tot;
+    const int ex = block_scan256(nseg, scan4, &tot);
+    for (int s = 0; s < nseg; ++s) {
+      const int n = off + ex + s;
+      if (n < cap) items[(int64_t)pair * cap + n] = BwdItem{kt, s * segm, min(segm, cnt - s * segm), nseg > 1};
+    }
+    if (nseg > 1) multi[atomicAdd(&nmulti, 1)] = kt;
+    __syncthreads();
+    // tiles cut into several segments accumulate with atomic adds: clear their rows first
+    const int nm = nmulti;
+    constexpr int V4 = D / 4;  // float4 per row
+    for (int x = tid; x < nm * 64 * V4; x += 256) {
+      const int m = x / (64 * V4), r = (x / V4) % 64, c4 = x % V4;
+      const int key = multi[m] * 64 + r;
+      if (key < L) {
+        const int64_t o = (int64_t)b * kb + (int64_t)g * kh + (int64_t)key * kt_ + 4 * c4;
+        *reinterpret_cast<f32x4 *>(dK + o) = f32x4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<f32x4 *>(dV + o) = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    off += tot;
+    __syncthreads();
+  }
+  if (tid == 0) icount[pair] = min(off, cap);
+}
+
+// ---------------------------------------------------------------------------------------------
+// dQ, row log-sum-exp, D_row and dgate partials
+// ---------------------------------------------------------------------------------------------
+template <int D, int NW, int BLK>
+__global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
+    SeqTable st, const uint16_t *__restrict__ Q, int64_t qb, int64_t qh, int64_t qt, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, int64_t kb, int64_t kh, int64_t kt, const uint16_t *__restrict__ O,
+    const uint16_t *__restrict__ dO, int64_t ob, int64_t oh, int64_t ot, int tq, int S, int QB, int G, int per_head,
+    int batch, int hq, int rtiles, const int32_t *__restrict__ idx, const int32_t *__restrict__ nsel,
+    const float *__restrict__ gate, int kcap, float scale_log2, float scale, float *__restrict__ dQ, int64_t dqb,
+    int64_t dqh, int64_t dqt, float *__restrict__ lse_ws, float *__restrict__ dd_ws, float *__restrict__ gpart,
+    int gslots) {
+  constexpr int NKK = D / 16, NDT = D / 32, tpb = BLK / 64;
+  __shared__ __attribute__((aligned(16))) uint16_t klds[2][64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vlds[2][64 * D];
+
+  // workgroup -> (query block heavy-first, sequence, selector head, row tile); the row tiles of a
+  // unit run on one XCD and share its K/V tiles in that L2
+  const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+  const int rt = q % rtiles;
+  int rest = (q / rtiles) * 8 + xcd;
+  if (rest >= QB * batch * S) return;
+  const int s = rest % S;
+  rest /= S;
+  const int b = rest % batch;
+  const int i = QB - 1 - rest / batch;
+  const int64_t u = ((int64_t)b * S + s) * QB + i;
+  const UnitGeo ug = unit_geo(st, u, S, QB, G, per_head, tq, BLK);
+  const int R = ug.rows * ug.nh;
+  const int r0 = rt * NW * 32;
+  if (ug.rows <= 0 || r0 >= R) return;
+  const int ns = nsel[u];
+  const int ntiles = ns * tpb;
+  const int nplain = ntiles - tpb;  // the current block (last entry) needs the causal mask
+  const int L = st.len[b], q0 = st.q0[b];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int rq = r0 + wave * 32 + col;
+  const bool qvalid = rq < R;
+  const int h = ug.h0 + (qvalid ? rq / ug.rows : 0);
+  const int t = ug.t_lo + (qvalid ? rq % ug.rows : 0);
+  const int qpos = q0 + t;
+
+  // Q^T, dO^T operands and D_row = dO . O (this lane's half of the head dim, then the other half)
+  bf16x8 qreg[NKK], doreg[NKK];
+  float drow = 0.f;
+  {
+    const uint16_t *qp = Q + b * qb + (int64_t)h * qh + (int64_t)t * qt + 8 * half;
+    const int64_t oo = b * ob + (int64_t)h * oh + (int64_t)t * ot + 8 * half;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      u32x4 vq = {0u, 0u, 0u, 0u}, vd = vq, vo = vq;
+      if (qvalid) {
+        vq = *reinterpret_cast<const u32x4 *>(qp + 16 * kk);
+        vd = *reinterpret_cast<const u32x4 *>(dO + oo + 16 * kk);
+        vo = *reinterpret_cast<const u32x4 *>(O + oo + 16 * kk);
+      }
+      qreg[kk] = as_bf8(vq);
+      doreg[kk] = as_bf8(vd);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) drow += bf16_lo(vd[x]) * bf16_lo(vo[x]) + bf16_hi(vd[x]) * bf16_hi(vo[x]);
+    }
+    drow += __shfl_xor(drow, 32, 64);
+  }
+
+  const int32_t *ulist = idx + u * kcap;
+  const float *glist = gate ? gate + u * kcap : nullptr;
+  const uint32_t row_bytes = (uint32_t)(kt * 2);
+  const uint32_t slab = (uint32_t)(L - 1) * row_bytes + D * 2;
+  const __amdgpu_buffer_rsrc_t krs = dev_rsrc(K + b * kb + ug.g * kh, slab);
+  const __amdgpu_buffer_rsrc_t vrs = dev_rsrc(V + b * kb + ug.g * kh, slab);
+  auto key0_of = [&](int tt) { return ulist[tt / tpb] * BLK + (tt % tpb) * 64; };
+  auto load = [&](int tt, int buf, bool withv) {
+    const int k0 = key0_of(tt);
+    copy_tile<D, NW>(krs, klds[buf], k0, L - 1, row_bytes, wave, lane);
+    if (withv) copy_tile<D, NW>(vrs, vlds[buf], k0, L - 1, row_bytes, wave, lane);
+  };
+  // S^T of tile tt (two 32-key halves), keys past the row's position at -inf on the current block
+  auto scores = [&](int tt, f32x16 *sacc) {
+    const uint16_t *kl = klds[tt & 1];
+    sacc[0] = rows_dot<D>(kl, 0, qreg, col, half);
+    sacc[1] = rows_dot<D>(kl, 32, qreg, col, half);
+    if (tt >= nplain) {
+      const int k0 = key0_of(tt);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (k0 + key > qpos) sacc[mt][r] = -INFINITY;
+        }
+    }
+  };
+
+  // ---- pass 1: running max and sum (log2 units) -> lse2 = log2 sum_k exp2(l_k log2 e)
+  float m_run = -INFINITY, l_run = 0.f;
+  if (ntiles > 0) load(0, 0, false);
+  wait_stores();
+  __syncthreads();
+  for (int tt = 0; tt < ntiles; ++tt) {
+    if (tt + 1 < ntiles) load(tt + 1, (tt + 1) & 1, false);
+    f32x16 sacc[2];
+    scores(tt, sacc);
+    const float gl2 = glist ? glist[tt / tpb] * LOG2E : 0.f;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_tile = (mx == -INFINITY) ? -INFINITY : mx * scale_log2 + gl2;
+    const float m_new = fmaxf(m_run, m_tile);
+    if (m_new != -INFINITY) {
+      l_run *= __builtin_amdgcn_exp2f(m_run - m_new);
+      const float bias = gl2 - m_new;
+      float ls = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ls += __builtin_amdgcn_exp2f(fmaf(sacc[mt][r], scale_log2, bias));
+      l_run += ls;
+      m_run = m_new;
+    }
+    wait_stores();
+    __syncthreads();
+  }
+  l_run += __shfl_xor(l_run, 32, 64);
+  const float lse2 = qvalid && l_run > 0.f ? m_run + log2f(l_run) : INFINITY;
+
+  // ---- pass 2: P, dP^T, dS^T; dQ^T += K^T dS^T; dgate partials per block
+  f32x16 acc[NDT];
+#pragma unroll
+  for (int x = 0; x < NDT; ++x)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[x][r] = 0.f;
+  const int slot = r0 / 32 + wave;
+  const bool wave_rows = r0 + wave * 32 < R;
+  float gsum = 0.f;
+  if (ntiles > 0) load(0, 0, true);
+  wait_stores();
+  __syncthreads();
+  for (int tt = 0; tt < ntiles; ++tt) {
+    if (tt + 1 < ntiles) load(tt + 1, (tt + 1) & 1, true);
+    f32x16 sacc[2];
+    scores(tt, sacc);
+    const float gl2 = glist ? glist[tt / tpb] * LOG2E : 0.f;
+    const float bias = gl2 - lse2;
+    const uint16_t *vl = vlds[tt & 1];
+    f32x16 dp[2];
+    dp[0] = rows_dot<D>(vl, 0, doreg, col, half);
+    dp[1] = rows_dot<D>(vl, 32, doreg, col, half);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[mt][r], scale_log2, bias));
+        const float ds = p * (dp[mt][r] - drow);
+        sacc[mt][r] = ds;
+        gsum += ds;
+      }
+    const uint16_t *kl = klds[tt & 1];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 dsop = pack_operand(sacc[ks >> 1], 8 * (ks & 1));
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(kl, ks, dt, col, half), dsop, acc[dt], 0, 0, 0);
+    }
+    if (gpart && tt % tpb == tpb - 1) {
+      const float gs = wave_sum(gsum);
+      if (lane == 0 && wave_rows) gpart[((int64_t)u * gslots + slot) * kcap + tt / tpb] = gs;
+      gsum = 0.f;
+    }
+    wait_stores();
+    __syncthreads();
+  }
+  if (!qvalid) return;
+  // ---- dQ = scale * (dQ^T)^T (lane holds dims 32dt + 8(r/4) + 4half + r%4 of its row), LSE, D
+  float *dqp = dQ + b * dqb + (int64_t)h * dqh + (int64_t)t * dqt;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const f32x4 v = {acc[dt][4 * rb] * scale, acc[dt][4 * rb + 1] * scale, acc[dt][4 * rb + 2] * scale,
+                       acc[dt][4 * rb + 3] * scale};
+      *reinterpret_cast<f32x4 *>(dqp + dt * 32 + 8 * rb + 4 * half) = v;
+    }
+  if (half == 0) {
+    const int64_t o = ((int64_t)b * hq + h) * tq + t;
+    lse_ws[o] = lse2;
+    dd_ws[o] = drow;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// dK, dV
+// ---------------------------------------------------------------------------------------------
+template <int D, int BLK>
+__global__ __launch_bounds__(128, 2) void bwd_dkv_kernel(
+    SeqTable st, const uint16_t *__restrict__ Q, int64_t qb, int64_t qh, int64_t qt, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, int64_t kb, int64_t kh, int64_t kt, const uint16_t *__restrict__ dO, int64_t ob,
+    int64_t oh, int64_t ot, int tq, int S, int QB, int G, int per_head, int hq, int hkv, int npairs, int pchunks,
+    int Ic, int cap, const BwdItem *__restrict__ items, const int32_t *__restrict__ icount,
+    const uint32_t *__restrict__ bits, const int16_t *__restrict__ epos, int NBm, int W, int UG,
+    const float *__restrict__ gate, int kcap, const float *__restrict__ lse_ws, const float *__restrict__ dd_ws,
+    float scale_log2, float scale, float *__restrict__ dK, float *__restrict__ dV, int64_t gb, int64_t gh,
+    int64_t gt) {
+  constexpr int NKK = D / 16, NDT = D / 32, CPR = D / 8, tpb = BLK / 64;
+  constexpr int SEGMAX = 64;  // units per work item (the host's segment size is at most this)
+  __shared__ __attribute__((aligned(16))) uint16_t qs[32 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t dos[32 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t klds[64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vlds[64 * D];
+  __shared__ __attribute__((aligned(16))) float lse_s[32];
+  __shared__ __attribute__((aligned(16))) float dd_s[32];
+  __shared__ __attribute__((aligned(16))) int lim_s[32];
+  __shared__ int mu[SEGMAX];
+  __shared__ float mgl[SEGMAX];
+  __shared__ int scan2[2];
+
+  const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+  const int cid = xcd + 8 * (q / Ic);
+  const int pair = cid / pchunks;
+  if (pair >= npairs) return;
+  const int n = cid % pchunks + pchunks * (q % Ic);
+  if (n >= icount[pair]) return;
+  const BwdItem it = items[(int64_t)pair * cap + n];
+  const int b = pair / hkv, g = pair % hkv;
+  const int L = st.len[b], q0 = st.q0[b];
+  const int j = it.kt / tpb;
+  const int key0 = it.kt * 64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
+
+  // ---- the item's units: ranks first .. first+count-1 of the set bits of block j's row
+  const int cnt = min(it.count, SEGMAX);
+  if (cnt > 0) {
+    const uint32_t *row = bits + ((int64_t)pair * NBm + j) * W;
+    int base = 0;
+    for (int w0 = 0; w0 < W && base < it.first + cnt; w0 += 128) {
+      const int w = w0 + tid;
+      uint32_t word = w < W ? row[w] : 0u;
+      const int pc = __popc(word);
+      int x = pc;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+      }
+      if (lane == 63) scan2[wave] = x;
+      __syncthreads();
+      int r = base + x - pc + (wave == 1 ? scan2[0] : 0);
+      while (word) {
+        const int bit = __ffs(word) - 1;
+        word &= word - 1;
+        if (r >= it.first && r < it.first + cnt) mu[r - it.first] = w * 32 + bit;
+        ++r;
+      }
+      base += scan2[0] + scan2[1];
+      __syncthreads();
+    }
+    for (int k = tid; k < cnt; k += 128) {
+      const int ugi = mu[k];
+      float gl2 = 0.f;
+      if (gate) {
+        const int i = per_head ? ugi / G : ugi;
+        const int s = per_head ? g * G + ugi % G : g;
+        const int64_t u = ((int64_t)b * S + s) * QB + i;
+        const int e = epos[((int64_t)pair * NBm + j) * UG + ugi];
+        gl2 = gate[u * kcap + e] * LOG2E;
+      }
+      mgl[k] = gl2;
+    }
+    __syncthreads();
+  }
+
+  // ---- the K and V tile (B operands of S and dP: wave w uses keys 32w .. 32w+31; rows past L
+  //      re-read row L-1 and are masked below)
+  const int mykey = key0 + wave * 32 + col;
+  {
+    const uint32_t row_bytes = (uint32_t)(kt * 2);
+    const uint32_t slab = (uint32_t)(L - 1) * row_bytes + D * 2;
+    copy_tile<D, 2>(dev_rsrc(K + b * kb + (int64_t)g * kh, slab), klds, key0, L - 1, row_bytes, wave, lane);
+    copy_tile<D, 2>(dev_rsrc(V + b * kb + (int64_t)g * kh, slab), vlds, key0, L - 1, row_bytes, wave, lane);
+  }
+  f32x16 adk[NDT], adv[NDT];
+#pragma unroll
+  for (int x = 0; x < NDT; ++x)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) adk[x][r] = adv[x][r] = 0.f;
+
+  for (int k = 0; k < cnt; ++k) {
+    const int ugi = mu[k];
+    const int i = per_head ? ugi / G : ugi;
+    const int s = per_head ? g * G + ugi % G : g;
+    const int64_t u = ((int64_t)b * S + s) * QB + i;
+    const UnitGeo ugeo = unit_geo(st, u, S, QB, G, per_head, tq, BLK);
+    const int F = ugeo.rows * ugeo.nh;
+    const float gl2 = mgl[k];
+    for (int c0 = 0; c0 < F; c0 += 32) {
+      // stage 32 rows of Q and dO (swizzled) and their LSE, D and position limit
+#pragma unroll
+      for (int x = 0; x < 32 * CPR / 128; ++x) {
+        const int e = x * 128 + tid;
+        const int r = e / CPR, cs = e % CPR;
+        const int fc = min(c0 + r, F - 1);
+        const int hh = ugeo.h0 + fc / ugeo.rows, tt = ugeo.t_lo + fc % ugeo.rows;
+        const int off = 8 * (cs ^ swz<D>(r));
+        load_lds16(Q + b * qb + (int64_t)hh * qh + (int64_t)tt * qt + off, qs + 8 * (x * 128 + wave * 64));
+        load_lds16(dO + b * ob + (int64_t)hh * oh + (int64_t)tt * ot + off, dos + 8 * (x * 128 + wave * 64));
+      }
+      if (tid < 32) {
+        const int f = c0 + tid;
+        if (f < F) {
+          const int hh = ugeo.h0 + f / ugeo.rows, tt = ugeo.t_lo + f % ugeo.rows;
+          const int64_t o = ((int64_t)b * hq + hh) * tq + tt;
+          lse_s[tid] = lse_ws[o];
+          dd_s[tid] = dd_ws[o];
+          lim_s[tid] = q0 + tt;
+        } else {
+          lse_s[tid] = 0.f;
+          dd_s[tid] = 0.f;
+          lim_s[tid] = -1;
+        }
+      }
+      wait_stores();
+      __syncthreads();
+      // S and dP (rows x this wave's keys): register r holds row 8(r/4) + 4half + r%4, key col
+      // (P overwrites S and dS overwrites dP in place)
+      f32x16 pa = rows_dot_lds<D>(qs, klds, wave * 32, col, half);
+      f32x16 dsa = rows_dot_lds<D>(dos, vlds, wave * 32, col, half);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&lse_s[8 * rb + 4 * half]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&dd_s[8 * rb + 4 * half]);
+        const i32x4 m4 = *reinterpret_cast<const i32x4 *>(&lim_s[8 * rb + 4 * half]);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int r = 4 * rb + x;
+          const float p = mykey > m4[x] ? 0.f : __builtin_amdgcn_exp2f(fmaf(pa[r], scale_log2, gl2 - l4[x]));
+          pa[r] = p;
+          dsa[r] = p * (dsa[r] - d4[x]);
+        }
+      }
+      // dV^T += dO^T P, dK^T += Q^T dS over the 32 rows (two 16-row steps)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 pop = pack_operand(pa, 8 * ks);
+        const bf16x8 dsop = pack_operand(dsa, 8 * ks);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          adv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(dos, ks, dt, col, half), pop, adv[dt], 0, 0, 0);
+          adk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(qs, ks, dt, col, half), dsop, adk[dt], 0, 0, 0);
+        }
+      }
+      __syncthreads();
+    }
+  }
+  wait_stores();  // no copy into LDS may outlive the workgroup (an item with no units copied the tile)
+  // ---- write (lane holds dims 32dt + 8(r/4) + 4half + r%4 of key mykey)
+  if (mykey >= L) return;
+  const int64_t o = b * gb + (int64_t)g * gh + (int64_t)mykey * gt;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int dim = dt * 32 + 8 * rb + 4 * half;
+      const f32x4 vk = {adk[dt][4 * rb] * scale, adk[dt][4 * rb + 1] * scale, adk[dt][4 * rb + 2] * scale,
+                        adk[dt][4 * rb + 3] * scale};
+      const f32x4 vv = {adv[dt][4 * rb], adv[dt][4 * rb + 1], adv[dt][4 * rb + 2], adv[dt][4 * rb + 3]};
+      if (it.multi) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          unsafeAtomicAdd(dK + o + dim + x, vk[x]);
+          unsafeAtomicAdd(dV + o + dim + x, vv[x]);
+        }
+      } else {
+        *reinterpret_cast<f32x4 *>(dK + o + dim) = vk;
+        *reinterpret_cast<f32x4 *>(dV + o + dim) = vv;
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// dgate, dscore
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_gate_kernel(SeqTable st, int64_t units, int S, int QB, int G, int per_head,
+                                                      int tq, int blk, const int32_t *__restrict__ nsel,
+                                                      const float *__restrict__ gate, int kcap,
+                                                      const float *__restrict__ gpart, int gslots,
+                                                      float *__restrict__ dgate, float *__restrict__ dscore) {
+  const int lane = threadIdx.x & 63;
+  const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (u >= units) return;
+  const UnitGeo x = unit_geo(st, u, S, QB, G, per_head, tq, blk);
+  const int ns = x.rows > 0 ? nsel[u] : 0;
+  const int nsl = cdiv(x.rows * x.nh, 32);
+  auto dg_of = [&](int e) {
+    float a = 0.f;
+    for (int sl = 0; sl < nsl; ++sl) a += gpart[((int64_t)u * gslots + sl) * kcap + e];
+    return a;
+  };
+  float tot = 0.f;
+  for (int e = lane; e < ns; e += 64) tot += dg_of(e);
+  tot = wave_sum(tot);
+  for (int e = lane; e < kcap; e += 64) {
+    float dg = 0.f, dsc = 0.f;
+    if (e < ns) {
+      dg = dg_of(e);
+      dsc = dg - expf(gate[u * kcap + e]) * tot;
+    }
+    dgate[u * kcap + e] = dg;
+    dscore[u * kcap + e] = dsc;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------------------------
+BwdPlan bwd_plan(const sas_problem &p, int32_t tq, int32_t sel_mode, int32_t kcap, bool gate) {
+  BwdPlan x{};
+  const int per_head = sel_mode == SAS_SEL_HEAD;
+  const int G = p.hq / p.hkv;
+  const int S = per_head ? p.hq : p.hkv;
+  x.QB = num_qblocks(tq, p.block);
+  x.units = (int64_t)p.batch * S * x.QB;
+  x.nh = per_head ? 1 : G;
+  const int rows_max = std::min(tq, p.block);
+  x.gslots = cdiv(rows_max * x.nh, 32);
+  x.NBm = cdiv(p.max_len, p.block);
+  x.UG = x.QB * (per_head ? G : 1);
+  x.W = cdiv(x.UG, 32);
+  x.npairs = p.batch * p.hkv;
+  x.tpb = p.block / 64;
+  x.T = cdiv(p.max_len, 64);
+  x.segm = std::max(1, std::min(64, 2048 / std::max(1, rows_max * x.nh)));
+  x.cap = (int)std::min<int64_t>(INT32_MAX / 2, x.T + cdiv64((int64_t)x.tpb * x.UG * kcap, x.segm));
+  auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  size_t off = 0;
+  const size_t rowsz = (size_t)p.batch * p.hq * tq * sizeof(float);
+  x.off_lse = off;
+  off += al(rowsz);
+  x.off_dd = off;
+  off += al(rowsz);
+  x.off_gpart = off;
+  if (gate) off += al((size_t)x.units * x.gslots * kcap * sizeof(float));
+  x.off_bits = off;
+  x.clear_words = (int64_t)x.npairs * x.NBm * (x.W + 1);
+  off += al((size_t)x.clear_words * sizeof(uint32_t));  // bits, then counts
+  x.off_epos = off;
+  if (gate) off += al((size_t)x.npairs * x.NBm * x.UG * sizeof(int16_t));
+  x.off_items = off;
+  off += al((size_t)x.npairs * x.cap * sizeof(BwdItem));
+  x.off_icount = off;
+  off += al((size_t)x.npairs * sizeof(int32_t));
+  x.bytes = off;
+  return x;
+}
+
+template <int D, int BLK>
+static hipError_t bwd_dispatch(const sas_problem &p, const SeqTable &st, const BwdPlan &pl, const void *Q,
+                               const int64_t *qs, const void *K, const void *V, const int64_t *kvs, const void *O,
+                               const void *dO, const int64_t *os, int32_t tq, int32_t sel_mode, const int32_t *idx,
+                               const int32_t *nsel, const float *gate, int32_t kcap, float scale, float *dQ,
+                               const int64_t *dqs, float *dK, float *dV, const int64_t *dkvs, float *dgate,
+                               float *dscore, char *ws, hipStream_t s) {
+  const int per_head = sel_mode == SAS_SEL_HEAD;
+  const int G = p.hq / p.hkv;
+  const int S = per_head ? p.hq : p.hkv;
+  float *lse = (float *)(ws + pl.off_lse), *dd = (float *)(ws + pl.off_dd);
+  float *gpart = gate ? (float *)(ws + pl.off_gpart) : nullptr;
+  uint32_t *bits = (uint32_t *)(ws + pl.off_bits);
+  int32_t *counts = (int32_t *)(bits + (int64_t)pl.npairs * pl.NBm * pl.W);
+  int16_t *epos = gate ? (int16_t *)(ws + pl.off_epos) : nullptr;
+  BwdItem *items = (BwdItem *)(ws + pl.off_items);
+  int32_t *icount = (int32_t *)(ws + pl.off_icount);
+  const float scale_log2 = scale * LOG2E;
+  const uint16_t *q16 = (const uint16_t *)Q, *k16 = (const uint16_t *)K, *v16 = (const uint16_t *)V;
+  const uint16_t *o16 = (const uint16_t *)O, *do16 = (const uint16_t *)dO;
+
+  // selection bitmap, counts, entry positions, work items
+  {
+    const int64_t n = pl.clear_words;
+    const unsigned g = (unsigned)std::min<int64_t>(4096, std::max<int64_t>(1, cdiv64(n, 256)));
+    hipLaunchKernelGGL(bwd_clear_kernel, dim3(g), dim3(256), 0, s, bits, n);
+    const int64_t m = pl.units * kcap;
+    hipLaunchKernelGGL(bwd_mark_kernel, dim3((unsigned)std::max<int64_t>(1, cdiv64(m, 256))), dim3(256), 0, s, idx,
+                       nsel, pl.units, kcap, S, pl.QB, G, per_head, p.hkv, pl.NBm, pl.W, pl.UG, bits, counts, epos);
+    hipLaunchKernelGGL((bwd_plan_kernel<D>), dim3(pl.npairs), dim3(256), 0, s, st, p.hkv, pl.NBm, pl.tpb, pl.segm,
+                       pl.cap, (const int32_t *)counts, items, icount, dK, dV, dkvs[0], dkvs[1], dkvs[2]);
+  }
+  // dQ, LSE, D, gate partials
+  {
+    const bool small = std::min(tq, p.block) * pl.nh <= 64;
+    const int NW = small ? 2 : 4;
+    const int rtiles = cdiv(std::min(tq, p.block) * pl.nh, NW * 32);
+    const int64_t nwg = 8 * cdiv64(pl.units, 8) * rtiles;
+#define SAS_BDQ(NW_)                                                                                                \
+  hipLaunchKernelGGL((bwd_dq_kernel<D, NW_, BLK>), dim3((unsigned)nwg), dim3(NW_ * 64), 0, s, st, q16, qs[0], qs[1], \
+                     qs[2], k16, v16, kvs[0], kvs[1], kvs[2], o16, do16, os[0], os[1], os[2], tq, S, pl.QB, G,       \
+                     per_head, p.batch, p.hq, rtiles, idx, nsel, gate, kcap, scale_log2, scale, dQ, dqs[0], dqs[1],  \
+                     dqs[2], lse, dd, gpart, pl.gslots)
+    if (small) SAS_BDQ(2);
+    else SAS_BDQ(4);
+#undef SAS_BDQ
+  }
+  // dK, dV
+  {
+    const int pchunks = 8 / std::gcd(pl.npairs, 8);
+    const int Ic = cdiv(pl.cap, pchunks);
+    const int64_t nwg = (int64_t)8 * cdiv(pl.npairs * pchunks, 8) * Ic;
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, BLK>), dim3((unsigned)nwg), dim3(128), 0, s, st, q16, qs[0], qs[1], qs[2],
+                       k16, v16, kvs[0], kvs[1], kvs[2], do16, os[0], os[1], os[2], tq, S, pl.QB, G, per_head, p.hq,
+                       p.hkv, pl.npairs, pchunks, Ic, pl.cap, (const BwdItem *)items, (const int32_t *)icount,
+                       (const uint32_t *)bits, (const int16_t *)epos, pl.NBm, pl.W, pl.UG, gate, kcap, lse, dd,
+                       scale_log2, scale, dK, dV, dkvs[0], dkvs[1], dkvs[2]);
+  }
+  if (gate) {
+    hipLaunchKernelGGL(bwd_gate_kernel, dim3((unsigned)cdiv64(pl.units, 4)), dim3(256), 0, s, st, pl.units, S, pl.QB,
+                       G, per_head, tq, p.block, nsel, gate, kcap, (const float *)gpart, pl.gslots, dgate, dscore);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_backward(const sas_problem &p, const SeqTable &st, const void *Q, const int64_t *qs,
+                                   const void *K, const void *V, const int64_t *kvs, const void *O, const void *dO,
+                                   const int64_t *os, int32_t tq, int32_t sel_mode, const int32_t *idx,
+                                   const int32_t *nsel, const float *gate, int32_t kcap, float scale, float *dQ,
+                                   const int64_t *dqs, float *dK, float *dV, const int64_t *dkvs, float *dgate,
+                                   float *dscore, void *workspace, hipStream_t s) {
+  const BwdPlan pl = bwd_plan(p, tq, sel_mode, kcap, gate != nullptr);
+  char *ws = (char *)workspace;
+#define SAS_BWD(D_, B_)                                                                                            \
+  return bwd_dispatch<D_, B_>(p, st, pl, Q, qs, K, V, kvs, O, dO, os, tq, sel_mode, idx, nsel, gate, kcap, scale, \
+                              dQ, dqs, dK, dV, dkvs, dgate, dscore, ws, s)
+  if (p.head_dim == 128) {
+    if (p.block == 64) SAS_BWD(128, 64);
+    SAS_BWD(128, 128);
+  }
+  if (p.block == 64) SAS_BWD(64, 64);
+  SAS_BWD(64, 128);
+#undef SAS_BWD
+}
+
+}  // namespace sas

@@ -269,4 +269,23 @@ hipError_t launch_hssa_decode(const sas_problem &p, const SeqTable &st, const vo
                               const int32_t *gidx, int32_t gcap, float scale, void *O, const int64_t *os,
                               float *workspace, hipStream_t s);
 
+
+// Backward of the sparse prefill: sizes and workspace layout (host formula shared with the size
+// query).  Workspace regions, 256-byte aligned: row LSE and D [B, Hq, tq] fp32; gate partials
+// [units, gslots, kcap] fp32 (with a gate); selection bitmap [pairs, NBm, W] u32 then per-block
+// counts [pairs, NBm]; entry positions [pairs, NBm, UG] int16 (with a gate); work items
+// [pairs, cap] x 16 bytes; item counts [pairs].
+struct BwdPlan {
+  int QB, nh, gslots, NBm, UG, W, npairs, tpb, T, segm, cap;
+  int64_t units, clear_words;
+  size_t off_lse, off_dd, off_gpart, off_bits, off_epos, off_items, off_icount, bytes;
+};
+BwdPlan bwd_plan(const sas_problem &p, int32_t tq, int32_t sel_mode, int32_t kcap, bool gate);
+hipError_t launch_prefill_backward(const sas_problem &p, const SeqTable &st, const void *Q, const int64_t *qs,
+                                   const void *K, const void *V, const int64_t *kvs, const void *O, const void *dO,
+                                   const int64_t *os, int32_t tq, int32_t sel_mode, const int32_t *idx,
+                                   const int32_t *nsel, const float *gate, int32_t kcap, float scale, float *dQ,
+                                   const int64_t *dqs, float *dK, float *dV, const int64_t *dkvs, float *dgate,
+                                   float *dscore, void *workspace, hipStream_t s);
+
 }  // namespace sas

@@ -34,7 +34,7 @@ from typing import Dict, List, Optional, Tuple
 import numpy as np
 
 # stream ids (second component of the seed sequence's spawn key)
-_S_LENS, _S_Q, _S_K, _S_V, _S_NEEDLE, _S_OFFSET, _S_GK, _S_GV, _S_MK, _S_MV = range(10)
+_S_LENS, _S_Q, _S_K, _S_V, _S_NEEDLE, _S_OFFSET, _S_GK, _S_GV, _S_MK, _S_MV, _S_DO = range(11)
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
@@ -183,6 +183,13 @@ class Workload:
     def q(self, b: int) -> np.ndarray:
         """Queries of sequence b: [hq, rows_b, d] (rows at positions q_start[b] + t)."""
         r = _rng(self.seed, _S_Q, b)
+        x = r.standard_normal((self.hq, self.rows[b], self.d), dtype=np.float32)
+        return self._finish(x)
+
+    def grad_out(self, b: int) -> np.ndarray:
+        """Output gradient dO of sequence b for a backward pass: [hq, rows_b, d], N(0, 1) entries
+        in the workload dtype (its own stream, so the other inputs do not change)."""
+        r = _rng(self.seed, _S_DO, b)
         x = r.standard_normal((self.hq, self.rows[b], self.d), dtype=np.float32)
         return self._finish(x)
 
