@@ -7,7 +7,7 @@ decode for the whole batch; the block representatives are resident (computed onc
 context, like the KV cache itself) and are timed separately under extra.reps.
 Throughput = algorithmic bytes of the step / step time; the L2s and the 256 MB MALL are
 flushed (1 GiB read) before every timed step, outside the timed interval, so bytes come
-from HBM.  extra.* holds the other workloads: causal prefill (TFLOP/s), the SSA-style gist
+from HBM.  extra.* holds the other workloads: causal prefill (TFLOP/s) and its backward, the SSA-style gist
 decode, and the mixed variable-length batch at sparsity 0.95 (prefill TFLOP/s, decode GB/s).
 
 Usage: python bench.py [--steps K] [--warmup W] [--only NAME,...] [--no-cpu-baseline]
@@ -228,7 +228,7 @@ def prefill_step_setup(sas, w, inp):
                         sel_mode=w.sel, idx=idx, nsel=nsel, gate=gate)
         attend()
 
-    return dict(step=step, attend=attend, reps=make_reps), dict(reps=reps, idx=idx, nsel=nsel, O=O)
+    return dict(step=step, attend=attend, reps=make_reps), dict(reps=reps, idx=idx, nsel=nsel, gate=gate, O=O)
 
 
 # ------------------------------------------------------------------------------------------------
@@ -370,7 +370,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="decode,paged,reps,prefill,gist,hssa,mixed",
+    ap.add_argument("--only", default="decode,paged,reps,prefill,backward,gist,hssa,mixed",
                     help="comma list of measurements: decode,reps,prefill,gist,mixed,copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -503,6 +503,37 @@ def main():
                        "flops": fl["flops"], "sparsity": round(fl["sparsity"], 4)}
         log(f"[bench] {name}: prefill {t_att:.3f} ms -> {tf:.0f} TFLOP/s; step {t_step:.3f} ms; "
             f"sparsity {fl['sparsity']:.3f}")
+        return fns, bufs, fl
+
+    def backward_measure(name, w, inp, desc, fns, bufs, fl):
+        """Gradients of the sparse prefill (loss sum(O * dO)) for the step's own lists and O."""
+        import numpy as np
+        fns["attend"]()
+        dO = torch.zeros_like(inp.Q)
+        dO[0] = torch.from_numpy(np.ascontiguousarray(w.grad_out(0))).to(torch.bfloat16).to(dO.device)
+        f32 = dict(dtype=torch.float32, device=inp.Q.device)
+        B, hq, tq, d = inp.Q.shape
+        _, hkv, lmax, _ = inp.K.shape
+        has_gate = bufs["gate"] is not None
+        grads = (torch.empty(B, hq, tq, d, **f32), torch.zeros(B, hkv, lmax, d, **f32),
+                 torch.zeros(B, hkv, lmax, d, **f32), torch.empty(bufs["idx"].shape, **f32) if has_gate else None,
+                 torch.empty(bufs["idx"].shape, **f32) if has_gate else None)
+        need = sas.prefill_backward_workspace_bytes(B, hq, hkv, d, w.block, lmax, inp.seq_lens, tq, w.sel,
+                                                    bufs["idx"].shape[1], has_gate)
+        ws = torch.empty(max(1, need), dtype=torch.uint8, device=inp.Q.device)
+
+        def backward():
+            sas.sparse_prefill_backward(inp.Q, inp.K, inp.V, bufs["O"], dO, inp.seq_lens, w.block, inp.q_start,
+                                        bufs["idx"], bufs["nsel"], bufs["gate"], sel_mode=w.sel, workspace=ws,
+                                        grads=grads)
+        t_bwd, _ = timer.time(backward, k_small, 2)
+        bflops = 2.5 * fl["flops"]  # 10 d per visible pair: S, dP, dQ, dK, dV (the forward's 4 d x 2.5)
+        tf = bflops / (t_bwd * 1e-3) / 1e12
+        extra[name] = {"workload": desc, "backward_ms": round(t_bwd, 4), "TFLOP/s": round(tf, 1),
+                       "pct_mfma_peak": round(100 * tf / BF16_PEAK_TFLOPS, 2), "flops": bflops,
+                       "workspace_bytes": need}
+        log(f"[bench] {name}: backward {t_bwd:.3f} ms -> {tf:.0f} TFLOP/s")
+        del grads, ws, dO
 
     def decode_measure(name, w, inp, desc, gist=False):
         fns, bufs = decode_step_setup(sas, w, inp, gist=gist)
@@ -521,7 +552,11 @@ def main():
         w3 = Workload(3)
         log("[bench] generating the 32K prefill workload")
         inp3 = upload(w3, [0])
-        prefill_measure("prefill_32k", w3, inp3, "prefill_b1_h28x4_d128_32768_blk128_top1/8+sink+current_gate")
+        pf = prefill_measure("prefill_32k", w3, inp3, "prefill_b1_h28x4_d128_32768_blk128_top1/8+sink+current_gate")
+        if "backward" in only:
+            backward_measure("prefill_backward_32k", w3, inp3,
+                             "backward of prefill_b1_h28x4_d128_32768_blk128_top1/8+sink+current_gate", *pf)
+        del pf
         del inp3
         torch.cuda.empty_cache()
     if "gist" in only:

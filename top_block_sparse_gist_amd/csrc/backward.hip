@@ -13,17 +13,17 @@
 //   bwd_clear  zero the selection bitmap and per-block counts (a fill kernel)
 //   bwd_mark   one lane per list entry: set the unit's bit in its block's row, count it, note the
 //              entry's list position
-//   bwd_plan   one workgroup per (sequence, KV head): cut each key tile's unit list into segments of
-//              bounded work; zero the dK/dV rows of tiles cut into more than one segment
+//   bwd_plan   one workgroup per (sequence, KV head): cut each block's unit list into segments of
+//              bounded work; zero the dK/dV rows of blocks cut into more than one segment
 //   bwd_dq     a unit's row tile, as in the forward (S^T = K Q^T with Q^T in registers): pass 1 walks
 //              the list for each row's log-sum-exp, pass 2 recomputes P, dP^T = V dO^T and dS, and
 //              accumulates dQ^T += K^T dS^T (transposing LDS reads of the K tile); writes LSE, D_row
 //              and per-32-row partial sums of dgate
-//   bwd_dkv    a (64-key tile, segment): the K and V tile stays in LDS while the units that selected
-//              the tile's block stream their rows through LDS 32 at a time (one wave per 32 keys);
+//   bwd_dkv    a (block, segment): K^T in registers and V in LDS while the units that selected the
+//              block stream their rows through LDS 32 at a time (one wave per 32 keys);
 //              S = Q K^T, dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS (transposing LDS reads)
 //   bwd_gate   per unit: dgate (partials summed in a fixed order) and dscore
-// dQ, dgate and dscore are deterministic; dK and dV too, except in tiles whose unit list was cut
+// dQ, dgate and dscore are deterministic; dK and dV too, except in blocks whose unit list was cut
 // into several segments (their partial sums meet in fp32 atomic adds).
 #include <algorithm>
 #include <numeric>
@@ -135,6 +135,29 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t *lds, int ks, int dt
   return as_bf8(w);
 }
 
+// Per-lane element offsets of the reads above, computed once so that a loop keeps a few registers
+// of addresses (the k-step, the tensor and the buffer only add constants):
+//   row[kk]: chunk 2kk + half of row `col` (rows_dot with row0 = 0; the same for row0 = 32w)
+//   tlo[dt], thi[dt]: tr_operand's two reads at ks = 0 (ks adds 16 ks rows)
+template <int D>
+struct LdsOffsets {
+  int row[D / 16], tlo[D / 32], thi[D / 32];
+  __device__ __forceinline__ LdsOffsets(int col, int half) {
+    const int f = swz<D>(col);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) row[kk] = col * D + 8 * ((2 * kk + half) ^ f);
+    const int c16 = col & 15, chi = col >> 4;
+    const int rlo = 4 * half + (c16 >> 2), rhi = rlo + 8;
+    const int sub = 4 * (c16 & 1);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int chunk = 4 * dt + 2 * chi + ((c16 & 3) >> 1);
+      tlo[dt] = rlo * D + 8 * (chunk ^ swz<D>(rlo)) + sub;
+      thi[dt] = rhi * D + 8 * (chunk ^ swz<D>(rhi)) + sub;
+    }
+  }
+};
+
 // registers 8 (ks & 1) .. + 7 of accumulator a as a bf16 B operand
 __device__ __forceinline__ bf16x8 pack_operand(const f32x16 &a, int r0) {
   u32x4 w;
@@ -174,8 +197,8 @@ __global__ __launch_bounds__(256) void bwd_mark_kernel(const int32_t *__restrict
   if (epos) epos[row * UG + ug] = (int16_t)e;
 }
 
-// Work items of the dK/dV kernel: key tile kt, matches first .. first+count-1 of its block's unit
-// list (in unit order), multi = the tile has several items.
+// Work items of the dK/dV kernel: block kt, matches first .. first+count-1 of its unit list (in
+// unit order), multi = the block has several items.
 struct BwdItem {
   int32_t kt, first, count, multi;
 };
@@ -204,7 +227,7 @@ __device__ __forceinline__ int block_scan256(int v, int *lds4, int *tot) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void bwd_plan_kernel(SeqTable st, int hkv, int NBm, int tpb, int segm, int cap,
+__global__ __launch_bounds__(256) void bwd_plan_kernel(SeqTable st, int hkv, int NBm, int blk, int segm, int cap,
                                                       const int32_t *__restrict__ counts, BwdItem *items,
                                                       int32_t *icount, float *dK, float *dV, int64_t kb, int64_t kh,
                                                       int64_t kt_) {
@@ -214,13 +237,13 @@ __global__ __launch_bounds__(256) void bwd_plan_kernel(SeqTable st, int hkv, int
   const int pair = blockIdx.x, tid = threadIdx.x;
   const int b = pair / hkv, g = pair % hkv;
   const int L = st.len[b];
-  const int T = cdiv(L, 64);
+  const int nb = cdiv(L, blk);
   int off = 0;
-  for (int k0 = 0; k0 < T; k0 += 256) {
+  for (int k0 = 0; k0 < nb; k0 += 256) {
     if (tid == 0) nmulti = 0;
-    const int kt = k0 + tid;
-    const bool valid = kt < T;
-    const int cnt = valid ? counts[(int64_t)pair * NBm + kt / tpb] : 0;
+    const int kt = k0 + tid;  // block
+    const bool valid = kt < nb;
+    const int cnt = valid ? counts[(int64_t)pair * NBm + kt] : 0;
     const int nseg = valid ? max(1, cdiv(cnt, segm)) : 0;
     int tot;
     const int ex = block_scan256(nseg, scan4, &tot);
@@ -230,12 +253,12 @@ __global__ __launch_bounds__(256) void bwd_plan_kernel(SeqTable st, int hkv, int
     }
     if (nseg > 1) multi[atomicAdd(&nmulti, 1)] = kt;
     __syncthreads();
-    // tiles cut into several segments accumulate with atomic adds: clear their rows first
+    // blocks cut into several segments accumulate with atomic adds: clear their rows first
     const int nm = nmulti;
     constexpr int V4 = D / 4;  // float4 per row
-    for (int x = tid; x < nm * 64 * V4; x += 256) {
-      const int m = x / (64 * V4), r = (x / V4) % 64, c4 = x % V4;
-      const int key = multi[m] * 64 + r;
+    for (int x = tid; x < nm * blk * V4; x += 256) {
+      const int m = x / (blk * V4), r = (x / V4) % blk, c4 = x % V4;
+      const int key = multi[m] * blk + r;
       if (key < L) {
         const int64_t o = (int64_t)b * kb + (int64_t)g * kh + (int64_t)key * kt_ + 4 * c4;
         *reinterpret_cast<f32x4 *>(dK + o) = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -447,8 +470,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
 // ---------------------------------------------------------------------------------------------
 // dK, dV
 // ---------------------------------------------------------------------------------------------
+// One workgroup per (block j, segment of its unit list), BLK / 32 waves, wave w owning keys
+// 32w .. 32w+31 of the block: K^T of those keys stays in registers and V in LDS for the whole walk,
+// while the units' rows stream through LDS 32 at a time (double-buffered: the copy of the next
+// 32 rows overlaps the compute of these).  A loaded row serves BLK keys.
 template <int D, int BLK>
-__global__ __launch_bounds__(128, 2) void bwd_dkv_kernel(
+__global__ __launch_bounds__(BLK * 2, 2) void bwd_dkv_kernel(
     SeqTable st, const uint16_t *__restrict__ Q, int64_t qb, int64_t qh, int64_t qt, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, int64_t kb, int64_t kh, int64_t kt, const uint16_t *__restrict__ dO, int64_t ob,
     int64_t oh, int64_t ot, int tq, int S, int QB, int G, int per_head, int hq, int hkv, int npairs, int pchunks,
@@ -457,18 +484,18 @@ __global__ __launch_bounds__(128, 2) void bwd_dkv_kernel(
     const float *__restrict__ gate, int kcap, const float *__restrict__ lse_ws, const float *__restrict__ dd_ws,
     float scale_log2, float scale, float *__restrict__ dK, float *__restrict__ dV, int64_t gb, int64_t gh,
     int64_t gt) {
-  constexpr int NKK = D / 16, NDT = D / 32, CPR = D / 8, tpb = BLK / 64;
-  constexpr int SEGMAX = 64;  // units per work item (the host's segment size is at most this)
-  __shared__ __attribute__((aligned(16))) uint16_t qs[32 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t dos[32 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t klds[64 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t vlds[64 * D];
-  __shared__ __attribute__((aligned(16))) float lse_s[32];
-  __shared__ __attribute__((aligned(16))) float dd_s[32];
-  __shared__ __attribute__((aligned(16))) int lim_s[32];
-  __shared__ int mu[SEGMAX];
-  __shared__ float mgl[SEGMAX];
-  __shared__ int scan2[2];
+  constexpr int NKK = D / 16, NDT = D / 32, CPR = D / 8, NWV = BLK / 32, NT = NWV * 64;
+  constexpr int NI = 32 * CPR / NT;  // 16-byte copies per thread per staged tensor
+  static_assert(NI >= 1 && 32 * CPR % NT == 0, "staging split");
+  __shared__ __attribute__((aligned(16))) uint16_t qs[2][32 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t dos[2][32 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vlds[BLK * D];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][64];
+  __shared__ __attribute__((aligned(16))) float dd_s[2][64];
+  __shared__ int mu[BWD_SEGMAX];
+  __shared__ float mgl[BWD_SEGMAX];
+  __shared__ __attribute__((aligned(16))) i32x4 ginfo[BWD_SEGMAX];  // h0, t_lo, c, rows | inverse << 8
+  __shared__ int scan_w[NWV];
 
   const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
   const int cid = xcd + 8 * (q / Ic);
@@ -479,18 +506,36 @@ __global__ __launch_bounds__(128, 2) void bwd_dkv_kernel(
   const BwdItem it = items[(int64_t)pair * cap + n];
   const int b = pair / hkv, g = pair % hkv;
   const int L = st.len[b], q0 = st.q0[b];
-  const int j = it.kt / tpb;
-  const int key0 = it.kt * 64;
+  const int j = it.kt;
+  const int key0 = j * BLK;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
+  const int mykey = key0 + wave * 32 + col;
+
+  // ---- V tile into LDS, K^T of this wave's keys into registers (rows past L re-read row L-1;
+  //      their keys are masked below)
+  {
+    const uint32_t row_bytes = (uint32_t)(kt * 2);
+    const uint32_t slab = (uint32_t)(L - 1) * row_bytes + D * 2;
+    const __amdgpu_buffer_rsrc_t vrs = dev_rsrc(V + b * kb + (int64_t)g * kh, slab);
+#pragma unroll
+    for (int t0 = 0; t0 < BLK; t0 += 64)
+      copy_tile<D, NWV>(vrs, vlds + t0 * D, key0 + t0, L - 1, row_bytes, wave, lane);
+  }
+  bf16x8 kreg[NKK];
+  {
+    const int64_t ro = b * kb + (int64_t)g * kh + (int64_t)min(mykey, L - 1) * kt + 8 * half;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) kreg[kk] = as_bf8(*reinterpret_cast<const u32x4 *>(K + ro + 16 * kk));
+  }
 
   // ---- the item's units: ranks first .. first+count-1 of the set bits of block j's row
-  const int cnt = min(it.count, SEGMAX);
+  const int cnt = min(it.count, BWD_SEGMAX);
   if (cnt > 0) {
     const uint32_t *row = bits + ((int64_t)pair * NBm + j) * W;
     int base = 0;
-    for (int w0 = 0; w0 < W && base < it.first + cnt; w0 += 128) {
+    for (int w0 = 0; w0 < W && base < it.first + cnt; w0 += NT) {
       const int w = w0 + tid;
       uint32_t word = w < W ? row[w] : 0u;
       const int pc = __popc(word);
@@ -500,116 +545,152 @@ __global__ __launch_bounds__(128, 2) void bwd_dkv_kernel(
         const int y = __shfl_up(x, o, 64);
         if (lane >= o) x += y;
       }
-      if (lane == 63) scan2[wave] = x;
+      if (lane == 63) scan_w[wave] = x;
       __syncthreads();
-      int r = base + x - pc + (wave == 1 ? scan2[0] : 0);
+      int before = 0, all = 0;
+#pragma unroll
+      for (int v = 0; v < NWV; ++v) {
+        before += v < wave ? scan_w[v] : 0;
+        all += scan_w[v];
+      }
+      int r = base + before + x - pc;
       while (word) {
         const int bit = __ffs(word) - 1;
         word &= word - 1;
         if (r >= it.first && r < it.first + cnt) mu[r - it.first] = w * 32 + bit;
         ++r;
       }
-      base += scan2[0] + scan2[1];
+      base += all;
       __syncthreads();
     }
-    for (int k = tid; k < cnt; k += 128) {
+    for (int k = tid; k < cnt; k += NT) {
       const int ugi = mu[k];
+      const int i = per_head ? ugi / G : ugi;
+      const int s = per_head ? g * G + ugi % G : g;
+      const int64_t u = ((int64_t)b * S + s) * QB + i;
       float gl2 = 0.f;
       if (gate) {
-        const int i = per_head ? ugi / G : ugi;
-        const int s = per_head ? g * G + ugi % G : g;
-        const int64_t u = ((int64_t)b * S + s) * QB + i;
         const int e = epos[((int64_t)pair * NBm + j) * UG + ugi];
         gl2 = gate[u * kcap + e] * LOG2E;
       }
       mgl[k] = gl2;
+      const UnitGeo x = unit_geo(st, u, S, QB, G, per_head, tq, BLK);
+      // rows <= 128 and flattened rows < 2^13: f / rows = (f * inv) >> 20 exactly
+      const int inv = ((1 << 20) + x.rows - 1) / max(x.rows, 1);
+      ginfo[k] = i32x4{x.h0, x.t_lo, x.c, x.rows | (inv << 8)};
     }
-    __syncthreads();
   }
+  struct Geo {
+    int h0, t_lo, c, rows, inv, F;
+  };
+  auto geo_of = [&](int k) {
+    const i32x4 v = ginfo[k];
+    const int rows = v[3] & 255, inv = (int)((uint32_t)v[3] >> 8);
+    return Geo{v[0], v[1], v[2], rows, inv, rows * (per_head ? 1 : G)};
+  };
+  auto head_row = [](const Geo &x, int f, int &hh, int &tt) {
+    const int qd = (int)(((uint32_t)f * (uint32_t)x.inv) >> 20);
+    hh = x.h0 + qd;
+    tt = x.t_lo + f - qd * x.rows;
+  };
+  // issue the copies of 32 rows (from flattened row c0 of unit k) into buffer buf
+  auto stage = [&](int k, int c0, int buf) {
+    const Geo x = geo_of(k);
+#pragma unroll
+    for (int y = 0; y < NI; ++y) {
+      const int e = y * NT + tid;
+      const int r = e / CPR, cs = e % CPR;
+      int hh, tt;
+      head_row(x, min(c0 + r, x.F - 1), hh, tt);
+      const int off = 8 * (cs ^ swz<D>(r));
+      load_lds16(Q + b * qb + (int64_t)hh * qh + (int64_t)tt * qt + off, qs[buf] + 8 * (y * NT + wave * 64));
+      load_lds16(dO + b * ob + (int64_t)hh * oh + (int64_t)tt * ot + off, dos[buf] + 8 * (y * NT + wave * 64));
+    }
+    if (wave == 0) {
+      int hh, tt;
+      head_row(x, min(c0 + min(lane, 31), x.F - 1), hh, tt);
+      const int64_t o = ((int64_t)b * hq + hh) * tq + tt;
+      load_lds<4>(lse_ws + o, lse_s[buf]);
+      load_lds<4>(dd_ws + o, dd_s[buf]);
+    }
+  };
 
-  // ---- the K and V tile (B operands of S and dP: wave w uses keys 32w .. 32w+31; rows past L
-  //      re-read row L-1 and are masked below)
-  const int mykey = key0 + wave * 32 + col;
-  {
-    const uint32_t row_bytes = (uint32_t)(kt * 2);
-    const uint32_t slab = (uint32_t)(L - 1) * row_bytes + D * 2;
-    copy_tile<D, 2>(dev_rsrc(K + b * kb + (int64_t)g * kh, slab), klds, key0, L - 1, row_bytes, wave, lane);
-    copy_tile<D, 2>(dev_rsrc(V + b * kb + (int64_t)g * kh, slab), vlds, key0, L - 1, row_bytes, wave, lane);
-  }
   f32x16 adk[NDT], adv[NDT];
 #pragma unroll
   for (int x = 0; x < NDT; ++x)
 #pragma unroll
     for (int r = 0; r < 16; ++r) adk[x][r] = adv[x][r] = 0.f;
 
-  for (int k = 0; k < cnt; ++k) {
-    const int ugi = mu[k];
-    const int i = per_head ? ugi / G : ugi;
-    const int s = per_head ? g * G + ugi % G : g;
-    const int64_t u = ((int64_t)b * S + s) * QB + i;
-    const UnitGeo ugeo = unit_geo(st, u, S, QB, G, per_head, tq, BLK);
-    const int F = ugeo.rows * ugeo.nh;
+  const LdsOffsets<D> lo(col, half);
+  __syncthreads();  // mu, mgl visible
+  int k = 0, c0 = 0, buf = 0;
+  if (cnt > 0) stage(0, 0, 0);
+  while (k < cnt) {
+    const Geo x = geo_of(k);
+    const int F = x.F;
     const float gl2 = mgl[k];
-    for (int c0 = 0; c0 < F; c0 += 32) {
-      // stage 32 rows of Q and dO (swizzled) and their LSE, D and position limit
-#pragma unroll
-      for (int x = 0; x < 32 * CPR / 128; ++x) {
-        const int e = x * 128 + tid;
-        const int r = e / CPR, cs = e % CPR;
-        const int fc = min(c0 + r, F - 1);
-        const int hh = ugeo.h0 + fc / ugeo.rows, tt = ugeo.t_lo + fc % ugeo.rows;
-        const int off = 8 * (cs ^ swz<D>(r));
-        load_lds16(Q + b * qb + (int64_t)hh * qh + (int64_t)tt * qt + off, qs + 8 * (x * 128 + wave * 64));
-        load_lds16(dO + b * ob + (int64_t)hh * oh + (int64_t)tt * ot + off, dos + 8 * (x * 128 + wave * 64));
-      }
-      if (tid < 32) {
-        const int f = c0 + tid;
-        if (f < F) {
-          const int hh = ugeo.h0 + f / ugeo.rows, tt = ugeo.t_lo + f % ugeo.rows;
-          const int64_t o = ((int64_t)b * hq + hh) * tq + tt;
-          lse_s[tid] = lse_ws[o];
-          dd_s[tid] = dd_ws[o];
-          lim_s[tid] = q0 + tt;
-        } else {
-          lse_s[tid] = 0.f;
-          dd_s[tid] = 0.f;
-          lim_s[tid] = -1;
-        }
-      }
-      wait_stores();
-      __syncthreads();
-      // S and dP (rows x this wave's keys): register r holds row 8(r/4) + 4half + r%4, key col
-      // (P overwrites S and dS overwrites dP in place)
-      f32x16 pa = rows_dot_lds<D>(qs, klds, wave * 32, col, half);
-      f32x16 dsa = rows_dot_lds<D>(dos, vlds, wave * 32, col, half);
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&lse_s[8 * rb + 4 * half]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&dd_s[8 * rb + 4 * half]);
-        const i32x4 m4 = *reinterpret_cast<const i32x4 *>(&lim_s[8 * rb + 4 * half]);
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int r = 4 * rb + x;
-          const float p = mykey > m4[x] ? 0.f : __builtin_amdgcn_exp2f(fmaf(pa[r], scale_log2, gl2 - l4[x]));
-          pa[r] = p;
-          dsa[r] = p * (dsa[r] - d4[x]);
-        }
-      }
-      // dV^T += dO^T P, dK^T += Q^T dS over the 32 rows (two 16-row steps)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 pop = pack_operand(pa, 8 * ks);
-        const bf16x8 dsop = pack_operand(dsa, 8 * ks);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          adv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(dos, ks, dt, col, half), pop, adv[dt], 0, 0, 0);
-          adk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(qs, ks, dt, col, half), dsop, adk[dt], 0, 0, 0);
-        }
-      }
-      __syncthreads();
+    const bool diag = j == x.c;
+    // the next step (the following 32 rows of this unit, or the first rows of the next unit)
+    int kn = k, cn = c0 + 32;
+    if (cn >= F) {
+      ++kn;
+      cn = 0;
     }
+    wait_stores();
+    __syncthreads();  // this step's rows have landed; every wave is done with the other buffer
+    if (kn < cnt) stage(kn, cn, buf ^ 1);
+    const uint16_t *qsb = qs[buf], *dsb = dos[buf];
+    // S and dP (rows x this wave's keys): register r holds row 8(r/4) + 4half + r%4, key col
+    f32x16 pa, dsa;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pa[r] = dsa[r] = 0.f;
+    const uint16_t *vw = vlds + wave * 32 * D;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const u32x4 qv = *reinterpret_cast<const u32x4 *>(qsb + lo.row[kk]);
+      pa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(qv), kreg[kk], pa, 0, 0, 0);
+      const u32x4 dv = *reinterpret_cast<const u32x4 *>(dsb + lo.row[kk]);
+      const u32x4 vv = *reinterpret_cast<const u32x4 *>(vw + lo.row[kk]);
+      dsa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(dv), as_bf8(vv), dsa, 0, 0, 0);
+    }
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&lse_s[buf][8 * rb + 4 * half]);
+      const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&dd_s[buf][8 * rb + 4 * half]);
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        const int r = 4 * rb + y;
+        const int f = c0 + 8 * rb + 4 * half + y;
+        bool vis = f < F && mykey < L;
+        if (diag) {
+          int hh, tt;
+          head_row(x, f, hh, tt);
+          vis = vis && mykey <= q0 + tt;
+        }
+        const float p = vis ? __builtin_amdgcn_exp2f(fmaf(pa[r], scale_log2, gl2 - l4[y])) : 0.f;
+        pa[r] = p;
+        dsa[r] = p * (dsa[r] - d4[y]);
+      }
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS over the 32 rows (two 16-row steps)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 pop = pack_operand(pa, 8 * ks);
+      const bf16x8 dsop = pack_operand(dsa, 8 * ks);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const u32x2 dlo = lds_read_tr16(dsb + lo.tlo[dt] + 16 * ks * D), dhi = lds_read_tr16(dsb + lo.thi[dt] + 16 * ks * D);
+        const u32x2 qlo = lds_read_tr16(qsb + lo.tlo[dt] + 16 * ks * D), qhi = lds_read_tr16(qsb + lo.thi[dt] + 16 * ks * D);
+        const u32x4 dw = {dlo[0], dlo[1], dhi[0], dhi[1]}, qw = {qlo[0], qlo[1], qhi[0], qhi[1]};
+        adv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(dw), pop, adv[dt], 0, 0, 0);
+        adk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(qw), dsop, adk[dt], 0, 0, 0);
+      }
+    }
+    k = kn;
+    c0 = cn;
+    buf ^= 1;
   }
-  wait_stores();  // no copy into LDS may outlive the workgroup (an item with no units copied the tile)
+  wait_stores();  // no copy into LDS may outlive the workgroup
   // ---- write (lane holds dims 32dt + 8(r/4) + 4half + r%4 of key mykey)
   if (mykey >= L) return;
   const int64_t o = b * gb + (int64_t)g * gh + (int64_t)mykey * gt;
@@ -623,9 +704,9 @@ __global__ __launch_bounds__(128, 2) void bwd_dkv_kernel(
       const f32x4 vv = {adv[dt][4 * rb], adv[dt][4 * rb + 1], adv[dt][4 * rb + 2], adv[dt][4 * rb + 3]};
       if (it.multi) {
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          unsafeAtomicAdd(dK + o + dim + x, vk[x]);
-          unsafeAtomicAdd(dV + o + dim + x, vv[x]);
+        for (int y = 0; y < 4; ++y) {
+          unsafeAtomicAdd(dK + o + dim + y, vk[y]);
+          unsafeAtomicAdd(dV + o + dim + y, vv[y]);
         }
       } else {
         *reinterpret_cast<f32x4 *>(dK + o + dim) = vk;
@@ -684,10 +765,9 @@ BwdPlan bwd_plan(const sas_problem &p, int32_t tq, int32_t sel_mode, int32_t kca
   x.UG = x.QB * (per_head ? G : 1);
   x.W = cdiv(x.UG, 32);
   x.npairs = p.batch * p.hkv;
-  x.tpb = p.block / 64;
-  x.T = cdiv(p.max_len, 64);
-  x.segm = std::max(1, std::min(64, 2048 / std::max(1, rows_max * x.nh)));
-  x.cap = (int)std::min<int64_t>(INT32_MAX / 2, x.T + cdiv64((int64_t)x.tpb * x.UG * kcap, x.segm));
+  // a segment holds about BWD_SEG_ROWS flattened rows (its units' rows x heads)
+  x.segm = std::max(1, std::min(BWD_SEGMAX, BWD_SEG_ROWS / std::max(1, rows_max * x.nh)));
+  x.cap = (int)std::min<int64_t>(INT32_MAX / 2, x.NBm + cdiv64((int64_t)x.UG * kcap, x.segm));
   auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
   size_t off = 0;
   const size_t rowsz = (size_t)p.batch * p.hq * tq * sizeof(float);
@@ -739,7 +819,7 @@ static hipError_t bwd_dispatch(const sas_problem &p, const SeqTable &st, const B
     const int64_t m = pl.units * kcap;
     hipLaunchKernelGGL(bwd_mark_kernel, dim3((unsigned)std::max<int64_t>(1, cdiv64(m, 256))), dim3(256), 0, s, idx,
                        nsel, pl.units, kcap, S, pl.QB, G, per_head, p.hkv, pl.NBm, pl.W, pl.UG, bits, counts, epos);
-    hipLaunchKernelGGL((bwd_plan_kernel<D>), dim3(pl.npairs), dim3(256), 0, s, st, p.hkv, pl.NBm, pl.tpb, pl.segm,
+    hipLaunchKernelGGL((bwd_plan_kernel<D>), dim3(pl.npairs), dim3(256), 0, s, st, p.hkv, pl.NBm, p.block, pl.segm,
                        pl.cap, (const int32_t *)counts, items, icount, dK, dV, dkvs[0], dkvs[1], dkvs[2]);
   }
   // dQ, LSE, D, gate partials
@@ -762,7 +842,7 @@ static hipError_t bwd_dispatch(const sas_problem &p, const SeqTable &st, const B
     const int pchunks = 8 / std::gcd(pl.npairs, 8);
     const int Ic = cdiv(pl.cap, pchunks);
     const int64_t nwg = (int64_t)8 * cdiv(pl.npairs * pchunks, 8) * Ic;
-    hipLaunchKernelGGL((bwd_dkv_kernel<D, BLK>), dim3((unsigned)nwg), dim3(128), 0, s, st, q16, qs[0], qs[1], qs[2],
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, BLK>), dim3((unsigned)nwg), dim3(BLK * 2), 0, s, st, q16, qs[0], qs[1], qs[2],
                        k16, v16, kvs[0], kvs[1], kvs[2], do16, os[0], os[1], os[2], tq, S, pl.QB, G, per_head, p.hq,
                        p.hkv, pl.npairs, pchunks, Ic, pl.cap, (const BwdItem *)items, (const int32_t *)icount,
                        (const uint32_t *)bits, (const int16_t *)epos, pl.NBm, pl.W, pl.UG, gate, kcap, lse, dd,

@@ -275,8 +275,11 @@ hipError_t launch_hssa_decode(const sas_problem &p, const SeqTable &st, const vo
 // [units, gslots, kcap] fp32 (with a gate); selection bitmap [pairs, NBm, W] u32 then per-block
 // counts [pairs, NBm]; entry positions [pairs, NBm, UG] int16 (with a gate); work items
 // [pairs, cap] x 16 bytes; item counts [pairs].
+constexpr int BWD_SEGMAX = 256;       // units per dK/dV work item
+constexpr int BWD_SEG_ROWS = 32768;   // flattened rows per dK/dV work item (a block's list is cut
+                                      // into items of about this much work)
 struct BwdPlan {
-  int QB, nh, gslots, NBm, UG, W, npairs, tpb, T, segm, cap;
+  int QB, nh, gslots, NBm, UG, W, npairs, segm, cap;
   int64_t units, clear_words;
   size_t off_lse, off_dd, off_gpart, off_bits, off_epos, off_items, off_icount, bytes;
 };
