@@ -508,7 +508,10 @@ def main():
     def backward_measure(name, w, inp, desc, fns, bufs, fl):
         """Gradients of the sparse prefill (loss sum(O * dO)) for the step's own lists and O."""
         import numpy as np
-        fns["attend"]()
+        # the training forward keeps each row's log-sum-exp for the backward
+        lse = torch.empty(inp.Q.shape[:3], dtype=torch.float32, device=inp.Q.device)
+        sas.sparse_prefill(inp.Q, inp.K, inp.V, inp.seq_lens, w.block, inp.q_start, bufs["idx"], bufs["nsel"],
+                           bufs["gate"], sel_mode=w.sel, O=bufs["O"], lse=lse)
         dO = torch.zeros_like(inp.Q)
         dO[0] = torch.from_numpy(np.ascontiguousarray(w.grad_out(0))).to(torch.bfloat16).to(dO.device)
         f32 = dict(dtype=torch.float32, device=inp.Q.device)
@@ -525,7 +528,7 @@ def main():
         def backward():
             sas.sparse_prefill_backward(inp.Q, inp.K, inp.V, bufs["O"], dO, inp.seq_lens, w.block, inp.q_start,
                                         bufs["idx"], bufs["nsel"], bufs["gate"], sel_mode=w.sel, workspace=ws,
-                                        grads=grads)
+                                        grads=grads, lse=lse)
         t_bwd, _ = timer.time(backward, k_small, 2)
         bflops = 2.5 * fl["flops"]  # 10 d per visible pair: S, dP, dQ, dK, dV (the forward's 4 d x 2.5)
         tf = bflops / (t_bwd * 1e-3) / 1e12

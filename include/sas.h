@@ -18,6 +18,7 @@
  *   sas_sparse_prefill / sas_sparse_decode  attention over the selected blocks only
  *   sas_hssa_select_decode / sas_hssa_decode  two-level gist selection (meta-gists) and its
  *                     attention, for decode
+ *   sas_sparse_prefill_lse  sas_sparse_prefill that also keeps each row's log-sum-exp (training)
  *   sas_sparse_prefill_backward  gradients of the sparse prefill (Q, K, V, gates, scores)
  *
  * Conventions shared by every entry point
@@ -183,6 +184,17 @@ sas_status sas_sparse_prefill(const sas_problem *p, const void *Q, const int64_t
                               int32_t kcap, float scale, void *O, const int64_t o_stride[3],
                               void *stream);
 
+/* sas_sparse_prefill that also writes each row's log-sum-exp of its logits (natural log):
+ *   lse[(b * Hq + h) * tq + t] = log sum_s exp(scale * q . k_s + gate_u(block(s))) over the row's
+ *   visible keys, fp32, for the rows the call computes (others untouched).  A training step keeps it
+ *   for sas_sparse_prefill_backward.  lse NULL: same as sas_sparse_prefill.  bf16 only (fp32:
+ *   SAS_ERR_UNSUPPORTED when lse is given). */
+sas_status sas_sparse_prefill_lse(const sas_problem *p, const void *Q, const int64_t q_stride[3],
+                                  const void *K, const void *V, const int64_t kv_stride[3], int32_t tq,
+                                  const int32_t *q_start, int32_t sel_mode, const int32_t *idx,
+                                  const int32_t *nsel, const float *gate, int32_t kcap, float scale, void *O,
+                                  const int64_t o_stride[3], float *lse, void *stream);
+
 /* A2 + A3 fused for decode: the scores and the selection of sas_block_scores (q_start = NULL)
  * followed by sas_topk_select, in one launch ([GSA] section 4 pseudo-code steps 1-2).  Same
  * outputs (scores rows j <= c, idx, nsel, gate).  Needs every current block c <= 2048 (e.g.
@@ -317,6 +329,8 @@ const char *sas_last_error(void);
  *   dscore_j = dgate_j - exp(g_j) * sum_j' dgate_j'.  Padding entries get 0.  Both are required
  *   iff gate != NULL (without a gate they are not written and may be NULL).
  *   O: the forward output (bf16, o_stride); dO: its gradient (bf16, same strides).
+ *   lse: the forward's row log-sum-exp from sas_sparse_prefill_lse ([B, Hq, tq] fp32), or NULL to
+ *   recompute it (one more pass over each unit's list).
  *   Q, K, V, idx, nsel, gate, kcap, scale: as given to sas_sparse_prefill (bf16 only).
  *   kcap <= 32767.  workspace: sas_sparse_prefill_backward_workspace(p, tq, sel_mode, kcap, gate
  *   != NULL) bytes of device scratch (no initial contents needed; it grows with the batch, the rows,
@@ -332,7 +346,8 @@ sas_status sas_sparse_prefill_backward(const sas_problem *p, const void *Q, cons
                                        const void *K, const void *V, const int64_t kv_stride[3], int32_t tq,
                                        const int32_t *q_start, int32_t sel_mode, const int32_t *idx,
                                        const int32_t *nsel, const float *gate, int32_t kcap, float scale,
-                                       const void *O, const void *dO, const int64_t o_stride[3], float *dQ,
+                                       const void *O, const void *dO, const int64_t o_stride[3],
+                                       const float *lse, float *dQ,
                                        const int64_t dq_stride[3], float *dK, float *dV,
                                        const int64_t dkv_stride[3], float *dgate, float *dscore,
                                        void *workspace, size_t workspace_bytes, void *stream);

@@ -71,3 +71,31 @@ def backward_sequence(Qb: np.ndarray, Kb: np.ndarray, Vb: np.ndarray, dOb: np.nd
         out["dgate"][key_u] = g.grad.numpy().copy()
         out["dscore"][key_u] = s_leaves[key_u].grad.numpy().copy()
     return out
+
+
+def row_logsumexp(Qb: np.ndarray, Kb: np.ndarray, L: int, q_start: int, blk: int, units, gate: bool,
+                  scale: Optional[float] = None) -> np.ndarray:
+    """Natural-log log-sum-exp of each (head, row)'s logits scale * q.k + g over its unit's visible
+    keys (the softmax normaliser of the forward above), float64 [hq, rows]; NaN for rows no unit
+    covers."""
+    hq, rows, d = Qb.shape
+    G = hq // Kb.shape[0]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = np.full((hq, rows), np.nan)
+    for u in units:
+        if u.sel is None:
+            continue
+        g = u.gate if gate else {}
+        for h in u.heads:
+            K = np.asarray(Kb[h // G], np.float64)
+            for t in range(u.t_lo, u.t_hi):
+                pos = q_start + t
+                q = np.asarray(Qb[h, t], np.float64)
+                logits = []
+                for j in u.sel:
+                    for s_ in range(j * blk, min((j + 1) * blk, L, pos + 1)):
+                        logits.append(scale * float(q @ K[s_]) + (g.get(j, 0.0) if gate else 0.0))
+                m = max(logits)
+                out[h, t] = m + math.log(sum(math.exp(x - m) for x in logits))
+    return out

@@ -312,8 +312,8 @@ def test_prefill_backward_validation_codes():
 
     def bw(gate=None, dgate=FAKE, ws=FAKE, wsb=None, q_start=qs, kcap=8, dQ=FAKE, prob=p):
         return lib.sas_sparse_prefill_backward(C.byref(prob), FAKE, q3, FAKE, FAKE, kv, 128, q_start,
-                                               _lib.SAS_SEL_GROUP, FAKE, FAKE, gate, kcap, 0.0, FAKE, FAKE, q3, dQ,
-                                               q3, FAKE, FAKE, kv, dgate, FAKE, ws,
+                                               _lib.SAS_SEL_GROUP, FAKE, FAKE, gate, kcap, 0.0, FAKE, FAKE, q3, None,
+                                               dQ, q3, FAKE, FAKE, kv, dgate, FAKE, ws,
                                                need if wsb is None else wsb, None)
 
     assert bw(q_start=None) == _lib.SAS_ERR_NULL
@@ -325,3 +325,6 @@ def test_prefill_backward_validation_codes():
     assert bw(gate=FAKE, wsb=need - 1) == _lib.SAS_ERR_WORKSPACE
     pf, af = _problem(lens=(1000, 700), dtype=_lib.SAS_F32)
     assert bw(prob=pf) == _lib.SAS_ERR_UNSUPPORTED                  # bf16 only
+    # the forward's log-sum-exp output exists on the bf16 path only
+    assert lib.sas_sparse_prefill_lse(C.byref(pf), FAKE, q3, FAKE, FAKE, kv, 128, qs, _lib.SAS_SEL_GROUP, FAKE,
+                                      FAKE, None, 8, 0.0, FAKE, q3, FAKE, None) == _lib.SAS_ERR_UNSUPPORTED

@@ -52,9 +52,11 @@ def _check(name, got, ref, stats):
     assert mean <= MEAN_REL * top + 1e-7, f"{name}: mean-abs {mean:.3e} vs max|ref| {top:.3e}"
 
 
-def run_backward_case(w: Workload, seqs=(0,)):
+def run_backward_case(w: Workload, seqs=(0,), use_lse=False):
+    """use_lse: the GPU forward writes each row's log-sum-exp (checked against the oracle's to 1e-3
+    absolute: fp32 sums of exact bf16 products) and the backward takes it instead of recomputing it."""
     seqs = list(seqs)
-    say(f"[bwd] {w.name} seqs={seqs} sel={w.sel} d={w.d} blk={w.block} gate={w.gate}")
+    say(f"[bwd] {w.name} seqs={seqs} sel={w.sel} d={w.d} blk={w.block} gate={w.gate} lse={use_lse}")
     inp = upload(w, seqs, keep_host=set(seqs))
     lens = inp.seq_lens
     B, blk, tq = len(seqs), w.block, w.tq
@@ -90,8 +92,21 @@ def run_backward_case(w: Workload, seqs=(0,)):
     t_idx = torch.from_numpy(idx).to(dev)
     t_nsel = torch.from_numpy(nsel).to(dev)
     t_gate = torch.from_numpy(gate).to(dev) if w.gate else None
+    lse = None
+    if use_lse:
+        lse = torch.full(inp.Q.shape[:3], float("nan"), dtype=torch.float32, device=dev)
+        sas.sparse_prefill(inp.Q, inp.K, inp.V, lens, blk, inp.q_start, t_idx, t_nsel, t_gate, sel_mode=w.sel,
+                           lse=lse)
+        torch.cuda.synchronize()
+        lse_h = lse.cpu().numpy()
+        for bi, b in enumerate(seqs):
+            h = inp.host[b]
+            ref = orcb.row_logsumexp(h["q"], h["k"], w.seq_lens[b], w.q_start[b], blk, res[b].units, w.gate, scale)
+            err = float(np.abs(lse_h[bi, :, :w.rows[b]] - ref).max())
+            say(f"[bwd] lse[{b}] max-abs {err:.2e}")
+            assert err <= 1e-3, f"row log-sum-exp differs by {err:.3e}"
     dQ, dK, dV, dgate, dscore = sas.sparse_prefill_backward(inp.Q, inp.K, inp.V, O, dO, lens, blk, inp.q_start,
-                                                            t_idx, t_nsel, t_gate, sel_mode=w.sel)
+                                                            t_idx, t_nsel, t_gate, sel_mode=w.sel, lse=lse)
     torch.cuda.synchronize()
     say("[bwd] gpu done")
     dQ, dK, dV = dQ.cpu().numpy(), dK.cpu().numpy(), dV.cpu().numpy()
@@ -126,6 +141,7 @@ def test_backward_group_unaligned_sink_gate():
     w = Workload(3, overrides=dict(tag="bwd_unaligned", seq_len=1000, tq=300, block=64, hq=4, hkv=2,
                                    frac_num=1, frac_den=4, sink=True, gate=True))
     run_backward_case(w)
+    run_backward_case(w, use_lse=True)
 
 
 def test_backward_per_head_d64_block128():
@@ -135,10 +151,19 @@ def test_backward_per_head_d64_block128():
     run_backward_case(w)
 
 
-def test_backward_per_head_sink_tile_split_into_segments():
-    """Block 0 is kept by every unit (64 per-head units per KV head): its key tile's unit list is
-    cut into several segments whose dK/dV partial sums meet in atomic adds."""
-    w = Workload(3, overrides=dict(tag="bwd_split", seq_len=1024, tq=1024, block=64, hq=4, hkv=1, sel="head",
+def test_backward_per_head_sink_forward_lse():
+    """Per-head units with a sink (block 0 kept by all 64 units of the KV head), the forward's row
+    log-sum-exp handed to the backward."""
+    w = Workload(3, overrides=dict(tag="bwd_headsink", seq_len=1024, tq=1024, block=64, hq=4, hkv=1, sel="head",
+                                   frac_num=0, frac_den=0, k_fixed=2, sink=True, gate=True))
+    run_backward_case(w, use_lse=True)
+
+
+def test_backward_block_list_split_into_segments():
+    """16 heads per KV head share each unit (2048 flattened rows), so a work item holds 16 units; the
+    sink block is kept by all 18 units and its list is cut into two items whose dK/dV partial sums
+    meet in atomic adds."""
+    w = Workload(3, overrides=dict(tag="bwd_split", seq_len=2304, tq=2304, block=128, hq=16, hkv=1,
                                    frac_num=0, frac_den=0, k_fixed=2, sink=True, gate=True))
     run_backward_case(w)
 
@@ -154,4 +179,4 @@ def test_backward_two_sequences_ragged():
     """Two sequences of different lengths in one call (the shorter one's rows past its length unused)."""
     w = Workload(3, overrides=dict(tag="bwd_two", seq_lens=[1300, 700], batch=2, tq=256, block=64, hq=4, hkv=2,
                                    frac_num=1, frac_den=4, sink=False, gate=True))
-    run_backward_case(w, seqs=[0, 1])
+    run_backward_case(w, seqs=[0, 1], use_lse=True)

@@ -589,3 +589,27 @@ def test_backward_all_blocks_gate_off_is_sdpa_backward():
     np.testing.assert_allclose(grads["dQ"], qt.grad.numpy(), rtol=0, atol=1e-10)
     np.testing.assert_allclose(grads["dK"], kt.grad.numpy().sum(axis=0, keepdims=True), rtol=0, atol=1e-10)
     np.testing.assert_allclose(grads["dV"], vt.grad.numpy().sum(axis=0, keepdims=True), rtol=0, atol=1e-10)
+
+
+def test_row_logsumexp_closed_forms():
+    """Row log-sum-exp of the backward oracle: with K = 0 and no gate every visible logit is 0, so it
+    equals log(number of visible keys) = log(pos + 1) under a dense causal selection; the row at
+    position 0 sees key 0 only, so it equals that one logit, scale q.k0 + g(0)."""
+    import math
+    from oracle import sas_oracle as o
+    from oracle import sas_backward as ob
+    rng = np.random.default_rng(7)
+    hq, hkv, d, blk, L = 2, 1, 8, 4, 19
+    Q = rng.standard_normal((hq, L, d))
+    K0 = np.zeros((hkv, L, d))
+    r = o.run_sequence(Q, K0, K0, L, 0, blk, "group", k_fixed=100, attend=False)
+    lse = ob.row_logsumexp(Q, K0, L, 0, blk, r.units, gate=False)
+    np.testing.assert_allclose(lse, np.log(np.arange(1, L + 1))[None, :].repeat(hq, 0), rtol=0, atol=1e-12)
+    K = rng.standard_normal((hkv, L, d))
+    r = o.run_sequence(Q, K, K, L, 0, blk, "group", k_fixed=2, sink=True, gate=True, attend=False)
+    lse = ob.row_logsumexp(Q, K, L, 0, blk, r.units, gate=True, scale=0.5)
+    u0 = [u for u in r.units if u.c == 0][0]
+    for h in range(hq):
+        assert abs(lse[h, 0] - (0.5 * float(Q[h, 0] @ K[0, 0]) + u0.gate[0])) <= 1e-12
+    # a row past the first block sees more keys than one, so its value differs from its first logit
+    assert np.isfinite(lse).all()

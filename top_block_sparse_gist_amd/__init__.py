@@ -244,8 +244,9 @@ def select_decode_workspace_bytes(B, hq, hkv, d, block, dtype, max_len, seq_lens
 
 
 def sparse_prefill(Q, K, V, seq_lens, block, q_start, idx, nsel, gate=None, sel_mode="group", scale=0.0,
-                   O=None, stream=None):
-    """A4: O [B, Hq, T, d] = attention of each row over its unit's selected blocks (causal)."""
+                   O=None, stream=None, lse=None):
+    """A4: O [B, Hq, T, d] = attention of each row over its unit's selected blocks (causal).
+    lse: optional fp32 [B, Hq, T] tensor that receives each row's log-sum-exp (for the backward)."""
     torch = _torch()
     B, hq, tq, d = Q.shape
     _, hkv, lmax, _ = K.shape
@@ -253,10 +254,13 @@ def sparse_prefill(Q, K, V, seq_lens, block, q_start, idx, nsel, gate=None, sel_
         raise ValueError("K and V must share strides")
     if O is None:
         O = torch.empty_like(Q)
+    if lse is not None and (not lse.is_contiguous() or tuple(lse.shape) != (B, hq, tq)):
+        raise ValueError("lse must be a contiguous [B, Hq, T] tensor")
     p = _Prob(B, hq, hkv, d, block, _dtype_code(Q), lmax, seq_lens)
-    check(load().sas_sparse_prefill(p.ref, _ptr(Q), _strides(Q, 3), _ptr(K), _ptr(V), _strides(K, 3), tq,
-                                    _qstart(q_start), sel_code(sel_mode), _ptr(idx), _ptr(nsel), _ptr(gate),
-                                    idx.shape[1], float(scale), _ptr(O), _strides(O, 3), _stream(stream)),
+    check(load().sas_sparse_prefill_lse(p.ref, _ptr(Q), _strides(Q, 3), _ptr(K), _ptr(V), _strides(K, 3), tq,
+                                        _qstart(q_start), sel_code(sel_mode), _ptr(idx), _ptr(nsel), _ptr(gate),
+                                        idx.shape[1], float(scale), _ptr(O), _strides(O, 3), _ptr(lse),
+                                        _stream(stream)),
           "sas_sparse_prefill")
     return O
 
@@ -267,10 +271,11 @@ def prefill_backward_workspace_bytes(B, hq, hkv, d, block, max_len, seq_lens, tq
 
 
 def sparse_prefill_backward(Q, K, V, O, dO, seq_lens, block, q_start, idx, nsel, gate=None, sel_mode="group",
-                            scale=0.0, workspace=None, grads=None, stream=None):
+                            scale=0.0, workspace=None, grads=None, stream=None, lse=None):
     """Gradients of sparse_prefill for the loss sum(O * dO): (dQ, dK, dV, dgate, dscore), fp32
     (dgate and dscore are None without a gate).  grads: optional preallocated (dQ, dK, dV, dgate,
-    dscore); dK/dV rows past a sequence's length are left as given (zeros when allocated here)."""
+    dscore); dK/dV rows past a sequence's length are left as given (zeros when allocated here).
+    lse: the forward's row log-sum-exp (sparse_prefill(..., lse=)), or None to recompute it."""
     torch = _torch()
     B, hq, tq, d = Q.shape
     _, hkv, lmax, _ = K.shape
@@ -295,7 +300,7 @@ def sparse_prefill_backward(Q, K, V, O, dO, seq_lens, block, q_start, idx, nsel,
         workspace = torch.empty(max(1, need), dtype=torch.uint8, device=Q.device)
     check(lib.sas_sparse_prefill_backward(p.ref, _ptr(Q), _strides(Q, 3), _ptr(K), _ptr(V), _strides(K, 3), tq,
                                           _qstart(q_start), sel_code(sel_mode), _ptr(idx), _ptr(nsel), _ptr(gate),
-                                          kcap, float(scale), _ptr(O), _ptr(dO), _strides(O, 3), _ptr(dQ),
+                                          kcap, float(scale), _ptr(O), _ptr(dO), _strides(O, 3), _ptr(lse), _ptr(dQ),
                                           _strides(dQ, 3), _ptr(dK), _ptr(dV), _strides(dK, 3), _ptr(dgate),
                                           _ptr(dscore), _ptr(workspace), workspace.numel(), _stream(stream)),
           "sas_sparse_prefill_backward")

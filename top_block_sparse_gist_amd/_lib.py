@@ -26,7 +26,7 @@ EXPORTED = ("sas_num_qblocks", "sas_required_kcap", "sas_block_reps", "sas_block
             "sas_sparse_prefill", "sas_sparse_decode_workspace", "sas_sparse_decode", "sas_hssa_select_workspace",
             "sas_hssa_select_decode", "sas_hssa_decode_workspace", "sas_hssa_decode", "sas_block_reps_paged",
             "sas_sparse_decode_paged", "sas_sparse_prefill_paged", "sas_sparse_prefill_backward_workspace",
-            "sas_sparse_prefill_backward", "sas_last_error")
+            "sas_sparse_prefill_backward", "sas_sparse_prefill_lse", "sas_last_error")
 
 
 class Problem(C.Structure):
@@ -82,7 +82,9 @@ _SIGS = {
     "sas_sparse_prefill_backward_workspace": (C.c_size_t, [_P, C.c_int32, C.c_int32, C.c_int32, C.c_int32]),
     "sas_sparse_prefill_backward": (C.c_int, [_P, _VP, _I64_3, _VP, _VP, _I64_3, C.c_int32, C.POINTER(C.c_int32),
                                               C.c_int32, _VP, _VP, _VP, C.c_int32, C.c_float, _VP, _VP, _I64_3, _VP,
-                                              _I64_3, _VP, _VP, _I64_3, _VP, _VP, _VP, C.c_size_t, _VP]),
+                                              _VP, _I64_3, _VP, _VP, _I64_3, _VP, _VP, _VP, C.c_size_t, _VP]),
+    "sas_sparse_prefill_lse": (C.c_int, [_P, _VP, _I64_3, _VP, _VP, _I64_3, C.c_int32, C.POINTER(C.c_int32),
+                                         C.c_int32, _VP, _VP, _VP, C.c_int32, C.c_float, _VP, _I64_3, _VP, _VP]),
     "sas_last_error": (C.c_char_p, []),
 }
 

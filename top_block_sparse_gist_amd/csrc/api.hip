@@ -251,6 +251,15 @@ sas_status sas_sparse_prefill(const sas_problem *p, const void *Q, const int64_t
                               const void *V, const int64_t kv_stride[3], int32_t tq, const int32_t *q_start,
                               int32_t sel_mode, const int32_t *idx, const int32_t *nsel, const float *gate,
                               int32_t kcap, float scale, void *O, const int64_t o_stride[3], void *stream) {
+  return sas_sparse_prefill_lse(p, Q, q_stride, K, V, kv_stride, tq, q_start, sel_mode, idx, nsel, gate, kcap, scale,
+                                O, o_stride, nullptr, stream);
+}
+
+sas_status sas_sparse_prefill_lse(const sas_problem *p, const void *Q, const int64_t q_stride[3], const void *K,
+                                  const void *V, const int64_t kv_stride[3], int32_t tq, const int32_t *q_start,
+                                  int32_t sel_mode, const int32_t *idx, const int32_t *nsel, const float *gate,
+                                  int32_t kcap, float scale, void *O, const int64_t o_stride[3], float *lse,
+                                  void *stream) {
   SeqTable tab{};
   sas_status st;
   if ((st = check_problem(p, &tab)) != SAS_OK) return st;
@@ -270,9 +279,11 @@ sas_status sas_sparse_prefill(const sas_problem *p, const void *Q, const int64_t
     return fail(SAS_ERR_UNSUPPORTED, "one (sequence, KV head) K/V slab must span less than 4 GiB");
   const float sc = resolve_scale(scale, p->head_dim);
   const hipStream_t s = (hipStream_t)stream;
+  if (lse && (p->dtype != SAS_BF16 || !aligned16(lse)))
+    return fail(SAS_ERR_UNSUPPORTED, "the row log-sum-exp is written by the bf16 path (16-byte aligned)");
   if (p->dtype == SAS_BF16)
     return hip_status(launch_prefill_bf16(*p, tab, Q, q_stride, K, V, kv_stride, tq, sel_mode, idx, nsel, gate, kcap,
-                                          sc, O, o_stride, s),
+                                          sc, O, o_stride, s, nullptr, 0, lse),
                       "sas_sparse_prefill");
   return hip_status(launch_attend_f32(*p, tab, Q, q_stride, K, V, kv_stride, nullptr, nullptr, nullptr, tq, sel_mode,
                                       idx, nsel, gate, kcap, sc, O, o_stride, s),
@@ -600,7 +611,8 @@ sas_status sas_sparse_prefill_backward(const sas_problem *p, const void *Q, cons
                                        const void *V, const int64_t kv_stride[3], int32_t tq, const int32_t *q_start,
                                        int32_t sel_mode, const int32_t *idx, const int32_t *nsel, const float *gate,
                                        int32_t kcap, float scale, const void *O, const void *dO,
-                                       const int64_t o_stride[3], float *dQ, const int64_t dq_stride[3], float *dK,
+                                       const int64_t o_stride[3], const float *lse, float *dQ,
+                                       const int64_t dq_stride[3], float *dK,
                                        float *dV, const int64_t dkv_stride[3], float *dgate, float *dscore,
                                        void *workspace, size_t workspace_bytes, void *stream) {
   SeqTable tab{};
@@ -627,7 +639,7 @@ sas_status sas_sparse_prefill_backward(const sas_problem *p, const void *Q, cons
   if (workspace_bytes < pl.bytes)
     return fail(SAS_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, pl.bytes);
   const float sc = resolve_scale(scale, p->head_dim);
-  return hip_status(launch_prefill_backward(*p, tab, Q, q_stride, K, V, kv_stride, O, dO, o_stride, tq, sel_mode, idx,
+  return hip_status(launch_prefill_backward(*p, tab, Q, q_stride, K, V, kv_stride, O, dO, o_stride, lse, tq, sel_mode, idx,
                                             nsel, gate, kcap, sc, dQ, dq_stride, dK, dV, dkv_stride, dgate, dscore,
                                             workspace, (hipStream_t)stream),
                     "sas_sparse_prefill_backward");

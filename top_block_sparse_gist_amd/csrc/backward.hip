@@ -282,7 +282,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
     int batch, int hq, int rtiles, const int32_t *__restrict__ idx, const int32_t *__restrict__ nsel,
     const float *__restrict__ gate, int kcap, float scale_log2, float scale, float *__restrict__ dQ, int64_t dqb,
     int64_t dqh, int64_t dqt, float *__restrict__ lse_ws, float *__restrict__ dd_ws, float *__restrict__ gpart,
-    int gslots) {
+    int gslots, const float *__restrict__ lse_in) {
   constexpr int NKK = D / 16, NDT = D / 32, tpb = BLK / 64;
   __shared__ __attribute__((aligned(16))) uint16_t klds[2][64 * D];
   __shared__ __attribute__((aligned(16))) uint16_t vlds[2][64 * D];
@@ -367,13 +367,15 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
     }
   };
 
-  // ---- pass 1: running max and sum (log2 units) -> lse2 = log2 sum_k exp2(l_k log2 e)
+  // ---- pass 1: running max and sum (log2 units) -> lse2 = log2 sum_k exp2(l_k log2 e); skipped
+  //      when the forward's log-sum-exp is given
   float m_run = -INFINITY, l_run = 0.f;
-  if (ntiles > 0) load(0, 0, false);
+  const int ntiles1 = lse_in ? 0 : ntiles;
+  if (ntiles1 > 0) load(0, 0, false);
   wait_stores();
   __syncthreads();
-  for (int tt = 0; tt < ntiles; ++tt) {
-    if (tt + 1 < ntiles) load(tt + 1, (tt + 1) & 1, false);
+  for (int tt = 0; tt < ntiles1; ++tt) {
+    if (tt + 1 < ntiles1) load(tt + 1, (tt + 1) & 1, false);
     f32x16 sacc[2];
     scores(tt, sacc);
     const float gl2 = glist ? glist[tt / tpb] * LOG2E : 0.f;
@@ -400,7 +402,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
     __syncthreads();
   }
   l_run += __shfl_xor(l_run, 32, 64);
-  const float lse2 = qvalid && l_run > 0.f ? m_run + log2f(l_run) : INFINITY;
+  float lse2 = qvalid && l_run > 0.f ? m_run + log2f(l_run) : INFINITY;
+  if (lse_in) lse2 = qvalid ? lse_in[((int64_t)b * hq + h) * tq + t] * LOG2E : INFINITY;
 
   // ---- pass 2: P, dP^T, dS^T; dQ^T += K^T dS^T; dgate partials per block
   f32x16 acc[NDT];
@@ -793,7 +796,8 @@ BwdPlan bwd_plan(const sas_problem &p, int32_t tq, int32_t sel_mode, int32_t kca
 template <int D, int BLK>
 static hipError_t bwd_dispatch(const sas_problem &p, const SeqTable &st, const BwdPlan &pl, const void *Q,
                                const int64_t *qs, const void *K, const void *V, const int64_t *kvs, const void *O,
-                               const void *dO, const int64_t *os, int32_t tq, int32_t sel_mode, const int32_t *idx,
+                               const void *dO, const int64_t *os, const float *lse_in, int32_t tq, int32_t sel_mode,
+                               const int32_t *idx,
                                const int32_t *nsel, const float *gate, int32_t kcap, float scale, float *dQ,
                                const int64_t *dqs, float *dK, float *dV, const int64_t *dkvs, float *dgate,
                                float *dscore, char *ws, hipStream_t s) {
@@ -832,7 +836,7 @@ static hipError_t bwd_dispatch(const sas_problem &p, const SeqTable &st, const B
   hipLaunchKernelGGL((bwd_dq_kernel<D, NW_, BLK>), dim3((unsigned)nwg), dim3(NW_ * 64), 0, s, st, q16, qs[0], qs[1], \
                      qs[2], k16, v16, kvs[0], kvs[1], kvs[2], o16, do16, os[0], os[1], os[2], tq, S, pl.QB, G,       \
                      per_head, p.batch, p.hq, rtiles, idx, nsel, gate, kcap, scale_log2, scale, dQ, dqs[0], dqs[1],  \
-                     dqs[2], lse, dd, gpart, pl.gslots)
+                     dqs[2], lse, dd, gpart, pl.gslots, lse_in)
     if (small) SAS_BDQ(2);
     else SAS_BDQ(4);
 #undef SAS_BDQ
@@ -857,14 +861,14 @@ static hipError_t bwd_dispatch(const sas_problem &p, const SeqTable &st, const B
 
 hipError_t launch_prefill_backward(const sas_problem &p, const SeqTable &st, const void *Q, const int64_t *qs,
                                    const void *K, const void *V, const int64_t *kvs, const void *O, const void *dO,
-                                   const int64_t *os, int32_t tq, int32_t sel_mode, const int32_t *idx,
-                                   const int32_t *nsel, const float *gate, int32_t kcap, float scale, float *dQ,
-                                   const int64_t *dqs, float *dK, float *dV, const int64_t *dkvs, float *dgate,
-                                   float *dscore, void *workspace, hipStream_t s) {
+                                   const int64_t *os, const float *lse_in, int32_t tq, int32_t sel_mode,
+                                   const int32_t *idx, const int32_t *nsel, const float *gate, int32_t kcap,
+                                   float scale, float *dQ, const int64_t *dqs, float *dK, float *dV,
+                                   const int64_t *dkvs, float *dgate, float *dscore, void *workspace, hipStream_t s) {
   const BwdPlan pl = bwd_plan(p, tq, sel_mode, kcap, gate != nullptr);
   char *ws = (char *)workspace;
 #define SAS_BWD(D_, B_)                                                                                            \
-  return bwd_dispatch<D_, B_>(p, st, pl, Q, qs, K, V, kvs, O, dO, os, tq, sel_mode, idx, nsel, gate, kcap, scale, \
+  return bwd_dispatch<D_, B_>(p, st, pl, Q, qs, K, V, kvs, O, dO, os, lse_in, tq, sel_mode, idx, nsel, gate, kcap, scale, \
                               dQ, dqs, dK, dV, dkvs, dgate, dscore, ws, s)
   if (p.head_dim == 128) {
     if (p.block == 64) SAS_BWD(128, 64);

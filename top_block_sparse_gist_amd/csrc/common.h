@@ -222,7 +222,7 @@ hipError_t launch_prefill_bf16(const sas_problem &p, const SeqTable &st, const v
                                int32_t sel_mode, const int32_t *idx, const int32_t *nsel,
                                const float *gate, int32_t kcap, float scale, void *O, const int64_t *os,
                                hipStream_t s,
-                               const int32_t *table = nullptr, int64_t tld = 0);
+                               const int32_t *table = nullptr, int64_t tld = 0, float *lse = nullptr);
 
 // table: DEVICE [B, tld] page of each block (paged K/V; kv strides are then {page, head, token}), or nullptr
 hipError_t launch_decode_bf16(const sas_problem &p, const SeqTable &st, const void *Q, const int64_t *qs,
@@ -286,9 +286,9 @@ struct BwdPlan {
 BwdPlan bwd_plan(const sas_problem &p, int32_t tq, int32_t sel_mode, int32_t kcap, bool gate);
 hipError_t launch_prefill_backward(const sas_problem &p, const SeqTable &st, const void *Q, const int64_t *qs,
                                    const void *K, const void *V, const int64_t *kvs, const void *O, const void *dO,
-                                   const int64_t *os, int32_t tq, int32_t sel_mode, const int32_t *idx,
-                                   const int32_t *nsel, const float *gate, int32_t kcap, float scale, float *dQ,
-                                   const int64_t *dqs, float *dK, float *dV, const int64_t *dkvs, float *dgate,
-                                   float *dscore, void *workspace, hipStream_t s);
+                                   const int64_t *os, const float *lse, int32_t tq, int32_t sel_mode,
+                                   const int32_t *idx, const int32_t *nsel, const float *gate, int32_t kcap,
+                                   float scale, float *dQ, const int64_t *dqs, float *dK, float *dV,
+                                   const int64_t *dkvs, float *dgate, float *dscore, void *workspace, hipStream_t s);
 
 }  // namespace sas

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
     int tq, int blk, int S, int QB, int G, int per_head, int batch, int rtiles, int pchunks,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ nsel, const float *__restrict__ gate,
     int kcap, float scale_log2, uint16_t *__restrict__ O, int64_t ob, int64_t oh, int64_t ot,
-    const int32_t *__restrict__ table, int64_t tld) {
+    const int32_t *__restrict__ table, int64_t tld, float *__restrict__ lse, int hq) {
   constexpr int NKK = D / 16;        // k-steps of S^T over the head dim
   constexpr int NDT = D / 32;        // 32-dim output tiles
   static_assert(D == 64 || D == 128, "head dim 64 or 128");
@@ -376,6 +376,9 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
   // ---- normalise and write O (lane holds dims 32dt + 8(r/4) + 4half + r%4 of its query)
   l_run += __shfl_xor(l_run, 32, 64);
   if (!qvalid) return;
+  // row log-sum-exp of the logits (natural log): p = exp2(logit log2 e - m_run) summed to l_run
+  if (lse && half == 0)
+    lse[((int64_t)b * hq + qh_idx) * tq + qt_idx] = (m_run + log2f(l_run)) * 0.6931471805599453f;
   const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
   uint16_t *op = O + b * ob + (int64_t)qh_idx * oh + (int64_t)qt_idx * ot;
 #pragma unroll
@@ -395,7 +398,7 @@ static hipError_t prefill_dispatch(const sas_problem &p, const SeqTable &st, con
                                    const void *K, const void *V, const int64_t *kvs, int32_t tq,
                                    int32_t sel_mode, const int32_t *idx, const int32_t *nsel,
                                    const float *gate, int32_t kcap, float scale, void *O, const int64_t *os,
-                                   hipStream_t s, const int32_t *table, int64_t tld) {
+                                   hipStream_t s, const int32_t *table, int64_t tld, float *lse) {
   const int per_head = sel_mode == SAS_SEL_HEAD;
   const int S = per_head ? p.hq : p.hkv;
   const int G = p.hq / p.hkv;
@@ -417,7 +420,7 @@ static hipError_t prefill_dispatch(const sas_problem &p, const SeqTable &st, con
   hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, BLK>), dim3((unsigned)nwg), dim3(NW * 64), 0, s, st, ord,
                      (const uint16_t *)Q, qs[0], qs[1], qs[2], (const uint16_t *)K, (const uint16_t *)V, kvs[0],
                      kvs[1], kvs[2], tq, p.block, S, QB, G, per_head, p.batch, rtiles, pchunks, idx, nsel, gate, kcap,
-                     scale_log2, (uint16_t *)O, os[0], os[1], os[2], table, tld);
+                     scale_log2, (uint16_t *)O, os[0], os[1], os[2], table, tld, lse, p.hq);
   return hipGetLastError();
 }
 
@@ -425,13 +428,13 @@ hipError_t launch_prefill_bf16(const sas_problem &p, const SeqTable &st, const v
                                const void *K, const void *V, const int64_t *kvs, int32_t tq,
                                int32_t sel_mode, const int32_t *idx, const int32_t *nsel,
                                const float *gate, int32_t kcap, float scale, void *O, const int64_t *os,
-                               hipStream_t s, const int32_t *table, int64_t tld) {
+                               hipStream_t s, const int32_t *table, int64_t tld, float *lse) {
   // rows per unit: blk (x G when the group shares one list); 2 waves cover a 64-row unit
   const int nh = sel_mode == SAS_SEL_HEAD ? 1 : p.hq / p.hkv;
   const bool small = std::min(tq, p.block) * nh <= 64;
 #define SAS_PF(D_, NW_, B_) \
   return prefill_dispatch<D_, NW_, B_>(p, st, Q, qs, K, V, kvs, tq, sel_mode, idx, nsel, gate, kcap, scale, O, os, s, \
-                                       table, tld)
+                                       table, tld, lse)
 #define SAS_PF_NW(D_, B_) \
   if (small) SAS_PF(D_, 2, B_);  \
   SAS_PF(D_, 4, B_)
