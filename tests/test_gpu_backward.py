@@ -180,3 +180,75 @@ def test_backward_two_sequences_ragged():
     w = Workload(3, overrides=dict(tag="bwd_two", seq_lens=[1300, 700], batch=2, tq=256, block=64, hq=4, hkv=2,
                                    frac_num=1, frac_den=4, sink=False, gate=True))
     run_backward_case(w, seqs=[0, 1], use_lse=True)
+
+
+def test_backward_full_32k_prefill_properties():
+    """The 32K prefill at full size, in the launch configuration bench.py times (its own lists, the
+    forward's log-sum-exp).  Identities that hold at any size, since each row's P sums to 1 over its
+    keys and so its dS sums to 0:
+      sum over keys of dV[b, g] = sum of dO over the rows of the heads of group g;
+      sum over keys of dK[b, g] = 0;  sum over a unit's list of dgate = 0 up to the bf16 rounding of O
+      (and dscore = dgate then);
+    and a second call gives the same bits for dQ, dgate and dscore, and for dK/dV outside the blocks
+    whose unit lists were cut into several work items."""
+    w = Workload(3)
+    say(f"[bwd-full] {w.name}")
+    inp = upload(w, [0])
+    lens, blk, tq = inp.seq_lens, w.block, w.tq
+    Lmax = inp.K.shape[2]
+    budget = sas.Budget(k_fixed=w.k_fixed, frac_num=w.frac_num, frac_den=w.frac_den,
+                        count_current=w.count_current, sink=w.sink, gate=w.gate)
+    reps = sas.block_reps(inp.K, lens, blk)
+    scores = sas.block_scores(inp.Q, reps, lens, blk, w.hkv, Lmax, q_start=inp.q_start, sel_mode=w.sel)
+    idx, nsel, gate = sas.topk_select(scores, lens, blk, w.hq, w.hkv, w.d, sas.SAS_BF16, Lmax, budget, tq=tq,
+                                      q_start=inp.q_start, sel_mode=w.sel)
+    lse = torch.empty(inp.Q.shape[:3], dtype=torch.float32, device=inp.Q.device)
+    O = sas.sparse_prefill(inp.Q, inp.K, inp.V, lens, blk, inp.q_start, idx, nsel, gate, sel_mode=w.sel, lse=lse)
+    g = torch.Generator(device="cpu").manual_seed(w.seed)
+    dO = torch.randn(inp.Q.shape, generator=g, dtype=torch.float32).to(torch.bfloat16).to(inp.Q.device)
+    r1 = sas.sparse_prefill_backward(inp.Q, inp.K, inp.V, O, dO, lens, blk, inp.q_start, idx, nsel, gate,
+                                     sel_mode=w.sel, lse=lse)
+    r2 = sas.sparse_prefill_backward(inp.Q, inp.K, inp.V, O, dO, lens, blk, inp.q_start, idx, nsel, gate,
+                                     sel_mode=w.sel, lse=lse)
+    torch.cuda.synchronize()
+    say("[bwd-full] gpu done")
+    dQ, dK, dV, dgate, dscore = r1
+    for x in (dQ, dK, dV, dgate, dscore):
+        assert torch.isfinite(x).all()
+    G = w.hq // w.hkv
+    L = lens[0]
+    dOf = dO.float()[0]
+    for gi in range(w.hkv):
+        want = dOf[gi * G:(gi + 1) * G].sum(dim=(0, 1))
+        got = dV[0, gi, :L].sum(dim=0)
+        err = float((got - want).abs().max())
+        scale_v = float(dV[0, gi, :L].abs().sum(dim=0).max())
+        say(f"[bwd-full] group {gi}: |sum dV - sum dO| {err:.3e} (sum |dV| {scale_v:.3e})")
+        assert err <= 1e-3 * scale_v
+        ksum = float(dK[0, gi, :L].sum(dim=0).abs().max())
+        scale_k = float(dK[0, gi, :L].abs().sum(dim=0).max())
+        say(f"[bwd-full] group {gi}: |sum dK| {ksum:.3e} (sum |dK| {scale_k:.3e})")
+        assert ksum <= 1e-3 * scale_k
+    # Each row's dS sums to dO . (O - O_bf16) rather than 0, since D_row takes the forward's bf16 O:
+    # at most 2^-8 sum_d |dO_d O_d| per row (round-to-nearest: |O - O_bf16| <= 2^-9 |O|, doubled for
+    # margin).  So |sum of a unit's dgate| <= the sum of that over the unit's rows and heads, plus fp32
+    # noise.
+    QB = sas.num_qblocks(tq, blk)
+    e_row = (dO.float()[0].abs() * O.float()[0].abs()).sum(-1) * 2.0 ** -8          # [hq, tq]
+    nb = tq // blk
+    bound = e_row.view(w.hkv, G, nb, blk).sum(dim=(1, 3))                            # [hkv, nb]
+    gs = dgate.sum(dim=1).abs().view(w.hkv, QB)[:, :nb]
+    noise = 1e-4 * float(dgate.abs().sum(dim=1).max())
+    excess = float((gs - bound - noise).max())
+    say(f"[bwd-full] |sum dgate| per unit: max {float(gs.max()):.3e}, its rounding bound up to "
+        f"{float(bound.max()):.3e}; worst excess {excess:.3e}")
+    assert excess <= 0
+    # dscore - dgate = -exp(g) sum(dgate) with exp(g) <= 1
+    diff = (dscore - dgate).abs().max(dim=1).values
+    assert bool((diff <= dgate.sum(dim=1).abs() * 1.0001 + 1e-5 * float(dgate.abs().max())).all())
+    assert torch.equal(r2[0], dQ) and torch.equal(r2[3], dgate) and torch.equal(r2[4], dscore)
+    # dK/dV: bitwise equal outside blocks kept by more units than one work item holds
+    same = (r2[1][0] == dK[0]).all(dim=-1) & (r2[2][0] == dV[0]).all(dim=-1)   # [hkv, Lmax]
+    frac = float(same[:, :L].float().mean())
+    say(f"[bwd-full] dK/dV rows bitwise equal across two calls: {frac:.4f}")
+    assert frac >= 0.9
