@@ -104,3 +104,50 @@ def test_prefill_step_graph_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(O, ref), f"replay {r}: outputs differ"
+
+
+def test_training_step_graph_replays_match_eager():
+    """Forward with the row log-sum-exp, then the backward (its workspace is cleared by a fill
+    kernel inside the call, not a memset node), replayed from a graph with the workspace and the
+    gradients scribbled over between replays."""
+    w = Workload(3, overrides=dict(tag="graph_bwd", seq_len=2048, tq=2048, block=128, hq=8, hkv=2,
+                                   frac_num=1, frac_den=4, sink=True, gate=True))
+    inp = upload(w, [0])
+    lens = inp.seq_lens
+    L = lens[0]
+    bud = sas.Budget(frac_num=1, frac_den=4, sink=True, gate=True)
+    reps = sas.block_reps(inp.K, lens, w.block)
+    scores = sas.block_scores(inp.Q, reps, lens, w.block, w.hkv, L, q_start=[0])
+    idx, nsel, gate = sas.topk_select(scores, lens, w.block, w.hq, w.hkv, w.d, sas.SAS_BF16, L, bud, tq=w.tq,
+                                      q_start=[0])
+    O = torch.empty_like(inp.Q)
+    lse = torch.empty(inp.Q.shape[:3], dtype=torch.float32, device="cuda")
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    dO = torch.randn(inp.Q.shape, generator=gen).to(torch.bfloat16).cuda()
+    f32 = dict(dtype=torch.float32, device="cuda")
+    grads = (torch.empty(inp.Q.shape, **f32), torch.zeros(inp.K.shape, **f32), torch.zeros(inp.K.shape, **f32),
+             torch.empty(idx.shape, **f32), torch.empty(idx.shape, **f32))
+    need = sas.prefill_backward_workspace_bytes(1, w.hq, w.hkv, w.d, w.block, L, lens, w.tq, w.sel, idx.shape[1],
+                                                True)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+
+    def step():
+        sas.sparse_prefill(inp.Q, inp.K, inp.V, lens, w.block, [0], idx, nsel, gate, O=O, lse=lse)
+        sas.sparse_prefill_backward(inp.Q, inp.K, inp.V, O, dO, lens, w.block, [0], idx, nsel, gate,
+                                    workspace=ws, grads=grads, lse=lse)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in grads]
+    g = _capture(step)
+    for r in range(3):
+        for x in grads:
+            x.fill_(float("nan"))
+        grads[1].zero_()
+        grads[2].zero_()
+        ws.fill_(0xAB)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, x, y in zip(("dQ", "dK", "dV", "dgate", "dscore"), grads, ref):
+            assert torch.equal(x, y), f"replay {r}: {name} differs"
