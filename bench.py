@@ -513,7 +513,8 @@ def main():
         sas.sparse_prefill(inp.Q, inp.K, inp.V, inp.seq_lens, w.block, inp.q_start, bufs["idx"], bufs["nsel"],
                            bufs["gate"], sel_mode=w.sel, O=bufs["O"], lse=lse)
         dO = torch.zeros_like(inp.Q)
-        dO[0] = torch.from_numpy(np.ascontiguousarray(w.grad_out(0))).to(torch.bfloat16).to(dO.device)
+        for bi, b in enumerate(inp.seqs):
+            dO[bi] = torch.from_numpy(np.ascontiguousarray(w.grad_out(b))).to(torch.bfloat16).to(dO.device)
         f32 = dict(dtype=torch.float32, device=inp.Q.device)
         B, hq, tq, d = inp.Q.shape
         _, hkv, lmax, _ = inp.K.shape
@@ -591,9 +592,11 @@ def main():
         w5 = Workload(5)
         log("[bench] generating the mixed variable-length workload")
         inp5p = upload(w5, w5.prefill_seqs())
-        prefill_measure("mixed_prefill_half", w5, inp5p,
-                        f"8 seqs, last 4096 rows, lens {inp5p.seq_lens}, 32/8 heads, per-head, 5% + current, gate")
-        del inp5p
+        desc5 = f"8 seqs, last 4096 rows, lens {inp5p.seq_lens}, 32/8 heads, per-head, 5% + current, gate"
+        pf = prefill_measure("mixed_prefill_half", w5, inp5p, desc5)
+        if "backward" in only:
+            backward_measure("mixed_prefill_backward", w5, inp5p, "backward of " + desc5, *pf)
+        del inp5p, pf
         torch.cuda.empty_cache()
         inp5d = upload(w5, w5.decode_seqs())
         decode_measure("mixed_decode_half", w5, inp5d,

@@ -284,8 +284,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
     int64_t dqh, int64_t dqt, float *__restrict__ lse_ws, float *__restrict__ dd_ws, float *__restrict__ gpart,
     int gslots, const float *__restrict__ lse_in) {
   constexpr int NKK = D / 16, NDT = D / 32, tpb = BLK / 64;
-  __shared__ __attribute__((aligned(16))) uint16_t klds[2][64 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t vlds[2][64 * D];
+  // 64-row workgroups keep one K and one V buffer (32 KiB at d 128), so that four fit per CU and
+  // their copies overlap across workgroups; 128-row workgroups double-buffer (tile t+1 in flight
+  // while tile t is computed)
+  constexpr int NBUF = NW == 2 ? 1 : 2;
+  __shared__ __attribute__((aligned(16))) uint16_t klds[NBUF][64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vlds[NBUF][64 * D];
 
   // workgroup -> (query block heavy-first, sequence, selector head, row tile); the row tiles of a
   // unit run on one XCD and share its K/V tiles in that L2
@@ -352,7 +356,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
   };
   // S^T of tile tt (two 32-key halves), keys past the row's position at -inf on the current block
   auto scores = [&](int tt, f32x16 *sacc) {
-    const uint16_t *kl = klds[tt & 1];
+    const uint16_t *kl = klds[NBUF == 2 ? (tt & 1) : 0];
     sacc[0] = rows_dot<D>(kl, 0, qreg, col, half);
     sacc[1] = rows_dot<D>(kl, 32, qreg, col, half);
     if (tt >= nplain) {
@@ -375,7 +379,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
   wait_stores();
   __syncthreads();
   for (int tt = 0; tt < ntiles1; ++tt) {
-    if (tt + 1 < ntiles1) load(tt + 1, (tt + 1) & 1, false);
+    if (NBUF == 2 && tt + 1 < ntiles1) load(tt + 1, (tt + 1) & 1, false);
     f32x16 sacc[2];
     scores(tt, sacc);
     const float gl2 = glist ? glist[tt / tpb] * LOG2E : 0.f;
@@ -398,6 +402,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
       l_run += ls;
       m_run = m_new;
     }
+    if constexpr (NBUF == 1) {
+      __syncthreads();  // every wave has read tile tt
+      if (tt + 1 < ntiles1) load(tt + 1, 0, false);
+    }
     wait_stores();
     __syncthreads();
   }
@@ -418,12 +426,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
   wait_stores();
   __syncthreads();
   for (int tt = 0; tt < ntiles; ++tt) {
-    if (tt + 1 < ntiles) load(tt + 1, (tt + 1) & 1, true);
+    if (NBUF == 2 && tt + 1 < ntiles) load(tt + 1, (tt + 1) & 1, true);
     f32x16 sacc[2];
     scores(tt, sacc);
     const float gl2 = glist ? glist[tt / tpb] * LOG2E : 0.f;
     const float bias = gl2 - lse2;
-    const uint16_t *vl = vlds[tt & 1];
+    const uint16_t *vl = vlds[NBUF == 2 ? (tt & 1) : 0];
     f32x16 dp[2];
     dp[0] = rows_dot<D>(vl, 0, doreg, col, half);
     dp[1] = rows_dot<D>(vl, 32, doreg, col, half);
@@ -436,7 +444,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
         sacc[mt][r] = ds;
         gsum += ds;
       }
-    const uint16_t *kl = klds[tt & 1];
+    const uint16_t *kl = klds[NBUF == 2 ? (tt & 1) : 0];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const bf16x8 dsop = pack_operand(sacc[ks >> 1], 8 * (ks & 1));
@@ -448,6 +456,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
       const float gs = wave_sum(gsum);
       if (lane == 0 && wave_rows) gpart[((int64_t)u * gslots + slot) * kcap + tt / tpb] = gs;
       gsum = 0.f;
+    }
+    if constexpr (NBUF == 1) {
+      __syncthreads();  // every wave has read tile tt
+      if (tt + 1 < ntiles) load(tt + 1, 0, true);
     }
     wait_stores();
     __syncthreads();
