@@ -336,9 +336,9 @@ const char *sas_last_error(void);
  *   != NULL) bytes of device scratch (no initial contents needed; it grows with the batch, the rows,
  *   the block count and, with a gate, the block count times the units per KV head).
  *   Arithmetic: P and dS are rounded to bf16 as matrix operands, with fp32 accumulation; dQ, dgate
- *   and dscore are deterministic; dK and dV are too, except in key tiles that more than 64 units
- *   (per head) or more than 2048 / (rows x heads) units select, whose partial sums meet in fp32
- *   atomic adds.
+ *   and dscore are deterministic; dK and dV are too, except in blocks whose selecting units hold
+ *   more than 32768 (row, head) pairs in all, or number more than 256: their unit list is cut into
+ *   several work items whose partial sums meet in fp32 atomic adds.
  *   Errors: as sas_sparse_prefill; SAS_ERR_UNSUPPORTED for fp32; SAS_ERR_WORKSPACE when too small. */
 size_t sas_sparse_prefill_backward_workspace(const sas_problem *p, int32_t tq, int32_t sel_mode, int32_t kcap,
                                              int32_t gate);

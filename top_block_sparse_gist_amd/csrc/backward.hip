@@ -16,7 +16,8 @@
 //   bwd_plan   one workgroup per (sequence, KV head): cut each block's unit list into segments of
 //              bounded work; zero the dK/dV rows of blocks cut into more than one segment
 //   bwd_dq     a unit's row tile, as in the forward (S^T = K Q^T with Q^T in registers): pass 1 walks
-//              the list for each row's log-sum-exp, pass 2 recomputes P, dP^T = V dO^T and dS, and
+//              the list for each row's log-sum-exp (skipped when the forward's is given), pass 2
+//              recomputes P, dP^T = V dO^T and dS, and
 //              accumulates dQ^T += K^T dS^T (transposing LDS reads of the K tile); writes LSE, D_row
 //              and per-32-row partial sums of dgate
 //   bwd_dkv    a (block, segment): K^T in registers and V in LDS while the units that selected the
