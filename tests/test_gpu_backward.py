@@ -69,7 +69,8 @@ def run_backward_case(w: Workload, seqs=(0,), use_lse=False):
         h = inp.host[b]
         res[b] = orc.run_sequence(h["q"], h["k"], h["v"], w.seq_lens[b], w.q_start[b], blk, w.sel,
                                   k_fixed=w.k_fixed, frac_num=w.frac_num, frac_den=w.frac_den,
-                                  count_current=w.count_current, sink=w.sink, gate=w.gate, scale=scale)
+                                  count_current=w.count_current, sink=w.sink, gate=w.gate, scale=scale,
+                                  coverage=w.spec.get("coverage", 0.0), shared=w.spec.get("shared", False))
     kcap = max(len(u.sel) for r in res.values() for u in r.units if u.sel is not None)
     units = B * S * QB
     idx = np.full((units, kcap), -1, np.int32)
@@ -165,6 +166,21 @@ def test_backward_block_list_split_into_segments():
     meet in atomic adds."""
     w = Workload(3, overrides=dict(tag="bwd_split", seq_len=2304, tq=2304, block=128, hq=16, hkv=1,
                                    frac_num=0, frac_den=0, k_fixed=2, sink=True, gate=True))
+    run_backward_case(w)
+
+
+def test_backward_shared_budget_lists_of_varying_length():
+    """Per-head lists under a budget shared by the 4 heads of a KV group (lengths differ per head)."""
+    w = Workload(3, overrides=dict(tag="bwd_shared", seq_len=1200, tq=700, block=64, hq=8, hkv=2, sel="head",
+                                   frac_num=0, frac_den=0, k_fixed=3, sink=True, gate=True, shared=True))
+    run_backward_case(w)
+
+
+def test_backward_coverage_budget_d64():
+    """Per-group lists from a coverage budget (the smallest top set holding 80 % of the selector's
+    softmax mass), d = 64."""
+    w = Workload(3, overrides=dict(tag="bwd_cov", seq_len=1100, tq=500, block=64, d=64, hq=4, hkv=1,
+                                   frac_num=0, frac_den=0, k_fixed=0, sink=False, gate=True, coverage=0.8))
     run_backward_case(w)
 
 
