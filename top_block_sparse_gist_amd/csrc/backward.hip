@@ -528,6 +528,18 @@ __global__ __launch_bounds__(BLK * 2, 2) void bwd_dkv_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
   const int mykey = key0 + wave * 32 + col;
+  if (it.count == 0) {
+    // no unit selected this block: its gradients are zero (a block of one item only)
+    if (mykey < L) {
+      const int64_t o = b * gb + (int64_t)g * gh + (int64_t)mykey * gt;
+#pragma unroll
+      for (int d4 = 0; d4 < D / 4; d4 += 2) {
+        *reinterpret_cast<f32x4 *>(dK + o + 4 * (d4 + half)) = f32x4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<f32x4 *>(dV + o + 4 * (d4 + half)) = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    return;
+  }
 
   // ---- V tile into LDS, K^T of this wave's keys into registers (rows past L re-read row L-1;
   //      their keys are masked below)
