@@ -103,24 +103,6 @@ __device__ __forceinline__ f32x16 rows_dot(const uint16_t *lds, int row0, const 
   return a;
 }
 
-// The same with the B operand read from LDS too (rows b0 .. b0+31 of a swizzled tile).
-template <int D>
-__device__ __forceinline__ f32x16 rows_dot_lds(const uint16_t *la, const uint16_t *lb, int b0, int col, int half) {
-  constexpr int NKK = D / 16;
-  f32x16 a;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) a[r] = 0.f;
-  const uint16_t *pa = la + col * D, *pb = lb + (b0 + col) * D;
-  const int fa = swz<D>(col), fb = swz<D>(b0 + col);
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    const u32x4 va = *reinterpret_cast<const u32x4 *>(pa + 8 * ((2 * kk + half) ^ fa));
-    const u32x4 vb = *reinterpret_cast<const u32x4 *>(pb + 8 * ((2 * kk + half) ^ fb));
-    a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(va), as_bf8(vb), a, 0, 0, 0);
-  }
-  return a;
-}
-
 // Transposed operand of a swizzled LDS tile for k-step ks: lane (col, half) gets column 32 dt + col
 // of rows 16 ks + 4 half + {0..3} and 16 ks + 8 + 4 half + {0..3}, the row order in which an
 // accumulator's registers 8 (ks & 1) .. + 7 hold their rows (keys).
@@ -138,7 +120,8 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t *lds, int ks, int dt
 
 // Per-lane element offsets of the reads above, computed once so that a loop keeps a few registers
 // of addresses (the k-step, the tensor and the buffer only add constants):
-//   row[kk]: chunk 2kk + half of row `col` (rows_dot with row0 = 0; the same for row0 = 32w)
+//   row[kk]: chunk 2kk + half of row `col` (rows_dot's read with row0 = 0; the same offsets serve
+//            row0 = 32w, since the swizzle of row 32w + col is that of row col)
 //   tlo[dt], thi[dt]: tr_operand's two reads at ks = 0 (ks adds 16 ks rows)
 template <int D>
 struct LdsOffsets {
