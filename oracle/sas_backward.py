@@ -20,9 +20,15 @@ import numpy as np
 
 
 def backward_sequence(Qb: np.ndarray, Kb: np.ndarray, Vb: np.ndarray, dOb: np.ndarray, L: int, q_start: int,
-                      blk: int, units, gate: bool, scale: Optional[float] = None) -> dict:
+                      blk: int, units, gate: bool, scale: Optional[float] = None,
+                      through_scores: bool = False) -> dict:
     """Qb, dOb: [hq, rows, d]; Kb, Vb: [hkv, >= L, d]; units: the oracle's selection units of this
-    sequence (their .sel lists and .scores), as run_sequence leaves them."""
+    sequence (their .sel lists and .scores), as run_sequence leaves them.
+
+    through_scores (with a gate, pooled representatives): the selector scores are not constants but
+    the function of Q and K that the forward scored with, s_j = scale * qbar . r_j (qbar the mean of
+    the unit's query vectors over its rows and heads, r_j the mean of block j's present keys), so dQ
+    and dK also carry the gradient that reaches the scores through the gate; the lists stay fixed."""
     import torch
     hq, rows, d = Qb.shape
     hkv = Kb.shape[0]
@@ -44,7 +50,14 @@ def backward_sequence(Qb: np.ndarray, Kb: np.ndarray, Vb: np.ndarray, dOb: np.nd
         sel = list(u.sel)
         key_u = (u.sel_head, u.c)
         if gate:
-            s = torch.tensor([float(u.scores[j]) for j in sel], dtype=f64, requires_grad=True)
+            if through_scores:
+                kvh = u.heads[0] // G
+                qbar = Q[list(u.heads), u.t_lo:u.t_hi].reshape(-1, d).mean(dim=0)
+                reps = torch.stack([K[kvh, j * blk:min((j + 1) * blk, L)].mean(dim=0) for j in sel])
+                s = scale * (reps @ qbar)
+                s.retain_grad()
+            else:
+                s = torch.tensor([float(u.scores[j]) for j in sel], dtype=f64, requires_grad=True)
             g = s - torch.logsumexp(s, dim=0)
             g.retain_grad()
             s_leaves[key_u], g_nodes[key_u] = s, g

@@ -571,6 +571,45 @@ def test_backward_matches_finite_differences_of_the_forward_oracle(sel_mode):
     np.testing.assert_allclose(grads["dscore"][key_u], dg - np.exp(g) * dg.sum(), rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("sel_mode", ["group", "head"])
+def test_backward_through_scores_matches_finite_differences(sel_mode):
+    """With the selector scores taken as the function of Q and K the forward scored with (pooled
+    query . block mean), the autograd dQ and dK against central differences of the numpy forward
+    oracle in which every unit's gate is recomputed from the perturbed Q and K (lists fixed); and
+    the gradient differs from the constant-score one (the selector path is not empty)."""
+    from oracle import sas_backward as ob
+    rng = np.random.default_rng(67)
+    hq, hkv, d, blk, L, tq = 4, 2, 8, 4, 4 * 9 + 3, 10
+    q0 = L - tq
+    scale = 1.0 / np.sqrt(d)
+    Q = rng.standard_normal((hq, tq, d)); K = rng.standard_normal((hkv, L, d)); V = rng.standard_normal((hkv, L, d))
+    dO = rng.standard_normal((hq, tq, d))
+    r = o.run_sequence(Q, K, V, L, q0, blk, sel_mode, k_fixed=2, sink=True, gate=True, attend=False)
+    grads = ob.backward_sequence(Q, K, V, dO, L, q0, blk, r.units, gate=True, through_scores=True)
+    plain = ob.backward_sequence(Q, K, V, dO, L, q0, blk, r.units, gate=True)
+    G = hq // hkv
+
+    def loss(Qx, Kx):
+        reps = np.stack([o.block_reps(Kx[g], L, blk) for g in range(hkv)])
+        ex = {}
+        for u in r.units:
+            g = u.heads[0] // G
+            sc = o.unit_scores(o.unit_query_vectors(Qx, u), reps[g], u.c + 1, scale)
+            ex[(u.sel_head, u.c)] = (list(u.sel), o.gate_values(sc, u.sel))
+        return _loss_numpy(Qx, Kx, V, dO, L, q0, blk, sel_mode, ex, True)
+    eps = 1e-6
+    for name, index in [("Q", (1, 3, 2)), ("Q", (3, 9, 7)), ("K", (0, 30, 1)), ("K", (1, 5, 4)), ("K", (0, 1, 3))]:
+        def at(e):
+            Qx, Kx = Q.copy(), K.copy()
+            (Qx if name == "Q" else Kx)[index] += e
+            return loss(Qx, Kx)
+        want = (at(eps) - at(-eps)) / (2 * eps)
+        got = grads["d" + name][index]
+        assert abs(got - want) <= 1e-6 * (1 + abs(got)), (name, index, got, want)
+    assert np.abs(grads["dK"] - plain["dK"]).max() > 1e-6
+    np.testing.assert_allclose(grads["dV"], plain["dV"], rtol=0, atol=1e-12)
+
+
 def test_backward_all_blocks_gate_off_is_sdpa_backward():
     """Every block selected and no gate: the gradients of dense causal attention, from torch's
     scaled_dot_product_attention in float64."""
