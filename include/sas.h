@@ -331,6 +331,13 @@ const char *sas_last_error(void);
  *   O: the forward output (bf16, o_stride); dO: its gradient (bf16, same strides).
  *   lse: the forward's row log-sum-exp from sas_sparse_prefill_lse ([B, Hq, tq] fp32), or NULL to
  *   recompute it (one more pass over each unit's list).
+ *   reps (with a gate; fp32 [B, Hkv, >= NB_b, d], rep_stride as in sas_block_reps): the block
+ *   representatives the selection scored, or NULL.  Given, the gradient continues through the
+ *   selector ([SAS] method: trained end to end through the gate): the scores are
+ *   s_j = scale * qbar . r_j of the unit's mean query vector qbar and the block means r_j, so each of
+ *   the unit's query vectors gets scale * sum_j dscore_j r_j / (its vector count) added to dQ, and
+ *   each present key of block j gets scale * sum over the units keeping j of dscore_j qbar, divided
+ *   by the block's key count, added to dK (those sums use fp32 atomic adds).  Lists stay fixed.
  *   Q, K, V, idx, nsel, gate, kcap, scale: as given to sas_sparse_prefill (bf16 only).
  *   kcap <= 32767.  workspace: sas_sparse_prefill_backward_workspace(p, tq, sel_mode, kcap, gate
  *   != NULL) bytes of device scratch (no initial contents needed; it grows with the batch, the rows,
@@ -339,7 +346,8 @@ const char *sas_last_error(void);
  *   and dscore are deterministic; dK and dV are too, except in blocks whose selecting units hold
  *   more than 32768 (row, head) pairs in all, or number more than 256: their unit list is cut into
  *   several work items whose partial sums meet in fp32 atomic adds.
- *   Errors: as sas_sparse_prefill; SAS_ERR_UNSUPPORTED for fp32; SAS_ERR_WORKSPACE when too small. */
+ *   Errors: as sas_sparse_prefill; SAS_ERR_UNSUPPORTED for fp32; SAS_ERR_WORKSPACE when too small;
+ *   SAS_ERR_SHAPE for reps without a gate. */
 size_t sas_sparse_prefill_backward_workspace(const sas_problem *p, int32_t tq, int32_t sel_mode, int32_t kcap,
                                              int32_t gate);
 sas_status sas_sparse_prefill_backward(const sas_problem *p, const void *Q, const int64_t q_stride[3],
@@ -350,7 +358,8 @@ sas_status sas_sparse_prefill_backward(const sas_problem *p, const void *Q, cons
                                        const float *lse, float *dQ,
                                        const int64_t dq_stride[3], float *dK, float *dV,
                                        const int64_t dkv_stride[3], float *dgate, float *dscore,
-                                       void *workspace, size_t workspace_bytes, void *stream);
+                                       const float *reps, const int64_t rep_stride[3], void *workspace,
+                                       size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

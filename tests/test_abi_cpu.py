@@ -310,16 +310,17 @@ def test_prefill_backward_validation_codes():
     # the gate adds the partial sums and the entry positions
     assert lib.sas_sparse_prefill_backward_workspace(C.byref(p), 128, _lib.SAS_SEL_GROUP, 8, 0) < need
 
-    def bw(gate=None, dgate=FAKE, ws=FAKE, wsb=None, q_start=qs, kcap=8, dQ=FAKE, prob=p):
+    def bw(gate=None, dgate=FAKE, ws=FAKE, wsb=None, q_start=qs, kcap=8, dQ=FAKE, prob=p, reps=None):
         return lib.sas_sparse_prefill_backward(C.byref(prob), FAKE, q3, FAKE, FAKE, kv, 128, q_start,
                                                _lib.SAS_SEL_GROUP, FAKE, FAKE, gate, kcap, 0.0, FAKE, FAKE, q3, None,
-                                               dQ, q3, FAKE, FAKE, kv, dgate, FAKE, ws,
+                                               dQ, q3, FAKE, FAKE, kv, dgate, FAKE, reps, kv, ws,
                                                need if wsb is None else wsb, None)
 
     assert bw(q_start=None) == _lib.SAS_ERR_NULL
     assert bw(dQ=None) == _lib.SAS_ERR_NULL
     assert bw(ws=None) == _lib.SAS_ERR_NULL
     assert bw(gate=FAKE, dgate=None) == _lib.SAS_ERR_NULL          # a gate needs dgate and dscore
+    assert bw(reps=FAKE) == _lib.SAS_ERR_SHAPE                      # the selector's gradient needs a gate
     assert bw(kcap=0) == _lib.SAS_ERR_SHAPE
     assert bw(kcap=40000) == _lib.SAS_ERR_SHAPE
     assert bw(gate=FAKE, wsb=need - 1) == _lib.SAS_ERR_WORKSPACE

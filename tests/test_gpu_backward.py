@@ -52,7 +52,7 @@ def _check(name, got, ref, stats):
     assert mean <= MEAN_REL * top + 1e-7, f"{name}: mean-abs {mean:.3e} vs max|ref| {top:.3e}"
 
 
-def run_backward_case(w: Workload, seqs=(0,), use_lse=False):
+def run_backward_case(w: Workload, seqs=(0,), use_lse=False, through_scores=False):
     """use_lse: the GPU forward writes each row's log-sum-exp (checked against the oracle's to 1e-3
     absolute: fp32 sums of exact bf16 products) and the backward takes it instead of recomputing it."""
     seqs = list(seqs)
@@ -106,8 +106,15 @@ def run_backward_case(w: Workload, seqs=(0,), use_lse=False):
             err = float(np.abs(lse_h[bi, :, :w.rows[b]] - ref).max())
             say(f"[bwd] lse[{b}] max-abs {err:.2e}")
             assert err <= 1e-3, f"row log-sum-exp differs by {err:.3e}"
+    reps = sas.block_reps(inp.K, lens, blk) if through_scores else None
     dQ, dK, dV, dgate, dscore = sas.sparse_prefill_backward(inp.Q, inp.K, inp.V, O, dO, lens, blk, inp.q_start,
-                                                            t_idx, t_nsel, t_gate, sel_mode=w.sel, lse=lse)
+                                                            t_idx, t_nsel, t_gate, sel_mode=w.sel, lse=lse, reps=reps)
+    plain = None
+    if through_scores:
+        # the same call without the representatives isolates the selector path's contribution
+        plain = sas.sparse_prefill_backward(inp.Q, inp.K, inp.V, O, dO, lens, blk, inp.q_start, t_idx, t_nsel,
+                                            t_gate, sel_mode=w.sel, lse=lse)
+        plain = (plain[0].cpu().numpy(), plain[1].cpu().numpy())
     torch.cuda.synchronize()
     say("[bwd] gpu done")
     dQ, dK, dV = dQ.cpu().numpy(), dK.cpu().numpy(), dV.cpu().numpy()
@@ -118,9 +125,14 @@ def run_backward_case(w: Workload, seqs=(0,), use_lse=False):
         h = inp.host[b]
         L, q0, rows = w.seq_lens[b], w.q_start[b], w.rows[b]
         ref = orcb.backward_sequence(h["q"], h["k"], h["v"], w.grad_out(b), L, q0, blk, res[b].units, w.gate,
-                                     scale)
+                                     scale, through_scores=through_scores)
         _check(f"dQ[{b}]", dQ[bi, :, :rows], ref["dQ"], stats)
         _check(f"dK[{b}]", dK[bi, :, :L], ref["dK"], stats)
+        if through_scores:
+            refp = orcb.backward_sequence(h["q"], h["k"], h["v"], w.grad_out(b), L, q0, blk, res[b].units, w.gate,
+                                          scale)
+            _check(f"selector path dQ[{b}]", dQ[bi, :, :rows] - plain[0][bi, :, :rows], ref["dQ"] - refp["dQ"], stats)
+            _check(f"selector path dK[{b}]", dK[bi, :, :L] - plain[1][bi, :, :L], ref["dK"] - refp["dK"], stats)
         _check(f"dV[{b}]", dV[bi, :, :L], ref["dV"], stats)
         if w.gate:
             g_got, g_ref, s_got, s_ref = [], [], [], []
@@ -167,6 +179,16 @@ def test_backward_block_list_split_into_segments():
     w = Workload(3, overrides=dict(tag="bwd_split", seq_len=2304, tq=2304, block=128, hq=16, hkv=1,
                                    frac_num=0, frac_den=0, k_fixed=2, sink=True, gate=True))
     run_backward_case(w)
+
+
+@pytest.mark.parametrize("sel", ["group", "head"])
+def test_backward_through_the_selector_scores(sel):
+    """The gradient carried on from dscore through the pooled query and the block means into dQ and
+    dK (the block representatives passed to the backward), against the oracle's through-scores mode."""
+    w = Workload(3, overrides=dict(tag="bwd_chain" + sel, seq_len=1000, tq=300, block=64 if sel == "group" else 128,
+                                   d=128 if sel == "group" else 64, hq=4, hkv=2, sel=sel, frac_num=1, frac_den=4,
+                                   sink=True, gate=True))
+    run_backward_case(w, through_scores=True)
 
 
 def test_backward_shared_budget_lists_of_varying_length():

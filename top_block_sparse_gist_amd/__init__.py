@@ -271,11 +271,13 @@ def prefill_backward_workspace_bytes(B, hq, hkv, d, block, max_len, seq_lens, tq
 
 
 def sparse_prefill_backward(Q, K, V, O, dO, seq_lens, block, q_start, idx, nsel, gate=None, sel_mode="group",
-                            scale=0.0, workspace=None, grads=None, stream=None, lse=None):
+                            scale=0.0, workspace=None, grads=None, stream=None, lse=None, reps=None):
     """Gradients of sparse_prefill for the loss sum(O * dO): (dQ, dK, dV, dgate, dscore), fp32
     (dgate and dscore are None without a gate).  grads: optional preallocated (dQ, dK, dV, dgate,
     dscore); dK/dV rows past a sequence's length are left as given (zeros when allocated here).
-    lse: the forward's row log-sum-exp (sparse_prefill(..., lse=)), or None to recompute it."""
+    lse: the forward's row log-sum-exp (sparse_prefill(..., lse=)), or None to recompute it.
+    reps: the block representatives the selection scored (with a gate): the gradient then continues
+    through the selector scores into dQ and dK."""
     torch = _torch()
     B, hq, tq, d = Q.shape
     _, hkv, lmax, _ = K.shape
@@ -302,7 +304,8 @@ def sparse_prefill_backward(Q, K, V, O, dO, seq_lens, block, q_start, idx, nsel,
                                           _qstart(q_start), sel_code(sel_mode), _ptr(idx), _ptr(nsel), _ptr(gate),
                                           kcap, float(scale), _ptr(O), _ptr(dO), _strides(O, 3), _ptr(lse), _ptr(dQ),
                                           _strides(dQ, 3), _ptr(dK), _ptr(dV), _strides(dK, 3), _ptr(dgate),
-                                          _ptr(dscore), _ptr(workspace), workspace.numel(), _stream(stream)),
+                                          _ptr(dscore), _ptr(reps), _strides(reps, 3) if reps is not None else None,
+                                          _ptr(workspace), workspace.numel(), _stream(stream)),
           "sas_sparse_prefill_backward")
     return dQ, dK, dV, dgate, dscore
 

@@ -82,7 +82,8 @@ _SIGS = {
     "sas_sparse_prefill_backward_workspace": (C.c_size_t, [_P, C.c_int32, C.c_int32, C.c_int32, C.c_int32]),
     "sas_sparse_prefill_backward": (C.c_int, [_P, _VP, _I64_3, _VP, _VP, _I64_3, C.c_int32, C.POINTER(C.c_int32),
                                               C.c_int32, _VP, _VP, _VP, C.c_int32, C.c_float, _VP, _VP, _I64_3, _VP,
-                                              _VP, _I64_3, _VP, _VP, _I64_3, _VP, _VP, _VP, C.c_size_t, _VP]),
+                                              _VP, _I64_3, _VP, _VP, _I64_3, _VP, _VP, _VP, _I64_3, _VP, C.c_size_t,
+                                              _VP]),
     "sas_sparse_prefill_lse": (C.c_int, [_P, _VP, _I64_3, _VP, _VP, _I64_3, C.c_int32, C.POINTER(C.c_int32),
                                          C.c_int32, _VP, _VP, _VP, C.c_int32, C.c_float, _VP, _I64_3, _VP, _VP]),
     "sas_last_error": (C.c_char_p, []),

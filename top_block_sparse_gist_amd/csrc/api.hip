@@ -614,7 +614,8 @@ sas_status sas_sparse_prefill_backward(const sas_problem *p, const void *Q, cons
                                        const int64_t o_stride[3], const float *lse, float *dQ,
                                        const int64_t dq_stride[3], float *dK,
                                        float *dV, const int64_t dkv_stride[3], float *dgate, float *dscore,
-                                       void *workspace, size_t workspace_bytes, void *stream) {
+                                       const float *reps, const int64_t rep_stride[3], void *workspace,
+                                       size_t workspace_bytes, void *stream) {
   SeqTable tab{};
   sas_status st;
   if ((st = check_problem(p, &tab)) != SAS_OK) return st;
@@ -625,6 +626,9 @@ sas_status sas_sparse_prefill_backward(const sas_problem *p, const void *Q, cons
       !dK || !dV || !dkv_stride || !workspace)
     return fail(SAS_ERR_NULL, "a required pointer is NULL");
   if (gate && (!dgate || !dscore)) return fail(SAS_ERR_NULL, "dgate and dscore are required with a gate");
+  if (reps && !gate) return fail(SAS_ERR_SHAPE, "reps carry the selector's gradient, which needs a gate");
+  if (reps && (!rep_stride || !aligned16(reps) || !strides_ok(rep_stride, 3, 4)))
+    return fail(SAS_ERR_SHAPE, "reps must be 16-byte aligned fp32 with 16-byte-multiple strides");
   if (p->dtype != SAS_BF16) return fail(SAS_ERR_UNSUPPORTED, "the backward takes bf16 Q/K/V/O/dO");
   if (kcap < 1 || kcap > 32767) return fail(SAS_ERR_SHAPE, "kcap must be in [1, 32767]");
   if (scale < 0.f || !isfinite(scale)) return fail(SAS_ERR_SHAPE, "scale must be finite and >= 0");
@@ -641,7 +645,7 @@ sas_status sas_sparse_prefill_backward(const sas_problem *p, const void *Q, cons
   const float sc = resolve_scale(scale, p->head_dim);
   return hip_status(launch_prefill_backward(*p, tab, Q, q_stride, K, V, kv_stride, O, dO, o_stride, lse, tq, sel_mode, idx,
                                             nsel, gate, kcap, sc, dQ, dq_stride, dK, dV, dkv_stride, dgate, dscore,
-                                            workspace, (hipStream_t)stream),
+                                            reps, rep_stride, workspace, (hipStream_t)stream),
                     "sas_sparse_prefill_backward");
 }
 

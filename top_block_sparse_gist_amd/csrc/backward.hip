@@ -760,6 +760,81 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(SeqTable st, int64_t unit
 }
 
 // ---------------------------------------------------------------------------------------------
+// through the selector: dscore -> dQ (pooled query) and the block means (dK)
+// ---------------------------------------------------------------------------------------------
+// One workgroup per unit.  s_j = scale qbar . r_j with qbar the mean of the unit's F query vectors
+// and r_j the mean of block j's present keys: dqbar = scale sum_j dscore_j r_j goes to each query
+// vector as dqbar / F; dr_j += scale dscore_j qbar (atomic adds: the units that selected j meet).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_chain_kernel(SeqTable st, const uint16_t *__restrict__ Q, int64_t qb,
+                                                       int64_t qh, int64_t qt, int tq, int S, int QB, int G,
+                                                       int per_head, int hkv, const int32_t *__restrict__ idx,
+                                                       const int32_t *__restrict__ nsel, int kcap,
+                                                       const float *__restrict__ dscore, const float *__restrict__ reps,
+                                                       int64_t rb, int64_t rh, int64_t rj, float scale,
+                                                       float *__restrict__ dQ, int64_t dqb, int64_t dqh, int64_t dqt,
+                                                       float *__restrict__ dreps, int NBm, int blk) {
+  constexpr int RG = 256 / D;  // row groups: thread (rg, dim)
+  __shared__ float part[RG][D];
+  __shared__ float qbar[D], dqbar[D];
+  const int64_t u = blockIdx.x;
+  const UnitGeo ug = unit_geo(st, u, S, QB, G, per_head, tq, blk);
+  const int ns = ug.rows > 0 ? nsel[u] : 0;
+  if (ns == 0) return;
+  const int F = ug.rows * ug.nh;
+  const int tid = threadIdx.x, dim = tid % D, rg = tid / D;
+  const uint16_t *qbase = Q + ug.b * qb;
+  float a = 0.f;
+  for (int f = rg; f < F; f += RG)
+    a += bf16_to_f32(qbase[(int64_t)(ug.h0 + f / ug.rows) * qh + (int64_t)(ug.t_lo + f % ug.rows) * qt + dim]);
+  part[rg][dim] = a;
+  __syncthreads();
+  if (rg == 0) {
+    float t = 0.f;
+#pragma unroll
+    for (int y = 0; y < RG; ++y) t += part[y][dim];
+    qbar[dim] = t / (float)F;
+  }
+  __syncthreads();
+  const int32_t *ul = idx + u * kcap;
+  const float *ds = dscore + u * kcap;
+  const float *rbase = reps + ug.b * rb + (int64_t)ug.g * rh;
+  a = 0.f;
+  for (int e = rg; e < ns; e += RG) a += ds[e] * rbase[(int64_t)ul[e] * rj + dim];
+  part[rg][dim] = a;
+  __syncthreads();
+  if (rg == 0) {
+    float t = 0.f;
+#pragma unroll
+    for (int y = 0; y < RG; ++y) t += part[y][dim];
+    dqbar[dim] = scale * t / (float)F;
+  }
+  __syncthreads();
+  for (int f = rg; f < F; f += RG)
+    dQ[ug.b * dqb + (int64_t)(ug.h0 + f / ug.rows) * dqh + (int64_t)(ug.t_lo + f % ug.rows) * dqt + dim] += dqbar[dim];
+  float *dr = dreps + ((int64_t)ug.b * hkv + ug.g) * NBm * D;
+  for (int e = rg; e < ns; e += RG) unsafeAtomicAdd(dr + (int64_t)ul[e] * D + dim, scale * ds[e] * qbar[dim]);
+}
+
+// dK[key] += dr_j / n_j for every present key of block j (n_j its present keys)
+__global__ __launch_bounds__(256) void bwd_chain_k_kernel(SeqTable st, int hkv, int blk, int NBm, int D, int64_t nkeys,
+                                                         const float *__restrict__ dreps, float *__restrict__ dK,
+                                                         int64_t gb, int64_t gh, int64_t gt, int64_t lmax) {
+  for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < nkeys * D; x += (int64_t)gridDim.x * 256) {
+    const int dim = (int)(x % D);
+    const int64_t r = x / D;
+    const int key = (int)(r % lmax);
+    const int64_t bg = r / lmax;
+    const int b = (int)(bg / hkv), g = (int)(bg % hkv);
+    const int L = st.len[b];
+    if (key >= L) continue;
+    const int j = key / blk;
+    const int nj = min(blk, L - j * blk);
+    dK[b * gb + (int64_t)g * gh + (int64_t)key * gt + dim] += dreps[(bg * NBm + j) * D + dim] / (float)nj;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------------------------
 BwdPlan bwd_plan(const sas_problem &p, int32_t tq, int32_t sel_mode, int32_t kcap, bool gate) {
@@ -789,8 +864,9 @@ BwdPlan bwd_plan(const sas_problem &p, int32_t tq, int32_t sel_mode, int32_t kca
   x.off_gpart = off;
   if (gate) off += al((size_t)x.units * x.gslots * kcap * sizeof(float));
   x.off_bits = off;
-  x.clear_words = (int64_t)x.npairs * x.NBm * (x.W + 1);
-  off += al((size_t)x.clear_words * sizeof(uint32_t));  // bits, then counts
+  // bits, then counts, then (with a gate) the block means' gradient [pairs, NBm, d] fp32
+  x.clear_words = (int64_t)x.npairs * x.NBm * (x.W + 1 + (gate ? p.head_dim : 0));
+  off += al((size_t)x.clear_words * sizeof(uint32_t));
   x.off_epos = off;
   if (gate) off += al((size_t)x.npairs * x.NBm * x.UG * sizeof(int16_t));
   x.off_items = off;
@@ -808,7 +884,7 @@ static hipError_t bwd_dispatch(const sas_problem &p, const SeqTable &st, const B
                                const int32_t *idx,
                                const int32_t *nsel, const float *gate, int32_t kcap, float scale, float *dQ,
                                const int64_t *dqs, float *dK, float *dV, const int64_t *dkvs, float *dgate,
-                               float *dscore, char *ws, hipStream_t s) {
+                               float *dscore, const float *reps, const int64_t *rs, char *ws, hipStream_t s) {
   const int per_head = sel_mode == SAS_SEL_HEAD;
   const int G = p.hq / p.hkv;
   const int S = per_head ? p.hq : p.hkv;
@@ -864,6 +940,17 @@ static hipError_t bwd_dispatch(const sas_problem &p, const SeqTable &st, const B
     hipLaunchKernelGGL(bwd_gate_kernel, dim3((unsigned)cdiv64(pl.units, 4)), dim3(256), 0, s, st, pl.units, S, pl.QB,
                        G, per_head, tq, p.block, nsel, gate, kcap, (const float *)gpart, pl.gslots, dgate, dscore);
   }
+  if (gate && reps) {
+    // on through the selector scores: into dQ (pooled query) and, via the block means, dK
+    float *dreps = (float *)(counts + (int64_t)pl.npairs * pl.NBm);
+    hipLaunchKernelGGL((bwd_chain_kernel<D>), dim3((unsigned)pl.units), dim3(256), 0, s, st, q16, qs[0], qs[1], qs[2],
+                       tq, S, pl.QB, G, per_head, p.hkv, idx, nsel, kcap, (const float *)dscore, reps, rs[0], rs[1],
+                       rs[2], scale, dQ, dqs[0], dqs[1], dqs[2], dreps, pl.NBm, p.block);
+    const int64_t nkeys = (int64_t)pl.npairs * p.max_len;
+    const unsigned g = (unsigned)std::min<int64_t>(8192, std::max<int64_t>(1, cdiv64(nkeys * D, 256)));
+    hipLaunchKernelGGL(bwd_chain_k_kernel, dim3(g), dim3(256), 0, s, st, p.hkv, p.block, pl.NBm, D, nkeys,
+                       (const float *)dreps, dK, dkvs[0], dkvs[1], dkvs[2], (int64_t)p.max_len);
+  }
   return hipGetLastError();
 }
 
@@ -872,12 +959,13 @@ hipError_t launch_prefill_backward(const sas_problem &p, const SeqTable &st, con
                                    const int64_t *os, const float *lse_in, int32_t tq, int32_t sel_mode,
                                    const int32_t *idx, const int32_t *nsel, const float *gate, int32_t kcap,
                                    float scale, float *dQ, const int64_t *dqs, float *dK, float *dV,
-                                   const int64_t *dkvs, float *dgate, float *dscore, void *workspace, hipStream_t s) {
+                                   const int64_t *dkvs, float *dgate, float *dscore, const float *reps,
+                                   const int64_t *rs, void *workspace, hipStream_t s) {
   const BwdPlan pl = bwd_plan(p, tq, sel_mode, kcap, gate != nullptr);
   char *ws = (char *)workspace;
 #define SAS_BWD(D_, B_)                                                                                            \
   return bwd_dispatch<D_, B_>(p, st, pl, Q, qs, K, V, kvs, O, dO, os, lse_in, tq, sel_mode, idx, nsel, gate, kcap, scale, \
-                              dQ, dqs, dK, dV, dkvs, dgate, dscore, ws, s)
+                              dQ, dqs, dK, dV, dkvs, dgate, dscore, reps, rs, ws, s)
   if (p.head_dim == 128) {
     if (p.block == 64) SAS_BWD(128, 64);
     SAS_BWD(128, 128);

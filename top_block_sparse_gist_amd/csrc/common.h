@@ -272,8 +272,8 @@ hipError_t launch_hssa_decode(const sas_problem &p, const SeqTable &st, const vo
 
 // Backward of the sparse prefill: sizes and workspace layout (host formula shared with the size
 // query).  Workspace regions, 256-byte aligned: row LSE and D [B, Hq, tq] fp32; gate partials
-// [units, gslots, kcap] fp32 (with a gate); selection bitmap [pairs, NBm, W] u32 then per-block
-// counts [pairs, NBm]; entry positions [pairs, NBm, UG] int16 (with a gate); work items
+// [units, gslots, kcap] fp32 (with a gate); selection bitmap [pairs, NBm, W] u32, per-block
+// counts [pairs, NBm] and (with a gate) the block means' gradient [pairs, NBm, d] fp32; entry positions [pairs, NBm, UG] int16 (with a gate); work items
 // [pairs, cap] x 16 bytes; item counts [pairs].
 constexpr int BWD_SEGMAX = 256;       // units per dK/dV work item
 constexpr int BWD_SEG_ROWS = 32768;   // flattened rows per dK/dV work item (a block's list is cut
@@ -289,6 +289,7 @@ hipError_t launch_prefill_backward(const sas_problem &p, const SeqTable &st, con
                                    const int64_t *os, const float *lse, int32_t tq, int32_t sel_mode,
                                    const int32_t *idx, const int32_t *nsel, const float *gate, int32_t kcap,
                                    float scale, float *dQ, const int64_t *dqs, float *dK, float *dV,
-                                   const int64_t *dkvs, float *dgate, float *dscore, void *workspace, hipStream_t s);
+                                   const int64_t *dkvs, float *dgate, float *dscore, const float *reps,
+                                   const int64_t *rs, void *workspace, hipStream_t s);
 
 }  // namespace sas
