@@ -290,3 +290,11 @@ def test_backward_full_32k_prefill_properties():
     frac = float(same[:, :L].float().mean())
     say(f"[bwd-full] dK/dV rows bitwise equal across two calls: {frac:.4f}")
     assert frac >= 0.9
+
+
+def test_backward_few_rows_per_unit():
+    """tq = 5 rows across a block boundary, per-head units of 2-3 rows: every 32-row step is mostly
+    padding (rows past the unit masked, staged rows clamped to the unit's last)."""
+    w = Workload(3, overrides=dict(tag="bwd_few", seq_len=646, tq=5, block=64, hq=6, hkv=2, sel="head",
+                                   frac_num=0, frac_den=0, k_fixed=3, sink=True, gate=True))
+    run_backward_case(w, use_lse=True, through_scores=True)
