@@ -82,14 +82,19 @@ typedef struct sas_problem {
 /* Budget ([SAS] method: a fixed budget of k context units per query, configurable;
  * [GSA] section 4 pseudo-code keep_ratio).  For a unit whose current block is c:
  *   candidates = blocks 0 .. c-1, minus block 0 when force_sink;
- *   k = k_fixed                                            if frac_den == 0
+ *   k = ceil(sqrt_num * sqrt(c + count_current) / sqrt_den) if sqrt_den > 0 (integer-exact)
+ *   k = k_fixed                                            else if frac_den == 0
  *   k = ceil(frac_num * (c + count_current) / frac_den)    otherwise (integer arithmetic)
  *   k is capped at the candidate count; the current block c is always added ([SAS] core
  *   insight), and block 0 when force_sink ([SF] 2.2.3, first prefix block).
+ *   The square-root rule is the length-adaptive budget ([SF] 4.3.2 iso-error curve: the budget
+ *   that keeps one error level goes from 1/10 of a 16K context to 1/20 of a 64K one, i.e. the kept
+ *   tokens double when the length quadruples; 4.4.2: grow the budget sub-linearly with length).
+ *   It is evaluated exactly: k is the smallest integer with (k sqrt_den)^2 >= sqrt_num^2 n.
  * Coverage budget ([SF] 2.3, threshold-based allocation), when coverage > 0: k is the
  *   smallest number of candidates, in (score descending, index ascending) order, whose share of
  *   the candidates' softmax mass (softmax of their scores) is >= coverage (<= 1), capped by the
- *   rule above only when k_fixed > 0 or frac_den > 0.  The shares are summed in fp32: where the
+ *   rule above only when k_fixed > 0, frac_den > 0 or sqrt_den > 0.  The shares are summed in fp32: where the
  *   exact share of the k-th candidate lies within ~1e-5 of coverage, k may differ by one from
  *   an exact evaluation.
  * Shared budget ([SF] 2.3, Ada-KV: top k x h over h heads), when shared_heads = 1 (per-head
@@ -105,6 +110,7 @@ typedef struct sas_budget {
   int32_t gate;             /* 1: write the log-gate over the selected set                  */
   float coverage;           /* 0: off; else in (0, 1]                                        */
   int32_t shared_heads;     /* 1: the heads of a KV group share G * k (per-head selection)     */
+  int32_t sqrt_num, sqrt_den; /* square-root (length-adaptive) rule when sqrt_den > 0; each <= 65535 */
 } sas_budget;
 
 /* Number of query blocks tq consecutive positions can touch: ceil((tq-1)/blk) + 1. */
@@ -163,6 +169,10 @@ sas_status sas_block_scores(const sas_problem *p, const void *Q, const int64_t q
  *   nsel [units] int32: list length (0 for unit slots no row falls in);
  *   gate [units, kcap] fp32 (required iff budget->gate, else ignored and may be NULL):
  *   g = s_j - log(sum over the selected set of exp(s)), 0 in the padding.
+ *   A gate value belongs to the unit, not to a row: in prefill it comes from scores that pool all of
+ *   the unit's rows, and the current block's score uses the mean of all of that block's present keys
+ *   (later positions included).  Which keys a row attends stays causal; the gate value added to its
+ *   logits is a unit-level quantity, so prefill and decode at the same position can differ in it.
  *   kcap must be >= sas_required_kcap(). */
 sas_status sas_topk_select(const sas_problem *p, const float *scores, int64_t scores_ld,
                            int32_t tq, const int32_t *q_start, int32_t sel_mode,
@@ -337,7 +347,11 @@ const char *sas_last_error(void);
  *   s_j = scale * qbar . r_j of the unit's mean query vector qbar and the block means r_j, so each of
  *   the unit's query vectors gets scale * sum_j dscore_j r_j / (its vector count) added to dQ, and
  *   each present key of block j gets scale * sum over the units keeping j of dscore_j qbar, divided
- *   by the block's key count, added to dK (those sums use fp32 atomic adds).  Lists stay fixed.
+ *   by the block's key count, added to dK (a fixed-order sum per block over the units that keep it,
+ *   so it is deterministic).  Lists stay fixed.  The gradient follows the forward as defined: a unit's
+ *   score pools all of its rows and the current block's mean covers all of that block's present keys,
+ *   so a row's loss also reaches, through its unit's gate value, the unit's other rows' queries and
+ *   the current block's keys after the row (see sas_topk_select).
  *   Q, K, V, idx, nsel, gate, kcap, scale: as given to sas_sparse_prefill (bf16 only).
  *   kcap <= 32767.  workspace: sas_sparse_prefill_backward_workspace(p, tq, sel_mode, kcap, gate
  *   != NULL) bytes of device scratch (no initial contents needed; it grows with the batch, the rows,
@@ -346,8 +360,8 @@ const char *sas_last_error(void);
  *   and dscore are deterministic; dK and dV are too, except in blocks whose selecting units hold
  *   more than 32768 (row, head) pairs in all, or number more than 256: their unit list is cut into
  *   several work items whose partial sums meet in fp32 atomic adds.
- *   Errors: as sas_sparse_prefill; SAS_ERR_UNSUPPORTED for fp32; SAS_ERR_WORKSPACE when too small;
- *   SAS_ERR_SHAPE for reps without a gate. */
+ *   Errors: as sas_sparse_prefill; SAS_ERR_UNSUPPORTED for fp32 and for per-group units with more than 64
+ *   query heads per KV head; SAS_ERR_WORKSPACE when too small; SAS_ERR_SHAPE for reps without a gate. */
 size_t sas_sparse_prefill_backward_workspace(const sas_problem *p, int32_t tq, int32_t sel_mode, int32_t kcap,
                                              int32_t gate);
 sas_status sas_sparse_prefill_backward(const sas_problem *p, const void *Q, const int64_t q_stride[3],

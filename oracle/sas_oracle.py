@@ -150,14 +150,37 @@ def unit_scores(qvecs: np.ndarray, reps: np.ndarray, upto: int, scale: float) ->
 # ---------------------------------------------------------------------------------------------
 # 4. budget and top-k
 # ---------------------------------------------------------------------------------------------
-def budget_k(c: int, n_cand: int, k_fixed: int, frac_num: int, frac_den: int, count_current: int) -> int:
+def sqrt_budget(n: int, num: int, den: int) -> int:
+    """Length-adaptive (sub-linear) budget: ceil(num * sqrt(n) / den), n = c + count_current blocks.
+
+    [SF] 4.3.2 (iso-error curve): the budget that holds one error level falls from 1/10 of a 16K
+    context to 1/20 of a 64K one, so the kept tokens double while the length quadruples, which is
+    growth as the square root of the length; [SF] 4.4.1-4.4.2: fixed-ratio budgets are suboptimal,
+    grow the budget sub-linearly with length.  Reading: k grows as sqrt(n) with a coefficient
+    num/den.  Evaluated exactly: num * sqrt(n) = sqrt(num^2 n), and k * den is an integer, so the
+    smallest k with k * den >= sqrt(num^2 n) is the ceiling of ceil(sqrt(num^2 n)) / den.
+    """
+    if n <= 0 or num <= 0:
+        return 0
+    x = num * num * n
+    r = math.isqrt(x)
+    if r * r < x:
+        r += 1
+    return -(-r // den)
+
+
+def budget_k(c: int, n_cand: int, k_fixed: int, frac_num: int, frac_den: int, count_current: int,
+             sqrt_num: int = 0, sqrt_den: int = 0) -> int:
     """Number of blocks the top-k part keeps for a unit whose current block is c.
 
     Fixed budget: k_fixed.  Fractional budget: ceil(frac_num * (c + count_current) / frac_den)
     in integers (the pages state budgets as a kept fraction, [GSA] section 4 pseudo-code
-    keep_ratio, [SF] 1.2: 0.95 sparsity keeps 1/20).  Never more than the candidates.
+    keep_ratio, [SF] 1.2: 0.95 sparsity keeps 1/20).  Square-root budget (sqrt_den > 0, which takes
+    precedence): sqrt_budget(c + count_current, sqrt_num, sqrt_den).  Never more than the candidates.
     """
-    if frac_den == 0:
+    if sqrt_den > 0:
+        k = sqrt_budget(c + count_current, sqrt_num, sqrt_den)
+    elif frac_den == 0:
         k = k_fixed
     else:
         num = frac_num * (c + count_current)
@@ -305,7 +328,7 @@ def run_sequence(Qb: np.ndarray, Kb: np.ndarray, Vb: np.ndarray, L: int, q_start
                  sel_mode: str, k_fixed: int = 0, frac_num: int = 0, frac_den: int = 0,
                  count_current: int = 0, sink: bool = False, gate: bool = False,
                  scale: Optional[float] = None, gist_k: Optional[np.ndarray] = None,
-                 coverage: float = 0.0, shared: bool = False,
+                 coverage: float = 0.0, shared: bool = False, sqrt_num: int = 0, sqrt_den: int = 0,
                  gist_v: Optional[np.ndarray] = None, mode: str = "skip",
                  unit_filter=None, attend: bool = True, reps: Optional[np.ndarray] = None,
                  explicit: Optional[Dict[Tuple[int, int], Tuple[List[int], Optional[Dict[int, float]]]]] = None
@@ -358,13 +381,14 @@ def run_sequence(Qb: np.ndarray, Kb: np.ndarray, Vb: np.ndarray, L: int, q_start
             s = unit_scores(qv, reps[g], u.c + 1, scale)
         u.scores = s
         n_cand = u.c - (1 if (sink and u.c > 0) else 0)
+        rule_k = budget_k(u.c, n_cand, k_fixed, frac_num, frac_den, count_current, sqrt_num, sqrt_den)
         if coverage > 0.0:
-            # coverage budget, capped by the fixed or fractional rule when one is given
+            # coverage budget, capped by the fixed, fractional or square-root rule when one is given
             kc = coverage_k(s, u.c, sink and u.c > 0, coverage)
-            capped = k_fixed > 0 or frac_den > 0
-            u.k = min(kc, budget_k(u.c, n_cand, k_fixed, frac_num, frac_den, count_current)) if capped else kc
+            capped = k_fixed > 0 or frac_den > 0 or sqrt_den > 0
+            u.k = min(kc, rule_k) if capped else kc
         else:
-            u.k = budget_k(u.c, n_cand, k_fixed, frac_num, frac_den, count_current)
+            u.k = rule_k
     # ---- selection
     if shared:
         by_group: Dict[Tuple[int, int], List[Unit]] = {}

@@ -101,7 +101,7 @@ def selection_matches(un, gsel: List[int], scores: np.ndarray, budget) -> Tuple[
     k_gpu = len(gsel) - nforced
     if k_gpu == un.k:
         return list_matches(un.sel, gsel, scores, un.c, un.k, budget.sink)
-    capped = budget.k_fixed > 0 or budget.frac_den > 0
+    capped = budget.k_fixed > 0 or budget.frac_den > 0 or budget.sqrt_den > 0
     if capped and k_gpu > un.k:
         return False, False, f"{k_gpu} kept above the cap's {un.k}"
     if not coverage_length_ok(scores, un.c, budget.sink, budget.coverage, k_gpu):
@@ -166,12 +166,18 @@ def sel_count(w: Workload) -> int:
 def budget_of(w: Workload) -> sas.Budget:
     return sas.Budget(k_fixed=w.k_fixed, frac_num=w.frac_num, frac_den=w.frac_den,
                       count_current=w.count_current, sink=w.sink, gate=w.gate,
-                      coverage=float(w.spec.get("coverage", 0.0)), shared=bool(w.spec.get("shared", False)))
+                      coverage=float(w.spec.get("coverage", 0.0)), shared=bool(w.spec.get("shared", False)),
+                      sqrt_num=w.sqrt_num, sqrt_den=w.sqrt_den)
 
 
 def run_case(w: Workload, seqs: List[int], unit_sample: Optional[int] = None, seed: int = 0,
-             budget_override: Optional[sas.Budget] = None, check_scores: bool = True) -> Report:
-    """Run the whole path for the given sequences (all prefill or all decode) and compare."""
+             budget_override: Optional[sas.Budget] = None, check_scores: bool = True, keep_n: int = 2,
+             unit_keys=()) -> Report:
+    """Run the whole path for the given sequences (all prefill or all decode) and compare.
+
+    unit_sample: compare a seeded sample of that many units per kept sequence (keep_n sequences kept
+    on the host) instead of every unit; unit_keys: (selector head, current block) pairs compared in
+    every kept sequence besides the sample."""
     import torch
     bf16 = w.is_bf16()
     gist = w.kind == "gist_decode"
@@ -181,7 +187,7 @@ def run_case(w: Workload, seqs: List[int], unit_sample: Optional[int] = None, se
     S = sel_count(w)
     say(f"[case] {w.name} seqs={seqs} decode={decode} gist={gist} sample={unit_sample}")
     # which sequences get oracle attention (sampled runs keep at most 2 sequences on the host)
-    keep = list(seqs) if unit_sample is None else list(rng.choice(seqs, size=min(2, len(seqs)), replace=False))
+    keep = list(seqs) if unit_sample is None else list(rng.choice(seqs, size=min(keep_n, len(seqs)), replace=False))
     inp = upload(w, seqs, keep_host=set(int(x) for x in keep), gist=gist)
     lens = inp.seq_lens
     B = len(seqs)
@@ -242,6 +248,7 @@ def run_case(w: Workload, seqs: List[int], unit_sample: Optional[int] = None, se
         chosen = set(range(len(units)))
         if unit_sample is not None:
             chosen = set(int(x) for x in rng.choice(len(units), size=min(unit_sample, len(units)), replace=False))
+            chosen |= {x for x, un in enumerate(units) if (un.sel_head, un.c) in set(unit_keys)}
         keyset = {(units[x].sel_head, units[x].c) for x in chosen}
         filt = lambda u: (u.sel_head, u.c) in keyset  # noqa: E731
         # oracle: reps/scores/selection for chosen units, no attention yet
@@ -251,7 +258,7 @@ def run_case(w: Workload, seqs: List[int], unit_sample: Optional[int] = None, se
                              frac_num=budget.frac_num, frac_den=budget.frac_den,
                              count_current=budget.count_current, sink=budget.sink, gate=budget.gate,
                              gist_k=gk, gist_v=gv, unit_filter=filt, attend=False, coverage=budget.coverage,
-                             shared=budget.shared)
+                             shared=budget.shared, sqrt_num=budget.sqrt_num, sqrt_den=budget.sqrt_den)
         if not gist:
             nb = orc.num_blocks(L, w.block)
             dr = np.abs(reps_h[bi, :, :nb] - r.reps)
@@ -317,7 +324,8 @@ def run_case(w: Workload, seqs: List[int], unit_sample: Optional[int] = None, se
                               frac_num=budget.frac_num, frac_den=budget.frac_den,
                               count_current=budget.count_current, sink=budget.sink, gate=budget.gate,
                               gist_k=gk, gist_v=gv, unit_filter=filt, reps=r.reps, explicit=explicit,
-                              coverage=budget.coverage, shared=budget.shared)
+                              coverage=budget.coverage, shared=budget.shared, sqrt_num=budget.sqrt_num,
+                              sqrt_den=budget.sqrt_den)
         mask = ~np.isnan(r2.O[:, :, 0])
         gpu_rows = O_h[bi] if not decode else O_h[bi][:, None, :]
         out_check(rep, gpu_rows[mask], r2.O[mask], bf16)

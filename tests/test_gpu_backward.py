@@ -292,6 +292,127 @@ def test_backward_full_32k_prefill_properties():
     assert frac >= 0.9
 
 
+def _unit_alone(h, dO_b, un, G, sel, blk, q0):
+    """The unit's own slice of the inputs: its heads' query/dO rows and its KV head, re-indexed so
+    that the oracle's backward builds a graph of this unit only (head 0.., KV head 0, rows 0..)."""
+    g = un.heads[0] // G
+    heads = list(un.heads)
+    q = h["q"][heads, un.t_lo:un.t_hi]
+    do = dO_b[heads, un.t_lo:un.t_hi]
+    u2 = orc.Unit(sel_head=0, c=un.c, t_lo=0, t_hi=un.t_hi - un.t_lo, heads=tuple(range(len(heads))),
+                  scores=un.scores, sel=un.sel, k=un.k, gate=un.gate)
+    return q, h["k"][g:g + 1], h["v"][g:g + 1], do, q0 + un.t_lo, u2
+
+
+def run_backward_full_sampled(w, seqs, keep, unit_sample, n_blocks, max_units_per_block, seed):
+    """Full size, in the launch configuration bench.py times: the GPU's own lists, gates, O and
+    log-sum-exp.  Each unit's dQ rows, dgate and dscore depend only on that unit, and each block's
+    dK/dV rows only on the units that keep it, so sampled units and sampled blocks (with every unit
+    keeping them) are compared with the float64 oracle, at the bars above."""
+    say(f"[bwd-sampled] {w.name} seqs={seqs} keep={keep} units={unit_sample} blocks={n_blocks}")
+    inp = upload(w, seqs, keep_host=set(keep))
+    lens, blk, tq = inp.seq_lens, w.block, w.tq
+    Lmax = inp.K.shape[2]
+    S = w.hkv if w.sel == "group" else w.hq
+    G = w.hq // w.hkv
+    QB = sas.num_qblocks(tq, blk)
+    scale = 1.0 / math.sqrt(w.d)
+    budget = sas.Budget(k_fixed=w.k_fixed, frac_num=w.frac_num, frac_den=w.frac_den,
+                        count_current=w.count_current, sink=w.sink, gate=w.gate)
+    reps = sas.block_reps(inp.K, lens, blk)
+    scores = sas.block_scores(inp.Q, reps, lens, blk, w.hkv, Lmax, q_start=inp.q_start, sel_mode=w.sel)
+    idx, nsel, gate = sas.topk_select(scores, lens, blk, w.hq, w.hkv, w.d, sas.SAS_BF16, Lmax, budget, tq=tq,
+                                      q_start=inp.q_start, sel_mode=w.sel)
+    lse = torch.empty(inp.Q.shape[:3], dtype=torch.float32, device=inp.Q.device)
+    O = sas.sparse_prefill(inp.Q, inp.K, inp.V, lens, blk, inp.q_start, idx, nsel, gate, sel_mode=w.sel, lse=lse)
+    dO = torch.zeros_like(inp.Q)
+    for bi, b in enumerate(seqs):
+        dO[bi] = _bf16(w.grad_out(b)).to(dO.device)
+    dQ, dK, dV, dgate, dscore = sas.sparse_prefill_backward(inp.Q, inp.K, inp.V, O, dO, lens, blk, inp.q_start, idx,
+                                                            nsel, gate, sel_mode=w.sel, lse=lse)
+    torch.cuda.synchronize()
+    say("[bwd-sampled] gpu done")
+    idx_h, nsel_h = idx.cpu().numpy(), nsel.cpu().numpy()
+    dgate_h, dscore_h = dgate.cpu().numpy(), dscore.cpu().numpy()
+    rng = np.random.default_rng(seed)
+    acc = {k: ([], []) for k in ("dQ", "dgate", "dscore", "dK", "dV")}
+    n_units = n_blk = 0
+    for b in keep:
+        bi = seqs.index(b)
+        h = inp.host[b]
+        L, q0 = w.seq_lens[b], w.q_start[b]
+        dO_b = w.grad_out(b)
+        reps_o = np.stack([orc.block_reps(h["k"][g], L, blk) for g in range(w.hkv)])
+        units = orc.make_units(q0, w.rows[b], blk, w.hq, w.hkv, w.sel)
+        slot = {}
+        for un in units:
+            x = (bi * S + un.sel_head) * QB + (un.c - q0 // blk)
+            slot[(un.sel_head, un.c)] = x
+            un.sel = [int(j) for j in idx_h[x, :nsel_h[x]]]
+            g = orc.kv_head_of(un, G, w.sel)
+            un.scores = orc.unit_scores(orc.unit_query_vectors(h["q"], un), reps_o[g], un.c + 1, scale)
+        dQ_b = dQ[bi].cpu().numpy()
+        for x in rng.choice(len(units), size=min(unit_sample, len(units)), replace=False):
+            un = units[int(x)]
+            q, k, v, do, qs, u2 = _unit_alone(h, dO_b, un, G, w.sel, blk, q0)
+            ref = orcb.backward_sequence(q, k, v, do, L, qs, blk, [u2], w.gate, scale)
+            acc["dQ"][0].append(dQ_b[list(un.heads), un.t_lo:un.t_hi].ravel())
+            acc["dQ"][1].append(ref["dQ"].ravel())
+            if w.gate:
+                n = len(un.sel)
+                xs = slot[(un.sel_head, un.c)]
+                acc["dgate"][0].append(dgate_h[xs, :n]); acc["dgate"][1].append(ref["dgate"][(0, un.c)])
+                acc["dscore"][0].append(dscore_h[xs, :n]); acc["dscore"][1].append(ref["dscore"][(0, un.c)])
+            n_units += 1
+        # blocks: every unit of the KV head that keeps the block contributes to its dK/dV rows
+        keepers = {}
+        for un in units:
+            for j in un.sel:
+                keepers.setdefault((orc.kv_head_of(un, G, w.sel), j), []).append(un)
+        cands = [(g, j, us) for (g, j), us in sorted(keepers.items()) if len(us) <= max_units_per_block]
+        for x in rng.choice(len(cands), size=min(n_blocks, len(cands)), replace=False):
+            g, j, us = cands[int(x)]
+            lo, hi = j * blk, min((j + 1) * blk, L)
+            rk = np.zeros((hi - lo, w.d))
+            rv = np.zeros((hi - lo, w.d))
+            for un in us:
+                q, k, v, do, qs, u2 = _unit_alone(h, dO_b, un, G, w.sel, blk, q0)
+                ref = orcb.backward_sequence(q, k, v, do, L, qs, blk, [u2], w.gate, scale)
+                rk += ref["dK"][0, lo:hi]
+                rv += ref["dV"][0, lo:hi]
+            acc["dK"][0].append(dK[bi, g, lo:hi].cpu().numpy().ravel()); acc["dK"][1].append(rk.ravel())
+            acc["dV"][0].append(dV[bi, g, lo:hi].cpu().numpy().ravel()); acc["dV"][1].append(rv.ravel())
+            n_blk += 1
+            say(f"[bwd-sampled] sequence {b}, KV head {g}, block {j}: {len(us)} units")
+    stats = {}
+    for name, (got, ref) in acc.items():
+        if got:
+            _check(name, np.concatenate(got), np.concatenate(ref), stats)
+    for k_, (a, m, top) in stats.items():
+        say(f"[bwd-sampled] {k_}: max-abs/max|ref| {a:.2e}  mean-abs/max|ref| {m:.2e}  (max|ref| {top:.3g})")
+    say(f"[bwd-sampled] {n_units} units, {n_blk} blocks checked")
+    assert n_units >= unit_sample and n_blk >= 1
+    return stats
+
+
+@pytest.mark.timeout(900)
+def test_backward_full_32k_sampled_against_the_oracle():
+    """The 32K prefill (28/4 heads, 128-key blocks, top c/8 + sink + current, gate): 48 units (896
+    query vectors each) and 4 blocks with all the units that keep them."""
+    w = Workload(3)
+    run_backward_full_sampled(w, [0], [0], unit_sample=48, n_blocks=4, max_units_per_block=24, seed=13)
+
+
+@pytest.mark.timeout(900)
+def test_backward_full_mixed_prefill_sampled_against_the_oracle():
+    """The mixed batch's prefill half (8 sequences of 4096 rows, per-head lists at sparsity 0.95,
+    gate), as bench.py times it: 64 units and 6 blocks in each of 2 sequences."""
+    w = Workload(5)
+    seqs = w.prefill_seqs()
+    run_backward_full_sampled(w, seqs, [seqs[1], seqs[6]], unit_sample=64, n_blocks=6, max_units_per_block=40,
+                              seed=17)
+
+
 def test_backward_few_rows_per_unit():
     """tq = 5 rows across a block boundary, per-head units of 2-3 rows: every 32-row step is mostly
     padding (rows past the unit masked, staged rows clamped to the unit's last)."""

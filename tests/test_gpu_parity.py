@@ -231,8 +231,12 @@ def test_c2_decode_full_sampled():
 
 @pytest.mark.timeout(600)
 def test_c3_prefill_full_sampled():
+    """32 random units plus all 4 KV heads of the last 8 query blocks (the longest lists: 33-34
+    blocks of 128 keys over 896 rows each)."""
     w = Workload(3)
-    run_case(w, [0], unit_sample=6, seed=3)
+    last = [(g, c) for g in range(w.hkv) for c in range(248, 256)]
+    rep = run_case(w, [0], unit_sample=32, seed=3, unit_keys=last)
+    assert rep.units >= 64
 
 
 @pytest.mark.timeout(600)
@@ -243,8 +247,12 @@ def test_c4_gist_decode_full_sampled():
 
 @pytest.mark.timeout(600)
 def test_c5_prefill_half_full_sampled():
+    """64 per-head units in each of 4 of the 8 prefill sequences, plus the last query block of every
+    head in them (the longest lists)."""
     w = Workload(5)
-    run_case(w, w.prefill_seqs(), unit_sample=24, seed=5)
+    last = [(h, (w.seq_lens[b] - 1) // w.block) for b in w.prefill_seqs() for h in range(w.hq)]
+    rep = run_case(w, w.prefill_seqs(), unit_sample=64, seed=5, keep_n=4, unit_keys=last)
+    assert rep.units >= 256
 
 
 @pytest.mark.timeout(600)
@@ -492,3 +500,120 @@ def test_shared_budget_prefill():
     w = Workload(3, overrides=dict(tag="sh", seq_len=3000, tq=800, hq=8, hkv=2, block=64, sel="head", frac_num=1,
                                    frac_den=8, sink=True, gate=True, shared=True))
     run_case(w, [0])
+
+
+# ------------------------------------------------------------------------------ near ties
+def test_near_tie_output_checked_on_the_gpu_list():
+    """Two planted needle blocks whose exact scores differ by ~1e-11 relative (inside the 1e-5 tie
+    band, not equal): the oracle keeps the later one, fp32 scoring sees a tie and keeps the earlier
+    one.  The lists must differ only inside the band, and the output is then compared with the
+    oracle run on the GPU's own list (the explicit-list branch), with and without the gate."""
+    w = Workload(2, overrides=dict(tag="ntie", seq_lens=[3000, 5000, 2000, 7000], batch=4, hq=8, hkv=2, k_fixed=1,
+                                   needles=0, near_tie=True, seq_len=None))
+    rep = run_case(w, list(range(4)))
+    assert rep.tie_band_units > 0, "no unit took the tie-band branch"
+    wg = Workload(2, overrides=dict(tag="ntieg", seq_lens=[3000, 5000, 2000, 7000], batch=4, hq=8, hkv=2, k_fixed=1,
+                                    needles=0, near_tie=True, gate=True, sink=True, seq_len=None))
+    repg = run_case(wg, list(range(4)))
+    assert repg.tie_band_units > 0, "no unit took the tie-band branch"
+
+
+# ------------------------------------------------------------------------------ square-root budgets
+def test_sqrt_budget_decode():
+    """k = ceil(8 sqrt(c + 1) / 5) (a 16K context keeps 1/10, a 64K one 1/20): per-group units
+    through the fused selection (one wave and the four-wave top-k) and the two calls, then per-head
+    units with the gate as in the mixed batch."""
+    w = Workload(2, overrides=dict(tag="sqrtg", seq_lens=[3000, 16384, 65536, 40000], batch=4, hq=8, hkv=2,
+                                   k_fixed=0, sqrt_num=8, sqrt_den=5, count_current=1, seq_len=None))
+    run_case(w, list(range(4)))
+    wh = Workload(2, overrides=dict(tag="sqrth", seq_lens=[20000, 6000], batch=2, sel="head", hq=8, hkv=2, k_fixed=0,
+                                    sqrt_num=8, sqrt_den=5, count_current=1, gate=True, seq_len=None))
+    run_case(wh, [0, 1])
+
+
+def test_sqrt_budget_prefill():
+    """Per-group (sink, gate) and per-head prefill units through the two-call top-k."""
+    w = Workload(3, overrides=dict(tag="sqrt", seq_len=4000, tq=1200, hq=8, hkv=2, block=64, frac_num=0, frac_den=0,
+                                   k_fixed=0, sqrt_num=3, sqrt_den=2, sink=True, gate=True))
+    run_case(w, [0])
+    wh = Workload(3, overrides=dict(tag="sqrth", seq_len=2600, tq=700, hq=4, hkv=2, block=64, sel="head",
+                                    frac_num=0, frac_den=0, k_fixed=0, sqrt_num=1, sqrt_den=1, count_current=1,
+                                    gate=True))
+    run_case(wh, [0])
+
+
+# ------------------------------------------------------------------------------ paged decode loop
+def test_paged_decode_loop_against_the_oracle():
+    """A decode loop over a paged cache: each step appends one token per sequence into its page (a
+    fresh page from a shuffled free list when the token opens a block), updates the block table,
+    pools again only the blocks from floor(L_old / blk) on through the table, selects, and attends
+    through the table; every step's reps, lists and outputs are compared with the oracle on the
+    contiguous cache at the new length (lengths cross block boundaries)."""
+    from oracle import sas_oracle as orc
+    from workloads.gen import round_bf16
+    from gpu_harness import list_matches, BF16_MAX_ABS, BF16_MEAN_ABS
+    lens = [1000, 127, 4096, 63]
+    steps, B, hq, hkv, d, blk, k = 3, 4, 8, 2, 128, 64, 4
+    Lmax = max(lens) + steps
+    nbmax = -(-Lmax // blk)
+    rng = np.random.default_rng(41)
+    K = round_bf16(rng.standard_normal((B, hkv, Lmax, d), dtype=np.float32))
+    V = round_bf16(rng.standard_normal((B, hkv, Lmax, d), dtype=np.float32))
+    Q = round_bf16(rng.standard_normal((B, hq, d), dtype=np.float32))
+    Qd = torch.from_numpy(Q).to(torch.bfloat16).cuda()
+    npages = B * nbmax + 7
+    free = [int(x) for x in rng.permutation(npages)]
+    Kp = torch.zeros((npages, hkv, blk, d), dtype=torch.bfloat16, device="cuda")
+    Vp = torch.zeros_like(Kp)
+    table_h = torch.full((B, nbmax), -1, dtype=torch.int32)
+
+    def write_tokens(b, lo, hi):
+        for j in range(lo // blk, -(-hi // blk)):
+            if int(table_h[b, j]) < 0:
+                table_h[b, j] = free.pop()
+            a, e = max(lo, j * blk), min(hi, (j + 1) * blk)
+            pg = int(table_h[b, j])
+            Kp[pg, :, a - j * blk:e - j * blk] = torch.from_numpy(K[b, :, a:e]).to(torch.bfloat16).cuda()
+            Vp[pg, :, a - j * blk:e - j * blk] = torch.from_numpy(V[b, :, a:e]).to(torch.bfloat16).cuda()
+
+    for b, L in enumerate(lens):
+        write_tokens(b, 0, L)
+    table = table_h.cuda()
+    bud = sas.Budget(k_fixed=k, sink=True, gate=True)
+    reps = torch.zeros((B, hkv, nbmax, d), dtype=torch.float32, device="cuda")
+    sas.block_reps_paged(Kp, table, lens, blk, hkv, Lmax, reps, hq=hq)
+    for step in range(steps):
+        old, lens = lens, [L + 1 for L in lens]
+        for b in range(B):
+            write_tokens(b, old[b], lens[b])
+        table.copy_(table_h)
+        sas.block_reps_paged(Kp, table, lens, blk, hkv, Lmax, reps, first_block=[L // blk for L in old], hq=hq)
+        _, idx, nsel, gate = sas.select_decode(Qd, reps, lens, blk, hkv, Lmax, bud)
+        O = sas.sparse_decode_paged(Qd, Kp, Vp, table, lens, blk, Lmax, idx, nsel, gate)
+        torch.cuda.synchronize()
+        reps_h, idx_h, nsel_h, O_h = reps.cpu().numpy(), idx.cpu().numpy(), nsel.cpu().numpy(), O.float().cpu().numpy()
+        err_sum, err_n = 0.0, 0
+        for b, L in enumerate(lens):
+            r = orc.run_sequence(Q[b][:, None, :], K[b], V[b], L, L - 1, blk, "group", k_fixed=k, sink=True,
+                                 gate=True)
+            nb = -(-L // blk)
+            dr = np.abs(reps_h[b, :, :nb] - r.reps).max()
+            assert dr <= 1e-5 * (1.0 + np.abs(r.reps).max()), f"step {step}, sequence {b}: reps differ by {dr:.3e}"
+            explicit = {}
+            for un in r.units:
+                u = b * hkv + un.sel_head
+                got = [int(x) for x in idx_h[u, :nsel_h[u]]]
+                ok, band, why = list_matches(un.sel, got, un.scores, un.c, un.k, True)
+                assert ok, f"step {step}, sequence {b}, KV head {un.sel_head}: {why}"
+                if band:
+                    explicit[(un.sel_head, un.c)] = (got, orc.gate_values(un.scores, got))
+            if explicit:
+                r = orc.run_sequence(Q[b][:, None, :], K[b], V[b], L, L - 1, blk, "group", k_fixed=k, sink=True,
+                                     gate=True, explicit=explicit)
+            diff = np.abs(O_h[b] - r.O[:, 0, :])
+            assert diff.max() <= BF16_MAX_ABS, f"step {step}, sequence {b}: max-abs {diff.max():.3e}"
+            err_sum += float(diff.sum())
+            err_n += diff.size
+        assert err_sum / err_n <= BF16_MEAN_ABS
+        say(f"[paged-loop] step {step}: lengths {lens}, pages in use {B * nbmax + 7 - len(free)}, "
+            f"reps, lists and outputs match the oracle")

@@ -30,9 +30,9 @@ def _torch():
 
 @dataclass
 class Budget:
-    """k = k_fixed, or ceil(frac_num * (c + count_current) / frac_den) when frac_den > 0; with
-    coverage > 0, the smallest k whose top candidates hold that share of the softmax mass (capped
-    by the rule when k_fixed or frac_den is set)."""
+    """k = ceil(sqrt_num * sqrt(c + count_current) / sqrt_den) when sqrt_den > 0, else k_fixed, or
+    ceil(frac_num * (c + count_current) / frac_den) when frac_den > 0; with coverage > 0, the smallest
+    k whose top candidates hold that share of the softmax mass (capped by the rule when one is set)."""
     k_fixed: int = 0
     frac_num: int = 0
     frac_den: int = 0
@@ -41,10 +41,13 @@ class Budget:
     gate: bool = False
     coverage: float = 0.0
     shared: bool = False
+    sqrt_num: int = 0
+    sqrt_den: int = 0
 
     def c_struct(self) -> _lib.Budget:
         return _lib.Budget(self.k_fixed, self.frac_num, self.frac_den, self.count_current,
-                           int(bool(self.sink)), int(bool(self.gate)), float(self.coverage), int(bool(self.shared)))
+                           int(bool(self.sink)), int(bool(self.gate)), float(self.coverage), int(bool(self.shared)),
+                           int(self.sqrt_num), int(self.sqrt_den))
 
 
 def sel_code(sel_mode) -> int:

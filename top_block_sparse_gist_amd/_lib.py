@@ -38,7 +38,8 @@ class Problem(C.Structure):
 class Budget(C.Structure):
     _fields_ = [("k_fixed", C.c_int32), ("frac_num", C.c_int32), ("frac_den", C.c_int32),
                 ("count_current", C.c_int32), ("force_sink", C.c_int32), ("gate", C.c_int32),
-                ("coverage", C.c_float), ("shared_heads", C.c_int32)]
+                ("coverage", C.c_float), ("shared_heads", C.c_int32), ("sqrt_num", C.c_int32),
+                ("sqrt_den", C.c_int32)]
 
 
 _P = C.POINTER(Problem)

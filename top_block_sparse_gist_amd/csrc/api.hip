@@ -93,6 +93,8 @@ sas_status check_budget(const sas_budget *bg) {
   if (!bg) return fail(SAS_ERR_NULL, "budget is NULL");
   if (bg->k_fixed < 0 || bg->frac_num < 0 || bg->frac_den < 0)
     return fail(SAS_ERR_SHAPE, "budget fields must be >= 0");
+  if (bg->sqrt_num < 0 || bg->sqrt_den < 0 || bg->sqrt_num > 65535 || bg->sqrt_den > 65535)
+    return fail(SAS_ERR_SHAPE, "sqrt_num and sqrt_den must be in [0, 65535]");
   if (bg->count_current != 0 && bg->count_current != 1)
     return fail(SAS_ERR_SHAPE, "count_current must be 0 or 1");
   if (!(bg->coverage >= 0.f && bg->coverage <= 1.f)) return fail(SAS_ERR_SHAPE, "coverage must be in [0, 1]");
@@ -106,7 +108,7 @@ float resolve_scale(float scale, int d) { return scale == 0.f ? 1.f / sqrtf((flo
 
 int32_t required_kcap(const sas_problem *p, int32_t tq, const int32_t *q_start, const sas_budget *bg) {
   Budget b{bg->k_fixed, bg->frac_num, bg->frac_den, bg->count_current, bg->force_sink ? 1 : 0, bg->gate,
-           bg->coverage, bg->shared_heads};
+           bg->coverage, bg->shared_heads, bg->sqrt_num, bg->sqrt_den};
   const int G = p->hq / p->hkv;
   int32_t need = 1;
   for (int s = 0; s < p->batch; ++s) {
@@ -240,8 +242,10 @@ sas_status sas_topk_select(const sas_problem *p, const float *scores, int64_t sc
   if (scores_ld < nbmax) return fail(SAS_ERR_SHAPE, "scores_ld %lld < %d blocks", (long long)scores_ld, nbmax);
   const int32_t need = required_kcap(p, tq, q_start, budget);
   if (kcap < need) return fail(SAS_ERR_SHAPE, "kcap %d < %d selected blocks", kcap, need);
-  Budget bg{budget->k_fixed, budget->frac_num, budget->frac_den, budget->count_current,
-            budget->force_sink ? 1 : 0, budget->gate ? 1 : 0, budget->coverage, budget->shared_heads ? 1 : 0};
+  Budget bg{budget->k_fixed,   budget->frac_num,         budget->frac_den,
+            budget->count_current, budget->force_sink ? 1 : 0, budget->gate ? 1 : 0,
+            budget->coverage,    budget->shared_heads ? 1 : 0, budget->sqrt_num,
+            budget->sqrt_den};
   return hip_status(launch_topk(*p, tab, scores, scores_ld, tq, sel_mode, bg, kcap, idx, nsel,
                                 budget->gate ? gate : nullptr, (hipStream_t)stream),
                     "sas_topk_select");
@@ -336,8 +340,10 @@ sas_status sas_select_decode(const sas_problem *p, const void *Q, const int64_t 
   if (!workspace || workspace_bytes < wneed)
     return fail(SAS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", wneed, workspace_bytes);
   if (!aligned16(workspace)) return fail(SAS_ERR_SHAPE, "workspace must be 16-byte aligned");
-  Budget bg{budget->k_fixed, budget->frac_num, budget->frac_den, budget->count_current,
-            budget->force_sink ? 1 : 0, budget->gate ? 1 : 0, budget->coverage, budget->shared_heads ? 1 : 0};
+  Budget bg{budget->k_fixed,   budget->frac_num,         budget->frac_den,
+            budget->count_current, budget->force_sink ? 1 : 0, budget->gate ? 1 : 0,
+            budget->coverage,    budget->shared_heads ? 1 : 0, budget->sqrt_num,
+            budget->sqrt_den};
   const int64_t qs3[3] = {q_stride[0], q_stride[1], 0};
   return hip_status(launch_select_decode(*p, tab, Q, qs3, reps, reps_kind, rep_stride, sel_mode,
                                          resolve_scale(scale, p->head_dim), scores, scores_ld, bg, kcap, idx, nsel,
@@ -632,6 +638,11 @@ sas_status sas_sparse_prefill_backward(const sas_problem *p, const void *Q, cons
   if (p->dtype != SAS_BF16) return fail(SAS_ERR_UNSUPPORTED, "the backward takes bf16 Q/K/V/O/dO");
   if (kcap < 1 || kcap > 32767) return fail(SAS_ERR_SHAPE, "kcap must be in [1, 32767]");
   if (scale < 0.f || !isfinite(scale)) return fail(SAS_ERR_SHAPE, "scale must be finite and >= 0");
+  // the dK/dV kernel splits a unit's flattened (head, row) index with a 20-bit reciprocal multiply,
+  // exact for indices below 128 rows x 64 heads
+  if (sel_mode == SAS_SEL_GROUP && p->hq / p->hkv > BWD_MAX_GROUP)
+    return fail(SAS_ERR_UNSUPPORTED, "the backward takes at most %d query heads per KV head with per-group units",
+                BWD_MAX_GROUP);
   const int eb = elem_bytes(p->dtype);
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) || !aligned16(dQ) ||
       !aligned16(dK) || !aligned16(dV) || !strides_ok(q_stride, 3, eb) || !strides_ok(kv_stride, 3, eb) ||

@@ -586,7 +586,8 @@ __global__ __launch_bounds__(BLK * 2, 2) void bwd_dkv_kernel(
       }
       mgl[k] = gl2;
       const UnitGeo x = unit_geo(st, u, S, QB, G, per_head, tq, BLK);
-      // rows <= 128 and flattened rows < 2^13: f / rows = (f * inv) >> 20 exactly
+      // rows <= 128 and flattened rows f < rows * 64 (the host rejects more than BWD_MAX_GROUP heads
+      // per unit): f / rows = (f * inv) >> 20 exactly, and f * inv < 2^27 fits 32 bits
       const int inv = ((1 << 20) + x.rows - 1) / max(x.rows, 1);
       ginfo[k] = i32x4{x.h0, x.t_lo, x.c, x.rows | (inv << 8)};
     }
@@ -764,7 +765,8 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(SeqTable st, int64_t unit
 // ---------------------------------------------------------------------------------------------
 // One workgroup per unit.  s_j = scale qbar . r_j with qbar the mean of the unit's F query vectors
 // and r_j the mean of block j's present keys: dqbar = scale sum_j dscore_j r_j goes to each query
-// vector as dqbar / F; dr_j += scale dscore_j qbar (atomic adds: the units that selected j meet).
+// vector as dqbar / F; scale qbar is kept per unit for the block means' gradient
+// dr_j = sum over the units keeping j of dscore_j scale qbar (bwd_chain_k_kernel).
 template <int D>
 __global__ __launch_bounds__(256) void bwd_chain_kernel(SeqTable st, const uint16_t *__restrict__ Q, int64_t qb,
                                                        int64_t qh, int64_t qt, int tq, int S, int QB, int G,
@@ -773,7 +775,7 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(SeqTable st, const uint1
                                                        const float *__restrict__ dscore, const float *__restrict__ reps,
                                                        int64_t rb, int64_t rh, int64_t rj, float scale,
                                                        float *__restrict__ dQ, int64_t dqb, int64_t dqh, int64_t dqt,
-                                                       float *__restrict__ dreps, int NBm, int blk) {
+                                                       float *__restrict__ qbs, int blk) {
   constexpr int RG = 256 / D;  // row groups: thread (rg, dim)
   __shared__ float part[RG][D];
   __shared__ float qbar[D], dqbar[D];
@@ -794,6 +796,7 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(SeqTable st, const uint1
 #pragma unroll
     for (int y = 0; y < RG; ++y) t += part[y][dim];
     qbar[dim] = t / (float)F;
+    qbs[u * D + dim] = scale * (t / (float)F);
   }
   __syncthreads();
   const int32_t *ul = idx + u * kcap;
@@ -812,25 +815,60 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(SeqTable st, const uint1
   __syncthreads();
   for (int f = rg; f < F; f += RG)
     dQ[ug.b * dqb + (int64_t)(ug.h0 + f / ug.rows) * dqh + (int64_t)(ug.t_lo + f % ug.rows) * dqt + dim] += dqbar[dim];
-  float *dr = dreps + ((int64_t)ug.b * hkv + ug.g) * NBm * D;
-  for (int e = rg; e < ns; e += RG) unsafeAtomicAdd(dr + (int64_t)ul[e] * D + dim, scale * ds[e] * qbar[dim]);
 }
 
-// dK[key] += dr_j / n_j for every present key of block j (n_j its present keys)
-__global__ __launch_bounds__(256) void bwd_chain_k_kernel(SeqTable st, int hkv, int blk, int NBm, int D, int64_t nkeys,
-                                                         const float *__restrict__ dreps, float *__restrict__ dK,
-                                                         int64_t gb, int64_t gh, int64_t gt, int64_t lmax) {
-  for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < nkeys * D; x += (int64_t)gridDim.x * 256) {
-    const int dim = (int)(x % D);
-    const int64_t r = x / D;
-    const int key = (int)(r % lmax);
-    const int64_t bg = r / lmax;
-    const int b = (int)(bg / hkv), g = (int)(bg % hkv);
-    const int L = st.len[b];
-    if (key >= L) continue;
-    const int j = key / blk;
-    const int nj = min(blk, L - j * blk);
-    dK[b * gb + (int64_t)g * gh + (int64_t)key * gt + dim] += dreps[(bg * NBm + j) * D + dim] / (float)nj;
+// dK[key] += dr_j / n_j for every present key of block j (n_j its present keys), with
+// dr_j = sum over the units keeping j of dscore_j (scale qbar).  One workgroup per (sequence, KV
+// head, block): the units come from the selection bitmap in ascending order, thread group rg takes
+// every RG-th of them, and the partial sums are added in a fixed order, so dK does not depend on the
+// order in which workgroups run.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_chain_k_kernel(SeqTable st, int hkv, int blk, int NBm, int W, int UG, int S,
+                                                         int QB, int G, int per_head, const uint32_t *__restrict__ bits,
+                                                         const int16_t *__restrict__ epos,
+                                                         const float *__restrict__ dscore, int kcap,
+                                                         const float *__restrict__ qbs, float *__restrict__ dK,
+                                                         int64_t gb, int64_t gh, int64_t gt) {
+  constexpr int RG = 256 / D;
+  __shared__ float part[RG][D];
+  const int64_t row = blockIdx.x;  // (sequence, KV head) pair * NBm + block
+  const int j = (int)(row % NBm);
+  const int pair = (int)(row / NBm);
+  const int b = pair / hkv, g = pair % hkv;
+  const int L = st.len[b];
+  if (j * blk >= L) return;
+  const int tid = threadIdx.x, dim = tid % D, rg = tid / D;
+  const uint32_t *brow = bits + row * W;
+  float a = 0.f;
+  int n = 0;
+  for (int w = 0; w < W; ++w) {
+    uint32_t word = brow[w];
+    while (word) {
+      const int bit = __ffs(word) - 1;
+      word &= word - 1;
+      if (n++ % RG != rg) continue;
+      const int ugi = w * 32 + bit;
+      const int i = per_head ? ugi / G : ugi;
+      const int s = per_head ? g * G + ugi % G : g;
+      const int64_t u = ((int64_t)b * S + s) * QB + i;
+      const int e = epos[row * UG + ugi];
+      a += dscore[u * kcap + e] * qbs[u * D + dim];
+    }
+  }
+  if (n == 0) return;  // no unit keeps this block (uniform across the workgroup)
+  part[rg][dim] = a;
+  __syncthreads();
+  if (rg == 0) {
+    float t = 0.f;
+#pragma unroll
+    for (int y = 0; y < RG; ++y) t += part[y][dim];
+    part[0][dim] = t;
+  }
+  __syncthreads();
+  const int nj = min(blk, L - j * blk);
+  for (int x = tid; x < nj * D; x += 256) {
+    const int key = j * blk + x / D, d2 = x % D;
+    dK[b * gb + (int64_t)g * gh + (int64_t)key * gt + d2] += part[0][d2] / (float)nj;
   }
 }
 
@@ -864,9 +902,12 @@ BwdPlan bwd_plan(const sas_problem &p, int32_t tq, int32_t sel_mode, int32_t kca
   x.off_gpart = off;
   if (gate) off += al((size_t)x.units * x.gslots * kcap * sizeof(float));
   x.off_bits = off;
-  // bits, then counts, then (with a gate) the block means' gradient [pairs, NBm, d] fp32
-  x.clear_words = (int64_t)x.npairs * x.NBm * (x.W + 1 + (gate ? p.head_dim : 0));
+  // bits, then counts
+  x.clear_words = (int64_t)x.npairs * x.NBm * (x.W + 1);
   off += al((size_t)x.clear_words * sizeof(uint32_t));
+  x.off_qbar = off;
+  // (with a gate) each unit's scaled mean query, for the selector path into dK
+  if (gate) off += al((size_t)x.units * p.head_dim * sizeof(float));
   x.off_epos = off;
   if (gate) off += al((size_t)x.npairs * x.NBm * x.UG * sizeof(int16_t));
   x.off_items = off;
@@ -942,14 +983,14 @@ static hipError_t bwd_dispatch(const sas_problem &p, const SeqTable &st, const B
   }
   if (gate && reps) {
     // on through the selector scores: into dQ (pooled query) and, via the block means, dK
-    float *dreps = (float *)(counts + (int64_t)pl.npairs * pl.NBm);
+    float *qbs = (float *)(ws + pl.off_qbar);
     hipLaunchKernelGGL((bwd_chain_kernel<D>), dim3((unsigned)pl.units), dim3(256), 0, s, st, q16, qs[0], qs[1], qs[2],
                        tq, S, pl.QB, G, per_head, p.hkv, idx, nsel, kcap, (const float *)dscore, reps, rs[0], rs[1],
-                       rs[2], scale, dQ, dqs[0], dqs[1], dqs[2], dreps, pl.NBm, p.block);
-    const int64_t nkeys = (int64_t)pl.npairs * p.max_len;
-    const unsigned g = (unsigned)std::min<int64_t>(8192, std::max<int64_t>(1, cdiv64(nkeys * D, 256)));
-    hipLaunchKernelGGL(bwd_chain_k_kernel, dim3(g), dim3(256), 0, s, st, p.hkv, p.block, pl.NBm, D, nkeys,
-                       (const float *)dreps, dK, dkvs[0], dkvs[1], dkvs[2], (int64_t)p.max_len);
+                       rs[2], scale, dQ, dqs[0], dqs[1], dqs[2], qbs, p.block);
+    hipLaunchKernelGGL((bwd_chain_k_kernel<D>), dim3((unsigned)((int64_t)pl.npairs * pl.NBm)), dim3(256), 0, s, st,
+                       p.hkv, p.block, pl.NBm, pl.W, pl.UG, S, pl.QB, G, per_head, (const uint32_t *)bits,
+                       (const int16_t *)epos, (const float *)dscore, kcap, (const float *)qbs, dK, dkvs[0], dkvs[1],
+                       dkvs[2]);
   }
   return hipGetLastError();
 }

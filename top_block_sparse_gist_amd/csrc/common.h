@@ -20,6 +20,7 @@ struct Budget {
   int32_t k_fixed, frac_num, frac_den, count_current, sink, gate;
   float coverage;  // 0: off (see coverage_count in the top-k bodies)
   int32_t shared;  // 1: the G heads of a KV group share G * k (per-head selection)
+  int32_t sqrt_num, sqrt_den;  // sqrt_den > 0: k = ceil(sqrt_num * sqrt(c + count_current) / sqrt_den)
 };
 
 // ---------------------------------------------------------------------------------------
@@ -33,11 +34,26 @@ __host__ __device__ inline int32_t num_qblocks(int32_t tq, int32_t blk) {
   return tq <= 1 ? 1 : cdiv(tq - 1, blk) + 1;
 }
 
+// ceil(sqrt(x)) for 0 <= x < 2^62, exact: a floating-point estimate corrected with integer compares.
+__host__ __device__ inline int64_t ceil_isqrt(int64_t x) {
+  if (x <= 0) return 0;
+  int64_t r = (int64_t)sqrt((double)x);
+  while (r > 0 && r * r > x) --r;
+  while ((r + 1) * (r + 1) <= x) ++r;  // r = floor(sqrt(x))
+  return r * r == x ? r : r + 1;
+}
+
 // Number of top-k blocks for a unit with current block c and n_cand candidates.
 __host__ __device__ inline int32_t budget_k(const Budget &bg, int32_t c, int32_t n_cand) {
   int32_t k;
-  if (bg.coverage > 0.f && bg.k_fixed <= 0 && bg.frac_den == 0) {
+  if (bg.coverage > 0.f && bg.k_fixed <= 0 && bg.frac_den == 0 && bg.sqrt_den == 0) {
     k = n_cand;  // an uncapped coverage budget may keep every candidate
+  } else if (bg.sqrt_den > 0) {
+    // square-root budget: the smallest k with k * sqrt_den >= sqrt_num * sqrt(n), n = c + count_current;
+    // k * sqrt_den is an integer, so that is ceil(ceil(sqrt(sqrt_num^2 n)) / sqrt_den)
+    const int64_t n = (int64_t)c + bg.count_current;
+    const int64_t r = ceil_isqrt((int64_t)bg.sqrt_num * bg.sqrt_num * n);
+    k = (int32_t)((r + bg.sqrt_den - 1) / bg.sqrt_den);
   } else if (bg.frac_den == 0) {
     k = bg.k_fixed;
   } else {
@@ -272,16 +288,17 @@ hipError_t launch_hssa_decode(const sas_problem &p, const SeqTable &st, const vo
 
 // Backward of the sparse prefill: sizes and workspace layout (host formula shared with the size
 // query).  Workspace regions, 256-byte aligned: row LSE and D [B, Hq, tq] fp32; gate partials
-// [units, gslots, kcap] fp32 (with a gate); selection bitmap [pairs, NBm, W] u32, per-block
-// counts [pairs, NBm] and (with a gate) the block means' gradient [pairs, NBm, d] fp32; entry positions [pairs, NBm, UG] int16 (with a gate); work items
-// [pairs, cap] x 16 bytes; item counts [pairs].
+// [units, gslots, kcap] fp32 (with a gate); selection bitmap [pairs, NBm, W] u32 and per-block
+// counts [pairs, NBm]; (with a gate) each unit's scaled mean query [units, d] fp32 and entry
+// positions [pairs, NBm, UG] int16; work items [pairs, cap] x 16 bytes; item counts [pairs].
 constexpr int BWD_SEGMAX = 256;       // units per dK/dV work item
+constexpr int BWD_MAX_GROUP = 64;     // query heads per KV head with per-group units (row mapping)
 constexpr int BWD_SEG_ROWS = 32768;   // flattened rows per dK/dV work item (a block's list is cut
                                       // into items of about this much work)
 struct BwdPlan {
   int QB, nh, gslots, NBm, UG, W, npairs, segm, cap;
   int64_t units, clear_words;
-  size_t off_lse, off_dd, off_gpart, off_bits, off_epos, off_items, off_icount, bytes;
+  size_t off_lse, off_dd, off_gpart, off_bits, off_qbar, off_epos, off_items, off_icount, bytes;
 };
 BwdPlan bwd_plan(const sas_problem &p, int32_t tq, int32_t sel_mode, int32_t kcap, bool gate);
 hipError_t launch_prefill_backward(const sas_problem &p, const SeqTable &st, const void *Q, const int64_t *qs,

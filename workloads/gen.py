@@ -33,6 +33,9 @@ from typing import Dict, List, Optional, Tuple
 
 import numpy as np
 
+# query coordinate 0 of the near-tie plant (exact in bf16)
+NEAR_TIE_Q0 = np.float32(2.0 ** -18)
+
 # stream ids (second component of the seed sequence's spawn key)
 _S_LENS, _S_Q, _S_K, _S_V, _S_NEEDLE, _S_OFFSET, _S_GK, _S_GV, _S_MK, _S_MV, _S_DO = range(11)
 
@@ -62,7 +65,9 @@ def _rng(seed: int, stream: int, index: int = 0) -> np.random.Generator:
 # ---------------------------------------------------------------------------------------------
 # The five workloads.  ``kind``: prefill | decode | gist_decode | mixed (prefill + decode halves).
 # Budget: k_u = min(#candidates, k_fixed) when frac_den == 0, else
-#         min(#candidates, ceil(frac_num * (c + count_current) / frac_den)).
+#         min(#candidates, ceil(frac_num * (c + count_current) / frac_den));
+#         optional keys sqrt_num / sqrt_den (sqrt_den > 0) select the square-root rule
+#         min(#candidates, ceil(sqrt_num * sqrt(c + count_current) / sqrt_den)).
 # ---------------------------------------------------------------------------------------------
 CONFIGS: Dict[int, dict] = {
     1: dict(name="tiny_causal_prefill_f32", kind="prefill", dtype="f32",
@@ -140,6 +145,8 @@ class Workload:
         self.frac_num: int = s["frac_num"]
         self.frac_den: int = s["frac_den"]
         self.count_current: int = s["count_current"]
+        self.sqrt_num: int = int(s.get("sqrt_num", 0))
+        self.sqrt_den: int = int(s.get("sqrt_den", 0))
         self.sink: bool = s["sink"]
         self.gate: bool = s["gate"]
         if self.kind == "mixed":
@@ -184,6 +191,8 @@ class Workload:
         """Queries of sequence b: [hq, rows_b, d] (rows at positions q_start[b] + t)."""
         r = _rng(self.seed, _S_Q, b)
         x = r.standard_normal((self.hq, self.rows[b], self.d), dtype=np.float32)
+        if self.spec.get("near_tie"):
+            x[:, :, 0] = NEAR_TIE_Q0
         return self._finish(x)
 
     def grad_out(self, b: int) -> np.ndarray:
@@ -238,7 +247,34 @@ class Workload:
             for j in needles:
                 lo, hi = int(j) * blk, min((int(j) + 1) * blk, L)
                 K[:, lo:hi, :] += dirs[:, None, :]
+        if self.spec.get("near_tie"):
+            return self._near_tie(K, b), self._finish(V)
         return self._finish(K), self._finish(V)
+
+    def near_tie_blocks(self, b: int) -> Tuple[int, int]:
+        """The planted pair (A, B), A < B, complete blocks before the first query row's block."""
+        pool = self.q_start[b] // self.block
+        assert pool >= 2, "a near tie needs two complete blocks before the query"
+        a, c = np.sort(_rng(self.seed, _S_NEEDLE, 10_000 + b).choice(pool, size=2, replace=False))
+        return int(a), int(c)
+
+    def _near_tie(self, K: np.ndarray, b: int) -> np.ndarray:
+        """Plant two needle blocks A < B whose selector scores differ by far less than 1e-5 relative
+        but are not equal: B is a copy of A (both get the needle offset 3 qhat) whose first key has
+        its coordinate 0 raised by one bf16 step, and every query has coordinate 0 = 2^-18.  B's
+        exact score then exceeds A's by about 1e-13 relative, below what fp32 sums resolve."""
+        assert self.is_bf16(), "the near tie is planted in bf16 inputs"
+        blk = self.block
+        A, B = self.near_tie_blocks(b)
+        dirs = (3.0 * self.needle_dirs(b)).astype(np.float32)
+        K[:, A * blk:(A + 1) * blk, :] += dirs[:, None, :]
+        K = self._finish(K)
+        K[:, B * blk:(B + 1) * blk, :] = K[:, A * blk:(A + 1) * blk, :]
+        v = np.ascontiguousarray(K[:, B * blk, 0], dtype=np.float32)
+        bits = v.view(np.uint32).copy()
+        up = np.where(v >= 0, bits + np.uint32(0x10000), bits - np.uint32(0x10000))   # next bf16 towards +inf
+        K[:, B * blk, 0] = up.view(np.float32)
+        return K
 
     def gist(self, b: int) -> Tuple[np.ndarray, np.ndarray]:
         """(gist_k, gist_v) of sequence b: each [hkv, NC, d], NC = number of complete chunks."""
@@ -271,7 +307,8 @@ class Workload:
     # ------------------------------------------------------------------ budget description
     def budget(self) -> dict:
         return dict(k_fixed=self.k_fixed, frac_num=self.frac_num, frac_den=self.frac_den,
-                    count_current=self.count_current, sink=self.sink, gate=self.gate)
+                    count_current=self.count_current, sqrt_num=self.sqrt_num, sqrt_den=self.sqrt_den,
+                    sink=self.sink, gate=self.gate)
 
     def describe(self) -> dict:
         return dict(name=self.name, kind=self.kind, dtype=self.dtype, batch=self.batch, hq=self.hq,
