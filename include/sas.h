@@ -243,6 +243,24 @@ sas_status sas_sparse_decode(const sas_problem *p, const void *Q, const int64_t 
                              const int64_t o_stride[2], void *workspace, size_t workspace_bytes,
                              void *stream);
 
+/* sas_sparse_decode for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): the same arguments without the workspace, the same
+ * kernels, outputs and errors.  The split-K scratch (arrival counters and partial records) lives in a static
+ * device array of the library, SAS_DECODE_NOALLOC_SCRATCH_BYTES per GPU, which each GPU the library runs on
+ * holds until the process ends; the call makes no allocation (its first call on a device looks up the
+ * array's device address).  Each call clears the array's arrival counters on `stream` with a small fill
+ * kernel before the attention kernel.  Every call on one GPU shares that GPU's array: calls that overlap in
+ * time on one GPU (two streams, two threads) race on it and must be serialised by the caller.
+ *   Errors: as sas_sparse_decode; SAS_ERR_WORKSPACE when sas_sparse_decode_workspace() for the call
+ *   exceeds SAS_DECODE_NOALLOC_SCRATCH_BYTES. */
+#define SAS_DECODE_NOALLOC_SCRATCH_BYTES (16u << 20)
+sas_status sas_sparse_decode_noalloc(const sas_problem *p, const void *Q, const int64_t q_stride[2],
+                                     const void *K, const void *V, const int64_t kv_stride[3],
+                                     const void *gist_k, const void *gist_v, const int64_t gist_stride[3],
+                                     int32_t sel_mode, const int32_t *idx, const int32_t *nsel,
+                                     const float *gate, int32_t kcap, float scale, void *O,
+                                     const int64_t o_stride[2], void *stream);
+
 /* Paged K/V ([BLOG] section 5: decode reads the KV cache; a serving cache is paged): the cache is
  * pages of one block each, [num_pages, Hkv, blk, d] (page_stride = {page, head, token}, or any
  * layout in which a page holds blk tokens of every KV head without overlapping the next), and

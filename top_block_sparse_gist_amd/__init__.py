@@ -348,6 +348,31 @@ def sparse_decode(Q, K, V, seq_lens, block, idx, nsel, gate=None, sel_mode="grou
     return O
 
 
+def sparse_decode_noalloc(Q, K, V, seq_lens, block, idx, nsel, gate=None, sel_mode="group", scale=0.0, gist_k=None,
+                          gist_v=None, O=None, stream=None):
+    """sparse_decode with the library's static scratch instead of a workspace
+    (sas_sparse_decode_noalloc): the call allocates no device memory itself (O is allocated here
+    when not given).  Calls that overlap in time on one GPU must not use it."""
+    torch = _torch()
+    B, hq, d = Q.shape
+    _, hkv, lmax, _ = K.shape
+    if K.stride() != V.stride():
+        raise ValueError("K and V must share strides")
+    gist = gist_k is not None
+    if gist and gist_k.stride() != gist_v.stride():
+        raise ValueError("gist K and V must share strides")
+    if O is None:
+        O = torch.empty_like(Q)
+    p = _Prob(B, hq, hkv, d, block, _dtype_code(Q), lmax, seq_lens)
+    check(load().sas_sparse_decode_noalloc(p.ref, _ptr(Q), _strides(Q, 2), _ptr(K), _ptr(V), _strides(K, 3),
+                                           _ptr(gist_k) if gist else None, _ptr(gist_v) if gist else None,
+                                           _strides(gist_k, 3) if gist else None, sel_code(sel_mode), _ptr(idx),
+                                           _ptr(nsel), _ptr(gate), idx.shape[1], float(scale), _ptr(O), _strides(O, 2),
+                                           _stream(stream)),
+          "sas_sparse_decode_noalloc")
+    return O
+
+
 def hssa_select_decode(Q, gist_k, meta_k, seq_lens, block, hkv, max_len, group_chunks, k1, k2, sel_mode="group",
                        scale=0.0, kcap=None, gcap=None, idx=None, nsel=None, gidx=None, gsel=None, workspace=None,
                        stream=None):

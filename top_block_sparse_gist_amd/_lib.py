@@ -16,6 +16,7 @@ SAS_F32, SAS_BF16 = 0, 1
 SAS_SEL_GROUP, SAS_SEL_HEAD = 0, 1
 SAS_REPS_POOLED, SAS_REPS_GIST = 0, 1
 SAS_MAX_BATCH = 64
+SAS_DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 STATUS_NAMES = {0: "SAS_OK", -1: "SAS_ERR_NULL", -2: "SAS_ERR_SHAPE", -3: "SAS_ERR_UNSUPPORTED",
                 -4: "SAS_ERR_WORKSPACE", -5: "SAS_ERR_HIP"}
@@ -26,7 +27,7 @@ EXPORTED = ("sas_num_qblocks", "sas_required_kcap", "sas_block_reps", "sas_block
             "sas_sparse_prefill", "sas_sparse_decode_workspace", "sas_sparse_decode", "sas_hssa_select_workspace",
             "sas_hssa_select_decode", "sas_hssa_decode_workspace", "sas_hssa_decode", "sas_block_reps_paged",
             "sas_sparse_decode_paged", "sas_sparse_prefill_paged", "sas_sparse_prefill_backward_workspace",
-            "sas_sparse_prefill_backward", "sas_sparse_prefill_lse", "sas_last_error")
+            "sas_sparse_prefill_backward", "sas_sparse_prefill_lse", "sas_sparse_decode_noalloc", "sas_last_error")
 
 
 class Problem(C.Structure):
@@ -66,6 +67,8 @@ _SIGS = {
     "sas_sparse_decode_workspace": (C.c_size_t, [_P, C.c_int32, C.c_int32, C.c_int32]),
     "sas_sparse_decode": (C.c_int, [_P, _VP, _I64_3, _VP, _VP, _I64_3, _VP, _VP, _I64_3, C.c_int32, _VP, _VP, _VP,
                                     C.c_int32, C.c_float, _VP, _I64_3, _VP, C.c_size_t, _VP]),
+    "sas_sparse_decode_noalloc": (C.c_int, [_P, _VP, _I64_3, _VP, _VP, _I64_3, _VP, _VP, _I64_3, C.c_int32, _VP,
+                                            _VP, _VP, C.c_int32, C.c_float, _VP, _I64_3, _VP]),
     "sas_hssa_select_workspace": (C.c_size_t, [_P, C.c_int32, C.c_int32, C.c_int32]),
     "sas_hssa_select_decode": (C.c_int, [_P, _VP, _I64_3, _VP, _I64_3, _VP, _I64_3, C.c_int32, C.c_int32, C.c_int32,
                                          C.c_int32, C.c_float, C.c_int32, C.c_int32, _VP, _VP, _VP, _VP, _VP,

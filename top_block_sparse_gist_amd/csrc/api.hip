@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 
@@ -356,11 +357,49 @@ size_t sas_sparse_decode_workspace(const sas_problem *p, int32_t sel_mode, int32
   return decode_workspace_bytes(*p, sel_mode, kcap, gist);
 }
 
-sas_status sas_sparse_decode(const sas_problem *p, const void *Q, const int64_t q_stride[2], const void *K,
-                             const void *V, const int64_t kv_stride[3], const void *gist_k, const void *gist_v,
-                             const int64_t gist_stride[3], int32_t sel_mode, const int32_t *idx,
-                             const int32_t *nsel, const float *gate, int32_t kcap, float scale, void *O,
-                             const int64_t o_stride[2], void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Scratch of sas_sparse_decode_noalloc: one array per GPU (each device that loads the library holds its
+// own copy until the process ends).  Host code must not pass `scratch` itself to a kernel: its host-side
+// name is not a device address.  The device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[SAS_DECODE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES] = {};
+
+// device address of the current device's scratch array (looked up on the first call on that device)
+sas_status scratch_address(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "sas_sparse_decode_noalloc (hipGetDevice)");
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(SAS_ERR_UNSUPPORTED, "device %d beyond %d devices", dev, MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "sas_sparse_decode_noalloc (hipGetSymbolAddress)");
+    if (!ptr) return fail(SAS_ERR_HIP, "sas_sparse_decode_noalloc: no device address for the scratch array");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SAS_OK;
+}
+
+// zeroes n 32-bit words (a fill kernel rather than a memset, so the call may sit in a captured graph)
+__global__ void clear_words_kernel(uint32_t *p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// sas_sparse_decode's body.  noalloc: the scratch is the static array above instead of `workspace`.
+sas_status sparse_decode_impl(const sas_problem *p, const void *Q, const int64_t q_stride[2], const void *K,
+                              const void *V, const int64_t kv_stride[3], const void *gist_k, const void *gist_v,
+                              const int64_t gist_stride[3], int32_t sel_mode, const int32_t *idx, const int32_t *nsel,
+                              const float *gate, int32_t kcap, float scale, void *O, const int64_t o_stride[2],
+                              void *workspace, size_t workspace_bytes, bool noalloc, void *stream) {
   SeqTable tab{};
   sas_status st;
   if ((st = check_problem(p, &tab)) != SAS_OK) return st;
@@ -393,12 +432,49 @@ sas_status sas_sparse_decode(const sas_problem *p, const void *Q, const int64_t 
     return fail(SAS_ERR_UNSUPPORTED, "kcap %d needs %d split-K records per unit; the merge holds %d", kcap, nwg,
                 cap);
   const size_t need = decode_workspace_bytes(*p, sel_mode, kcap, gist ? 1 : 0);
-  if (!workspace || workspace_bytes < need)
-    return fail(SAS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
-  if (!aligned16(workspace)) return fail(SAS_ERR_SHAPE, "workspace must be 16-byte aligned");
+  if (noalloc) {
+    if (need > (size_t)SAS_DECODE_NOALLOC_SCRATCH_BYTES)
+      return fail(SAS_ERR_WORKSPACE, "this call needs %zu bytes of scratch; the library's static array holds %zu",
+                  need, (size_t)SAS_DECODE_NOALLOC_SCRATCH_BYTES);
+    void *ptr = nullptr;
+    if ((st = scratch_address(&ptr)) != SAS_OK) return st;
+    // the array keeps the last call's contents: clear the arrival counters, which must start at zero
+    const int64_t words = (int64_t)(decode_counter_bytes(*p, sel_mode) / 4);
+    hipLaunchKernelGGL(clear_words_kernel, dim3((unsigned)cdiv64(words, 256)), dim3(256), 0, s, (uint32_t *)ptr,
+                       words);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_status(e, "sas_sparse_decode_noalloc (clear)");
+    workspace = ptr;
+  } else {
+    if (!workspace || workspace_bytes < need)
+      return fail(SAS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+    if (!aligned16(workspace)) return fail(SAS_ERR_SHAPE, "workspace must be 16-byte aligned");
+  }
   return hip_status(launch_decode_bf16(*p, tab, Q, q_stride, K, V, kv_stride, gist_k, gist_v, gist_stride, sel_mode,
                                        idx, nsel, gate, kcap, sc, O, o_stride, (float *)workspace, s),
-                    "sas_sparse_decode");
+                    noalloc ? "sas_sparse_decode_noalloc" : "sas_sparse_decode");
+}
+
+}  // namespace
+
+extern "C" {
+
+sas_status sas_sparse_decode(const sas_problem *p, const void *Q, const int64_t q_stride[2], const void *K,
+                             const void *V, const int64_t kv_stride[3], const void *gist_k, const void *gist_v,
+                             const int64_t gist_stride[3], int32_t sel_mode, const int32_t *idx,
+                             const int32_t *nsel, const float *gate, int32_t kcap, float scale, void *O,
+                             const int64_t o_stride[2], void *workspace, size_t workspace_bytes, void *stream) {
+  return sparse_decode_impl(p, Q, q_stride, K, V, kv_stride, gist_k, gist_v, gist_stride, sel_mode, idx, nsel, gate,
+                            kcap, scale, O, o_stride, workspace, workspace_bytes, false, stream);
+}
+
+sas_status sas_sparse_decode_noalloc(const sas_problem *p, const void *Q, const int64_t q_stride[2], const void *K,
+                                     const void *V, const int64_t kv_stride[3], const void *gist_k,
+                                     const void *gist_v, const int64_t gist_stride[3], int32_t sel_mode,
+                                     const int32_t *idx, const int32_t *nsel, const float *gate, int32_t kcap,
+                                     float scale, void *O, const int64_t o_stride[2], void *stream) {
+  return sparse_decode_impl(p, Q, q_stride, K, V, kv_stride, gist_k, gist_v, gist_stride, sel_mode, idx, nsel, gate,
+                            kcap, scale, O, o_stride, nullptr, 0, true, stream);
 }
 
 // ---- paged K/V (one block per page, a block table per sequence) ------------------------------

@@ -264,6 +264,8 @@ constexpr int32_t SELECT_DECODE_MAX_C = 2048;
 
 // Bytes of split-K partials the decode path needs (host formula shared with the size query).
 size_t decode_workspace_bytes(const sas_problem &p, int32_t sel_mode, int32_t kcap, int32_t gist);
+// leading bytes of that workspace that hold the per-unit arrival counters (256-byte aligned)
+size_t decode_counter_bytes(const sas_problem &p, int32_t sel_mode);
 // whether the split-K merge of the bf16 decode fits its LDS for this list capacity (nwg records
 // per unit against cap)
 bool decode_merge_fits(const sas_problem &p, const SeqTable &st, int32_t sel_mode, int32_t kcap, int32_t gist,

@@ -56,6 +56,11 @@ bool decode_merge_fits(const sas_problem &p, const SeqTable &st, int32_t sel_mod
   return *nwg_out <= *cap_out;
 }
 
+size_t decode_counter_bytes(const sas_problem &p, int32_t sel_mode) {
+  const DecodeShape d = decode_shape(p, sel_mode, 1, 0, 0);
+  return ((size_t)d.units * 4 + 255) / 256 * 256;
+}
+
 size_t decode_workspace_bytes(const sas_problem &p, int32_t sel_mode, int32_t kcap, int32_t gist) {
   const int maxc = (p.max_len - 1) / p.block;
   DecodeShape d = decode_shape(p, sel_mode, kcap, gist, maxc);
