@@ -29,13 +29,38 @@ __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
   return op(op(r0, r1), op(r2, r3));
 }
 
-// Number of keys >= t over the wave: per-lane counts in four independent chains, one reduction.
+// Number of keys >= t over the wave: one compare per register into its own scalar mask, counted with
+// the scalar unit's popcount (independent compares, no cross-lane reduction).
 template <int NPL>
 __device__ __forceinline__ uint32_t count_ge(const uint32_t (&key)[NPL], uint32_t t) {
-  uint32_t a[4] = {0u, 0u, 0u, 0u};
+  uint32_t n = 0u;
 #pragma unroll
-  for (int r = 0; r < NPL; ++r) a[r & 3] += key[r] >= t ? 1u : 0u;
-  return wave_reduce_u32((a[0] + a[1]) + (a[2] + a[3]), [](uint32_t x, uint32_t y) { return x + y; });
+  for (int r = 0; r < NPL; ++r) n += (uint32_t)__popcll(__ballot(key[r] >= t));
+  return n;
+}
+
+// Wave-wide max / sum of a float to a uniform value: DPP within each 16-lane row, then the four row
+// results through scalar registers (the same shape as wave_reduce_u32).
+template <typename Op>
+__device__ __forceinline__ float wave_reduce_f32(float v, Op op) {
+  auto dpp = [](float x, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value, 0xF, 0xF, false));
+  };
+  v = op(v, dpp(v, std::integral_constant<int, 0xB1>{}));   // lane ^ 1
+  v = op(v, dpp(v, std::integral_constant<int, 0x4E>{}));   // lane ^ 2
+  v = op(v, dpp(v, std::integral_constant<int, 0x124>{}));  // row_ror:4
+  v = op(v, dpp(v, std::integral_constant<int, 0x128>{}));  // row_ror:8
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return op(op(r0, r1), op(r2, r3));
+}
+__device__ __forceinline__ float wave_fmax_dpp(float v) {
+  return wave_reduce_f32(v, [](float x, float y) { return fmaxf(x, y); });
+}
+__device__ __forceinline__ float wave_fsum_dpp(float v) {
+  return wave_reduce_f32(v, [](float x, float y) { return x + y; });
 }
 
 // A team of waves that selects for one unit; each wave holds its own contiguous share of the
@@ -168,15 +193,26 @@ __device__ void team_topk(const float *__restrict__ row, int c, bool sinkf, cons
   // order-preserving keys of the candidates, 0 elsewhere: a candidate's key is never 0 (that is
   // the key of one NaN pattern only, and NaN scores are not ranked)
   uint32_t key[NPL];
+  float s_c = 0.f, s_0 = 0.f;
+  if (act) {
+    // device-coherent loads through a buffer resource (not atomics, which the compiler issues one at
+    // a time, each waiting for the previous): every lane loads (entries up to c exist), all loads are
+    // issued before the first key is formed
+    const __amdgpu_buffer_rsrc_t rr = dev_rsrc(row, (uint32_t)(c + 1) * 4u);
+    float sv[NPL];
 #pragma unroll
-  for (int r = 0; r < NPL; ++r) {
-    // every lane loads (entries up to c exist), so the loads issue back to back
-    const int j = jw + lane + 64 * r;
-    const float s = act ? load_dev(row + min(j, c)) : 0.f;
-    key[r] = (act && j >= lo && j < c) ? max(float_order_key(s), 1u) : 0u;
+    for (int r = 0; r < NPL; ++r) sv[r] = load4_dev(rr, (uint32_t)min(jw + lane + 64 * r, c) * 4u);
+    s_c = load4_dev(rr, (uint32_t)c * 4u);
+    s_0 = load4_dev(rr, 0u);
+#pragma unroll
+    for (int r = 0; r < NPL; ++r) {
+      const int j = jw + lane + 64 * r;
+      key[r] = (j >= lo && j < c) ? max(float_order_key(sv[r]), 1u) : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < NPL; ++r) key[r] = 0u;
   }
-  const float s_c = act ? load_dev(row + c) : 0.f;
-  const float s_0 = act ? load_dev(row) : 0.f;
   auto count = [&](uint32_t t) { return team.sum(count_ge(key, t)); };
   if constexpr (COV) {  // compiled only into the launches that carry a coverage budget
     if (bg.coverage > 0.f && k > 0) k = min(k, (int)coverage_count(key, bg.coverage, team));
@@ -238,8 +274,9 @@ __device__ void team_topk(const float *__restrict__ row, int c, bool sinkf, cons
         if (bisect) {
           step = span >> 1;
         } else {
-          // f in [0, 1); the float product is clamped below 2^32 before the conversion
-          const float f = __fdividef((float)(cl - (uint32_t)k), (float)(cl - ch));
+          // f in [0, 1): where the line between (lo, cl) and (hi, ch) reaches k; the float product is
+          // clamped below 2^32 before the conversion
+          const float f = (float)(cl - (uint32_t)k) * __builtin_amdgcn_rcpf((float)(cl - ch));
           step = (uint32_t)fminf((float)span * f, 4294967040.f);
           step = max(min(step, span - 1u), 1u);
         }
@@ -295,7 +332,7 @@ __device__ void team_topk(const float *__restrict__ row, int c, bool sinkf, cons
     for (int r = 0; r < NPL; ++r) mx = fmaxf(mx, ((selbits >> r) & 1u) ? order_key_float(key[r]) : -INFINITY);
     mx = fmaxf(mx, s_c);
     if (sink) mx = fmaxf(mx, s_0);
-    mx = JOINT ? wave_max(mx) : team.fmax(wave_max(mx));  // shared: each head's own set
+    mx = JOINT ? wave_fmax_dpp(mx) : team.fmax(wave_fmax_dpp(mx));  // shared: each head's own set
     // exp(x - mx) as 2^((x - mx) log2 e): one v_exp_f32 each; terms that flush to 0 are below the
     // largest (1) by more than the float's precision
     constexpr float L2E = 1.4426950408889634f;
@@ -305,7 +342,7 @@ __device__ void team_topk(const float *__restrict__ row, int c, bool sinkf, cons
       const float e = __builtin_amdgcn_exp2f((order_key_float(key[r]) - mx) * L2E);
       sm += ((selbits >> r) & 1u) ? e : 0.f;
     }
-    sm = JOINT ? wave_sum(sm) : team.fsum(wave_sum(sm));
+    sm = JOINT ? wave_fsum_dpp(sm) : team.fsum(wave_fsum_dpp(sm));
     sm += __builtin_amdgcn_exp2f((s_c - mx) * L2E);
     if (sink) sm += __builtin_amdgcn_exp2f((s_0 - mx) * L2E);
     lse = mx + logf(sm);
