@@ -168,12 +168,24 @@ def decode_step_setup(sas, w, inp, gist=False):
         sas.sparse_decode(inp.Q, inp.K, inp.V, lens, w.block, idx, nsel, gate, sel_mode=w.sel, gist_k=gk,
                           gist_v=gv, O=O, workspace=ws)
 
-    def step():
+    def select():
         sas.select_decode(inp.Q, reps, lens, w.block, w.hkv, Lmax, budget, sel_mode=w.sel, gist=gist,
                           kcap=idx.shape[1], scores=scores, idx=idx, nsel=nsel, gate=gate, workspace=sel_ws)
+
+    idx2, nsel2 = torch.empty_like(idx), torch.empty_like(nsel)
+    gate2 = torch.empty_like(gate) if gate is not None else None
+
+    def select_two_calls():
+        # the same selection as two launches: block scores, then the top-k
+        sas.block_scores(inp.Q, reps, lens, w.block, w.hkv, Lmax, sel_mode=w.sel, gist=gist, scores=scores)
+        sas.topk_select(scores, lens, w.block, w.hq, w.hkv, w.d, dt, Lmax, budget, sel_mode=w.sel,
+                        kcap=idx.shape[1], idx=idx2, nsel=nsel2, gate=gate2)
+
+    def step():
+        select()
         attend()
 
-    fns = dict(step=step, attend=attend)
+    fns = dict(step=step, attend=attend, select=select, select_two_calls=select_two_calls)
     return fns, dict(reps=reps, scores=scores, idx=idx, nsel=nsel, gate=gate, O=O)
 
 
@@ -535,6 +547,8 @@ def main():
         t_pf_att, _ = timer.time(pf_fns["attend"], k_small, 2)
         t_pf_sel, _ = timer.time(pf_fns["select"], k_small, 2)
         t_dc_att, _ = timer.time(dc_fns["attend"], K_, W_)
+        t_dc_sel, _ = timer.time(dc_fns["select"], K_, W_)
+        t_dc_sel2, _ = timer.time(dc_fns["select_two_calls"], K_, W_)
         t_dc_graph, _ = timer.time(dc_fns["step"], K_, W_, use_graph=True)
         value = by["total"] / (t_dc * 1e-3) / 1e9
         tf_half = fl["flops"] / (t_pf * 1e-3) / 1e12
@@ -557,6 +571,8 @@ def main():
                        "decode_half_ms": round(t_dc, 5), "decode_bytes_per_step": by["total"],
                        "decode_pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
                        "decode_graph_replay_ms": round(t_dc_graph, 5),
+                       "decode_selection_ms": round(t_dc_sel, 5),
+                       "decode_selection_two_calls_ms": round(t_dc_sel2, 5),
                        "prefill_half_ms": round(t_pf, 5), "prefill_half_TFLOP/s": round(tf_half, 1),
                        "prefill_half_pct_mfma_peak": round(100 * tf_half / BF16_PEAK_TFLOPS, 2),
                        "prefill_selection_ms": round(t_pf_sel, 5),
@@ -590,7 +606,8 @@ def main():
                                        f"{cpu['t_pf']:.1f} s on the same pool, extrapolated to the "
                                        f"{cpu['pf_units']} units of the prefill half")}}
         log(f"[bench] mixed: decode half {t_dc * 1e3:.1f} us -> {value:.0f} GB/s ({100 * value / HBM_PEAK_GBS:.1f} %); "
-            f"attention {t_dc_att * 1e3:.1f} us -> {ach:.0f} GB/s; graph {t_dc_graph * 1e3:.1f} us")
+            f"attention {t_dc_att * 1e3:.1f} us -> {ach:.0f} GB/s; graph {t_dc_graph * 1e3:.1f} us; selection {t_dc_sel * 1e3:.1f} us "
+            f"(two calls {t_dc_sel2 * 1e3:.1f} us)")
         log(f"[bench] mixed: prefill half {t_pf:.3f} ms -> {tf_half:.0f} TFLOP/s; attention {t_pf_att:.3f} ms -> "
             f"{tf_att:.0f} TFLOP/s ({100 * tf_att / BF16_PEAK_TFLOPS:.1f} %); selection {t_pf_sel:.3f} ms")
         if "backward" in only:

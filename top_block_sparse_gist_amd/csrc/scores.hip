@@ -111,7 +111,13 @@ __global__ __launch_bounds__(256) void score_gemm_kernel(SeqTable st, const floa
   if (j0 > cmax) return;
   const int nrep = gist ? L / blk : cdiv(L, blk);
   const int tid = threadIdx.x;
-  const int tm = tid / 16, tn = tid % 16;
+  // wave w owns the 32 x 32 output block (units mw.., blocks nw..) of the 64 x 64 tile, formed with
+  // v_mfma_f32_32x32x2_f32: lane l supplies A[unit mw + l % 32][dim k + l / 32] and
+  // B[dim k + l / 32][block nw + l % 32]; register r of its result is unit mw + 8 (r / 4) + 4 (l / 32)
+  // + r % 4, block nw + l % 32.  A wave whose units all lie past M skips the products.
+  const int wave = tid >> 6, lane = tid & 63;
+  const int mw = 32 * (wave >> 1), nw = 32 * (wave & 1);
+  const bool wave_live = m0 + mw < M;
 
   auto unit_row = [&](int m) -> int64_t {
     int sl = m / nqb, i = m % nqb;
@@ -119,77 +125,91 @@ __global__ __launch_bounds__(256) void score_gemm_kernel(SeqTable st, const floa
     return ((int64_t)b * S + s) * QB + i;
   };
 
-  float acc[4][4];
+  f32x16 acc;
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
-#pragma unroll
-    for (int y = 0; y < 4; ++y) acc[x][y] = 0.f;
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 
-  for (int k0 = 0; k0 < D; k0 += KC) {
-    // A tile: 64 units x 32 dims (2 float4 per lane)
+  // the next d chunk's global loads are issued into registers before this chunk's products, so
+  // they fly during them (each product still sums its d terms in order 0..D-1)
+  const R *rbase = reps + b * rb + g * rh;
+  auto load_a = [&](int k0, f32x4 (&ra)[2]) {
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
-      int e = tid + w * 256;  // 0..511
-      int mm = e / 8, kq = (e % 8) * 4;
-      int m = m0 + mm;
-      f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (m < M) v = *reinterpret_cast<const f32x4 *>(qbar + unit_row(m) * D + k0 + kq);
-      As[kq + 0][mm] = v[0];
-      As[kq + 1][mm] = v[1];
-      As[kq + 2][mm] = v[2];
-      As[kq + 3][mm] = v[3];
+      const int e = tid + w * 256;  // 64 units x 8 float4
+      const int m = m0 + e / 8, kq = (e % 8) * 4;
+      ra[w] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (m < M) ra[w] = *reinterpret_cast<const f32x4 *>(qbar + unit_row(m) * D + k0 + kq);
     }
-    // B tile: 64 reps x 32 dims
-    const R *rbase = reps + b * rb + g * rh;
+  };
+  auto load_b = [&](int k0, u32x4 (&rv)[2]) {
     if constexpr (sizeof(R) == 4) {
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
-        int e = tid + w * 256;
-        int jj = e / 8, kq = (e % 8) * 4;
-        int j = j0 + jj;
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (j < nrep) v = *reinterpret_cast<const f32x4 *>(rbase + (int64_t)j * rj + k0 + kq);
-        Bs[kq + 0][jj] = v[0];
-        Bs[kq + 1][jj] = v[1];
-        Bs[kq + 2][jj] = v[2];
-        Bs[kq + 3][jj] = v[3];
+        const int e = tid + w * 256;  // 64 reps x 8 float4
+        const int j = j0 + e / 8, kq = (e % 8) * 4;
+        rv[w] = u32x4{0u, 0u, 0u, 0u};
+        if (j < nrep) rv[w] = *reinterpret_cast<const u32x4 *>(rbase + (int64_t)j * rj + k0 + kq);
       }
     } else {
-      int jj = tid / 4, kq = (tid % 4) * 8;
-      int j = j0 + jj;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (j < nrep) v = *reinterpret_cast<const u32x4 *>(rbase + (int64_t)j * rj + k0 + kq);
+      const int j = j0 + tid / 4, kq = (tid % 4) * 8;  // 64 reps x 4 chunks of 8 bf16
+      rv[0] = u32x4{0u, 0u, 0u, 0u};
+      if (j < nrep) rv[0] = *reinterpret_cast<const u32x4 *>(rbase + (int64_t)j * rj + k0 + kq);
+    }
+  };
+  f32x4 ra[2];
+  u32x4 rv[2];
+  load_a(0, ra);
+  load_b(0, rv);
+  for (int k0 = 0; k0 < D; k0 += KC) {
+    // A tile: 64 units x 32 dims; B tile: 64 reps x 32 dims (transposed into LDS)
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const int e = tid + w * 256;
+      const int mm = e / 8, kq = (e % 8) * 4;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) As[kq + x][mm] = ra[w][x];
+    }
+    if constexpr (sizeof(R) == 4) {
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const int e = tid + w * 256;
+        const int jj = e / 8, kq = (e % 8) * 4;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) Bs[kq + x][jj] = __uint_as_float(rv[w][x]);
+      }
+    } else {
+      const int jj = tid / 4, kq = (tid % 4) * 8;
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        Bs[kq + 2 * x][jj] = bf16_lo(v[x]);
-        Bs[kq + 2 * x + 1][jj] = bf16_hi(v[x]);
+        Bs[kq + 2 * x][jj] = bf16_lo(rv[0][x]);
+        Bs[kq + 2 * x + 1][jj] = bf16_hi(rv[0][x]);
       }
     }
     __syncthreads();
-#pragma unroll 8
-    for (int k = 0; k < KC; ++k) {
-      f32x4 a = *reinterpret_cast<const f32x4 *>(&As[k][tm * 4]);
-      f32x4 bb = *reinterpret_cast<const f32x4 *>(&Bs[k][tn * 4]);
+    if (k0 + KC < D) {
+      load_a(k0 + KC, ra);
+      load_b(k0 + KC, rv);
+    }
+    if (wave_live) {
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(a[x], bb[y], acc[x][y]);
+      for (int k = 0; k < KC; k += 2) {
+        const float a = As[k + (lane >> 5)][mw + (lane & 31)];
+        const float bb = Bs[k + (lane >> 5)][nw + (lane & 31)];
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bb, acc, 0, 0, 0);
+      }
     }
     __syncthreads();
   }
+  if (!wave_live) return;
+  const int j = j0 + nw + (lane & 31);
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    int m = m0 + tm * 4 + x;
+  for (int r = 0; r < 16; ++r) {
+    const int m = m0 + mw + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
     if (m >= M) continue;
-    int c = c0 + m % nqb;
-    float *row = scores + unit_row(m) * ld;
+    const int c = c0 + m % nqb;
     // gist keys exist for the complete chunks before the current one only
     const int have = gist ? min(nrep, c) : nrep;
-#pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      int j = j0 + tn * 4 + y;
-      if (j <= c) row[j] = (j < have) ? acc[x][y] * scale : -INFINITY;
-    }
+    if (j <= c) scores[unit_row(m) * ld + j] = (j < have) ? acc[r] * scale : -INFINITY;
   }
 }
 

@@ -11,6 +11,7 @@
 // compacted in ascending order with ballot/popcount block scans, so the list comes out
 // sorted without a sort.  The gate is s_j - logsumexp over the selected set (fp32).
 #include "common.h"
+#include "decode_parts.h"
 
 namespace sas {
 
@@ -367,10 +368,70 @@ __global__ __launch_bounds__(256) void topk_joint_kernel(SeqTable st, const floa
   }
 }
 
+// One wave per unit, four units per workgroup (no barriers: waves finish independently): the
+// unit's scores are read into registers, NPL per lane, and the register-resident top-k of the
+// fused decode selection (team_topk on one wave: interpolation search over order-preserving keys
+// with ballot counts, ballot compaction, the gate) selects.  Plain budgets with current blocks below
+// 64 NPL (a unit with fewer candidates runs a shorter register loop); many waves per SIMD overlap the
+// search's dependent steps.  Same lists and gates as topk_kernel.
+template <int NPL>
+__global__ __launch_bounds__(256) void topk_wave_kernel(SeqTable st, const float *__restrict__ scores, int64_t ld,
+                                                        int tq, int blk, int S, int QB, Budget bg, int kcap,
+                                                        int32_t *__restrict__ idx, int32_t *__restrict__ nsel,
+                                                        float *__restrict__ gate, int64_t units) {
+  const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (u >= units) return;
+  const int lane = threadIdx.x & 63;
+  const int i = (int)(u % QB);
+  const int b = (int)(u / QB) / S;
+  const int q0 = st.q0[b];
+  const int c0 = q0 / blk;
+  const int nqb = (q0 + tq - 1) / blk - c0 + 1;
+  int32_t *out = idx + u * kcap;
+  float *gout = bg.gate ? gate + u * kcap : nullptr;
+  if (i >= nqb) {
+    for (int p = lane; p < kcap; p += 64) {
+      out[p] = -1;
+      if (gout) gout[p] = 0.f;
+    }
+    if (lane == 0) nsel[u] = 0;
+    return;
+  }
+  // the unit's own register count: rows over fewer candidates take a shorter loop
+  const int c = c0 + i;
+  const float *row = scores + u * ld;
+  if (NPL > 8 && c < 64 * 8) {
+    team_topk<(NPL > 8 ? 8 : NPL), SoloTeam, TK_PLAIN>(row, c, bg.sink != 0, bg, kcap, out, nsel + u, gout, SoloTeam{});
+  } else if (NPL > 16 && c < 64 * 16) {
+    team_topk<(NPL > 16 ? 16 : NPL), SoloTeam, TK_PLAIN>(row, c, bg.sink != 0, bg, kcap, out, nsel + u, gout,
+                                                         SoloTeam{});
+  } else {
+    team_topk<NPL, SoloTeam, TK_PLAIN>(row, c, bg.sink != 0, bg, kcap, out, nsel + u, gout, SoloTeam{});
+  }
+}
+
 hipError_t launch_topk(const sas_problem &p, const SeqTable &st, const float *scores, int64_t ld,
                        int32_t tq, int32_t sel_mode, const Budget &bg, int32_t kcap, int32_t *idx,
                        int32_t *nsel, float *gate, hipStream_t s) {
   const int QB = num_qblocks(tq, p.block);
+  if (!bg.shared && !(bg.coverage > 0.f)) {
+    int maxc = 0;
+    for (int b = 0; b < p.batch; ++b) maxc = std::max(maxc, (st.q0[b] + tq - 1) / p.block);
+    if (maxc < 64 * 32) {
+      const int S = sel_mode == SAS_SEL_HEAD ? p.hq : p.hkv;
+      const int64_t units = (int64_t)p.batch * S * QB;
+      const dim3 grid((unsigned)cdiv64(units, 4));
+#define SAS_TKW(NPL_)                                                                                      \
+  hipLaunchKernelGGL((topk_wave_kernel<NPL_>), grid, dim3(256), 0, s, st, scores, ld, tq, p.block, S, QB, bg, \
+                     kcap, idx, nsel, gate, units)
+      if (maxc < 64 * 4) SAS_TKW(4);
+      else if (maxc < 64 * 8) SAS_TKW(8);
+      else if (maxc < 64 * 16) SAS_TKW(16);
+      else SAS_TKW(32);
+#undef SAS_TKW
+      return hipGetLastError();
+    }
+  }
   if (bg.shared) {
     const int64_t groups = (int64_t)p.batch * p.hkv * QB;
     hipLaunchKernelGGL(topk_joint_kernel, dim3((unsigned)groups), dim3(256), 0, s, st, scores, ld, tq, p.block,
