@@ -639,6 +639,33 @@ def main():
                                    "bytes_per_step": by2["total"], "attend_traffic_bytes": tr["bytes"] if tr else None}
             log(f"[bench] decode 32K: step {ms * 1e3:.1f} us (graph {ms_graph * 1e3:.1f}) -> {gbs:.0f} GB/s; "
                 f"attention {ms_att * 1e3:.1f} us -> {att:.0f} GB/s")
+        if "decode" in only:
+            # the same step with the lengths in device memory (what a graph-replayed decode loop uses):
+            # the current blocks pooled again, fused selection, attention
+            lens_dev = torch.tensor(inp2.seq_lens, dtype=torch.int32, device="cuda")
+            Lm2 = inp2.K.shape[2]
+            bud2 = sas.Budget(k_fixed=w2.k_fixed)
+            O_dev = torch.empty_like(inp2.Q)
+            ws_sel = torch.zeros(sas.select_decode_workspace_bytes(w2.batch, w2.hq, w2.hkv, w2.d, w2.block,
+                                                                   sas.SAS_BF16, Lm2, inp2.seq_lens),
+                                 dtype=torch.uint8, device="cuda")
+            ws_dec = torch.zeros(sas.decode_workspace_bytes(w2.batch, w2.hq, w2.hkv, w2.d, w2.block, sas.SAS_BF16, Lm2,
+                                                            inp2.seq_lens, w2.sel, bufs["idx"].shape[1], False),
+                                 dtype=torch.uint8, device="cuda")
+
+            def step_dev():
+                sas.block_reps(inp2.K, lens_dev, w2.block, reps=bufs["reps"], current_block=True)
+                sas.select_decode(inp2.Q, bufs["reps"], lens_dev, w2.block, w2.hkv, Lm2, bud2, kcap=bufs["idx"].shape[1],
+                                  scores=bufs["scores"], idx=bufs["idx"], nsel=bufs["nsel"], workspace=ws_sel)
+                sas.sparse_decode(inp2.Q, inp2.K, inp2.V, lens_dev, w2.block, bufs["idx"], bufs["nsel"], None, O=O_dev,
+                                  workspace=ws_dec)
+            t_dev, _ = timer.time(step_dev, K_, W_)
+            t_dev_g, _ = timer.time(step_dev, K_, W_, use_graph=True)
+            extra["decode_32k_device_lengths"] = {
+                "step_us": round(t_dev * 1e3, 2), "graph_replay_us": round(t_dev_g * 1e3, 2),
+                "what": "lengths read from device memory: current blocks pooled again, fused selection, attention"}
+            log(f"[bench] decode 32K with device lengths (reps update + selection + attention): {t_dev * 1e3:.1f} us, "
+                f"graph {t_dev_g * 1e3:.1f} us")
         if "paged" in only:
             paged_measure(sas, torch, np, timer, extra, w2, inp2, bufs, K_, W_)
         if "reps" in only:

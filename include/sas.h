@@ -76,8 +76,20 @@ typedef struct sas_problem {
   int32_t block;            /* blk: tokens per block (SSA: per chunk)                       */
   int32_t dtype;            /* sas_dtype of Q, K, V, O and gist K/V                         */
   int32_t max_len;          /* Lmax: token capacity of K/V (every L_b <= Lmax)              */
-  const int32_t *seq_lens;  /* HOST [B]: L_b >= 1                                           */
+  const int32_t *seq_lens;  /* HOST [B]: L_b >= 1 (DEVICE [B] when seq_lens_device = 1)     */
+  int32_t seq_lens_device;  /* 0: seq_lens is host memory; 1: device memory (see below)     */
 } sas_problem;
+
+/* Lengths in device memory (seq_lens_device = 1) serve a decode loop whose step is captured once in
+ * a HIP graph and replayed while the lengths grow: the kernels read L_b from seq_lens when they run,
+ * so nothing on the host depends on them.  The host sizes launches and checks kcap, scores_ld and
+ * workspaces for the capacity max_len; a length outside [1, max_len] is clamped into it.  Taken by
+ *   sas_block_reps (every block up to L_b), sas_block_reps_update (first_block must be NULL: the
+ *   block holding position L_b - 1 is pooled again, which is all one appended token changes),
+ *   sas_block_reps_paged, sas_select_decode, sas_sparse_decode (bf16), sas_sparse_decode_noalloc,
+ *   sas_sparse_decode_paged;
+ * every other entry point returns SAS_ERR_UNSUPPORTED.  kcap comes from sas_required_kcap on a
+ * host problem at max_len. */
 
 /* Budget ([SAS] method: a fixed budget of k context units per query, configurable;
  * [GSA] section 4 pseudo-code keep_ratio).  For a unit whose current block is c:

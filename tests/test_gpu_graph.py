@@ -151,3 +151,100 @@ def test_training_step_graph_replays_match_eager():
         torch.cuda.synchronize()
         for name, x, y in zip(("dQ", "dK", "dV", "dgate", "dscore"), grads, ref):
             assert torch.equal(x, y), f"replay {r}: {name} differs"
+
+
+@pytest.mark.parametrize("sel", ["group", "head"])
+def test_decode_loop_with_device_lengths_from_one_graph(sel):
+    """A decode loop whose step -- pool the current block again, fused scores + top-k, attention -- is
+    captured ONCE with the lengths in device memory and replayed while every sequence grows by one
+    token per step (lengths cross block boundaries: a block fills up, a new one opens with one token).
+    Between replays, outside the graph, the new token's K/V and the step's queries are written and the
+    device lengths incremented.  Each replay must match the oracle at the new lengths (reps, lists under
+    the tie rule, outputs to the bf16 bars) and the same step run eagerly with host lengths, bit for bit."""
+    from oracle import sas_oracle as orc
+    from workloads.gen import round_bf16
+    from gpu_harness import list_matches, BF16_MAX_ABS, BF16_MEAN_ABS, say
+    lens = [1000, 127, 4095, 63]
+    steps, B, hq, hkv, d, blk = 4, 4, 8, 2, 128, 64
+    Lmax = 4200
+    rng = np.random.default_rng(53 if sel == "group" else 59)
+    K = round_bf16(rng.standard_normal((B, hkv, Lmax, d), dtype=np.float32))
+    V = round_bf16(rng.standard_normal((B, hkv, Lmax, d), dtype=np.float32))
+    Qs = round_bf16(rng.standard_normal((steps, B, hq, d), dtype=np.float32))
+    Kd = torch.zeros((B, hkv, Lmax, d), dtype=torch.bfloat16, device="cuda")
+    Vd = torch.zeros_like(Kd)
+    for b, L in enumerate(lens):
+        Kd[b, :, :L] = torch.from_numpy(K[b, :, :L]).to(torch.bfloat16).cuda()
+        Vd[b, :, :L] = torch.from_numpy(V[b, :, :L]).to(torch.bfloat16).cuda()
+    Qd = torch.zeros((B, hq, d), dtype=torch.bfloat16, device="cuda")
+    lens_dev = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    bud = sas.Budget(k_fixed=0, frac_num=1, frac_den=20, count_current=1, sink=True, gate=True) if sel == "head" \
+        else sas.Budget(k_fixed=4, sink=True, gate=True)
+    kcap = sas.required_kcap(B, hq, hkv, d, blk, sas.SAS_BF16, Lmax, [Lmax] * B, 1, None, bud)
+    S = hq if sel == "head" else hkv
+    nbm = -(-Lmax // blk)
+    reps = torch.zeros((B, hkv, nbm, d), dtype=torch.float32, device="cuda")
+    sas.block_reps(Kd, lens, blk, reps=reps)
+    scores = torch.full((B * S, nbm), float("-inf"), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B * S, kcap), dtype=torch.int32, device="cuda")
+    nsel = torch.empty((B * S,), dtype=torch.int32, device="cuda")
+    gate = torch.empty((B * S, kcap), dtype=torch.float32, device="cuda")
+    O = torch.empty_like(Qd)
+    sel_ws = torch.zeros(sas.select_decode_workspace_bytes(B, hq, hkv, d, blk, sas.SAS_BF16, Lmax, [Lmax] * B),
+                         dtype=torch.uint8, device="cuda")
+    dec_ws = torch.zeros(sas.decode_workspace_bytes(B, hq, hkv, d, blk, sas.SAS_BF16, Lmax, [Lmax] * B, sel, kcap,
+                                                    False), dtype=torch.uint8, device="cuda")
+
+    def step():
+        sas.block_reps(Kd, lens_dev, blk, reps=reps, current_block=True)
+        sas.select_decode(Qd, reps, lens_dev, blk, hkv, Lmax, bud, sel_mode=sel, kcap=kcap, scores=scores, idx=idx,
+                          nsel=nsel, gate=gate, workspace=sel_ws)
+        sas.sparse_decode(Qd, Kd, Vd, lens_dev, blk, idx, nsel, gate, sel_mode=sel, O=O, workspace=dec_ws)
+
+    # capture at the starting lengths (the capture's warm-up call pools the current blocks again,
+    # which leaves reps unchanged)
+    Qd.copy_(torch.from_numpy(Qs[0]).to(torch.bfloat16))
+    g = _capture(step)
+    for s in range(steps):
+        for b in range(B):
+            L = lens[b]
+            Kd[b, :, L] = torch.from_numpy(K[b, :, L]).to(torch.bfloat16).cuda()
+            Vd[b, :, L] = torch.from_numpy(V[b, :, L]).to(torch.bfloat16).cuda()
+        lens = [L + 1 for L in lens]
+        lens_dev.copy_(torch.tensor(lens, dtype=torch.int32))
+        Qd.copy_(torch.from_numpy(Qs[s]).to(torch.bfloat16))
+        g.replay()
+        torch.cuda.synchronize()
+        r_idx, r_nsel, r_O, r_reps = idx.clone(), nsel.clone(), O.clone(), reps.clone()
+        # the same step eagerly, with host lengths
+        full = sas.block_reps(Kd, lens, blk, reps=torch.full_like(reps, float("nan")))
+        _, e_idx, e_nsel, e_gate = sas.select_decode(Qd, full, lens, blk, hkv, Lmax, bud, sel_mode=sel, kcap=kcap)
+        e_O = sas.sparse_decode(Qd, Kd, Vd, lens, blk, e_idx, e_nsel, e_gate, sel_mode=sel)
+        torch.cuda.synchronize()
+        for b, L in enumerate(lens):
+            nb = -(-L // blk)
+            assert torch.equal(r_reps[b, :, :nb], full[b, :, :nb]), f"step {s}: reps of sequence {b} differ"
+        assert torch.equal(r_nsel, e_nsel) and torch.equal(r_idx, e_idx), f"step {s}: lists differ from eager"
+        assert torch.equal(r_O, e_O), f"step {s}: outputs differ from the eager host-length step"
+        idx_h, nsel_h, O_h = r_idx.cpu().numpy(), r_nsel.cpu().numpy(), r_O.float().cpu().numpy()
+        err_sum, err_n = 0.0, 0
+        for b, L in enumerate(lens):
+            kw = dict(frac_num=1, frac_den=20, count_current=1) if sel == "head" else dict(k_fixed=4)
+            r = orc.run_sequence(Qs[s][b][:, None, :], K[b], V[b], L, L - 1, blk, sel, sink=True, gate=True, **kw)
+            explicit = {}
+            for un in r.units:
+                u = b * S + un.sel_head
+                got = [int(x) for x in idx_h[u, :nsel_h[u]]]
+                ok, band, why = list_matches(un.sel, got, un.scores, un.c, un.k, True)
+                assert ok, f"step {s}, sequence {b}, unit {un.sel_head}: {why}"
+                if band:
+                    explicit[(un.sel_head, un.c)] = (got, orc.gate_values(un.scores, got))
+            if explicit:
+                r = orc.run_sequence(Qs[s][b][:, None, :], K[b], V[b], L, L - 1, blk, sel, sink=True, gate=True,
+                                     explicit=explicit, **kw)
+            diff = np.abs(O_h[b] - r.O[:, 0, :])
+            assert diff.max() <= BF16_MAX_ABS, f"step {s}, sequence {b}: max-abs {diff.max():.3e}"
+            err_sum += float(diff.sum())
+            err_n += diff.size
+        assert err_sum / err_n <= BF16_MEAN_ABS
+        say(f"[graph-loop {sel}] replay {s}: lengths {lens} match the oracle and the eager host-length step")

@@ -75,3 +75,30 @@ def test_backward_rejects_per_group_units_beyond_the_row_split():
                                         None, None, None, FAKE, 1 << 30, None)
     assert r == _lib.SAS_ERR_UNSUPPORTED
     assert b"per KV head" in lib.sas_last_error()
+
+
+@needs_lib
+def test_device_lengths_are_refused_where_the_host_needs_them():
+    """seq_lens in device memory (seq_lens_device = 1) serve the decode loop's entry points only; the
+    others refuse them before anything is launched, and a bad flag is a shape error."""
+    lib = _lib.load()
+    lens = _lib.i32x([4096, 4096])
+    dev = _lib.Problem(2, 8, 2, 128, 64, _lib.SAS_BF16, 4096, C.cast(lens, C.POINTER(C.c_int32)), 1)
+    bad = _lib.Problem(2, 8, 2, 128, 64, _lib.SAS_BF16, 4096, C.cast(lens, C.POINTER(C.c_int32)), 2)
+    b = _lib.Budget(4, 0, 0, 0, 0, 0)
+    assert lib.sas_required_kcap(C.byref(dev), 1, None, C.byref(b)) == _lib.SAS_ERR_UNSUPPORTED
+    assert lib.sas_required_kcap(C.byref(bad), 1, None, C.byref(b)) == _lib.SAS_ERR_SHAPE
+    qs3 = _lib.i64x([8 * 4096 * 128, 4096 * 128, 128])
+    rs = _lib.i64x([2 * 64 * 128, 64 * 128, 128])
+    r = lib.sas_block_scores(C.byref(dev), FAKE, qs3, 1, None, FAKE, _lib.SAS_REPS_POOLED, rs, _lib.SAS_SEL_GROUP,
+                             0.0, FAKE, 64, None, 0, None)
+    assert r == _lib.SAS_ERR_UNSUPPORTED
+    assert b"host memory" in lib.sas_last_error()
+    r = lib.sas_topk_select(C.byref(dev), FAKE, 64, 1, None, _lib.SAS_SEL_GROUP, C.byref(b), 8, FAKE, FAKE, None, None)
+    assert r == _lib.SAS_ERR_UNSUPPORTED
+    # the incremental reps of a decode loop: the block to pool is found on the device, so no first_block
+    ks = _lib.i64x([2 * 4096 * 128, 4096 * 128, 128])
+    first = _lib.i32x([63, 63])
+    r = lib.sas_block_reps_update(C.byref(dev), FAKE, ks, FAKE, rs, first, None)
+    assert r == _lib.SAS_ERR_SHAPE
+    assert b"first_block must be NULL" in lib.sas_last_error()

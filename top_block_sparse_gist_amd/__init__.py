@@ -68,16 +68,38 @@ def _dtype_code(t) -> int:
 
 
 class _Prob:
-    """sas_problem plus the host arrays it points to (kept alive for the call)."""
+    """sas_problem plus the host arrays it points to (kept alive for the call).  seq_lens: a sequence of
+    ints (host lengths), or an int32 tensor on the GPU (lengths the kernels read from device memory)."""
 
     def __init__(self, batch, hq, hkv, d, block, dtype, max_len, seq_lens):
-        self.lens = i32x(seq_lens)
-        self.s = _lib.Problem(batch, hq, hkv, d, block, dtype, max_len,
-                              C.cast(self.lens, C.POINTER(C.c_int32)))
+        if _is_device_lens(seq_lens):
+            self.lens = seq_lens
+            self.s = _lib.Problem(batch, hq, hkv, d, block, dtype, max_len,
+                                  C.cast(C.c_void_p(seq_lens.data_ptr()), C.POINTER(C.c_int32)), 1)
+        else:
+            self.lens = i32x(seq_lens)
+            self.s = _lib.Problem(batch, hq, hkv, d, block, dtype, max_len,
+                                  C.cast(self.lens, C.POINTER(C.c_int32)), 0)
 
     @property
     def ref(self):
         return C.byref(self.s)
+
+
+def _is_device_lens(seq_lens) -> bool:
+    if hasattr(seq_lens, "is_cuda") and seq_lens.is_cuda:
+        torch = _torch()
+        if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
+            raise ValueError("device seq_lens must be a contiguous int32 tensor")
+        return True
+    return False
+
+
+def _max_blocks(seq_lens, block, max_len) -> int:
+    """Blocks of the longest sequence (device lengths: of the capacity max_len)."""
+    if _is_device_lens(seq_lens):
+        return -(-int(max_len) // block)
+    return max(-(-int(L) // block) for L in seq_lens)
 
 
 def _stream(stream):
@@ -116,22 +138,27 @@ def required_kcap(batch, hq, hkv, d, block, dtype, max_len, seq_lens, tq, q_star
 
 
 def block_reps(K, seq_lens: Sequence[int], block: int, hq: Optional[int] = None, reps=None, stream=None,
-               first_block: Optional[Sequence[int]] = None):
+               first_block: Optional[Sequence[int]] = None, current_block: bool = False):
     """A1: fp32 mean of every block's keys; K [B, Hkv, Lmax, d] -> reps [B, Hkv, NBmax, d].
 
     first_block (one int per sequence): recompute only blocks first_block[b] .. NB_b - 1 of an
     existing ``reps`` (sas_block_reps_update), e.g. floor(L_old / block) after appending tokens.
+    current_block (seq_lens a device tensor): recompute only the block holding each sequence's last
+    position, found on the device (sas_block_reps_update with first_block NULL).
     """
     torch = _torch()
     B, hkv, lmax, d = K.shape
-    nb = max(-(-int(L) // block) for L in seq_lens)
+    nb = _max_blocks(seq_lens, block, lmax)
     if reps is None:
-        if first_block is not None:
+        if first_block is not None or current_block:
             raise ValueError("an incremental update needs the existing reps")
         reps = torch.empty((B, hkv, nb, d), dtype=torch.float32, device=K.device)
     p = _Prob(B, hq or hkv, hkv, d, block, _dtype_code(K), lmax, seq_lens)
     lib = load()
-    if first_block is None:
+    if current_block:
+        check(lib.sas_block_reps_update(p.ref, _ptr(K), _strides(K, 3), _ptr(reps), _strides(reps, 3), None,
+                                        _stream(stream)), "sas_block_reps_update")
+    elif first_block is None:
         check(lib.sas_block_reps(p.ref, _ptr(K), _strides(K, 3), _ptr(reps), _strides(reps, 3), _stream(stream)),
               "sas_block_reps")
     else:
@@ -214,12 +241,14 @@ def select_decode(Q, reps, seq_lens, block, hkv, max_len, budget: Budget, sel_mo
     B, hq, d = Q.shape
     sm = sel_code(sel_mode)
     S = hq if sm == SAS_SEL_HEAD else hkv
-    nb = max(-(-int(L) // block) for L in seq_lens)
+    nb = _max_blocks(seq_lens, block, max_len)
     p = _Prob(B, hq, hkv, d, block, _dtype_code(Q), max_len, seq_lens)
     bs = budget.c_struct()
     lib = load()
     if kcap is None:
-        kcap = lib.sas_required_kcap(p.ref, 1, None, C.byref(bs))
+        # device lengths: the capacity's kcap (a host problem at max_len)
+        hp = _Prob(B, hq, hkv, d, block, _dtype_code(Q), max_len, [max_len] * B) if _is_device_lens(seq_lens) else p
+        kcap = lib.sas_required_kcap(hp.ref, 1, None, C.byref(bs))
         if kcap < 0:
             check(kcap, "sas_required_kcap")
     if scores is None:

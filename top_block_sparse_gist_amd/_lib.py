@@ -33,7 +33,7 @@ EXPORTED = ("sas_num_qblocks", "sas_required_kcap", "sas_block_reps", "sas_block
 class Problem(C.Structure):
     _fields_ = [("batch", C.c_int32), ("hq", C.c_int32), ("hkv", C.c_int32), ("head_dim", C.c_int32),
                 ("block", C.c_int32), ("dtype", C.c_int32), ("max_len", C.c_int32),
-                ("seq_lens", C.POINTER(C.c_int32))]
+                ("seq_lens", C.POINTER(C.c_int32)), ("seq_lens_device", C.c_int32)]
 
 
 class Budget(C.Structure):

@@ -55,6 +55,19 @@ sas_status check_problem(const sas_problem *p, SeqTable *tab) {
     return fail(SAS_ERR_UNSUPPORTED, "block %d not supported (64, 128)", p->block);
   if (p->dtype != SAS_F32 && p->dtype != SAS_BF16) return fail(SAS_ERR_UNSUPPORTED, "dtype %d", p->dtype);
   if (p->max_len < 1) return fail(SAS_ERR_SHAPE, "max_len must be >= 1");
+  if (p->seq_lens_device != 0 && p->seq_lens_device != 1)
+    return fail(SAS_ERR_SHAPE, "seq_lens_device must be 0 or 1 (got %d)", p->seq_lens_device);
+  if (p->seq_lens_device) {
+    // lengths in device memory: the host sizes everything for the capacity; kernels read the lengths
+    if (tab) {
+      for (int b = 0; b < p->batch; ++b) {
+        tab->len[b] = p->max_len;
+        tab->q0[b] = p->max_len - 1;
+      }
+      tab->dlen = p->seq_lens;
+    }
+    return SAS_OK;
+  }
   for (int b = 0; b < p->batch; ++b) {
     const int L = p->seq_lens[b];
     if (L < 1 || L > p->max_len)
@@ -67,8 +80,29 @@ sas_status check_problem(const sas_problem *p, SeqTable *tab) {
   return SAS_OK;
 }
 
+// Entry points that need the lengths on the host refuse device lengths.
+sas_status host_lengths_only(const sas_problem *p, const char *what) {
+  if (p && p->seq_lens_device)
+    return fail(SAS_ERR_UNSUPPORTED, "%s needs seq_lens in host memory (seq_lens_device = 0)", what);
+  return SAS_OK;
+}
+
+// The problem as the host sees it: with device lengths, a copy whose lengths are the capacity held by
+// the checked table (valid while `tab` lives).
+sas_problem host_view(const sas_problem *p, const SeqTable &tab) {
+  sas_problem h = *p;
+  if (p->seq_lens_device) {
+    h.seq_lens = tab.len;
+    h.seq_lens_device = 0;
+  }
+  return h;
+}
+
 // Prefill rows: q_start (host) gives the first row position, rows [q0, q0 + tq) within [0, L).
 sas_status check_rows(const sas_problem *p, int32_t tq, const int32_t *q_start, SeqTable *tab) {
+  // the entry points that take rows (scores, top-k, prefill, backward, kcap) work from host lengths
+  sas_status st;
+  if ((st = host_lengths_only(p, "this entry point")) != SAS_OK) return st;
   if (tq < 1) return fail(SAS_ERR_SHAPE, "tq must be >= 1 (got %d)", tq);
   if (!q_start) {
     if (tq != 1) return fail(SAS_ERR_SHAPE, "decode (q_start == NULL) needs tq == 1 (got %d)", tq);
@@ -142,6 +176,7 @@ int32_t sas_num_qblocks(int32_t tq, int32_t block) {
 int32_t sas_required_kcap(const sas_problem *p, int32_t tq, const int32_t *q_start, const sas_budget *budget) {
   sas_status st;
   if ((st = check_problem(p, nullptr)) != SAS_OK) return st;
+  if ((st = host_lengths_only(p, "sas_required_kcap")) != SAS_OK) return st;
   if ((st = check_rows(p, tq, q_start, nullptr)) != SAS_OK) return st;
   if ((st = check_budget(budget)) != SAS_OK) return st;
   return required_kcap(p, tq, q_start, budget);
@@ -165,11 +200,19 @@ sas_status sas_block_reps_update(const sas_problem *p, const void *K, const int6
   SeqTable tab{};
   sas_status st;
   if ((st = check_problem(p, &tab)) != SAS_OK) return st;
-  if (!K || !reps || !k_stride || !rep_stride || !first_block)
-    return fail(SAS_ERR_NULL, "K, reps, a stride array or first_block is NULL");
+  if (!K || !reps || !k_stride || !rep_stride) return fail(SAS_ERR_NULL, "K, reps or a stride array is NULL");
   if (!aligned16(K) || !aligned16(reps) || !strides_ok(k_stride, 3, elem_bytes(p->dtype)) ||
       !strides_ok(rep_stride, 3, 4))
     return fail(SAS_ERR_SHAPE, "K / reps must be 16-byte aligned with 16-byte-multiple row strides");
+  if (p->seq_lens_device) {
+    // lengths in device memory: the block of each sequence's last position, found on the device
+    if (first_block)
+      return fail(SAS_ERR_SHAPE, "with device seq_lens, first_block must be NULL (the current block is pooled)");
+    return hip_status(launch_reps(*p, tab, K, k_stride, reps, rep_stride, nullptr, (hipStream_t)stream, nullptr, 0,
+                                  true),
+                      "sas_block_reps_update");
+  }
+  if (!first_block) return fail(SAS_ERR_NULL, "first_block is NULL");
   for (int b = 0; b < p->batch; ++b) {
     const int nb = cdiv(tab.len[b], p->block);
     if (first_block[b] < 0 || first_block[b] > nb)
@@ -326,16 +369,18 @@ sas_status sas_select_decode(const sas_problem *p, const void *Q, const int64_t 
   if (!aligned16(Q) || !aligned16(reps) || !strides_ok(q_stride, 2, elem_bytes(p->dtype)) ||
       !strides_ok(rep_stride, 3, rep_bytes))
     return fail(SAS_ERR_SHAPE, "Q / reps must be 16-byte aligned with 16-byte-multiple row strides");
+  // with device lengths every bound below is taken at the capacity max_len
+  const sas_problem hv = host_view(p, tab);
   int nbmax = 0, maxc = 0;
   for (int b = 0; b < p->batch; ++b) {
-    nbmax = std::max(nbmax, cdiv(p->seq_lens[b], p->block));
-    maxc = std::max(maxc, (p->seq_lens[b] - 1) / p->block);
+    nbmax = std::max(nbmax, cdiv(tab.len[b], p->block));
+    maxc = std::max(maxc, (tab.len[b] - 1) / p->block);
   }
   if (maxc > SELECT_DECODE_MAX_C)
     return fail(SAS_ERR_UNSUPPORTED, "current block %d > %d: use sas_block_scores + sas_topk_select", maxc,
                 SELECT_DECODE_MAX_C);
   if (scores_ld < nbmax) return fail(SAS_ERR_SHAPE, "scores_ld %lld < %d blocks", (long long)scores_ld, nbmax);
-  const int32_t need = required_kcap(p, 1, nullptr, budget);
+  const int32_t need = required_kcap(&hv, 1, nullptr, budget);
   if (kcap < need) return fail(SAS_ERR_SHAPE, "kcap %d < %d selected blocks", kcap, need);
   const size_t wneed = sas_select_decode_workspace(p);
   if (!workspace || workspace_bytes < wneed)
@@ -419,6 +464,7 @@ sas_status sparse_decode_impl(const sas_problem *p, const void *Q, const int64_t
   const float sc = resolve_scale(scale, p->head_dim);
   const hipStream_t s = (hipStream_t)stream;
   if (p->dtype == SAS_F32) {
+    if ((st = host_lengths_only(p, "the fp32 decode")) != SAS_OK) return st;
     const int64_t qs3[3] = {q_stride[0], q_stride[1], 0};
     const int64_t os3[3] = {o_stride[0], o_stride[1], 0};
     return hip_status(launch_attend_f32(*p, tab, Q, qs3, K, V, kv_stride, gist_k, gist_v, gist_stride, 1, sel_mode,
@@ -582,6 +628,7 @@ sas_status sas_sparse_prefill_paged(const sas_problem *p, const void *Q, const i
 static sas_status check_hssa(const sas_problem *p, const SeqTable &tab, int32_t sel_mode, int32_t M, int32_t gcap,
                              int *maxc_out) {
   sas_status st;
+  if ((st = host_lengths_only(p, "the two-level gist decode")) != SAS_OK) return st;
   if ((st = check_sel(sel_mode)) != SAS_OK) return st;
   if (p->dtype != SAS_BF16) return fail(SAS_ERR_UNSUPPORTED, "two-level gist selection needs bf16 inputs");
   if (M < 4 || M > 64) return fail(SAS_ERR_UNSUPPORTED, "group_chunks %d outside [4, 64]", M);

@@ -10,11 +10,20 @@
 
 namespace sas {
 
-// Per-call sequence table, passed by value as a kernel argument (no device upload).
+// Per-call sequence table, passed by value as a kernel argument (no device upload).  With the
+// lengths in device memory (dlen != nullptr: a decode loop replayed from a captured graph while the
+// lengths grow) len[] holds the capacity max_len, which sizes the grids, and kernels read L_b from
+// dlen through seq_len().
 struct SeqTable {
-  int32_t len[SAS_MAX_BATCH];  // L_b
+  int32_t len[SAS_MAX_BATCH];  // L_b (device lengths: max_len)
   int32_t q0[SAS_MAX_BATCH];   // position of the first query row (decode: L_b - 1)
+  const int32_t *dlen;         // DEVICE [B] lengths, or nullptr
 };
+
+// L_b of sequence b; a device length is clamped to [1, max_len] (the host cannot check it).
+__device__ __forceinline__ int seq_len(const SeqTable &st, int b) {
+  return st.dlen ? min(max(st.dlen[b], 1), st.len[b]) : st.len[b];
+}
 
 struct Budget {
   int32_t k_fixed, frac_num, frac_den, count_current, sink, gate;
@@ -210,10 +219,11 @@ __device__ __forceinline__ uint32_t float_order_key(float f) {
 // ---------------------------------------------------------------------------------------
 namespace sas {
 
-// first: host [batch] first block to compute per sequence, or NULL for every block
+// first: host [batch] first block to compute per sequence, or NULL for every block; current: only the
+// block holding position L_b - 1 of each sequence (found on the device)
 hipError_t launch_reps(const sas_problem &p, const SeqTable &st, const void *K, const int64_t *ks,
                        float *reps, const int64_t *rs, const int32_t *first, hipStream_t s,
-                       const int32_t *table = nullptr, int64_t tld = 0);
+                       const int32_t *table = nullptr, int64_t tld = 0, bool current = false);
 
 hipError_t launch_pool_queries(const sas_problem &p, const SeqTable &st, const void *Q,
                                const int64_t *qs, int32_t tq, int32_t sel_mode, float *qbar,

@@ -421,7 +421,7 @@ __device__ __forceinline__ void select_tile_body(
   auto scs = reinterpret_cast<float(*)[64]>(lds + Lds::SCS);
   int &last_sh = *reinterpret_cast<int *>(lds + Lds::LAST);
   const int j0 = bx * 64;
-  const int L = st.len[b];
+  const int L = seq_len(st, b);
   const int c = (L - 1) / blk;
   const int ntile = select_tiles(c, gist);
   if (bx >= ntile) return;
@@ -612,7 +612,7 @@ __device__ __forceinline__ void decode_tile_body(
   const int g = per_head ? s / G : s;
   const int nh = per_head ? 1 : G;
   const int h0 = per_head ? s : s * G;
-  const int L = st.len[b];
+  const int L = seq_len(st, b);
   const int c = (L - 1) / blk;
   const int tpb = blk / 64;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;

@@ -13,9 +13,11 @@
 
 namespace sas {
 
-// First block computed per sequence (grid x counts blocks from it).
+// First block computed per sequence (grid x counts blocks from it); current: the one block that holds
+// position L_b - 1, found on the device (lengths in device memory).
 struct BlockStart {
   int32_t j[SAS_MAX_BATCH];
+  int32_t current;
 };
 
 template <typename T, int D, int BLK>
@@ -31,8 +33,9 @@ __global__ __launch_bounds__(256) void reps_kernel(SeqTable st, BlockStart start
   __shared__ float part[RPP][D + 1];
 
   const int g = blockIdx.y, b = blockIdx.z;
-  const int j = start.j[b] + (int)blockIdx.x;
-  const int L = st.len[b];
+  const int L = seq_len(st, b);
+  // current-block mode (lengths in device memory): the block that holds position L - 1
+  const int j = (start.current ? (L - 1) / BLK : start.j[b]) + (int)blockIdx.x;
   const int t0 = j * BLK;
   if (t0 >= L) return;
   const int n = min(BLK, L - t0);
@@ -79,12 +82,17 @@ __global__ __launch_bounds__(256) void reps_kernel(SeqTable st, BlockStart start
 template <typename T, int D>
 static hipError_t reps_dispatch_blk(const sas_problem &p, const SeqTable &st, const void *K,
                                     const int64_t *ks, float *reps, const int64_t *rs, const int32_t *first,
-                                    hipStream_t s, const int32_t *table, int64_t tld) {
+                                    hipStream_t s, const int32_t *table, int64_t tld, bool current) {
   BlockStart start{};
   int nbmax = 0;
-  for (int b = 0; b < p.batch; ++b) {
-    start.j[b] = first ? first[b] : 0;
-    nbmax = max(nbmax, cdiv(st.len[b], p.block) - start.j[b]);
+  if (current) {
+    start.current = 1;
+    nbmax = 1;
+  } else {
+    for (int b = 0; b < p.batch; ++b) {
+      start.j[b] = first ? first[b] : 0;
+      nbmax = max(nbmax, cdiv(st.len[b], p.block) - start.j[b]);
+    }
   }
   if (nbmax <= 0) return hipSuccess;  // nothing to compute
   dim3 grid(nbmax, p.hkv, p.batch);
@@ -99,13 +107,14 @@ static hipError_t reps_dispatch_blk(const sas_problem &p, const SeqTable &st, co
 
 hipError_t launch_reps(const sas_problem &p, const SeqTable &st, const void *K, const int64_t *ks,
                        float *reps, const int64_t *rs, const int32_t *first, hipStream_t s, const int32_t *table,
-                       int64_t tld) {
+                       int64_t tld, bool current) {
   if (p.dtype == SAS_BF16) {
-    if (p.head_dim == 128) return reps_dispatch_blk<uint16_t, 128>(p, st, K, ks, reps, rs, first, s, table, tld);
-    return reps_dispatch_blk<uint16_t, 64>(p, st, K, ks, reps, rs, first, s, table, tld);
+    if (p.head_dim == 128)
+      return reps_dispatch_blk<uint16_t, 128>(p, st, K, ks, reps, rs, first, s, table, tld, current);
+    return reps_dispatch_blk<uint16_t, 64>(p, st, K, ks, reps, rs, first, s, table, tld, current);
   }
-  if (p.head_dim == 128) return reps_dispatch_blk<float, 128>(p, st, K, ks, reps, rs, first, s, table, tld);
-  return reps_dispatch_blk<float, 64>(p, st, K, ks, reps, rs, first, s, table, tld);
+  if (p.head_dim == 128) return reps_dispatch_blk<float, 128>(p, st, K, ks, reps, rs, first, s, table, tld, current);
+  return reps_dispatch_blk<float, 64>(p, st, K, ks, reps, rs, first, s, table, tld, current);
 }
 
 }  // namespace sas
