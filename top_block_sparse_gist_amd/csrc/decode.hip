@@ -28,6 +28,36 @@
 
 namespace sas {
 
+// Workgroup id -> (workgroup of the unit, unit).  Workgroup i runs on XCD i % 8, each XCD with its
+// own L2.  Per-head units of one (sequence, KV head) read the same K/V rows wherever their lists
+// overlap (the current block, blocks every head ranks high), so with `grouped` all workgroups of
+// such a pair are placed on one XCD, pairs dealt round-robin, and within a pair the G heads'
+// workgroups of each list range run back to back: a tile the heads share is fetched into that
+// L2 once.  Pairs past the last multiple of 8 are placed in order.  Otherwise unit-major.
+__device__ __forceinline__ void decode_place(int id, int nwg, int64_t units, int G, bool grouped, int &x,
+                                             int64_t &u) {
+  if (!grouped) {
+    u = id / nwg;
+    x = id % nwg;
+    return;
+  }
+  const int W = G * nwg;  // workgroups of one pair
+  const int64_t full = units / G / 8 * 8;
+  int64_t p;
+  int w;
+  if (id < full * W) {
+    const int r = id / 8;
+    p = (int64_t)(r / W) * 8 + id % 8;
+    w = r % W;
+  } else {
+    const int64_t j = id - full * W;
+    p = full + j / W;
+    w = (int)(j % W);
+  }
+  x = w / G;
+  u = p * G + w % G;
+}
+
 template <int D, int WPW, int TPW, typename OT, bool HS>
 __global__ __launch_bounds__(WPW * 64) __attribute__((amdgpu_waves_per_eu(2))) void decode_bf16_kernel(
     SeqTable st, const uint16_t *__restrict__ Q, int64_t qb, int64_t qh, const uint16_t *__restrict__ K,
@@ -35,9 +65,12 @@ __global__ __launch_bounds__(WPW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     const uint16_t *__restrict__ GV, int64_t gb, int64_t gh, int64_t gt, int gist, int blk, int S, int G,
     int per_head, const int32_t *__restrict__ idx, const int32_t *__restrict__ nsel, const float *__restrict__ gate,
     int kcap, float scale_log2, float *__restrict__ work, uint32_t *__restrict__ counters, OT *__restrict__ O,
-    int64_t ob, int64_t oh, MetaArgs ma, PageArgs pg) {
+    int64_t ob, int64_t oh, MetaArgs ma, PageArgs pg, int nwg, int64_t units) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[DecodeLds<D, WPW>::BYTES];
-  decode_tile_body<D, WPW, TPW, OT, HS>(blockIdx.x, blockIdx.y, gridDim.x, lds, st, Q, qb, qh, K, V, kb, kh, kt,
+  int x;
+  int64_t u;
+  decode_place((int)blockIdx.x, nwg, units, G, per_head && G > 1, x, u);
+  decode_tile_body<D, WPW, TPW, OT, HS>(x, u, nwg, lds, st, Q, qb, qh, K, V, kb, kh, kt,
                                           GK, GV, gb, gh, gt, gist, blk, S, G, per_head, idx, nsel, gate, kcap,
                                           scale_log2, work, counters, O, ob, oh, ma, pg);
 }
@@ -93,11 +126,12 @@ static hipError_t decode_launch(const sas_problem &p, const SeqTable &st, const 
                                 int per_head, const int32_t *idx, const int32_t *nsel, const float *gate, int32_t kcap,
                                 float scale_log2, float *work, uint32_t *counters, void *O, const int64_t *os,
                                 const MetaArgs &ma, const PageArgs &pg, hipStream_t s) {
-  hipLaunchKernelGGL((decode_bf16_kernel<D, WPW, TPW, uint16_t, HS>), dim3(nwg, (unsigned)d.units), dim3(WPW * 64), 0,
+  if ((uint64_t)nwg * (uint64_t)d.units * WPW * 64 > 0xFFFFFFFFull) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((decode_bf16_kernel<D, WPW, TPW, uint16_t, HS>), dim3((unsigned)(nwg * d.units)), dim3(WPW * 64), 0,
                      s, st, (const uint16_t *)Q, qs[0], qs[1], (const uint16_t *)K, (const uint16_t *)V, kvs[0],
                      kvs[1], kvs[2], (const uint16_t *)gk, (const uint16_t *)gv, gb, gh, gt, gist, p.block, d.S,
                      p.hq / p.hkv, per_head, idx, nsel, gate, kcap, scale_log2, work, counters, (uint16_t *)O, os[0],
-                     os[1], ma, pg);
+                     os[1], ma, pg, nwg, d.units);
   return hipGetLastError();
 }
 

@@ -39,6 +39,28 @@ __device__ __forceinline__ uint32_t count_ge(const uint32_t (&key)[NPL], uint32_
   return n;
 }
 
+// Keys >= ta and keys >= tb over the wave, in one pass over the registers.
+template <int NPL>
+__device__ __forceinline__ void count_ge2(const uint32_t (&key)[NPL], uint32_t ta, uint32_t tb, uint32_t &na,
+                                          uint32_t &nb) {
+  na = nb = 0u;
+#pragma unroll
+  for (int r = 0; r < NPL; ++r) {
+    na += (uint32_t)__popcll(__ballot(key[r] >= ta));
+    nb += (uint32_t)__popcll(__ballot(key[r] >= tb));
+  }
+}
+
+// z with P(Z > z) = q for a standard normal Z, 0 < q < 1: the rational approximation of
+// Abramowitz and Stegun, formula 26.2.23 (absolute error below 4.5e-4), mirrored for q > 1/2.
+__device__ __forceinline__ float upper_normal_quantile(float q) {
+  const float p = fminf(q, 1.f - q);
+  const float t = sqrtf(-2.f * __logf(p));
+  const float z = t - (2.515517f + t * (0.802853f + t * 0.010328f)) /
+                          (1.f + t * (1.432788f + t * (0.189269f + t * 0.001308f)));
+  return q > 0.5f ? -z : z;
+}
+
 // Wave-wide max / sum of a float to a uniform value: DPP within each 16-lane row, then the four row
 // results through scalar registers (the same shape as wave_reduce_u32).
 template <typename Op>
@@ -194,6 +216,9 @@ __device__ void team_topk(const float *__restrict__ row, int c, bool sinkf, cons
   // the key of one NaN pattern only, and NaN scores are not ranked)
   uint32_t key[NPL];
   float s_c = 0.f, s_0 = 0.f;
+  // the interpolation search below takes its first bracket from the candidates' score moments
+  constexpr bool GUESS = NPL * Team::SIZE > 8;
+  float m1 = 0.f, m2 = 0.f;
   if (act) {
     // device-coherent loads through a buffer resource (not atomics, which the compiler issues one at
     // a time, each waiting for the previous): every lane loads (entries up to c exist), all loads are
@@ -207,7 +232,13 @@ __device__ void team_topk(const float *__restrict__ row, int c, bool sinkf, cons
 #pragma unroll
     for (int r = 0; r < NPL; ++r) {
       const int j = jw + lane + 64 * r;
-      key[r] = (j >= lo && j < c) ? max(float_order_key(sv[r]), 1u) : 0u;
+      const bool cand = j >= lo && j < c;
+      key[r] = cand ? max(float_order_key(sv[r]), 1u) : 0u;
+      if constexpr (GUESS) {
+        const float x = (cand && fabsf(sv[r]) < 1.0e18f) ? sv[r] : 0.f;
+        m1 += x;
+        m2 = fmaf(x, x, m2);
+      }
     }
   } else {
 #pragma unroll
@@ -268,7 +299,42 @@ __device__ void team_topk(const float *__restrict__ row, int c, bool sinkf, cons
       // is the k-th largest key, with k - ch of its holders taken.
       uint32_t lo = kmin, hi = kmax, cl = (uint32_t)ncand, ch = c_hi;
       bool exact = false, bisect = false;
-      while (hi - lo > 1u) {
+      // First bracket: with the candidates' mean and spread, a normal model puts 3k/2 and 2k/3
+      // scores above two values; both are counted in one pass.  A count moves lo or hi whatever
+      // the model's error (counts fall as the probe rises), so the model decides only how many
+      // probes follow.
+      const float M1 = team.fsum(wave_fsum_dpp(m1)), M2 = team.fsum(wave_fsum_dpp(m2));
+      if (hi - lo > 2u) {
+        const float nc = (float)ncand, mu = M1 / nc, sd = sqrtf(fmaxf(M2 / nc - mu * mu, 0.f));
+        if (sd > 0.f && sd < 1.0e18f) {
+          auto probe = [&](float above) {
+            const float v = fmaf(sd, upper_normal_quantile(fminf(fmaxf(above, 0.5f), nc - 0.5f) / nc), mu);
+            return min(max(float_order_key(v), lo + 1u), hi - 1u);
+          };
+          const uint32_t ta = probe(1.5f * (float)k), tb = max(probe((float)k / 1.5f), ta);
+          uint32_t ca, cb;
+          count_ge2(key, ta, tb, ca, cb);
+          ca = team.sum(ca);
+          cb = team.sum(cb);
+          if (ca >= (uint32_t)k) {
+            lo = ta;
+            cl = ca;
+            exact = ca == (uint32_t)k;
+            if (!exact && cb >= (uint32_t)k) {
+              lo = tb;
+              cl = cb;
+              exact = cb == (uint32_t)k;
+            } else if (!exact && tb < hi) {
+              hi = tb;
+              ch = cb;
+            }
+          } else {
+            hi = ta;
+            ch = ca;
+          }
+        }
+      }
+      while (!exact && hi - lo > 1u) {
         const uint32_t span = hi - lo;
         uint32_t step;
         if (bisect) {
