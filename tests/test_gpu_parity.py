@@ -617,3 +617,41 @@ def test_paged_decode_loop_against_the_oracle():
         assert err_sum / err_n <= BF16_MEAN_ABS
         say(f"[paged-loop] step {step}: lengths {lens}, pages in use {B * nbmax + 7 - len(free)}, "
             f"reps, lists and outputs match the oracle")
+
+
+@pytest.mark.parametrize("sel,d", [("group", 128), ("head", 64)])
+def test_prefill_scores_against_gist_keys(sel, d):
+    """Prefill block scores with gist keys as representatives (bf16 keys into the fp32 score
+    product): every unit's row against the oracle's definition (mean over the unit's query vectors
+    of scale * q . g_j) for the complete chunks before its current one, -inf for the rest up to c."""
+    from oracle import sas_oracle as orc
+    rng = np.random.default_rng(7)
+    B, hq, hkv, blk = 2, 8, 2, 64
+    lens, tq = [2000, 1500], 600
+    q_start = [L - tq for L in lens]
+    Lmax = max(lens)
+    NC = Lmax // blk
+    Q = torch.from_numpy(rng.standard_normal((B, hq, tq, d)).astype(np.float32)).to(torch.bfloat16)
+    gk = torch.from_numpy(rng.standard_normal((B, hkv, NC, d)).astype(np.float32)).to(torch.bfloat16)
+    scores = sas.block_scores(Q.cuda(), gk.cuda(), lens, blk, hkv, Lmax, q_start=q_start, sel_mode=sel, gist=True)
+    torch.cuda.synchronize()
+    sc = scores.cpu().numpy().astype(np.float64)
+    S = hkv if sel == "group" else hq
+    QB = sas.num_qblocks(tq, blk)
+    scale = 1.0 / np.sqrt(d)
+    worst = 0.0
+    for b in range(B):
+        Qb = Q[b].float().numpy()
+        units = orc.make_units(q_start[b], tq, blk, hq, hkv, sel)
+        for un in units:
+            u = (b * S + un.sel_head) * QB + (un.c - q_start[b] // blk)
+            g = orc.kv_head_of(un, hq // hkv, sel)
+            have = min(lens[b] // blk, un.c)
+            ref = orc.unit_scores(orc.unit_query_vectors(Qb, un), gk[b, g].float().numpy(), have, scale)
+            got = sc[u, :un.c + 1]
+            assert np.isneginf(got[have:]).all(), f"unit {u}: entries past the complete chunks are not -inf"
+            err = np.abs(got[:have] - ref).max() if have else 0.0
+            tol = 1e-5 * (1.0 + np.abs(ref).max()) if have else 0.0
+            assert err <= tol, f"unit {u}: scores differ by {err:.3e} (tol {tol:.1e})"
+            worst = max(worst, err / (1.0 + (np.abs(ref).max() if have else 0.0)))
+    say(f"[case] gist-key prefill scores {sel} d{d}: max rel err {worst:.2e}")
