@@ -27,7 +27,9 @@
  *     tokens; block j covers positions [j*blk, min((j+1)*blk, L_b)); NB_b = ceil(L_b/blk).
  *   - Element strides are in elements (not bytes); the last dimension (d) is contiguous.
  *     Q and O are [B, Hq, T, d]; K and V are [B, Hkv, Lmax, d]; gist K/V [B, Hkv, NC, d].
- *   - seq_lens and q_start are HOST arrays of int32 (read during the call, not kept).
+ *   - seq_lens and q_start are HOST arrays of int32 (read during the call, not kept), except
+ *     that the decode loop's entry points take seq_lens in device memory when
+ *     sas_problem.seq_lens_device = 1 (see below).
  *     Every other pointer is DEVICE memory owned by the caller; the library never
  *     allocates, frees or keeps device memory, and never synchronises the stream.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream).

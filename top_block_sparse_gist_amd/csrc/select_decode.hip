@@ -10,10 +10,11 @@
 // are formed with a shuffle reduction and written.  The last workgroup to finish a
 // (sequence, KV head) -- found with one device-scope atomic on an arrival counter, which it
 // resets to zero -- runs the top-k of that KV head's units, one wave per unit: the unit's
-// scores are loaded once into registers as order-preserving integer keys, an interpolation
-// search over the key range (counts of keys at or above a probe, VALU counts + one DPP
-// reduction per probe) finds the k-th largest key, and a ballot/popcount compaction writes the
-// selected blocks in ascending order (ties go to the lower block).
+// scores are loaded once into registers as order-preserving integer keys, a search over the
+// key range (first bracket from the scores' moments, then interpolation; each probe counts the
+// keys at or above it with one ballot popcount per register) finds the k-th largest key, and a
+// ballot/popcount compaction writes the selected blocks in ascending order (ties go to the lower
+// block).
 #include <algorithm>
 
 #include "common.h"
