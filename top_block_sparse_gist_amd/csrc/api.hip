@@ -260,6 +260,13 @@ sas_status sas_block_scores(const sas_problem *p, const void *Q, const int64_t q
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(SAS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
   if (need > 0 && !aligned16(workspace)) return fail(SAS_ERR_SHAPE, "workspace must be 16-byte aligned");
+  // the prefill score product addresses one (sequence, KV head) slab of representatives with
+  // 32-bit byte offsets
+  if ((int64_t)(cdiv(p->max_len, p->block) - 1) * rep_stride[2] * rep_bytes + (int64_t)p->head_dim * rep_bytes >
+      0xFFFFFFFFll)
+    return fail(SAS_ERR_UNSUPPORTED, "one (sequence, KV head) slab of representatives must span less than 4 GiB");
+  // and reads the pooled queries with 32-bit byte offsets
+  if (need > 0xFFFFF000ull) return fail(SAS_ERR_UNSUPPORTED, "the pooled queries must span less than 4 GiB");
   float *qbar = (float *)workspace;
   hipError_t e = launch_pool_queries(*p, tab, Q, q_stride, tq, sel_mode, qbar, s);
   if (e != hipSuccess) return hip_status(e, "sas_block_scores (pool)");

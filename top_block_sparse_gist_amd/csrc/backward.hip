@@ -67,10 +67,11 @@ __device__ __forceinline__ UnitGeo unit_geo(const SeqTable &st, int64_t u, int S
   return x;
 }
 
-// 64 rows of a K or V slab into a swizzled LDS tile: NW waves, 16 bytes per lane, rows past rlast
+// 64 rows of a K or V slab into a swizzled LDS tile at LDS byte address lds: NW waves, 16 bytes per
+// lane, rows past rlast
 // re-read row rlast (in bounds; their keys are masked).
 template <int D, int NW>
-__device__ __forceinline__ void copy_tile(__amdgpu_buffer_rsrc_t rs, uint16_t *lds, int key0, int rlast,
+__device__ __forceinline__ void copy_tile(i32x4 rs, uint32_t lds, int key0, int rlast,
                                           uint32_t row_bytes, int wave, int lane) {
   constexpr int CPR = D / 8, RPI = 64 / CPR, RPW = 64 / NW, NDMA = RPW / RPI;
   static_assert(NDMA >= 1, "rows per wave");
@@ -80,7 +81,7 @@ __device__ __forceinline__ void copy_tile(__amdgpu_buffer_rsrc_t rs, uint16_t *l
     const int row0 = wave * RPW + x * RPI;
     const int row = row0 + rin;
     const uint32_t roff = (uint32_t)min(key0 + row, rlast) * row_bytes;
-    buf_load_lds<16>(rs, lds + row0 * D, roff + (uint32_t)(cslot ^ swz<D>(row)) * 16u, 0u);
+    buf_load_lds<16>(rs, lds + 2u * (row0 * D), roff + (uint32_t)(cslot ^ swz<D>(row)) * 16u, 0u);
   }
 }
 
@@ -330,13 +331,13 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
   const float *glist = gate ? gate + u * kcap : nullptr;
   const uint32_t row_bytes = (uint32_t)(kt * 2);
   const uint32_t slab = (uint32_t)(L - 1) * row_bytes + D * 2;
-  const __amdgpu_buffer_rsrc_t krs = dev_rsrc(K + b * kb + ug.g * kh, slab);
-  const __amdgpu_buffer_rsrc_t vrs = dev_rsrc(V + b * kb + ug.g * kh, slab);
+  const i32x4 krs = lds_rsrc(K + b * kb + ug.g * kh, slab);
+  const i32x4 vrs = lds_rsrc(V + b * kb + ug.g * kh, slab);
   auto key0_of = [&](int tt) { return ulist[tt / tpb] * BLK + (tt % tpb) * 64; };
   auto load = [&](int tt, int buf, bool withv) {
     const int k0 = key0_of(tt);
-    copy_tile<D, NW>(krs, klds[buf], k0, L - 1, row_bytes, wave, lane);
-    if (withv) copy_tile<D, NW>(vrs, vlds[buf], k0, L - 1, row_bytes, wave, lane);
+    copy_tile<D, NW>(krs, lds_base(klds) + 2u * (buf * 64 * D), k0, L - 1, row_bytes, wave, lane);
+    if (withv) copy_tile<D, NW>(vrs, lds_base(vlds) + 2u * (buf * 64 * D), k0, L - 1, row_bytes, wave, lane);
   };
   // S^T of tile tt (two 32-key halves), keys past the row's position at -inf on the current block
   auto scores = [&](int tt, f32x16 *sacc) {
@@ -529,10 +530,10 @@ __global__ __launch_bounds__(BLK * 2, 2) void bwd_dkv_kernel(
   {
     const uint32_t row_bytes = (uint32_t)(kt * 2);
     const uint32_t slab = (uint32_t)(L - 1) * row_bytes + D * 2;
-    const __amdgpu_buffer_rsrc_t vrs = dev_rsrc(V + b * kb + (int64_t)g * kh, slab);
+    const i32x4 vrs = lds_rsrc(V + b * kb + (int64_t)g * kh, slab);
 #pragma unroll
     for (int t0 = 0; t0 < BLK; t0 += 64)
-      copy_tile<D, NWV>(vrs, vlds + t0 * D, key0 + t0, L - 1, row_bytes, wave, lane);
+      copy_tile<D, NWV>(vrs, lds_base(vlds) + 2u * (t0 * D), key0 + t0, L - 1, row_bytes, wave, lane);
   }
   bf16x8 kreg[NKK];
   {
@@ -615,15 +616,16 @@ __global__ __launch_bounds__(BLK * 2, 2) void bwd_dkv_kernel(
       int hh, tt;
       head_row(x, min(c0 + r, x.F - 1), hh, tt);
       const int off = 8 * (cs ^ swz<D>(r));
-      load_lds16(Q + b * qb + (int64_t)hh * qh + (int64_t)tt * qt + off, qs[buf] + 8 * (y * NT + wave * 64));
-      load_lds16(dO + b * ob + (int64_t)hh * oh + (int64_t)tt * ot + off, dos[buf] + 8 * (y * NT + wave * 64));
+      const uint32_t lo16 = 2u * (buf * 32 * D + 8 * (y * NT + wave * 64));
+      load_lds16(Q + b * qb + (int64_t)hh * qh + (int64_t)tt * qt + off, lds_base(qs) + lo16);
+      load_lds16(dO + b * ob + (int64_t)hh * oh + (int64_t)tt * ot + off, lds_base(dos) + lo16);
     }
     if (wave == 0) {
       int hh, tt;
       head_row(x, min(c0 + min(lane, 31), x.F - 1), hh, tt);
       const int64_t o = ((int64_t)b * hq + hh) * tq + tt;
-      load_lds<4>(lse_ws + o, lse_s[buf]);
-      load_lds<4>(dd_ws + o, dd_s[buf]);
+      load_lds<4>(lse_ws + o, lds_base(lse_s) + 4u * (buf * 64));
+      load_lds<4>(dd_ws + o, lds_base(dd_s) + 4u * (buf * 64));
     }
   };
 

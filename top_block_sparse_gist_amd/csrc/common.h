@@ -157,33 +157,72 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t *p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// 16 bytes per lane straight from global memory into LDS (global_load_lds_dwordx4): the wave
-// writes 64 x 16 B contiguously at `lds`, lane l at lds + 16 l.  Completion is tracked by vmcnt.
-__device__ __forceinline__ void load_lds16(const void *g, void *lds) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+// Copies from global memory straight into LDS (global_load_lds / buffer_load ... lds).
+// They are issued from inline asm.  The compiler treats a copy it emits itself as a store to LDS
+// that may alias every later LDS read, so it puts `s_waitcnt vmcnt` before those reads, and that
+// wait also covers the copies of the next tile.  A double-buffered loop then stalls on its own
+// prefetch every iteration.  The asm copies are invisible to that tracking.  Every kernel that
+// uses them therefore waits for its copies explicitly (s_waitcnt vmcnt, then a barrier) before it
+// reads the LDS they fill, and it lets no copy outlive the workgroup.  Waits the compiler places
+// for its own loads stay correct: the copies only add to the count of outstanding operations it
+// waits down to.  The copies have no register results, and the asm sets M0 (the LDS address;
+// one wait state before the copy reads it) and declares it clobbered.
+// LDS addresses are passed as integers: the byte address of a __shared__ array itself (lds_base,
+// a link-time constant) plus offsets computed as integers.  (Converting a pointer into such an
+// array at run time would go through a 64-bit generic address.)
+template <typename T>
+__device__ __forceinline__ uint32_t lds_base(T *shared_array) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)shared_array;
 }
 
-// BYTES (1, 2, 4, 12 or 16) per lane from global memory into LDS (global_load_lds): the wave
-// writes 64 x BYTES contiguously at `lds`, lane l at lds + l * BYTES.  Tracked by vmcnt.
+// 16 bytes per lane from global memory into LDS (global_load_lds_dwordx4): the wave writes 64 x
+// 16 B contiguously at LDS byte address `lds` (wave-uniform), lane l at lds + 16 l.  Tracked by vmcnt.
+__device__ __forceinline__ void load_lds16(const void *g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(__builtin_amdgcn_readfirstlane(lds)),
+               "v"(g)
+               : "memory", "m0");
+}
+
+// BYTES (4 or 16) per lane from global memory into LDS (global_load_lds): the wave writes 64 x
+// BYTES contiguously at LDS byte address `lds`, lane l at lds + l * BYTES.  Tracked by vmcnt.
 template <int BYTES>
-__device__ __forceinline__ void load_lds(const void *g, void *lds) {
-  // the size operand must be a literal
-  auto *l = (__attribute__((address_space(3))) void *)lds;
-  if constexpr (BYTES == 2) __builtin_amdgcn_global_load_lds(g, l, 2, 0, 0);
-  else if constexpr (BYTES == 4) __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
-  else __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+__device__ __forceinline__ void load_lds(const void *g, uint32_t lds) {
+  static_assert(BYTES == 4 || BYTES == 16, "4- or 16-byte copies");
+  if constexpr (BYTES == 4)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(__builtin_amdgcn_readfirstlane(lds)),
+                 "v"(g)
+                 : "memory", "m0");
+  else
+    load_lds16(g, lds);
 }
 
 // BYTES (4 or 16) per lane through a buffer resource into LDS (buffer_load ... lds): the wave
-// writes 64 x BYTES contiguously at `lds`, lane i at lds + BYTES * i; the lane reads
-// rsrc + soff + voff.  Row offsets can stay scalar (soff).  Tracked by vmcnt.  (2-byte copies
-// are not offered: a head-dim-64 prefill that used them read wrong values.)
+// writes 64 x BYTES contiguously at LDS byte address `lds`, lane i at lds + BYTES * i; the lane reads
+// rsrc + soff + voff, and an access past the resource's range writes zeros.  Row offsets can stay
+// scalar (soff).  Tracked by vmcnt.  (2-byte copies are not offered: a head-dim-64 prefill that
+// used them read wrong values.)
+// Buffer resource for these copies, in scalar registers: base address, no stride, `bytes` in range,
+// the same flags as dev_rsrc (words 0-3 of the descriptor).
+__device__ __forceinline__ i32x4 lds_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return i32x4{(int32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
+               (int32_t)(__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) & 0xffffu),
+               (int32_t)__builtin_amdgcn_readfirstlane(bytes), 0x00020000};
+}
 template <int BYTES>
-__device__ __forceinline__ void buf_load_lds(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voff, uint32_t soff) {
+__device__ __forceinline__ void buf_load_lds(i32x4 rv, uint32_t lds, uint32_t voff, uint32_t soff) {
   static_assert(BYTES == 4 || BYTES == 16, "4- or 16-byte copies");
-  auto *l = (__attribute__((address_space(3))) void *)lds;
-  if constexpr (BYTES == 4) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 4, voff, soff, 0, 0);
-  else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, voff, soff, 0, 0);
+  // the descriptor is wave-uniform; this keeps it in scalar registers whatever path formed it
+  const i32x4 r = {__builtin_amdgcn_readfirstlane(rv[0]), __builtin_amdgcn_readfirstlane(rv[1]),
+                   __builtin_amdgcn_readfirstlane(rv[2]), __builtin_amdgcn_readfirstlane(rv[3])};
+  if constexpr (BYTES == 4)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds" ::"s"(__builtin_amdgcn_readfirstlane(lds)),
+                 "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff))
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(__builtin_amdgcn_readfirstlane(lds)),
+                 "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff))
+                 : "memory", "m0");
 }
 
 // Sum over aligned groups of W lanes (W = 8, 16 or 32), valid in the group's first lane (lane %

@@ -69,13 +69,14 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
   //    copy instruction (4 bytes per lane).  On the per-head batches these run on, which are bound
   //    by L2 misses, it measured ~5 % faster than the swizzled copy.  (A D = 64 row would take
   //    2 bytes per lane, a copy width that does not land packed in LDS.)
-  constexpr bool SWZ = !SINGLE || D == 64;
+  constexpr bool SWZ = true;
   constexpr int ROWK = SWZ ? D : D + 8, ROWV = SWZ ? D : D + 32;
   constexpr int CPR = D / 8;         // 16-byte chunks per row
   constexpr int RPI = SWZ ? 64 / CPR : 1;  // rows per copy instruction
   constexpr int DMA = SWZ ? 16 : 4;  // bytes per lane of one copy instruction
   __shared__ __attribute__((aligned(16))) uint16_t klds2[NBUF][64 * ROWK];
   __shared__ __attribute__((aligned(16))) uint16_t vlds2[NBUF][64 * ROWV];
+  const uint32_t klds_a = lds_base(klds2), vlds_a = lds_base(vlds2);  // LDS byte addresses
   auto fK = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
   auto fV = [](int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); };
 
@@ -177,11 +178,11 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
   constexpr int NDMA = RPW / RPI;    // copy instructions per wave for one K (V) tile
   const uint32_t row_bytes = (uint32_t)(kt * 2);
   const uint32_t slab = (uint32_t)(L - 1) * row_bytes + D * 2;
-  const __amdgpu_buffer_rsrc_t krs = dev_rsrc(kbase, slab), vrs = dev_rsrc(vbase, slab);
+  const i32x4 krs = lds_rsrc(kbase, slab), vrs = lds_rsrc(vbase, slab);
   // Paged K/V (table != nullptr): block j lives in page table[b * tld + j] (kb is the page stride);
   // a tile's copies then take a resource over its page and rows counted inside the page.
   struct Src {
-    __amdgpu_buffer_rsrc_t k, v;
+    i32x4 k, v;
     int r0, rlast;  // the tile's first row and the last present row, from the resource's base
   };
   auto tile_src = [&](int t) {
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
     if (table) {
       const int64_t page = table[b * tld + j];
       const uint32_t pbytes = (uint32_t)(BLK - 1) * row_bytes + D * 2;
-      return Src{dev_rsrc(K + page * kb + g * kh, pbytes), dev_rsrc(V + page * kb + g * kh, pbytes),
+      return Src{lds_rsrc(K + page * kb + g * kh, pbytes), lds_rsrc(V + page * kb + g * kh, pbytes),
                  (t % tpb) * 64, min(BLK, L - j * BLK) - 1};
     }
     return Src{krs, vrs, j * BLK + (t % tpb) * 64, L - 1};
@@ -208,8 +209,8 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
         for (int x = 0; x < NDMA; ++x) {
           const int row0 = wave * RPW + x * RPI;  // wave-uniform
           const uint32_t soff = (uint32_t)(key0 + row0) * row_bytes;
-          if (k) buf_load_lds<16>(sr.k, &klds2[buf][row0 * D], lrow + (uint32_t)(kx ^ fK(row0)) * 16u, soff);
-          if (v) buf_load_lds<16>(sr.v, &vlds2[buf][row0 * D], voff_v, soff);
+          if (k) buf_load_lds<16>(sr.k, klds_a + 2u * (buf * 64 * ROWK + row0 * D), lrow + (uint32_t)(kx ^ fK(row0)) * 16u, soff);
+          if (v) buf_load_lds<16>(sr.v, vlds_a + 2u * (buf * 64 * ROWV + row0 * D), voff_v, soff);
         }
       } else {
 #pragma unroll
@@ -217,8 +218,8 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
           const int row0 = wave * RPW + x * RPI;
           const int row = row0 + rin;
           const uint32_t roff = (uint32_t)min(key0 + row, sr.rlast) * row_bytes;
-          if (k) buf_load_lds<16>(sr.k, &klds2[buf][row0 * D], roff + (uint32_t)(cslot ^ fK(row)) * 16u, 0u);
-          if (v) buf_load_lds<16>(sr.v, &vlds2[buf][row0 * D], roff + (uint32_t)(cslot ^ fV(row)) * 16u, 0u);
+          if (k) buf_load_lds<16>(sr.k, klds_a + 2u * (buf * 64 * ROWK + row0 * D), roff + (uint32_t)(cslot ^ fK(row)) * 16u, 0u);
+          if (v) buf_load_lds<16>(sr.v, vlds_a + 2u * (buf * 64 * ROWV + row0 * D), roff + (uint32_t)(cslot ^ fV(row)) * 16u, 0u);
         }
       }
     } else {
@@ -226,8 +227,8 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
       for (int x = 0; x < RPW; ++x) {
         const int row = wave + x * NW;
         const uint32_t soff = (uint32_t)min(key0 + row, sr.rlast) * row_bytes;
-        if (k) buf_load_lds<DMA>(sr.k, &klds2[buf][row * ROWK], lane * DMA, soff);
-        if (v) buf_load_lds<DMA>(sr.v, &vlds2[buf][row * ROWV], lane * DMA, soff);
+        if (k) buf_load_lds<DMA>(sr.k, klds_a + 2u * (buf * 64 * ROWK + row * ROWK), lane * DMA, soff);
+        if (v) buf_load_lds<DMA>(sr.v, vlds_a + 2u * (buf * 64 * ROWV + row * ROWV), lane * DMA, soff);
       }
     }
   };

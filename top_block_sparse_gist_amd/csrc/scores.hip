@@ -10,6 +10,8 @@
 // Decode : score_decode_kernel pools the (<= 16) query vectors of each unit in LDS and
 //          streams one 64-block tile of representatives per workgroup (HBM-bound GEMV).
 // Only entries j <= c(u) are written.
+#include <algorithm>
+
 #include "common.h"
 
 namespace sas {
@@ -80,137 +82,191 @@ __global__ __launch_bounds__(256) void pool_kernel(SeqTable st, const T *__restr
 }
 
 // ------------------------------------------------------------------------------------------
-// qbar x R^T, 64 units x 64 blocks per workgroup, fp32 FMA (4x4 outputs per lane)
+// qbar x R^T per (sequence, KV head), fp32 on v_mfma_f32_32x32x2_f32.
+// Work items are (sequence, KV head, range of 64 blocks, chunk of 32 units), in that order.  The
+// grid is one workgroup per resident slot, and workgroup k takes an equal contiguous run of the
+// items (XCD x holds the x-th eighth of them, so a pair's units stay in one L2).  A workgroup has
+// two waves; wave w keeps the representatives of blocks 32w.. of the current range in registers
+// (the B operand, reloaded when the run moves to the next range) and forms their scores against
+// the chunk's units.  The units' qbar rows stream through LDS: the next item's chunk is copied
+// HBM -> LDS by the buffer unit while this one is multiplied (two buffers, one barrier per item),
+// and an item's scores are stored during the next item, so no wait covers a store.  The d index of
+// each MFMA is permuted so that a lane reads 4 consecutive elements with one 16-byte load (B from
+// global memory, A from LDS): MFMA 4a + e takes, in k-slot s = lane / 32, element 8a + 4s + e of
+// both operands.  A score is a sum of d products in an order fixed by that permutation; the
+// oracle's bound (1e-5 relative to the largest score) holds for any order.  LDS rows are stored
+// unpadded with their 16-byte chunks XOR-swizzled by (row & 7), so the A reads of 8 consecutive
+// rows at one logical chunk fall on distinct banks.
 // ------------------------------------------------------------------------------------------
+constexpr int SCORE_UNITS = 32;  // units per chunk
+constexpr int SCORE_RANGE = 64;  // blocks per range (two waves of 32)
+
+// first item of each sequence (over its KV heads, ranges and chunks); off[batch] = all items
+struct ScoreItems {
+  int32_t off[SAS_MAX_BATCH + 1];
+};
+
 template <typename R, int D>
-__global__ __launch_bounds__(256) void score_gemm_kernel(SeqTable st, const float *__restrict__ qbar,
-                                                         const R *__restrict__ reps, int64_t rb,
-                                                         int64_t rh, int64_t rj, int gist, int tq,
-                                                         int blk, int S, int QB, int G, int per_head,
-                                                         int hkv, float scale,
-                                                         float *__restrict__ scores, int64_t ld) {
-  constexpr int KC = 32;  // d chunk
-  __shared__ float As[KC][64 + 4];
-  __shared__ float Bs[KC][64 + 4];
-  const int b = blockIdx.z / hkv, g = blockIdx.z % hkv;
-  const int L = st.len[b];
-  const int q0 = st.q0[b];
-  const int c0 = q0 / blk;
-  const int nqb = (q0 + tq - 1) / blk - c0 + 1;
+__global__ __launch_bounds__(128, 2) void score_gemm_kernel(SeqTable st, ScoreItems items, const float *__restrict__ qbar,
+                                                            uint32_t qbar_bytes, const R *__restrict__ reps,
+                                                            int64_t rb, int64_t rh, int64_t rj, int gist,
+                                                            int tq, int blk, int S, int QB, int G, int per_head,
+                                                            int hkv, int batch, float scale,
+                                                            float *__restrict__ scores, int64_t ld) {
+  constexpr int CPR = D / 4;                             // 16-byte chunks per qbar row
+  constexpr int NCP = SCORE_UNITS * D * 4 / 1024 / 2;    // 1 KiB copies per wave per chunk
+  __shared__ __attribute__((aligned(16))) float abuf[2][SCORE_UNITS * D];
+  __shared__ int64_t trow[3][SCORE_UNITS];  // score row of each unit of an item's chunk (three slots)
+  __shared__ int32_t tcur[3][SCORE_UNITS];  // its current block (-1: no unit)
+  // this workgroup's run of items: XCD x = n % 8 takes the x-th eighth
+  const int per = gridDim.x >> 3;
+  const int run = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  const int T = items.off[batch];
+  const int it1 = (int)((int64_t)(run + 1) * T / gridDim.x);
+  int it = (int)((int64_t)run * T / gridDim.x);
   const int nU = per_head ? G : 1;
-  const int M = nU * nqb;
-  const int m0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
-  if (m0 >= M) return;
-  // largest current block among this tile's units
-  int cmax = 0;
-  {
-    int mlast = min(M, m0 + 64) - 1;
-    int ilo = m0 % nqb, ihi = mlast % nqb;
-    cmax = (mlast / nqb != m0 / nqb) ? c0 + nqb - 1 : c0 + max(ilo, ihi);
-  }
-  if (j0 > cmax) return;
-  const int nrep = gist ? L / blk : cdiv(L, blk);
-  const int tid = threadIdx.x;
-  // wave w owns the 32 x 32 output block (units mw.., blocks nw..) of the 64 x 64 tile, formed with
-  // v_mfma_f32_32x32x2_f32: lane l supplies A[unit mw + l % 32][dim k + l / 32] and
-  // B[dim k + l / 32][block nw + l % 32]; register r of its result is unit mw + 8 (r / 4) + 4 (l / 32)
-  // + r % 4, block nw + l % 32.  A wave whose units all lie past M skips the products.
-  const int wave = tid >> 6, lane = tid & 63;
-  const int mw = 32 * (wave >> 1), nw = 32 * (wave & 1);
-  const bool wave_live = m0 + mw < M;
 
-  auto unit_row = [&](int m) -> int64_t {
-    int sl = m / nqb, i = m % nqb;
-    int s = per_head ? g * G + sl : g;
-    return ((int64_t)b * S + s) * QB + i;
+  struct Item {
+    int it, b, g, r, ch, c0, nqb, M, nrep, j0, cmax;
   };
+  // item geometry; cmax: the largest current block among the chunk's units (the item is dead when
+  // it is below the range's first block)
+  auto geo = [&](int x) {
+    Item a;
+    a.it = x;
+    int b = 0;
+    while (items.off[b + 1] <= x) ++b;
+    const int q0 = st.q0[b];
+    a.b = b;
+    a.c0 = q0 / blk;
+    a.nqb = (q0 + tq - 1) / blk - a.c0 + 1;
+    a.M = nU * a.nqb;
+    a.nrep = gist ? st.len[b] / blk : cdiv(st.len[b], blk);
+    const int nr = (a.c0 + a.nqb - 1) / SCORE_RANGE + 1, nch = cdiv(a.M, SCORE_UNITS);
+    int rem = x - items.off[b];
+    a.g = rem / (nr * nch);
+    rem -= a.g * nr * nch;
+    a.r = rem / nch;
+    a.ch = rem - a.r * nch;
+    a.j0 = a.r * SCORE_RANGE;
+    const int lo = a.ch * SCORE_UNITS, last = min(a.M, lo + SCORE_UNITS) - 1;
+    a.cmax = (last / a.nqb != lo / a.nqb) ? a.c0 + a.nqb - 1 : a.c0 + max(lo % a.nqb, last % a.nqb);
+    return a;
+  };
+  auto next_live = [&](int x) {
+    Item a;
+    a.it = -1;
+    for (; x < it1; ++x) {
+      a = geo(x);
+      if (a.cmax >= a.j0) return a;
+    }
+    a.it = -1;
+    return a;
+  };
+  Item cur = next_live(it);
+  if (cur.it < 0) return;
 
-  f32x16 acc;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ks = lane >> 5, l32 = lane & 31;
+  // qbar through a range-checked buffer resource: a unit past M reads zeros
+  const i32x4 qrs = lds_rsrc(qbar, qbar_bytes);
+  // table slot `slot` and LDS buffer `buf` take item a's chunk: lane l32 forms unit 32 ch + l32's
+  // row; the copy lanes fetch their rows' chunks from it (the LDS chunk (row, cl) holds qbar
+  // chunk cl ^ (row & 7))
+  auto prep = [&](const Item &a, int slot, int buf) {
+    const int m = a.ch * SCORE_UNITS + l32;
+    const bool ok = m < a.M;
+    int64_t ur = 0;
+    if (ok) {
+      const int sl = m / a.nqb, i = m - sl * a.nqb;
+      const int sh = per_head ? a.g * G + sl : a.g;
+      ur = ((int64_t)a.b * S + sh) * QB + i;
+    }
+    if (wave == 0 && ks == 0) {
+      trow[slot][l32] = ur;
+      tcur[slot][l32] = ok ? a.c0 + m % a.nqb : -1;
+    }
+    // a unit past M reads at the end of qbar: out of range, zeros
+    const uint32_t boff = ok ? (uint32_t)(ur * (D * 4)) : qbar_bytes;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    for (int i = 0; i < NCP; ++i) {
+      const int e = (wave * NCP + i) * 64 + lane;
+      const int row = e / CPR, cl = e % CPR;
+      const uint32_t voff = (uint32_t)__shfl((int)boff, row, 64) + 16u * (cl ^ (row & 7));
+      buf_load_lds<16>(qrs, lds_base(abuf) + 4u * (buf * SCORE_UNITS * D + (wave * NCP + i) * 256), voff, 0u);
+    }
+  };
+  // B operand of item a's range: bf[4a + e] = rep[j0 + 32 wave + l32][8a + 4 ks + e] (0 past the
+  // representatives)
+  float bf[D / 2];
+  auto load_b = [&](const Item &a) {
+    const int j = a.j0 + 32 * wave + l32;
+    const bool ok = j < a.nrep;
+    const R *rrow = reps + a.b * rb + a.g * rh + (ok ? (int64_t)j * rj : 0) + 4 * ks;
+#pragma unroll
+    for (int x = 0; x < D / 8; ++x) {
+      if constexpr (sizeof(R) == 4) {
+        const f32x4 v = ok ? *reinterpret_cast<const f32x4 *>(rrow + 8 * x) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bf[4 * x + e] = v[e];
+      } else {
+        const u32x2 v = ok ? *reinterpret_cast<const u32x2 *>(rrow + 8 * x) : u32x2{0u, 0u};
+        bf[4 * x + 0] = bf16_lo(v[0]);
+        bf[4 * x + 1] = bf16_hi(v[0]);
+        bf[4 * x + 2] = bf16_lo(v[1]);
+        bf[4 * x + 3] = bf16_hi(v[1]);
+      }
+    }
+  };
+  prep(cur, 0, 0);
+  load_b(cur);
 
-  // the next d chunk's global loads are issued into registers before this chunk's products, so
-  // they fly during them (each product still sums its d terms in order 0..D-1)
-  const R *rbase = reps + b * rb + g * rh;
-  auto load_a = [&](int k0, f32x4 (&ra)[2]) {
+  // scores of the item whose chunk is in table slot `slot` (lane: block j, units 8 (r / 4) + 4 ks +
+  // r % 4 of the chunk)
+  auto store = [&](const f32x16 &acc, int slot, int j, int nrep) {
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      const int e = tid + w * 256;  // 64 units x 8 float4
-      const int m = m0 + e / 8, kq = (e % 8) * 4;
-      ra[w] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (m < M) ra[w] = *reinterpret_cast<const f32x4 *>(qbar + unit_row(m) * D + k0 + kq);
+    for (int rr = 0; rr < 16; ++rr) {
+      const int ml = 8 * (rr >> 2) + 4 * ks + (rr & 3);
+      const int c = tcur[slot][ml];
+      // gist keys exist for the complete chunks before the current one only
+      const int have = gist ? min(nrep, c) : nrep;
+      if (j <= c) scores[trow[slot][ml] * ld + j] = (j < have) ? acc[rr] * scale : -INFINITY;
     }
   };
-  auto load_b = [&](int k0, u32x4 (&rv)[2]) {
-    if constexpr (sizeof(R) == 4) {
+  f32x16 pacc;
+  int pslot = -1, pj = 0, pnrep = 0;
+  for (int k = 0; cur.it >= 0; ++k) {
+    const int buf = k & 1, slot = k % 3;
+    wait_vmcnt<0>();
+    __syncthreads();  // the item's chunk and B are in place; the other buffer and the oldest slot are free
+    const Item nx = next_live(cur.it + 1);
+    if (nx.it >= 0) prep(nx, (k + 1) % 3, buf ^ 1);
+    if (pslot >= 0) store(pacc, pslot, pj, pnrep);
+    pslot = -1;
+    const int js = cur.j0 + 32 * wave;
+    if (js <= cur.cmax) {  // some unit of the chunk reaches this wave's blocks
+      f32x16 acc;
 #pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        const int e = tid + w * 256;  // 64 reps x 8 float4
-        const int j = j0 + e / 8, kq = (e % 8) * 4;
-        rv[w] = u32x4{0u, 0u, 0u, 0u};
-        if (j < nrep) rv[w] = *reinterpret_cast<const u32x4 *>(rbase + (int64_t)j * rj + k0 + kq);
+      for (int rr = 0; rr < 16; ++rr) acc[rr] = 0.f;
+      const float *arow = &abuf[buf][l32 * D];
+      const int sw = l32 & 7;
+#pragma unroll
+      for (int x = 0; x < D / 8; ++x) {
+        const f32x4 av = *reinterpret_cast<const f32x4 *>(arow + 4 * ((2 * x + ks) ^ sw));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[e], bf[4 * x + e], acc, 0, 0, 0);
       }
-    } else {
-      const int j = j0 + tid / 4, kq = (tid % 4) * 8;  // 64 reps x 4 chunks of 8 bf16
-      rv[0] = u32x4{0u, 0u, 0u, 0u};
-      if (j < nrep) rv[0] = *reinterpret_cast<const u32x4 *>(rbase + (int64_t)j * rj + k0 + kq);
+      pacc = acc;
+      pslot = slot;
+      pj = js + l32;
+      pnrep = cur.nrep;
     }
-  };
-  f32x4 ra[2];
-  u32x4 rv[2];
-  load_a(0, ra);
-  load_b(0, rv);
-  for (int k0 = 0; k0 < D; k0 += KC) {
-    // A tile: 64 units x 32 dims; B tile: 64 reps x 32 dims (transposed into LDS)
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      const int e = tid + w * 256;
-      const int mm = e / 8, kq = (e % 8) * 4;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) As[kq + x][mm] = ra[w][x];
-    }
-    if constexpr (sizeof(R) == 4) {
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        const int e = tid + w * 256;
-        const int jj = e / 8, kq = (e % 8) * 4;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) Bs[kq + x][jj] = __uint_as_float(rv[w][x]);
-      }
-    } else {
-      const int jj = tid / 4, kq = (tid % 4) * 8;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        Bs[kq + 2 * x][jj] = bf16_lo(rv[0][x]);
-        Bs[kq + 2 * x + 1][jj] = bf16_hi(rv[0][x]);
-      }
-    }
-    __syncthreads();
-    if (k0 + KC < D) {
-      load_a(k0 + KC, ra);
-      load_b(k0 + KC, rv);
-    }
-    if (wave_live) {
-#pragma unroll
-      for (int k = 0; k < KC; k += 2) {
-        const float a = As[k + (lane >> 5)][mw + (lane & 31)];
-        const float bb = Bs[k + (lane >> 5)][nw + (lane & 31)];
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bb, acc, 0, 0, 0);
-      }
-    }
-    __syncthreads();
+    // the next item's range: its representatives replace these (in flight until the next barrier)
+    if (nx.it >= 0 && (nx.b != cur.b || nx.g != cur.g || nx.r != cur.r)) load_b(nx);
+    cur = nx;
   }
-  if (!wave_live) return;
-  const int j = j0 + nw + (lane & 31);
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int m = m0 + mw + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-    if (m >= M) continue;
-    const int c = c0 + m % nqb;
-    // gist keys exist for the complete chunks before the current one only
-    const int have = gist ? min(nrep, c) : nrep;
-    if (j <= c) scores[unit_row(m) * ld + j] = (j < have) ? acc[r] * scale : -INFINITY;
-  }
+  if (pslot >= 0) store(pacc, pslot, pj, pnrep);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -316,6 +372,19 @@ hipError_t launch_pool_queries(const sas_problem &p, const SeqTable &st, const v
                            : pool_dispatch<float, 64>(p, st, Q, qs, tq, sel_mode, qbar, s);
 }
 
+// resident workgroup slots of the score product on the current device (four per CU: LDS-bound)
+static int score_slots() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (!cached[dev]) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cached[dev] = 4 * cus;
+  }
+  return cached[dev];
+}
+
 template <typename R, int D>
 static hipError_t gemm_dispatch(const sas_problem &p, const SeqTable &st, const float *qbar,
                                 int32_t tq, const void *reps, int gist, const int64_t *rs,
@@ -325,12 +394,26 @@ static hipError_t gemm_dispatch(const sas_problem &p, const SeqTable &st, const 
   const int per_head = sel_mode == SAS_SEL_HEAD;
   const int S = per_head ? p.hq : p.hkv;
   const int G = p.hq / p.hkv;
-  int nbmax = 0;
-  for (int b = 0; b < p.batch; ++b) nbmax = max(nbmax, cdiv(st.len[b], p.block));
-  const int M = (per_head ? G : 1) * QB;
-  dim3 grid(cdiv(nbmax, 64), cdiv(M, 64), p.batch * p.hkv);
-  hipLaunchKernelGGL((score_gemm_kernel<R, D>), grid, dim3(256), 0, s, st, qbar, (const R *)reps, rs[0],
-                     rs[1], rs[2], gist, tq, p.block, S, QB, G, per_head, p.hkv, scale, scores, ld);
+  const int nU = per_head ? G : 1;
+  // items per sequence: KV heads x ranges of 64 blocks (up to the last unit's current block) x
+  // chunks of 32 units
+  ScoreItems items{};
+  int64_t T = 0;
+  for (int b = 0; b < p.batch; ++b) {
+    const int q0 = st.q0[b], c0 = q0 / p.block;
+    const int nqb = (q0 + tq - 1) / p.block - c0 + 1;
+    const int nr = (c0 + nqb - 1) / SCORE_RANGE + 1;
+    items.off[b] = (int32_t)T;
+    T += (int64_t)p.hkv * nr * cdiv(nU * nqb, SCORE_UNITS);
+  }
+  if (T > 0x7fffffff) return hipErrorInvalidConfiguration;
+  items.off[p.batch] = (int32_t)T;
+  // one workgroup per slot (a multiple of 8: the eighths of the item list go to the 8 XCDs)
+  const int64_t nwg = std::min<int64_t>(8 * cdiv64(T, 8), 8 * (score_slots() / 8));
+  const uint32_t qbar_bytes = (uint32_t)((int64_t)p.batch * S * QB * D * 4);
+  hipLaunchKernelGGL((score_gemm_kernel<R, D>), dim3((unsigned)nwg), dim3(128), 0, s, st, items, qbar, qbar_bytes,
+                     (const R *)reps, rs[0], rs[1], rs[2], gist, tq, p.block, S, QB, G, per_head, p.hkv, p.batch,
+                     scale, scores, ld);
   return hipGetLastError();
 }
 
