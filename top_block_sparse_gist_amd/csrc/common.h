@@ -167,6 +167,9 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t *p) {
 // for its own loads stay correct: the copies only add to the count of outstanding operations it
 // waits down to.  The copies have no register results, and the asm sets M0 (the LDS address;
 // one wait state before the copy reads it) and declares it clobbered.
+// M0 is named as clobbered on purpose (each copy sets it); clang warns that it is reserved.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 // LDS addresses are passed as integers: the byte address of a __shared__ array itself (lds_base,
 // a link-time constant) plus offsets computed as integers.  (Converting a pointer into such an
 // array at run time would go through a 64-bit generic address.)
@@ -224,6 +227,7 @@ __device__ __forceinline__ void buf_load_lds(i32x4 rv, uint32_t lds, uint32_t vo
                  "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff))
                  : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // Sum over aligned groups of W lanes (W = 8, 16 or 32), valid in the group's first lane (lane %
 // W == 0).  Within a 16-lane row the adds use DPP (quad xor 1, quad xor 2, then row rotates: a
