@@ -83,10 +83,10 @@ __global__ __launch_bounds__(256) void pool_kernel(SeqTable st, const T *__restr
 
 // ------------------------------------------------------------------------------------------
 // qbar x R^T per (sequence, KV head), fp32 on v_mfma_f32_32x32x2_f32.
-// Work items are (sequence, KV head, range of 64 blocks, chunk of 32 units), in that order.  The
+// Work items are (sequence, KV head, range of 128 blocks, chunk of 32 units), in that order.  The
 // grid is one workgroup per resident slot, and workgroup k takes an equal contiguous run of the
 // items (XCD x holds the x-th eighth of them, so a pair's units stay in one L2).  A workgroup has
-// two waves; wave w keeps the representatives of blocks 32w.. of the current range in registers
+// four waves; wave w keeps the representatives of blocks 32w.. of the current range in registers
 // (the B operand, reloaded when the run moves to the next range) and forms their scores against
 // the chunk's units.  The units' qbar rows stream through LDS: the next item's chunk is copied
 // HBM -> LDS by the buffer unit while this one is multiplied (two buffers, one barrier per item),
@@ -98,8 +98,9 @@ __global__ __launch_bounds__(256) void pool_kernel(SeqTable st, const T *__restr
 // unpadded with their 16-byte chunks XOR-swizzled by (row & 7), so the A reads of 8 consecutive
 // rows at one logical chunk fall on distinct banks.
 // ------------------------------------------------------------------------------------------
-constexpr int SCORE_UNITS = 32;  // units per chunk
-constexpr int SCORE_RANGE = 64;  // blocks per range (two waves of 32)
+constexpr int SCORE_UNITS = 32;                  // units per chunk
+constexpr int SCORE_WAVES = 4;                   // waves per workgroup, 32 blocks each
+constexpr int SCORE_RANGE = 32 * SCORE_WAVES;    // blocks per range
 
 // first item of each sequence (over its KV heads, ranges and chunks); off[batch] = all items
 struct ScoreItems {
@@ -107,14 +108,15 @@ struct ScoreItems {
 };
 
 template <typename R, int D>
-__global__ __launch_bounds__(128, 2) void score_gemm_kernel(SeqTable st, ScoreItems items, const float *__restrict__ qbar,
+__global__ __launch_bounds__(64 * SCORE_WAVES, 3) void score_gemm_kernel(SeqTable st, ScoreItems items, const float *__restrict__ qbar,
                                                             uint32_t qbar_bytes, const R *__restrict__ reps,
                                                             int64_t rb, int64_t rh, int64_t rj, int gist,
                                                             int tq, int blk, int S, int QB, int G, int per_head,
                                                             int hkv, int batch, float scale,
                                                             float *__restrict__ scores, int64_t ld) {
   constexpr int CPR = D / 4;                             // 16-byte chunks per qbar row
-  constexpr int NCP = SCORE_UNITS * D * 4 / 1024 / 2;    // 1 KiB copies per wave per chunk
+  constexpr int NCP = SCORE_UNITS * D * 4 / 1024 / SCORE_WAVES;  // 1 KiB copies per wave per chunk
+  static_assert(NCP >= 1, "each wave copies whole KiB");
   __shared__ __attribute__((aligned(16))) float abuf[2][SCORE_UNITS * D];
   __shared__ int64_t trow[3][SCORE_UNITS];  // score row of each unit of an item's chunk (three slots)
   __shared__ int32_t tcur[3][SCORE_UNITS];  // its current block (-1: no unit)
@@ -372,7 +374,8 @@ hipError_t launch_pool_queries(const sas_problem &p, const SeqTable &st, const v
                            : pool_dispatch<float, 64>(p, st, Q, qs, tq, sel_mode, qbar, s);
 }
 
-// resident workgroup slots of the score product on the current device (four per CU: LDS-bound)
+// resident workgroup slots of the score product on the current device (four per CU: 34 KB of LDS and
+// 128 VGPRs each)
 static int score_slots() {
   static int cached[64] = {0};
   int dev = 0;
@@ -395,7 +398,7 @@ static hipError_t gemm_dispatch(const sas_problem &p, const SeqTable &st, const 
   const int S = per_head ? p.hq : p.hkv;
   const int G = p.hq / p.hkv;
   const int nU = per_head ? G : 1;
-  // items per sequence: KV heads x ranges of 64 blocks (up to the last unit's current block) x
+  // items per sequence: KV heads x ranges of 128 blocks (up to the last unit's current block) x
   // chunks of 32 units
   ScoreItems items{};
   int64_t T = 0;
@@ -411,7 +414,7 @@ static hipError_t gemm_dispatch(const sas_problem &p, const SeqTable &st, const 
   // one workgroup per slot (a multiple of 8: the eighths of the item list go to the 8 XCDs)
   const int64_t nwg = std::min<int64_t>(8 * cdiv64(T, 8), 8 * (score_slots() / 8));
   const uint32_t qbar_bytes = (uint32_t)((int64_t)p.batch * S * QB * D * 4);
-  hipLaunchKernelGGL((score_gemm_kernel<R, D>), dim3((unsigned)nwg), dim3(128), 0, s, st, items, qbar, qbar_bytes,
+  hipLaunchKernelGGL((score_gemm_kernel<R, D>), dim3((unsigned)nwg), dim3(64 * SCORE_WAVES), 0, s, st, items, qbar, qbar_bytes,
                      (const R *)reps, rs[0], rs[1], rs[2], gist, tq, p.block, S, QB, G, per_head, p.hkv, p.batch,
                      scale, scores, ld);
   return hipGetLastError();
