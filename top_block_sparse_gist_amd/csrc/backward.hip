@@ -40,12 +40,18 @@ constexpr float LOG2E = 1.4426950408889634f;
 __device__ __forceinline__ bf16x8 as_bf8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // XOR swizzle of the 16-byte chunks of an LDS row (rows of D bf16, unpadded): row-operand reads
-// (16 rows at one chunk) and transposing reads (4 rows x 2 chunks) stay spread over the banks.
-template <int D>
+// (16 consecutive rows at one logical chunk) stay on distinct banks.  TR: the tile is also read by
+// transposing reads (4 consecutive rows, 4-row aligned, over one aligned group of 4 chunks).  At
+// D = 128 (16 chunks per row, a row per pass of the 64 banks) that swizzle sends the low two row
+// bits to the chunk's high two bits and the next two row bits to its low two bits, so 4 aligned
+// rows also move an aligned 4-chunk group to 4 distinct groups (r & 15 puts them on one group:
+// four-way bank conflicts).  The dK/dV kernel's staged rows take it; in the dQ kernel the extra
+// address arithmetic spilled registers and cost more than the conflicts it removed.
+template <int D, bool TR = false>
 __device__ __forceinline__ int swz(int r) {
-  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+  if constexpr (D == 128) return TR ? (((r & 3) << 2) | ((r >> 2) & 3)) : (r & 15);
+  return (r >> 1) & 7;
 }
-
 // Geometry of selection unit u = (b * S + s) * QB + i.
 struct UnitGeo {
   int b, s, i, c, t_lo, rows, h0, nh, g;
@@ -70,7 +76,7 @@ __device__ __forceinline__ UnitGeo unit_geo(const SeqTable &st, int64_t u, int S
 // 64 rows of a K or V slab into a swizzled LDS tile at LDS byte address lds: NW waves, 16 bytes per
 // lane, rows past rlast
 // re-read row rlast (in bounds; their keys are masked).
-template <int D, int NW>
+template <int D, int NW, bool TR = false>
 __device__ __forceinline__ void copy_tile(i32x4 rs, uint32_t lds, int key0, int rlast,
                                           uint32_t row_bytes, int wave, int lane) {
   constexpr int CPR = D / 8, RPI = 64 / CPR, RPW = 64 / NW, NDMA = RPW / RPI;
@@ -81,7 +87,7 @@ __device__ __forceinline__ void copy_tile(i32x4 rs, uint32_t lds, int key0, int 
     const int row0 = wave * RPW + x * RPI;
     const int row = row0 + rin;
     const uint32_t roff = (uint32_t)min(key0 + row, rlast) * row_bytes;
-    buf_load_lds<16>(rs, lds + 2u * (row0 * D), roff + (uint32_t)(cslot ^ swz<D>(row)) * 16u, 0u);
+    buf_load_lds<16>(rs, lds + 2u * (row0 * D), roff + (uint32_t)(cslot ^ swz<D, TR>(row)) * 16u, 0u);
   }
 }
 
@@ -124,11 +130,11 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t *lds, int ks, int dt
 //   row[kk]: chunk 2kk + half of row `col` (rows_dot's read with row0 = 0; the same offsets serve
 //            row0 = 32w, since the swizzle of row 32w + col is that of row col)
 //   tlo[dt], thi[dt]: tr_operand's two reads at ks = 0 (ks adds 16 ks rows)
-template <int D>
+template <int D, bool TR = false>
 struct LdsOffsets {
   int row[D / 16], tlo[D / 32], thi[D / 32];
   __device__ __forceinline__ LdsOffsets(int col, int half) {
-    const int f = swz<D>(col);
+    const int f = swz<D, TR>(col);
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) row[kk] = col * D + 8 * ((2 * kk + half) ^ f);
     const int c16 = col & 15, chi = col >> 4;
@@ -137,8 +143,8 @@ struct LdsOffsets {
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
       const int chunk = 4 * dt + 2 * chi + ((c16 & 3) >> 1);
-      tlo[dt] = rlo * D + 8 * (chunk ^ swz<D>(rlo)) + sub;
-      thi[dt] = rhi * D + 8 * (chunk ^ swz<D>(rhi)) + sub;
+      tlo[dt] = rlo * D + 8 * (chunk ^ swz<D, TR>(rlo)) + sub;
+      thi[dt] = rhi * D + 8 * (chunk ^ swz<D, TR>(rhi)) + sub;
     }
   }
 };
@@ -533,7 +539,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void bwd_dkv_kernel(
     const i32x4 vrs = lds_rsrc(V + b * kb + (int64_t)g * kh, slab);
 #pragma unroll
     for (int t0 = 0; t0 < BLK; t0 += 64)
-      copy_tile<D, NWV>(vrs, lds_base(vlds) + 2u * (t0 * D), key0 + t0, L - 1, row_bytes, wave, lane);
+      copy_tile<D, NWV, true>(vrs, lds_base(vlds) + 2u * (t0 * D), key0 + t0, L - 1, row_bytes, wave, lane);
   }
   bf16x8 kreg[NKK];
   {
@@ -615,7 +621,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void bwd_dkv_kernel(
       const int r = e / CPR, cs = e % CPR;
       int hh, tt;
       head_row(x, min(c0 + r, x.F - 1), hh, tt);
-      const int off = 8 * (cs ^ swz<D>(r));
+      const int off = 8 * (cs ^ swz<D, true>(r));
       const uint32_t lo16 = 2u * (buf * 32 * D + 8 * (y * NT + wave * 64));
       load_lds16(Q + b * qb + (int64_t)hh * qh + (int64_t)tt * qt + off, lds_base(qs) + lo16);
       load_lds16(dO + b * ob + (int64_t)hh * oh + (int64_t)tt * ot + off, lds_base(dos) + lo16);
@@ -635,7 +641,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void bwd_dkv_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) adk[x][r] = adv[x][r] = 0.f;
 
-  const LdsOffsets<D> lo(col, half);
+  const LdsOffsets<D, true> lo(col, half);
   __syncthreads();  // mu, mgl visible
   int k = 0, c0 = 0, buf = 0;
   if (cnt > 0) stage(0, 0, 0);
