@@ -588,7 +588,13 @@ def main():
                                  "achieved": round(tf_att, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                  "frac": round(tf_att / BF16_PEAK_TFLOPS, 4), "traffic": tr_p["bytes"] if tr_p else None,
                                  "flops_per_launch": fl["flops"], "avg_launch_ms": round(t_pf_att, 5),
-                                 "traffic_detail": tr_p},
+                                 "traffic_detail": tr_p,
+                                 # the bandwidth roof that the kernel's measured traffic implies (its FLOP per
+                                 # HBM byte x 8 TB/s), and the fraction of that roof reached
+                                 "traffic_roof": ({"flop_per_byte": round(fl["flops"] / tr_p["bytes"], 2),
+                                                   "roof_TFLOP/s": round(fl["flops"] / tr_p["bytes"] * HBM_PEAK_GBS / 1e3, 1),
+                                                   "frac": round(tf_att / (fl["flops"] / tr_p["bytes"] * HBM_PEAK_GBS / 1e3), 4)}
+                                                  if tr_p else None)},
         })
         if cpu is not None:
             result["cpu_baseline"] = {
