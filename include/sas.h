@@ -392,8 +392,9 @@ const char *sas_last_error(void);
  *   and dscore are deterministic; dK and dV are too, except in blocks whose selecting units hold
  *   more than 32768 (row, head) pairs in all, or number more than 256: their unit list is cut into
  *   several work items whose partial sums meet in fp32 atomic adds.
- *   Errors: as sas_sparse_prefill; SAS_ERR_UNSUPPORTED for fp32 and for per-group units with more than 64
- *   query heads per KV head; SAS_ERR_WORKSPACE when too small; SAS_ERR_SHAPE for reps without a gate. */
+ *   Errors: as sas_sparse_prefill; SAS_ERR_UNSUPPORTED for fp32, for per-group units with more than 64
+ *   query heads per KV head and for token strides of Q or dO at which 32 rows span 4 GiB or more;
+ *   SAS_ERR_WORKSPACE when too small; SAS_ERR_SHAPE for reps without a gate. */
 size_t sas_sparse_prefill_backward_workspace(const sas_problem *p, int32_t tq, int32_t sel_mode, int32_t kcap,
                                              int32_t gate);
 sas_status sas_sparse_prefill_backward(const sas_problem *p, const void *Q, const int64_t q_stride[3],

@@ -780,6 +780,8 @@ sas_status sas_sparse_prefill_backward(const sas_problem *p, const void *Q, cons
     return fail(SAS_ERR_SHAPE, "inputs and gradients must be 16-byte aligned with 16-byte-multiple row strides");
   if ((int64_t)(p->max_len - 1) * kv_stride[2] * eb + (int64_t)p->head_dim * eb > 0xFFFFFFFFll)
     return fail(SAS_ERR_UNSUPPORTED, "one (sequence, KV head) K/V slab must span less than 4 GiB");
+  if ((31 * q_stride[2] + p->head_dim) * eb > 0xFFFFFFFFll || (31 * o_stride[2] + p->head_dim) * eb > 0xFFFFFFFFll)
+    return fail(SAS_ERR_UNSUPPORTED, "32 rows of Q or dO must span less than 4 GiB");
   const BwdPlan pl = bwd_plan(*p, tq, sel_mode, kcap, gate != nullptr);
   if (workspace_bytes < pl.bytes)
     return fail(SAS_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, pl.bytes);

@@ -21,13 +21,17 @@
 //              accumulates dQ^T += K^T dS^T (transposing LDS reads of the K tile); writes LSE, D_row
 //              and per-32-row partial sums of dgate
 //   bwd_dkv    a (block, segment): K^T in registers and V in LDS while the units that selected the
-//              block stream their rows through LDS 32 at a time (one wave per 32 keys);
-//              S = Q K^T, dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS (transposing LDS reads)
+//              block stream their rows through LDS 32 at a time (one wave per 32 keys, or two
+//              that split the head dim of dK and dV for 64-key blocks); S = Q K^T, dP = dO V^T,
+//              then dV^T += dO^T P and dK^T += Q^T dS (transposing LDS reads).  A step of 32 rows of
+//              one head is copied through a buffer resource based at its first row (lane offsets
+//              fixed for the whole walk), and only steps on a causal or length edge are masked.
 //   bwd_gate   per unit: dgate (partials summed in a fixed order) and dscore
 // dQ, dgate and dscore are deterministic; dK and dV too, except in blocks whose unit list was cut
 // into several segments (their partial sums meet in fp32 atomic adds).
 #include <algorithm>
 #include <numeric>
+#include <type_traits>
 
 #include "common.h"
 
@@ -125,27 +129,25 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t *lds, int ks, int dt
   return as_bf8(w);
 }
 
-// Per-lane element offsets of the reads above, computed once so that a loop keeps a few registers
-// of addresses (the k-step, the tensor and the buffer only add constants):
-//   row[kk]: chunk 2kk + half of row `col` (rows_dot's read with row0 = 0; the same offsets serve
-//            row0 = 32w, since the swizzle of row 32w + col is that of row col)
-//   tlo[dt], thi[dt]: tr_operand's two reads at ks = 0 (ks adds 16 ks rows)
+// Per-lane element offsets of the reads above, as three bases that an immediate XOR completes (a
+// loop keeps three registers of addresses; the k-step, the tensor and the buffer only add constants):
+//   row(kk) = rb ^ 16 kk: chunk 2kk + half of row `col` (rows_dot's read with row0 = 0; the same
+//            offsets serve row0 = 32w, since the swizzle of row 32w + col is that of row col)
+//   tlo(x) = tlb ^ 32 x, thi(x) = thb ^ 32 x: tr_operand's two reads at ks = 0 for output tile
+//            dt = dt0 + x (dt0 a multiple of the tile count; ks adds 16 ks rows)
+// The chunk index is (2kk) ^ (half ^ swizzle) and (4dt) ^ (2chi + bit) ^ swizzle, and 8 x chunk sits
+// below the row's multiple of D, so the XOR with 16 kk or 32 dt acts on the bits that hold kk or dt.
 template <int D, bool TR = false>
 struct LdsOffsets {
-  int row[D / 16], tlo[D / 32], thi[D / 32];
-  __device__ __forceinline__ LdsOffsets(int col, int half) {
-    const int f = swz<D, TR>(col);
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) row[kk] = col * D + 8 * ((2 * kk + half) ^ f);
+  int rb, tlb, thb;
+  __device__ __forceinline__ LdsOffsets(int col, int half, int dt0 = 0) {
+    rb = col * D + 8 * (swz<D, TR>(col) ^ half);
     const int c16 = col & 15, chi = col >> 4;
     const int rlo = 4 * half + (c16 >> 2), rhi = rlo + 8;
     const int sub = 4 * (c16 & 1);
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      const int chunk = 4 * dt + 2 * chi + ((c16 & 3) >> 1);
-      tlo[dt] = rlo * D + 8 * (chunk ^ swz<D, TR>(rlo)) + sub;
-      thi[dt] = rhi * D + 8 * (chunk ^ swz<D, TR>(rhi)) + sub;
-    }
+    const int m = 2 * chi + ((c16 & 3) >> 1);
+    tlb = (rlo * D + 8 * (m ^ swz<D, TR>(rlo)) + sub) ^ (32 * dt0);
+    thb = (rhi * D + 8 * (m ^ swz<D, TR>(rhi)) + sub) ^ (32 * dt0);
   }
 };
 
@@ -480,8 +482,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
 // 32w .. 32w+31 of the block: K^T of those keys stays in registers and V in LDS for the whole walk,
 // while the units' rows stream through LDS 32 at a time (double-buffered: the copy of the next
 // 32 rows overlaps the compute of these).  A loaded row serves BLK keys.
-template <int D, int BLK>
-__global__ __launch_bounds__(BLK * 2, 2) void bwd_dkv_kernel(
+// NDH waves share each 32 keys, wave dh accumulating dK and dV over head-dim tiles
+// [dh NDT / NDH, (dh + 1) NDT / NDH); each recomputes the keys' S and dP.  With NDH = 2 a 64-key
+// block's wave holds half the accumulators, so two waves fit per SIMD (the LDS of two workgroups per
+// CU allows no more), at 1.5 times the matrix work of one wave per 32 keys.
+template <int D, int BLK, int NDH>
+__global__ __launch_bounds__(BLK * 2 * NDH, 2) void bwd_dkv_kernel(
     SeqTable st, const uint16_t *__restrict__ Q, int64_t qb, int64_t qh, int64_t qt, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, int64_t kb, int64_t kh, int64_t kt, const uint16_t *__restrict__ dO, int64_t ob,
     int64_t oh, int64_t ot, int tq, int S, int QB, int G, int per_head, int hq, int hkv, int npairs, int pchunks,
@@ -490,7 +496,8 @@ __global__ __launch_bounds__(BLK * 2, 2) void bwd_dkv_kernel(
     const float *__restrict__ gate, int kcap, const float *__restrict__ lse_ws, const float *__restrict__ dd_ws,
     float scale_log2, float scale, float *__restrict__ dK, float *__restrict__ dV, int64_t gb, int64_t gh,
     int64_t gt) {
-  constexpr int NKK = D / 16, NDT = D / 32, CPR = D / 8, NWV = BLK / 32, NT = NWV * 64;
+  constexpr int NKK = D / 16, NDT = D / 32, CPR = D / 8, NKW = BLK / 32, NWV = NKW * NDH, NT = NWV * 64;
+  constexpr int NX = NDT / NDH;  // head-dim tiles per wave
   constexpr int NI = 32 * CPR / NT;  // 16-byte copies per thread per staged tensor
   static_assert(NI >= 1 && 32 * CPR % NT == 0, "staging split");
   __shared__ __attribute__((aligned(16))) uint16_t qs[2][32 * D];
@@ -516,14 +523,15 @@ __global__ __launch_bounds__(BLK * 2, 2) void bwd_dkv_kernel(
   const int key0 = j * BLK;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kw = wave % NKW, dh = wave / NKW;  // this wave's 32 keys and head-dim share
   const int col = lane & 31, half = lane >> 5;
-  const int mykey = key0 + wave * 32 + col;
+  const int mykey = key0 + kw * 32 + col;
   if (it.count == 0) {
     // no unit selected this block: its gradients are zero (a block of one item only)
     if (mykey < L) {
       const int64_t o = b * gb + (int64_t)g * gh + (int64_t)mykey * gt;
 #pragma unroll
-      for (int d4 = 0; d4 < D / 4; d4 += 2) {
+      for (int d4 = dh * (D / 4 / NDH); d4 < (dh + 1) * (D / 4 / NDH); d4 += 2) {
         *reinterpret_cast<f32x4 *>(dK + o + 4 * (d4 + half)) = f32x4{0.f, 0.f, 0.f, 0.f};
         *reinterpret_cast<f32x4 *>(dV + o + 4 * (d4 + half)) = f32x4{0.f, 0.f, 0.f, 0.f};
       }
@@ -602,19 +610,60 @@ __global__ __launch_bounds__(BLK * 2, 2) void bwd_dkv_kernel(
   struct Geo {
     int h0, t_lo, c, rows, inv, F;
   };
+  // (k is wave-uniform, so is the unit's geometry: scalar registers)
   auto geo_of = [&](int k) {
     const i32x4 v = ginfo[k];
-    const int rows = v[3] & 255, inv = (int)((uint32_t)v[3] >> 8);
-    return Geo{v[0], v[1], v[2], rows, inv, rows * (per_head ? 1 : G)};
+    const int w3 = __builtin_amdgcn_readfirstlane(v[3]);
+    const int rows = w3 & 255, inv = (int)((uint32_t)w3 >> 8);
+    return Geo{__builtin_amdgcn_readfirstlane(v[0]), __builtin_amdgcn_readfirstlane(v[1]),
+               __builtin_amdgcn_readfirstlane(v[2]), rows, inv, rows * (per_head ? 1 : G)};
   };
   auto head_row = [](const Geo &x, int f, int &hh, int &tt) {
     const int qd = (int)(((uint32_t)f * (uint32_t)x.inv) >> 20);
     hh = x.h0 + qd;
     tt = x.t_lo + f - qd * x.rows;
   };
+  // Byte offsets of this thread's 16-byte chunks within 32 consecutive rows of one head (the same
+  // for every step whose rows are that: a unit whose row count is a multiple of 32).  When a copy
+  // instruction covers a multiple of 16 rows, copy y's rows are copy 0's moved by y such row groups, with the
+  // same swizzle (it depends on the row's low 4 bits): one lane offset and a scalar row offset serve.
+  constexpr int RPC = NT / CPR;  // rows per copy instruction of the workgroup
+  constexpr int NOFF = RPC % 16 == 0 ? 1 : NI;
+  uint32_t qoff[NOFF], ooff[NOFF];
+#pragma unroll
+  for (int y = 0; y < NOFF; ++y) {
+    const int e = y * NT + tid;
+    const int r = e / CPR, off = 8 * ((e % CPR) ^ swz<D, true>(r));
+    qoff[y] = 2u * (uint32_t)(r * qt + off);
+    ooff[y] = 2u * (uint32_t)(r * ot + off);
+  }
   // issue the copies of 32 rows (from flattened row c0 of unit k) into buffer buf
   auto stage = [&](int k, int c0, int buf) {
     const Geo x = geo_of(k);
+    if (x.rows % 32 == 0) {
+      // the 32 rows are rows tt0 .. tt0 + 31 of head hh: one buffer resource per tensor, based at
+      // the first row, spans them; the lanes' offsets were formed above
+      const int qd = (int)(((uint32_t)c0 * (uint32_t)x.inv) >> 20);
+      const int hh = x.h0 + qd, tt0 = x.t_lo + c0 - qd * x.rows;
+      const i32x4 rq = lds_rsrc(Q + b * qb + (int64_t)hh * qh + (int64_t)tt0 * qt, (uint32_t)(31 * qt + D) * 2u);
+      const i32x4 ro = lds_rsrc(dO + b * ob + (int64_t)hh * oh + (int64_t)tt0 * ot, (uint32_t)(31 * ot + D) * 2u);
+#pragma unroll
+      for (int y = 0; y < NI; ++y) {
+        const uint32_t lo16 = 2u * (buf * 32 * D + 8 * (y * NT + wave * 64));
+        const int yo = NOFF == 1 ? 0 : y;
+        const uint32_t rows_q = NOFF == 1 ? (uint32_t)(y * RPC * qt) * 2u : 0u;
+        const uint32_t rows_o = NOFF == 1 ? (uint32_t)(y * RPC * ot) * 2u : 0u;
+        buf_load_lds<16>(rq, lds_base(qs) + lo16, qoff[yo], rows_q);
+        buf_load_lds<16>(ro, lds_base(dos) + lo16, ooff[yo], rows_o);
+      }
+      if (wave == 0) {
+        const int64_t o = ((int64_t)b * hq + hh) * tq + tt0;
+        const uint32_t lo4 = 4u * (uint32_t)min(lane, 31);
+        buf_load_lds<4>(lds_rsrc(lse_ws + o, 128u), lds_base(lse_s) + 4u * (buf * 64), lo4, 0u);
+        buf_load_lds<4>(lds_rsrc(dd_ws + o, 128u), lds_base(dd_s) + 4u * (buf * 64), lo4, 0u);
+      }
+      return;
+    }
 #pragma unroll
     for (int y = 0; y < NI; ++y) {
       const int e = y * NT + tid;
@@ -635,13 +684,13 @@ __global__ __launch_bounds__(BLK * 2, 2) void bwd_dkv_kernel(
     }
   };
 
-  f32x16 adk[NDT], adv[NDT];
+  f32x16 adk[NX], adv[NX];
 #pragma unroll
-  for (int x = 0; x < NDT; ++x)
+  for (int x = 0; x < NX; ++x)
 #pragma unroll
     for (int r = 0; r < 16; ++r) adk[x][r] = adv[x][r] = 0.f;
 
-  const LdsOffsets<D, true> lo(col, half);
+  const LdsOffsets<D, true> lo0(col, half, dh * NX);
   __syncthreads();  // mu, mgl visible
   int k = 0, c0 = 0, buf = 0;
   if (cnt > 0) stage(0, 0, 0);
@@ -660,50 +709,66 @@ __global__ __launch_bounds__(BLK * 2, 2) void bwd_dkv_kernel(
     __syncthreads();  // this step's rows have landed; every wave is done with the other buffer
     if (kn < cnt) stage(kn, cn, buf ^ 1);
     const uint16_t *qsb = qs[buf], *dsb = dos[buf];
+    // the offsets' bases, opaque per step so that the XORed offsets are formed where they are used
+    // instead of being kept in registers across the loop
+    LdsOffsets<D, true> lo = lo0;
+    asm volatile("" : "+v"(lo.rb), "+v"(lo.tlb), "+v"(lo.thb));
     // S and dP (rows x this wave's keys): register r holds row 8(r/4) + 4half + r%4, key col
     f32x16 pa, dsa;
 #pragma unroll
     for (int r = 0; r < 16; ++r) pa[r] = dsa[r] = 0.f;
-    const uint16_t *vw = vlds + wave * 32 * D;
+    const uint16_t *vw = vlds + kw * 32 * D;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      const u32x4 qv = *reinterpret_cast<const u32x4 *>(qsb + lo.row[kk]);
+      const int ro = lo.rb ^ (16 * kk);
+      const u32x4 qv = *reinterpret_cast<const u32x4 *>(qsb + ro);
       pa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(qv), kreg[kk], pa, 0, 0, 0);
-      const u32x4 dv = *reinterpret_cast<const u32x4 *>(dsb + lo.row[kk]);
-      const u32x4 vv = *reinterpret_cast<const u32x4 *>(vw + lo.row[kk]);
+      const u32x4 dv = *reinterpret_cast<const u32x4 *>(dsb + ro);
+      const u32x4 vv = *reinterpret_cast<const u32x4 *>(vw + ro);
       dsa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(dv), as_bf8(vv), dsa, 0, 0, 0);
     }
+    // P and dS; only the unit's current block, a step past the unit's last row and the sequence's
+    // last block need masks (wave-uniform test)
+    auto softmax = [&](auto edge_t) {
+      constexpr bool EDGE = decltype(edge_t)::value;
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&lse_s[buf][8 * rb + 4 * half]);
-      const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&dd_s[buf][8 * rb + 4 * half]);
+      for (int rb = 0; rb < 4; ++rb) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&lse_s[buf][8 * rb + 4 * half]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&dd_s[buf][8 * rb + 4 * half]);
 #pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        const int r = 4 * rb + y;
-        const int f = c0 + 8 * rb + 4 * half + y;
-        bool vis = f < F && mykey < L;
-        if (diag) {
-          int hh, tt;
-          head_row(x, f, hh, tt);
-          vis = vis && mykey <= q0 + tt;
+        for (int y = 0; y < 4; ++y) {
+          const int r = 4 * rb + y;
+          float p = __builtin_amdgcn_exp2f(fmaf(pa[r], scale_log2, gl2 - l4[y]));
+          if constexpr (EDGE) {
+            const int f = c0 + 8 * rb + 4 * half + y;
+            bool vis = f < F && mykey < L;
+            if (diag) {
+              int hh, tt;
+              head_row(x, min(f, F - 1), hh, tt);
+              vis = vis && mykey <= q0 + tt;
+            }
+            p = vis ? p : 0.f;
+          }
+          pa[r] = p;
+          dsa[r] = p * (dsa[r] - d4[y]);
         }
-        const float p = vis ? __builtin_amdgcn_exp2f(fmaf(pa[r], scale_log2, gl2 - l4[y])) : 0.f;
-        pa[r] = p;
-        dsa[r] = p * (dsa[r] - d4[y]);
       }
-    }
+    };
+    if (diag || c0 + 32 > F || key0 + BLK > L) softmax(std::true_type{});
+    else softmax(std::false_type{});
     // dV^T += dO^T P, dK^T += Q^T dS over the 32 rows (two 16-row steps)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const bf16x8 pop = pack_operand(pa, 8 * ks);
       const bf16x8 dsop = pack_operand(dsa, 8 * ks);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const u32x2 dlo = lds_read_tr16(dsb + lo.tlo[dt] + 16 * ks * D), dhi = lds_read_tr16(dsb + lo.thi[dt] + 16 * ks * D);
-        const u32x2 qlo = lds_read_tr16(qsb + lo.tlo[dt] + 16 * ks * D), qhi = lds_read_tr16(qsb + lo.thi[dt] + 16 * ks * D);
+      for (int x = 0; x < NX; ++x) {
+        const int tl = (lo.tlb ^ (32 * x)) + 16 * ks * D, th = (lo.thb ^ (32 * x)) + 16 * ks * D;
+        const u32x2 dlo = lds_read_tr16(dsb + tl), dhi = lds_read_tr16(dsb + th);
+        const u32x2 qlo = lds_read_tr16(qsb + tl), qhi = lds_read_tr16(qsb + th);
         const u32x4 dw = {dlo[0], dlo[1], dhi[0], dhi[1]}, qw = {qlo[0], qlo[1], qhi[0], qhi[1]};
-        adv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(dw), pop, adv[dt], 0, 0, 0);
-        adk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(qw), dsop, adk[dt], 0, 0, 0);
+        adv[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(dw), pop, adv[x], 0, 0, 0);
+        adk[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(qw), dsop, adk[x], 0, 0, 0);
       }
     }
     k = kn;
@@ -715,13 +780,13 @@ __global__ __launch_bounds__(BLK * 2, 2) void bwd_dkv_kernel(
   if (mykey >= L) return;
   const int64_t o = b * gb + (int64_t)g * gh + (int64_t)mykey * gt;
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
+  for (int x = 0; x < NX; ++x)
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
-      const int dim = dt * 32 + 8 * rb + 4 * half;
-      const f32x4 vk = {adk[dt][4 * rb] * scale, adk[dt][4 * rb + 1] * scale, adk[dt][4 * rb + 2] * scale,
-                        adk[dt][4 * rb + 3] * scale};
-      const f32x4 vv = {adv[dt][4 * rb], adv[dt][4 * rb + 1], adv[dt][4 * rb + 2], adv[dt][4 * rb + 3]};
+      const int dim = (dh * NX + x) * 32 + 8 * rb + 4 * half;
+      const f32x4 vk = {adk[x][4 * rb] * scale, adk[x][4 * rb + 1] * scale, adk[x][4 * rb + 2] * scale,
+                        adk[x][4 * rb + 3] * scale};
+      const f32x4 vv = {adv[x][4 * rb], adv[x][4 * rb + 1], adv[x][4 * rb + 2], adv[x][4 * rb + 3]};
       if (it.multi) {
 #pragma unroll
         for (int y = 0; y < 4; ++y) {
@@ -979,7 +1044,9 @@ static hipError_t bwd_dispatch(const sas_problem &p, const SeqTable &st, const B
     const int pchunks = 8 / std::gcd(pl.npairs, 8);
     const int Ic = cdiv(pl.cap, pchunks);
     const int64_t nwg = (int64_t)8 * cdiv(pl.npairs * pchunks, 8) * Ic;
-    hipLaunchKernelGGL((bwd_dkv_kernel<D, BLK>), dim3((unsigned)nwg), dim3(BLK * 2), 0, s, st, q16, qs[0], qs[1], qs[2],
+    constexpr int NDH = (D == 128 && BLK == 64) ? 2 : 1;
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, BLK, NDH>), dim3((unsigned)nwg), dim3(BLK * 2 * NDH), 0, s, st, q16, qs[0],
+                       qs[1], qs[2],
                        k16, v16, kvs[0], kvs[1], kvs[2], do16, os[0], os[1], os[2], tq, S, pl.QB, G, per_head, p.hq,
                        p.hkv, pl.npairs, pchunks, Ic, pl.cap, (const BwdItem *)items, (const int32_t *)icount,
                        (const uint32_t *)bits, (const int16_t *)epos, pl.NBm, pl.W, pl.UG, gate, kcap, lse, dd,
