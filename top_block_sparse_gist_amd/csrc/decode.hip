@@ -58,7 +58,7 @@ __device__ __forceinline__ void decode_place(int id, int nwg, int64_t units, int
   u = p * G + w % G;
 }
 
-template <int D, int WPW, int TPW, typename OT, bool HS>
+template <int D, int WPW, int TPW, typename OT, bool HS, int VK>
 __global__ __launch_bounds__(WPW * 64) __attribute__((amdgpu_waves_per_eu(2))) void decode_bf16_kernel(
     SeqTable st, const uint16_t *__restrict__ Q, int64_t qb, int64_t qh, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, int64_t kb, int64_t kh, int64_t kt, const uint16_t *__restrict__ GK,
@@ -66,11 +66,11 @@ __global__ __launch_bounds__(WPW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     int per_head, const int32_t *__restrict__ idx, const int32_t *__restrict__ nsel, const float *__restrict__ gate,
     int kcap, float scale_log2, float *__restrict__ work, uint32_t *__restrict__ counters, OT *__restrict__ O,
     int64_t ob, int64_t oh, MetaArgs ma, PageArgs pg, int nwg, int64_t units) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[DecodeLds<D, WPW>::BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[DecodeLds<D, WPW, VK>::BYTES];
   int x;
   int64_t u;
   decode_place((int)blockIdx.x, nwg, units, G, per_head && G > 1, x, u);
-  decode_tile_body<D, WPW, TPW, OT, HS>(x, u, nwg, lds, st, Q, qb, qh, K, V, kb, kh, kt,
+  decode_tile_body<D, WPW, TPW, OT, HS, VK>(x, u, nwg, lds, st, Q, qb, qh, K, V, kb, kh, kt,
                                           GK, GV, gb, gh, gt, gist, blk, S, G, per_head, idx, nsel, gate, kcap,
                                           scale_log2, work, counters, O, ob, oh, ma, pg);
 }
@@ -119,6 +119,24 @@ static int64_t decode_resident_workgroups(int head_dim) {
   return (int64_t)per_cu * n;
 }
 
+template <int D, int WPW, int TPW, bool HS, int VK>
+static hipError_t decode_launch_vk(const sas_problem &p, const SeqTable &st, const DecodeShape &d, int nwg,
+                                const void *Q, const int64_t *qs, const void *K, const void *V, const int64_t *kvs,
+                                const void *gk, const void *gv, int64_t gb, int64_t gh, int64_t gt, int gist,
+                                int per_head, const int32_t *idx, const int32_t *nsel, const float *gate, int32_t kcap,
+                                float scale_log2, float *work, uint32_t *counters, void *O, const int64_t *os,
+                                const MetaArgs &ma, const PageArgs &pg, hipStream_t s) {
+  if ((uint64_t)nwg * (uint64_t)d.units * WPW * 64 > 0xFFFFFFFFull) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((decode_bf16_kernel<D, WPW, TPW, uint16_t, HS, VK>), dim3((unsigned)(nwg * d.units)), dim3(WPW * 64), 0,
+                     s, st, (const uint16_t *)Q, qs[0], qs[1], (const uint16_t *)K, (const uint16_t *)V, kvs[0],
+                     kvs[1], kvs[2], (const uint16_t *)gk, (const uint16_t *)gv, gb, gh, gt, gist, p.block, d.S,
+                     p.hq / p.hkv, per_head, idx, nsel, gate, kcap, scale_log2, work, counters, (uint16_t *)O, os[0],
+                     os[1], ma, pg, nwg, d.units);
+  return hipGetLastError();
+}
+
+// One-tile-per-wave launches over units of one head stage V in half tiles (decode_v_keys): with
+// half the LDS, three such workgroups fit per CU instead of two (their registers allow three).
 template <int D, int WPW, int TPW, bool HS>
 static hipError_t decode_launch(const sas_problem &p, const SeqTable &st, const DecodeShape &d, int nwg,
                                 const void *Q, const int64_t *qs, const void *K, const void *V, const int64_t *kvs,
@@ -126,13 +144,12 @@ static hipError_t decode_launch(const sas_problem &p, const SeqTable &st, const 
                                 int per_head, const int32_t *idx, const int32_t *nsel, const float *gate, int32_t kcap,
                                 float scale_log2, float *work, uint32_t *counters, void *O, const int64_t *os,
                                 const MetaArgs &ma, const PageArgs &pg, hipStream_t s) {
-  if ((uint64_t)nwg * (uint64_t)d.units * WPW * 64 > 0xFFFFFFFFull) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((decode_bf16_kernel<D, WPW, TPW, uint16_t, HS>), dim3((unsigned)(nwg * d.units)), dim3(WPW * 64), 0,
-                     s, st, (const uint16_t *)Q, qs[0], qs[1], (const uint16_t *)K, (const uint16_t *)V, kvs[0],
-                     kvs[1], kvs[2], (const uint16_t *)gk, (const uint16_t *)gv, gb, gh, gt, gist, p.block, d.S,
-                     p.hq / p.hkv, per_head, idx, nsel, gate, kcap, scale_log2, work, counters, (uint16_t *)O, os[0],
-                     os[1], ma, pg, nwg, d.units);
-  return hipGetLastError();
+  if constexpr (TPW == 1)
+    if (decode_v_keys(d.nh) == 32)
+      return decode_launch_vk<D, WPW, TPW, HS, 32>(p, st, d, nwg, Q, qs, K, V, kvs, gk, gv, gb, gh, gt, gist, per_head,
+                                                 idx, nsel, gate, kcap, scale_log2, work, counters, O, os, ma, pg, s);
+  return decode_launch_vk<D, WPW, TPW, HS, 64>(p, st, d, nwg, Q, qs, K, V, kvs, gk, gv, gb, gh, gt, gist, per_head,
+                                               idx, nsel, gate, kcap, scale_log2, work, counters, O, os, ma, pg, s);
 }
 
 hipError_t launch_decode_bf16(const sas_problem &p, const SeqTable &st, const void *Q, const int64_t *qs,

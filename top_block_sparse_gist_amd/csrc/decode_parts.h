@@ -619,11 +619,13 @@ __host__ __device__ inline int64_t record_floats(int nh, int D) { return (int64_
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// LDS of one attention workgroup: the V tiles (reused for the merges), then small arrays.
-template <int D, int WPW>
+// LDS of one attention workgroup: the V tiles (reused for the merges), then small arrays.  VK keys
+// of a wave's V tile are staged at a time: all 64, or (units of one head, whose in-workgroup merge
+// needs a sixteenth of the region) 32, in two halves, which halves the workgroup's LDS.
+template <int D, int WPW, int VK = 64>
 struct DecodeLds {
   static constexpr int VROW = D + VPAD;
-  static constexpr int TILE_BYTES = WPW * 64 * VROW * 2;
+  static constexpr int TILE_BYTES = WPW * VK * VROW * 2;
   static constexpr int SMALL_FLOATS = 2 * WPW * 16 + 4 + 32;  // m, l per wave; flag; M, L per head
   static constexpr int BYTES = TILE_BYTES + SMALL_FLOATS * 4;
 };
@@ -653,7 +655,7 @@ struct PageArgs {
 // past them is -1), so it needs only the first nwg_u of the nwg workgroups: the others exit
 // before touching the records, and the last of the nwg_u to arrive merges their records and
 // writes O.
-template <int D, int WPW, int TPW, typename OT, bool HS = false>
+template <int D, int WPW, int TPW, typename OT, bool HS = false, int VK = 64>
 __device__ __forceinline__ void decode_tile_body(
     int bx, int64_t u, int nwg, unsigned char *lds, SeqTable st, const uint16_t *__restrict__ Q, int64_t qb,
     int64_t qh, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, int64_t kb, int64_t kh, int64_t kt,
@@ -666,8 +668,10 @@ __device__ __forceinline__ void decode_tile_body(
   constexpr int NDT = D / 16;   // 16-dim output tiles
   constexpr int VROW = D + VPAD;
   constexpr int NT = WPW * 64;
-  using Lds = DecodeLds<D, WPW>;
-  auto vlds = reinterpret_cast<uint16_t(*)[64 * VROW]>(lds);
+  using Lds = DecodeLds<D, WPW, VK>;
+  static_assert(VK == 64 || VK == 32, "V staged as a whole tile or in two halves");
+  static_assert(VK == 64 || WPW * VK * VROW * 2 >= WPW * 16 * D * 4, "in-workgroup merge region");
+  auto vlds = reinterpret_cast<uint16_t(*)[VK * VROW]>(lds);
   float *small = reinterpret_cast<float *>(lds + Lds::TILE_BYTES);
   auto m_sh = reinterpret_cast<float(*)[16]>(small);
   auto l_sh = reinterpret_cast<float(*)[16]>(small + WPW * 16);
@@ -818,6 +822,19 @@ __device__ __forceinline__ void decode_tile_body(
   constexpr int VCH = D / 8;  // 16-byte chunks per V row; VCH loads per lane
   u32x4 kreg[4][NKK];
   u32x4 vreg[VCH];
+  uint16_t *vl = vlds[wave];
+  // V loads x in [x0, x1): with half-tile staging the second half's registers are reloaded only
+  // after that half has been copied to LDS
+  auto issue_v = [&](const Tile &d, int x0, int x1) {
+#pragma unroll
+    for (int x = x0; x < x1; ++x) {
+      const int e = x * 64 + lane;
+      const int key = e / VCH, ch = e % VCH;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (key < d.nvalid) v = *reinterpret_cast<const u32x4 *>(d.vbase + (int64_t)(d.roff + key) * d.rstride + ch * 8);
+      vreg[x] = v;
+    }
+  };
   auto issue = [&](const Tile &d) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -831,7 +848,7 @@ __device__ __forceinline__ void decode_tile_body(
       }
     }
 #pragma unroll
-    for (int x = 0; x < VCH; ++x) {
+    for (int x = 0; x < (VK == 64 ? VCH : VCH / 2); ++x) {
       const int e = x * 64 + lane;
       const int key = e / VCH, ch = e % VCH;
       u32x4 v = {0u, 0u, 0u, 0u};
@@ -839,8 +856,18 @@ __device__ __forceinline__ void decode_tile_body(
       vreg[x] = v;
     }
   };
-  uint16_t *vl = vlds[wave];
+  // (half-tile staging) V rows of keys [32h, 32h + 32) to this wave's LDS rows 0..31 (register x
+  // holds key (64x + lane) / VCH, so each half is a contiguous range of registers)
+  auto stage_v = [&](int h) {
+#pragma unroll
+    for (int x = h * (VCH / 2); x < (h + 1) * (VCH / 2); ++x) {
+      const int e = x * 64 + lane;
+      const int key = e / VCH - 32 * h, ch = e % VCH;
+      *reinterpret_cast<u32x4 *>(vl + key * VROW + ch * 8) = vreg[x];
+    }
+  };
   issue(tl[0]);
+  if constexpr (VK == 32) issue_v(tl[0], VCH / 2, VCH);
 #pragma unroll
   for (int k = 0; k < TPW; ++k) {
     const Tile &d = tl[k];
@@ -857,11 +884,15 @@ __device__ __forceinline__ void decode_tile_body(
       }
       // the V tile region is this wave's own: the reads of the previous tile's PV precede these
       // writes in the wave's LDS queue
+      if constexpr (VK == 64) {
 #pragma unroll
-      for (int x = 0; x < VCH; ++x) {
-        const int e = x * 64 + lane;
-        const int key = e / VCH, ch = e % VCH;
-        *reinterpret_cast<u32x4 *>(vl + key * VROW + ch * 8) = vreg[x];
+        for (int x = 0; x < VCH; ++x) {
+          const int e = x * 64 + lane;
+          const int key = e / VCH, ch = e % VCH;
+          *reinterpret_cast<u32x4 *>(vl + key * VROW + ch * 8) = vreg[x];
+        }
+      } else {
+        stage_v(0);
       }
     }
     // the registers are free: the next tile's loads fly during this tile's softmax and PV
@@ -912,21 +943,46 @@ __device__ __forceinline__ void decode_tile_body(
         w[3] = pack_bf16x2(sacc[2 * ks + 1][2], sacc[2 * ks + 1][3]);
         preg[ks] = as_bf16x8(w);
       }
-      // the V tile is written and read by this wave only: wait for its LDS writes
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
       // ---- O^T += V^T P^T; the V^T operand (dim 16dt + col, keys 32ks + 4grp + {0..3} then
       //      32ks + 16 + 4grp + {0..3}) comes from two transpose reads of the row-major tile
+      if constexpr (VK == 64) {
+        // the V tile is written and read by this wave only: wait for its LDS writes
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
+        for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const uint16_t *src = vl + (ks * 32 + 4 * grp + (col >> 2)) * VROW + dt * 16 + 4 * (col & 3);
+            const u32x2 lo = lds_read_tr16(src);
+            const u32x2 hi = lds_read_tr16(src + 16 * VROW);
+            const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+            acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w), preg[ks], acc_o[dt], 0, 0, 0);
+          }
+        }
+      } else {
+        // two halves through the same 32 rows: keys 0..31 (staged above), then 32..63, whose
+        // writes follow the first half's transposing reads in the wave's LDS queue
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const uint16_t *src = vl + (ks * 32 + 4 * grp + (col >> 2)) * VROW + dt * 16 + 4 * (col & 3);
-          const u32x2 lo = lds_read_tr16(src);
-          const u32x2 hi = lds_read_tr16(src + 16 * VROW);
-          const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-          acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w), preg[ks], acc_o[dt], 0, 0, 0);
+          if (ks == 1) {
+            stage_v(1);
+            // the second half's registers are free: the next tile's loads of them fly now
+            if (k + 1 < TPW) issue_v(tl[k + 1], VCH / 2, VCH);
+          }
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            const uint16_t *src = vl + (4 * grp + (col >> 2)) * VROW + dt * 16 + 4 * (col & 3);
+            const u32x2 lo = lds_read_tr16(src);
+            const u32x2 hi = lds_read_tr16(src + 16 * VROW);
+            const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+            acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w), preg[ks], acc_o[dt], 0, 0, 0);
+          }
         }
       }
+    } else if constexpr (VK == 32) {
+      // an empty tile still hands the next tile its second half of V registers
+      if (k + 1 < TPW) issue_v(tl[k + 1], VCH / 2, VCH);
     }
   }
   l_run += __shfl_xor(l_run, 16, 64);
@@ -1072,6 +1128,11 @@ __device__ __forceinline__ void decode_tile_body(
   if (tid == 0) __hip_atomic_store(&counters[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Keys of V staged in LDS at a time by one-tile-per-wave launches: units of one head stage half tiles
+// (their workgroups need half the LDS, so more of them fit per CU).  The merge capacity below is
+// taken at that size for every launch of such units.
+static inline int decode_v_keys(int nh) { return nh == 1 ? 32 : 64; }
+
 struct DecodeShape {
   int S, nh, tiles_cap, wpw, nwg_cap;
   int64_t units;
@@ -1089,12 +1150,14 @@ static inline DecodeShape decode_shape(const sas_problem &p, int32_t sel_mode, i
   return d;
 }
 
-// Tiles per wave for a launch: two on long lists (the second tile's loads overlap the first one's
-// compute, and the merge reads half the records), one on short lists, where more workgroups in
-// flight matter more; three when that brings a grid that would need two rounds of `slots`
-// resident workgroups down to one.
+// Tiles per wave for a launch: one on short lists, where more workgroups in flight matter more,
+// and for units of one head, whose half-tile V staging lets three one-tile workgroups run per CU
+// (12 waves, each with a whole tile of loads in flight, against 8 at two tiles per wave: 69.0
+// against 72.8 us on a batch of 8 long per-head lists); otherwise two on long lists (the second
+// tile's loads overlap the first one's compute, and the merge reads half the records), three
+// when that brings a grid that would need two rounds of `slots` resident workgroups down to one.
 static inline int decode_tiles_per_wave(const DecodeShape &d, int64_t slots) {
-  if (d.tiles_cap < 32) return 1;
+  if (d.tiles_cap < 32 || decode_v_keys(d.nh) == 32) return 1;
   const int64_t wg2 = d.units * ((d.tiles_cap + 2 * d.wpw - 1) / (2 * d.wpw));
   const int64_t wg3 = d.units * ((d.tiles_cap + 3 * d.wpw - 1) / (3 * d.wpw));
   return (wg2 > slots && wg3 <= slots) ? 3 : 2;
@@ -1105,7 +1168,7 @@ static inline int decode_tiles_per_wave(const DecodeShape &d, int64_t slots) {
 static inline int decode_merge_capacity(int nh, int D, int wpw) {
   const int nt = wpw * 64, q4 = nh * (D / 4);
   const int rg = q4 >= nt ? 1 : nt / q4;
-  const int tile_bytes = wpw * 64 * (D + VPAD) * 2;
+  const int tile_bytes = wpw * decode_v_keys(nh) * (D + VPAD) * 2;
   const int red_bytes = rg > 1 ? rg * q4 * 16 : 0;
   return (tile_bytes - red_bytes - 16) / (12 * nh);
 }
