@@ -555,7 +555,7 @@ def main():
         tf_att = fl["flops"] / (t_pf_att * 1e-3) / 1e12
         dec_bytes = by["kv"] + by["qo"]
         ach = dec_bytes / (t_dc_att * 1e-3) / 1e9
-        tr_d = measured_traffic("decode_bf16_kernel<128, 4, 2, unsigned short, false>")
+        tr_d = measured_traffic("decode_bf16_kernel<128, 4, 1, unsigned short, false, 32>")
         tr_p = measured_traffic("prefill_bf16_kernel<128, 2, 64>")
         result.update({
             "value": round(value, 2), "ms_per_step": round(t_pf + t_dc, 5),
@@ -636,7 +636,7 @@ def main():
             ms_att, _ = timer.time(fns["attend"], K_, W_)
             gbs = by2["total"] / (ms * 1e-3) / 1e9
             att = (by2["kv"] + by2["qo"]) / (ms_att * 1e-3) / 1e9
-            tr = measured_traffic("decode_bf16_kernel<128, 4, 1, unsigned short, false>")
+            tr = measured_traffic("decode_bf16_kernel<128, 4, 1, unsigned short, false, 64>")
             extra["decode_32k"] = {"workload": "decode_b8_h32x8_d128_ctx32768_blk64_top16+current (sparsity 0.967)",
                                    "step_us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
                                    "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
