@@ -246,7 +246,8 @@ sas_status sas_select_decode(const sas_problem *p, const void *Q, const int64_t 
  *   one workspace must not overlap in time.
  *   bf16: SAS_ERR_UNSUPPORTED when kcap (plus the gist tiles) needs more split-K records per
  *   unit than the in-kernel merge can stage (with 16 heads per KV head at d 128: about 3000
- *   list entries of 64 keys; far more with fewer heads). */
+ *   list entries of 64 keys; far more with fewer heads; units of one head, per-head selection,
+ *   about 10,900 tiles of 64 keys). */
 size_t sas_sparse_decode_workspace(const sas_problem *p, int32_t sel_mode, int32_t kcap,
                                    int32_t gist);
 sas_status sas_sparse_decode(const sas_problem *p, const void *Q, const int64_t q_stride[2],
