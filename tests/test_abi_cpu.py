@@ -184,6 +184,13 @@ def test_attention_validation_codes():
     assert b"merge holds 383" in lib.sas_last_error()
     need_ok = lib.sas_sparse_decode_workspace(C.byref(p16), 0, 3000, 0)
     assert need_ok > 0  # 3000 entries: 375 records, within the merge
+    # units of one head (per-head lists) run one tile per wave and stage V in half tiles: the merge
+    # holds 2729 records of 4 tiles, so 10,916 entries of 64 keys fit and 10,917 do not
+    ph, aph = _problem()
+    need_ph = lib.sas_sparse_decode_workspace(C.byref(ph), _lib.SAS_SEL_HEAD, 10917, 0)
+    assert lib.sas_sparse_decode(C.byref(ph), FAKE, qs2, FAKE, FAKE, kvs, None, None, None, _lib.SAS_SEL_HEAD, FAKE,
+                                 FAKE, None, 10917, 0.0, FAKE, qs2, FAKE, need_ph, None) == _lib.SAS_ERR_UNSUPPORTED
+    assert b"needs 2730 split-K records per unit; the merge holds 2729" in lib.sas_last_error()
     # more than 16 query heads per KV head in per-group decode
     p9, a9 = _problem(hq=34, hkv=2)
     need9 = lib.sas_sparse_decode_workspace(C.byref(p9), 0, 8, 0)
